@@ -1,0 +1,280 @@
+"""CPU oracle of the DSA layer step -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product library
+(``sparse_attention_scores_amd``) never imports it and shares no code with it.
+
+The arithmetic lives in ``dsa_oracle.c`` (plain C, IEEE double, OpenMP over
+query rows).  This module only compiles it with gcc and marshals numpy arrays.
+
+Pins (see ``tests/test_oracle_*.py``): every function here is checked against
+closed forms, the worked examples of the "Module glm5next_dsa_ref" page,
+brute force on tiny inputs, and library routines (numpy / torch in float64).
+Parity unpinned: numerics of real GLM-5.x checkpoints (no weights or goldens
+exist here); the readings of the pages that the oracle takes are listed in the
+header of each function in ``dsa_oracle.c``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "dsa_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libdsa_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+INVALID = -1
+F32, BF16, E4M3, F64 = 0, 1, 2, 3
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (OpenMP) into libdsa_oracle.so."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+               "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH):
+                build(force=True)
+            lib = ctypes.CDLL(_LIB_PATH)
+            P = ctypes.c_void_p
+            I64 = ctypes.c_int64
+            I32 = ctypes.c_int32
+            D = ctypes.c_double
+            lib.orc_bf16_value.argtypes = [ctypes.c_uint16]
+            lib.orc_bf16_value.restype = D
+            lib.orc_e4m3_value.argtypes = [ctypes.c_uint8]
+            lib.orc_e4m3_value.restype = D
+            lib.orc_token_visible.argtypes = [I32, I32, I64]
+            lib.orc_pool_visible.argtypes = [I32, I32, I32, I64]
+            lib.orc_index_scores.argtypes = [I64, I64, I64, I64, I64, P, ctypes.c_int, P,
+                                             ctypes.c_int, P, P, D, P, P, I32, P, I64, P, P]
+            lib.orc_topk.argtypes = [P, I64, I64, I64, P, P, I32, I32, P]
+            lib.orc_pool_keys.argtypes = [I64, I64, I64, I32, P, ctypes.c_int, P,
+                                          ctypes.c_int, P, P, P]
+            lib.orc_pool_select.argtypes = [P, I64, I64, I64, P, P, I32, I32, I32, P, P]
+            lib.orc_topk_to_mask.argtypes = [P, I64, I64, ctypes.c_int, I32, I32, P]
+            lib.orc_topk_to_mask.restype = None
+            lib.orc_sparse_attend.argtypes = [I64, I64, I64, I64, I64, I64, I64, I64,
+                                              P, ctypes.c_int, P, I64, P, I64, P, P, P, D,
+                                              P, I64, P, P]
+            lib.orc_max_threads.argtypes = []
+            _lib = lib
+    return _lib
+
+
+def threads() -> int:
+    """Number of OpenMP threads the oracle uses."""
+    return int(_load().orc_max_threads())
+
+
+# --------------------------------------------------------------------------
+# marshalling helpers
+# --------------------------------------------------------------------------
+
+def _storage(a):
+    """Return (contiguous numpy array, dtype code) for a numpy array or a CPU
+    torch tensor.  bf16 tensors travel as their raw uint16 bits and float8
+    e4m3fn tensors as their raw uint8 codes."""
+    try:
+        import torch
+        if isinstance(a, torch.Tensor):
+            t = a.detach().cpu().contiguous()
+            if t.dtype == torch.bfloat16:
+                return t.view(torch.int16).numpy().view(np.uint16), BF16
+            if t.dtype == torch.float8_e4m3fn:
+                return t.view(torch.uint8).numpy(), E4M3
+            a = t.numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.float32:
+        return a, F32
+    if a.dtype == np.float64:
+        return a, F64
+    if a.dtype == np.uint16:
+        return a, BF16
+    if a.dtype == np.uint8:
+        return a, E4M3
+    raise TypeError("unsupported oracle input dtype %s" % a.dtype)
+
+
+def _i32(a):
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def _f32(a):
+    try:
+        import torch
+        if isinstance(a, torch.Tensor):
+            a = a.detach().cpu().float().numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _rows(rows, n_all):
+    if rows is None:
+        return None, n_all
+    r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    return r, len(r)
+
+
+# --------------------------------------------------------------------------
+# public functions
+# --------------------------------------------------------------------------
+
+def bf16_value(bits: int) -> float:
+    return _load().orc_bf16_value(bits)
+
+
+def e4m3_value(code: int) -> float:
+    return _load().orc_e4m3_value(code)
+
+
+def token_visible(pad: int, qpos: int, s: int) -> bool:
+    return bool(_load().orc_token_visible(pad, qpos, s))
+
+
+def pool_visible(pad: int, kpool: int, qpos: int, i: int) -> bool:
+    return bool(_load().orc_pool_visible(pad, kpool, qpos, i))
+
+
+def index_scores(q, k, w, scale, q_pos, pad, k_scale=None, kpool=0, rows=None,
+                 want_mag=False):
+    """Index scores for the given query rows.
+
+    q: [B,Tq,H,d]; k: [B,Tk,d] (Tk pools when kpool > 0); w: [B,Tq,H];
+    q_pos: [B,Tq] query positions; pad: [B] left-padding counts.
+    Returns S [n_rows,Tk] float32 (and the magnitude A [n_rows,Tk] float64)."""
+    qa, qt = _storage(q)
+    ka, kt = _storage(k)
+    B, Tq, H, d = qa.shape
+    Tk = ka.shape[1]
+    assert ka.shape == (B, Tk, d)
+    wa = _f32(w).reshape(B, Tq, H)
+    ks = None if k_scale is None else _f32(k_scale).reshape(B, Tk)
+    qp = _i32(q_pos).reshape(B * Tq)
+    pd = _i32(pad).reshape(B)
+    r, n = _rows(rows, B * Tq)
+    S = np.empty((n, Tk), np.float32)
+    A = np.empty((n, Tk), np.float64) if want_mag else None
+    rc = _load().orc_index_scores(B, Tq, Tk, H, d, _ptr(qa), qt, _ptr(ka), kt, _ptr(ks),
+                                  _ptr(wa), float(scale), _ptr(qp), _ptr(pd), int(kpool),
+                                  _ptr(r), n, _ptr(S), _ptr(A))
+    if rc != 0:
+        raise ValueError("oracle index_scores: NaN input")
+    return (S, A) if want_mag else S
+
+
+def topk(S, row_qpos, row_pad, k, kpool=0):
+    """Top-k per row (higher score, then smaller index), INVALID-padded.
+
+    S: [rows, n_cols] float32; row_qpos/row_pad: per-row query position and
+    sequence padding (visibility)."""
+    Sa = _f32(S)
+    n_rows, n_cols = Sa.shape
+    out = np.empty((n_rows, k), np.int32)
+    rc = _load().orc_topk(_ptr(Sa), n_rows, n_cols, n_cols, _ptr(_i32(row_qpos)),
+                          _ptr(_i32(row_pad)), int(kpool), int(k), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle topk: NaN score")
+    return out
+
+
+def pool_keys(k, gate, pad, kpool):
+    """Pooled indexer keys in float64: [B, L//kpool, d], and n_pools [B]."""
+    ka, kt = _storage(k)
+    ga, gt = _storage(gate)
+    B, L, d = ka.shape
+    pd = _i32(pad).reshape(B)
+    pk = np.empty((B, L // kpool, d), np.float64)
+    npools = np.empty(B, np.int32)
+    _load().orc_pool_keys(B, L, d, int(kpool), _ptr(ka), kt, _ptr(ga), gt, _ptr(pd),
+                          _ptr(pk), _ptr(npools))
+    return pk, npools
+
+
+def pool_select(S, row_qpos, row_pad, kpool, select_k, out_width, want_pools=False):
+    """topk_pools + expand_selection per row. S: [rows, n_pool_cols]."""
+    Sa = _f32(S)
+    n_rows, n_cols = Sa.shape
+    tok = np.empty((n_rows, out_width), np.int32)
+    pools = np.empty((n_rows, select_k), np.int32) if want_pools else None
+    rc = _load().orc_pool_select(_ptr(Sa), n_rows, n_cols, n_cols, _ptr(_i32(row_qpos)),
+                                 _ptr(_i32(row_pad)), int(kpool), int(select_k),
+                                 int(out_width), _ptr(tok), _ptr(pools))
+    if rc == -1:
+        raise ValueError("oracle pool_select: NaN score")
+    if rc == -2:
+        raise ValueError("oracle pool_select: out_width too small")
+    return (tok, pools) if want_pools else tok
+
+
+def topk_to_mask(idx_row, Tk, pad=None, qpos=None):
+    """Boolean mask over Tk keys of the selected set of one index row."""
+    ia = _i32(idx_row).reshape(-1)
+    m = np.empty(Tk, np.uint8)
+    has = pad is not None and qpos is not None
+    _load().orc_topk_to_mask(_ptr(ia), len(ia), int(Tk), int(has),
+                             int(pad or 0), int(qpos or 0), _ptr(m))
+    return m.astype(bool)
+
+
+def sparse_attend(q, K, V, idx, scale, kv_heads, q_pos=None, pad=None, rows=None,
+                  k_row_stride=None, v_row_stride=None, vd=None, v_offset=0):
+    """Sparse attention over each query's selected set, in float64.
+
+    q: [B,Tq,H,kd]; K: [B,Tk,kv_heads,kd] (or any [B,Tk,...] whose rows are
+    k_row_stride elements apart); V likewise, or V=None to use the first vd
+    columns of K's rows (absorbed MLA).  idx: [B,Tq,n_sel].
+    Returns (out [n_rows,H,vd], lse [n_rows,H])."""
+    qa, qt = _storage(q)
+    Ka, kt = _storage(K)
+    B, Tq, H, kd = qa.shape
+    Tk = Ka.shape[1]
+    ks = k_row_stride if k_row_stride is not None else int(np.prod(Ka.shape[2:]))
+    if V is None:
+        Va, vt = Ka, kt
+        vs = ks if v_row_stride is None else v_row_stride
+        assert vd is not None
+    else:
+        Va, vt = _storage(V)
+        vs = v_row_stride if v_row_stride is not None else int(np.prod(Va.shape[2:]))
+        if vd is None:
+            vd = Va.shape[-1]
+    assert qt == kt == vt, "q, K and V must share a storage dtype"
+    ia = _i32(idx).reshape(B, Tq, -1)
+    n_sel = ia.shape[2]
+    qp = None if q_pos is None else _i32(q_pos).reshape(B * Tq)
+    pd = None if pad is None else _i32(pad).reshape(B)
+    r, n = _rows(rows, B * Tq)
+    out = np.empty((n, H, vd), np.float64)
+    lse = np.empty((n, H), np.float64)
+    vptr = _ptr(Va)
+    if v_offset:
+        vptr = ctypes.c_void_p(vptr.value + v_offset * Va.itemsize)
+    rc = _load().orc_sparse_attend(B, Tq, Tk, H, kd, vd, int(kv_heads), n_sel, _ptr(qa), qt,
+                                   _ptr(Ka), ks, vptr, vs, _ptr(ia), _ptr(qp), _ptr(pd),
+                                   float(scale), _ptr(r), n, _ptr(out), _ptr(lse))
+    if rc != 0:
+        raise ValueError("oracle sparse_attend: bad kv_heads")
+    return out, lse
