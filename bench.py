@@ -1,0 +1,260 @@
+"""Benchmark of the DSA layer step on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config 2] [--no-cpu]
+
+One step = the whole hot path over one batch of synthetic inputs already
+resident in HBM: lightning-indexer scores -> per-query top-k -> sparse MLA
+attention (for the pooled configuration: pool keys -> pooled scores -> pool
+select -> per-head attention).  Prints one JSON line with the throughput in
+query tokens/s, the roofline of the dominant kernel (timed live with HIP
+events on the stream the kernels run on), and the CPU oracle timed on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+
+METRIC = "DSA layer tokens/s on 1 MI355X; indexer MFMA % and attend HBM GB/s of peak"
+
+WORKLOAD_TEXT = {
+    1: "tiny fp32 layer: 1 x 64 causal queries over 64 keys; indexer 4 heads x 32, top_k 8; "
+       "attention 4 heads, kd 48, vd 32, per-head K/V",
+    2: "decode: 32 sequences x 1 query over 8192 keys; indexer 32 heads x 128 bf16, "
+       "top_k 2048; absorbed MLA 64 heads over shared 576-wide latent rows, vd 512",
+    3: "causal prefill: 1 sequence x 4096 queries over 4096 keys; indexer 32 heads x 128 bf16, "
+       "top_k 2048; absorbed MLA 64 heads, kd 576, vd 512",
+    4: "long-context decode: 8 sequences x 1 query over 131072 keys; fp8-e4m3 indexer keys "
+       "with per-row scales, 32 heads x 128, top_k 2048; absorbed MLA 64 heads, kd 576, vd 512",
+}
+
+
+def _parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4])
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-rows", type=int, default=8, help="query rows in the oracle sample")
+    return ap.parse_args()
+
+
+class Step:
+    """Preallocated buffers and the three ABI calls of one layer step."""
+
+    def __init__(self, dsa, inp):
+        import torch
+        self.dsa, self.inp = dsa, inp
+        self.lo, self.hi = dsa.visibility_ranges(inp["pad"], inp["q_pos"])
+        B, Tq, Tk = inp["B"], inp["Tq"], inp["Tk"]
+        dev = inp["q_pos"].device
+        self.k = inp["top_k"]
+        self.S = torch.empty((B, Tq, Tk), dtype=torch.float32, device=dev)
+        self.idx = torch.empty((B, Tq, self.k), dtype=torch.int32, device=dev)
+        self.f32 = inp["dtype"] == "f32"
+        H, vd = inp["H"], inp["vd"]
+        self.out = torch.empty((B, Tq, H, vd), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((B, Tq, H), dtype=torch.float32, device=dev)
+        nt = dsa.topk_workspace_size(B * Tq, Tk, self.k)
+        self.ws_topk = torch.empty(max(nt, 1), dtype=torch.uint8, device=dev)
+        if self.f32:
+            self.K, self.V, self.kvh = inp["K"], inp["V"], H
+            self.ws_attn = None
+        else:
+            self.K, self.V, self.kvh = inp["KV"], None, 1
+            dims = dsa._AttnDims(B, Tq, Tk, H, inp["kd"], vd, 1, self.k, inp["scale_attn"])
+            na = dsa.sparse_attend_workspace_size(dims)
+            self.ws_attn = torch.empty(max(na, 1), dtype=torch.uint8, device=dev)
+
+    def index(self):
+        i = self.inp
+        self.dsa.index_scores(i["q_idx"], i["k_idx"], i["w"], self.lo, self.hi, i["scale_idx"],
+                              k_scale=i["k_scale"], out=self.S)
+
+    def topk(self):
+        self.dsa.topk(self.S, self.lo, self.hi, self.k, out=self.idx, workspace=self.ws_topk)
+
+    def attend(self):
+        i = self.inp
+        self.dsa.sparse_attend(i["q"], self.K, self.V, self.idx, i["scale_attn"], self.kvh,
+                               vd=i["vd"], vis_lo=self.lo, vis_hi=self.hi, out=self.out,
+                               lse=self.lse, workspace=self.ws_attn)
+
+    stages = ("index", "topk", "attend")
+
+
+def algorithmic_work(inp):
+    """Bytes the method must move and flops it must do, per stage (see the
+    measurement section of the design doc): only visible pairs and selected keys
+    count, not the dense work the method avoids."""
+    B, Tq, Tk, Hi, d = inp["B"], inp["Tq"], inp["Tk"], inp["Hi"], inp["d"]
+    H, kd, vd, k = inp["H"], inp["kd"], inp["vd"], inp["top_k"]
+    f32 = inp["dtype"] == "f32"
+    eb = 4 if f32 else 2
+    kb = 1 if inp.get("fp8_keys") else eb
+    if inp.get("causal"):
+        vis_pairs = B * Tq * (Tq + 1) // 2
+        sel_pairs = B * sum(min(t + 1, k) for t in range(Tq))
+    else:
+        vis_pairs = B * Tq * Tk
+        sel_pairs = B * Tq * min(k, Tk)
+    idx_bytes = (B * Tk * d * kb + (B * Tk * 4 if inp.get("fp8_keys") else 0)
+                 + B * Tq * Hi * d * eb + B * Tq * Hi * 4 + vis_pairs * 4)
+    idx_flops = 2 * Hi * d * vis_pairs
+    topk_bytes = vis_pairs * 4 + B * Tq * k * 4
+    row_bytes = (kd * eb) if not f32 else (kd + vd) * eb * H  # f32 config: per-head K and V rows
+    if inp.get("causal") and not f32:
+        # the selected rows are re-read from cache; the method's own HBM bytes
+        # are the distinct rows once
+        gather = B * Tk * kd * eb
+    else:
+        gather = sel_pairs * row_bytes
+    att_bytes = gather + B * Tq * H * kd * eb + B * Tq * k * 4 + B * Tq * H * (vd + 1) * 4
+    att_flops = 2 * H * (kd + vd) * sel_pairs
+    return {"index": (idx_bytes, idx_flops), "topk": (topk_bytes, 0),
+            "attend": (att_bytes, att_flops)}
+
+
+def cpu_baseline(cfg, rows_wanted):
+    """The oracle (as it stands) on a bounded sample of the same workload:
+    `rows_wanted` query rows through index scores -> top-k -> attention."""
+    import numpy as np
+
+    import oracle
+    from sparse_attention_scores_amd import workloads as W
+    inp = W.make(cfg, device="cpu")
+    B, Tq = inp["B"], inp["Tq"]
+    rows = np.linspace(0, B * Tq - 1, num=min(rows_wanted, B * Tq)).round().astype(np.int64)
+    rows = np.unique(rows)
+    qp_all = inp["q_pos"].numpy().reshape(-1)
+    pd_all = np.repeat(inp["pad"].numpy(), Tq)
+    t0 = time.perf_counter()
+    S = oracle.index_scores(inp["q_idx"], inp["k_idx"], inp["w"], inp["scale_idx"],
+                            inp["q_pos"], inp["pad"], k_scale=inp["k_scale"], rows=rows)
+    sel = oracle.topk(S, qp_all[rows], pd_all[rows], inp["top_k"])
+    idx = np.full((B * Tq, inp["top_k"]), -1, np.int32)
+    idx[rows] = sel
+    idx = idx.reshape(B, Tq, -1)
+    if inp["dtype"] == "f32":
+        oracle.sparse_attend(inp["q"], inp["K"], inp["V"], idx, inp["scale_attn"], inp["H"],
+                             q_pos=inp["q_pos"], pad=inp["pad"], rows=rows)
+    else:
+        oracle.sparse_attend(inp["q"], inp["KV"], None, idx, inp["scale_attn"], 1,
+                             q_pos=inp["q_pos"], pad=inp["pad"], rows=rows,
+                             k_row_stride=inp["kd"], vd=inp["vd"])
+    dt = time.perf_counter() - t0
+    return {"value": len(rows) / dt, "unit": "tokens/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"{len(rows)} of {B * Tq} query rows of the same workload, full step "
+                      f"(index scores over all keys, top-k, attention), {dt:.2f} s"}
+
+
+def main():
+    args = _parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(see DESIGN.md for how it would shard)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from sparse_attention_scores_amd import binding as dsa
+    from sparse_attention_scores_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dsa.load()
+    cfg = args.config
+    print(f"[bench] config {cfg}: generating inputs", file=sys.stderr, flush=True)
+    inp = W.make(cfg, device="cuda")
+    step = Step(dsa, inp)
+    stages = [getattr(step, s) for s in Step.stages]
+
+    def run_once():
+        for f in stages:
+            f()
+
+    for _ in range(args.warmup):
+        run_once()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup {args.warmup} done; timing {args.steps} steps", file=sys.stderr,
+          flush=True)
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+          for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        e = ev[s]
+        e[0].record()
+        for j, f in enumerate(stages):
+            f()
+            e[j + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stage_ms = {}
+    for j, name in enumerate(Step.stages):
+        stage_ms[name] = sum(ev[s][j].elapsed_time(ev[s][j + 1]) for s in range(K)) / K
+    tokens = inp["B"] * inp["Tq"]
+    ms_per_step = wall * 1e3 / K
+    work = algorithmic_work(inp)
+    per_stage = {}
+    for name in Step.stages:
+        by, fl = work[name]
+        t = stage_ms[name] * 1e-3
+        per_stage[name] = {"ms": round(stage_ms[name], 5),
+                           "alg_GBps": round(by / t / 1e9, 1),
+                           "alg_TFLOPs": round(fl / t / 1e12, 2)}
+    dom = max(Step.stages, key=lambda n: stage_ms[n])
+    by, fl = work[dom]
+    t = stage_ms[dom] * 1e-3
+    hbm_bound = cfg in (1, 2, 4) or dom == "topk"
+    if hbm_bound:
+        ach = by / t / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+    else:
+        ach = fl / t / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFS,
+                "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFS, 4), "traffic": None}
+    roof["kernel"] = dom
+    roof["alg_bytes_per_launch"] = by
+    roof["alg_flops_per_launch"] = fl
+    result = {
+        "metric": METRIC,
+        "value": round(tokens * K / wall, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if inp["dtype"] == "f32" else "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_TEXT[cfg], "config_id": cfg,
+                   "query_tokens_per_step": tokens, "seed": inp["seed"]},
+        "roofline": roof,
+        "stages": per_stage,
+    }
+    if not args.no_cpu:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_rows)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

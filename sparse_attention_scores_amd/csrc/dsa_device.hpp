@@ -1,0 +1,130 @@
+// dsa_device.hpp -- device-side helpers shared by the libdsa kernels (gfx950).
+//
+// MFMA operand layouts used throughout (CDNA3/CDNA4 wave64 conventions):
+//  v_mfma_f32_32x32x16_bf16: lane l supplies A[l%32][g*8 .. g*8+7] and
+//    B[g*8 .. g*8+7][l%32] with g = l/32; it receives
+//    C[8*(i/4) + 4*g + i%4][l%32] in accumulator i (i < 16).
+//  v_mfma_f32_16x16x32_bf16: lane l supplies A[l%16][g*8 .. g*8+7] and
+//    B[g*8 .. g*8+7][l%16] with g = l/16; it receives C[4*g + i][l%16] in
+//    accumulator i (i < 4).
+// The contraction index k = g*8 + j is only a label: any bijection between
+// (g, j) and the physical reduction index gives the same product as long as
+// A and B use the same one.  The kernels use that freedom to make each
+// lane's loads contiguous.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16)
+{
+    return __uint_as_float(b16 << 16);
+}
+
+// Round-to-nearest-even float -> bf16 bits (hardware v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
+{
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// Two floats -> packed bf16x2 (low half = a).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
+{
+    return f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
+}
+
+__device__ __forceinline__ f32x4_t mfma_16x16x32(const u32x4_t &a, const u32x4_t &b, f32x4_t c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16_t mfma_32x32x16(const u32x4_t &a, const u32x4_t &b, f32x16_t c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// Four OCP e4m3 codes (one dword) -> four bf16 (two dwords).  Every e4m3
+// value is exactly representable in bf16 (4 significant bits, exponent range
+// inside bf16's), so truncating the exact f32 to its upper half is exact.
+__device__ __forceinline__ u32x2_t e4m3x4_to_bf16x4(uint32_t codes)
+{
+    f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)codes, false);
+    f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)codes, true);
+    u32x2_t r;
+    r[0] = (__float_as_uint(lo[0]) >> 16) | (__float_as_uint(lo[1]) & 0xffff0000u);
+    r[1] = (__float_as_uint(hi[0]) >> 16) | (__float_as_uint(hi[1]) & 0xffff0000u);
+    return r;
+}
+
+// Order-preserving map of an f32 score to u32: larger score <=> larger key.
+// -0 is first folded onto +0 so that the two compare equal.
+__device__ __forceinline__ uint32_t score_order_key(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if (u == 0x80000000u)
+        u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Wave-wide reductions (wave64) via cross-lane shuffles.
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        v = min(v, (uint32_t)__shfl_xor((int)v, o, kWave));
+    return v;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        v = max(v, (uint32_t)__shfl_xor((int)v, o, kWave));
+    return v;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_inclusive_scan(int v)
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        int t = __shfl_up(v, o, kWave);
+        if (lane >= o)
+            v += t;
+    }
+    return v;
+}
+
+} // namespace dsa

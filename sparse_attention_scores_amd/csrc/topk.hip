@@ -1,0 +1,168 @@
+// topk.hip -- per-row top-k on gfx950, exact.
+//
+// Rank order: higher score first, then smaller column index ("Module
+// glm5next_dsa_ref", topk_pools); at most min(k, n_visible) entries, the
+// rest INVALID (ik_llama.cpp PR #2063, batch-local indexer commit:
+// top_k(min(top_k, n_tokens))).
+//
+// Each candidate becomes one 64-bit composite key
+//     (order_key(score) << 32) | (0xffffffff - column)
+// whose unsigned order is exactly the rank order (larger key = better rank),
+// with -0 folded onto +0.  All keys of a row are distinct, so "the k
+// largest keys" is one well-defined set and the selection is exact.
+//
+// One block owns a row (or a chunk of a long row):
+//  1. the row's order keys are cached in LDS (coalesced loads);
+//  2. a block-wide min/max finds the bits all keys share;
+//  3. radix select, 8 bits per pass starting below the shared bits, with an
+//     LDS histogram, finds the threshold T with exactly k keys >= T;
+//  4. the k winners are compacted to LDS and bitonic-sorted (descending).
+// Rows longer than one block's cache run in two launches: each chunk keeps
+// its own k largest keys (the global top-k is a subset of the union of the
+// chunk top-ks because the order is total), then one block per row selects
+// and sorts among those candidates.
+#include "dsa_internal.hpp"
+#include "topk_device.hpp"
+
+namespace dsa {
+
+// Mode 0: whole row in one block, writes the sorted index row.
+// Mode 1: chunk c of the row, writes its (unsorted) winners as composite
+//         keys to ws[row][c][0..k), zero-padded.
+template <int NT, int CAP, int MODE>
+__global__ __launch_bounds__(NT) void topk_rows_kernel(const float *__restrict__ scores,
+                                                       int n_cols, int64_t row_stride,
+                                                       const int32_t *__restrict__ vlo,
+                                                       const int32_t *__restrict__ vhi, int k,
+                                                       int32_t *__restrict__ out,
+                                                       uint64_t *__restrict__ ws, int n_chunks)
+{
+    __shared__ TopkSmem<NT, CAP> sm;
+    const int tid = threadIdx.x;
+    int row, chunk = 0;
+    if (MODE == 0) {
+        row = blockIdx.x;
+    } else {
+        row = blockIdx.x / n_chunks;
+        chunk = blockIdx.x % n_chunks;
+    }
+    int lo = max(vlo[row], 0), hi = min(vhi[row], n_cols);
+    if (MODE == 1) {
+        const int c0 = chunk * CAP;
+        lo = max(lo, c0);
+        hi = min(hi, c0 + CAP);
+    }
+    const float *rp = scores + (int64_t)row * row_stride;
+    const int n = load_row(sm, rp, lo, hi);
+    auto key_at = [&](int i) -> uint64_t { return compose_key(sm.ord[i], (uint32_t)(lo + i)); };
+    int m;
+    if (n > k) {
+        radix_select(sm, n, k, key_at);
+        m = k;
+    } else {
+        for (int i = tid; i < n; i += NT)
+            sm.sel[i] = key_at(i);
+        __syncthreads();
+        m = n;
+    }
+    if (MODE == 0) {
+        bitonic_desc(sm, m);
+        int32_t *o = out + (int64_t)row * k;
+        for (int i = tid; i < k; i += NT)
+            o[i] = i < m ? (int32_t)(0xffffffffu - (uint32_t)sm.sel[i]) : -1;
+    } else {
+        uint64_t *o = ws + ((int64_t)row * n_chunks + chunk) * k;
+        for (int i = tid; i < k; i += NT)
+            o[i] = i < m ? sm.sel[i] : 0ull;
+    }
+}
+
+// Second launch of the long-row path: select and sort among the chunk
+// winners ws[row][0 .. n_chunks*k).  Zero keys are padding; there are always
+// at least min(k, n_visible) real keys, and every real key is > 0.
+template <int NT>
+__global__ __launch_bounds__(NT) void topk_merge_kernel(const uint64_t *__restrict__ ws,
+                                                        int n_chunks, int k,
+                                                        int32_t *__restrict__ out)
+{
+    __shared__ TopkSmem<NT, 1> sm;
+    const int tid = threadIdx.x;
+    const int row = blockIdx.x;
+    const uint64_t *cand = ws + (int64_t)row * n_chunks * k;
+    const int n = n_chunks * k;
+    // count the real candidates
+    if (tid == 0)
+        sm.count = 0;
+    __syncthreads();
+    int local = 0;
+    for (int i = tid; i < n; i += NT)
+        local += cand[i] != 0ull;
+    atomicAdd(&sm.count, local);
+    __syncthreads();
+    const int real = sm.count;
+    __syncthreads();
+    auto key_at = [&](int i) -> uint64_t { return cand[i]; };
+    int m;
+    if (real > k) {
+        radix_select(sm, n, k, key_at);
+        m = k;
+    } else {
+        if (tid == 0)
+            sm.count = 0;
+        __syncthreads();
+        for (int i = tid; i < n; i += NT) {
+            const uint64_t key = cand[i];
+            if (key != 0ull) {
+                const int pos = atomicAdd(&sm.count, 1);
+                sm.sel[pos] = key;
+            }
+        }
+        __syncthreads();
+        m = real;
+    }
+    bitonic_desc(sm, m);
+    int32_t *o = out + (int64_t)row * k;
+    for (int i = tid; i < k; i += NT)
+        o[i] = i < m ? (int32_t)(0xffffffffu - (uint32_t)sm.sel[i]) : -1;
+}
+
+constexpr int kCapLarge = 16384;
+constexpr int kCapSmall = 4096;
+
+size_t topk_workspace_bytes(int rows, int n_cols, int k)
+{
+    if (n_cols <= kCapLarge)
+        return 0;
+    const int64_t n_chunks = (n_cols + kCapLarge - 1) / kCapLarge;
+    return (size_t)rows * (size_t)n_chunks * (size_t)k * sizeof(uint64_t);
+}
+
+hipError_t launch_topk(const TopkArgs &a, hipStream_t st)
+{
+    if (a.n_cols <= kCapSmall) {
+        constexpr int NT = 256;
+        hipLaunchKernelGGL((topk_rows_kernel<NT, kCapSmall, 0>), dim3(a.rows), dim3(NT), 0, st,
+                           a.scores, a.n_cols, a.row_stride, a.vis_lo, a.vis_hi, a.k, a.out,
+                           nullptr, 1);
+        return hipGetLastError();
+    }
+    constexpr int NT = 1024;
+    if (a.n_cols <= kCapLarge) {
+        hipLaunchKernelGGL((topk_rows_kernel<NT, kCapLarge, 0>), dim3(a.rows), dim3(NT), 0, st,
+                           a.scores, a.n_cols, a.row_stride, a.vis_lo, a.vis_hi, a.k, a.out,
+                           nullptr, 1);
+        return hipGetLastError();
+    }
+    const int n_chunks = (a.n_cols + kCapLarge - 1) / kCapLarge;
+    hipLaunchKernelGGL((topk_rows_kernel<NT, kCapLarge, 1>), dim3(a.rows * n_chunks), dim3(NT),
+                       0, st, a.scores, a.n_cols, a.row_stride, a.vis_lo, a.vis_hi, a.k,
+                       a.out, static_cast<uint64_t *>(a.workspace), n_chunks);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL((topk_merge_kernel<NT>), dim3(a.rows), dim3(NT), 0, st,
+                       static_cast<const uint64_t *>(a.workspace), n_chunks, a.k, a.out);
+    return hipGetLastError();
+}
+
+} // namespace dsa

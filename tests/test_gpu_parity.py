@@ -1,0 +1,304 @@
+"""GPU parity: every stage of the libdsa path against the CPU oracle.
+
+Stage-wise, as the correctness criteria are stated: scores on identical
+inputs; top-k as the oracle's top-k applied to the GPU's own scores
+(bit-exact); attention fed the oracle's selection.  Sizes span several tiles
+and a ragged tail.  All calls go through the C ABI (binding -> libdsa.so)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_attention_scores_amd import workloads as W
+from tests.parity import FLT_MAX, bf16_ulp_ok, check_attend, check_scores, cpu, note
+
+pytestmark = pytest.mark.gpu
+
+INV = -1
+
+
+@pytest.fixture(scope="module")
+def dsa():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: the gpu tests need an MI355X")
+    from sparse_attention_scores_amd import binding
+    binding.load()
+    return binding
+
+
+def _ranges(dsa, inp, kpool=0):
+    return dsa.visibility_ranges(inp["pad"], inp["q_pos"], kpool)
+
+
+def _rows_qpos_pad(inp):
+    B, Tq = inp["q_pos"].shape
+    qp = cpu(inp["q_pos"]).numpy().reshape(-1)
+    pd = np.repeat(cpu(inp["pad"]).numpy(), Tq)
+    return qp, pd
+
+
+# ---------------------------------------------------------------- visibility
+
+def test_visibility_ranges_match_definition(dsa):
+    note("visibility ranges")
+    pad = torch.tensor([0, 3, 7], dtype=torch.int32, device="cuda")
+    q_pos = torch.arange(12, dtype=torch.int32, device="cuda").repeat(3, 1)
+    lo, hi = dsa.visibility_ranges(pad, q_pos, 0)
+    plo, phi = dsa.visibility_ranges(pad, q_pos, 4)
+    torch.cuda.synchronize()
+    lo, hi, plo, phi = (cpu(x).numpy() for x in (lo, hi, plo, phi))
+    for b, p in enumerate([0, 3, 7]):
+        for t in range(12):
+            vis = [s for s in range(12) if oracle.token_visible(p, t, s)]
+            got = list(range(lo[b, t], hi[b, t]))
+            assert got == vis, (b, t)
+            pools = [i for i in range(3) if oracle.pool_visible(p, 4, t, i)]
+            assert list(range(plo[b, t], phi[b, t])) == pools, (b, t)
+
+
+# ---------------------------------------------------------------- index scores
+
+INDEX_CASES = [
+    # (config, overrides, variant)
+    (1, {}, None),
+    (2, dict(B=2, Tk=1000), None),
+    (2, dict(B=3, Tk=517), "tie"),
+    (3, dict(Tq=300, Tk=300), None),
+    (4, dict(B=2, Tk=4133), None),
+]
+
+
+def _index_case(dsa, cfg, over, variant, seed=None):
+    inp = W.make(cfg, device="cuda", variant=variant, seed=seed, **over)
+    lo, hi = _ranges(dsa, inp)
+    S = dsa.index_scores(inp["q_idx"], inp["k_idx"], inp["w"], lo, hi, inp["scale_idx"],
+                         k_scale=inp["k_scale"])
+    torch.cuda.synchronize()
+    return inp, lo, hi, S
+
+
+@pytest.mark.parametrize("cfg,over,variant", INDEX_CASES)
+def test_index_scores_parity(dsa, cfg, over, variant):
+    note(f"index scores config {cfg} {over} {variant}")
+    inp, lo, hi, S = _index_case(dsa, cfg, over, variant)
+    ref, A = oracle.index_scores(cpu(inp["q_idx"]), cpu(inp["k_idx"]), cpu(inp["w"]),
+                                 inp["scale_idx"], cpu(inp["q_pos"]), cpu(inp["pad"]),
+                                 k_scale=None if inp["k_scale"] is None else cpu(inp["k_scale"]),
+                                 want_mag=True)
+    rtol = 1e-5 if inp["dtype"] == "f32" else 1e-3
+    check_scores(cpu(S).numpy().reshape(ref.shape), ref, A, rtol, f"config {cfg}")
+
+
+def test_index_scores_padding_and_pooled_ranges(dsa):
+    note("index scores: left padding + pooled visibility")
+    B, L, H, d, kp = 3, 70, 32, 128, 4
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    q = (torch.randn(B, L, H, d, generator=gen, device="cuda") / d ** 0.5).bfloat16()
+    k = (torch.randn(B, L // kp, d, generator=gen, device="cuda") / d ** 0.5).bfloat16()
+    w = torch.rand(B, L, H, generator=gen, device="cuda")
+    pad = torch.tensor([0, 5, 66], dtype=torch.int32, device="cuda")
+    q_pos = torch.arange(L, dtype=torch.int32, device="cuda").repeat(B, 1)
+    lo, hi = dsa.visibility_ranges(pad, q_pos, kp)
+    S = dsa.index_scores(q, k, w, lo, hi, 0.088)
+    torch.cuda.synchronize()
+    ref, A = oracle.index_scores(cpu(q), cpu(k), cpu(w), 0.088, cpu(q_pos), cpu(pad), kpool=kp,
+                                 want_mag=True)
+    check_scores(cpu(S).numpy().reshape(ref.shape), ref, A, 1e-3, "pooled ranges")
+
+
+# ---------------------------------------------------------------- top-k
+
+TOPK_CASES = [
+    (1, {}, None, 8),
+    (2, dict(B=4, Tk=8192), None, 2048),     # bench row length, one block per row
+    (2, dict(B=3, Tk=517), "tie", 64),       # massive exact ties
+    (2, dict(B=2, Tk=3000), None, 2048),     # k > visible for none, small-block path
+    (3, dict(Tq=300, Tk=300), None, 100),    # causal: k >= visible on early rows
+    (4, dict(B=2, Tk=40000), None, 2048),    # > one block's cache: two-launch path
+    (4, dict(B=1, Tk=40000), "tie", 2048),   # two-launch path with ties
+]
+
+
+@pytest.mark.parametrize("cfg,over,variant,k", TOPK_CASES)
+def test_topk_bit_exact_on_gpu_scores(dsa, cfg, over, variant, k):
+    note(f"topk config {cfg} {over} {variant} k={k}")
+    inp, lo, hi, S = _index_case(dsa, cfg, over, variant)
+    idx = dsa.topk(S, lo, hi, k)
+    torch.cuda.synchronize()
+    Sc = cpu(S).numpy().reshape(-1, S.shape[-1])
+    qp, pd = _rows_qpos_pad(inp)
+    ref = oracle.topk(Sc, qp, pd, k)
+    got = cpu(idx).numpy().reshape(ref.shape)
+    bad = np.nonzero((got != ref).any(1))[0]
+    assert bad.size == 0, f"rows differ: {bad[:10]} first: {got[bad[0]][:16]} vs {ref[bad[0]][:16]}"
+
+
+def test_topk_edge_rows(dsa):
+    note("topk edge rows")
+    n = 777
+    rows = []
+    rows.append(np.full(n, 0.5, np.float32))                             # all equal
+    rows.append(np.where(np.arange(n) % 2 == 0, 0.0, -0.0).astype(np.float32))  # +-0
+    r = np.random.default_rng(3).standard_normal(n).astype(np.float32)
+    rows.append(r)                                                       # empty range
+    rows.append(r)                                                       # 1 visible key
+    rows.append(-np.abs(r))                                              # negatives
+    rows.append(np.array([np.inf, -np.inf] * (n // 2) + [1.0], np.float32))
+    S = torch.tensor(np.stack(rows), device="cuda")
+    lo = torch.tensor([0, 3, 5, 10, 0, 0], dtype=torch.int32, device="cuda")
+    hi = torch.tensor([n, n, 5, 11, 600, n], dtype=torch.int32, device="cuda")
+    for k in (1, 5, 300, 2048):
+        idx = dsa.topk(S, lo, hi, k)
+        torch.cuda.synchronize()
+        got = cpu(idx).numpy()
+        for i in range(len(rows)):
+            l0, h0 = int(lo[i]), int(hi[i])
+            cand = sorted(range(l0, h0), key=lambda s: (-float(rows[i][s]), s))[:k]
+            exp = cand + [INV] * (k - len(cand))
+            assert got[i].tolist() == exp, (i, k)
+
+
+# ---------------------------------------------------------------- attention
+
+def _oracle_sel(inp, S, k):
+    Sc = cpu(S).numpy().reshape(-1, S.shape[-1])
+    qp, pd = _rows_qpos_pad(inp)
+    return oracle.topk(Sc, qp, pd, k).reshape(S.shape[0], S.shape[1], k)
+
+
+ABSORBED_CASES = [
+    (2, dict(B=3, Tk=1500), None, 512),
+    (2, dict(B=2, Tk=2111), "sharp", 2048),
+    (3, dict(Tq=200, Tk=200), None, 64),
+    (4, dict(B=2, Tk=5000), None, 2048),
+]
+
+
+@pytest.mark.parametrize("cfg,over,variant,k", ABSORBED_CASES)
+def test_absorbed_attend_parity(dsa, cfg, over, variant, k):
+    note(f"absorbed attend config {cfg} {over} {variant} k={k}")
+    inp, lo, hi, S = _index_case(dsa, cfg, over, variant)
+    sel = _oracle_sel(inp, S, k)
+    idx = torch.tensor(sel, device="cuda")
+    kd, vd = inp["kd"], inp["vd"]
+    out, lse = dsa.sparse_attend(inp["q"], inp["KV"], None, idx, inp["scale_attn"], kv_heads=1,
+                                 vd=vd, vis_lo=lo, vis_hi=hi)
+    torch.cuda.synchronize()
+    ref, lref = oracle.sparse_attend(cpu(inp["q"]), cpu(inp["KV"]), None, sel, inp["scale_attn"],
+                                     kv_heads=1, q_pos=cpu(inp["q_pos"]), pad=cpu(inp["pad"]),
+                                     k_row_stride=kd, vd=vd)
+    check_attend(cpu(out).numpy().reshape(ref.shape), ref, cpu(lse).numpy().reshape(lref.shape),
+                 lref, bf16=True, what=f"config {cfg}")
+
+
+def test_absorbed_attend_set_semantics(dsa):
+    """Duplicates, INVALID, out-of-range and invisible entries, empty rows."""
+    note("absorbed attend: set semantics")
+    inp = W.make(2, device="cuda", B=4, Tk=700)
+    B, Tk = 4, 700
+    rng = np.random.default_rng(5)
+    sel = rng.integers(-3, Tk + 40, (B, 1, 300)).astype(np.int32)
+    sel[0, 0, :] = INV                        # empty
+    sel[1, 0, 150:] = sel[1, 0, :150]         # every entry twice
+    sel[2, 0, :] = 17                         # one key, many times
+    idx = torch.tensor(sel, device="cuda")
+    lo = torch.full((B, 1), 5, dtype=torch.int32, device="cuda")
+    hi = torch.full((B, 1), 650, dtype=torch.int32, device="cuda")
+    out, lse = dsa.sparse_attend(inp["q"], inp["KV"], None, idx, inp["scale_attn"], 1, vd=512,
+                                 vis_lo=lo, vis_hi=hi)
+    torch.cuda.synchronize()
+    ref, lref = oracle.sparse_attend(cpu(inp["q"]), cpu(inp["KV"]), None, sel,
+                                     inp["scale_attn"], 1, q_pos=np.full((B, 1), 649),
+                                     pad=np.full(B, 5), k_row_stride=576, vd=512)
+    check_attend(cpu(out).numpy().reshape(ref.shape), ref, cpu(lse).numpy().reshape(lref.shape),
+                 lref, bf16=True, what="set semantics")
+    assert torch.all(out[0] == 0) and torch.all(torch.isneginf(lse[0]))
+
+
+def test_attend_plain_f32_per_head_and_shared(dsa):
+    note("plain attend f32 (config 1)")
+    inp = W.make(1, device="cuda")
+    lo, hi = _ranges(dsa, inp)
+    S = dsa.index_scores(inp["q_idx"], inp["k_idx"], inp["w"], lo, hi, inp["scale_idx"])
+    torch.cuda.synchronize()
+    sel = _oracle_sel(inp, S, 8)
+    idx = torch.tensor(sel, device="cuda")
+    for K, V, kvh in ((inp["K"], inp["V"], 4), (inp["K1"], inp["V1"], 1)):
+        out, lse = dsa.sparse_attend(inp["q"], K, V, idx, inp["scale_attn"], kvh, vis_lo=lo,
+                                     vis_hi=hi)
+        torch.cuda.synchronize()
+        ref, lref = oracle.sparse_attend(cpu(inp["q"]), cpu(K), cpu(V), sel, inp["scale_attn"],
+                                         kvh, q_pos=cpu(inp["q_pos"]), pad=cpu(inp["pad"]))
+        check_attend(cpu(out).numpy().reshape(ref.shape), ref,
+                     cpu(lse).numpy().reshape(lref.shape), lref, bf16=False,
+                     what=f"config 1 kv_heads {kvh}")
+
+
+def test_attend_plain_bf16_per_head_small(dsa):
+    note("plain attend bf16 per-head (small pooled shape)")
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    B, T, H, kd, vd = 2, 50, 4, 192, 256
+    q = (torch.randn(B, T, H, kd, generator=gen, device="cuda") / kd ** 0.5).bfloat16()
+    K = (torch.randn(B, T, H, kd, generator=gen, device="cuda") / kd ** 0.5).bfloat16()
+    V = (torch.randn(B, T, H, vd, generator=gen, device="cuda") / vd ** 0.5).bfloat16()
+    sel = np.random.default_rng(2).integers(-1, T, (B, T, 20)).astype(np.int32)
+    idx = torch.tensor(sel, device="cuda")
+    out, lse = dsa.sparse_attend(q, K, V, idx, kd ** -0.5, H)
+    torch.cuda.synchronize()
+    ref, lref = oracle.sparse_attend(cpu(q), cpu(K), cpu(V), sel, kd ** -0.5, H)
+    check_attend(cpu(out).numpy().reshape(ref.shape), ref, cpu(lse).numpy().reshape(lref.shape),
+                 lref, bf16=True, what="plain bf16")
+
+
+# ---------------------------------------------------------------- pooled path
+
+def test_pool_keys_within_one_ulp(dsa):
+    note("pool keys (config 5 shape, reduced length)")
+    inp = W.make(5, device="cuda", L=1030)
+    pk, npools = dsa.pool_keys(inp["k_idx"], inp["gate"], inp["pad"], 4)
+    torch.cuda.synchronize()
+    ref, rn = oracle.pool_keys(cpu(inp["k_idx"]), cpu(inp["gate"]), cpu(inp["pad"]), 4)
+    assert cpu(npools).tolist() == rn.tolist()
+    bf16_ulp_ok(cpu(pk), ref, "pool keys")
+    for b, n in enumerate(rn):
+        assert torch.all(pk[b, n:] == 0)
+
+
+@pytest.mark.parametrize("variant", [None, "tie"])
+def test_pool_select_bit_exact(dsa, variant):
+    note(f"pool select (config 5 shape, reduced) {variant}")
+    L, kp, sk, width = 1030, 4, 64, 64 * 4 + 4
+    inp = W.make(5, device="cuda", L=L, variant=variant)
+    pk, _ = dsa.pool_keys(inp["k_idx"], inp["gate"], inp["pad"], kp)
+    lo, hi = dsa.visibility_ranges(inp["pad"], inp["q_pos"], kp)
+    S = dsa.index_scores(inp["q_idx"], pk, inp["w"], lo, hi, inp["scale_idx"])
+    tok, pools = dsa.pool_select(S, inp["pad"], inp["q_pos"], kp, sk, width, want_pools=True)
+    torch.cuda.synchronize()
+    Sc = cpu(S).numpy().reshape(-1, S.shape[-1])
+    qp, pd = _rows_qpos_pad(inp)
+    rtok, rpools = oracle.pool_select(Sc, qp, pd, kp, sk, width, want_pools=True)
+    assert np.array_equal(cpu(tok).numpy().reshape(rtok.shape), rtok)
+    assert np.array_equal(cpu(pools).numpy().reshape(rpools.shape), rpools)
+
+
+# ---------------------------------------------------------------- ABI contract
+
+def test_abi_rejects_bad_arguments(dsa):
+    note("ABI argument errors")
+    S = torch.zeros(2, 10, device="cuda")
+    lo = torch.zeros(2, dtype=torch.int32, device="cuda")
+    hi = torch.full((2,), 10, dtype=torch.int32, device="cuda")
+    with pytest.raises(dsa.DsaError) as e:
+        dsa.topk(S, lo, hi, 4096)
+    assert e.value.code == -2
+    with pytest.raises(dsa.DsaError) as e:
+        dsa.topk(S, lo, hi, 0)
+    assert e.value.code == -1
+    q = torch.zeros(1, 1, 48, 128, dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros(1, 8, 128, dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros(1, 1, 48, device="cuda")
+    l1 = torch.zeros(1, 1, dtype=torch.int32, device="cuda")
+    with pytest.raises(dsa.DsaError) as e:
+        dsa.index_scores(q, k, w, l1, l1, 1.0)
+    assert e.value.code == -2
+    assert "n_heads" in str(e.value)
