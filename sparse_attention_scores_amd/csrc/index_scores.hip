@@ -86,38 +86,25 @@ __global__ __launch_bounds__(256) void index_scores_mfma_kernel(
     const int c1 = min(c0 + chunk, n_k);
     const int ntiles = (c1 - c0 + 31) / 32;
 
-    for (int tile = wk; tile < ntiles; tile += WK) {
-        const int s0 = c0 + tile * 32;
-        const int key = s0 + col;
-        bool active = false;
+    // A tile is "active" if any of the wave's queries sees a key in it.
+    auto tile_active = [&](int s0) {
+        bool act = false;
 #pragma unroll
         for (int qi = 0; qi < QPW; ++qi)
-            active |= (lo[qi] < s0 + 32) && (hi[qi] > s0) && (lo[qi] < hi[qi]);
-        if (!active) {
-            if (lane < 32 && key < c1) {
-#pragma unroll
-                for (int qi = 0; qi < QPW; ++qi)
-                    if (qok[qi])
-                        scores[qrow[qi] * n_k + key] = -FLT_MAX;
-            }
-            continue;
-        }
-        const int kl = min(key, n_k - 1);
-        u32x4_t kf[KS];
-        float gsc = scale;
+            act |= (lo[qi] < s0 + 32) && (hi[qi] > s0) && (lo[qi] < hi[qi]);
+        return act;
+    };
+    // B-operand fragments of the tile's keys (lane = key s0 + col), and the
+    // per-key factor scale * k_scale.
+    auto load_tile = [&](int s0, u32x4_t (&kf)[KS], float &gsc) {
+        const int kl = min(s0 + col, n_k - 1);
+        gsc = scale;
         if constexpr (FP8) {
             const uint8_t *kp = reinterpret_cast<const uint8_t *>(kv) +
                                 ((int64_t)b * n_k + kl) * D + g * (D / 2);
 #pragma unroll
-            for (int p = 0; p < KS / 2; ++p) {
-                u32x4_t c = *reinterpret_cast<const u32x4_t *>(kp + p * 16);
-                u32x2_t a0 = e4m3x4_to_bf16x4(c[0]);
-                u32x2_t a1 = e4m3x4_to_bf16x4(c[1]);
-                u32x2_t a2 = e4m3x4_to_bf16x4(c[2]);
-                u32x2_t a3 = e4m3x4_to_bf16x4(c[3]);
-                kf[2 * p] = u32x4_t{a0[0], a0[1], a1[0], a1[1]};
-                kf[2 * p + 1] = u32x4_t{a2[0], a2[1], a3[0], a3[1]};
-            }
+            for (int p = 0; p < KS / 2; ++p)
+                kf[2 * p] = *reinterpret_cast<const u32x4_t *>(kp + p * 16);
             gsc = scale * kscale[(int64_t)b * n_k + kl];
         } else {
             const uint16_t *kp = reinterpret_cast<const uint16_t *>(kv) +
@@ -125,6 +112,31 @@ __global__ __launch_bounds__(256) void index_scores_mfma_kernel(
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
                 kf[ks] = *reinterpret_cast<const u32x4_t *>(kp + ks * 16);
+        }
+    };
+    auto compute_tile = [&](int s0, bool act, u32x4_t (&kf)[KS], float gsc) {
+        const int key = s0 + col;
+        if (!act) {
+            if (lane < 32 && key < c1) {
+#pragma unroll
+                for (int qi = 0; qi < QPW; ++qi)
+                    if (qok[qi])
+                        scores[qrow[qi] * n_k + key] = -FLT_MAX;
+            }
+            return;
+        }
+        if constexpr (FP8) {
+            // 16 raw e4m3 codes per 16-byte load -> two k-steps of 8 bf16
+#pragma unroll
+            for (int p = KS / 2 - 1; p >= 0; --p) {
+                const u32x4_t c = kf[2 * p];
+                const u32x2_t a0 = e4m3x4_to_bf16x4(c[0]);
+                const u32x2_t a1 = e4m3x4_to_bf16x4(c[1]);
+                const u32x2_t a2 = e4m3x4_to_bf16x4(c[2]);
+                const u32x2_t a3 = e4m3x4_to_bf16x4(c[3]);
+                kf[2 * p] = u32x4_t{a0[0], a0[1], a1[0], a1[1]};
+                kf[2 * p + 1] = u32x4_t{a2[0], a2[1], a3[0], a3[1]};
+            }
         }
 #pragma unroll
         for (int qi = 0; qi < QPW; ++qi) {
@@ -143,6 +155,34 @@ __global__ __launch_bounds__(256) void index_scores_mfma_kernel(
             if (lane < 32 && key < c1 && qok[qi])
                 scores[qrow[qi] * n_k + key] = (key >= lo[qi] && key < hi[qi]) ? part : -FLT_MAX;
         }
+    };
+
+    // Two tiles in flight per wave: the next tile's loads are issued before
+    // the current tile's MFMA work.
+    u32x4_t kfa[KS], kfb[KS];
+    float ga = scale, gb = scale;
+    int tile = wk;
+    bool act_a = false;
+    if (tile < ntiles) {
+        act_a = tile_active(c0 + tile * 32);
+        if (act_a)
+            load_tile(c0 + tile * 32, kfa, ga);
+    }
+    while (tile < ntiles) {
+        const int nxt = tile + WK;
+        bool act_b = false;
+        if (nxt < ntiles) {
+            act_b = tile_active(c0 + nxt * 32);
+            if (act_b)
+                load_tile(c0 + nxt * 32, kfb, gb);
+        }
+        compute_tile(c0 + tile * 32, act_a, kfa, ga);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            kfa[ks] = kfb[ks];
+        ga = gb;
+        act_a = act_b;
+        tile = nxt;
     }
 }
 

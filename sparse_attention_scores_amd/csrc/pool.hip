@@ -138,7 +138,7 @@ hipError_t launch_pool_keys(const PoolKeysArgs &a, hipStream_t st)
 }
 
 // ------------------------------------------------------------------ pool select
-template <int NT, int CAP>
+template <int NT, int CAP, int EPT>
 __global__ __launch_bounds__(NT) void pool_select_kernel(
     const float *__restrict__ scores, const int32_t *__restrict__ pad,
     const int32_t *__restrict__ q_pos, int32_t *__restrict__ out_tok,
@@ -164,7 +164,14 @@ __global__ __launch_bounds__(NT) void pool_select_kernel(
         __syncthreads();
         m = n;
     }
-    bitonic_desc(sm, m);
+    {
+        uint64_t v[EPT];
+        bitonic_sort_regs<NT, EPT>(sm, m, v);
+#pragma unroll
+        for (int b = 0; b < EPT; ++b)
+            sm.sel[tid * EPT + b] = v[b];
+        __syncthreads();
+    }
     // expand_selection: pools' tokens (rank order), the visible tail, INVALID
     const int pool_toks = m * kpool;
     const int tail = t >= p ? (t + 1) - (p + n_full * kpool) : 0;
@@ -190,14 +197,19 @@ hipError_t launch_pool_select(const PoolSelectArgs &a, hipStream_t st)
 {
     const int np_cols = a.seq / a.kpool;
     const unsigned rows = (unsigned)(a.batch * a.n_q);
-    if (np_cols <= 4096)
-        hipLaunchKernelGGL((pool_select_kernel<256, 4096>), dim3(rows), dim3(256), 0, st,
-                           a.scores, a.pad, a.q_pos, a.out_tok, a.out_pools, a.n_q, np_cols,
-                           a.kpool, a.select_k, a.out_width);
-    else
-        hipLaunchKernelGGL((pool_select_kernel<1024, 16384>), dim3(rows), dim3(1024), 0, st,
-                           a.scores, a.pad, a.q_pos, a.out_tok, a.out_pools, a.n_q, np_cols,
-                           a.kpool, a.select_k, a.out_width);
+#define DSA_POOL_SELECT(NT, CAP, EPT)                                                              \
+    hipLaunchKernelGGL((pool_select_kernel<NT, CAP, EPT>), dim3(rows), dim3(NT), 0, st, a.scores,  \
+                       a.pad, a.q_pos, a.out_tok, a.out_pools, a.n_q, np_cols, a.kpool,            \
+                       a.select_k, a.out_width)
+    if (np_cols <= 4096) {
+        if (a.select_k <= 512)
+            DSA_POOL_SELECT(256, 4096, 2);
+        else
+            DSA_POOL_SELECT(256, 4096, 8);
+    } else {
+        DSA_POOL_SELECT(1024, 16384, 2);
+    }
+#undef DSA_POOL_SELECT
     return hipGetLastError();
 }
 

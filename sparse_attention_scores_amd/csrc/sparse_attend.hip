@@ -103,26 +103,38 @@ constexpr int AB_H = 64;
 constexpr int AB_KD = 576;
 constexpr int AB_VD = 512;
 constexpr int AB_TILE = 32;
-constexpr int AB_KS = AB_KD / 32;  // 18 k-steps of the 16x16x32 MFMA
-constexpr int AB_NC = AB_VD / 16;  // 32 output column tiles per wave
-constexpr int AB_KPITCH = AB_KD + 8;     // LDS K-tile row pitch (bf16): 1168 B
-constexpr int AB_VPITCH = AB_TILE + 4;   // LDS V^T-tile row pitch (bf16): 72 B
-constexpr int AB_LIST = 1024;            // keys per block
+constexpr int AB_KS = AB_KD / 32;        // 18 k-steps of the 16x16x32 MFMA
+constexpr int AB_NC = AB_VD / 16;        // 32 output column tiles per wave
+constexpr int AB_KPITCH = AB_KD + 8;     // K tile row pitch (bf16): 1168 B
+constexpr int AB_VPITCH = 20;            // V^T row pitch (dwords): 16 + 4 pad
+constexpr int AB_LIST = 1024;            // keys per batch of a block
 constexpr int AB_NT = 256;
+constexpr int AB_CHUNKS = AB_KD / 8;     // 16-byte chunks per latent row
+constexpr int AB_LD = 5;                 // chunk slots per thread (16 pairs x 72 chunks / 256)
 
-struct AbsTiles {
+// One stage of the double buffer.  K: row-major latent rows (bf16).  VT: the
+// first AB_VD columns transposed; dword r of row c holds key r (low half) and
+// key r+16 (high half), so a lane's PV operand (keys 4g..4g+3 and
+// 16+4g..16+4g+3) is one 16-byte read.
+struct __attribute__((aligned(16))) AbsBuf {
     uint16_t k[AB_TILE * AB_KPITCH];
-    uint16_t vt[AB_VD * AB_VPITCH];
+    uint32_t vt[AB_VD * AB_VPITCH];
 };
 
-struct AbsSmem {
+struct __attribute__((aligned(16))) AbsSmem {
     union {
-        AbsTiles t;
+        AbsBuf buf[2];
         uint32_t bitmap[kBitmapMaxWords];
     } u;
     int32_t list[AB_LIST];
     int wave_tot[AB_NT / 64];
 };
+
+__device__ __forceinline__ uint32_t pick_half(const u32x4_t &v, int e)
+{
+    const uint32_t w = v[e >> 1];
+    return (e & 1) ? (w >> 16) : (w & 0xffffu);
+}
 
 __global__ __launch_bounds__(AB_NT) void attend_gather_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kv, int64_t row_stride,
@@ -148,7 +160,7 @@ __global__ __launch_bounds__(AB_NT) void attend_gather_kernel(
     const int wpt = (nw + AB_NT - 1) / AB_NT;
     const int w0 = min(tid * wpt, nw), w1 = min(w0 + wpt, nw);
 
-    // ---- Q^T fragments: lane holds head wid*16+col, dims ks*32 + g*8 .. +8
+    // Q^T fragments (B operand): lane holds head wid*16+col, dims ks*32+g*8..+8
     const int head = wid * 16 + col;
     u32x4_t qf[AB_KS];
     {
@@ -164,10 +176,46 @@ __global__ __launch_bounds__(AB_NT) void attend_gather_kernel(
     float m_run = -INFINITY, l_part = 0.f;
 
     const uint16_t *kvb = kv + b * (int64_t)n_k * row_stride;
+    // gather roles: pair pr = rows (pr, pr+16); chunks c8 = tid/16 + 16*j
+    const int pr = tid & 15;
+    const int cbase = tid >> 4;
+    u32x4_t R[AB_LD][2];
+
+    auto load_tile = [&](int t0, int nvalid) {
+        const int k0 = sm.list[t0 + min(pr, nvalid - 1)];
+        const int k1 = sm.list[t0 + min(pr + 16, nvalid - 1)];
+        const uint16_t *p0 = kvb + (int64_t)k0 * row_stride;
+        const uint16_t *p1 = kvb + (int64_t)k1 * row_stride;
+#pragma unroll
+        for (int j = 0; j < AB_LD; ++j) {
+            const int c8 = cbase + 16 * j;
+            if (c8 < AB_CHUNKS) {
+                R[j][0] = *reinterpret_cast<const u32x4_t *>(p0 + c8 * 8);
+                R[j][1] = *reinterpret_cast<const u32x4_t *>(p1 + c8 * 8);
+            }
+        }
+    };
+    auto store_tile = [&](AbsBuf &B) {
+#pragma unroll
+        for (int j = 0; j < AB_LD; ++j) {
+            const int c8 = cbase + 16 * j;
+            if (c8 < AB_CHUNKS) {
+                *reinterpret_cast<u32x4_t *>(&B.k[pr * AB_KPITCH + c8 * 8]) = R[j][0];
+                *reinterpret_cast<u32x4_t *>(&B.k[(pr + 16) * AB_KPITCH + c8 * 8]) = R[j][1];
+                if (c8 < AB_VD / 8) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        B.vt[(c8 * 8 + e) * AB_VPITCH + pr] =
+                            pick_half(R[j][0], e) | (pick_half(R[j][1], e) << 16);
+                }
+            }
+        }
+    };
+
     // The block's share of the selected set is ranks [r0, r1) in ascending
-    // key order; it is read out in batches of AB_LIST keys.  The bitmap
-    // shares LDS with the tiles, so each batch rebuilds it (one pass over
-    // the row's n_sel indices).
+    // key order, read out in batches of AB_LIST keys.  The bitmap shares LDS
+    // with the tile buffers, so each batch rebuilds it (one pass over the
+    // row's n_sel indices).
     for (int batch = 0;; ++batch) {
         build_bitmap<AB_NT>(sm.u.bitmap, nw, idx + (int64_t)row * n_sel, n_sel, lo, hi);
         int cnt = 0;
@@ -184,96 +232,94 @@ __global__ __launch_bounds__(AB_NT) void attend_gather_kernel(
         extract_keys(sm.u.bitmap, w0, w1, before, rb, re, sm.list);
         __syncthreads();
         const int n_my = re - rb;
-    for (int t0 = 0; t0 < n_my; t0 += AB_TILE) {
-        const int nvalid = min(AB_TILE, n_my - t0);
-        // ---- gather 32 latent rows: 32 rows x 72 chunks of 16 bytes
-#pragma unroll
-        for (int it = 0; it < (AB_TILE * (AB_KD / 8)) / AB_NT; ++it) {
-            const int item = tid + it * AB_NT;
-            const int r = item / (AB_KD / 8);
-            const int c8 = item % (AB_KD / 8);
-            const int key = sm.list[t0 + min(r, nvalid - 1)];
-            const u32x4_t v = *reinterpret_cast<const u32x4_t *>(kvb + (int64_t)key * row_stride +
-                                                                  c8 * 8);
-            *reinterpret_cast<u32x4_t *>(&sm.u.t.k[r * AB_KPITCH + c8 * 8]) = v;
-            if (c8 < AB_VD / 8) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    sm.u.t.vt[(c8 * 8 + 2 * j) * AB_VPITCH + r] = (uint16_t)(v[j] & 0xffffu);
-                    sm.u.t.vt[(c8 * 8 + 2 * j + 1) * AB_VPITCH + r] = (uint16_t)(v[j] >> 16);
-                }
-            }
-        }
-        __syncthreads();
+        const int ntiles = (n_my + AB_TILE - 1) / AB_TILE;
 
-        // ---- S^T[key][head] for keys 0-15 (s0) and 16-31 (s1)
-        f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+        load_tile(0, min(AB_TILE, n_my));
+        store_tile(sm.u.buf[0]);
+        __syncthreads();
+        for (int t = 0; t < ntiles; ++t) {
+            const int t0 = t * AB_TILE;
+            const int nvalid = min(AB_TILE, n_my - t0);
+            if (t + 1 < ntiles)
+                load_tile(t0 + AB_TILE, min(AB_TILE, n_my - t0 - AB_TILE));
+            const AbsBuf &B = sm.u.buf[t & 1];
+
+            // ---- S^T[key][head]: keys 0-15 (s0) and 16-31 (s1), two chains each
+            f32x4_t s0a = {0.f, 0.f, 0.f, 0.f}, s0b = s0a, s1a = s0a, s1b = s0a;
 #pragma unroll
-        for (int ks = 0; ks < AB_KS; ++ks) {
-            const u32x4_t a0 =
-                *reinterpret_cast<const u32x4_t *>(&sm.u.t.k[col * AB_KPITCH + ks * 32 + g * 8]);
-            const u32x4_t a1 = *reinterpret_cast<const u32x4_t *>(
-                &sm.u.t.k[(16 + col) * AB_KPITCH + ks * 32 + g * 8]);
-            s0 = mfma_16x16x32(a0, qf[ks], s0);
-            s1 = mfma_16x16x32(a1, qf[ks], s1);
-        }
-        // ---- online softmax (log2 domain); lane's keys: 4g+i and 16+4g+i
-        float x0[4], x1[4];
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            x0[i] = (4 * g + i < nvalid) ? s0[i] * scale_log2 : -INFINITY;
-            x1[i] = (16 + 4 * g + i < nvalid) ? s1[i] * scale_log2 : -INFINITY;
-            tmax = fmaxf(tmax, fmaxf(x0[i], x1[i]));
-        }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-        const float m_new = fmaxf(m_run, tmax);
-        const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
-        float p0[4], p1[4];
-        float psum = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            p0[i] = (m_new == -INFINITY) ? 0.f : exp2f(x0[i] - m_new);
-            p1[i] = (m_new == -INFINITY) ? 0.f : exp2f(x1[i] - m_new);
-            psum += p0[i] + p1[i];
-        }
-        l_part = l_part * alpha + psum;
-        m_run = m_new;
-        if (__any(alpha != 1.f)) {
-#pragma unroll
-            for (int n = 0; n < AB_NC; ++n)
-                oacc[n] *= alpha;
-        }
-        // ---- P^T fragments (B operand): k-slot g*8+j <-> key 4g+j (j<4),
-        //      16+4g+j-4 (j>=4); two-term bf16 split
-        u32x4_t bhi, blo;
-        {
-            float h0[4], h1[4];
+            for (int ks = 0; ks < AB_KS; ks += 2) {
+                const u32x4_t a0 = *reinterpret_cast<const u32x4_t *>(
+                    &B.k[col * AB_KPITCH + ks * 32 + g * 8]);
+                const u32x4_t a1 = *reinterpret_cast<const u32x4_t *>(
+                    &B.k[(16 + col) * AB_KPITCH + ks * 32 + g * 8]);
+                const u32x4_t a2 = *reinterpret_cast<const u32x4_t *>(
+                    &B.k[col * AB_KPITCH + (ks + 1) * 32 + g * 8]);
+                const u32x4_t a3 = *reinterpret_cast<const u32x4_t *>(
+                    &B.k[(16 + col) * AB_KPITCH + (ks + 1) * 32 + g * 8]);
+                s0a = mfma_16x16x32(a0, qf[ks], s0a);
+                s1a = mfma_16x16x32(a1, qf[ks], s1a);
+                s0b = mfma_16x16x32(a2, qf[ks + 1], s0b);
+                s1b = mfma_16x16x32(a3, qf[ks + 1], s1b);
+            }
+            const f32x4_t s0 = s0a + s0b, s1 = s1a + s1b;
+
+            // ---- online softmax (log2 domain); lane's keys: 4g+i and 16+4g+i
+            float x0[4], x1[4];
+            float tmax = -INFINITY;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                h0[i] = bf16_bits_to_f32(f32_to_bf16_bits(p0[i]));
-                h1[i] = bf16_bits_to_f32(f32_to_bf16_bits(p1[i]));
+                x0[i] = (4 * g + i < nvalid) ? s0[i] * scale_log2 : -INFINITY;
+                x1[i] = (16 + 4 * g + i < nvalid) ? s1[i] * scale_log2 : -INFINITY;
+                tmax = fmaxf(tmax, fmaxf(x0[i], x1[i]));
             }
-            bhi = u32x4_t{pack_bf16x2(h0[0], h0[1]), pack_bf16x2(h0[2], h0[3]),
-                          pack_bf16x2(h1[0], h1[1]), pack_bf16x2(h1[2], h1[3])};
-            blo = u32x4_t{pack_bf16x2(p0[0] - h0[0], p0[1] - h0[1]),
-                          pack_bf16x2(p0[2] - h0[2], p0[3] - h0[3]),
-                          pack_bf16x2(p1[0] - h1[0], p1[1] - h1[1]),
-                          pack_bf16x2(p1[2] - h1[2], p1[3] - h1[3])};
-        }
-        // ---- O^T[c][head] += V^T[c][keys] P^T[keys][head]
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+            const float m_new = fmaxf(m_run, tmax);
+            const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
+            float p0[4], p1[4];
+            float psum = 0.f;
 #pragma unroll
-        for (int n = 0; n < AB_NC; ++n) {
-            const uint16_t *vr = &sm.u.t.vt[(n * 16 + col) * AB_VPITCH];
-            const u32x2_t va = *reinterpret_cast<const u32x2_t *>(vr + 4 * g);
-            const u32x2_t vb = *reinterpret_cast<const u32x2_t *>(vr + 16 + 4 * g);
-            const u32x4_t a = u32x4_t{va[0], va[1], vb[0], vb[1]};
-            oacc[n] = mfma_16x16x32(a, bhi, oacc[n]);
-            oacc[n] = mfma_16x16x32(a, blo, oacc[n]);
+            for (int i = 0; i < 4; ++i) {
+                p0[i] = (m_new == -INFINITY) ? 0.f : exp2f(x0[i] - m_new);
+                p1[i] = (m_new == -INFINITY) ? 0.f : exp2f(x1[i] - m_new);
+                psum += p0[i] + p1[i];
+            }
+            l_part = l_part * alpha + psum;
+            m_run = m_new;
+            if (__any(alpha != 1.f)) {
+#pragma unroll
+                for (int n = 0; n < AB_NC; ++n)
+                    oacc[n] *= alpha;
+            }
+            // ---- P^T fragments (B operand), element j <-> key (j even: 4g+j/2,
+            //      j odd: 16+4g+j/2), as a two-term bf16 split
+            u32x4_t bhi, blo;
+            {
+                float h0[4], h1[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    h0[i] = bf16_bits_to_f32(f32_to_bf16_bits(p0[i]));
+                    h1[i] = bf16_bits_to_f32(f32_to_bf16_bits(p1[i]));
+                }
+                bhi = u32x4_t{pack_bf16x2(h0[0], h1[0]), pack_bf16x2(h0[1], h1[1]),
+                              pack_bf16x2(h0[2], h1[2]), pack_bf16x2(h0[3], h1[3])};
+                blo = u32x4_t{pack_bf16x2(p0[0] - h0[0], p1[0] - h1[0]),
+                              pack_bf16x2(p0[1] - h0[1], p1[1] - h1[1]),
+                              pack_bf16x2(p0[2] - h0[2], p1[2] - h1[2]),
+                              pack_bf16x2(p0[3] - h0[3], p1[3] - h1[3])};
+            }
+            // ---- O^T[c][head] += V^T[c][keys] P^T[keys][head]
+#pragma unroll
+            for (int n = 0; n < AB_NC; ++n) {
+                const u32x4_t a = *reinterpret_cast<const u32x4_t *>(
+                    &B.vt[(n * 16 + col) * AB_VPITCH + 4 * g]);
+                oacc[n] = mfma_16x16x32(a, bhi, oacc[n]);
+                oacc[n] = mfma_16x16x32(a, blo, oacc[n]);
+            }
+            if (t + 1 < ntiles)
+                store_tile(sm.u.buf[(t + 1) & 1]);
+            __syncthreads();
         }
-        __syncthreads();  // tile buffers are rewritten next iteration
-    }
     }
 
     // ---- epilogue: l over the 4 lane groups of the head
@@ -289,20 +335,21 @@ __global__ __launch_bounds__(AB_NT) void attend_gather_kernel(
             lse[(int64_t)row * AB_H + head] =
                 l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
     } else {
-        const int64_t pr = ((int64_t)row * splits + split) * AB_H + head;
-        float *op = ws_o + pr * AB_VD + 4 * g;
+        const int64_t pr_ = ((int64_t)row * splits + split) * AB_H + head;
+        float *op = ws_o + pr_ * AB_VD + 4 * g;
 #pragma unroll
         for (int n = 0; n < AB_NC; ++n)
             *reinterpret_cast<f32x4_t *>(op + n * 16) = oacc[n];
         if (g == 0) {
-            ws_ml[pr * 2] = l_tot > 0.f ? m_run : -INFINITY;
-            ws_ml[pr * 2 + 1] = l_tot;
+            ws_ml[pr_ * 2] = l_tot > 0.f ? m_run : -INFINITY;
+            ws_ml[pr_ * 2 + 1] = l_tot;
         }
     }
 }
 
 // Merge the split partials of each (row, head): O = sum_s 2^(m_s - m) O_s / L.
-__global__ __launch_bounds__(256) void attend_combine_kernel(const float *__restrict__ ws_o,
+// One block per (row, head); each thread owns 4 consecutive columns.
+__global__ __launch_bounds__(128) void attend_combine_kernel(const float *__restrict__ ws_o,
                                                              const float *__restrict__ ws_ml,
                                                              float *__restrict__ out,
                                                              float *__restrict__ lse, int H,
@@ -320,15 +367,15 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(const float *__rest
         L += (m == -INFINITY || ms == -INFINITY) ? 0.f : exp2f(ms - m) * ws_ml[pr * 2 + 1];
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
-    for (int c = threadIdx.x; c < vd; c += blockDim.x) {
-        float acc = 0.f;
+    for (int c = threadIdx.x * 4; c < vd; c += blockDim.x * 4) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
         for (int s = 0; s < splits; ++s) {
             const int64_t pr = ((int64_t)row * splits + s) * H + h;
             const float ms = ws_ml[pr * 2];
             if (ms != -INFINITY)
-                acc += exp2f(ms - m) * ws_o[pr * vd + c];
+                acc += exp2f(ms - m) * *reinterpret_cast<const f32x4_t *>(ws_o + pr * vd + c);
         }
-        out[((int64_t)row * H + h) * vd + c] = acc * inv;
+        *reinterpret_cast<f32x4_t *>(out + ((int64_t)row * H + h) * vd + c) = acc * inv;
     }
     if (lse && threadIdx.x == 0)
         lse[(int64_t)row * H + h] = L > 0.f ? (m + log2f(L)) * kLn2 : -INFINITY;
@@ -440,7 +487,7 @@ bool attend_gather_supported(const AttendArgs &a)
 int attend_gather_splits(const AttendArgs &a)
 {
     const int64_t rows = (int64_t)a.batch * a.n_q;
-    int by_fill = (int)((512 + rows - 1) / rows);
+    int by_fill = (int)((256 + rows - 1) / rows);
     int by_work = max(1, min(a.n_sel, a.n_k) / 64);
     return max(1, min(by_fill, by_work));
 }
@@ -483,7 +530,7 @@ hipError_t launch_attend(const AttendArgs &a, hipStream_t st)
         hipError_t e = hipGetLastError();
         if (e != hipSuccess || splits == 1)
             return e;
-        hipLaunchKernelGGL(attend_combine_kernel, dim3((unsigned)(rows * AB_H)), dim3(256), 0, st,
+        hipLaunchKernelGGL(attend_combine_kernel, dim3((unsigned)(rows * AB_H)), dim3(128), 0, st,
                            ws_o, ws_ml, a.out, a.lse, AB_H, AB_VD, splits);
         return hipGetLastError();
     }

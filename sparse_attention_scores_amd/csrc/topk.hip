@@ -29,7 +29,7 @@ namespace dsa {
 // Mode 0: whole row in one block, writes the sorted index row.
 // Mode 1: chunk c of the row, writes its (unsorted) winners as composite
 //         keys to ws[row][c][0..k), zero-padded.
-template <int NT, int CAP, int MODE>
+template <int NT, int CAP, int MODE, int EPT>
 __global__ __launch_bounds__(NT) void topk_rows_kernel(const float *__restrict__ scores,
                                                        int n_cols, int64_t row_stride,
                                                        const int32_t *__restrict__ vlo,
@@ -66,10 +66,15 @@ __global__ __launch_bounds__(NT) void topk_rows_kernel(const float *__restrict__
         m = n;
     }
     if (MODE == 0) {
-        bitonic_desc(sm, m);
+        uint64_t v[EPT];
+        bitonic_sort_regs<NT, EPT>(sm, m, v);
         int32_t *o = out + (int64_t)row * k;
-        for (int i = tid; i < k; i += NT)
-            o[i] = i < m ? (int32_t)(0xffffffffu - (uint32_t)sm.sel[i]) : -1;
+#pragma unroll
+        for (int b = 0; b < EPT; ++b) {
+            const int i = tid * EPT + b;
+            if (i < k)
+                o[i] = i < m ? (int32_t)(0xffffffffu - (uint32_t)v[b]) : -1;
+        }
     } else {
         uint64_t *o = ws + ((int64_t)row * n_chunks + chunk) * k;
         for (int i = tid; i < k; i += NT)
@@ -80,7 +85,7 @@ __global__ __launch_bounds__(NT) void topk_rows_kernel(const float *__restrict__
 // Second launch of the long-row path: select and sort among the chunk
 // winners ws[row][0 .. n_chunks*k).  Zero keys are padding; there are always
 // at least min(k, n_visible) real keys, and every real key is > 0.
-template <int NT>
+template <int NT, int EPT>
 __global__ __launch_bounds__(NT) void topk_merge_kernel(const uint64_t *__restrict__ ws,
                                                         int n_chunks, int k,
                                                         int32_t *__restrict__ out)
@@ -120,10 +125,15 @@ __global__ __launch_bounds__(NT) void topk_merge_kernel(const uint64_t *__restri
         __syncthreads();
         m = real;
     }
-    bitonic_desc(sm, m);
+    uint64_t v[EPT];
+    bitonic_sort_regs<NT, EPT>(sm, m, v);
     int32_t *o = out + (int64_t)row * k;
-    for (int i = tid; i < k; i += NT)
-        o[i] = i < m ? (int32_t)(0xffffffffu - (uint32_t)sm.sel[i]) : -1;
+#pragma unroll
+    for (int b = 0; b < EPT; ++b) {
+        const int i = tid * EPT + b;
+        if (i < k)
+            o[i] = i < m ? (int32_t)(0xffffffffu - (uint32_t)v[b]) : -1;
+    }
 }
 
 constexpr int kCapLarge = 16384;
@@ -139,28 +149,34 @@ size_t topk_workspace_bytes(int rows, int n_cols, int k)
 
 hipError_t launch_topk(const TopkArgs &a, hipStream_t st)
 {
+    // sort sizes: NT threads x EPT keys >= k
     if (a.n_cols <= kCapSmall) {
         constexpr int NT = 256;
-        hipLaunchKernelGGL((topk_rows_kernel<NT, kCapSmall, 0>), dim3(a.rows), dim3(NT), 0, st,
-                           a.scores, a.n_cols, a.row_stride, a.vis_lo, a.vis_hi, a.k, a.out,
-                           nullptr, 1);
+        if (a.k <= NT * 2)
+            hipLaunchKernelGGL((topk_rows_kernel<NT, kCapSmall, 0, 2>), dim3(a.rows), dim3(NT), 0,
+                               st, a.scores, a.n_cols, a.row_stride, a.vis_lo, a.vis_hi, a.k,
+                               a.out, nullptr, 1);
+        else
+            hipLaunchKernelGGL((topk_rows_kernel<NT, kCapSmall, 0, 8>), dim3(a.rows), dim3(NT), 0,
+                               st, a.scores, a.n_cols, a.row_stride, a.vis_lo, a.vis_hi, a.k,
+                               a.out, nullptr, 1);
         return hipGetLastError();
     }
     constexpr int NT = 1024;
     if (a.n_cols <= kCapLarge) {
-        hipLaunchKernelGGL((topk_rows_kernel<NT, kCapLarge, 0>), dim3(a.rows), dim3(NT), 0, st,
+        hipLaunchKernelGGL((topk_rows_kernel<NT, kCapLarge, 0, 2>), dim3(a.rows), dim3(NT), 0, st,
                            a.scores, a.n_cols, a.row_stride, a.vis_lo, a.vis_hi, a.k, a.out,
                            nullptr, 1);
         return hipGetLastError();
     }
     const int n_chunks = (a.n_cols + kCapLarge - 1) / kCapLarge;
-    hipLaunchKernelGGL((topk_rows_kernel<NT, kCapLarge, 1>), dim3(a.rows * n_chunks), dim3(NT),
-                       0, st, a.scores, a.n_cols, a.row_stride, a.vis_lo, a.vis_hi, a.k,
+    hipLaunchKernelGGL((topk_rows_kernel<NT, kCapLarge, 1, 2>), dim3(a.rows * n_chunks),
+                       dim3(NT), 0, st, a.scores, a.n_cols, a.row_stride, a.vis_lo, a.vis_hi, a.k,
                        a.out, static_cast<uint64_t *>(a.workspace), n_chunks);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL((topk_merge_kernel<NT>), dim3(a.rows), dim3(NT), 0, st,
+    hipLaunchKernelGGL((topk_merge_kernel<NT, 2>), dim3(a.rows), dim3(NT), 0, st,
                        static_cast<const uint64_t *>(a.workspace), n_chunks, a.k, a.out);
     return hipGetLastError();
 }

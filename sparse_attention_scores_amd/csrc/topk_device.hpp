@@ -14,7 +14,7 @@ namespace dsa {
 constexpr int kTopkMaxK = 2048;
 
 template <int NT, int CAP>
-struct TopkSmem {
+struct __attribute__((aligned(16))) TopkSmem {
     uint32_t ord[CAP];          // order keys of the row (source = scores)
     uint64_t sel[kTopkMaxK];    // winners
     uint32_t hist[256];
@@ -120,14 +120,27 @@ __device__ void radix_select(TopkSmem<NT, CAP> &sm, int n, int k, KeyAt key_at)
             break;
         top = shift - 1;
     }
-    // ---- compaction: exactly k keys satisfy (key & mask) >= prefix
+    // ---- compaction: exactly k keys satisfy (key & mask) >= prefix.  One
+    //      LDS atomic per wave (ballot + prefix count) rather than per key.
     if (tid == 0)
         sm.count = 0;
     __syncthreads();
-    for (int i = tid; i < n; i += NT) {
-        const uint64_t key = key_at(i);
-        if ((key & mask) >= prefix) {
-            const int pos = atomicAdd(&sm.count, 1);
+    for (int i0 = 0; i0 < n; i0 += NT) {
+        const int i = i0 + tid;
+        uint64_t key = 0;
+        bool take = false;
+        if (i < n) {
+            key = key_at(i);
+            take = (key & mask) >= prefix;
+        }
+        const uint64_t bal = __ballot(take);
+        const int cnt = __popcll(bal);
+        int base = 0;
+        if (lane == 0 && cnt)
+            base = atomicAdd(&sm.count, cnt);
+        base = __shfl(base, 0, kWave);
+        if (take) {
+            const int pos = base + __popcll(bal & ((1ull << lane) - 1ull));
             if (pos < kTopkMaxK)
                 sm.sel[pos] = key;
         }
@@ -135,35 +148,67 @@ __device__ void radix_select(TopkSmem<NT, CAP> &sm, int n, int k, KeyAt key_at)
     __syncthreads();
 }
 
-// Descending bitonic sort of sm.sel[0..m), padded with zeros (smaller than
-// every real key) to a power of two.
-template <int NT, int CAP>
-__device__ void bitonic_desc(TopkSmem<NT, CAP> &sm, int m)
+// Descending bitonic sort of the P = NT*EPT keys sm.sel[0..m) (zero-padded;
+// zero is below every real key), held in registers: thread t owns positions
+// t*EPT .. t*EPT+EPT-1.  Strides below EPT stay inside a thread, strides up
+// to 64*EPT use cross-lane shuffles within the wave, larger strides go
+// through LDS.  On return v[b] holds the key of rank t*EPT + b.
+template <int NT, int EPT, int CAP>
+__device__ void bitonic_sort_regs(TopkSmem<NT, CAP> &sm, int m, uint64_t (&v)[EPT])
 {
+    constexpr int P = NT * EPT;
+    static_assert(P <= kTopkMaxK, "sort size exceeds the LDS staging array");
     const int tid = threadIdx.x;
-    int P = 1;
-    while (P < m)
-        P <<= 1;
-    if (P < 2)
-        P = 2;
-    for (int i = m + tid; i < P; i += NT)
-        sm.sel[i] = 0ull;
-    __syncthreads();
+#pragma unroll
+    for (int b = 0; b < EPT; ++b) {
+        const int i = tid * EPT + b;
+        v[b] = i < m ? sm.sel[i] : 0ull;
+    }
+#pragma unroll
     for (int size = 2; size <= P; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int t = tid; t < P / 2; t += NT) {
-                const int i = 2 * t - (t & (stride - 1));
-                const int j = i + stride;
-                const uint64_t a = sm.sel[i], b = sm.sel[j];
-                const bool desc = (i & size) == 0;
-                if (desc ? (a < b) : (a > b)) {
-                    sm.sel[i] = b;
-                    sm.sel[j] = a;
+#pragma unroll
+        for (int s = size >> 1; s > 0; s >>= 1) {
+            if (s < EPT) {
+#pragma unroll
+                for (int b = 0; b < EPT; ++b) {
+                    if ((b & s) == 0) {
+                        const int i = tid * EPT + b;
+                        const bool desc = (i & size) == 0;
+                        const uint64_t x = v[b], y = v[b + s];
+                        const bool sw = desc ? (x < y) : (x > y);
+                        v[b] = sw ? y : x;
+                        v[b + s] = sw ? x : y;
+                    }
+                }
+            } else {
+                uint64_t pv[EPT];
+                if (s / EPT < 64) {
+#pragma unroll
+                    for (int b = 0; b < EPT; ++b)
+                        pv[b] = shfl_xor_u64(v[b], s / EPT);
+                } else {
+                    __syncthreads();
+#pragma unroll
+                    for (int b = 0; b < EPT; ++b)
+                        sm.sel[tid * EPT + b] = v[b];
+                    __syncthreads();
+#pragma unroll
+                    for (int b = 0; b < EPT; ++b)
+                        pv[b] = sm.sel[(tid * EPT + b) ^ s];
+                }
+#pragma unroll
+                for (int b = 0; b < EPT; ++b) {
+                    const int i = tid * EPT + b;
+                    const bool lower = (i & s) == 0;
+                    const bool desc = (i & size) == 0;
+                    const uint64_t x = v[b], y = pv[b];
+                    const uint64_t hi = x > y ? x : y, lo = x > y ? y : x;
+                    v[b] = (lower == desc) ? hi : lo;
                 }
             }
-            __syncthreads();
         }
     }
+    __syncthreads();
 }
 
 // Load scores[lo, hi) of one row into sm.ord and return n.
