@@ -36,6 +36,9 @@ WORKLOAD_TEXT = {
        "top_k 2048; absorbed MLA 64 heads, kd 576, vd 512",
     4: "long-context decode: 8 sequences x 1 query over 131072 keys; fp8-e4m3 indexer keys "
        "with per-row scales, 32 heads x 128, top_k 2048; absorbed MLA 64 heads, kd 576, vd 512",
+    5: "pooled NoPE: 4 sequences x 16384 tokens (left pads 0, 2, 37, 64), all positions are "
+       "queries; kpool 4 softmax-pooled indexer keys, 32 heads x 128; top 512 pools + visible "
+       "tail (out_width 2052); per-head attention 64 heads, kd 192, vd 256",
 }
 
 
@@ -44,7 +47,7 @@ def _parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4])
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=64, help="query rows in the oracle sample")
     return ap.parse_args()
@@ -92,6 +95,76 @@ class Step:
                                lse=self.lse, workspace=self.ws_attn)
 
     stages = ("index", "topk", "attend")
+
+
+class PooledStep:
+    """The pooled NoPE step: pool keys -> pooled index scores -> pool select
+    -> per-head attention over the selected tokens."""
+
+    stages = ("pool_keys", "index", "pool_select", "attend")
+
+    def __init__(self, dsa, inp):
+        import torch
+        self.dsa, self.inp = dsa, inp
+        B, L, d, kp = inp["B"], inp["L"], inp["d"], inp["kpool"]
+        dev = inp["q_pos"].device
+        self.kp, self.sk, self.width = kp, inp["select_k"], inp["out_width"]
+        self.plo, self.phi = dsa.visibility_ranges(inp["pad"], inp["q_pos"], kp)
+        self.lo, self.hi = dsa.visibility_ranges(inp["pad"], inp["q_pos"])
+        self.pk = torch.empty((B, L // kp, d), dtype=torch.bfloat16, device=dev)
+        self.npools = torch.empty(B, dtype=torch.int32, device=dev)
+        self.S = torch.empty((B, L, L // kp), dtype=torch.float32, device=dev)
+        self.tok = torch.empty((B, L, self.width), dtype=torch.int32, device=dev)
+        H, vd = inp["H"], inp["vd"]
+        self.out = torch.empty((B, L, H, vd), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((B, L, H), dtype=torch.float32, device=dev)
+        dims = dsa._AttnDims(B, L, L, H, inp["kd"], vd, H, self.width, inp["scale_attn"])
+        self.ws_attn = torch.empty(max(dsa.sparse_attend_workspace_size(dims), 1),
+                                   dtype=torch.uint8, device=dev)
+
+    def pool_keys(self):
+        i = self.inp
+        self.dsa.pool_keys(i["k_idx"], i["gate"], i["pad"], self.kp, out=self.pk,
+                           n_pools=self.npools)
+
+    def index(self):
+        i = self.inp
+        self.dsa.index_scores(i["q_idx"], self.pk, i["w"], self.plo, self.phi, i["scale_idx"],
+                              out=self.S)
+
+    def pool_select(self):
+        i = self.inp
+        self.dsa.pool_select(self.S, i["pad"], i["q_pos"], self.kp, self.sk, self.width,
+                             out_tok=self.tok)
+
+    def attend(self):
+        i = self.inp
+        self.dsa.sparse_attend(i["q"], i["K"], i["V"], self.tok, i["scale_attn"], i["H"],
+                               vis_lo=self.lo, vis_hi=self.hi, out=self.out, lse=self.lse,
+                               workspace=self.ws_attn)
+
+
+def pooled_work(inp):
+    """Algorithmic bytes/flops of the pooled step (visible pool pairs and
+    selected tokens only)."""
+    B, L, d, Hi, kp = inp["B"], inp["L"], inp["d"], inp["Hi"], inp["kpool"]
+    H, kd, vd, sk, width = inp["H"], inp["kd"], inp["vd"], inp["select_k"], inp["out_width"]
+    pads = [int(p) for p in inp["pad"].cpu().tolist()]
+    vis_pairs = sel_pairs = queries = 0
+    for p in pads:
+        for t in range(p, L):
+            n_full = (t - p + 1) // kp
+            vis_pairs += n_full
+            sel_pairs += min(sk, n_full) * kp + (t + 1 - (p + n_full * kp))
+            queries += 1
+    np_ = L // kp
+    pk_bytes = 2 * B * L * d * 2 + B * np_ * d * 2
+    idx_bytes = B * L * Hi * d * 2 + B * np_ * d * 2 + B * L * Hi * 4 + vis_pairs * 4
+    sel_bytes = vis_pairs * 4 + B * L * width * 4
+    att_bytes = (B * L * H * (kd + kd + vd) * 2 + B * L * width * 4 + B * L * H * (vd + 1) * 4)
+    return {"pool_keys": (pk_bytes, 0), "index": (idx_bytes, 2 * Hi * d * vis_pairs),
+            "pool_select": (sel_bytes, 0),
+            "attend": (att_bytes, 2 * H * (kd + vd) * sel_pairs)}, queries
 
 
 def algorithmic_work(inp):
@@ -190,8 +263,9 @@ def main():
     cfg = args.config
     print(f"[bench] config {cfg}: generating inputs", file=sys.stderr, flush=True)
     inp = W.make(cfg, device="cuda")
-    step = Step(dsa, inp)
-    stages = [getattr(step, s) for s in Step.stages]
+    step = PooledStep(dsa, inp) if cfg == 5 else Step(dsa, inp)
+    names = type(step).stages
+    stages = [getattr(step, s) for s in names]
 
     def run_once():
         for f in stages:
@@ -216,22 +290,24 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     stage_ms = {}
-    for j, name in enumerate(Step.stages):
+    for j, name in enumerate(names):
         stage_ms[name] = sum(ev[s][j].elapsed_time(ev[s][j + 1]) for s in range(K)) / K
-    tokens = inp["B"] * inp["Tq"]
+    if cfg == 5:
+        work, tokens = pooled_work(inp)
+    else:
+        work, tokens = algorithmic_work(inp), inp["B"] * inp["Tq"]
     ms_per_step = wall * 1e3 / K
-    work = algorithmic_work(inp)
     per_stage = {}
-    for name in Step.stages:
+    for name in names:
         by, fl = work[name]
         t = stage_ms[name] * 1e-3
         per_stage[name] = {"ms": round(stage_ms[name], 5),
                            "alg_GBps": round(by / t / 1e9, 1),
                            "alg_TFLOPs": round(fl / t / 1e12, 2)}
-    dom = max(Step.stages, key=lambda n: stage_ms[n])
+    dom = max(names, key=lambda n: stage_ms[n])
     by, fl = work[dom]
     t = stage_ms[dom] * 1e-3
-    hbm_bound = cfg in (1, 2, 4) or dom == "topk"
+    hbm_bound = cfg in (1, 2, 4) or dom in ("topk", "pool_select", "pool_keys")
     if hbm_bound:
         ach = by / t / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
@@ -261,7 +337,7 @@ def main():
         "roofline": roof,
         "stages": per_stage,
     }
-    if not args.no_cpu:
+    if not args.no_cpu and cfg != 5:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_rows)
     print(json.dumps(result), flush=True)

@@ -65,7 +65,7 @@ def _load():
                                              ctypes.c_int, P, P, D, P, P, I32, P, I64, P, P]
             lib.orc_topk.argtypes = [P, I64, I64, I64, P, P, I32, I32, P]
             lib.orc_pool_keys.argtypes = [I64, I64, I64, I32, P, ctypes.c_int, P,
-                                          ctypes.c_int, P, P, P]
+                                          ctypes.c_int, P, P, P, P]
             lib.orc_pool_select.argtypes = [P, I64, I64, I64, P, P, I32, I32, I32, P, P]
             lib.orc_topk_to_mask.argtypes = [P, I64, I64, ctypes.c_int, I32, I32, P]
             lib.orc_topk_to_mask.restype = None
@@ -200,17 +200,19 @@ def topk(S, row_qpos, row_pad, k, kpool=0):
     return out
 
 
-def pool_keys(k, gate, pad, kpool):
-    """Pooled indexer keys in float64: [B, L//kpool, d], and n_pools [B]."""
+def pool_keys(k, gate, pad, kpool, want_mag=False):
+    """Pooled indexer keys in float64: [B, L//kpool, d], and n_pools [B]
+    (and, with want_mag, sum_j softmax_j |k_j| of each pooled value)."""
     ka, kt = _storage(k)
     ga, gt = _storage(gate)
     B, L, d = ka.shape
     pd = _i32(pad).reshape(B)
     pk = np.empty((B, L // kpool, d), np.float64)
+    mag = np.empty((B, L // kpool, d), np.float64) if want_mag else None
     npools = np.empty(B, np.int32)
     _load().orc_pool_keys(B, L, d, int(kpool), _ptr(ka), kt, _ptr(ga), gt, _ptr(pd),
-                          _ptr(pk), _ptr(npools))
-    return pk, npools
+                          _ptr(pk), _ptr(npools), _ptr(mag))
+    return (pk, npools, mag) if want_mag else (pk, npools)
 
 
 def pool_select(S, row_qpos, row_pad, kpool, select_k, out_width, want_pools=False):

@@ -241,10 +241,12 @@ int orc_topk(const float *S, int64_t n_rows, int64_t n_cols, int64_t row_stride,
  * holds tokens pad + i*kpool + j, j < kpool; a trailing partial pool is not a
  * pool, so n_pools[b] = floor((L - pad[b]) / kpool).  For each channel c,
  * pk = sum_j softmax_j(gate[t_j,c]) * k[t_j,c].  pk: [B, L/kpool, d] in f64;
- * rows i >= n_pools[b] are 0. */
+ * rows i >= n_pools[b] are 0.  mag (optional, same shape) receives
+ * sum_j softmax_j |k[t_j,c]|, which bounds the rounding error of any
+ * evaluation of the weighted sum. */
 int orc_pool_keys(int64_t B, int64_t L, int64_t d, int32_t kpool,
                   const void *k, int k_dtype, const void *gate, int g_dtype,
-                  const int32_t *pad, double *pk, int32_t *n_pools)
+                  const int32_t *pad, double *pk, int32_t *n_pools, double *mag)
 {
     int64_t np_max = L / kpool;
     for (int64_t b = 0; b < B; ++b) {
@@ -255,8 +257,11 @@ int orc_pool_keys(int64_t B, int64_t L, int64_t d, int32_t kpool,
         for (int64_t i = 0; i < np_max; ++i) {
             for (int64_t c = 0; c < d; ++c) {
                 double *o = &pk[(b * np_max + i) * d + c];
+                double *om = mag ? &mag[(b * np_max + i) * d + c] : NULL;
                 if (i >= np) {
                     *o = 0.0;
+                    if (om)
+                        *om = 0.0;
                     continue;
                 }
                 int64_t t0 = pad[b] + i * kpool;
@@ -266,13 +271,17 @@ int orc_pool_keys(int64_t B, int64_t L, int64_t d, int32_t kpool,
                     if (g > m)
                         m = g;
                 }
-                double num = 0.0, den = 0.0;
+                double num = 0.0, den = 0.0, anum = 0.0;
                 for (int32_t j = 0; j < kpool; ++j) {
                     double e = exp(load(gate, g_dtype, (b * L + t0 + j) * d + c) - m);
-                    num += e * load(k, k_dtype, (b * L + t0 + j) * d + c);
+                    double kv = load(k, k_dtype, (b * L + t0 + j) * d + c);
+                    num += e * kv;
+                    anum += e * fabs(kv);
                     den += e;
                 }
                 *o = num / den;
+                if (om)
+                    *om = anum / den;
             }
         }
     }

@@ -242,8 +242,7 @@ def sparse_attend(q, k, v, idx, scale: float, kv_heads: int, vd: int | None = No
         out = torch.empty((B, n_q, H, vd), dtype=torch.float32, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty((B, n_q, H), dtype=torch.float32, device=q.device)
-    need = sparse_attend_workspace_size(dims) if v is None else 0
-    ws, wsb = _workspace(need, workspace, q.device)
+    ws, wsb = _workspace(sparse_attend_workspace_size(dims), workspace, q.device)
     _check(load().dsa_sparse_attend(ctypes.byref(dims), _dtype_code(q), _p(q), _p(k), k_row,
                                     v_ptr, v_row, _p(_i32(idx)), _p(vis_lo), _p(vis_hi), _p(out),
                                     _p(lse), _p(ws), wsb, _stream()))

@@ -28,6 +28,9 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 constexpr int kWave = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+// Online softmax: the running reference max is only raised when a tile's max
+// exceeds it by more than this (log2 units), bounding p = 2^(x - m) by 2^8.
+constexpr float kRescaleLog2 = 8.f;
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16)
 {
@@ -69,6 +72,55 @@ __device__ __forceinline__ u32x2_t e4m3x4_to_bf16x4(uint32_t codes)
     r[0] = (__float_as_uint(lo[0]) >> 16) | (__float_as_uint(lo[1]) & 0xffff0000u);
     r[1] = (__float_as_uint(hi[0]) >> 16) | (__float_as_uint(hi[1]) & 0xffff0000u);
     return r;
+}
+
+// LDS pointers for the gfx950 LDS builtins.
+typedef short lds_v4i16_t __attribute__((ext_vector_type(4)));
+#define DSA_LDS_PTR(T, p) ((T __attribute__((address_space(3))) *)(p))
+
+// Direct global -> LDS copy (global_load_lds_dwordx4): each lane copies 16
+// bytes from its own `src`; lane l's bytes land at lds_base + 16*l, so one
+// wave instruction fills 1 KB of LDS.  lds_base must be wave-uniform.
+// Completion is tracked by vmcnt (wait with s_waitcnt before reading).
+__device__ __forceinline__ void lds_dma16(const void *src, void *lds_base)
+{
+    __builtin_amdgcn_global_load_lds(src, DSA_LDS_PTR(void, lds_base), 16, 0, 0);
+}
+
+// Make an LDS object's address visible to an opaque asm.  An LDS array that
+// only lds_dma16 ever fills is otherwise seen by the optimizer as never
+// stored to (its initial value is undefined), and reads of it may be folded.
+#define DSA_LDS_ESCAPE(obj) asm volatile("" ::"s"((const void *)&(obj)) : "memory")
+
+// Wait for this wave's outstanding global loads, LDS DMA included.  The
+// memory clobber tells the optimizer that LDS contents changed: data that
+// arrives only through lds_dma16 is otherwise invisible to it, and reads of
+// an LDS array it never saw stored to could be folded away.
+__device__ __forceinline__ void lds_dma_wait()
+{
+    __builtin_amdgcn_s_waitcnt(0);
+    asm volatile("" ::: "memory");
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16): in each group of 16 lanes, lane
+// r points at 4 consecutive 16-bit values M[r][0..3]; lane i receives
+// M[i/4 + 4j][i%4] for j = 0..3.  With source lane r = a + 4j pointing at
+// row key_j, columns 4a..4a+3 of a row-major tile, lane i therefore receives
+// column i of rows key_0..key_3 -- an MFMA operand fragment read across rows.
+__device__ __forceinline__ u32x2_t lds_read_tr16x4(const void *lds_addr)
+{
+    const lds_v4i16_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(DSA_LDS_PTR(lds_v4i16_t, lds_addr));
+    return __builtin_bit_cast(u32x2_t, r);
+}
+
+// XOR swizzle of the 16-byte chunks of row r of an LDS tile whose rows are a
+// multiple of 128 bytes apart and hold a multiple of 8 chunks: physical chunk
+// = logical chunk ^ chunk_swz(r).  Eight consecutive rows read at the same
+// logical chunk (ds_read_b128 operand fetches) hit 8 different chunk slots,
+// and the 4 rows x 2 adjacent chunks of a transposing read do too.
+__device__ __forceinline__ int chunk_swz(int row)
+{
+    return ((row & 3) << 1) | ((row >> 2) & 1);
 }
 
 // Order-preserving map of an f32 score to u32: larger score <=> larger key.

@@ -50,6 +50,8 @@ bool attend_gather_supported(const AttendArgs &a);
 bool attend_masked_supported(const AttendArgs &a);
 bool attend_plain_supported(const AttendArgs &a);
 size_t attend_workspace_bytes(const AttendArgs &a);
+size_t attend_masked_workspace_bytes(const AttendArgs &a);
+hipError_t launch_attend_masked(const AttendArgs &a, hipStream_t st);
 hipError_t launch_attend(const AttendArgs &a, hipStream_t st);
 
 struct RangeArgs {

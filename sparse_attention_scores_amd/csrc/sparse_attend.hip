@@ -103,37 +103,29 @@ constexpr int AB_H = 64;
 constexpr int AB_KD = 576;
 constexpr int AB_VD = 512;
 constexpr int AB_TILE = 32;
-constexpr int AB_KS = AB_KD / 32;        // 18 k-steps of the 16x16x32 MFMA
-constexpr int AB_NC = AB_VD / 16;        // 32 output column tiles per wave
-constexpr int AB_KPITCH = AB_KD + 8;     // K tile row pitch (bf16): 1168 B
-constexpr int AB_VPITCH = 20;            // V^T row pitch (dwords): 16 + 4 pad
-constexpr int AB_LIST = 1024;            // keys per batch of a block
+constexpr int AB_KS = AB_KD / 32;             // 18 k-steps of the 16x16x32 MFMA
+constexpr int AB_NC = AB_VD / 16;             // 32 output column tiles per wave
+constexpr int AB_ROWB = AB_KD * 2;            // 1152 bytes per latent row
+constexpr int AB_TILEB = AB_TILE * AB_ROWB;   // 36 KB per tile (36 DMA instructions)
+constexpr int AB_LIST = 1024;                 // keys per batch of a block
 constexpr int AB_NT = 256;
-constexpr int AB_CHUNKS = AB_KD / 8;     // 16-byte chunks per latent row
-constexpr int AB_LD = 5;                 // chunk slots per thread (16 pairs x 72 chunks / 256)
 
-// One stage of the double buffer.  K: row-major latent rows (bf16).  VT: the
-// first AB_VD columns transposed; dword r of row c holds key r (low half) and
-// key r+16 (high half), so a lane's PV operand (keys 4g..4g+3 and
-// 16+4g..16+4g+3) is one 16-byte read.
-struct __attribute__((aligned(16))) AbsBuf {
-    uint16_t k[AB_TILE * AB_KPITCH];
-    uint32_t vt[AB_VD * AB_VPITCH];
-};
-
+// LDS tile: 32 latent rows, 1152 bytes apart, with the 16-byte chunks of row
+// r stored XOR-swizzled (chunk_swz) so that both the row-wise Q.K^T operand
+// reads and the transposing P.V operand reads spread over all banks.  V is
+// the first 512 columns of the same rows.
 struct __attribute__((aligned(16))) AbsSmem {
     union {
-        AbsBuf buf[2];
+        unsigned char tile[2][AB_TILEB];
         uint32_t bitmap[kBitmapMaxWords];
     } u;
     int32_t list[AB_LIST];
     int wave_tot[AB_NT / 64];
 };
 
-__device__ __forceinline__ uint32_t pick_half(const u32x4_t &v, int e)
+__device__ __forceinline__ int ab_chunk(int row, int logical)
 {
-    const uint32_t w = v[e >> 1];
-    return (e & 1) ? (w >> 16) : (w & 0xffffu);
+    return row * (AB_ROWB / 16) + (logical ^ chunk_swz(row));
 }
 
 __global__ __launch_bounds__(AB_NT) void attend_gather_kernel(
@@ -144,6 +136,7 @@ __global__ __launch_bounds__(AB_NT) void attend_gather_kernel(
     int splits, float scale_log2)
 {
     __shared__ AbsSmem sm;
+    DSA_LDS_ESCAPE(sm);
     const int tid = threadIdx.x;
     const int lane = tid & 63, wid = tid >> 6;
     const int g = lane >> 4, col = lane & 15;
@@ -175,40 +168,19 @@ __global__ __launch_bounds__(AB_NT) void attend_gather_kernel(
         oacc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_part = 0.f;
 
-    const uint16_t *kvb = kv + b * (int64_t)n_k * row_stride;
-    // gather roles: pair pr = rows (pr, pr+16); chunks c8 = tid/16 + 16*j
-    const int pr = tid & 15;
-    const int cbase = tid >> 4;
-    u32x4_t R[AB_LD][2];
+    const unsigned char *kvb =
+        reinterpret_cast<const unsigned char *>(kv) + b * (int64_t)n_k * row_stride * 2;
 
-    auto load_tile = [&](int t0, int nvalid) {
-        const int k0 = sm.list[t0 + min(pr, nvalid - 1)];
-        const int k1 = sm.list[t0 + min(pr + 16, nvalid - 1)];
-        const uint16_t *p0 = kvb + (int64_t)k0 * row_stride;
-        const uint16_t *p1 = kvb + (int64_t)k1 * row_stride;
-#pragma unroll
-        for (int j = 0; j < AB_LD; ++j) {
-            const int c8 = cbase + 16 * j;
-            if (c8 < AB_CHUNKS) {
-                R[j][0] = *reinterpret_cast<const u32x4_t *>(p0 + c8 * 8);
-                R[j][1] = *reinterpret_cast<const u32x4_t *>(p1 + c8 * 8);
-            }
-        }
-    };
-    auto store_tile = [&](AbsBuf &B) {
-#pragma unroll
-        for (int j = 0; j < AB_LD; ++j) {
-            const int c8 = cbase + 16 * j;
-            if (c8 < AB_CHUNKS) {
-                *reinterpret_cast<u32x4_t *>(&B.k[pr * AB_KPITCH + c8 * 8]) = R[j][0];
-                *reinterpret_cast<u32x4_t *>(&B.k[(pr + 16) * AB_KPITCH + c8 * 8]) = R[j][1];
-                if (c8 < AB_VD / 8) {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        B.vt[(c8 * 8 + e) * AB_VPITCH + pr] =
-                            pick_half(R[j][0], e) | (pick_half(R[j][1], e) << 16);
-                }
-            }
+    // DMA one tile: 36 wave instructions of 1 KB; lane slot p of instruction
+    // s is LDS byte s*1024 + 16*lane = (row, physical chunk) -> its logical
+    // chunk of that row's key.
+    auto dma_tile = [&](unsigned char *dst, int t0, int nvalid) {
+        for (int s = wid; s < AB_TILEB / 1024; s += AB_NT / 64) {
+            const int c = s * 64 + lane;            // physical chunk index in the tile
+            const int r = c / (AB_ROWB / 16);
+            const int logical = (c % (AB_ROWB / 16)) ^ chunk_swz(r);
+            const int key = sm.list[t0 + min(r, nvalid - 1)];
+            lds_dma16(kvb + (int64_t)key * row_stride * 2 + logical * 16, dst + s * 1024);
         }
     };
 
@@ -234,28 +206,26 @@ __global__ __launch_bounds__(AB_NT) void attend_gather_kernel(
         const int n_my = re - rb;
         const int ntiles = (n_my + AB_TILE - 1) / AB_TILE;
 
-        load_tile(0, min(AB_TILE, n_my));
-        store_tile(sm.u.buf[0]);
-        __syncthreads();
+        dma_tile(sm.u.tile[0], 0, min(AB_TILE, n_my));
         for (int t = 0; t < ntiles; ++t) {
             const int t0 = t * AB_TILE;
             const int nvalid = min(AB_TILE, n_my - t0);
+            // tile t has landed (own DMA) and is visible to all waves
+            lds_dma_wait();
+            __syncthreads();
             if (t + 1 < ntiles)
-                load_tile(t0 + AB_TILE, min(AB_TILE, n_my - t0 - AB_TILE));
-            const AbsBuf &B = sm.u.buf[t & 1];
+                dma_tile(sm.u.tile[(t + 1) & 1], t0 + AB_TILE, min(AB_TILE, n_my - t0 - AB_TILE));
+            const unsigned char *T = sm.u.tile[t & 1];
+            const u32x4_t *T16 = reinterpret_cast<const u32x4_t *>(T);
 
             // ---- S^T[key][head]: keys 0-15 (s0) and 16-31 (s1), two chains each
             f32x4_t s0a = {0.f, 0.f, 0.f, 0.f}, s0b = s0a, s1a = s0a, s1b = s0a;
 #pragma unroll
             for (int ks = 0; ks < AB_KS; ks += 2) {
-                const u32x4_t a0 = *reinterpret_cast<const u32x4_t *>(
-                    &B.k[col * AB_KPITCH + ks * 32 + g * 8]);
-                const u32x4_t a1 = *reinterpret_cast<const u32x4_t *>(
-                    &B.k[(16 + col) * AB_KPITCH + ks * 32 + g * 8]);
-                const u32x4_t a2 = *reinterpret_cast<const u32x4_t *>(
-                    &B.k[col * AB_KPITCH + (ks + 1) * 32 + g * 8]);
-                const u32x4_t a3 = *reinterpret_cast<const u32x4_t *>(
-                    &B.k[(16 + col) * AB_KPITCH + (ks + 1) * 32 + g * 8]);
+                const u32x4_t a0 = T16[ab_chunk(col, 4 * ks + g)];
+                const u32x4_t a1 = T16[ab_chunk(16 + col, 4 * ks + g)];
+                const u32x4_t a2 = T16[ab_chunk(col, 4 * (ks + 1) + g)];
+                const u32x4_t a3 = T16[ab_chunk(16 + col, 4 * (ks + 1) + g)];
                 s0a = mfma_16x16x32(a0, qf[ks], s0a);
                 s1a = mfma_16x16x32(a1, qf[ks], s1a);
                 s0b = mfma_16x16x32(a2, qf[ks + 1], s0b);
@@ -274,25 +244,39 @@ __global__ __launch_bounds__(AB_NT) void attend_gather_kernel(
             }
             tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
             tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-            const float m_new = fmaxf(m_run, tmax);
-            const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
+            // Lazy rescale: the reference max only moves when the tile max
+            // exceeds it by more than kRescaleLog2, so p <= 2^kRescaleLog2
+            // and the O accumulators are rarely touched.  Exact: l and O
+            // always share the same reference.
+            const bool grow = tmax > m_run + kRescaleLog2;
+            if (__any(grow)) {
+                const float m_new = grow ? tmax : m_run;
+                // lanes that do not grow keep alpha = 1 (m_run may still be -inf
+                // there, and -inf - -inf would be NaN); a growing lane with
+                // m_run = -inf gets 0
+                const float alpha = grow ? exp2f(m_run - m_new) : 1.f;
+                if (__any(grow && m_run != -INFINITY)) {
+#pragma unroll
+                    for (int n = 0; n < AB_NC; ++n)
+                        oacc[n] *= alpha;
+                }
+                l_part *= alpha;
+                m_run = m_new;
+            }
+            // m_run is -inf only while every key seen so far (this tile
+            // included) is masked; then all x are -inf and p must be 0.
+            const float m_ref = (m_run == -INFINITY) ? 0.f : m_run;
             float p0[4], p1[4];
             float psum = 0.f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                p0[i] = (m_new == -INFINITY) ? 0.f : exp2f(x0[i] - m_new);
-                p1[i] = (m_new == -INFINITY) ? 0.f : exp2f(x1[i] - m_new);
+                p0[i] = exp2f(x0[i] - m_ref);
+                p1[i] = exp2f(x1[i] - m_ref);
                 psum += p0[i] + p1[i];
             }
-            l_part = l_part * alpha + psum;
-            m_run = m_new;
-            if (__any(alpha != 1.f)) {
-#pragma unroll
-                for (int n = 0; n < AB_NC; ++n)
-                    oacc[n] *= alpha;
-            }
-            // ---- P^T fragments (B operand), element j <-> key (j even: 4g+j/2,
-            //      j odd: 16+4g+j/2), as a two-term bf16 split
+            l_part += psum;
+            // ---- P^T fragments (B operand): element j <-> key 4g+j (j < 4),
+            //      16+4g+(j-4) (j >= 4); two-term bf16 split
             u32x4_t bhi, blo;
             {
                 float h0[4], h1[4];
@@ -301,25 +285,33 @@ __global__ __launch_bounds__(AB_NT) void attend_gather_kernel(
                     h0[i] = bf16_bits_to_f32(f32_to_bf16_bits(p0[i]));
                     h1[i] = bf16_bits_to_f32(f32_to_bf16_bits(p1[i]));
                 }
-                bhi = u32x4_t{pack_bf16x2(h0[0], h1[0]), pack_bf16x2(h0[1], h1[1]),
-                              pack_bf16x2(h0[2], h1[2]), pack_bf16x2(h0[3], h1[3])};
-                blo = u32x4_t{pack_bf16x2(p0[0] - h0[0], p1[0] - h1[0]),
-                              pack_bf16x2(p0[1] - h0[1], p1[1] - h1[1]),
-                              pack_bf16x2(p0[2] - h0[2], p1[2] - h1[2]),
-                              pack_bf16x2(p0[3] - h0[3], p1[3] - h1[3])};
+                bhi = u32x4_t{pack_bf16x2(h0[0], h0[1]), pack_bf16x2(h0[2], h0[3]),
+                              pack_bf16x2(h1[0], h1[1]), pack_bf16x2(h1[2], h1[3])};
+                blo = u32x4_t{pack_bf16x2(p0[0] - h0[0], p0[1] - h0[1]),
+                              pack_bf16x2(p0[2] - h0[2], p0[3] - h0[3]),
+                              pack_bf16x2(p1[0] - h1[0], p1[1] - h1[1]),
+                              pack_bf16x2(p1[2] - h1[2], p1[3] - h1[3])};
             }
-            // ---- O^T[c][head] += V^T[c][keys] P^T[keys][head]
+            // ---- O^T[c][head] += V^T[c][keys] P^T[keys][head]; the V^T
+            //      fragment of column c = n*16+col is read transposed from the
+            //      row-major tile: source lane col = a + 4j points at row
+            //      4g + j (then 16 + 4g + j), columns n*16 + 4a .. + 3.
+            {
+                const int ra = 4 * g + (col >> 2);
+                const int a8 = (col & 3) * 8;            // byte offset of 4 columns
 #pragma unroll
-            for (int n = 0; n < AB_NC; ++n) {
-                const u32x4_t a = *reinterpret_cast<const u32x4_t *>(
-                    &B.vt[(n * 16 + col) * AB_VPITCH + 4 * g]);
-                oacc[n] = mfma_16x16x32(a, bhi, oacc[n]);
-                oacc[n] = mfma_16x16x32(a, blo, oacc[n]);
+                for (int n = 0; n < AB_NC; ++n) {
+                    const int lc = 2 * n + (a8 >> 4);    // logical 16-byte chunk
+                    const u32x2_t va = lds_read_tr16x4(T + ab_chunk(ra, lc) * 16 + (a8 & 8));
+                    const u32x2_t vb =
+                        lds_read_tr16x4(T + ab_chunk(16 + ra, lc) * 16 + (a8 & 8));
+                    const u32x4_t av = u32x4_t{va[0], va[1], vb[0], vb[1]};
+                    oacc[n] = mfma_16x16x32(av, bhi, oacc[n]);
+                    oacc[n] = mfma_16x16x32(av, blo, oacc[n]);
+                }
             }
-            if (t + 1 < ntiles)
-                store_tile(sm.u.buf[(t + 1) & 1]);
-            __syncthreads();
         }
+        __syncthreads();  // last tile consumed before the bitmap reuses LDS
     }
 
     // ---- epilogue: l over the 4 lane groups of the head
@@ -494,6 +486,8 @@ int attend_gather_splits(const AttendArgs &a)
 
 size_t attend_workspace_bytes(const AttendArgs &a)
 {
+    if (attend_masked_supported(a))
+        return attend_masked_workspace_bytes(a);
     if (!attend_gather_supported(a))
         return 0;
     const int s = attend_gather_splits(a);
@@ -501,12 +495,6 @@ size_t attend_workspace_bytes(const AttendArgs &a)
         return 0;
     const int64_t rows = (int64_t)a.batch * a.n_q;
     return (size_t)rows * s * AB_H * (AB_VD + 2) * sizeof(float);
-}
-
-bool attend_masked_supported(const AttendArgs &a)
-{
-    (void)a;
-    return false;
 }
 
 bool attend_plain_supported(const AttendArgs &a)
@@ -534,6 +522,8 @@ hipError_t launch_attend(const AttendArgs &a, hipStream_t st)
                            ws_o, ws_ml, a.out, a.lse, AB_H, AB_VD, splits);
         return hipGetLastError();
     }
+    if (attend_masked_supported(a))
+        return launch_attend_masked(a, st);
     const unsigned blocks = (unsigned)(rows * a.n_heads);
     if (a.f32)
         hipLaunchKernelGGL(attend_plain_kernel<float>, dim3(blocks), dim3(PL_NT), 0, st,

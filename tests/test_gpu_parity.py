@@ -234,10 +234,10 @@ def test_attend_plain_f32_per_head_and_shared(dsa):
                      what=f"config 1 kv_heads {kvh}")
 
 
-def test_attend_plain_bf16_per_head_small(dsa):
-    note("plain attend bf16 per-head (small pooled shape)")
+def test_attend_plain_bf16_per_head_other_shape(dsa):
+    note("plain attend bf16 per-head (shape outside the MFMA kernels)")
     gen = torch.Generator(device="cuda").manual_seed(11)
-    B, T, H, kd, vd = 2, 50, 4, 192, 256
+    B, T, H, kd, vd = 2, 50, 4, 96, 80
     q = (torch.randn(B, T, H, kd, generator=gen, device="cuda") / kd ** 0.5).bfloat16()
     K = (torch.randn(B, T, H, kd, generator=gen, device="cuda") / kd ** 0.5).bfloat16()
     V = (torch.randn(B, T, H, vd, generator=gen, device="cuda") / vd ** 0.5).bfloat16()
@@ -257,9 +257,10 @@ def test_pool_keys_within_one_ulp(dsa):
     inp = W.make(5, device="cuda", L=1030)
     pk, npools = dsa.pool_keys(inp["k_idx"], inp["gate"], inp["pad"], 4)
     torch.cuda.synchronize()
-    ref, rn = oracle.pool_keys(cpu(inp["k_idx"]), cpu(inp["gate"]), cpu(inp["pad"]), 4)
+    ref, rn, mag = oracle.pool_keys(cpu(inp["k_idx"]), cpu(inp["gate"]), cpu(inp["pad"]), 4,
+                                    want_mag=True)
     assert cpu(npools).tolist() == rn.tolist()
-    bf16_ulp_ok(cpu(pk), ref, "pool keys")
+    bf16_ulp_ok(cpu(pk), ref, mag, "pool keys")
     for b, n in enumerate(rn):
         assert torch.all(pk[b, n:] == 0)
 
@@ -302,3 +303,59 @@ def test_abi_rejects_bad_arguments(dsa):
         dsa.index_scores(q, k, w, l1, l1, 1.0)
     assert e.value.code == -2
     assert "n_heads" in str(e.value)
+
+
+# ---------------------------------------------------------------- masked per-head attention
+
+def _pooled_selection(dsa, inp, kp, sk, width):
+    pk, _ = dsa.pool_keys(inp["k_idx"], inp["gate"], inp["pad"], kp)
+    lo, hi = dsa.visibility_ranges(inp["pad"], inp["q_pos"], kp)
+    S = dsa.index_scores(inp["q_idx"], pk, inp["w"], lo, hi, inp["scale_idx"])
+    torch.cuda.synchronize()
+    Sc = cpu(S).numpy().reshape(-1, S.shape[-1])
+    qp, pd = _rows_qpos_pad(inp)
+    return oracle.pool_select(Sc, qp, pd, kp, sk, width).reshape(inp["B"], inp["Tq"], width)
+
+
+@pytest.mark.parametrize("L,sk,variant", [(700, 32, None), (333, 16, "sharp")])
+def test_masked_attend_pooled_selection(dsa, L, sk, variant):
+    """Per-head attention over the oracle's pool selection (config 5 shape,
+    reduced length; ragged query blocks and key tiles)."""
+    note(f"masked attend, pooled selection L={L} select_k={sk} {variant}")
+    kp = 4
+    width = sk * kp + kp
+    inp = W.make(5, device="cuda", L=L, variant=variant)
+    sel = _pooled_selection(dsa, inp, kp, sk, width)
+    idx = torch.tensor(sel, device="cuda")
+    lo, hi = dsa.visibility_ranges(inp["pad"], inp["q_pos"])
+    out, lse = dsa.sparse_attend(inp["q"], inp["K"], inp["V"], idx, inp["scale_attn"],
+                                 kv_heads=inp["H"], vis_lo=lo, vis_hi=hi)
+    torch.cuda.synchronize()
+    ref, lref = oracle.sparse_attend(cpu(inp["q"]), cpu(inp["K"]), cpu(inp["V"]), sel,
+                                     inp["scale_attn"], inp["H"], q_pos=cpu(inp["q_pos"]),
+                                     pad=cpu(inp["pad"]))
+    check_attend(cpu(out).numpy().reshape(ref.shape), ref, cpu(lse).numpy().reshape(lref.shape),
+                 lref, bf16=True, what=f"masked L={L}")
+    # padded queries attend to nothing
+    pads = cpu(inp["pad"]).tolist()
+    for b, p in enumerate(pads):
+        if p:
+            assert torch.all(out[b, :p] == 0) and torch.all(torch.isneginf(lse[b, :p]))
+
+
+def test_masked_attend_set_semantics(dsa):
+    note("masked attend: duplicates / INVALID / out-of-range, no visibility ranges")
+    gen = torch.Generator(device="cuda").manual_seed(13)
+    B, T, H, kd, vd = 2, 150, 8, 192, 256
+    q = (torch.randn(B, T, H, kd, generator=gen, device="cuda") / kd ** 0.5).bfloat16()
+    K = (torch.randn(B, T, H, kd, generator=gen, device="cuda") / kd ** 0.5).bfloat16()
+    V = (torch.randn(B, T, H, vd, generator=gen, device="cuda") / vd ** 0.5).bfloat16()
+    sel = np.random.default_rng(4).integers(-2, T + 9, (B, T, 40)).astype(np.int32)
+    sel[:, :, 20:] = sel[:, :, :20]
+    sel[0, 3, :] = INV
+    idx = torch.tensor(sel, device="cuda")
+    out, lse = dsa.sparse_attend(q, K, V, idx, kd ** -0.5, H)
+    torch.cuda.synchronize()
+    ref, lref = oracle.sparse_attend(cpu(q), cpu(K), cpu(V), sel, kd ** -0.5, H)
+    check_attend(cpu(out).numpy().reshape(ref.shape), ref, cpu(lse).numpy().reshape(lref.shape),
+                 lref, bf16=True, what="masked set semantics")
