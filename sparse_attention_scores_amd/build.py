@@ -26,6 +26,9 @@ ARCH = "gfx950"
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA accumulators in VGPRs: with them in AGPRs the compiler copies
+    # the whole attention accumulator set through VALU moves every key tile
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wall", "-Wno-unused-function",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]

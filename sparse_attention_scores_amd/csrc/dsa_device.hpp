@@ -49,6 +49,28 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
     return f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
 }
 
+// Two floats -> packed bf16x2 (low half = a), one v_cvt_pk_bf16_f32 (RNE).
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b)
+{
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
+// Two-term bf16 split of 8 f32 weights, packed as MFMA operands:
+// hi = bf16(p), lo = bf16(p - hi).  p - hi is exact in f32, so hi + lo
+// carries about 16 significant bits of p.
+__device__ __forceinline__ void split_bf16x8(const float (&p)[8], uint32_t (&hi)[4],
+                                             uint32_t (&lo)[4])
+{
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t h = cvt_pk_bf16(p[2 * k], p[2 * k + 1]);
+        hi[k] = h;
+        lo[k] = cvt_pk_bf16(p[2 * k] - __uint_as_float(h << 16),
+                            p[2 * k + 1] - __uint_as_float(h & 0xffff0000u));
+    }
+}
+
 __device__ __forceinline__ f32x4_t mfma_16x16x32(const u32x4_t &a, const u32x4_t &b, f32x4_t c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -102,6 +124,47 @@ __device__ __forceinline__ void lds_dma_wait()
     asm volatile("" ::: "memory");
 }
 
+// Wait until at most N of this wave's vector-memory operations (LDS DMA
+// included; they complete in issue order) are outstanding.  gfx9 s_waitcnt
+// immediate: vmcnt in bits [3:0] and [15:14]; expcnt (7) and lgkmcnt (15)
+// left at "no wait".
+template <int N>
+__device__ __forceinline__ void vm_wait()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+    asm volatile("" ::: "memory");
+}
+
+// vm_wait<N * per_tile> for a runtime N in [0, 3] (the tiles still in flight
+// behind the one needed).
+template <int PER_TILE>
+__device__ __forceinline__ void vm_wait_tiles(int tiles_after)
+{
+    switch (tiles_after) {
+    case 0: vm_wait<0>(); break;
+    case 1: vm_wait<PER_TILE>(); break;
+    case 2: vm_wait<2 * PER_TILE>(); break;
+    default: vm_wait<3 * PER_TILE>(); break;
+    }
+}
+
+// Workgroup barrier that orders LDS only: this wave's LDS reads and writes
+// are complete before it arrives.  __syncthreads() also makes the compiler
+// wait for every direct-to-LDS load still in flight (it counts them as
+// pending LDS writes), which would drain the tiles being prefetched; callers
+// of this barrier wait for the tiles they need themselves (vm_wait).
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// 4 bytes per lane, global -> LDS at lds_base + 4*lane.
+__device__ __forceinline__ void lds_dma4(const void *src, void *lds_base)
+{
+    __builtin_amdgcn_global_load_lds(src, DSA_LDS_PTR(void, lds_base), 4, 0, 0);
+}
+
 // Transposing LDS read (ds_read_b64_tr_b16): in each group of 16 lanes, lane
 // r points at 4 consecutive 16-bit values M[r][0..3]; lane i receives
 // M[i/4 + 4j][i%4] for j = 0..3.  With source lane r = a + 4j pointing at
@@ -113,6 +176,71 @@ __device__ __forceinline__ u32x2_t lds_read_tr16x4(const void *lds_addr)
     return __builtin_bit_cast(u32x2_t, r);
 }
 
+// Sixteen transposing LDS reads and the wait for them, in one asm statement:
+// va[r] from b[r & 3] + (r < 4 ? O0 : O1), vb[r] from the same address + ROW.
+// The wait sits inside the statement, so the destination registers are
+// complete when the compiler first sees them.  (The builtin form cannot be
+// used next to direct-to-LDS loads: the compiler puts a wait for every
+// outstanding vector-memory operation in front of it, which would drain the
+// tiles still in flight.)
+template <int O0, int O1, int ROW>
+__device__ __forceinline__ void lds_read_tr16x4_x16(u32x2_t (&va)[8], u32x2_t (&vb)[8],
+                                                    uint32_t b0, uint32_t b1, uint32_t b2,
+                                                    uint32_t b3)
+{
+    static_assert(O0 >= 0 && O1 + ROW < 65536, "ds offset is 16 bits");
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %16 offset:%20\n\t"
+        "ds_read_b64_tr_b16 %1, %17 offset:%20\n\t"
+        "ds_read_b64_tr_b16 %2, %18 offset:%20\n\t"
+        "ds_read_b64_tr_b16 %3, %19 offset:%20\n\t"
+        "ds_read_b64_tr_b16 %4, %16 offset:%21\n\t"
+        "ds_read_b64_tr_b16 %5, %17 offset:%21\n\t"
+        "ds_read_b64_tr_b16 %6, %18 offset:%21\n\t"
+        "ds_read_b64_tr_b16 %7, %19 offset:%21\n\t"
+        "ds_read_b64_tr_b16 %8, %16 offset:%22\n\t"
+        "ds_read_b64_tr_b16 %9, %17 offset:%22\n\t"
+        "ds_read_b64_tr_b16 %10, %18 offset:%22\n\t"
+        "ds_read_b64_tr_b16 %11, %19 offset:%22\n\t"
+        "ds_read_b64_tr_b16 %12, %16 offset:%23\n\t"
+        "ds_read_b64_tr_b16 %13, %17 offset:%23\n\t"
+        "ds_read_b64_tr_b16 %14, %18 offset:%23\n\t"
+        "ds_read_b64_tr_b16 %15, %19 offset:%23\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(va[0]), "=&v"(va[1]), "=&v"(va[2]), "=&v"(va[3]), "=&v"(va[4]), "=&v"(va[5]),
+          "=&v"(va[6]), "=&v"(va[7]), "=&v"(vb[0]), "=&v"(vb[1]), "=&v"(vb[2]), "=&v"(vb[3]),
+          "=&v"(vb[4]), "=&v"(vb[5]), "=&v"(vb[6]), "=&v"(vb[7])
+        : "v"(b0), "v"(b1), "v"(b2), "v"(b3), "i"(O0), "i"(O1), "i"(O0 + ROW), "i"(O1 + ROW)
+        : "memory");
+}
+
+// Six 16-byte LDS reads and the wait for them, in one asm statement (for
+// the same reason as above): a[2j] from base + O + 128j and a[2j+1] from
+// base + O + 128j + ROW, j < 3.
+template <int O, int ROW>
+__device__ __forceinline__ void lds_read_b128_x6(u32x4_t (&a)[6], uint32_t base)
+{
+    static_assert(O >= 0 && O + 256 + ROW < 65536, "ds offset is 16 bits");
+    asm volatile(
+        "ds_read_b128 %0, %6 offset:%7\n\t"
+        "ds_read_b128 %1, %6 offset:%8\n\t"
+        "ds_read_b128 %2, %6 offset:%9\n\t"
+        "ds_read_b128 %3, %6 offset:%10\n\t"
+        "ds_read_b128 %4, %6 offset:%11\n\t"
+        "ds_read_b128 %5, %6 offset:%12\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4]), "=&v"(a[5])
+        : "v"(base), "i"(O), "i"(O + ROW), "i"(O + 128), "i"(O + 128 + ROW), "i"(O + 256),
+          "i"(O + 256 + ROW)
+        : "memory");
+}
+
+// 32-bit LDS byte address of a pointer into shared memory.
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
+{
+    return (uint32_t)(uintptr_t)DSA_LDS_PTR(const char, p);
+}
+
 // XOR swizzle of the 16-byte chunks of row r of an LDS tile whose rows are a
 // multiple of 128 bytes apart and hold a multiple of 8 chunks: physical chunk
 // = logical chunk ^ chunk_swz(r).  Eight consecutive rows read at the same
@@ -121,6 +249,18 @@ __device__ __forceinline__ u32x2_t lds_read_tr16x4(const void *lds_addr)
 __device__ __forceinline__ int chunk_swz(int row)
 {
     return ((row & 3) << 1) | ((row >> 2) & 1);
+}
+
+// Swizzle for tiles whose rows are an odd multiple of 128 bytes apart (e.g.
+// 1152-byte latent rows).  LDS has 64 banks of 4 bytes (256 bytes a cycle),
+// so rows r and r+1 start half a bank cycle apart and the XOR must separate
+// rows of equal parity: rows 0..15 at one logical chunk hit 16 different
+// 16-byte bank slots (a 16-lane ds_read_b128 group), and rows 0..7 (8..15)
+// at two adjacent logical chunks hit 16 different slots too (the 32 lanes
+// of one transposing ds_read_b64_tr_b16 cycle).
+__device__ __forceinline__ int chunk_swz_odd(int row)
+{
+    return (((row >> 1) & 3) << 1) | ((row >> 3) & 1);
 }
 
 // Order-preserving map of an f32 score to u32: larger score <=> larger key.

@@ -32,6 +32,8 @@
 #include <float.h>
 #include <math.h>
 
+#include <type_traits>
+
 namespace dsa {
 
 // ------------------------------------------------------------------ shared
@@ -104,30 +106,41 @@ constexpr int AB_KD = 576;
 constexpr int AB_VD = 512;
 constexpr int AB_TILE = 32;
 constexpr int AB_KS = AB_KD / 32;             // 18 k-steps of the 16x16x32 MFMA
-constexpr int AB_NC = AB_VD / 16;             // 32 output column tiles per wave
 constexpr int AB_ROWB = AB_KD * 2;            // 1152 bytes per latent row
-constexpr int AB_TILEB = AB_TILE * AB_ROWB;   // 36 KB per tile (36 DMA instructions)
+constexpr int AB_CPR = AB_ROWB / 16;          // 72 16-byte chunks per row
+constexpr int AB_TILEB = AB_TILE * AB_ROWB;   // 36 KB per tile
+constexpr int AB_DMA = AB_TILEB / 1024;       // 36 one-KB wave DMA instructions per tile
 constexpr int AB_LIST = 1024;                 // keys per batch of a block
-constexpr int AB_NT = 256;
+constexpr int AB_NT = 512;                    // 8 waves: 4 head groups x 2 halves
+constexpr int AB_NW = AB_NT / 64;
+constexpr int AB_NC = AB_VD / 2 / 16;         // 16 output column tiles per wave
+constexpr int AB_STAGES = 3;                  // tiles resident in LDS (ring)
+// wave w issues the tile's DMA instructions w, w + 8, ...: 5 for waves 0-3,
+// 4 for waves 4-7
+constexpr int AB_DMA_HI = (AB_DMA + AB_NW - 1) / AB_NW;
+constexpr int AB_DMA_LO = AB_DMA / AB_NW;
+static_assert(AB_DMA % AB_NW == AB_NW / 2, "waves 0-3 issue one DMA more than waves 4-7");
 
 // LDS tile: 32 latent rows, 1152 bytes apart, with the 16-byte chunks of row
-// r stored XOR-swizzled (chunk_swz) so that both the row-wise Q.K^T operand
+// r stored XOR-swizzled (chunk_swz_odd) so that both the row-wise Q.K^T operand
 // reads and the transposing P.V operand reads spread over all banks.  V is
 // the first 512 columns of the same rows.
-struct __attribute__((aligned(16))) AbsSmem {
+// The tiles are the only LDS object the direct-to-LDS loads write, and they
+// are only read through asm; the other LDS data live in objects of their own,
+// so the compiler can tell them apart and puts no wait for the tile loads in
+// front of their accesses.
+struct __attribute__((aligned(16))) AbsTiles {
     union {
-        unsigned char tile[2][AB_TILEB];
+        unsigned char tile[AB_STAGES][AB_TILEB];
         uint32_t bitmap[kBitmapMaxWords];
     } u;
-    int32_t list[AB_LIST];
-    int wave_tot[AB_NT / 64];
 };
 
-__device__ __forceinline__ int ab_chunk(int row, int logical)
-{
-    return row * (AB_ROWB / 16) + (logical ^ chunk_swz(row));
-}
-
+// Wave w of a block owns heads 16*(w&3) .. +15 and half h = w>>2 of the work
+// on them: the k-steps ks = 2m + h of Q.K^T (the partner wave w^4 does the
+// others; the two partial score tiles are exchanged through LDS, so both
+// hold the same S) and output columns 256h .. 256h + 255 of P.V.  Partners
+// share a SIMD, so one's LDS waits overlap the other's MFMAs.
 __global__ __launch_bounds__(AB_NT) void attend_gather_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kv, int64_t row_stride,
     const int32_t *__restrict__ idx, const int32_t *__restrict__ vlo,
@@ -135,11 +148,16 @@ __global__ __launch_bounds__(AB_NT) void attend_gather_kernel(
     float *__restrict__ ws_o, float *__restrict__ ws_ml, int n_q, int n_k, int n_sel,
     int splits, float scale_log2)
 {
-    __shared__ AbsSmem sm;
+    __shared__ AbsTiles sm;
+    __shared__ f32x4_t sm_xs[AB_NW][2][64];  // partial S^T of each wave, for its partner
+    __shared__ int32_t sm_list[AB_LIST];
+    __shared__ int sm_wave_tot[AB_NW];
     DSA_LDS_ESCAPE(sm);
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wid = tid >> 6;
+    const int lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, col = lane & 15;
+    const int hg = wid & 3, half = wid >> 2;
     const int row = blockIdx.x / splits;
     const int split = blockIdx.x % splits;
     const int64_t b = row / n_q;
@@ -153,14 +171,15 @@ __global__ __launch_bounds__(AB_NT) void attend_gather_kernel(
     const int wpt = (nw + AB_NT - 1) / AB_NT;
     const int w0 = min(tid * wpt, nw), w1 = min(w0 + wpt, nw);
 
-    // Q^T fragments (B operand): lane holds head wid*16+col, dims ks*32+g*8..+8
-    const int head = wid * 16 + col;
-    u32x4_t qf[AB_KS];
+    // Q^T fragments (B operand) of this wave's k-steps ks = 2m + half: lane
+    // holds head hg*16+col, dims ks*32 + g*8 .. +8
+    const int head = hg * 16 + col;
+    u32x4_t qf[AB_KS / 2];
     {
-        const uint16_t *qp = q + ((int64_t)row * AB_H + head) * AB_KD + g * 8;
+        const uint16_t *qp = q + ((int64_t)row * AB_H + head) * AB_KD + half * 32 + g * 8;
 #pragma unroll
-        for (int ks = 0; ks < AB_KS; ++ks)
-            qf[ks] = *reinterpret_cast<const u32x4_t *>(qp + ks * 32);
+        for (int m = 0; m < AB_KS / 2; ++m)
+            qf[m] = *reinterpret_cast<const u32x4_t *>(qp + m * 64);
     }
     f32x4_t oacc[AB_NC];
 #pragma unroll
@@ -171,18 +190,48 @@ __global__ __launch_bounds__(AB_NT) void attend_gather_kernel(
     const unsigned char *kvb =
         reinterpret_cast<const unsigned char *>(kv) + b * (int64_t)n_k * row_stride * 2;
 
-    // DMA one tile: 36 wave instructions of 1 KB; lane slot p of instruction
-    // s is LDS byte s*1024 + 16*lane = (row, physical chunk) -> its logical
-    // chunk of that row's key.
+    // DMA one tile: wave instruction s (1 KB) fills LDS bytes s*1024 + 16*lane
+    // = (row, physical chunk) from the logical chunk of that row's key.  The
+    // (row, byte offset) of each of this lane's slots is fixed; the keys are
+    // looked up first so the list reads overlap.
+    int dma_row[AB_DMA_HI], dma_off[AB_DMA_HI];
+#pragma unroll
+    for (int i = 0; i < AB_DMA_HI; ++i) {
+        const int c = (wid + i * AB_NW) * 64 + lane;
+        dma_row[i] = c / AB_CPR;
+        dma_off[i] = ((c % AB_CPR) ^ chunk_swz_odd(c / AB_CPR)) * 16;
+    }
+    const int64_t rs2 = row_stride * 2;
     auto dma_tile = [&](unsigned char *dst, int t0, int nvalid) {
-        for (int s = wid; s < AB_TILEB / 1024; s += AB_NT / 64) {
-            const int c = s * 64 + lane;            // physical chunk index in the tile
-            const int r = c / (AB_ROWB / 16);
-            const int logical = (c % (AB_ROWB / 16)) ^ chunk_swz(r);
-            const int key = sm.list[t0 + min(r, nvalid - 1)];
-            lds_dma16(kvb + (int64_t)key * row_stride * 2 + logical * 16, dst + s * 1024);
-        }
+        int key[AB_DMA_HI];
+#pragma unroll
+        for (int i = 0; i < AB_DMA_HI; ++i)
+            if (wid + i * AB_NW < AB_DMA)
+                key[i] = sm_list[t0 + min(dma_row[i], nvalid - 1)];
+#pragma unroll
+        for (int i = 0; i < AB_DMA_HI; ++i)
+            if (wid + i * AB_NW < AB_DMA)
+                lds_dma16(kvb + (int64_t)key[i] * rs2 + dma_off[i],
+                          dst + (wid + i * AB_NW) * 1024);
     };
+
+    // Per-lane LDS byte offsets inside a tile (constant over tiles).
+    //  Q.K^T: lane reads rows col and 16+col at logical chunk 4*ks + g =
+    //  8m + 4*half + g; the swizzle only touches the low 3 bits, so that is
+    //  physical chunk 8m + ((4*half + g) ^ swz(col)): one base, immediates.
+    const uint32_t qk_base = (col * AB_CPR + ((4 * half + g) ^ chunk_swz_odd(col))) * 16;
+    //  P.V: the V^T fragment of output column tile n = 16*half + 8M + r is
+    //  read transposed from rows ra and 16+ra at logical chunk 2n + hb, i.e.
+    //  physical chunk 32*half + 16M + 8(r>>2) + ((2(r&3) + hb) ^ swz(ra)):
+    //  four bases (r & 3) plus immediates; byte (col&1)*8 inside the chunk.
+    const int ra = 4 * g + (col >> 2);
+    const int hb = (col & 3) >> 1;
+    const int swr = chunk_swz_odd(ra);
+    uint32_t pv_base[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        pv_base[r] = (ra * AB_CPR + ((2 * r + hb) ^ swr)) * 16 + (col & 1) * 8 + half * 512;
+    const uint32_t lds_tiles = lds_addr(sm.u.tile[0]);
 
     // The block's share of the selected set is ranks [r0, r1) in ascending
     // key order, read out in batches of AB_LIST keys.  The bitmap shares LDS
@@ -194,54 +243,95 @@ __global__ __launch_bounds__(AB_NT) void attend_gather_kernel(
         for (int wd = w0; wd < w1; ++wd)
             cnt += __popc(sm.u.bitmap[wd]);
         int total;
-        const int before = block_exclusive_scan<AB_NT>(cnt, sm.wave_tot, total);
+        const int before = block_exclusive_scan<AB_NT>(cnt, sm_wave_tot, total);
         const int r0 = (int)(((int64_t)total * split) / splits);
         const int r1 = (int)(((int64_t)total * (split + 1)) / splits);
         const int rb = r0 + batch * AB_LIST;
         if (rb >= r1)
             break;
         const int re = min(rb + AB_LIST, r1);
-        extract_keys(sm.u.bitmap, w0, w1, before, rb, re, sm.list);
+        extract_keys(sm.u.bitmap, w0, w1, before, rb, re, sm_list);
         __syncthreads();
         const int n_my = re - rb;
         const int ntiles = (n_my + AB_TILE - 1) / AB_TILE;
+        // the Q fragments (and anything else loaded so far) are in registers
+        // before the first tile DMA, so no later wait is needed for them
+        vm_wait<0>();
 
-        dma_tile(sm.u.tile[0], 0, min(AB_TILE, n_my));
+        // ring of AB_STAGES tiles: tiles t+1 .. t+AB_STAGES-1 are in flight
+        // while tile t is consumed
+        for (int s = 0; s < AB_STAGES - 1 && s < ntiles; ++s)
+            dma_tile(sm.u.tile[s], s * AB_TILE, min(AB_TILE, n_my - s * AB_TILE));
         for (int t = 0; t < ntiles; ++t) {
             const int t0 = t * AB_TILE;
             const int nvalid = min(AB_TILE, n_my - t0);
-            // tile t has landed (own DMA) and is visible to all waves
-            lds_dma_wait();
-            __syncthreads();
-            if (t + 1 < ntiles)
-                dma_tile(sm.u.tile[(t + 1) & 1], t0 + AB_TILE, min(AB_TILE, n_my - t0 - AB_TILE));
-            const unsigned char *T = sm.u.tile[t & 1];
-            const u32x4_t *T16 = reinterpret_cast<const u32x4_t *>(T);
+            // tile t has landed (this wave's DMA; the later tiles may still fly)
+            const int after = min(ntiles - 1, t + AB_STAGES - 2) - t;
+            if (wid < AB_NW / 2)
+                vm_wait_tiles<AB_DMA_HI>(after);
+            else
+                vm_wait_tiles<AB_DMA_LO>(after);
+            lds_barrier();  // ... for every wave, and tile t-1's buffer is free
+            const int tn = t + AB_STAGES - 1;
+            if (tn < ntiles)
+                dma_tile(sm.u.tile[tn % AB_STAGES], tn * AB_TILE,
+                         min(AB_TILE, n_my - tn * AB_TILE));
+            const int toff = (t % AB_STAGES) * AB_TILEB;
 
-            // ---- S^T[key][head]: keys 0-15 (s0) and 16-31 (s1), two chains each
+            // ---- partial S^T[key][head] over this wave's 9 k-steps: keys
+            //      0-15 (s0) and 16-31 (s1), two chains each; operands read in
+            //      groups of 3 k-steps
             f32x4_t s0a = {0.f, 0.f, 0.f, 0.f}, s0b = s0a, s1a = s0a, s1b = s0a;
+            {
+                const uint32_t kb = lds_tiles + toff + qk_base;
+                constexpr int R16 = 16 * AB_ROWB;  // rows 16..31
+                auto qk_group = [&](auto J, const u32x4_t(&a)[6]) {
+                    constexpr int j = decltype(J)::value;
 #pragma unroll
-            for (int ks = 0; ks < AB_KS; ks += 2) {
-                const u32x4_t a0 = T16[ab_chunk(col, 4 * ks + g)];
-                const u32x4_t a1 = T16[ab_chunk(16 + col, 4 * ks + g)];
-                const u32x4_t a2 = T16[ab_chunk(col, 4 * (ks + 1) + g)];
-                const u32x4_t a3 = T16[ab_chunk(16 + col, 4 * (ks + 1) + g)];
-                s0a = mfma_16x16x32(a0, qf[ks], s0a);
-                s1a = mfma_16x16x32(a1, qf[ks], s1a);
-                s0b = mfma_16x16x32(a2, qf[ks + 1], s0b);
-                s1b = mfma_16x16x32(a3, qf[ks + 1], s1b);
+                    for (int u = 0; u < 3; ++u) {
+                        const int m = 3 * j + u;
+                        if (m & 1) {
+                            s0b = mfma_16x16x32(a[2 * u], qf[m], s0b);
+                            s1b = mfma_16x16x32(a[2 * u + 1], qf[m], s1b);
+                        } else {
+                            s0a = mfma_16x16x32(a[2 * u], qf[m], s0a);
+                            s1a = mfma_16x16x32(a[2 * u + 1], qf[m], s1a);
+                        }
+                    }
+                };
+                u32x4_t a[6];
+                lds_read_b128_x6<0, R16>(a, kb);
+                qk_group(std::integral_constant<int, 0>{}, a);
+                lds_read_b128_x6<384, R16>(a, kb);
+                qk_group(std::integral_constant<int, 1>{}, a);
+                lds_read_b128_x6<768, R16>(a, kb);
+                qk_group(std::integral_constant<int, 2>{}, a);
             }
-            const f32x4_t s0 = s0a + s0b, s1 = s1a + s1b;
+            f32x4_t s0 = s0a + s0b, s1 = s1a + s1b;
+            // ---- add the partner's partial (same lane layout); a + b == b + a,
+            //      so both waves hold bit-identical scores
+            sm_xs[wid][0][lane] = s0;
+            sm_xs[wid][1][lane] = s1;
+            lds_barrier();
+            s0 += sm_xs[wid ^ (AB_NW / 2)][0][lane];
+            s1 += sm_xs[wid ^ (AB_NW / 2)][1][lane];
 
             // ---- online softmax (log2 domain); lane's keys: 4g+i and 16+4g+i
             float x0[4], x1[4];
-            float tmax = -INFINITY;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                x0[i] = (4 * g + i < nvalid) ? s0[i] * scale_log2 : -INFINITY;
-                x1[i] = (16 + 4 * g + i < nvalid) ? s1[i] * scale_log2 : -INFINITY;
-                tmax = fmaxf(tmax, fmaxf(x0[i], x1[i]));
+                x0[i] = s0[i] * scale_log2;
+                x1[i] = s1[i] * scale_log2;
             }
+            if (nvalid < AB_TILE) {  // ragged last tile: rows past the end are padding
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    x0[i] = (4 * g + i < nvalid) ? x0[i] : -INFINITY;
+                    x1[i] = (16 + 4 * g + i < nvalid) ? x1[i] : -INFINITY;
+                }
+            }
+            float tmax = fmaxf(fmaxf(fmaxf(x0[0], x0[1]), fmaxf(x0[2], x0[3])),
+                               fmaxf(fmaxf(x1[0], x1[1]), fmaxf(x1[2], x1[3])));
             tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
             tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
             // Lazy rescale: the reference max only moves when the tile max
@@ -265,50 +355,51 @@ __global__ __launch_bounds__(AB_NT) void attend_gather_kernel(
             }
             // m_run is -inf only while every key seen so far (this tile
             // included) is masked; then all x are -inf and p must be 0.
+            // x - m_ref <= kRescaleLog2, so the hardware exp2 (no denormal
+            // results) is all that is needed.
             const float m_ref = (m_run == -INFINITY) ? 0.f : m_run;
-            float p0[4], p1[4];
-            float psum = 0.f;
+            float p[8];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                p0[i] = exp2f(x0[i] - m_ref);
-                p1[i] = exp2f(x1[i] - m_ref);
-                psum += p0[i] + p1[i];
+                p[i] = __builtin_amdgcn_exp2f(x0[i] - m_ref);
+                p[4 + i] = __builtin_amdgcn_exp2f(x1[i] - m_ref);
             }
-            l_part += psum;
+            l_part += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
             // ---- P^T fragments (B operand): element j <-> key 4g+j (j < 4),
             //      16+4g+(j-4) (j >= 4); two-term bf16 split
             u32x4_t bhi, blo;
             {
-                float h0[4], h1[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    h0[i] = bf16_bits_to_f32(f32_to_bf16_bits(p0[i]));
-                    h1[i] = bf16_bits_to_f32(f32_to_bf16_bits(p1[i]));
-                }
-                bhi = u32x4_t{pack_bf16x2(h0[0], h0[1]), pack_bf16x2(h0[2], h0[3]),
-                              pack_bf16x2(h1[0], h1[1]), pack_bf16x2(h1[2], h1[3])};
-                blo = u32x4_t{pack_bf16x2(p0[0] - h0[0], p0[1] - h0[1]),
-                              pack_bf16x2(p0[2] - h0[2], p0[3] - h0[3]),
-                              pack_bf16x2(p1[0] - h1[0], p1[1] - h1[1]),
-                              pack_bf16x2(p1[2] - h1[2], p1[3] - h1[3])};
+                uint32_t h[4], l[4];
+                split_bf16x8(p, h, l);
+                bhi = u32x4_t{h[0], h[1], h[2], h[3]};
+                blo = u32x4_t{l[0], l[1], l[2], l[3]};
             }
-            // ---- O^T[c][head] += V^T[c][keys] P^T[keys][head]; the V^T
-            //      fragment of column c = n*16+col is read transposed from the
-            //      row-major tile: source lane col = a + 4j points at row
-            //      4g + j (then 16 + 4g + j), columns n*16 + 4a .. + 3.
+            // ---- O^T[c][head] += V^T[c][keys] P^T[keys][head], 8 column tiles
+            //      per group: 16 transposing reads, then the hi terms of all 8
+            //      tiles and the lo terms, so no MFMA waits on its predecessor.
             {
-                const int ra = 4 * g + (col >> 2);
-                const int a8 = (col & 3) * 8;            // byte offset of 4 columns
+                const uint32_t tb = lds_tiles + toff;
+                const uint32_t b0 = tb + pv_base[0], b1 = tb + pv_base[1];
+                const uint32_t b2 = tb + pv_base[2], b3 = tb + pv_base[3];
+                auto pv_group = [&](auto M, const u32x2_t(&va)[8], const u32x2_t(&vb)[8]) {
+                    constexpr int m = decltype(M)::value;
+                    u32x4_t av[8];
 #pragma unroll
-                for (int n = 0; n < AB_NC; ++n) {
-                    const int lc = 2 * n + (a8 >> 4);    // logical 16-byte chunk
-                    const u32x2_t va = lds_read_tr16x4(T + ab_chunk(ra, lc) * 16 + (a8 & 8));
-                    const u32x2_t vb =
-                        lds_read_tr16x4(T + ab_chunk(16 + ra, lc) * 16 + (a8 & 8));
-                    const u32x4_t av = u32x4_t{va[0], va[1], vb[0], vb[1]};
-                    oacc[n] = mfma_16x16x32(av, bhi, oacc[n]);
-                    oacc[n] = mfma_16x16x32(av, blo, oacc[n]);
-                }
+                    for (int r = 0; r < 8; ++r)
+                        av[r] = u32x4_t{va[r][0], va[r][1], vb[r][0], vb[r][1]};
+#pragma unroll
+                    for (int r = 0; r < 8; ++r)
+                        oacc[8 * m + r] = mfma_16x16x32(av[r], bhi, oacc[8 * m + r]);
+#pragma unroll
+                    for (int r = 0; r < 8; ++r)
+                        oacc[8 * m + r] = mfma_16x16x32(av[r], blo, oacc[8 * m + r]);
+                };
+                constexpr int ROW16 = 16 * AB_ROWB;
+                u32x2_t va[8], vb[8];
+                lds_read_tr16x4_x16<0, 128, ROW16>(va, vb, b0, b1, b2, b3);
+                pv_group(std::integral_constant<int, 0>{}, va, vb);
+                lds_read_tr16x4_x16<256, 384, ROW16>(va, vb, b0, b1, b2, b3);
+                pv_group(std::integral_constant<int, 1>{}, va, vb);
             }
         }
         __syncthreads();  // last tile consumed before the bitmap reuses LDS
@@ -319,20 +410,20 @@ __global__ __launch_bounds__(AB_NT) void attend_gather_kernel(
     l_tot += __shfl_xor(l_tot, 32, kWave);
     if (splits == 1) {
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        float *op = out + ((int64_t)row * AB_H + head) * AB_VD + 4 * g;
+        float *op = out + ((int64_t)row * AB_H + head) * AB_VD + half * (AB_VD / 2) + 4 * g;
 #pragma unroll
         for (int n = 0; n < AB_NC; ++n)
             *reinterpret_cast<f32x4_t *>(op + n * 16) = oacc[n] * inv;
-        if (lse && g == 0)
+        if (lse && half == 0 && g == 0)
             lse[(int64_t)row * AB_H + head] =
                 l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
     } else {
         const int64_t pr_ = ((int64_t)row * splits + split) * AB_H + head;
-        float *op = ws_o + pr_ * AB_VD + 4 * g;
+        float *op = ws_o + pr_ * AB_VD + half * (AB_VD / 2) + 4 * g;
 #pragma unroll
         for (int n = 0; n < AB_NC; ++n)
             *reinterpret_cast<f32x4_t *>(op + n * 16) = oacc[n];
-        if (g == 0) {
+        if (half == 0 && g == 0) {
             ws_ml[pr_ * 2] = l_tot > 0.f ? m_run : -INFINITY;
             ws_ml[pr_ * 2 + 1] = l_tot;
         }
