@@ -42,6 +42,53 @@ WORKLOAD_TEXT = {
 }
 
 
+# short workload names (file names under profiles/)
+WORKLOAD_NAME = {1: "tiny_fp32_64", 2: "decode_b32x8192", 3: "prefill_4096",
+                 4: "decode_b8x131072_fp8", 5: "pooled_b4x16384"}
+
+# the kernels each ABI call of a stage launches (substrings of their names)
+STAGE_KERNELS = {
+    "index": ("index_scores",),
+    "topk": ("topk_rows_kernel", "topk_merge_kernel"),
+    "attend": ("attend_gather_kernel", "attend_combine_kernel", "topk_to_mask_kernel",
+               "attend_masked_kernel", "attend_plain_kernel"),
+    "pool_keys": ("pool_keys_kernel", "pool_counts_kernel"),
+    "pool_select": ("pool_select_kernel",),
+}
+
+
+def measured_traffic(cfg, stage):
+    """HBM bytes per call of `stage` from the rocprofv3 counter record under
+    profiles/, or None when there is none or the kernel sources changed
+    since it was taken."""
+    from sparse_attention_scores_amd import profile_summary as ps
+    path = os.path.join(ROOT, "profiles", f"dsa_step_{WORKLOAD_NAME[cfg]}_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None, None
+    digest, ff, wf, kern = ps.read_traffic(path)
+    if digest != ps.source_digest() or ff is None or wf is None:
+        return None, os.path.relpath(path, ROOT)
+    tot, hit = 0.0, False
+    for name, (f, w) in kern.items():
+        if any(pat in name for pat in STAGE_KERNELS[stage]):
+            tot += f * 1024.0 * ff + w * 1024.0 * wf
+            hit = True
+    return (round(tot) if hit else None), os.path.relpath(path, ROOT)
+
+
+def copy_probe(mib):
+    """A plain streaming kernel of known traffic (y = -x over float32, `mib`
+    MiB each way): its counter readings calibrate FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    n = mib * (1 << 20) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    return n * 4
+
+
 def _parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -50,6 +97,8 @@ def _parse():
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=64, help="query rows in the oracle sample")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="also run a plain copy kernel of MIB MiB (counter calibration)")
     return ap.parse_args()
 
 
@@ -311,12 +360,17 @@ def main():
     if hbm_bound:
         ach = by / t / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4)}
     else:
         ach = fl / t / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFS,
-                "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFS, 4), "traffic": None}
+                "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFS, 4)}
+    traffic, tsrc = measured_traffic(cfg, dom)
+    roof["traffic"] = traffic
+    roof["traffic_record"] = tsrc
     roof["kernel"] = dom
+    roof["kernels"] = list(STAGE_KERNELS[dom])
+    roof["ms_per_launch"] = round(stage_ms[dom], 5)
     roof["alg_bytes_per_launch"] = by
     roof["alg_flops_per_launch"] = fl
     result = {
@@ -337,6 +391,8 @@ def main():
         "roofline": roof,
         "stages": per_stage,
     }
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
     if not args.no_cpu and cfg != 5:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_rows)

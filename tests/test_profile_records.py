@@ -1,0 +1,51 @@
+"""Host logic of the profile records: kernel-name shortening, the traffic
+record round trip and the source digest that invalidates stale records."""
+import os
+
+import bench
+from sparse_attention_scores_amd import profile_summary as ps
+
+
+def test_short_name_keeps_templates_drops_arguments():
+    n = "void dsa::topk_rows_kernel<1024, 16384, 0, 2>(float const*, int, int*) [clone .kd]"
+    assert ps.short_name(n) == "dsa::topk_rows_kernel<1024, 16384, 0, 2> [clone .kd]"
+    assert ps.short_name("dsa::attend_gather_kernel(unsigned short const*)") == "dsa::attend_gather_kernel"
+
+
+def test_traffic_record_round_trip(tmp_path):
+    fetch = tmp_path / "f.csv"
+    write = tmp_path / "w.csv"
+    hdr = "Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n"
+    fetch.write_text(hdr + "1,void at::native::neg_kernel_cuda(float),FETCH_SIZE,512\n"
+                     "2,dsa::attend_gather_kernel(int),FETCH_SIZE,100\n"
+                     "2,dsa::attend_gather_kernel(int),FETCH_SIZE,20\n"
+                     "3,dsa::attend_gather_kernel(int),FETCH_SIZE,120\n")
+    write.write_text(hdr + "1,void at::native::neg_kernel_cuda(float),WRITE_SIZE,1024\n"
+                     "2,dsa::attend_gather_kernel(int),WRITE_SIZE,8\n"
+                     "3,dsa::attend_gather_kernel(int),WRITE_SIZE,8\n")
+    text = ps.traffic(str(fetch), str(write), 1 << 20, "cmd f", "cmd w")
+    rec = tmp_path / "r.txt"
+    rec.write_text(text)
+    digest, ff, wf, kern = ps.read_traffic(str(rec))
+    assert digest == ps.source_digest()
+    assert abs(ff - 2.0) < 1e-9 and abs(wf - 1.0) < 1e-9
+    # per-dispatch averages: fetch (120 + 120) / 2, write 8
+    assert kern == {"dsa::attend_gather_kernel": (120.0, 8.0)}
+
+
+def test_bench_uses_record_only_for_current_sources(tmp_path, monkeypatch):
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    name = f"dsa_step_{bench.WORKLOAD_NAME[2]}_hbm_traffic.txt"
+    body = ("fetch_factor 2.0\nwrite_factor 1.0\n"
+            "kernel dsa::attend_gather_kernel fetch_kib 10.0 write_kib 1.0 dispatches 2\n"
+            "kernel dsa::attend_combine_kernel fetch_kib 4.0 write_kib 2.0 dispatches 2\n"
+            "kernel dsa::index_scores_mfma_kernel<128,1,1,1,false> fetch_kib 7.0 write_kib 0.0 dispatches 2\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    (prof / name).write_text(f"source_digest {ps.source_digest()}\n" + body)
+    t, src = bench.measured_traffic(2, "attend")
+    assert t == round((10 * 2 + 1 + 4 * 2 + 2) * 1024) and src.endswith(name)
+    (prof / name).write_text("source_digest 0000\n" + body)
+    assert bench.measured_traffic(2, "attend")[0] is None
+    os.remove(prof / name)
+    assert bench.measured_traffic(2, "attend") == (None, None)
