@@ -263,6 +263,20 @@ __device__ __forceinline__ int chunk_swz_odd(int row)
     return (((row >> 1) & 3) << 1) | ((row >> 3) & 1);
 }
 
+// XCD-aware block order.  The dispatcher deals consecutive workgroup ids
+// round-robin over the 8 XCDs (each with its own L2), so id b runs on XCD
+// b % 8.  This maps b to a logical index such that each XCD receives one
+// contiguous range of logical indices: blocks that share data (the splits
+// of one query row, and later the merge of that row) then share an L2.  A
+// bijection on [0, total) for any total.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_remap(int b, int total)
+{
+    const int per = total / kXcds, rem = total % kXcds;
+    const int x = b % kXcds, j = b / kXcds;
+    return (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + j;
+}
+
 // Order-preserving map of an f32 score to u32: larger score <=> larger key.
 // -0 is first folded onto +0 so that the two compare equal.
 __device__ __forceinline__ uint32_t score_order_key(float f)

@@ -158,8 +158,12 @@ __global__ __launch_bounds__(AB_NT) void attend_gather_kernel(
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, col = lane & 15;
     const int hg = wid & 3, half = wid >> 2;
-    const int row = blockIdx.x / splits;
-    const int split = blockIdx.x % splits;
+    // the splits of one row run on one XCD (shared q, idx and partials);
+    // without splits the rows keep launch order, which spreads the uneven
+    // causal rows evenly over the XCDs
+    const int lb = splits > 1 ? xcd_remap(blockIdx.x, gridDim.x) : blockIdx.x;
+    const int row = lb / splits;
+    const int split = lb % splits;
     const int64_t b = row / n_q;
 
     int lo = 0, hi = n_k;
@@ -430,38 +434,47 @@ __global__ __launch_bounds__(AB_NT) void attend_gather_kernel(
     }
 }
 
-// Merge the split partials of each (row, head): O = sum_s 2^(m_s - m) O_s / L.
-// One block per (row, head); each thread owns 4 consecutive columns.
-__global__ __launch_bounds__(128) void attend_combine_kernel(const float *__restrict__ ws_o,
-                                                             const float *__restrict__ ws_ml,
-                                                             float *__restrict__ out,
-                                                             float *__restrict__ lse, int H,
-                                                             int vd, int splits)
+// Merge the split partials of each (row, head):
+//   O = sum_s 2^(m_s - m) O_s / L,  L = sum_s 2^(m_s - m) l_s,  m = max_s m_s.
+// One block per (row, 4 heads), one wave per head; lane j owns columns
+// 8j .. 8j+7 of the 512, so every split's partial row is one coalesced 2 KB
+// read.  Blocks follow the gather kernel's XCD order, so a row's partials are
+// read back from the L2 they were written to.
+constexpr int CB_HEADS = 4;
+__global__ __launch_bounds__(64 * CB_HEADS) void attend_combine_kernel(
+    const float *__restrict__ ws_o, const float *__restrict__ ws_ml, float *__restrict__ out,
+    float *__restrict__ lse, int splits)
 {
-    const int row = blockIdx.x / H;
-    const int h = blockIdx.x % H;
-    float m = -INFINITY;
-    for (int s = 0; s < splits; ++s)
-        m = fmaxf(m, ws_ml[(((int64_t)row * splits + s) * H + h) * 2]);
-    float L = 0.f;
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int lb = xcd_remap(blockIdx.x, gridDim.x);
+    const int row = lb / (AB_H / CB_HEADS);
+    const int h = (lb % (AB_H / CB_HEADS)) * CB_HEADS + wid;
+    // lane s < splits holds split s's (m, l)
+    float ms = -INFINITY, ls = 0.f;
+    if (lane < splits) {
+        const int64_t pr = ((int64_t)row * splits + lane) * AB_H + h;
+        ms = ws_ml[pr * 2];
+        ls = ws_ml[pr * 2 + 1];
+    }
+    const float m = wave_max(ms);
+    const float wgt = (ms == -INFINITY) ? 0.f : exp2f(ms - m);
+    const float L = wave_sum(wgt * ls);
+    f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
     for (int s = 0; s < splits; ++s) {
-        const int64_t pr = ((int64_t)row * splits + s) * H + h;
-        const float ms = ws_ml[pr * 2];
-        L += (m == -INFINITY || ms == -INFINITY) ? 0.f : exp2f(ms - m) * ws_ml[pr * 2 + 1];
+        const float ws_ = __shfl(wgt, s, kWave);
+        if (ws_ != 0.f) {
+            const f32x4_t *src = reinterpret_cast<const f32x4_t *>(
+                ws_o + (((int64_t)row * splits + s) * AB_H + h) * AB_VD + 8 * lane);
+            a0 += ws_ * src[0];
+            a1 += ws_ * src[1];
+        }
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
-    for (int c = threadIdx.x * 4; c < vd; c += blockDim.x * 4) {
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-        for (int s = 0; s < splits; ++s) {
-            const int64_t pr = ((int64_t)row * splits + s) * H + h;
-            const float ms = ws_ml[pr * 2];
-            if (ms != -INFINITY)
-                acc += exp2f(ms - m) * *reinterpret_cast<const f32x4_t *>(ws_o + pr * vd + c);
-        }
-        *reinterpret_cast<f32x4_t *>(out + ((int64_t)row * H + h) * vd + c) = acc * inv;
-    }
-    if (lse && threadIdx.x == 0)
-        lse[(int64_t)row * H + h] = L > 0.f ? (m + log2f(L)) * kLn2 : -INFINITY;
+    f32x4_t *dst = reinterpret_cast<f32x4_t *>(out + ((int64_t)row * AB_H + h) * AB_VD + 8 * lane);
+    dst[0] = a0 * inv;
+    dst[1] = a1 * inv;
+    if (lse && lane == 0)
+        lse[(int64_t)row * AB_H + h] = L > 0.f ? (m + log2f(L)) * kLn2 : -INFINITY;
 }
 
 // ------------------------------------------------------------------ plain kernel
@@ -572,7 +585,8 @@ int attend_gather_splits(const AttendArgs &a)
     const int64_t rows = (int64_t)a.batch * a.n_q;
     int by_fill = (int)((256 + rows - 1) / rows);
     int by_work = max(1, min(a.n_sel, a.n_k) / 64);
-    return max(1, min(by_fill, by_work));
+    // the merge kernel keeps one split per lane
+    return max(1, min(min(by_fill, by_work), 64));
 }
 
 size_t attend_workspace_bytes(const AttendArgs &a)
@@ -609,8 +623,8 @@ hipError_t launch_attend(const AttendArgs &a, hipStream_t st)
         hipError_t e = hipGetLastError();
         if (e != hipSuccess || splits == 1)
             return e;
-        hipLaunchKernelGGL(attend_combine_kernel, dim3((unsigned)(rows * AB_H)), dim3(128), 0, st,
-                           ws_o, ws_ml, a.out, a.lse, AB_H, AB_VD, splits);
+        hipLaunchKernelGGL(attend_combine_kernel, dim3((unsigned)(rows * (AB_H / CB_HEADS))),
+                           dim3(64 * CB_HEADS), 0, st, ws_o, ws_ml, a.out, a.lse, splits);
         return hipGetLastError();
     }
     if (attend_masked_supported(a))

@@ -84,29 +84,54 @@ __global__ __launch_bounds__(NT) void topk_rows_kernel(const float *__restrict__
 
 // Second launch of the long-row path: select and sort among the chunk
 // winners ws[row][0 .. n_chunks*k).  Zero keys are padding; there are always
-// at least min(k, n_visible) real keys, and every real key is > 0.
-template <int NT, int EPT>
+// at least min(k, n_visible) real keys, and every real key is > 0.  With
+// CACHE the candidates (at most CACHE_KEYS) are first copied to LDS in one
+// batched pass, so the select passes re-read LDS instead of global memory.
+constexpr int kMergeCacheKeys = 16384;
+template <int NT, int EPT, bool CACHE>
 __global__ __launch_bounds__(NT) void topk_merge_kernel(const uint64_t *__restrict__ ws,
                                                         int n_chunks, int k,
                                                         int32_t *__restrict__ out)
 {
-    __shared__ TopkSmem<NT, 1> sm;
+    // CACHE: the 64-bit candidates live in sm.ord (two words each)
+    __shared__ TopkSmem<NT, CACHE ? 2 * kMergeCacheKeys : 1> sm;
     const int tid = threadIdx.x;
     const int row = blockIdx.x;
     const uint64_t *cand = ws + (int64_t)row * n_chunks * k;
     const int n = n_chunks * k;
-    // count the real candidates
+    uint64_t *cache = reinterpret_cast<uint64_t *>(sm.ord);
+    // count the real candidates (and fill the cache)
     if (tid == 0)
         sm.count = 0;
     __syncthreads();
     int local = 0;
-    for (int i = tid; i < n; i += NT)
-        local += cand[i] != 0ull;
+    if (CACHE) {
+        constexpr int U = 8;
+        for (int base = 0; base < n; base += NT * U) {
+            uint64_t v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int i = base + u * NT + tid;
+                v[u] = i < n ? cand[i] : 0ull;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int i = base + u * NT + tid;
+                if (i < n) {
+                    cache[i] = v[u];
+                    local += v[u] != 0ull;
+                }
+            }
+        }
+    } else {
+        for (int i = tid; i < n; i += NT)
+            local += cand[i] != 0ull;
+    }
     atomicAdd(&sm.count, local);
     __syncthreads();
     const int real = sm.count;
     __syncthreads();
-    auto key_at = [&](int i) -> uint64_t { return cand[i]; };
+    auto key_at = [&](int i) -> uint64_t { return CACHE ? cache[i] : cand[i]; };
     int m;
     if (real > k) {
         radix_select(sm, n, k, key_at);
@@ -116,7 +141,7 @@ __global__ __launch_bounds__(NT) void topk_merge_kernel(const uint64_t *__restri
             sm.count = 0;
         __syncthreads();
         for (int i = tid; i < n; i += NT) {
-            const uint64_t key = cand[i];
+            const uint64_t key = key_at(i);
             if (key != 0ull) {
                 const int pos = atomicAdd(&sm.count, 1);
                 sm.sel[pos] = key;
@@ -176,8 +201,12 @@ hipError_t launch_topk(const TopkArgs &a, hipStream_t st)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL((topk_merge_kernel<NT, 2>), dim3(a.rows), dim3(NT), 0, st,
-                       static_cast<const uint64_t *>(a.workspace), n_chunks, a.k, a.out);
+    if ((int64_t)n_chunks * a.k <= kMergeCacheKeys)
+        hipLaunchKernelGGL((topk_merge_kernel<NT, 2, true>), dim3(a.rows), dim3(NT), 0, st,
+                           static_cast<const uint64_t *>(a.workspace), n_chunks, a.k, a.out);
+    else
+        hipLaunchKernelGGL((topk_merge_kernel<NT, 2, false>), dim3(a.rows), dim3(NT), 0, st,
+                           static_cast<const uint64_t *>(a.workspace), n_chunks, a.k, a.out);
     return hipGetLastError();
 }
 

@@ -13,11 +13,21 @@ namespace dsa {
 
 constexpr int kTopkMaxK = 2048;
 
+// Radix histogram copies: waves add into copy (wave % HC) so that LDS
+// atomics on a popular bin are spread over HC addresses.
+template <int NT, int CAP>
+constexpr int topk_hist_copies()
+{
+    // the 16384-key merge cache leaves room for 4 copies only
+    return CAP > 16384 ? 4 : NT / 64;
+}
+
 template <int NT, int CAP>
 struct __attribute__((aligned(16))) TopkSmem {
+    static constexpr int HC = topk_hist_copies<NT, CAP>();
     uint32_t ord[CAP];          // order keys of the row (source = scores)
     uint64_t sel[kTopkMaxK];    // winners
-    uint32_t hist[256];
+    uint32_t hist[HC][256];
     uint64_t red_min[NT / 64];
     uint64_t red_max[NT / 64];
     int count;
@@ -36,6 +46,36 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int o)
     uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
     lo = (uint32_t)__shfl_xor((int)lo, o, kWave);
     hi = (uint32_t)__shfl_xor((int)hi, o, kWave);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// x[lane ^ o] for o a power of two below 64, without going through LDS where
+// the lane pattern allows: DPP quad permutations for 1 and 2, a quad
+// reversal followed by a half-row mirror for 4 (i ^ 3 ^ 7), a row mirror
+// followed by a half-row mirror for 8 (i ^ 15 ^ 7), ds_swizzle (xor mask
+// within 32 lanes, no memory access) for 16, ds_bpermute for 32.  `o` must
+// fold to a constant.
+__device__ __forceinline__ uint32_t lane_xor_u32(uint32_t x, int o)
+{
+    switch (o) {
+    case 1: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false);
+    case 2: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false);
+    case 4: {
+        const int y = __builtin_amdgcn_update_dpp(0, (int)x, 0x1B, 0xF, 0xF, false);
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, y, 0x141, 0xF, 0xF, false);
+    }
+    case 8: {
+        const int y = __builtin_amdgcn_update_dpp(0, (int)x, 0x140, 0xF, 0xF, false);
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, y, 0x141, 0xF, 0xF, false);
+    }
+    case 16: return (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, 0x401F);
+    default: return (uint32_t)__shfl_xor((int)x, o, kWave);
+    }
+}
+
+__device__ __forceinline__ uint64_t lane_xor_u64(uint64_t v, int o)
+{
+    const uint32_t lo = lane_xor_u32((uint32_t)v, o), hi = lane_xor_u32((uint32_t)(v >> 32), o);
     return ((uint64_t)hi << 32) | lo;
 }
 
@@ -80,13 +120,15 @@ __device__ void radix_select(TopkSmem<NT, CAP> &sm, int n, int k, KeyAt key_at)
         const int shift = top >= 7 ? top - 7 : 0;
         const int width = top - shift + 1;
         const uint32_t dmask = (1u << width) - 1u;
-        for (int i = tid; i < 256; i += NT)
-            sm.hist[i] = 0;
+        constexpr int HC = TopkSmem<NT, CAP>::HC;
+        for (int i = tid; i < 256 * HC; i += NT)
+            (&sm.hist[0][0])[i] = 0;
         __syncthreads();
+        uint32_t *hist = sm.hist[wid % HC];
         for (int i = tid; i < n; i += NT) {
             const uint64_t key = key_at(i);
             if ((key & mask) == prefix)
-                atomicAdd(&sm.hist[(uint32_t)(key >> shift) & dmask], 1u);
+                atomicAdd(&hist[(uint32_t)(key >> shift) & dmask], 1u);
         }
         __syncthreads();
         if (wid == 0) {
@@ -95,7 +137,11 @@ __device__ void radix_select(TopkSmem<NT, CAP> &sm, int n, int k, KeyAt key_at)
             int s = 0;
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                c[t] = (int)sm.hist[255 - 4 * lane - t];
+                int ct = 0;
+#pragma unroll
+                for (int h = 0; h < HC; ++h)
+                    ct += (int)sm.hist[h][255 - 4 * lane - t];
+                c[t] = ct;
                 s += c[t];
             }
             int above = wave_inclusive_scan(s) - s;
@@ -185,7 +231,7 @@ __device__ void bitonic_sort_regs(TopkSmem<NT, CAP> &sm, int m, uint64_t (&v)[EP
                 if (s / EPT < 64) {
 #pragma unroll
                     for (int b = 0; b < EPT; ++b)
-                        pv[b] = shfl_xor_u64(v[b], s / EPT);
+                        pv[b] = lane_xor_u64(v[b], s / EPT);
                 } else {
                     __syncthreads();
 #pragma unroll
@@ -211,13 +257,28 @@ __device__ void bitonic_sort_regs(TopkSmem<NT, CAP> &sm, int m, uint64_t (&v)[EP
     __syncthreads();
 }
 
-// Load scores[lo, hi) of one row into sm.ord and return n.
+// Load scores[lo, hi) of one row into sm.ord and return n.  Each thread
+// issues all of its loads of a round before it stores any, so a row costs one
+// or two memory round trips rather than one per element.
 template <int NT, int CAP>
 __device__ int load_row(TopkSmem<NT, CAP> &sm, const float *__restrict__ row, int lo, int hi)
 {
+    constexpr int U = (CAP / NT) < 8 ? (CAP / NT) : 8;
     const int n = max(hi - lo, 0);
-    for (int i = threadIdx.x; i < n; i += NT)
-        sm.ord[i] = score_order_key(row[lo + i]);
+    for (int base = 0; base < n; base += NT * U) {
+        float v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = base + u * NT + (int)threadIdx.x;
+            v[u] = i < n ? row[lo + i] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = base + u * NT + (int)threadIdx.x;
+            if (i < n)
+                sm.ord[i] = score_order_key(v[u]);
+        }
+    }
     __syncthreads();
     return n;
 }

@@ -116,6 +116,7 @@ TOPK_CASES = [
     (3, dict(Tq=300, Tk=300), None, 100),    # causal: k >= visible on early rows
     (4, dict(B=2, Tk=40000), None, 2048),    # > one block's cache: two-launch path
     (4, dict(B=1, Tk=40000), "tie", 2048),   # two-launch path with ties
+    (4, dict(B=1, Tk=150000), None, 2048),   # merge candidates beyond the LDS cache
 ]
 
 
