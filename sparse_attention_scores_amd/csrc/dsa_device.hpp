@@ -235,6 +235,28 @@ __device__ __forceinline__ void lds_read_b128_x6(u32x4_t (&a)[6], uint32_t base)
         : "memory");
 }
 
+// Eight 16-byte LDS reads and the wait for them: a[2j] from be + O + j*ROW,
+// a[2j+1] from bo + O + j*ROW, j < 4.
+template <int O, int ROW>
+__device__ __forceinline__ void lds_read_b128_x8(u32x4_t (&a)[8], uint32_t be, uint32_t bo)
+{
+    static_assert(O >= 0 && O + 3 * ROW < 65536, "ds offset is 16 bits");
+    asm volatile(
+        "ds_read_b128 %0, %8 offset:%10\n\t"
+        "ds_read_b128 %1, %9 offset:%10\n\t"
+        "ds_read_b128 %2, %8 offset:%11\n\t"
+        "ds_read_b128 %3, %9 offset:%11\n\t"
+        "ds_read_b128 %4, %8 offset:%12\n\t"
+        "ds_read_b128 %5, %9 offset:%12\n\t"
+        "ds_read_b128 %6, %8 offset:%13\n\t"
+        "ds_read_b128 %7, %9 offset:%13\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4]), "=&v"(a[5]),
+          "=&v"(a[6]), "=&v"(a[7])
+        : "v"(be), "v"(bo), "i"(O), "i"(O + ROW), "i"(O + 2 * ROW), "i"(O + 3 * ROW)
+        : "memory");
+}
+
 // 32-bit LDS byte address of a pointer into shared memory.
 __device__ __forceinline__ uint32_t lds_addr(const void *p)
 {
@@ -251,16 +273,16 @@ __device__ __forceinline__ int chunk_swz(int row)
     return ((row & 3) << 1) | ((row >> 2) & 1);
 }
 
-// Swizzle for tiles whose rows are an odd multiple of 128 bytes apart (e.g.
-// 1152-byte latent rows).  LDS has 64 banks of 4 bytes (256 bytes a cycle),
-// so rows r and r+1 start half a bank cycle apart and the XOR must separate
-// rows of equal parity: rows 0..15 at one logical chunk hit 16 different
-// 16-byte bank slots (a 16-lane ds_read_b128 group), and rows 0..7 (8..15)
-// at two adjacent logical chunks hit 16 different slots too (the 32 lanes
-// of one transposing ds_read_b64_tr_b16 cycle).
+// Swizzle for tiles whose rows are an odd multiple of 128 bytes apart (the
+// 1152-byte latent rows): physical chunk = logical chunk ^ (row & 7).  On
+// gfx950 (64 banks of 4 bytes) this keeps both access patterns of the
+// absorbed attention at full LDS rate, measured: the Q.K^T operand reads
+// (ds_read_b128, 16 rows x 4 chunk columns per instruction) and the
+// transposing P.V reads (ds_read_b64_tr_b16, 16 rows x 2 chunks); the
+// swizzles built for 32 lanes per cycle halve the ds_read_b128 rate.
 __device__ __forceinline__ int chunk_swz_odd(int row)
 {
-    return (((row >> 1) & 3) << 1) | ((row >> 3) & 1);
+    return row & 7;
 }
 
 // XCD-aware block order.  The dispatcher deals consecutive workgroup ids
@@ -318,6 +340,31 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
     for (int o = 32; o > 0; o >>= 1)
         v = max(v, (uint32_t)__shfl_xor((int)v, o, kWave));
     return v;
+}
+
+// max / sum over the four lanes l, l^16, l^32, l^48 (the four 16-lane rows)
+// with the gfx950 row-swap instructions: v_permlane16_swap pairs each lane
+// with its partner one row away, v_permlane32_swap with the partner half a
+// wave away; each returns both values of the pair, so a symmetric op of the
+// two is the reduction over the pair (no LDS round trip).
+__device__ __forceinline__ float max_across_rows(float v)
+{
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                    false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                    false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float sum_across_rows(float v)
+{
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                    false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                    false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave.

@@ -195,28 +195,34 @@ __global__ __launch_bounds__(AB_NT) void attend_gather_kernel(
         reinterpret_cast<const unsigned char *>(kv) + b * (int64_t)n_k * row_stride * 2;
 
     // DMA one tile: wave instruction s (1 KB) fills LDS bytes s*1024 + 16*lane
-    // = (row, physical chunk) from the logical chunk of that row's key.  The
-    // (row, byte offset) of each of this lane's slots is fixed; the keys are
-    // looked up first so the list reads overlap.
-    int dma_row[AB_DMA_HI], dma_off[AB_DMA_HI];
+    // = (row, physical chunk) from the logical chunk of that row's key.  Wave
+    // w issues instructions w + 8i for i < 4, and waves 0-3 also w + 32.  The
+    // (row, byte offset) of each of this lane's slots is fixed and packed in
+    // one register; the keys are looked up first so the list reads overlap.
+    // Offsets are 32-bit (the host keeps 2*row_stride below 2^31).
+    uint32_t dma_slot[AB_DMA_HI];
 #pragma unroll
     for (int i = 0; i < AB_DMA_HI; ++i) {
-        const int c = (wid + i * AB_NW) * 64 + lane;
-        dma_row[i] = c / AB_CPR;
-        dma_off[i] = ((c % AB_CPR) ^ chunk_swz_odd(c / AB_CPR)) * 16;
+        const int c = min(wid + i * AB_NW, AB_DMA - 1) * 64 + lane;
+        dma_slot[i] = ((uint32_t)(c / AB_CPR) << 16) |
+                      (uint32_t)(((c % AB_CPR) ^ chunk_swz_odd(c / AB_CPR)) * 16);
     }
-    const int64_t rs2 = row_stride * 2;
+    const uint32_t rs2 = (uint32_t)(row_stride * 2);
+    const bool dma_extra = wid < AB_DMA - AB_DMA_LO * AB_NW;
     auto dma_tile = [&](unsigned char *dst, int t0, int nvalid) {
+        const int32_t *lst = sm_list + t0;
         int key[AB_DMA_HI];
 #pragma unroll
         for (int i = 0; i < AB_DMA_HI; ++i)
-            if (wid + i * AB_NW < AB_DMA)
-                key[i] = sm_list[t0 + min(dma_row[i], nvalid - 1)];
+            key[i] = lst[min((int)(dma_slot[i] >> 16), nvalid - 1)];
 #pragma unroll
-        for (int i = 0; i < AB_DMA_HI; ++i)
-            if (wid + i * AB_NW < AB_DMA)
-                lds_dma16(kvb + (int64_t)key[i] * rs2 + dma_off[i],
-                          dst + (wid + i * AB_NW) * 1024);
+        for (int i = 0; i < AB_DMA_LO; ++i)
+            lds_dma16(kvb + (uint64_t)(uint32_t)key[i] * rs2 + (dma_slot[i] & 0xffffu),
+                      dst + (wid + i * AB_NW) * 1024);
+        if (dma_extra)
+            lds_dma16(kvb + (uint64_t)(uint32_t)key[AB_DMA_LO] * rs2 +
+                          (dma_slot[AB_DMA_LO] & 0xffffu),
+                      dst + (wid + AB_DMA_LO * AB_NW) * 1024);
     };
 
     // Per-lane LDS byte offsets inside a tile (constant over tiles).
@@ -336,8 +342,7 @@ __global__ __launch_bounds__(AB_NT) void attend_gather_kernel(
             }
             float tmax = fmaxf(fmaxf(fmaxf(x0[0], x0[1]), fmaxf(x0[2], x0[3])),
                                fmaxf(fmaxf(x1[0], x1[1]), fmaxf(x1[2], x1[3])));
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+            tmax = max_across_rows(tmax);
             // Lazy rescale: the reference max only moves when the tile max
             // exceeds it by more than kRescaleLog2, so p <= 2^kRescaleLog2
             // and the O accumulators are rarely touched.  Exact: l and O
@@ -410,8 +415,7 @@ __global__ __launch_bounds__(AB_NT) void attend_gather_kernel(
     }
 
     // ---- epilogue: l over the 4 lane groups of the head
-    float l_tot = l_part + __shfl_xor(l_part, 16, kWave);
-    l_tot += __shfl_xor(l_tot, 32, kWave);
+    const float l_tot = sum_across_rows(l_part);
     if (splits == 1) {
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
         float *op = out + ((int64_t)row * AB_H + head) * AB_VD + half * (AB_VD / 2) + 4 * g;
@@ -577,7 +581,8 @@ __global__ __launch_bounds__(PL_NT) void attend_plain_kernel(
 bool attend_gather_supported(const AttendArgs &a)
 {
     return !a.f32 && a.kv_heads == 1 && a.n_heads == AB_H && a.kd == AB_KD && a.vd == AB_VD &&
-           a.v == a.k && a.v_row_stride == a.k_row_stride && a.k_row_stride % 8 == 0;
+           a.v == a.k && a.v_row_stride == a.k_row_stride && a.k_row_stride % 8 == 0 &&
+           a.k_row_stride >= AB_KD && a.k_row_stride < (1ll << 30);
 }
 
 int attend_gather_splits(const AttendArgs &a)
