@@ -82,6 +82,34 @@ __global__ __launch_bounds__(NT) void topk_rows_kernel(const float *__restrict__
     }
 }
 
+// Whole row in one block, sorted output: 32-bit select, stable compaction,
+// stable radix sort (topk_device.hpp).
+template <int NT, int CAP>
+__global__ __launch_bounds__(NT) void topk_sorted_kernel(const float *__restrict__ scores,
+                                                         int n_cols, int64_t row_stride,
+                                                         const int32_t *__restrict__ vlo,
+                                                         const int32_t *__restrict__ vhi, int k,
+                                                         int32_t *__restrict__ out)
+{
+    __shared__ Topk32Smem<NT, CAP> sm;
+    const int tid = threadIdx.x;
+    const int row = blockIdx.x;
+    const int lo = max(vlo[row], 0), hi = min(vhi[row], n_cols);
+    uint32_t omin, omax;
+    const int n = load_row32(sm, scores + (int64_t)row * row_stride, lo, hi, omin, omax);
+    // n <= k: everything wins (mask 0 makes every key a candidate, all taken)
+    uint32_t prefix = 0u, mask = 0u;
+    int need = n, cand = n;
+    if (n > k)
+        select32(sm, n, k, omin, omax, prefix, mask, need, cand);
+    uint32_t wmin, wmax;
+    const int m = compact32(sm, n, lo, prefix, mask, need, cand, wmin, wmax);
+    const int buf = bucket_sort32(sm, m, wmin, wmax) ? 0 : sort32(sm, m, wmin, wmax);
+    int32_t *o = out + (int64_t)row * k;
+    for (int i = tid; i < k; i += NT)
+        o[i] = i < m ? (int32_t)sm.wcol[buf][i] : -1;
+}
+
 // Second launch of the long-row path: select and sort among the chunk
 // winners ws[row][0 .. n_chunks*k).  Zero keys are padding; there are always
 // at least min(k, n_visible) real keys, and every real key is > 0.  With
@@ -176,22 +204,14 @@ hipError_t launch_topk(const TopkArgs &a, hipStream_t st)
 {
     // sort sizes: NT threads x EPT keys >= k
     if (a.n_cols <= kCapSmall) {
-        constexpr int NT = 256;
-        if (a.k <= NT * 2)
-            hipLaunchKernelGGL((topk_rows_kernel<NT, kCapSmall, 0, 2>), dim3(a.rows), dim3(NT), 0,
-                               st, a.scores, a.n_cols, a.row_stride, a.vis_lo, a.vis_hi, a.k,
-                               a.out, nullptr, 1);
-        else
-            hipLaunchKernelGGL((topk_rows_kernel<NT, kCapSmall, 0, 8>), dim3(a.rows), dim3(NT), 0,
-                               st, a.scores, a.n_cols, a.row_stride, a.vis_lo, a.vis_hi, a.k,
-                               a.out, nullptr, 1);
+        hipLaunchKernelGGL((topk_sorted_kernel<512, kCapSmall>), dim3(a.rows), dim3(512), 0, st,
+                           a.scores, a.n_cols, a.row_stride, a.vis_lo, a.vis_hi, a.k, a.out);
         return hipGetLastError();
     }
     constexpr int NT = 1024;
     if (a.n_cols <= kCapLarge) {
-        hipLaunchKernelGGL((topk_rows_kernel<NT, kCapLarge, 0, 2>), dim3(a.rows), dim3(NT), 0, st,
-                           a.scores, a.n_cols, a.row_stride, a.vis_lo, a.vis_hi, a.k, a.out,
-                           nullptr, 1);
+        hipLaunchKernelGGL((topk_sorted_kernel<NT, kCapLarge>), dim3(a.rows), dim3(NT), 0, st,
+                           a.scores, a.n_cols, a.row_stride, a.vis_lo, a.vis_hi, a.k, a.out);
         return hipGetLastError();
     }
     const int n_chunks = (a.n_cols + kCapLarge - 1) / kCapLarge;

@@ -284,3 +284,458 @@ __device__ int load_row(TopkSmem<NT, CAP> &sm, const float *__restrict__ row, in
 }
 
 } // namespace dsa
+
+namespace dsa {
+
+// ---------------------------------------------------------------------------
+// Sorted top-k of one row on 32-bit order keys.
+//
+// The row's order keys sit in LDS in column order.  Rank order is "larger
+// order key first, then smaller column", so:
+//  1. a radix select over the 32-bit order keys finds the boundary: keys whose
+//     masked value is above the boundary prefix all win, and among the keys
+//     equal to it the first `need` in column order win;
+//  2. a stable compaction (ballots and wave totals, no atomics) writes the
+//     winners in column order;
+//  3. a stable LSD radix sort on the inverted order key (8-bit digits, only
+//     over the bits in which the winners differ) then leaves equal keys in
+//     column order, which is exactly the tie rule.
+template <int NT, int CAP>
+struct __attribute__((aligned(16))) Topk32Smem {
+    static constexpr int NW = NT / 64;
+    static constexpr int EPT = kTopkMaxK / NT;           // sort rounds (winners per thread)
+    static constexpr int NCNT = 256 * EPT * NW;          // (digit, round, wave) counters
+    static constexpr int NB = 2048;                      // bucket-sort buckets
+    static constexpr int R = CAP / NT;                   // compaction rounds
+    static_assert(CAP * 4 >= NCNT * 2 && CAP * 4 >= NB * 8, "sort arrays overlay the key cache");
+    static_assert(R <= 32, "round flags are kept in one 32-bit mask");
+    union {
+        uint32_t ord[CAP];        // order keys of the row, column order
+        uint16_t cnt[NCNT];       // radix-sort counters, after the compaction
+        struct {
+            uint32_t off[NB];     // bucket offsets
+            uint32_t fill[NB];    // bucket counts, then fill pointers
+        } bk;
+    } a;
+    int tab[2][R * NW + 1];       // (round, wave) counts -> exclusive prefixes, + total
+    uint32_t word[2][kTopkMaxK];  // winners' order keys (sort ping-pong)
+    uint32_t wcol[2][kTopkMaxK];  // winners' columns
+    uint32_t hist[NW][256];       // per-wave select histograms
+    int red[2][2][NW];            // per-wave totals (two round parities x two counts)
+    uint32_t mm[2][NW];           // per-wave min / max
+    int bin, above, bincnt;
+};
+
+// Load scores[lo, hi) into sm.a.ord (column order) and reduce their min/max.
+template <int NT, int CAP>
+__device__ int load_row32(Topk32Smem<NT, CAP> &sm, const float *__restrict__ row, int lo, int hi,
+                          uint32_t &omin, uint32_t &omax)
+{
+    constexpr int U = (CAP / NT) < 8 ? (CAP / NT) : 8;
+    constexpr int NW = NT / 64;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int n = max(hi - lo, 0);
+    uint32_t mn = ~0u, mx = 0u;
+    for (int base = 0; base < n; base += NT * U) {
+        float v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = base + u * NT + tid;
+            v[u] = i < n ? row[lo + i] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = base + u * NT + tid;
+            if (i < n) {
+                const uint32_t o = score_order_key(v[u]);
+                sm.a.ord[i] = o;
+                mn = min(mn, o);
+                mx = max(mx, o);
+            }
+        }
+    }
+    mn = wave_min_u32(mn);
+    mx = wave_max_u32(mx);
+    if (lane == 0) {
+        sm.mm[0][wid] = mn;
+        sm.mm[1][wid] = mx;
+    }
+    __syncthreads();
+    omin = sm.mm[0][0];
+    omax = sm.mm[1][0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+        omin = min(omin, sm.mm[0][w]);
+        omax = max(omax, sm.mm[1][w]);
+    }
+    __syncthreads();
+    return n;
+}
+
+// Boundary of the k largest of the n order keys in sm.a.ord (n > k >= 1):
+// keys with (ord & mask) > prefix win (k - need of them); of the `cand` keys
+// with (ord & mask) == prefix, the first `need` in column order win.
+template <int NT, int CAP>
+__device__ void select32(Topk32Smem<NT, CAP> &sm, int n, int k, uint32_t omin, uint32_t omax,
+                         uint32_t &prefix, uint32_t &mask, int &need, int &cand)
+{
+    constexpr int NW = NT / 64;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const uint32_t diff = omin ^ omax;
+    int top = diff ? 31 - __clz(diff) : -1;  // highest bit in which keys differ
+    mask = top >= 0 ? ~((2u << top) - 1u) : ~0u;
+    prefix = omin & mask;
+    need = k;
+    cand = n;
+    while (top >= 0) {
+        const int shift = top >= 7 ? top - 7 : 0;
+        const int width = top - shift + 1;
+        const uint32_t dmask = (1u << width) - 1u;
+        for (int i = tid; i < 256 * NW; i += NT)
+            (&sm.hist[0][0])[i] = 0u;
+        __syncthreads();
+        uint32_t *hist = sm.hist[wid];
+        for (int i = tid; i < n; i += NT) {
+            const uint32_t key = sm.a.ord[i];
+            if ((key & mask) == prefix)
+                atomicAdd(&hist[(key >> shift) & dmask], 1u);
+        }
+        __syncthreads();
+        if (wid == 0) {
+            // lane j owns bins 255-4j .. 252-4j (descending)
+            int c[4];
+            int s = 0;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                int ct = 0;
+#pragma unroll
+                for (int h = 0; h < NW; ++h)
+                    ct += (int)sm.hist[h][255 - 4 * lane - t];
+                c[t] = ct;
+                s += ct;
+            }
+            int above = wave_inclusive_scan(s) - s;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                if (above < need && need <= above + c[t]) {
+                    sm.bin = 255 - 4 * lane - t;
+                    sm.above = above;
+                    sm.bincnt = c[t];
+                }
+                above += c[t];
+            }
+        }
+        __syncthreads();
+        need -= sm.above;
+        cand = sm.bincnt;
+        prefix |= (uint32_t)sm.bin << shift;
+        mask |= dmask << shift;
+        __syncthreads();  // everyone has read sm.bin before the next pass
+        if (cand == need)
+            break;
+        top = shift - 1;
+    }
+}
+
+// Exclusive scan, in place, of tab[0 .. e) by wave 0 (e <= 256); the total
+// goes to tab[e].  Callers synchronise before and after.
+__device__ __forceinline__ void wave_scan_table(int *tab, int e)
+{
+    const int lane = threadIdx.x & 63;
+    int v[4], s = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        v[j] = 4 * lane + j < e ? tab[4 * lane + j] : 0;
+        s += v[j];
+    }
+    const int incl = wave_inclusive_scan(s);
+    int run = incl - s;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (4 * lane + j < e)
+            tab[4 * lane + j] = run;
+        run += v[j];
+    }
+    if (lane == 63)
+        tab[e] = incl;
+}
+
+// Stable compaction of the winners into sm.word[0] / sm.wcol[0] (column
+// order); returns their count (k when n > k, else n) and their min / max.
+// Element i = r*NT + tid is held by thread tid in round r, so column order
+// is (round, wave, lane): each thread keeps its per-round flags in a bit
+// mask, the (round, wave) counts are scanned once by one wave, and the
+// positions follow from ballots -- two barriers per counted quantity.
+template <int NT, int CAP>
+__device__ int compact32(Topk32Smem<NT, CAP> &sm, int n, int col0, uint32_t prefix, uint32_t mask,
+                         int need, int cand, uint32_t &wmin, uint32_t &wmax)
+{
+    constexpr int NW = NT / 64;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const uint64_t lt = (1ull << lane) - 1ull;
+    const int rounds = (n + NT - 1) / NT;
+    const int e = rounds * NW;
+    uint32_t abv = 0u, eqm = 0u;
+    for (int r = 0; r < rounds; ++r) {
+        const int i = r * NT + tid;
+        if (i < n) {
+            const uint32_t key = sm.a.ord[i] & mask;
+            abv |= (uint32_t)(key > prefix) << r;
+            eqm |= (uint32_t)(key == prefix) << r;
+        }
+    }
+    uint32_t winm = abv;
+    if (cand > need) {
+        // ties at the boundary: the first `need` candidates in column order win
+        for (int r = 0; r < rounds; ++r) {
+            const uint64_t cb = __ballot((eqm >> r) & 1u);
+            if (lane == 0)
+                sm.tab[0][r * NW + wid] = __popcll(cb);
+        }
+        __syncthreads();
+        if (wid == 0)
+            wave_scan_table(sm.tab[0], e);
+        __syncthreads();
+        for (int r = 0; r < rounds; ++r) {
+            const uint64_t cb = __ballot((eqm >> r) & 1u);
+            const int rank = sm.tab[0][r * NW + wid] + __popcll(cb & lt);
+            winm |= (uint32_t)(((eqm >> r) & 1u) && rank < need) << r;
+        }
+    } else {
+        winm |= eqm;  // the whole boundary group wins
+    }
+    for (int r = 0; r < rounds; ++r) {
+        const uint64_t wb = __ballot((winm >> r) & 1u);
+        if (lane == 0)
+            sm.tab[1][r * NW + wid] = __popcll(wb);
+    }
+    __syncthreads();
+    if (wid == 0)
+        wave_scan_table(sm.tab[1], e);
+    __syncthreads();
+    uint32_t mn = ~0u, mx = 0u;
+    for (int r = 0; r < rounds; ++r) {
+        const uint64_t wb = __ballot((winm >> r) & 1u);
+        if ((winm >> r) & 1u) {
+            const int i = r * NT + tid;
+            const uint32_t key = sm.a.ord[i];
+            const int pos = sm.tab[1][r * NW + wid] + __popcll(wb & lt);
+            sm.word[0][pos] = key;
+            sm.wcol[0][pos] = (uint32_t)(col0 + i);
+            mn = min(mn, key);
+            mx = max(mx, key);
+        }
+    }
+    const int total = sm.tab[1][e];
+    mn = wave_min_u32(mn);
+    mx = wave_max_u32(mx);
+    if (lane == 0) {
+        sm.mm[0][wid] = mn;
+        sm.mm[1][wid] = mx;
+    }
+    __syncthreads();
+    wmin = sm.mm[0][0];
+    wmax = sm.mm[1][0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+        wmin = min(wmin, sm.mm[0][w]);
+        wmax = max(wmax, sm.mm[1][w]);
+    }
+    return total;
+}
+
+// Bucket sort of the m winners (sm.word / sm.wcol buffer 0, column order) by
+// descending order key: buckets on the top (up to) 11 bits in which the
+// winners differ, then each winner's place inside its bucket by counting the
+// bucket's members that rank above it (larger key, or equal key and smaller
+// column).  The result replaces buffer 0.  Returns false, touching nothing
+// but the bucket arrays, when a bucket holds more than 64 winners (many
+// equal high bits): the caller then sorts with sort32.
+template <int NT, int CAP>
+__device__ bool bucket_sort32(Topk32Smem<NT, CAP> &sm, int m, uint32_t wmin, uint32_t wmax)
+{
+    using S = Topk32Smem<NT, CAP>;
+    constexpr int NB = S::NB, NW = S::NW, PB = NB / NT;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const uint32_t diff = wmin ^ wmax;
+    const int bits = diff ? 32 - __clz(diff) : 0;
+    if (bits == 0)
+        return true;  // all keys equal: column order is rank order
+    const int dbits = bits < 11 ? bits : 11;
+    const int shift = bits - dbits;
+    const uint32_t dmask = (1u << dbits) - 1u;
+    const int nb = 1 << dbits;
+    for (int i = tid; i < nb; i += NT)
+        sm.a.bk.fill[i] = 0u;
+    __syncthreads();
+    for (int i = tid; i < m; i += NT) {
+        const int bkt = nb - 1 - (int)((sm.word[0][i] >> shift) & dmask);  // descending
+        atomicAdd(&sm.a.bk.fill[bkt], 1u);
+    }
+    __syncthreads();
+    // exclusive scan of the nb counts (thread t owns PB consecutive buckets)
+    // and their maximum
+    {
+        uint32_t v[PB];
+        int s = 0, mx = 0;
+#pragma unroll
+        for (int j = 0; j < PB; ++j) {
+            const int bkt = tid * PB + j;
+            v[j] = bkt < nb ? sm.a.bk.fill[bkt] : 0u;
+            s += (int)v[j];
+            mx = max(mx, (int)v[j]);
+        }
+        const int incl = wave_inclusive_scan(s);
+        mx = (int)wave_max_u32((uint32_t)mx);
+        if (lane == 63) {
+            sm.tab[0][wid] = incl;
+            sm.tab[1][wid] = mx;
+        }
+        __syncthreads();
+        int before = incl - s;
+        int big = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            before += w < wid ? sm.tab[0][w] : 0;
+            big = max(big, sm.tab[1][w]);
+        }
+        if (big > 64)
+            return false;  // uniform: every thread read the same maximum
+#pragma unroll
+        for (int j = 0; j < PB; ++j) {
+            const int bkt = tid * PB + j;
+            if (bkt < nb) {
+                sm.a.bk.off[bkt] = (uint32_t)before;
+                sm.a.bk.fill[bkt] = (uint32_t)before;
+            }
+            before += (int)v[j];
+        }
+    }
+    __syncthreads();
+    // scatter into buffer 1 by bucket (order inside a bucket arbitrary), as
+    // composite keys (order key, complemented column): one 64-bit compare
+    // then decides the rank order
+    uint64_t *ck = reinterpret_cast<uint64_t *>(&sm.word[1][0]);  // word[1], wcol[0..1] region
+    static_assert(sizeof(sm.word[1]) + sizeof(sm.wcol) >= kTopkMaxK * 8, "composite key buffer");
+    uint64_t mine[S::EPT];
+    int mbkt[S::EPT];
+#pragma unroll
+    for (int r = 0; r < S::EPT; ++r) {
+        const int i = r * NT + tid;
+        mine[r] = 0ull;
+        mbkt[r] = 0;
+        if (i < m) {
+            const uint32_t key = sm.word[0][i];
+            mine[r] = ((uint64_t)key << 32) | (uint64_t)(0xffffffffu - sm.wcol[0][i]);
+            mbkt[r] = nb - 1 - (int)((key >> shift) & dmask);
+        }
+    }
+    __syncthreads();  // buffer 0's columns are read before the region is reused
+#pragma unroll
+    for (int r = 0; r < S::EPT; ++r)
+        if (r * NT + tid < m)
+            ck[atomicAdd(&sm.a.bk.fill[mbkt[r]], 1u)] = mine[r];
+    __syncthreads();
+    // place each winner inside its bucket: rank = members with a larger key
+#pragma unroll
+    for (int r = 0; r < S::EPT; ++r) {
+        if (r * NT + tid < m) {
+            const int b0 = (int)sm.a.bk.off[mbkt[r]], b1 = (int)sm.a.bk.fill[mbkt[r]];
+            int rank = 0;
+            for (int j = b0; j < b1; ++j)
+                rank += ck[j] > mine[r];
+            sm.word[0][b0 + rank] = (uint32_t)(mine[r] >> 32);
+            // columns go to buffer 0's column array only after every rank is
+            // known (it overlaps the composite keys)
+            mbkt[r] = b0 + rank;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < S::EPT; ++r)
+        if (r * NT + tid < m)
+            sm.wcol[0][mbkt[r]] = 0xffffffffu - (uint32_t)mine[r];
+    __syncthreads();
+    return true;
+}
+
+// Stable LSD radix sort of the m winners (sm.word / sm.wcol buffer 0) by
+// descending order key; returns the buffer that holds the result.
+template <int NT, int CAP>
+__device__ int sort32(Topk32Smem<NT, CAP> &sm, int m, uint32_t wmin, uint32_t wmax)
+{
+    using S = Topk32Smem<NT, CAP>;
+    constexpr int NW = S::NW, EPT = S::EPT, NCNT = S::NCNT;
+    constexpr int PER = NCNT / NT;  // counters scanned per thread
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const uint64_t lt = (1ull << lane) - 1ull;
+    const uint32_t diff = wmin ^ wmax;
+    const int bits = diff ? 32 - __clz(diff) : 0;
+    int src = 0;
+    for (int shift = 0; shift < bits; shift += 8) {
+        // zero the counters (as 32-bit words)
+        for (int i = tid; i < NCNT / 2; i += NT)
+            reinterpret_cast<uint32_t *>(sm.a.cnt)[i] = 0u;
+        __syncthreads();
+        int dig[EPT], rank[EPT];
+#pragma unroll
+        for (int r = 0; r < EPT; ++r) {
+            const int i = r * NT + tid;
+            const bool valid = i < m;
+            // inverted digit: larger keys first
+            const int d = valid ? 255 - (int)((sm.word[src][i] >> shift) & 255u) : 0;
+            uint64_t same = __ballot(valid);
+#pragma unroll
+            for (int b = 0; b < 8; ++b) {
+                const uint64_t bal = __ballot((d >> b) & 1);
+                same &= ((d >> b) & 1) ? bal : ~bal;
+            }
+            dig[r] = d;
+            rank[r] = __popcll(same & lt);
+            // the highest lane of each digit group records the group size
+            if (valid && (same >> lane) == 1ull)
+                sm.a.cnt[(d * EPT + r) * NW + wid] = (uint16_t)__popcll(same);
+        }
+        __syncthreads();
+        // exclusive scan over (digit, round, wave): thread t owns PER
+        // consecutive counters
+        {
+            uint32_t v[PER];
+            int s = 0;
+#pragma unroll
+            for (int j = 0; j < PER; ++j) {
+                v[j] = sm.a.cnt[tid * PER + j];
+                s += (int)v[j];
+            }
+            const int incl = wave_inclusive_scan(s);
+            if (lane == 63)
+                sm.red[0][0][wid] = incl;
+            __syncthreads();
+            int before = incl - s;
+#pragma unroll
+            for (int w = 0; w < NW; ++w)
+                before += w < wid ? sm.red[0][0][w] : 0;
+#pragma unroll
+            for (int j = 0; j < PER; ++j) {
+                sm.a.cnt[tid * PER + j] = (uint16_t)before;
+                before += (int)v[j];
+            }
+        }
+        __syncthreads();
+        // scatter
+#pragma unroll
+        for (int r = 0; r < EPT; ++r) {
+            const int i = r * NT + tid;
+            if (i < m) {
+                const int pos = (int)sm.a.cnt[(dig[r] * EPT + r) * NW + wid] + rank[r];
+                sm.word[src ^ 1][pos] = sm.word[src][i];
+                sm.wcol[src ^ 1][pos] = sm.wcol[src][i];
+            }
+        }
+        __syncthreads();
+        src ^= 1;
+    }
+    return src;
+}
+
+} // namespace dsa
