@@ -141,30 +141,42 @@ hipError_t launch_pool_keys(const PoolKeysArgs &a, hipStream_t st)
 // topk_pools + expand_selection ("Module glm5next_dsa_ref"): the top
 // select_k visible pools of each query in rank order (higher pooled score,
 // then smaller pool id), each expanded to its kpool token ids ascending, then
-// the visible tail, then INVALID to out_width.
-template <int NT, int CAP>
+// the visible tail, then INVALID to out_width.  The pools' 64-bit composite
+// keys are selected by radix passes and ordered by a bitonic sort.
+template <int NT, int CAP, int EPT>
 __global__ __launch_bounds__(NT) void pool_select_kernel(
     const float *__restrict__ scores, const int32_t *__restrict__ pad,
     const int32_t *__restrict__ q_pos, int32_t *__restrict__ out_tok,
     int32_t *__restrict__ out_pools, int n_q, int np_cols, int kpool, int select_k,
     int out_width)
 {
-    __shared__ Topk32Smem<NT, CAP> sm;
+    __shared__ TopkSmem<NT, CAP> sm;
     const int tid = threadIdx.x;
     const int row = blockIdx.x;
     const int b = row / n_q;
     const int p = pad[b];
     const int t = q_pos[row];
     const int n_full = t >= p ? min((t - p + 1) / kpool, np_cols) : 0;
-    uint32_t omin, omax;
-    const int n = load_row32(sm, scores + (int64_t)row * np_cols, 0, n_full, omin, omax);
-    uint32_t prefix = 0u, mask = 0u;
-    int need = n, cand = n;
-    if (n > select_k)
-        select32(sm, n, select_k, omin, omax, prefix, mask, need, cand);
-    uint32_t wmin, wmax;
-    const int m = compact32(sm, n, 0, prefix, mask, need, cand, wmin, wmax);
-    const int buf = bucket_sort32(sm, m, wmin, wmax) ? 0 : sort32(sm, m, wmin, wmax);
+    const int n = load_row(sm, scores + (int64_t)row * np_cols, 0, n_full);
+    auto key_at = [&](int i) -> uint64_t { return compose_key(sm.ord[i], (uint32_t)i); };
+    int m;
+    if (n > select_k) {
+        radix_select(sm, n, select_k, key_at);
+        m = select_k;
+    } else {
+        for (int i = tid; i < n; i += NT)
+            sm.sel[i] = key_at(i);
+        __syncthreads();
+        m = n;
+    }
+    {
+        uint64_t v[EPT];
+        bitonic_sort_regs<NT, EPT>(sm, m, v);
+#pragma unroll
+        for (int b = 0; b < EPT; ++b)
+            sm.sel[tid * EPT + b] = v[b];
+        __syncthreads();
+    }
     // expand_selection: pools' tokens (rank order), the visible tail, INVALID
     const int pool_toks = m * kpool;
     const int tail = t >= p ? (t + 1) - (p + n_full * kpool) : 0;
@@ -172,7 +184,7 @@ __global__ __launch_bounds__(NT) void pool_select_kernel(
     for (int i = tid; i < out_width; i += NT) {
         int v = -1;
         if (i < pool_toks) {
-            const int pool = (int)sm.wcol[buf][i / kpool];
+            const int pool = (int)(0xffffffffu - (uint32_t)sm.sel[i / kpool]);
             v = p + pool * kpool + i % kpool;
         } else if (i < pool_toks + tail) {
             v = p + n_full * kpool + (i - pool_toks);
@@ -182,7 +194,7 @@ __global__ __launch_bounds__(NT) void pool_select_kernel(
     if (out_pools) {
         int32_t *op = out_pools + (int64_t)row * select_k;
         for (int i = tid; i < select_k; i += NT)
-            op[i] = i < m ? (int32_t)sm.wcol[buf][i] : -1;
+            op[i] = i < m ? (int32_t)(0xffffffffu - (uint32_t)sm.sel[i]) : -1;
     }
 }
 
@@ -190,14 +202,18 @@ hipError_t launch_pool_select(const PoolSelectArgs &a, hipStream_t st)
 {
     const int np_cols = a.seq / a.kpool;
     const unsigned rows = (unsigned)(a.batch * a.n_q);
-#define DSA_POOL_SELECT(NT, CAP)                                                                   \
-    hipLaunchKernelGGL((pool_select_kernel<NT, CAP>), dim3(rows), dim3(NT), 0, st, a.scores,       \
+#define DSA_POOL_SELECT(NT, CAP, EPT)                                                              \
+    hipLaunchKernelGGL((pool_select_kernel<NT, CAP, EPT>), dim3(rows), dim3(NT), 0, st, a.scores,  \
                        a.pad, a.q_pos, a.out_tok, a.out_pools, a.n_q, np_cols, a.kpool,            \
                        a.select_k, a.out_width)
-    if (np_cols <= 4096)
-        DSA_POOL_SELECT(256, 4096);
-    else
-        DSA_POOL_SELECT(1024, 16384);
+    if (np_cols <= 4096) {
+        if (a.select_k <= 512)
+            DSA_POOL_SELECT(256, 4096, 2);
+        else
+            DSA_POOL_SELECT(256, 4096, 8);
+    } else {
+        DSA_POOL_SELECT(1024, 16384, 2);
+    }
 #undef DSA_POOL_SELECT
     return hipGetLastError();
 }

@@ -561,7 +561,11 @@ __device__ bool bucket_sort32(Topk32Smem<NT, CAP> &sm, int m, uint32_t wmin, uin
     const int bits = diff ? 32 - __clz(diff) : 0;
     if (bits == 0)
         return true;  // all keys equal: column order is rank order
-    const int dbits = bits < 11 ? bits : 11;
+    // about one bucket per winner (at least 64, at most NB)
+    int lg = 6;
+    while (lg < 11 && (1 << lg) < m)
+        ++lg;
+    const int dbits = bits < lg ? bits : lg;
     const int shift = bits - dbits;
     const uint32_t dmask = (1u << dbits) - 1u;
     const int nb = 1 << dbits;
