@@ -58,15 +58,91 @@ __global__ __launch_bounds__(256) void topk_to_mask_kernel(const int32_t *__rest
         mr[i] = bits[i];
 }
 
+// LDS row swizzles of the per-head tiles, chosen by measurement on gfx950
+// (both keep their access pattern at the full LDS rate):
+//  K rows (192 bf16 = 384 bytes = 24 chunks): physical chunk = logical ^
+//  ((row >> 1) & 7) -- the 32x32x16 operand reads (32 rows at one chunk);
+//  V rows (256 bf16 = 512 bytes = 32 chunks, so every row starts on bank 0):
+//  physical chunk = logical ^ (((row & 3) << 2) | ((row >> 2) & 3)) -- the
+//  transposing reads (4 rows x 2 chunks per 16 lanes).
+__device__ __forceinline__ int mk_swz_k(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int mk_swz_v(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+
+// Six 16-byte LDS reads with one base each and the wait for them (asm, for
+// the reason given at lds_read_tr16x4_x16).
+template <int O0, int O1, int O2, int O3, int O4, int O5>
+__device__ __forceinline__ void lds_read_b128_6(u32x4_t (&a)[6], uint32_t b0, uint32_t b1,
+                                                uint32_t b2, uint32_t b3, uint32_t b4,
+                                                uint32_t b5)
+{
+    asm volatile(
+        "ds_read_b128 %0, %6 offset:%12\n\t"
+        "ds_read_b128 %1, %7 offset:%13\n\t"
+        "ds_read_b128 %2, %8 offset:%14\n\t"
+        "ds_read_b128 %3, %9 offset:%15\n\t"
+        "ds_read_b128 %4, %10 offset:%16\n\t"
+        "ds_read_b128 %5, %11 offset:%17\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4]), "=&v"(a[5])
+        : "v"(b0), "v"(b1), "v"(b2), "v"(b3), "v"(b4), "v"(b5), "i"(O0), "i"(O1), "i"(O2),
+          "i"(O3), "i"(O4), "i"(O5)
+        : "memory");
+}
+
+// Eight transposing LDS reads (4 column tiles x rows ra / rb) and the wait.
+template <int O>
+__device__ __forceinline__ void lds_read_tr16x4_8(u32x2_t (&a)[8], uint32_t r0, uint32_t r1,
+                                                  uint32_t r2, uint32_t r3, uint32_t s0,
+                                                  uint32_t s1, uint32_t s2, uint32_t s3)
+{
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %1, %12 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %2, %9 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %3, %13 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %4, %10 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %5, %14 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %6, %11 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %7, %15 offset:%16\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4]), "=&v"(a[5]),
+          "=&v"(a[6]), "=&v"(a[7])
+        : "v"(r0), "v"(r1), "v"(r2), "v"(r3), "v"(s0), "v"(s1), "v"(s2), "v"(s3), "i"(O)
+        : "memory");
+}
+
+// Three 4-byte LDS reads and the wait (asm: the words arrive by direct-to-LDS
+// loads, and the compiler would otherwise wait for every such load in flight).
+__device__ __forceinline__ void lds_read_b32_3(uint32_t &x, uint32_t &y, uint32_t &z,
+                                               uint32_t ax, uint32_t ay, uint32_t az)
+{
+    asm volatile(
+        "ds_read_b32 %0, %3\n\t"
+        "ds_read_b32 %1, %4\n\t"
+        "ds_read_b32 %2, %5\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(x), "=&v"(y), "=&v"(z)
+        : "v"(ax), "v"(ay), "v"(az)
+        : "memory");
+}
+
+constexpr int MK_STAGES = 2;  // tiles resident in LDS (ring)
+
 template <int KD, int VD>
 struct __attribute__((aligned(16))) MaskedSmem {
     static constexpr int KB = 32 * KD * 2;  // K tile bytes (32 keys, row-major, swizzled)
     static constexpr int VB = 32 * VD * 2;  // V tile bytes
-    unsigned char k[2][KB];
-    unsigned char v[2][VB];
-    int red[8];
+    unsigned char k[MK_STAGES][KB];
+    unsigned char v[MK_STAGES][VB];
+    uint32_t mw[MK_STAGES][4][64];          // mask words of the tile: [wave][lane & 31]
 };
 
+// Per (sequence, head, block of 128 queries); wave w owns queries
+// q0 + 32w .. +31 (lane col = query, half g = lane >> 5).  Tiles of 32 keys
+// stream through a ring of MK_STAGES LDS tiles by direct-to-LDS loads, with the
+// queries' mask words for the tile riding along (one 4-byte load per lane);
+// each wave issues the same number of loads per tile (7 of the 28 K/V
+// instructions plus its mask words), so a counted wait finds its tile.
 template <int KD, int VD>
 __global__ __launch_bounds__(256) void attend_masked_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, int64_t ksr,
@@ -79,14 +155,18 @@ __global__ __launch_bounds__(256) void attend_masked_kernel(
     constexpr int NCT = VD / 32;     // output column tiles of 32
     constexpr int KCH = KD / 8;      // 16-byte chunks of a K row
     constexpr int VCH = VD / 8;      // 16-byte chunks of a V row
-    static_assert(KCH % 8 == 0 && VCH % 8 == 0, "rows must hold a multiple of 8 chunks");
+    static_assert(KD == 192 && VD == 256, "the swizzles and read groups are laid out for 192/256");
     using Sm = MaskedSmem<KD, VD>;
-    static_assert(Sm::KB % 1024 == 0 && Sm::VB % 1024 == 0, "tiles are whole DMA instructions");
+    constexpr int NKV = (Sm::KB + Sm::VB) / 1024;  // 28 K/V DMA instructions per tile
+    constexpr int PER = NKV / 4;                   // 7 per wave
+    static_assert(NKV % 4 == 0, "K/V DMA splits evenly over the waves");
     __shared__ Sm sm;
+    __shared__ int sm_red[8];
     DSA_LDS_ESCAPE(sm);
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wid = tid >> 6;
+    const int lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, col = lane & 31;
     // Head-major order: the query blocks of one (sequence, head) run together
     // and stream the same K/V tiles (served from L2/MALL after the first
@@ -114,12 +194,12 @@ __global__ __launch_bounds__(256) void attend_masked_kernel(
             mx = max(mx, __shfl_xor(mx, o, kWave));
         }
         if (lane == 0) {
-            sm.red[wid] = mn;
-            sm.red[4 + wid] = mx;
+            sm_red[wid] = mn;
+            sm_red[4 + wid] = mx;
         }
         __syncthreads();
-        lo = min(min(sm.red[0], sm.red[1]), min(sm.red[2], sm.red[3]));
-        hi = max(max(sm.red[4], sm.red[5]), max(sm.red[6], sm.red[7]));
+        lo = min(min(sm_red[0], sm_red[1]), min(sm_red[2], sm_red[3]));
+        hi = max(max(sm_red[4], sm_red[5]), max(sm_red[6], sm_red[7]));
     }
     const int t_begin = lo / 32;
     const int t_end = hi > lo ? (hi + 31) / 32 : t_begin;
@@ -143,128 +223,187 @@ __global__ __launch_bounds__(256) void attend_masked_kernel(
         reinterpret_cast<const unsigned char *>(k + (int64_t)b * n_k * ksr + (int64_t)kvh * KD);
     const unsigned char *vb =
         reinterpret_cast<const unsigned char *>(v + (int64_t)b * n_k * vsr + (int64_t)kvh * VD);
-    const uint32_t *mrow = mask + row * nw;
+    // mask words of this lane's query (lanes 32..63 repeat lanes 0..31; an
+    // invalid query reads a valid row of the batch and is never used)
+    const uint32_t *mrow =
+        mask + ((int64_t)b * n_q + min(q0 + wid * 32 + col, n_q - 1)) * nw;
 
-    // DMA the 32 K rows and 32 V rows of tile t (rows past n_k repeat the
-    // last key; they are masked out).
-    auto dma_tile = [&](int t, int par) {
-        const int k0 = t * 32;
-        for (int s = wid; s < (Sm::KB + Sm::VB) / 1024; s += 4) {
-            if (s < Sm::KB / 1024) {
-                const int c = s * 64 + lane;
-                const int r = c / KCH;
-                const int logical = (c % KCH) ^ chunk_swz(r);
-                const int key = min(k0 + r, n_k - 1);
-                lds_dma16(kb + ((int64_t)key * ksr) * 2 + logical * 16, sm.k[par] + s * 1024);
-            } else {
-                const int sv = s - Sm::KB / 1024;
-                const int c = sv * 64 + lane;
-                const int r = c / VCH;
-                const int logical = (c % VCH) ^ chunk_swz(r);
-                const int key = min(k0 + r, n_k - 1);
-                lds_dma16(vb + ((int64_t)key * vsr) * 2 + logical * 16, sm.v[par] + sv * 1024);
-            }
+    // DMA slots of this wave: instruction s = wid + 4i (i < 7) of the tile's
+    // 28 (12 for K, then 16 for V); row in bits 16+, byte offset in the low 16
+    uint32_t slot[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int s_ = wid + 4 * i;
+        if (s_ < Sm::KB / 1024) {
+            const int c = s_ * 64 + lane, r = c / KCH;
+            slot[i] = ((uint32_t)r << 16) | (uint32_t)(((c % KCH) ^ mk_swz_k(r)) * 16);
+        } else {
+            const int c = (s_ - Sm::KB / 1024) * 64 + lane, r = c / VCH;
+            slot[i] = ((uint32_t)r << 16) | (uint32_t)(((c % VCH) ^ mk_swz_v(r)) * 16);
         }
+    }
+    const uint32_t ksr2 = (uint32_t)(ksr * 2), vsr2 = (uint32_t)(vsr * 2);
+    auto dma_tile = [&](int t, int st) {
+        const int k0 = t * 32;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int s_ = wid + 4 * i;
+            const int key = min(k0 + (int)(slot[i] >> 16), n_k - 1);  // rows past n_k masked
+            if (s_ < Sm::KB / 1024)
+                lds_dma16(kb + (uint64_t)(uint32_t)key * ksr2 + (slot[i] & 0xffffu),
+                          sm.k[st] + s_ * 1024);
+            else
+                lds_dma16(vb + (uint64_t)(uint32_t)key * vsr2 + (slot[i] & 0xffffu),
+                          sm.v[st] + (s_ - Sm::KB / 1024) * 1024);
+        }
+        lds_dma4(mrow + t, sm.mw[st][wid]);
     };
 
-    if (t_begin < t_end)
-        dma_tile(t_begin, 0);
+    // per-lane LDS byte offsets inside a stage (constant over tiles)
+    //  Q.K^T: row col, logical chunk 2ks + g = 8(ks>>2) + (2(ks&3) + g):
+    //  one base per ks & 3, immediates 128 * (ks >> 2)
+    const int swk = mk_swz_k(col);
+    uint32_t kq[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        kq[j] = (col * KCH + ((2 * j + g) ^ swk)) * 16;
+    //  P.V: 16-lane group (gg, ch), lane i = a + 4j reads row kh*16 + 4gg + j
+    //  (ra) and ra + 8 (rb), logical chunk 4n + c' with c' = 2ch + (a >> 1),
+    //  byte 8(a & 1): 16(n >> 2) + ((4(n & 3) + c') ^ swz) -- one base per
+    //  (row, n & 3), immediates 256 * (n >> 2) and 16 rows * 512 for kh
+    const int grp = lane >> 4, gg = grp >> 1, ch = grp & 1;
+    const int li = lane & 15, la = li & 3, lj = li >> 2;
+    const int ra = 4 * gg + lj, rb = ra + 8;
+    const int cp = 2 * ch + (la >> 1);
+    uint32_t va_[4], vb_[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        va_[j] = (ra * VCH + ((4 * j + cp) ^ mk_swz_v(ra))) * 16 + 8 * (la & 1);
+        vb_[j] = (rb * VCH + ((4 * j + cp) ^ mk_swz_v(rb))) * 16 + 8 * (la & 1);
+    }
+    const uint32_t lds_k = lds_addr(sm.k[0]), lds_v = lds_addr(sm.v[0]);
+
+    // the Q fragments and ranges are in registers before the first tile DMA
+    vm_wait<0>();
+    for (int j = 0; j < MK_STAGES - 1 && t_begin + j < t_end; ++j)
+        dma_tile(t_begin + j, j);
     for (int t = t_begin; t < t_end; ++t) {
-        const int par = (t - t_begin) & 1;
-        const uint32_t word = q_ok ? mrow[t] : 0u;
-        lds_dma_wait();
-        const bool any = __syncthreads_or(word != 0u);  // also: tile t visible to all
-        if (t + 1 < t_end)
-            dma_tile(t + 1, par ^ 1);
-        if (any) {
-            const u32x4_t *K16 = reinterpret_cast<const u32x4_t *>(sm.k[par]);
-            const unsigned char *Vt = sm.v[par];
-            // ---- S^T[key][query] for the 32 keys of the tile
-            f32x16_t sa = {}, sb = {};
+        const int st = (t - t_begin) % MK_STAGES;
+        // this wave's part of tile t has landed (later tiles may still fly)
+        vm_wait_tiles<PER + 1>(min(t_end - 1, t + MK_STAGES - 2) - t);
+        lds_barrier();  // ... every wave's, and tile t-1's stage is free
+        if (t + MK_STAGES - 1 < t_end)
+            dma_tile(t + MK_STAGES - 1, (t - t_begin + MK_STAGES - 1) % MK_STAGES);
+        uint32_t word, w0, w1;
+        {
+            const uint32_t mb = lds_addr(&sm.mw[st][0][0]) + 4 * col;
+            lds_read_b32_3(word, w0, w1, mb + 256 * wid, mb + 256 * g, mb + 256 * (2 + g));
+        }
+        // skip the tile when none of the block's 128 queries selects a key in it
+        if (!__any((w0 | w1) != 0u))
+            continue;
+        // ---- S^T[key][query] for the 32 keys of the tile
+        f32x16_t s = {};
+        {
+            const uint32_t kt = lds_k + st * Sm::KB;
+            u32x4_t a6[6];
+            lds_read_b128_6<0, 0, 0, 0, 128, 128>(a6, kt + kq[0], kt + kq[1], kt + kq[2],
+                                                  kt + kq[3], kt + kq[0], kt + kq[1]);
 #pragma unroll
-            for (int ks = 0; ks < KS; ks += 2) {
-                sa = mfma_32x32x16(K16[col * KCH + ((2 * ks + g) ^ chunk_swz(col))], qf[ks], sa);
-                if (ks + 1 < KS)
-                    sb = mfma_32x32x16(K16[col * KCH + ((2 * ks + 2 + g) ^ chunk_swz(col))],
-                                       qf[ks + 1], sb);
+            for (int j = 0; j < 6; ++j)
+                s = mfma_32x32x16(a6[j], qf[j], s);
+            lds_read_b128_6<128, 128, 256, 256, 256, 256>(a6, kt + kq[2], kt + kq[3], kt + kq[0],
+                                                          kt + kq[1], kt + kq[2], kt + kq[3]);
+#pragma unroll
+            for (int j = 0; j < 6; ++j)
+                s = mfma_32x32x16(a6[j], qf[6 + j], s);
+        }
+        // lane holds keys 8*(i/4) + 4g + i%4 of the tile for query qi
+        float x[16];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int kk = 8 * (i / 4) + 4 * g + (i % 4);
+            x[i] = ((word >> kk) & 1u) ? s[i] * scale_log2 : -INFINITY;
+            tmax = fmaxf(tmax, x[i]);
+        }
+        {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax),
+                                                             __float_as_uint(tmax), false, false);
+            tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        }
+        // lazy rescale (see the gather kernel): p <= 2^kRescaleLog2
+        const bool grow = tmax > m_run + kRescaleLog2;
+        if (__any(grow)) {
+            const float m_new = grow ? tmax : m_run;
+            // lanes that do not grow keep alpha = 1 (m_run may still be -inf
+            // there, and -inf - -inf would be NaN); a growing lane with
+            // m_run = -inf gets 0
+            const float alpha = grow ? exp2f(m_run - m_new) : 1.f;
+            if (__any(grow && m_run != -INFINITY)) {
+#pragma unroll
+                for (int n = 0; n < NCT; ++n)
+                    oacc[n] *= alpha;
             }
-            const f32x16_t s = sa + sb;
-            // lane holds keys 8*(i/4) + 4g + i%4 of the tile for query qi
-            float x[16];
-            float tmax = -INFINITY;
+            l_part *= alpha;
+            m_run = m_new;
+        }
+        // m_run is -inf only while every key seen so far (this tile
+        // included) is masked; then all x are -inf and p must be 0.
+        const float m_ref = (m_run == -INFINITY) ? 0.f : m_run;
+        float p[16];
+        float psum = 0.f;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int kk = 8 * (i / 4) + 4 * g + (i % 4);
-                x[i] = ((word >> kk) & 1u) ? s[i] * scale_log2 : -INFINITY;
-                tmax = fmaxf(tmax, x[i]);
-            }
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-            // lazy rescale (see the gather kernel): p <= 2^kRescaleLog2
-            const bool grow = tmax > m_run + kRescaleLog2;
-            if (__any(grow)) {
-                const float m_new = grow ? tmax : m_run;
-                // lanes that do not grow keep alpha = 1 (m_run may still be -inf
-                // there, and -inf - -inf would be NaN); a growing lane with
-                // m_run = -inf gets 0
-                const float alpha = grow ? exp2f(m_run - m_new) : 1.f;
-                if (__any(grow && m_run != -INFINITY)) {
+        for (int i = 0; i < 16; ++i) {
+            p[i] = __builtin_amdgcn_exp2f(x[i] - m_ref);
+            psum += p[i];
+        }
+        l_part += psum;
+        // ---- O^T[c][query] += V^T[c][keys] P^T[keys][query], per 16-key half
+        const uint32_t vt = lds_v + st * Sm::VB;
 #pragma unroll
-                    for (int n = 0; n < NCT; ++n)
-                        oacc[n] *= alpha;
-                }
-                l_part *= alpha;
-                m_run = m_new;
-            }
-            // m_run is -inf only while every key seen so far (this tile
-            // included) is masked; then all x are -inf and p must be 0.
-            const float m_ref = (m_run == -INFINITY) ? 0.f : m_run;
-            float p[16];
-            float psum = 0.f;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                p[i] = exp2f(x[i] - m_ref);
-                psum += p[i];
-            }
-            l_part += psum;
-            // ---- O^T[c][query] += V^T[c][keys] P^T[keys][query], per 16-key half.
-            //      V^T fragments are read transposed from the row-major V tile:
-            //      16-lane group G = (g, column half ch); source lane i = a + 4j
-            //      points at row kh*16 + 4g + j (then + 8), columns
-            //      n*32 + ch*16 + 4a .. + 3.
-            const int grp = lane >> 4, gg = grp >> 1, ch = grp & 1;
-            const int li = lane & 15, la = li & 3, lj = li >> 2;
-#pragma unroll
-            for (int kh = 0; kh < 2; ++kh) {
-                float hv[8];
+        for (int kh = 0; kh < 2; ++kh) {
+            uint32_t hi4[4], lo4[4];
+            {
+                float ph[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j)
-                    hv[j] = bf16_bits_to_f32(f32_to_bf16_bits(p[kh * 8 + j]));
-                const u32x4_t bhi = {pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]),
-                                     pack_bf16x2(hv[4], hv[5]), pack_bf16x2(hv[6], hv[7])};
-                const u32x4_t blo = {
-                    pack_bf16x2(p[kh * 8 + 0] - hv[0], p[kh * 8 + 1] - hv[1]),
-                    pack_bf16x2(p[kh * 8 + 2] - hv[2], p[kh * 8 + 3] - hv[3]),
-                    pack_bf16x2(p[kh * 8 + 4] - hv[4], p[kh * 8 + 5] - hv[5]),
-                    pack_bf16x2(p[kh * 8 + 6] - hv[6], p[kh * 8 + 7] - hv[7])};
-                const int ra = kh * 16 + 4 * gg + lj, rb2 = ra + 8;
-#pragma unroll
-                for (int n = 0; n < NCT; ++n) {
-                    const int lc = 4 * n + 2 * ch + (la >> 1);  // logical 16-byte chunk
-                    const int off = 8 * (la & 1);
-                    const u32x2_t va =
-                        lds_read_tr16x4(Vt + (ra * VCH + (lc ^ chunk_swz(ra))) * 16 + off);
-                    const u32x2_t vbb =
-                        lds_read_tr16x4(Vt + (rb2 * VCH + (lc ^ chunk_swz(rb2))) * 16 + off);
-                    const u32x4_t a = u32x4_t{va[0], va[1], vbb[0], vbb[1]};
-                    oacc[n] = mfma_32x32x16(a, bhi, oacc[n]);
-                    oacc[n] = mfma_32x32x16(a, blo, oacc[n]);
-                }
+                    ph[j] = p[kh * 8 + j];
+                split_bf16x8(ph, hi4, lo4);
             }
+            const u32x4_t bhi = {hi4[0], hi4[1], hi4[2], hi4[3]};
+            const u32x4_t blo = {lo4[0], lo4[1], lo4[2], lo4[3]};
+            const uint32_t vk = vt + kh * 16 * VD * 2;
+            auto pv4 = [&](auto N0, const u32x2_t(&rd)[8]) {
+                constexpr int n0 = decltype(N0)::value;
+                u32x4_t av[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    av[j] = u32x4_t{rd[2 * j][0], rd[2 * j][1], rd[2 * j + 1][0], rd[2 * j + 1][1]};
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    oacc[n0 + j] = mfma_32x32x16(av[j], bhi, oacc[n0 + j]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    oacc[n0 + j] = mfma_32x32x16(av[j], blo, oacc[n0 + j]);
+            };
+            u32x2_t rd[8];
+            lds_read_tr16x4_8<0>(rd, vk + va_[0], vk + va_[1], vk + va_[2], vk + va_[3],
+                                 vk + vb_[0], vk + vb_[1], vk + vb_[2], vk + vb_[3]);
+            pv4(std::integral_constant<int, 0>{}, rd);
+            lds_read_tr16x4_8<256>(rd, vk + va_[0], vk + va_[1], vk + va_[2], vk + va_[3],
+                                   vk + vb_[0], vk + vb_[1], vk + vb_[2], vk + vb_[3]);
+            pv4(std::integral_constant<int, 4>{}, rd);
         }
     }
 
     // ---- epilogue
-    const float l_tot = l_part + __shfl_xor(l_part, 32, kWave);
+    float l_tot;
+    {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_part),
+                                                         __float_as_uint(l_part), false, false);
+        l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
     if (q_ok) {
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
         float *op = out + (row * H + h) * VD;
