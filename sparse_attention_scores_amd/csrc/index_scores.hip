@@ -186,6 +186,175 @@ __global__ __launch_bounds__(256) void index_scores_mfma_kernel(
     }
 }
 
+// Prefill kernel (bf16 keys, 32 heads x 128 dims, many queries): a block of
+// 8 waves x 2 queries shares each key tile.  Tiles of 32 keys (8 KB) stream
+// into a 3-stage LDS ring by direct-to-LDS loads (one 1-KB instruction per
+// wave per tile) and every wave reads its B operands from there, so a key
+// row crosses L2 once per 16 queries instead of once per 2.  The 16-byte
+// chunks of key row r sit at chunk ^ (r & 15), which keeps the operand reads
+// (32 rows at two adjacent chunks) at the full LDS rate on gfx950, measured.
+constexpr int IP_D = 128, IP_H = 32, IP_QPW = 2, IP_NW = 8, IP_QB = IP_QPW * IP_NW;
+constexpr int IP_TILEB = 32 * IP_D * 2, IP_STAGES = 3;
+static_assert(IP_TILEB == 1024 * IP_NW, "one DMA instruction per wave per tile");
+
+__global__ __launch_bounds__(64 * IP_NW) void index_scores_prefill_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ kv, const float *__restrict__ w,
+    const int32_t *__restrict__ vlo, const int32_t *__restrict__ vhi, float *__restrict__ scores,
+    int n_q, int n_k, float scale, int n_qblocks, int n_chunks, int chunk)
+{
+    constexpr int KS = IP_D / 16;
+    __shared__ __attribute__((aligned(16))) unsigned char tiles[IP_STAGES][IP_TILEB];
+    DSA_LDS_ESCAPE(tiles);
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int g = lane >> 5, col = lane & 31;
+    int bid = blockIdx.x;
+    const int kc = bid % n_chunks;
+    bid /= n_chunks;
+    // latest query blocks first: under a causal mask they see the most keys,
+    // and the light early blocks then fill in behind them
+    const int qblk = n_qblocks - 1 - bid % n_qblocks;
+    const int b = bid / n_qblocks;
+
+    // the block's queries and the union of their visible ranges
+    int ulo = n_k, uhi = 0;
+    {
+        const int t = qblk * IP_QB + (lane & (IP_QB - 1));
+        if (t < n_q) {
+            const int64_t r = (int64_t)b * n_q + t;
+            ulo = max(vlo[r], 0);
+            uhi = min(vhi[r], n_k);
+            if (ulo >= uhi) {
+                ulo = n_k;
+                uhi = 0;
+            }
+        }
+        ulo = (int)wave_min_u32((uint32_t)ulo);
+        uhi = (int)wave_max_u32((uint32_t)uhi);
+    }
+    u32x4_t qf[IP_QPW][KS];
+    float wr[IP_QPW][16];
+    int lo[IP_QPW], hi[IP_QPW];
+    int64_t qrow[IP_QPW];
+    bool qok[IP_QPW];
+#pragma unroll
+    for (int qi = 0; qi < IP_QPW; ++qi) {
+        const int t = qblk * IP_QB + wid * IP_QPW + qi;
+        qok[qi] = t < n_q;
+        qrow[qi] = (int64_t)b * n_q + (qok[qi] ? t : 0);
+        lo[qi] = qok[qi] ? max(vlo[qrow[qi]], 0) : 0;
+        hi[qi] = qok[qi] ? min(vhi[qrow[qi]], n_k) : 0;
+        const uint16_t *qp = q + (qrow[qi] * IP_H + col) * IP_D + g * 8;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            qf[qi][ks] = *reinterpret_cast<const u32x4_t *>(qp + ks * 16);
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            wr[qi][i] = w[qrow[qi] * IP_H + 8 * (i / 4) + 4 * g + (i % 4)] * fabsf(scale);
+    }
+    const bool neg_scale = scale < 0.f;
+
+    const int c0 = kc * chunk;
+    const int c1 = min(c0 + chunk, n_k);
+    const int nt = (c1 - c0 + 31) / 32;
+    // tiles [ta, tb) hold a key some query of the block sees
+    const int ta = ulo < uhi ? max(0, (ulo - c0) / 32) : nt;
+    const int tb = ulo < uhi ? min(nt, (uhi - c0 + 31) / 32) : nt;
+
+    // tiles no query sees: -FLT_MAX
+    for (int tt = 0; tt < nt; ++tt) {
+        if (tt >= ta && tt < tb)
+            continue;
+        const int key = c0 + tt * 32 + col;
+#pragma unroll
+        for (int qi = 0; qi < IP_QPW; ++qi)
+            if (lane < 32 && key < c1 && qok[qi])
+                scores[qrow[qi] * n_k + key] = -FLT_MAX;
+    }
+    if (ta >= tb)
+        return;
+
+    const unsigned char *kb = reinterpret_cast<const unsigned char *>(kv) + (int64_t)b * n_k * IP_D * 2;
+    // DMA: wave w fills LDS bytes w*1024 + 16*lane of the tile = row r, physical
+    // chunk p <- logical chunk p ^ (r & 15) of key c0 + 32*tile + r
+    const int dr = (wid * 64 + lane) / 16;
+    const uint32_t doff = (uint32_t)((((wid * 64 + lane) % 16) ^ (dr & 15)) * 16);
+    auto dma_tile = [&](int tt, int st) {
+        const int key = min(c0 + tt * 32 + dr, n_k - 1);
+        lds_dma16(kb + (int64_t)key * (IP_D * 2) + doff, tiles[st] + wid * 1024);
+    };
+    // B operand of k-step ks: row col, logical chunk 2ks + g
+    uint32_t kaddr[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+        kaddr[ks] = (uint32_t)((col * 16 + ((2 * ks + g) ^ (col & 15))) * 16);
+    const uint32_t lds0 = lds_addr(tiles[0]);
+
+    // epilogue of one tile: w * relu(scale * s) = (w * |scale|) * max(sign(scale) * s, 0),
+    // summed over the lane's 16 heads and the other half-wave's 16
+    auto finish = [&](const f32x16_t(&acc)[IP_QPW], int tt) {
+        const int key = c0 + tt * 32 + col;
+#pragma unroll
+        for (int qi = 0; qi < IP_QPW; ++qi) {
+            float part = 0.f;
+            if (neg_scale) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    part += wr[qi][i] * fmaxf(-acc[qi][i], 0.f);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    part += wr[qi][i] * fmaxf(acc[qi][i], 0.f);
+            }
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part),
+                                                             __float_as_uint(part), false, false);
+            part = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+            if (lane < 32 && key < c1 && qok[qi])
+                scores[qrow[qi] * n_k + key] = (key >= lo[qi] && key < hi[qi]) ? part : -FLT_MAX;
+        }
+    };
+
+    // the query data are in registers before the first tile DMA
+    vm_wait<0>();
+    for (int j = 0; j < IP_STAGES - 1 && ta + j < tb; ++j)
+        dma_tile(ta + j, j);
+    for (int tt = ta; tt < tb; ++tt) {
+        const int st = (tt - ta) % IP_STAGES;
+        vm_wait_tiles<1>(min(tb - 1, tt + IP_STAGES - 2) - tt);
+        lds_barrier();
+        if (tt + IP_STAGES - 1 < tb)
+            dma_tile(tt + IP_STAGES - 1, (tt - ta + IP_STAGES - 1) % IP_STAGES);
+        const uint32_t base = lds0 + st * IP_TILEB;
+        u32x4_t kf[KS];
+        asm volatile(
+            "ds_read_b128 %0, %8\n\t"
+            "ds_read_b128 %1, %9\n\t"
+            "ds_read_b128 %2, %10\n\t"
+            "ds_read_b128 %3, %11\n\t"
+            "ds_read_b128 %4, %12\n\t"
+            "ds_read_b128 %5, %13\n\t"
+            "ds_read_b128 %6, %14\n\t"
+            "ds_read_b128 %7, %15\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(kf[0]), "=&v"(kf[1]), "=&v"(kf[2]), "=&v"(kf[3]), "=&v"(kf[4]),
+              "=&v"(kf[5]), "=&v"(kf[6]), "=&v"(kf[7])
+            : "v"(base + kaddr[0]), "v"(base + kaddr[1]), "v"(base + kaddr[2]),
+              "v"(base + kaddr[3]), "v"(base + kaddr[4]), "v"(base + kaddr[5]),
+              "v"(base + kaddr[6]), "v"(base + kaddr[7])
+            : "memory");
+        f32x16_t acc[IP_QPW];
+#pragma unroll
+        for (int qi = 0; qi < IP_QPW; ++qi)
+            acc[qi] = f32x16_t{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int qi = 0; qi < IP_QPW; ++qi)
+                acc[qi] = mfma_32x32x16(qf[qi][ks], kf[ks], acc[qi]);
+        finish(acc, tt);
+    }
+}
+
 // Plain f32 kernel: one thread per (query row, key).
 __global__ void index_scores_f32_kernel(const float *__restrict__ q, const float *__restrict__ k,
                                         const float *__restrict__ w,
@@ -237,6 +406,20 @@ static hipError_t launch_mfma(const IndexArgs &a, hipStream_t st)
 template <int D, int MT, bool FP8>
 static hipError_t launch_mfma_mode(const IndexArgs &a, hipStream_t st)
 {
+    if (!FP8 && D == IP_D && MT * 32 == IP_H && a.n_q >= IP_QB) {
+        // long key chunks: a block's 16 queries are loaded once per chunk
+        const int n_qblocks = (a.n_q + IP_QB - 1) / IP_QB;
+        const int chunk = 4096;
+        const int n_chunks = (a.n_k + chunk - 1) / chunk;
+        const int64_t blocks = (int64_t)a.batch * n_qblocks * n_chunks;
+        if (blocks > 0x7fffffff)
+            return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL(index_scores_prefill_kernel, dim3((unsigned)blocks), dim3(64 * IP_NW), 0,
+                           st, static_cast<const uint16_t *>(a.q),
+                           static_cast<const uint16_t *>(a.k), a.w, a.vis_lo, a.vis_hi, a.scores,
+                           a.n_q, a.n_k, a.scale, n_qblocks, n_chunks, chunk);
+        return hipGetLastError();
+    }
     if (a.n_q >= 8)
         return launch_mfma<D, MT, 2, 4, FP8>(a, st);
     return launch_mfma<D, MT, 1, 1, FP8>(a, st);
