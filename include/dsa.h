@@ -177,11 +177,12 @@ int dsa_topk(const float *scores, int32_t rows, int32_t n_cols,
  *
  * dtype (q, k, v): BF16 or F32.  Envelope: n_k <= 524288.  BF16 with
  * kv_heads == 1 runs the gather kernel (MFMA, keys gathered per query and
- * shared by all heads; n_heads == 64, kd == 576, vd == 512).  BF16 with
- * kv_heads == n_heads runs the masked-tile kernel (MFMA over key tiles with
- * a per-query selection bitmap; kd == 192, vd == 256).  Other shapes run a
- * plain (non-MFMA) kernel.  The softmax weights enter the value product as
- * a two-term bf16 split (about 16 significant bits); sums are f32.
+ * shared by all heads; n_heads == 64, kd == 576, vd == 512, n_k <= 262144).
+ * BF16 with kv_heads == n_heads runs the masked-tile kernel (MFMA over key
+ * tiles with a per-query selection bitmap; kd == 192, vd == 256).  Other
+ * shapes run a plain (non-MFMA) kernel.  The softmax weights enter the
+ * value product as a two-term bf16 split (about 16 significant bits); sums
+ * are f32.
  * ------------------------------------------------------------------------ */
 typedef struct {
     int32_t batch, n_q, n_k, n_heads, kd, vd, kv_heads, n_sel;

@@ -235,6 +235,25 @@ __device__ __forceinline__ void lds_read_b128_x6(u32x4_t (&a)[6], uint32_t base)
         : "memory");
 }
 
+// Six 16-byte LDS reads and the wait for them: a[2j] from be + O + 128j and
+// a[2j+1] from bo + O + 128j, j < 3 (three even/odd k-step pairs of one row).
+template <int O>
+__device__ __forceinline__ void lds_read_b128_x6eo(u32x4_t (&a)[6], uint32_t be, uint32_t bo)
+{
+    static_assert(O >= 0 && O + 256 < 65536, "ds offset is 16 bits");
+    asm volatile(
+        "ds_read_b128 %0, %6 offset:%8\n\t"
+        "ds_read_b128 %1, %7 offset:%8\n\t"
+        "ds_read_b128 %2, %6 offset:%9\n\t"
+        "ds_read_b128 %3, %7 offset:%9\n\t"
+        "ds_read_b128 %4, %6 offset:%10\n\t"
+        "ds_read_b128 %5, %7 offset:%10\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4]), "=&v"(a[5])
+        : "v"(be), "v"(bo), "i"(O), "i"(O + 128), "i"(O + 256)
+        : "memory");
+}
+
 // Eight 16-byte LDS reads and the wait for them: a[2j] from be + O + j*ROW,
 // a[2j+1] from bo + O + j*ROW, j < 4.
 template <int O, int ROW>
@@ -255,6 +274,15 @@ __device__ __forceinline__ void lds_read_b128_x8(u32x4_t (&a)[8], uint32_t be, u
           "=&v"(a[6]), "=&v"(a[7])
         : "v"(be), "v"(bo), "i"(O), "i"(O + ROW), "i"(O + 2 * ROW), "i"(O + 3 * ROW)
         : "memory");
+}
+
+// LDS atomic OR without return (ds_or_b32) at a byte address.  Written as asm
+// so that the compiler does not order it behind the direct-to-LDS loads in
+// flight (it would wait for them before any LDS store); the next
+// lds_barrier (s_waitcnt lgkmcnt(0)) covers its completion.
+__device__ __forceinline__ void lds_or_async(uint32_t lds_byte_addr, uint32_t bits)
+{
+    asm volatile("ds_or_b32 %0, %1" ::"v"(lds_byte_addr), "v"(bits) : "memory");
 }
 
 // 32-bit LDS byte address of a pointer into shared memory.
@@ -367,16 +395,20 @@ __device__ __forceinline__ float sum_across_rows(float v)
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
+// Inclusive prefix sum over the 64 lanes of a wave (all lanes active), with
+// DPP moves: shifts by 1, 2, 4 and 8 lanes inside each 16-lane row give the
+// row prefixes, then row_bcast:15 adds row r-1's total into rows 1 and 3 and
+// row_bcast:31 adds the total of rows 0-1 into rows 2 and 3.  A lane whose
+// source is outside its row, or whose row is masked off, reads the "old"
+// operand 0.
 __device__ __forceinline__ int wave_inclusive_scan(int v)
 {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        int t = __shfl_up(v, o, kWave);
-        if (lane >= o)
-            v += t;
-    }
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
     return v;
 }
 

@@ -6,20 +6,23 @@
 // table under "What changed"; "Module glm5next_dsa_ref", topk_to_mask and
 // mla_masked_attention).
 //
-// Set semantics without a separate pass: each block inserts the row's valid
-// indices into an LDS bitmap over the n_k keys (duplicates collapse there),
-// takes a popcount prefix sum, and reads its share of the set bits back in
-// ascending key order.  The keys are therefore processed in a fixed order
-// (deterministic results) and the gathers walk memory upwards.
+// Set semantics: a row's selected set has each valid key once.  The gather
+// kernel first takes the valid entries in index order (rows without a
+// repeated key, the case of every top-k output) and checks behind the first
+// tiles, with an LDS bitmap over the n_k keys, that no key repeats; a row
+// that has one is redone from the bitmap, whose popcount prefix sums give
+// each block its share of the set bits in ascending key order (duplicates
+// collapse there).  The other kernels always use the bitmap.  Either way a
+// row's keys are processed in a fixed order, so results are deterministic.
 //
 // Gather kernel (absorbed MLA: one 576-wide latent row per key, shared by
 // all 64 heads, V = its first 512 columns):
-//  * block = 4 waves x 16 heads of one query, over a contiguous share of the
-//    query's selected keys (split-K across blocks when there are few
-//    queries, merged by a combine kernel);
-//  * per tile of 32 keys the rows are gathered once into LDS (row-major for
-//    Q.K^T, transposed for P.V) with 16-byte coalesced loads, and reused by
-//    all 4 waves (64 heads);
+//  * block = 4 waves (one per SIMD) x 16 heads of one query, over a
+//    contiguous share of the query's selected keys (split-K across blocks
+//    when there are few queries, merged by a combine kernel);
+//  * per tile of 32 keys the rows are gathered once into LDS with
+//    direct-to-LDS loads (16 bytes per lane) through a three-stage ring, and
+//    read by all 4 waves (64 heads): row-major for Q.K^T, transposed for P.V;
 //  * S^T = K Q^T on 16x16x32 bf16 MFMA with Q held in registers; online
 //    softmax in f32 (exp2, log2e folded into the scale);
 //  * O^T += V^T P^T on MFMA, with P entering as a two-term bf16 split
@@ -39,87 +42,114 @@ namespace dsa {
 // ------------------------------------------------------------------ shared
 constexpr int kBitmapMaxWords = 16384;  // n_k <= 524288
 
-// Block-wide exclusive scan of one int per thread (blockDim.x == NT).
-template <int NT>
-__device__ int block_exclusive_scan(int v, int *wave_tot, int &total)
+// Indices base + u*NT + tid (u < U) of a row, -1 past the end.  All U loads
+// are issued before any is used.
+template <int NT, int U>
+__device__ __forceinline__ void load_indices(int (&v)[U], const int32_t *__restrict__ idx_row,
+                                             int n_sel, int base)
 {
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    const int incl = wave_inclusive_scan(v);
-    if (lane == 63)
-        wave_tot[wid] = incl;
-    __syncthreads();
-    int before = 0, tot = 0;
 #pragma unroll
-    for (int i = 0; i < NT / 64; ++i) {
-        const int t = wave_tot[i];
-        before += i < wid ? t : 0;
-        tot += t;
+    for (int u = 0; u < U; ++u) {
+        const int i = base + u * NT + (int)threadIdx.x;
+        v[u] = i < n_sel ? idx_row[i] : -1;
     }
-    total = tot;
-    __syncthreads();
-    return before + incl - v;
 }
 
 // Build the selected set of one query row in `bitmap` (words [0, nw)).
-template <int NT>
-__device__ void build_bitmap(uint32_t *bitmap, int nw, const int32_t *__restrict__ idx_row,
-                             int n_sel, int lo, int hi)
+// `first` holds the row's first NT*U indices (load_indices at base 0), loaded
+// by the caller ahead of other work; the rest are read U per thread at a time.
+template <int NT, int U>
+__device__ void build_bitmap(uint32_t *bitmap, int nw, const int (&first)[U],
+                             const int32_t *__restrict__ idx_row, int n_sel, int lo, int hi)
 {
     for (int i = threadIdx.x; i < nw; i += NT)
         bitmap[i] = 0u;
     __syncthreads();
-    for (int i = threadIdx.x; i < n_sel; i += NT) {
-        const int j = idx_row[i];
-        if (j >= lo && j < hi)
-            atomicOr(&bitmap[j >> 5], 1u << (j & 31));
+    int v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        v[u] = first[u];
+    for (int base = 0; base < n_sel; base += NT * U) {
+        if (base > 0)
+            load_indices<NT, U>(v, idx_row, n_sel, base);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = v[u];
+            if (j >= lo && j < hi)  // lo >= 0, so INVALID and padding drop here
+                atomicOr(&bitmap[j >> 5], 1u << (j & 31));
+        }
     }
     __syncthreads();
 }
 
-// Write the set keys with rank in [r0, r1) to list[0 .. r1-r0), ascending.
-// Each thread owns a contiguous run of words; `before` is the number of set
-// bits in earlier runs.
-__device__ __forceinline__ void extract_keys(const uint32_t *bitmap, int w0, int w1, int before,
-                                             int r0, int r1, int32_t *list)
+// The bitmap words are read in chunks of 64 (one word per lane, so the
+// reads are conflict-free); wave w of NW owns the contiguous chunks
+// [c0, c1), so the waves' shares are in key order.
+template <int NW>
+__device__ __forceinline__ void wave_chunk_range(int nw, int wid, int &c0, int &c1)
 {
-    int rank = before;
-    for (int wd = w0; wd < w1 && rank < r1; ++wd) {
-        uint32_t bits = bitmap[wd];
+    const int nch = (nw + 63) >> 6;
+    c0 = wid * nch / NW;
+    c1 = (wid + 1) * nch / NW;
+}
+
+// Number of set bits in this wave's chunks (the same value in every lane).
+__device__ __forceinline__ int wave_chunk_count(const uint32_t *bitmap, int nw, int c0, int c1)
+{
+    const int lane = threadIdx.x & 63;
+    int cnt = 0;
+    for (int c = c0; c < c1; ++c) {
+        const int wd = c * 64 + lane;
+        cnt += wd < nw ? __popc(bitmap[wd]) : 0;
+    }
+    return __builtin_amdgcn_readlane(wave_inclusive_scan(cnt), 63);
+}
+
+// Write the set keys of this wave's chunks whose rank (number of set bits
+// below them in the whole bitmap) is in [r0, r1) to list[rank - r0]; `run` is
+// the number of set bits before chunk c0.
+__device__ __forceinline__ void wave_chunk_extract(const uint32_t *bitmap, int nw, int c0, int c1,
+                                                   int run, int r0, int r1, int32_t *list)
+{
+    const int lane = threadIdx.x & 63;
+    for (int c = c0; c < c1 && run < r1; ++c) {
+        const int wd = c * 64 + lane;
+        uint32_t bits = wd < nw ? bitmap[wd] : 0u;
         const int pc = __popc(bits);
-        if (rank + pc <= r0) {
-            rank += pc;
-            continue;
+        const int incl = wave_inclusive_scan(pc);
+        int rank = run + incl - pc;
+        if (rank < r1 && rank + pc > r0) {
+            while (bits) {
+                const int bit = __ffs(bits) - 1;
+                bits &= bits - 1;
+                if (rank >= r0 && rank < r1)
+                    list[rank - r0] = wd * 32 + bit;
+                ++rank;
+            }
         }
-        while (bits) {
-            const int bit = __ffs(bits) - 1;
-            bits &= bits - 1;
-            if (rank >= r0 && rank < r1)
-                list[rank - r0] = wd * 32 + bit;
-            ++rank;
-        }
+        run += __builtin_amdgcn_readlane(incl, 63);
     }
 }
 
 // ------------------------------------------------------------------ gather kernel
-constexpr int AB_H = 64;
+constexpr int AB_H = 64;                      // heads of the absorbed attention
 constexpr int AB_KD = 576;
 constexpr int AB_VD = 512;
-constexpr int AB_TILE = 32;
+constexpr int AB_TILE = 32;                   // keys per LDS tile
 constexpr int AB_KS = AB_KD / 32;             // 18 k-steps of the 16x16x32 MFMA
 constexpr int AB_ROWB = AB_KD * 2;            // 1152 bytes per latent row
 constexpr int AB_CPR = AB_ROWB / 16;          // 72 16-byte chunks per row
 constexpr int AB_TILEB = AB_TILE * AB_ROWB;   // 36 KB per tile
 constexpr int AB_DMA = AB_TILEB / 1024;       // 36 one-KB wave DMA instructions per tile
-constexpr int AB_LIST = 1024;                 // keys per batch of a block
-constexpr int AB_NT = 512;                    // 8 waves: 4 head groups x 2 halves
+constexpr int AB_NT = 256;                    // 4 waves, one per SIMD: 16 heads each
 constexpr int AB_NW = AB_NT / 64;
-constexpr int AB_NC = AB_VD / 2 / 16;         // 16 output column tiles per wave
+constexpr int AB_NC = AB_VD / 16;             // 32 output column tiles per wave
+constexpr int AB_PER = AB_DMA / AB_NW;        // 9 DMA instructions per wave per tile
 constexpr int AB_STAGES = 3;                  // tiles resident in LDS (ring)
-// wave w issues the tile's DMA instructions w, w + 8, ...: 5 for waves 0-3,
-// 4 for waves 4-7
-constexpr int AB_DMA_HI = (AB_DMA + AB_NW - 1) / AB_NW;
-constexpr int AB_DMA_LO = AB_DMA / AB_NW;
-static_assert(AB_DMA % AB_NW == AB_NW / 2, "waves 0-3 issue one DMA more than waves 4-7");
+constexpr int AB_LIST = 2048;                 // keys per batch of a block
+constexpr int AB_IDX_U = 8;                   // fast path: row entries per thread (n_sel <= 2048)
+constexpr int AB_SET_WORDS = 8192;            // set bitmap of the row: n_k <= 262144
+static_assert(AB_DMA % AB_NW == 0, "every wave issues the same DMA count");
 
 // LDS tile: 32 latent rows, 1152 bytes apart, with the 16-byte chunks of row
 // r stored XOR-swizzled (chunk_swz_odd) so that both the row-wise Q.K^T operand
@@ -130,17 +160,22 @@ static_assert(AB_DMA % AB_NW == AB_NW / 2, "waves 0-3 issue one DMA more than wa
 // so the compiler can tell them apart and puts no wait for the tile loads in
 // front of their accesses.
 struct __attribute__((aligned(16))) AbsTiles {
-    union {
-        unsigned char tile[AB_STAGES][AB_TILEB];
-        uint32_t bitmap[kBitmapMaxWords];
-    } u;
+    unsigned char tile[AB_STAGES][AB_TILEB];
 };
 
-// Wave w of a block owns heads 16*(w&3) .. +15 and half h = w>>2 of the work
-// on them: the k-steps ks = 2m + h of Q.K^T (the partner wave w^4 does the
-// others; the two partial score tiles are exchanged through LDS, so both
-// hold the same S) and output columns 256h .. 256h + 255 of P.V.  Partners
-// share a SIMD, so one's LDS waits overlap the other's MFMAs.
+// Block = (query row, key split), 4 waves, one per SIMD.  Wave w owns heads
+// 16w .. 16w+15 with Q for all 576 dims and O for all 512 columns in
+// registers, and every key of every tile; each tile (loaded once, 36 KB)
+// feeds all 64 heads.  Nothing is exchanged between waves per tile: the only
+// per-tile synchronisation is the ring barrier.
+//
+// Which keys: the selected set of the row (distinct, in range, visible) is
+// split into `splits` contiguous shares.  Fast path (n_sel <= 2048): the
+// shares are taken from the valid entries in index order and the tiles start
+// streaming at once; one LDS OR per tile builds the row's set bitmap behind
+// them, and if it then holds fewer keys than there were valid entries (a key
+// repeats) the block starts over from the bitmap (keys in ascending order,
+// duplicates collapsed).  Rows with n_sel > 2048 go to the bitmap directly.
 __global__ __launch_bounds__(AB_NT) void attend_gather_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kv, int64_t row_stride,
     const int32_t *__restrict__ idx, const int32_t *__restrict__ vlo,
@@ -149,182 +184,186 @@ __global__ __launch_bounds__(AB_NT) void attend_gather_kernel(
     int splits, float scale_log2)
 {
     __shared__ AbsTiles sm;
-    __shared__ f32x4_t sm_xs[AB_NW][2][64];  // partial S^T of each wave, for its partner
     __shared__ int32_t sm_list[AB_LIST];
+    __shared__ uint32_t sm_set[AB_SET_WORDS];
     __shared__ int sm_wave_tot[AB_NW];
     DSA_LDS_ESCAPE(sm);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, col = lane & 15;
-    const int hg = wid & 3, half = wid >> 2;
     // the splits of one row run on one XCD (shared q, idx and partials);
     // without splits the rows keep launch order, which spreads the uneven
     // causal rows evenly over the XCDs
     const int lb = splits > 1 ? xcd_remap(blockIdx.x, gridDim.x) : blockIdx.x;
     const int row = lb / splits;
-    const int split = lb % splits;
-    const int64_t b = row / n_q;
+    const int split = lb - row * splits;
+    const int64_t bseq = row / n_q;
+    const int32_t *idx_row = idx + (int64_t)row * n_sel;
+    const int nw = (n_k + 31) >> 5;
+    bool fast = n_sel <= AB_NT * AB_IDX_U;
 
+    // the row's indices are requested first (thread t: entries 8t .. 8t+7),
+    // then Q; the validity scan below waits for the indices alone
+    int ent[AB_IDX_U];
+    if (fast) {
+#pragma unroll
+        for (int u = 0; u < AB_IDX_U; ++u) {
+            const int i = AB_IDX_U * tid + u;
+            ent[u] = i < n_sel ? idx_row[i] : -1;
+        }
+    }
+
+    // Q^T fragments (B operand) of all 18 k-steps: lane holds head
+    // 16w + col, dims 32ks + 8g .. +8
+    const int head = wid * 16 + col;
+    u32x4_t qf[AB_KS];
+    {
+        const uint16_t *qp = q + ((int64_t)row * AB_H + head) * AB_KD + g * 8;
+#pragma unroll
+        for (int ks = 0; ks < AB_KS; ++ks)
+            qf[ks] = *reinterpret_cast<const u32x4_t *>(qp + ks * 32);
+    }
     int lo = 0, hi = n_k;
     if (vlo) {
         lo = max(vlo[row], 0);
         hi = min(vhi[row], n_k);
     }
-    const int nw = (n_k + 31) >> 5;
-    const int wpt = (nw + AB_NT - 1) / AB_NT;
-    const int w0 = min(tid * wpt, nw), w1 = min(w0 + wpt, nw);
+    for (int i = tid; i < nw; i += AB_NT)
+        sm_set[i] = 0u;
 
-    // Q^T fragments (B operand) of this wave's k-steps ks = 2m + half: lane
-    // holds head hg*16+col, dims ks*32 + g*8 .. +8
-    const int head = hg * 16 + col;
-    u32x4_t qf[AB_KS / 2];
-    {
-        const uint16_t *qp = q + ((int64_t)row * AB_H + head) * AB_KD + half * 32 + g * 8;
-#pragma unroll
-        for (int m = 0; m < AB_KS / 2; ++m)
-            qf[m] = *reinterpret_cast<const u32x4_t *>(qp + m * 64);
-    }
     f32x4_t oacc[AB_NC];
+    float m_run, l_part;
+    auto reset_acc = [&]() {
 #pragma unroll
-    for (int n = 0; n < AB_NC; ++n)
-        oacc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_part = 0.f;
+        for (int n = 0; n < AB_NC; ++n)
+            oacc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        m_run = -INFINITY;
+        l_part = 0.f;
+    };
+    reset_acc();
 
     const unsigned char *kvb =
-        reinterpret_cast<const unsigned char *>(kv) + b * (int64_t)n_k * row_stride * 2;
+        reinterpret_cast<const unsigned char *>(kv) + bseq * (int64_t)n_k * row_stride * 2;
 
     // DMA one tile: wave instruction s (1 KB) fills LDS bytes s*1024 + 16*lane
-    // = (row, physical chunk) from the logical chunk of that row's key.  Wave
-    // w issues instructions w + 8i for i < 4, and waves 0-3 also w + 32.  The
-    // (row, byte offset) of each of this lane's slots is fixed and packed in
-    // one register; the keys are looked up first so the list reads overlap.
-    // Offsets are 32-bit (the host keeps 2*row_stride below 2^31).
-    uint32_t dma_slot[AB_DMA_HI];
+    // = (row, physical chunk) from the logical chunk of that row's key; wave
+    // w issues instructions w + 4i, i < 9.  The (row, byte offset) of each of
+    // this lane's slots is fixed and packed in one register.  Offsets are
+    // 32-bit (the host keeps 2*row_stride below 2^31).
+    uint32_t dma_slot[AB_PER];
 #pragma unroll
-    for (int i = 0; i < AB_DMA_HI; ++i) {
-        const int c = min(wid + i * AB_NW, AB_DMA - 1) * 64 + lane;
+    for (int i = 0; i < AB_PER; ++i) {
+        const int c = (wid + i * AB_NW) * 64 + lane;
         dma_slot[i] = ((uint32_t)(c / AB_CPR) << 16) |
                       (uint32_t)(((c % AB_CPR) ^ chunk_swz_odd(c / AB_CPR)) * 16);
     }
     const uint32_t rs2 = (uint32_t)(row_stride * 2);
-    const bool dma_extra = wid < AB_DMA - AB_DMA_LO * AB_NW;
-    auto dma_tile = [&](unsigned char *dst, int t0, int nvalid) {
+    // the keys of this lane's slots of tile t0 / AB_TILE (nvalid rows)
+    auto dma_keys = [&](int (&key)[AB_PER], int t0, int nvalid) {
         const int32_t *lst = sm_list + t0;
-        int key[AB_DMA_HI];
 #pragma unroll
-        for (int i = 0; i < AB_DMA_HI; ++i)
+        for (int i = 0; i < AB_PER; ++i)
             key[i] = lst[min((int)(dma_slot[i] >> 16), nvalid - 1)];
+    };
+    auto dma_one = [&](unsigned char *dst, const int (&key)[AB_PER], int i) {
+        lds_dma16(kvb + (uint64_t)(uint32_t)key[i] * rs2 + (dma_slot[i] & 0xffffu),
+                  dst + (wid + i * AB_NW) * 1024);
+    };
+    auto dma_tile = [&](unsigned char *dst, int t0, int nvalid) {
+        int key[AB_PER];
+        dma_keys(key, t0, nvalid);
 #pragma unroll
-        for (int i = 0; i < AB_DMA_LO; ++i)
-            lds_dma16(kvb + (uint64_t)(uint32_t)key[i] * rs2 + (dma_slot[i] & 0xffffu),
-                      dst + (wid + i * AB_NW) * 1024);
-        if (dma_extra)
-            lds_dma16(kvb + (uint64_t)(uint32_t)key[AB_DMA_LO] * rs2 +
-                          (dma_slot[AB_DMA_LO] & 0xffffu),
-                      dst + (wid + AB_DMA_LO * AB_NW) * 1024);
+        for (int i = 0; i < AB_PER; ++i)
+            dma_one(dst, key, i);
     };
 
     // Per-lane LDS byte offsets inside a tile (constant over tiles).
-    //  Q.K^T: lane reads rows col and 16+col at logical chunk 4*ks + g =
-    //  8m + 4*half + g; the swizzle only touches the low 3 bits, so that is
-    //  physical chunk 8m + ((4*half + g) ^ swz(col)): one base, immediates.
-    const uint32_t qk_base = (col * AB_CPR + ((4 * half + g) ^ chunk_swz_odd(col))) * 16;
-    //  P.V: the V^T fragment of output column tile n = 16*half + 8M + r is
-    //  read transposed from rows ra and 16+ra at logical chunk 2n + hb, i.e.
-    //  physical chunk 32*half + 16M + 8(r>>2) + ((2(r&3) + hb) ^ swz(ra)):
-    //  four bases (r & 3) plus immediates; byte (col&1)*8 inside the chunk.
+    //  Q.K^T: lane reads rows col and 16+col (same swizzle) at logical chunk
+    //  4ks + g, i.e. physical chunk 8(ks>>1) + ((4(ks&1) + g) ^ swz(col)): an
+    //  even and an odd base plus immediates.
+    constexpr int R16 = 16 * AB_ROWB;
+    const uint32_t qk_e = (col * AB_CPR + (g ^ chunk_swz_odd(col))) * 16;
+    const uint32_t qk_o = (col * AB_CPR + ((4 + g) ^ chunk_swz_odd(col))) * 16;
+    //  P.V: the V^T fragment of column tile n is read transposed from rows
+    //  ra = 4g + (col>>2) and 16+ra at logical chunk 2n + hb, i.e. physical
+    //  chunk 8(n>>2) + ((2(n&3) + hb) ^ swz(ra)): four bases (n & 3) plus
+    //  immediates; byte (col&1)*8 inside the chunk.  Lane (col, g) receives
+    //  V[4g + j][16n + col] and V[16 + 4g + j][16n + col], j < 4.
     const int ra = 4 * g + (col >> 2);
     const int hb = (col & 3) >> 1;
     const int swr = chunk_swz_odd(ra);
     uint32_t pv_base[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-        pv_base[r] = (ra * AB_CPR + ((2 * r + hb) ^ swr)) * 16 + (col & 1) * 8 + half * 512;
-    const uint32_t lds_tiles = lds_addr(sm.u.tile[0]);
+        pv_base[r] = (ra * AB_CPR + ((2 * r + hb) ^ swr)) * 16 + (col & 1) * 8;
+    const uint32_t lds_tiles = lds_addr(sm.tile[0]);
+    const uint32_t lds_set = lds_addr(sm_set);
 
-    // The block's share of the selected set is ranks [r0, r1) in ascending
-    // key order, read out in batches of AB_LIST keys.  The bitmap shares LDS
-    // with the tile buffers, so each batch rebuilds it (one pass over the
-    // row's n_sel indices).
-    for (int batch = 0;; ++batch) {
-        build_bitmap<AB_NT>(sm.u.bitmap, nw, idx + (int64_t)row * n_sel, n_sel, lo, hi);
-        int cnt = 0;
-        for (int wd = w0; wd < w1; ++wd)
-            cnt += __popc(sm.u.bitmap[wd]);
-        int total;
-        const int before = block_exclusive_scan<AB_NT>(cnt, sm_wave_tot, total);
-        const int r0 = (int)(((int64_t)total * split) / splits);
-        const int r1 = (int)(((int64_t)total * (split + 1)) / splits);
-        const int rb = r0 + batch * AB_LIST;
-        if (rb >= r1)
-            break;
-        const int re = min(rb + AB_LIST, r1);
-        extract_keys(sm.u.bitmap, w0, w1, before, rb, re, sm_list);
-        __syncthreads();
-        const int n_my = re - rb;
+    // fast path: valid entries of this thread (bit u: entry 8t+u); one goes
+    // into the set bitmap per tile (shifted out)
+    uint32_t vm = 0;
+    auto insert_one = [&]() {
+        if (vm & 1u)
+            lds_or_async(lds_set + (uint32_t)(ent[0] >> 5) * 4u, 1u << (ent[0] & 31));
+#pragma unroll
+        for (int u = 0; u + 1 < AB_IDX_U; ++u)
+            ent[u] = ent[u + 1];
+        vm >>= 1;
+    };
+
+    // The tiles of the list sm_list[0 .. n_my) through a ring of AB_STAGES
+    // buffers: tiles t+1 .. t+AB_STAGES-1 are in flight while tile t is
+    // consumed.
+    auto run_tiles = [&](int n_my) {
         const int ntiles = (n_my + AB_TILE - 1) / AB_TILE;
         // the Q fragments (and anything else loaded so far) are in registers
-        // before the first tile DMA, so no later wait is needed for them
+        // before the first tile DMA, so the ring's waits count tiles only
         vm_wait<0>();
-
-        // ring of AB_STAGES tiles: tiles t+1 .. t+AB_STAGES-1 are in flight
-        // while tile t is consumed
         for (int s = 0; s < AB_STAGES - 1 && s < ntiles; ++s)
-            dma_tile(sm.u.tile[s], s * AB_TILE, min(AB_TILE, n_my - s * AB_TILE));
+            dma_tile(sm.tile[s], s * AB_TILE, min(AB_TILE, n_my - s * AB_TILE));
         for (int t = 0; t < ntiles; ++t) {
-            const int t0 = t * AB_TILE;
-            const int nvalid = min(AB_TILE, n_my - t0);
+            const int nvalid = min(AB_TILE, n_my - t * AB_TILE);
             // tile t has landed (this wave's DMA; the later tiles may still fly)
-            const int after = min(ntiles - 1, t + AB_STAGES - 2) - t;
-            if (wid < AB_NW / 2)
-                vm_wait_tiles<AB_DMA_HI>(after);
-            else
-                vm_wait_tiles<AB_DMA_LO>(after);
+            vm_wait_tiles<AB_PER>(min(ntiles - 1, t + AB_STAGES - 2) - t);
             lds_barrier();  // ... for every wave, and tile t-1's buffer is free
             const int tn = t + AB_STAGES - 1;
             if (tn < ntiles)
-                dma_tile(sm.u.tile[tn % AB_STAGES], tn * AB_TILE,
+                dma_tile(sm.tile[tn % AB_STAGES], tn * AB_TILE,
                          min(AB_TILE, n_my - tn * AB_TILE));
-            const int toff = (t % AB_STAGES) * AB_TILEB;
+            if (fast)
+                insert_one();
+            const uint32_t tb = lds_tiles + (t % AB_STAGES) * AB_TILEB;
 
-            // ---- partial S^T[key][head] over this wave's 9 k-steps: keys
-            //      0-15 (s0) and 16-31 (s1), two chains each; operands read in
-            //      groups of 3 k-steps
+            // ---- S^T[key][head]: keys 0-15 (s0) and 16-31 (s1), two chains
+            //      each (even and odd k-steps); operands read in groups of 3
+            //      k-steps of one parity x 2 rows
             f32x4_t s0a = {0.f, 0.f, 0.f, 0.f}, s0b = s0a, s1a = s0a, s1b = s0a;
             {
-                const uint32_t kb = lds_tiles + toff + qk_base;
-                constexpr int R16 = 16 * AB_ROWB;  // rows 16..31
-                auto qk_group = [&](auto J, const u32x4_t(&a)[6]) {
-                    constexpr int j = decltype(J)::value;
+                auto qk_group = [&](auto G) {
+                    constexpr int gi = decltype(G)::value, j = gi >> 1, par = gi & 1;
+                    u32x4_t a[6];
+                    lds_read_b128_x6<384 * j, R16>(a, tb + (par ? qk_o : qk_e));
 #pragma unroll
                     for (int u = 0; u < 3; ++u) {
-                        const int m = 3 * j + u;
-                        if (m & 1) {
-                            s0b = mfma_16x16x32(a[2 * u], qf[m], s0b);
-                            s1b = mfma_16x16x32(a[2 * u + 1], qf[m], s1b);
+                        const int ks = 2 * (3 * j + u) + par;
+                        if (par == 0) {
+                            s0a = mfma_16x16x32(a[2 * u], qf[ks], s0a);
+                            s1a = mfma_16x16x32(a[2 * u + 1], qf[ks], s1a);
                         } else {
-                            s0a = mfma_16x16x32(a[2 * u], qf[m], s0a);
-                            s1a = mfma_16x16x32(a[2 * u + 1], qf[m], s1a);
+                            s0b = mfma_16x16x32(a[2 * u], qf[ks], s0b);
+                            s1b = mfma_16x16x32(a[2 * u + 1], qf[ks], s1b);
                         }
                     }
                 };
-                u32x4_t a[6];
-                lds_read_b128_x6<0, R16>(a, kb);
-                qk_group(std::integral_constant<int, 0>{}, a);
-                lds_read_b128_x6<384, R16>(a, kb);
-                qk_group(std::integral_constant<int, 1>{}, a);
-                lds_read_b128_x6<768, R16>(a, kb);
-                qk_group(std::integral_constant<int, 2>{}, a);
+                qk_group(std::integral_constant<int, 0>{});
+                qk_group(std::integral_constant<int, 1>{});
+                qk_group(std::integral_constant<int, 2>{});
+                qk_group(std::integral_constant<int, 3>{});
+                qk_group(std::integral_constant<int, 4>{});
+                qk_group(std::integral_constant<int, 5>{});
             }
-            f32x4_t s0 = s0a + s0b, s1 = s1a + s1b;
-            // ---- add the partner's partial (same lane layout); a + b == b + a,
-            //      so both waves hold bit-identical scores
-            sm_xs[wid][0][lane] = s0;
-            sm_xs[wid][1][lane] = s1;
-            lds_barrier();
-            s0 += sm_xs[wid ^ (AB_NW / 2)][0][lane];
-            s1 += sm_xs[wid ^ (AB_NW / 2)][1][lane];
+            const f32x4_t s0 = s0a + s0b, s1 = s1a + s1b;
 
             // ---- online softmax (log2 domain); lane's keys: 4g+i and 16+4g+i
             float x0[4], x1[4];
@@ -385,13 +424,14 @@ __global__ __launch_bounds__(AB_NT) void attend_gather_kernel(
             }
             // ---- O^T[c][head] += V^T[c][keys] P^T[keys][head], 8 column tiles
             //      per group: 16 transposing reads, then the hi terms of all 8
-            //      tiles and the lo terms, so no MFMA waits on its predecessor.
+            //      tiles and the lo terms, so no MFMA waits on its predecessor
             {
-                const uint32_t tb = lds_tiles + toff;
                 const uint32_t b0 = tb + pv_base[0], b1 = tb + pv_base[1];
                 const uint32_t b2 = tb + pv_base[2], b3 = tb + pv_base[3];
-                auto pv_group = [&](auto M, const u32x2_t(&va)[8], const u32x2_t(&vb)[8]) {
+                auto pv_group = [&](auto M) {
                     constexpr int m = decltype(M)::value;
+                    u32x2_t va[8], vb[8];
+                    lds_read_tr16x4_x16<256 * m, 256 * m + 128, R16>(va, vb, b0, b1, b2, b3);
                     u32x4_t av[8];
 #pragma unroll
                     for (int r = 0; r < 8; ++r)
@@ -403,35 +443,140 @@ __global__ __launch_bounds__(AB_NT) void attend_gather_kernel(
                     for (int r = 0; r < 8; ++r)
                         oacc[8 * m + r] = mfma_16x16x32(av[r], blo, oacc[8 * m + r]);
                 };
-                constexpr int ROW16 = 16 * AB_ROWB;
-                u32x2_t va[8], vb[8];
-                lds_read_tr16x4_x16<0, 128, ROW16>(va, vb, b0, b1, b2, b3);
-                pv_group(std::integral_constant<int, 0>{}, va, vb);
-                lds_read_tr16x4_x16<256, 384, ROW16>(va, vb, b0, b1, b2, b3);
-                pv_group(std::integral_constant<int, 1>{}, va, vb);
+                pv_group(std::integral_constant<int, 0>{});
+                pv_group(std::integral_constant<int, 1>{});
+                pv_group(std::integral_constant<int, 2>{});
+                pv_group(std::integral_constant<int, 3>{});
             }
         }
-        __syncthreads();  // last tile consumed before the bitmap reuses LDS
+    };
+
+    int n_my = 0, n_valid = 0;
+    if (fast) {
+        // valid entries, their ranks in index order (entry order = position)
+#pragma unroll
+        for (int u = 0; u < AB_IDX_U; ++u)
+            vm |= (ent[u] >= lo && ent[u] < hi) ? 1u << u : 0u;  // lo >= 0: INVALID drops
+        const int c = __popc(vm);
+        const int incl = wave_inclusive_scan(c);
+        if (lane == 63)
+            sm_wave_tot[wid] = incl;
+        __syncthreads();  // also orders the set-bitmap clear before the inserts
+        int before = 0;
+#pragma unroll
+        for (int i = 0; i < AB_NW; ++i) {
+            const int t = sm_wave_tot[i];
+            before += i < wid ? t : 0;
+            n_valid += t;
+        }
+        // balanced contiguous shares of the valid entries: the first
+        // n_valid % splits get one more
+        const int per = n_valid / splits, extra = n_valid % splits;
+        const int r0 = split * per + min(split, extra);
+        const int r1 = r0 + per + (split < extra ? 1 : 0);
+        int rank = before + incl - c;
+#pragma unroll
+        for (int u = 0; u < AB_IDX_U; ++u) {
+            if (vm & (1u << u)) {
+                if (rank >= r0 && rank < r1)
+                    sm_list[rank - r0] = ent[u];
+                ++rank;
+            }
+        }
+        __syncthreads();
+        n_my = r1 - r0;
+    } else {
+        // the set bitmap of the whole row, in one pass
+        int first[8];
+        load_indices<AB_NT, 8>(first, idx_row, n_sel, 0);
+        __syncthreads();  // the clear above is complete
+        for (int base = 0; base < n_sel; base += AB_NT * 8) {
+            if (base > 0)
+                load_indices<AB_NT, 8>(first, idx_row, n_sel, base);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int j = first[u];
+                if (j >= lo && j < hi)
+                    atomicOr(&sm_set[j >> 5], 1u << (j & 31));
+            }
+        }
+        __syncthreads();
+    }
+
+    int c0, c1;
+    wave_chunk_range<AB_NW>(nw, wid, c0, c1);
+    for (int batch = fast ? -1 : 0;; ++batch) {
+        int re = 0, r1 = 0, total = 0, before = 0;
+        if (batch >= 0) {
+            // Slow path: the block's share is ranks [r0, r1) of the selected
+            // set in ascending key order, in batches of AB_LIST keys.
+            const int wcnt = wave_chunk_count(sm_set, nw, c0, c1);
+            if (lane == 0)
+                sm_wave_tot[wid] = wcnt;
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < AB_NW; ++i) {
+                const int t = sm_wave_tot[i];
+                before += i < wid ? t : 0;
+                total += t;
+            }
+            const int per = total / splits, extra = total % splits;
+            const int r0 = split * per + min(split, extra);
+            r1 = r0 + per + (split < extra ? 1 : 0);
+            const int rb = r0 + batch * AB_LIST;
+            if (rb >= r1)
+                break;
+            re = min(rb + AB_LIST, r1);
+            wave_chunk_extract(sm_set, nw, c0, c1, before, rb, re, sm_list);
+            __syncthreads();
+            n_my = re - rb;
+        }
+        run_tiles(n_my);
+        if (batch < 0) {
+            // the rest of this thread's entries go into the set bitmap; fewer
+            // set bits than valid entries means a key repeats in the row
+#pragma unroll
+            for (int u = 0; u < AB_IDX_U; ++u)
+                insert_one();
+            lds_barrier();  // every insert is in, every wave is done with the tiles
+            const int wcnt = wave_chunk_count(sm_set, nw, c0, c1);
+            if (lane == 0)
+                sm_wave_tot[wid] = wcnt;
+            __syncthreads();
+            int bits = 0;
+#pragma unroll
+            for (int i = 0; i < AB_NW; ++i)
+                bits += sm_wave_tot[i];
+            if (bits == n_valid)
+                break;
+            reset_acc();
+            fast = false;
+            __syncthreads();  // sm_wave_tot is rewritten by the first batch
+            continue;
+        }
+        if (re >= r1)
+            break;
+        __syncthreads();  // the list is rewritten only after every wave's last tile
     }
 
     // ---- epilogue: l over the 4 lane groups of the head
     const float l_tot = sum_across_rows(l_part);
     if (splits == 1) {
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        float *op = out + ((int64_t)row * AB_H + head) * AB_VD + half * (AB_VD / 2) + 4 * g;
+        float *op = out + ((int64_t)row * AB_H + head) * AB_VD + 4 * g;
 #pragma unroll
         for (int n = 0; n < AB_NC; ++n)
             *reinterpret_cast<f32x4_t *>(op + n * 16) = oacc[n] * inv;
-        if (lse && half == 0 && g == 0)
+        if (lse && g == 0)
             lse[(int64_t)row * AB_H + head] =
                 l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
     } else {
         const int64_t pr_ = ((int64_t)row * splits + split) * AB_H + head;
-        float *op = ws_o + pr_ * AB_VD + half * (AB_VD / 2) + 4 * g;
+        float *op = ws_o + pr_ * AB_VD + 4 * g;
 #pragma unroll
         for (int n = 0; n < AB_NC; ++n)
             *reinterpret_cast<f32x4_t *>(op + n * 16) = oacc[n];
-        if (half == 0 && g == 0) {
+        if (g == 0) {
             ws_ml[pr_ * 2] = l_tot > 0.f ? m_run : -INFINITY;
             ws_ml[pr_ * 2 + 1] = l_tot;
         }
@@ -445,6 +590,7 @@ __global__ __launch_bounds__(AB_NT) void attend_gather_kernel(
 // read.  Blocks follow the gather kernel's XCD order, so a row's partials are
 // read back from the L2 they were written to.
 constexpr int CB_HEADS = 4;
+constexpr int CB_U = 8;
 __global__ __launch_bounds__(64 * CB_HEADS) void attend_combine_kernel(
     const float *__restrict__ ws_o, const float *__restrict__ ws_ml, float *__restrict__ out,
     float *__restrict__ lse, int splits)
@@ -464,13 +610,25 @@ __global__ __launch_bounds__(64 * CB_HEADS) void attend_combine_kernel(
     const float wgt = (ms == -INFINITY) ? 0.f : exp2f(ms - m);
     const float L = wave_sum(wgt * ls);
     f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
-    for (int s = 0; s < splits; ++s) {
-        const float ws_ = __shfl(wgt, s, kWave);
-        if (ws_ != 0.f) {
-            const f32x4_t *src = reinterpret_cast<const f32x4_t *>(
-                ws_o + (((int64_t)row * splits + s) * AB_H + h) * AB_VD + 8 * lane);
-            a0 += ws_ * src[0];
-            a1 += ws_ * src[1];
+    // CB_U splits per round, all loads issued before the first is used
+    const float *base = ws_o + ((int64_t)row * splits * AB_H + h) * AB_VD + 8 * lane;
+    const int64_t sstride = (int64_t)AB_H * AB_VD;
+    for (int s0 = 0; s0 < splits; s0 += CB_U) {
+        f32x4_t v[CB_U][2];
+#pragma unroll
+        for (int u = 0; u < CB_U; ++u) {
+            const int s = min(s0 + u, splits - 1);
+            const f32x4_t *src = reinterpret_cast<const f32x4_t *>(base + s * sstride);
+            v[u][0] = src[0];
+            v[u][1] = src[1];
+        }
+#pragma unroll
+        for (int u = 0; u < CB_U; ++u) {
+            // an empty split has weight 0 and zero partials; splits past the
+            // end re-read the last one with weight 0
+            const float ws_ = s0 + u < splits ? __shfl(wgt, s0 + u, kWave) : 0.f;
+            a0 += ws_ * v[u][0];
+            a1 += ws_ * v[u][1];
         }
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
@@ -525,7 +683,12 @@ __global__ __launch_bounds__(PL_NT) void attend_plain_kernel(
         hi = min(vhi[row], n_k);
     }
     const int nw = (n_k + 31) >> 5;
-    build_bitmap<PL_NT>(sm.bitmap, nw, idx + (int64_t)row * n_sel, n_sel, lo, hi);
+    {
+        const int32_t *idx_row = idx + (int64_t)row * n_sel;
+        int first[8];
+        load_indices<PL_NT, 8>(first, idx_row, n_sel, 0);
+        build_bitmap<PL_NT, 8>(sm.bitmap, nw, first, idx_row, n_sel, lo, hi);
+    }
     const T *qp = q + ((int64_t)row * H + h) * kd;
     float o[PL_MAXVD / PL_NT];
 #pragma unroll
@@ -581,12 +744,14 @@ __global__ __launch_bounds__(PL_NT) void attend_plain_kernel(
 bool attend_gather_supported(const AttendArgs &a)
 {
     return !a.f32 && a.kv_heads == 1 && a.n_heads == AB_H && a.kd == AB_KD && a.vd == AB_VD &&
+           a.n_k <= AB_SET_WORDS * 32 &&
            a.v == a.k && a.v_row_stride == a.k_row_stride && a.k_row_stride % 8 == 0 &&
            a.k_row_stride >= AB_KD && a.k_row_stride < (1ll << 30);
 }
 
 int attend_gather_splits(const AttendArgs &a)
 {
+    // blocks = rows x splits; 256 of them fill the CUs
     const int64_t rows = (int64_t)a.batch * a.n_q;
     int by_fill = (int)((256 + rows - 1) / rows);
     int by_work = max(1, min(a.n_sel, a.n_k) / 64);

@@ -195,13 +195,15 @@ def test_absorbed_attend_parity(dsa, cfg, over, variant, k):
 def test_absorbed_attend_set_semantics(dsa):
     """Duplicates, INVALID, out-of-range and invisible entries, empty rows."""
     note("absorbed attend: set semantics")
-    inp = W.make(2, device="cuda", B=4, Tk=700)
-    B, Tk = 4, 700
+    inp = W.make(2, device="cuda", B=5, Tk=700)
+    B, Tk = 5, 700
     rng = np.random.default_rng(5)
     sel = rng.integers(-3, Tk + 40, (B, 1, 300)).astype(np.int32)
     sel[0, 0, :] = INV                        # empty
     sel[1, 0, 150:] = sel[1, 0, :150]         # every entry twice
     sel[2, 0, :] = 17                         # one key, many times
+    # distinct entries, some INVALID (-1), negative, past n_k or invisible
+    sel[4, 0, :] = rng.permutation(Tk + 43)[:300] - 3
     idx = torch.tensor(sel, device="cuda")
     lo = torch.full((B, 1), 5, dtype=torch.int32, device="cuda")
     hi = torch.full((B, 1), 650, dtype=torch.int32, device="cuda")
@@ -214,6 +216,28 @@ def test_absorbed_attend_set_semantics(dsa):
     check_attend(cpu(out).numpy().reshape(ref.shape), ref, cpu(lse).numpy().reshape(lref.shape),
                  lref, bf16=True, what="set semantics")
     assert torch.all(out[0] == 0) and torch.all(torch.isneginf(lse[0]))
+
+
+def test_absorbed_attend_long_context_distinct(dsa):
+    """n_k past the duplicate-check bitmap (300000 keys): the set bitmap path
+    with distinct keys, INVALID entries and a visibility window."""
+    note("absorbed attend: n_k = 300000")
+    B, Tk = 1, 300000
+    inp = W.make(2, device="cuda", B=B, Tk=Tk)
+    rng = np.random.default_rng(11)
+    sel = np.full((B, 1, 512), INV, dtype=np.int32)
+    sel[0, 0, :400] = rng.choice(Tk, 400, replace=False)
+    idx = torch.tensor(sel, device="cuda")
+    lo = torch.full((B, 1), 1000, dtype=torch.int32, device="cuda")
+    hi = torch.full((B, 1), 290000, dtype=torch.int32, device="cuda")
+    out, lse = dsa.sparse_attend(inp["q"], inp["KV"], None, idx, inp["scale_attn"], 1, vd=512,
+                                 vis_lo=lo, vis_hi=hi)
+    torch.cuda.synchronize()
+    ref, lref = oracle.sparse_attend(cpu(inp["q"]), cpu(inp["KV"]), None, sel,
+                                     inp["scale_attn"], 1, q_pos=np.full((B, 1), 289999),
+                                     pad=np.full(B, 1000), k_row_stride=576, vd=512)
+    check_attend(cpu(out).numpy().reshape(ref.shape), ref, cpu(lse).numpy().reshape(lref.shape),
+                 lref, bf16=True, what="long context")
 
 
 def test_attend_plain_f32_per_head_and_shared(dsa):
