@@ -99,6 +99,9 @@ def _parse():
     ap.add_argument("--cpu-rows", type=int, default=64, help="query rows in the oracle sample")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="also run a plain copy kernel of MIB MiB (counter calibration)")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay one captured HIP graph per timed step instead of launching "
+                         "the step's kernels one by one")
     return ap.parse_args()
 
 
@@ -248,6 +251,24 @@ def algorithmic_work(inp):
             "attend": (att_bytes, att_flops)}
 
 
+def capture_step(torch, run_once):
+    """One step of kernels captured as a HIP graph (torch.cuda.CUDAGraph is
+    hipGraph on ROCm).  The step only launches kernels on the current stream
+    into preallocated buffers: no allocation, memset or synchronisation is
+    recorded."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run_once()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run_once()
+    torch.cuda.synchronize()
+    return g
+
+
 def cpu_baseline(cfg, rows_wanted, min_seconds=10.0, max_passes=20):
     """The oracle (as it stands) on a bounded sample of the same workload:
     up to `rows_wanted` query rows through index scores -> top-k ->
@@ -323,24 +344,43 @@ def main():
     for _ in range(args.warmup):
         run_once()
     torch.cuda.synchronize()
-    print(f"[bench] warmup {args.warmup} done; timing {args.steps} steps", file=sys.stderr,
-          flush=True)
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
-          for _ in range(K)]
+    # Whole-step timing: K steps launched back to back (or K replays of one
+    # captured HIP graph per step), nothing recorded between them.  An event
+    # recorded between two kernels holds the second back until the first has
+    # fully drained, so per-stage events inside this loop would add their own
+    # gaps to the step.
+    graph = None
+    if args.graph:
+        graph = capture_step(torch, run_once)
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+    print(f"[bench] warmup {args.warmup} done; timing {K} steps "
+          f"({'eager' if graph is None else 'graph replay'})", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(K):
-        e = ev[s]
-        e[0].record()
-        for j, f in enumerate(stages):
-            f()
-            e[j + 1].record()
+        if graph is None:
+            run_once()
+        else:
+            graph.replay()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # Per-stage timing: K back-to-back launches of each stage on the step's
+    # own buffers, bracketed by two HIP events on the stream the kernels run
+    # on; the average launch duration feeds the stage breakdown and the
+    # roofline.
     stage_ms = {}
-    for j, name in enumerate(names):
-        stage_ms[name] = sum(ev[s][j].elapsed_time(ev[s][j + 1]) for s in range(K)) / K
+    for name, f in zip(names, stages):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(K):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        stage_ms[name] = e0.elapsed_time(e1) / K
     if cfg == 5:
         work, tokens = pooled_work(inp)
     else:
@@ -387,7 +427,8 @@ def main():
         "dtype": "f32" if inp["dtype"] == "f32" else "bf16",
         "data": "synthetic",
         "config": {"workload": WORKLOAD_TEXT[cfg], "config_id": cfg,
-                   "query_tokens_per_step": tokens, "seed": inp["seed"]},
+                   "query_tokens_per_step": tokens, "seed": inp["seed"],
+                   "launch": "eager" if graph is None else "hip graph per step"},
         "roofline": roof,
         "stages": per_stage,
     }
