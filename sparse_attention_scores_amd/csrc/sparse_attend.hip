@@ -180,7 +180,7 @@ __global__ __launch_bounds__(AB_NT) void attend_gather_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kv, int64_t row_stride,
     const int32_t *__restrict__ idx, const int32_t *__restrict__ vlo,
     const int32_t *__restrict__ vhi, float *__restrict__ out, float *__restrict__ lse,
-    float *__restrict__ ws_o, float *__restrict__ ws_ml, int n_q, int n_k, int n_sel,
+    uint16_t *__restrict__ ws_o, f32x4_t *__restrict__ ws_ml, int n_q, int n_k, int n_sel,
     int splits, float scale_log2)
 {
     __shared__ AbsTiles sm;
@@ -571,64 +571,85 @@ __global__ __launch_bounds__(AB_NT) void attend_gather_kernel(
             lse[(int64_t)row * AB_H + head] =
                 l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
     } else {
-        const int64_t pr_ = ((int64_t)row * splits + split) * AB_H + head;
-        float *op = ws_o + pr_ * AB_VD + 4 * g;
+        // Split partial: O in fp16 with a power-of-two scale per (row, split,
+        // head) that puts the head's largest |O| in [2^14, 2^15), so every
+        // element keeps fp16's 11 significant bits (more than the bf16
+        // operands carry) whatever the magnitude of V; O = stored * 2^e.
+        float amax = 0.f;
 #pragma unroll
         for (int n = 0; n < AB_NC; ++n)
-            *reinterpret_cast<f32x4_t *>(op + n * 16) = oacc[n];
-        if (g == 0) {
-            ws_ml[pr_ * 2] = l_tot > 0.f ? m_run : -INFINITY;
-            ws_ml[pr_ * 2 + 1] = l_tot;
+            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(oacc[n][0]), fabsf(oacc[n][1])),
+                                     fmaxf(fabsf(oacc[n][2]), fabsf(oacc[n][3]))));
+        amax = max_across_rows(amax);
+        const int e = __builtin_amdgcn_frexp_expf(amax) - 15;
+        const int64_t pr_ = ((int64_t)row * splits + split) * AB_H + head;
+        uint16_t *op = ws_o + pr_ * AB_VD + 4 * g;
+#pragma unroll
+        for (int n = 0; n < AB_NC; ++n) {
+            typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+            const f32x4_t sc = {ldexpf(oacc[n][0], -e), ldexpf(oacc[n][1], -e),
+                                ldexpf(oacc[n][2], -e), ldexpf(oacc[n][3], -e)};
+            *reinterpret_cast<u32x2_t *>(op + n * 16) =
+                __builtin_bit_cast(u32x2_t, __builtin_convertvector(sc, h4_t));
         }
+        if (g == 0)
+            ws_ml[pr_] = f32x4_t{l_tot > 0.f ? m_run : -INFINITY, l_tot, (float)e, 0.f};
     }
 }
 
 // Merge the split partials of each (row, head):
-//   O = sum_s 2^(m_s - m) O_s / L,  L = sum_s 2^(m_s - m) l_s,  m = max_s m_s.
-// One block per (row, 4 heads), one wave per head; lane j owns columns
-// 8j .. 8j+7 of the 512, so every split's partial row is one coalesced 2 KB
-// read.  Blocks follow the gather kernel's XCD order, so a row's partials are
-// read back from the L2 they were written to.
+//   O = sum_s 2^(m_s - m) O_s / L,  L = sum_s 2^(m_s - m) l_s,  m = max_s m_s,
+// with O_s = stored_s * 2^(e_s) (fp16 partials, see the gather epilogue), so
+// the weight of the stored values is 2^(m_s - m + e_s).  One block per (row,
+// 4 heads), one wave per head; lane j owns columns 8j .. 8j+7 of the 512, so
+// every split's partial row is one coalesced 1 KB read.  Blocks follow the
+// gather kernel's XCD order, so a row's partials are read back from the L2
+// they were written to.
 constexpr int CB_HEADS = 4;
 constexpr int CB_U = 8;
 __global__ __launch_bounds__(64 * CB_HEADS) void attend_combine_kernel(
-    const float *__restrict__ ws_o, const float *__restrict__ ws_ml, float *__restrict__ out,
-    float *__restrict__ lse, int splits)
+    const uint16_t *__restrict__ ws_o, const f32x4_t *__restrict__ ws_ml,
+    float *__restrict__ out, float *__restrict__ lse, int splits)
 {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int lb = xcd_remap(blockIdx.x, gridDim.x);
     const int row = lb / (AB_H / CB_HEADS);
     const int h = (lb % (AB_H / CB_HEADS)) * CB_HEADS + wid;
-    // lane s < splits holds split s's (m, l)
-    float ms = -INFINITY, ls = 0.f;
+    // lane s < splits holds split s's (m, l, e)
+    float ms = -INFINITY, ls = 0.f, es = 0.f;
     if (lane < splits) {
-        const int64_t pr = ((int64_t)row * splits + lane) * AB_H + h;
-        ms = ws_ml[pr * 2];
-        ls = ws_ml[pr * 2 + 1];
+        const f32x4_t ml = ws_ml[((int64_t)row * splits + lane) * AB_H + h];
+        ms = ml[0];
+        ls = ml[1];
+        es = ml[2];
     }
     const float m = wave_max(ms);
     const float wgt = (ms == -INFINITY) ? 0.f : exp2f(ms - m);
     const float L = wave_sum(wgt * ls);
+    const float wo = ldexpf(wgt, (int)es);  // weight of the stored fp16 values
     f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
     // CB_U splits per round, all loads issued before the first is used
-    const float *base = ws_o + ((int64_t)row * splits * AB_H + h) * AB_VD + 8 * lane;
+    const uint16_t *base = ws_o + ((int64_t)row * splits * AB_H + h) * AB_VD + 8 * lane;
     const int64_t sstride = (int64_t)AB_H * AB_VD;
+    typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
     for (int s0 = 0; s0 < splits; s0 += CB_U) {
-        f32x4_t v[CB_U][2];
+        u32x4_t v[CB_U];
 #pragma unroll
         for (int u = 0; u < CB_U; ++u) {
             const int s = min(s0 + u, splits - 1);
-            const f32x4_t *src = reinterpret_cast<const f32x4_t *>(base + s * sstride);
-            v[u][0] = src[0];
-            v[u][1] = src[1];
+            v[u] = *reinterpret_cast<const u32x4_t *>(base + s * sstride);
         }
 #pragma unroll
         for (int u = 0; u < CB_U; ++u) {
             // an empty split has weight 0 and zero partials; splits past the
             // end re-read the last one with weight 0
-            const float ws_ = s0 + u < splits ? __shfl(wgt, s0 + u, kWave) : 0.f;
-            a0 += ws_ * v[u][0];
-            a1 += ws_ * v[u][1];
+            const float w_ = s0 + u < splits ? __shfl(wo, s0 + u, kWave) : 0.f;
+            const f32x4_t lo4 = __builtin_convertvector(
+                __builtin_bit_cast(h4_t, u32x2_t{v[u][0], v[u][1]}), f32x4_t);
+            const f32x4_t hi4 = __builtin_convertvector(
+                __builtin_bit_cast(h4_t, u32x2_t{v[u][2], v[u][3]}), f32x4_t);
+            a0 += w_ * lo4;
+            a1 += w_ * hi4;
         }
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
@@ -769,7 +790,8 @@ size_t attend_workspace_bytes(const AttendArgs &a)
     if (s <= 1)
         return 0;
     const int64_t rows = (int64_t)a.batch * a.n_q;
-    return (size_t)rows * s * AB_H * (AB_VD + 2) * sizeof(float);
+    // fp16 partials plus one (m, l, e, -) f32 quadruple per (row, split, head)
+    return (size_t)rows * s * AB_H * (AB_VD * sizeof(uint16_t) + 4 * sizeof(float));
 }
 
 bool attend_plain_supported(const AttendArgs &a)
@@ -783,8 +805,9 @@ hipError_t launch_attend(const AttendArgs &a, hipStream_t st)
     const float scale_log2 = a.scale * kLog2e;
     if (attend_gather_supported(a)) {
         const int splits = attend_gather_splits(a);
-        float *ws_o = static_cast<float *>(a.workspace);
-        float *ws_ml = ws_o ? ws_o + rows * splits * AB_H * AB_VD : nullptr;
+        uint16_t *ws_o = static_cast<uint16_t *>(a.workspace);
+        f32x4_t *ws_ml =
+            ws_o ? reinterpret_cast<f32x4_t *>(ws_o + rows * splits * AB_H * AB_VD) : nullptr;
         hipLaunchKernelGGL(attend_gather_kernel, dim3((unsigned)(rows * splits)), dim3(AB_NT), 0,
                            st, static_cast<const uint16_t *>(a.q),
                            static_cast<const uint16_t *>(a.k), a.k_row_stride, a.idx, a.vis_lo,

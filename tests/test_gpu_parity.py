@@ -218,6 +218,29 @@ def test_absorbed_attend_set_semantics(dsa):
     assert torch.all(out[0] == 0) and torch.all(torch.isneginf(lse[0]))
 
 
+def test_absorbed_attend_split_partials_large_values(dsa):
+    """Few rows (split-K partials) with latent rows x 2^26 and queries x 2^-26
+    (both exact in bf16): the scores are unchanged and |V| reaches ~10^6, past
+    the fp16 range the split partials are stored in, so their per-(row, split,
+    head) power-of-two scale is what keeps the result."""
+    note("absorbed attend: large V through the split partials")
+    inp, lo, hi, S = _index_case(dsa, 2, dict(B=2, Tk=3000), None)
+    sel = _oracle_sel(inp, S, 2048)
+    idx = torch.tensor(sel, device="cuda")
+    q = (inp["q"].float() * 2.0 ** -26).to(torch.bfloat16)
+    kv = (inp["KV"].float() * 2.0 ** 26).to(torch.bfloat16)
+    assert torch.equal(q.float() * 2.0 ** 26, inp["q"].float())
+    out, lse = dsa.sparse_attend(q, kv, None, idx, inp["scale_attn"], kv_heads=1, vd=512,
+                                 vis_lo=lo, vis_hi=hi)
+    torch.cuda.synchronize()
+    assert float(cpu(out).abs().max()) > 65504.0
+    ref, lref = oracle.sparse_attend(cpu(q), cpu(kv), None, sel, inp["scale_attn"],
+                                     kv_heads=1, q_pos=cpu(inp["q_pos"]), pad=cpu(inp["pad"]),
+                                     k_row_stride=576, vd=512)
+    check_attend(cpu(out).numpy().reshape(ref.shape), ref, cpu(lse).numpy().reshape(lref.shape),
+                 lref, bf16=True, what="large values")
+
+
 def test_absorbed_attend_long_context_distinct(dsa):
     """n_k past the duplicate-check bitmap (300000 keys): the set bitmap path
     with distinct keys, INVALID entries and a visibility window."""
