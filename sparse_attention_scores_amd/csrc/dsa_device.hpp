@@ -337,37 +337,46 @@ __device__ __forceinline__ uint32_t score_order_key(float f)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Wave-wide reductions (wave64) via cross-lane shuffles.
+// Wave-wide reductions (wave64), every lane gets the result, without LDS:
+// DPP quad_perm [1,0,3,2] and [2,3,0,1] reduce each quad, row_half_mirror
+// pairs the two quads of each half-row, row_mirror the two halves of each
+// 16-lane row, then the gfx950 row swaps v_permlane16_swap / v_permlane32_swap
+// pair the rows (each returns both values of the pair).
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce_bits(uint32_t v, Op op)
+{
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xf, 0xf, false));
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xf, 0xf, false));
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xf, 0xf, false));
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xf, 0xf, false));
+    const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = op(a[0], a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return op(b[0], b[1]);
+}
+
 __device__ __forceinline__ float wave_max(float v)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1)
-        v = fmaxf(v, __shfl_xor(v, o, kWave));
-    return v;
+    return __uint_as_float(wave_reduce_bits(__float_as_uint(v), [](uint32_t x, uint32_t y) {
+        return __float_as_uint(fmaxf(__uint_as_float(x), __uint_as_float(y)));
+    }));
 }
 
 __device__ __forceinline__ float wave_sum(float v)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1)
-        v += __shfl_xor(v, o, kWave);
-    return v;
+    return __uint_as_float(wave_reduce_bits(__float_as_uint(v), [](uint32_t x, uint32_t y) {
+        return __float_as_uint(__uint_as_float(x) + __uint_as_float(y));
+    }));
 }
 
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1)
-        v = min(v, (uint32_t)__shfl_xor((int)v, o, kWave));
-    return v;
+    return wave_reduce_bits(v, [](uint32_t x, uint32_t y) { return x < y ? x : y; });
 }
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1)
-        v = max(v, (uint32_t)__shfl_xor((int)v, o, kWave));
-    return v;
+    return wave_reduce_bits(v, [](uint32_t x, uint32_t y) { return x > y ? x : y; });
 }
 
 // max / sum over the four lanes l, l^16, l^32, l^48 (the four 16-lane rows)

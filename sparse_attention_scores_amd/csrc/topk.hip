@@ -102,9 +102,25 @@ __global__ __launch_bounds__(NT) void topk_sorted_kernel(const float *__restrict
     int need = n, cand = n;
     if (n > k)
         select32(sm, n, k, omin, omax, prefix, mask, need, cand);
+    // The bucket sort places each winner by its composite key (order key,
+    // column), so it takes them in any order; when the whole boundary group
+    // wins (no tie at the boundary to break by column) the fast unordered
+    // compaction feeds it.  Equal order keys everywhere, or a bucket sort
+    // that gives up, need the winners in column order (the stable radix
+    // sort keeps it for equal keys): then the stable compaction reruns from
+    // the key cache, which the bucket sort leaves intact.
     uint32_t wmin, wmax;
-    const int m = compact32(sm, n, lo, prefix, mask, need, cand, wmin, wmax);
-    const int buf = bucket_sort32(sm, m, wmin, wmax) ? 0 : sort32(sm, m, wmin, wmax);
+    const bool any_order = cand == need;
+    int m = any_order ? compact32_any(sm, n, lo, prefix, mask, wmin, wmax)
+                      : compact32(sm, n, lo, prefix, mask, need, cand, wmin, wmax);
+    bool sorted = (!any_order || wmin != wmax) && bucket_sort32(sm, m, wmin, wmax);
+    int buf = 0;
+    if (!sorted) {
+        if (any_order)
+            m = compact32(sm, n, lo, prefix, mask, need, cand, wmin, wmax);
+        // all keys equal: column order is the rank order already
+        buf = wmin == wmax ? 0 : sort32(sm, m, wmin, wmax);
+    }
     int32_t *o = out + (int64_t)row * k;
     for (int i = tid; i < k; i += NT)
         o[i] = i < m ? (int32_t)sm.wcol[buf][i] : -1;

@@ -307,23 +307,25 @@ struct __attribute__((aligned(16))) Topk32Smem {
     static constexpr int NCNT = 256 * EPT * NW;          // (digit, round, wave) counters
     static constexpr int NB = 2048;                      // bucket-sort buckets
     static constexpr int R = CAP / NT;                   // compaction rounds
-    static_assert(CAP * 4 >= NCNT * 2 && CAP * 4 >= NB * 8, "sort arrays overlay the key cache");
+    static_assert(CAP * 4 >= NCNT * 2, "radix-sort counters overlay the key cache");
     static_assert(R <= 32, "round flags are kept in one 32-bit mask");
     union {
         uint32_t ord[CAP];        // order keys of the row, column order
-        uint16_t cnt[NCNT];       // radix-sort counters, after the compaction
-        struct {
-            uint32_t off[NB];     // bucket offsets
-            uint32_t fill[NB];    // bucket counts, then fill pointers
-        } bk;
+        uint16_t cnt[NCNT];       // radix-sort counters, after the last compaction
     } a;
     int tab[2][R * NW + 1];       // (round, wave) counts -> exclusive prefixes, + total
     uint32_t word[2][kTopkMaxK];  // winners' order keys (sort ping-pong)
     uint32_t wcol[2][kTopkMaxK];  // winners' columns
-    uint32_t hist[NW][256];       // per-wave select histograms
+    union {
+        uint32_t hist[NW][256];   // per-wave select histograms
+        struct {
+            uint32_t off[NB];     // bucket offsets
+            uint32_t fill[NB];    // bucket counts, then fill pointers
+        } bk;                     // (the bucket sort leaves the key cache intact)
+    };
     int red[2][2][NW];            // per-wave totals (two round parities x two counts)
     uint32_t mm[2][NW];           // per-wave min / max
-    int bin, above, bincnt;
+    int bin, above, bincnt, fill;
 };
 
 // Load scores[lo, hi) into sm.a.ord (column order) and reduce their min/max.
@@ -544,6 +546,72 @@ __device__ int compact32(Topk32Smem<NT, CAP> &sm, int n, int col0, uint32_t pref
     return total;
 }
 
+// Compaction of the winners into sm.word[0] / sm.wcol[0] in no particular
+// order, for the case where the whole boundary group wins (cand == need, or
+// n <= k with mask 0): every key with (ord & mask) >= prefix.  Each wave
+// counts its winners over all rounds first and claims one range of an LDS
+// counter with a single atomic; the positions inside it follow from the
+// ballots.  Returns the count and the winners' min / max.
+template <int NT, int CAP>
+__device__ int compact32_any(Topk32Smem<NT, CAP> &sm, int n, int col0, uint32_t prefix,
+                             uint32_t mask, uint32_t &wmin, uint32_t &wmax)
+{
+    constexpr int NW = NT / 64, R = CAP / NT;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const uint64_t lt = (1ull << lane) - 1ull;
+    if (tid == 0)
+        sm.fill = 0;
+    __syncthreads();
+    const int rounds = (n + NT - 1) / NT;
+    uint32_t key[R];
+    uint64_t wb[R];
+    int cnt = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int i = r * NT + tid;
+        key[r] = 0u;
+        wb[r] = 0ull;
+        if (r < rounds) {  // uniform
+            key[r] = i < n ? sm.a.ord[i] : 0u;
+            wb[r] = __ballot(i < n && (key[r] & mask) >= prefix);
+            cnt += __popcll(wb[r]);
+        }
+    }
+    int base = 0;
+    if (lane == 0 && cnt)
+        base = atomicAdd(&sm.fill, cnt);
+    base = __builtin_amdgcn_readfirstlane(base);
+    uint32_t mn = ~0u, mx = 0u;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        if ((wb[r] >> lane) & 1ull) {
+            const int pos = base + __popcll(wb[r] & lt);
+            sm.word[0][pos] = key[r];
+            sm.wcol[0][pos] = (uint32_t)(col0 + r * NT + tid);
+            mn = min(mn, key[r]);
+            mx = max(mx, key[r]);
+        }
+        base += __popcll(wb[r]);
+    }
+    mn = wave_min_u32(mn);
+    mx = wave_max_u32(mx);
+    if (lane == 0) {
+        sm.mm[0][wid] = mn;
+        sm.mm[1][wid] = mx;
+    }
+    __syncthreads();
+    wmin = sm.mm[0][0];
+    wmax = sm.mm[1][0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+        wmin = min(wmin, sm.mm[0][w]);
+        wmax = max(wmax, sm.mm[1][w]);
+    }
+    const int total = sm.fill;
+    __syncthreads();  // mm and fill are read before they are reused
+    return total;
+}
+
 // Bucket sort of the m winners (sm.word / sm.wcol buffer 0, column order) by
 // descending order key: buckets on the top (up to) 11 bits in which the
 // winners differ, then each winner's place inside its bucket by counting the
@@ -570,11 +638,11 @@ __device__ bool bucket_sort32(Topk32Smem<NT, CAP> &sm, int m, uint32_t wmin, uin
     const uint32_t dmask = (1u << dbits) - 1u;
     const int nb = 1 << dbits;
     for (int i = tid; i < nb; i += NT)
-        sm.a.bk.fill[i] = 0u;
+        sm.bk.fill[i] = 0u;
     __syncthreads();
     for (int i = tid; i < m; i += NT) {
         const int bkt = nb - 1 - (int)((sm.word[0][i] >> shift) & dmask);  // descending
-        atomicAdd(&sm.a.bk.fill[bkt], 1u);
+        atomicAdd(&sm.bk.fill[bkt], 1u);
     }
     __syncthreads();
     // exclusive scan of the nb counts (thread t owns PB consecutive buckets)
@@ -585,7 +653,7 @@ __device__ bool bucket_sort32(Topk32Smem<NT, CAP> &sm, int m, uint32_t wmin, uin
 #pragma unroll
         for (int j = 0; j < PB; ++j) {
             const int bkt = tid * PB + j;
-            v[j] = bkt < nb ? sm.a.bk.fill[bkt] : 0u;
+            v[j] = bkt < nb ? sm.bk.fill[bkt] : 0u;
             s += (int)v[j];
             mx = max(mx, (int)v[j]);
         }
@@ -609,8 +677,8 @@ __device__ bool bucket_sort32(Topk32Smem<NT, CAP> &sm, int m, uint32_t wmin, uin
         for (int j = 0; j < PB; ++j) {
             const int bkt = tid * PB + j;
             if (bkt < nb) {
-                sm.a.bk.off[bkt] = (uint32_t)before;
-                sm.a.bk.fill[bkt] = (uint32_t)before;
+                sm.bk.off[bkt] = (uint32_t)before;
+                sm.bk.fill[bkt] = (uint32_t)before;
             }
             before += (int)v[j];
         }
@@ -638,13 +706,13 @@ __device__ bool bucket_sort32(Topk32Smem<NT, CAP> &sm, int m, uint32_t wmin, uin
 #pragma unroll
     for (int r = 0; r < S::EPT; ++r)
         if (r * NT + tid < m)
-            ck[atomicAdd(&sm.a.bk.fill[mbkt[r]], 1u)] = mine[r];
+            ck[atomicAdd(&sm.bk.fill[mbkt[r]], 1u)] = mine[r];
     __syncthreads();
     // place each winner inside its bucket: rank = members with a larger key
 #pragma unroll
     for (int r = 0; r < S::EPT; ++r) {
         if (r * NT + tid < m) {
-            const int b0 = (int)sm.a.bk.off[mbkt[r]], b1 = (int)sm.a.bk.fill[mbkt[r]];
+            const int b0 = (int)sm.bk.off[mbkt[r]], b1 = (int)sm.bk.fill[mbkt[r]];
             int rank = 0;
             for (int j = b0; j < b1; ++j)
                 rank += ck[j] > mine[r];
