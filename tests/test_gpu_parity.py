@@ -134,6 +134,33 @@ def test_topk_bit_exact_on_gpu_scores(dsa, cfg, over, variant, k):
     assert bad.size == 0, f"rows differ: {bad[:10]} first: {got[bad[0]][:16]} vs {ref[bad[0]][:16]}"
 
 
+def test_topk_long_rows_skewed(dsa):
+    """Long rows (chunked path) where one chunk holds every top score, so the
+    merge's lower bound prunes almost nothing and the survivors overflow the
+    LDS cache; and a row whose visible window leaves chunks with fewer than
+    their quota of real keys."""
+    note("topk long rows, skewed")
+    rng = np.random.default_rng(21)
+    n, k = 150000, 2048
+    rows = rng.standard_normal((3, n)).astype(np.float32)
+    rows[0, 20000:40000] += 50.0          # the top scores all in one chunk
+    rows[1, :] = rng.standard_normal(n).astype(np.float32) * 1e-3
+    rows[1, 131072:] += 10.0              # the last (partial) chunk wins
+    S = torch.tensor(rows, device="cuda")
+    lo = torch.tensor([0, 0, 100000], dtype=torch.int32, device="cuda")
+    hi = torch.tensor([n, n, 116500], dtype=torch.int32, device="cuda")
+    idx = dsa.topk(S, lo, hi, k)
+    torch.cuda.synchronize()
+    got = cpu(idx).numpy()
+    for i in range(3):
+        l0, h0 = int(lo[i]), int(hi[i])
+        r = rows[i]
+        cand = np.arange(l0, h0)
+        order = cand[np.lexsort((cand, -r[l0:h0].astype(np.float64)))][:k]
+        exp = np.concatenate([order, np.full(k - order.size, INV)])
+        assert (got[i] == exp).all(), i
+
+
 def test_topk_edge_rows(dsa):
     note("topk edge rows")
     n = 777
