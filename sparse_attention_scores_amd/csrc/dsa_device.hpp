@@ -176,6 +176,20 @@ __device__ __forceinline__ u32x2_t lds_read_tr16x4(const void *lds_addr)
     return __builtin_bit_cast(u32x2_t, r);
 }
 
+// Plain LDS reads at a 32-bit LDS byte address, for waves that issue no
+// direct-to-LDS loads themselves (the compiler then has no such loads to wait
+// for in front of them, and schedules and allocates them freely).
+__device__ __forceinline__ u32x4_t lds_ld128(uint32_t a)
+{
+    return *(const u32x4_t __attribute__((address_space(3))) *)(uintptr_t)a;
+}
+__device__ __forceinline__ u32x2_t lds_ld_tr16(uint32_t a)
+{
+    const lds_v4i16_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16_t __attribute__((address_space(3))) *)(uintptr_t)a);
+    return __builtin_bit_cast(u32x2_t, r);
+}
+
 // Sixteen transposing LDS reads and the wait for them, in one asm statement:
 // va[r] from b[r & 3] + (r < 4 ? O0 : O1), vb[r] from the same address + ROW.
 // The wait sits inside the statement, so the destination registers are
@@ -283,6 +297,24 @@ __device__ __forceinline__ void lds_read_b128_x8(u32x4_t (&a)[8], uint32_t be, u
 __device__ __forceinline__ void lds_or_async(uint32_t lds_byte_addr, uint32_t bits)
 {
     asm volatile("ds_or_b32 %0, %1" ::"v"(lds_byte_addr), "v"(bits) : "memory");
+}
+
+// Six 4-byte LDS reads from per-lane byte addresses and the wait for them, in
+// one asm statement (the destinations are complete when the compiler first
+// sees them; no wait for direct-to-LDS loads in flight is implied).
+__device__ __forceinline__ void lds_read_u32_x6(uint32_t (&v)[6], const uint32_t (&a)[6])
+{
+    asm volatile(
+        "ds_read_b32 %0, %6\n\t"
+        "ds_read_b32 %1, %7\n\t"
+        "ds_read_b32 %2, %8\n\t"
+        "ds_read_b32 %3, %9\n\t"
+        "ds_read_b32 %4, %10\n\t"
+        "ds_read_b32 %5, %11\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5])
+        : "memory");
 }
 
 // 32-bit LDS byte address of a pointer into shared memory.

@@ -141,15 +141,19 @@ constexpr int AB_ROWB = AB_KD * 2;            // 1152 bytes per latent row
 constexpr int AB_CPR = AB_ROWB / 16;          // 72 16-byte chunks per row
 constexpr int AB_TILEB = AB_TILE * AB_ROWB;   // 36 KB per tile
 constexpr int AB_DMA = AB_TILEB / 1024;       // 36 one-KB wave DMA instructions per tile
-constexpr int AB_NT = 256;                    // 4 waves, one per SIMD: 16 heads each
-constexpr int AB_NW = AB_NT / 64;
+constexpr int AB_CW = 4;                      // compute waves, one per SIMD: 16 heads each
+constexpr int AB_CT = 64 * AB_CW;             // compute threads
+constexpr int AB_NT = AB_CT + 64;             // plus one loader wave
 constexpr int AB_NC = AB_VD / 16;             // 32 output column tiles per wave
-constexpr int AB_PER = AB_DMA / AB_NW;        // 9 DMA instructions per wave per tile
 constexpr int AB_STAGES = 3;                  // tiles resident in LDS (ring)
+constexpr int AB_EARLY = 12;                  // DMAs of tile j issued before tile j-1 is released
+constexpr int AB_KB = 6;                      // loader key reads per LDS batch
 constexpr int AB_LIST = 2048;                 // keys per batch of a block
 constexpr int AB_IDX_U = 8;                   // fast path: row entries per thread (n_sel <= 2048)
 constexpr int AB_SET_WORDS = 8192;            // set bitmap of the row: n_k <= 262144
-static_assert(AB_DMA % AB_NW == 0, "every wave issues the same DMA count");
+static_assert(AB_DMA % AB_KB == 0 && AB_EARLY % AB_KB == 0 && AB_EARLY < AB_DMA,
+              "the loader issues whole key batches");
+static_assert(AB_LIST == AB_CT * AB_IDX_U, "the fast path lists a whole row");
 
 // LDS tile: 32 latent rows, 1152 bytes apart, with the 16-byte chunks of row
 // r stored XOR-swizzled (chunk_swz_odd) so that both the row-wise Q.K^T operand
@@ -163,34 +167,51 @@ struct __attribute__((aligned(16))) AbsTiles {
     unsigned char tile[AB_STAGES][AB_TILEB];
 };
 
-// Block = (query row, key split), 4 waves, one per SIMD.  Wave w owns heads
-// 16w .. 16w+15 with Q for all 576 dims and O for all 512 columns in
-// registers, and every key of every tile; each tile (loaded once, 36 KB)
-// feeds all 64 heads.  Nothing is exchanged between waves per tile: the only
-// per-tile synchronisation is the ring barrier.
+// Block = (query row, key split): 4 compute waves (one per SIMD) and one
+// loader wave.  Compute wave w owns heads 16w .. 16w+15 with Q for all 576
+// dims and O for all 512 columns in registers, and every key of every tile;
+// each tile (loaded once, 36 KB) feeds all 64 heads.  The loader wave issues
+// every direct-to-LDS load of the tiles, so the compute waves never stall on
+// a full memory queue: a wave that issues loads waits at each one until the
+// queue takes it, and while the kernel streams rows the queue is full.  Tile
+// j's first AB_EARLY loads are issued before the loader waits for tile j-1,
+// so the queue stays fed across the barrier that releases tile j-1.
 //
 // Which keys: the selected set of the row (distinct, in range, visible) is
 // split into `splits` contiguous shares.  Fast path (n_sel <= 2048): the
-// shares are taken from the valid entries in index order and the tiles start
-// streaming at once; one LDS OR per tile builds the row's set bitmap behind
-// them, and if it then holds fewer keys than there were valid entries (a key
-// repeats) the block starts over from the bitmap (keys in ascending order,
-// duplicates collapsed).  Rows with n_sel > 2048 go to the bitmap directly.
-__global__ __launch_bounds__(AB_NT) void attend_gather_kernel(
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ kv, int64_t row_stride,
-    const int32_t *__restrict__ idx, const int32_t *__restrict__ vlo,
+// valid entries are listed in index order and the shares taken from that
+// list, so the tiles start streaming at once; the loader wave builds the
+// row's set bitmap from the list while the last tile is computed, and if it
+// holds fewer keys than there were valid entries (a key repeats) the block
+// starts over from the bitmap (keys in ascending order, duplicates
+// collapsed).  Rows with n_sel > 2048 go to the bitmap directly.
+// The two roles are separate instantiations, so the registers of one (Q and
+// O of the compute waves, the load slots of the loader) are not live in the
+// other; they share only LDS and the barriers, which both pass in the same
+// sequence.
+struct AbsShared {
+    AbsTiles sm;
+    int32_t list[AB_LIST];
+    uint32_t set[AB_SET_WORDS];
+    int wave_tot[AB_CW];
+};
+
+template <bool LOADER>
+__device__ __forceinline__ void attend_gather_role(
+    AbsShared &shm, const uint16_t *__restrict__ q, const uint16_t *__restrict__ kv,
+    int64_t row_stride, const int32_t *__restrict__ idx, const int32_t *__restrict__ vlo,
     const int32_t *__restrict__ vhi, float *__restrict__ out, float *__restrict__ lse,
     uint16_t *__restrict__ ws_o, f32x4_t *__restrict__ ws_ml, int n_q, int n_k, int n_sel,
     int splits, float scale_log2)
 {
-    __shared__ AbsTiles sm;
-    __shared__ int32_t sm_list[AB_LIST];
-    __shared__ uint32_t sm_set[AB_SET_WORDS];
-    __shared__ int sm_wave_tot[AB_NW];
-    DSA_LDS_ESCAPE(sm);
+    AbsTiles &sm = shm.sm;
+    int32_t *sm_list = shm.list;
+    uint32_t *sm_set = shm.set;
+    int *sm_wave_tot = shm.wave_tot;
+    constexpr bool loader = LOADER;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wid = LOADER ? AB_CW : __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, col = lane & 15;
     // the splits of one row run on one XCD (shared q, idx and partials);
     // without splits the rows keep launch order, which spreads the uneven
@@ -201,12 +222,12 @@ __global__ __launch_bounds__(AB_NT) void attend_gather_kernel(
     const int64_t bseq = row / n_q;
     const int32_t *idx_row = idx + (int64_t)row * n_sel;
     const int nw = (n_k + 31) >> 5;
-    bool fast = n_sel <= AB_NT * AB_IDX_U;
+    bool fast = n_sel <= AB_LIST;
 
-    // the row's indices are requested first (thread t: entries 8t .. 8t+7),
-    // then Q; the validity scan below waits for the indices alone
+    // compute threads request the row's indices first (thread t: entries
+    // 8t .. 8t+7), then Q; the validity scan below waits for the indices alone
     int ent[AB_IDX_U];
-    if (fast) {
+    if (fast && !loader) {
 #pragma unroll
         for (int u = 0; u < AB_IDX_U; ++u) {
             const int i = AB_IDX_U * tid + u;
@@ -216,9 +237,9 @@ __global__ __launch_bounds__(AB_NT) void attend_gather_kernel(
 
     // Q^T fragments (B operand) of all 18 k-steps: lane holds head
     // 16w + col, dims 32ks + 8g .. +8
-    const int head = wid * 16 + col;
+    const int head = min(wid, AB_CW - 1) * 16 + col;
     u32x4_t qf[AB_KS];
-    {
+    if (!loader) {
         const uint16_t *qp = q + ((int64_t)row * AB_H + head) * AB_KD + g * 8;
 #pragma unroll
         for (int ks = 0; ks < AB_KS; ++ks)
@@ -245,37 +266,41 @@ __global__ __launch_bounds__(AB_NT) void attend_gather_kernel(
 
     const unsigned char *kvb =
         reinterpret_cast<const unsigned char *>(kv) + bseq * (int64_t)n_k * row_stride * 2;
-
-    // DMA one tile: wave instruction s (1 KB) fills LDS bytes s*1024 + 16*lane
-    // = (row, physical chunk) from the logical chunk of that row's key; wave
-    // w issues instructions w + 4i, i < 9.  The (row, byte offset) of each of
-    // this lane's slots is fixed and packed in one register.  Offsets are
-    // 32-bit (the host keeps 2*row_stride below 2^31).
-    uint32_t dma_slot[AB_PER];
-#pragma unroll
-    for (int i = 0; i < AB_PER; ++i) {
-        const int c = (wid + i * AB_NW) * 64 + lane;
-        dma_slot[i] = ((uint32_t)(c / AB_CPR) << 16) |
-                      (uint32_t)(((c % AB_CPR) ^ chunk_swz_odd(c / AB_CPR)) * 16);
-    }
     const uint32_t rs2 = (uint32_t)(row_stride * 2);
-    // the keys of this lane's slots of tile t0 / AB_TILE (nvalid rows)
-    auto dma_keys = [&](int (&key)[AB_PER], int t0, int nvalid) {
-        const int32_t *lst = sm_list + t0;
+    const uint32_t lds_tiles = lds_addr(sm.tile[0]);
+    const uint32_t lds_list = lds_addr(sm_list);
+    const uint32_t lds_set = lds_addr(sm_set);
+
+    // Loader: wave instruction s (1 KB) of a tile fills LDS bytes s*1024 +
+    // 16*lane = (row, physical chunk) from the logical chunk of that row's
+    // key.  The (row, byte offset) of this lane's slot s is fixed and packed
+    // in one register.  Offsets are 32-bit (the host keeps 2*row_stride
+    // below 2^31).
+    uint32_t slot[AB_DMA];
+    if (loader) {
 #pragma unroll
-        for (int i = 0; i < AB_PER; ++i)
-            key[i] = lst[min((int)(dma_slot[i] >> 16), nvalid - 1)];
-    };
-    auto dma_one = [&](unsigned char *dst, const int (&key)[AB_PER], int i) {
-        lds_dma16(kvb + (uint64_t)(uint32_t)key[i] * rs2 + (dma_slot[i] & 0xffffu),
-                  dst + (wid + i * AB_NW) * 1024);
-    };
-    auto dma_tile = [&](unsigned char *dst, int t0, int nvalid) {
-        int key[AB_PER];
-        dma_keys(key, t0, nvalid);
+        for (int s = 0; s < AB_DMA; ++s) {
+            const int c = s * 64 + lane;
+            slot[s] = ((uint32_t)(c / AB_CPR) << 16) |
+                      (uint32_t)(((c % AB_CPR) ^ chunk_swz_odd(c / AB_CPR)) * 16);
+        }
+    }
+    // loads [S0, S1) of the tile whose keys start at LDS byte lkeys (nvalid
+    // of them; the padding rows repeat the last key)
+    auto issue = [&](auto S0c, auto S1c, unsigned char *dst, uint32_t lkeys, int nvalid) {
+        constexpr int S0 = decltype(S0c)::value, S1 = decltype(S1c)::value;
 #pragma unroll
-        for (int i = 0; i < AB_PER; ++i)
-            dma_one(dst, key, i);
+        for (int s = S0; s < S1; s += AB_KB) {
+            uint32_t ka[AB_KB], key[AB_KB];
+#pragma unroll
+            for (int b = 0; b < AB_KB; ++b)
+                ka[b] = lkeys + 4u * (uint32_t)min((int)(slot[s + b] >> 16), nvalid - 1);
+            lds_read_u32_x6(key, ka);
+#pragma unroll
+            for (int b = 0; b < AB_KB; ++b)
+                lds_dma16(kvb + (uint64_t)key[b] * rs2 + (slot[s + b] & 0xffffu),
+                          dst + (s + b) * 1024);
+        }
     };
 
     // Per-lane LDS byte offsets inside a tile (constant over tiles).
@@ -297,267 +322,316 @@ __global__ __launch_bounds__(AB_NT) void attend_gather_kernel(
 #pragma unroll
     for (int r = 0; r < 4; ++r)
         pv_base[r] = (ra * AB_CPR + ((2 * r + hb) ^ swr)) * 16 + (col & 1) * 8;
-    const uint32_t lds_tiles = lds_addr(sm.tile[0]);
-    const uint32_t lds_set = lds_addr(sm_set);
 
-    // fast path: valid entries of this thread (bit u: entry 8t+u); one goes
-    // into the set bitmap per tile (shifted out)
-    uint32_t vm = 0;
-    auto insert_one = [&]() {
-        if (vm & 1u)
-            lds_or_async(lds_set + (uint32_t)(ent[0] >> 5) * 4u, 1u << (ent[0] & 31));
+    // One tile of a compute wave: S^T = K Q^T, online softmax, O^T += V^T P^T.
+    auto compute_tile = [&](uint32_t tb, int nvalid) {
+        // ---- S^T[key][head]: keys 0-15 (s0) and 16-31 (s1), two chains
+        //      each (even and odd k-steps); operands read in groups of 3
+        //      k-steps of one parity x 2 rows
+        f32x4_t s0a = {0.f, 0.f, 0.f, 0.f}, s0b = s0a, s1a = s0a, s1b = s0a;
+        {
+            auto qk_group = [&](auto G) {
+                constexpr int gi = decltype(G)::value, j = gi >> 1, par = gi & 1;
+                const uint32_t base = tb + (par ? qk_o : qk_e) + 384 * j;
+                u32x4_t a[6];
 #pragma unroll
-        for (int u = 0; u + 1 < AB_IDX_U; ++u)
-            ent[u] = ent[u + 1];
-        vm >>= 1;
+                for (int u = 0; u < 3; ++u) {
+                    a[2 * u] = lds_ld128(base + 128 * u);
+                    a[2 * u + 1] = lds_ld128(base + 128 * u + R16);
+                }
+#pragma unroll
+                for (int u = 0; u < 3; ++u) {
+                    const int ks = 2 * (3 * j + u) + par;
+                    if (par == 0) {
+                        s0a = mfma_16x16x32(a[2 * u], qf[ks], s0a);
+                        s1a = mfma_16x16x32(a[2 * u + 1], qf[ks], s1a);
+                    } else {
+                        s0b = mfma_16x16x32(a[2 * u], qf[ks], s0b);
+                        s1b = mfma_16x16x32(a[2 * u + 1], qf[ks], s1b);
+                    }
+                }
+            };
+            qk_group(std::integral_constant<int, 0>{});
+            qk_group(std::integral_constant<int, 1>{});
+            qk_group(std::integral_constant<int, 2>{});
+            qk_group(std::integral_constant<int, 3>{});
+            qk_group(std::integral_constant<int, 4>{});
+            qk_group(std::integral_constant<int, 5>{});
+        }
+        const f32x4_t s0 = s0a + s0b, s1 = s1a + s1b;
+
+        // ---- online softmax (log2 domain); lane's keys: 4g+i and 16+4g+i
+        float x0[4], x1[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x0[i] = s0[i] * scale_log2;
+            x1[i] = s1[i] * scale_log2;
+        }
+        if (nvalid < AB_TILE) {  // ragged last tile: rows past the end are padding
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x0[i] = (4 * g + i < nvalid) ? x0[i] : -INFINITY;
+                x1[i] = (16 + 4 * g + i < nvalid) ? x1[i] : -INFINITY;
+            }
+        }
+        float tmax = fmaxf(fmaxf(fmaxf(x0[0], x0[1]), fmaxf(x0[2], x0[3])),
+                           fmaxf(fmaxf(x1[0], x1[1]), fmaxf(x1[2], x1[3])));
+        tmax = max_across_rows(tmax);
+        // Lazy rescale: the reference max only moves when the tile max
+        // exceeds it by more than kRescaleLog2, so p <= 2^kRescaleLog2
+        // and the O accumulators are rarely touched.  Exact: l and O
+        // always share the same reference.
+        const bool grow = tmax > m_run + kRescaleLog2;
+        if (__any(grow)) {
+            const float m_new = grow ? tmax : m_run;
+            // lanes that do not grow keep alpha = 1 (m_run may still be -inf
+            // there, and -inf - -inf would be NaN); a growing lane with
+            // m_run = -inf gets 0
+            const float alpha = grow ? exp2f(m_run - m_new) : 1.f;
+            if (__any(grow && m_run != -INFINITY)) {
+#pragma unroll
+                for (int n = 0; n < AB_NC; ++n)
+                    oacc[n] *= alpha;
+            }
+            l_part *= alpha;
+            m_run = m_new;
+        }
+        // m_run is -inf only while every key seen so far (this tile
+        // included) is masked; then all x are -inf and p must be 0.
+        // x - m_ref <= kRescaleLog2, so the hardware exp2 (no denormal
+        // results) is all that is needed.
+        const float m_ref = (m_run == -INFINITY) ? 0.f : m_run;
+        float p[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            p[i] = __builtin_amdgcn_exp2f(x0[i] - m_ref);
+            p[4 + i] = __builtin_amdgcn_exp2f(x1[i] - m_ref);
+        }
+        l_part += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+        // ---- P^T fragments (B operand): element j <-> key 4g+j (j < 4),
+        //      16+4g+(j-4) (j >= 4); two-term bf16 split
+        u32x4_t bhi, blo;
+        {
+            uint32_t h[4], l[4];
+            split_bf16x8(p, h, l);
+            bhi = u32x4_t{h[0], h[1], h[2], h[3]};
+            blo = u32x4_t{l[0], l[1], l[2], l[3]};
+        }
+        // ---- O^T[c][head] += V^T[c][keys] P^T[keys][head], 4 column tiles
+        //      per group: 8 transposing reads, then the hi terms of all 4
+        //      tiles and the lo terms, so no MFMA waits on its predecessor
+        {
+            const uint32_t b0 = tb + pv_base[0], b1 = tb + pv_base[1];
+            const uint32_t b2 = tb + pv_base[2], b3 = tb + pv_base[3];
+            auto pv_group = [&](auto M) {
+                constexpr int m = decltype(M)::value;
+                const uint32_t bb[4] = {b0, b1, b2, b3};
+                u32x4_t av[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const uint32_t a = bb[r] + 128 * m;
+                    const u32x2_t va = lds_ld_tr16(a), vb = lds_ld_tr16(a + R16);
+                    av[r] = u32x4_t{va[0], va[1], vb[0], vb[1]};
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    oacc[4 * m + r] = mfma_16x16x32(av[r], bhi, oacc[4 * m + r]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    oacc[4 * m + r] = mfma_16x16x32(av[r], blo, oacc[4 * m + r]);
+            };
+            pv_group(std::integral_constant<int, 0>{});
+            pv_group(std::integral_constant<int, 1>{});
+            pv_group(std::integral_constant<int, 2>{});
+            pv_group(std::integral_constant<int, 3>{});
+            pv_group(std::integral_constant<int, 4>{});
+            pv_group(std::integral_constant<int, 5>{});
+            pv_group(std::integral_constant<int, 6>{});
+            pv_group(std::integral_constant<int, 7>{});
+        }
     };
 
-    // The tiles of the list sm_list[0 .. n_my) through a ring of AB_STAGES
-    // buffers: tiles t+1 .. t+AB_STAGES-1 are in flight while tile t is
-    // consumed.
-    auto run_tiles = [&](int n_my) {
+    // The tiles of the key list sm_list[first .. first + n_my) through a ring
+    // of AB_STAGES buffers.  Barrier B_t releases tile t to the compute
+    // waves; they reach it after finishing tile t-1, so once past B_t the
+    // loader may refill tile t-1's buffer with tile t+2.  Both roles pass
+    // the same ntiles barriers, then one more after the last tile.
+    auto run_tiles = [&](int first, int n_my) {
         const int ntiles = (n_my + AB_TILE - 1) / AB_TILE;
-        // the Q fragments (and anything else loaded so far) are in registers
-        // before the first tile DMA, so the ring's waits count tiles only
-        vm_wait<0>();
-        for (int s = 0; s < AB_STAGES - 1 && s < ntiles; ++s)
-            dma_tile(sm.tile[s], s * AB_TILE, min(AB_TILE, n_my - s * AB_TILE));
-        for (int t = 0; t < ntiles; ++t) {
-            const int nvalid = min(AB_TILE, n_my - t * AB_TILE);
-            // tile t has landed (this wave's DMA; the later tiles may still fly)
-            vm_wait_tiles<AB_PER>(min(ntiles - 1, t + AB_STAGES - 2) - t);
-            lds_barrier();  // ... for every wave, and tile t-1's buffer is free
-            const int tn = t + AB_STAGES - 1;
-            if (tn < ntiles)
-                dma_tile(sm.tile[tn % AB_STAGES], tn * AB_TILE,
-                         min(AB_TILE, n_my - tn * AB_TILE));
-            if (fast)
-                insert_one();
-            const uint32_t tb = lds_tiles + (t % AB_STAGES) * AB_TILEB;
-
-            // ---- S^T[key][head]: keys 0-15 (s0) and 16-31 (s1), two chains
-            //      each (even and odd k-steps); operands read in groups of 3
-            //      k-steps of one parity x 2 rows
-            f32x4_t s0a = {0.f, 0.f, 0.f, 0.f}, s0b = s0a, s1a = s0a, s1b = s0a;
-            {
-                auto qk_group = [&](auto G) {
-                    constexpr int gi = decltype(G)::value, j = gi >> 1, par = gi & 1;
-                    u32x4_t a[6];
-                    lds_read_b128_x6<384 * j, R16>(a, tb + (par ? qk_o : qk_e));
-#pragma unroll
-                    for (int u = 0; u < 3; ++u) {
-                        const int ks = 2 * (3 * j + u) + par;
-                        if (par == 0) {
-                            s0a = mfma_16x16x32(a[2 * u], qf[ks], s0a);
-                            s1a = mfma_16x16x32(a[2 * u + 1], qf[ks], s1a);
-                        } else {
-                            s0b = mfma_16x16x32(a[2 * u], qf[ks], s0b);
-                            s1b = mfma_16x16x32(a[2 * u + 1], qf[ks], s1b);
-                        }
-                    }
-                };
-                qk_group(std::integral_constant<int, 0>{});
-                qk_group(std::integral_constant<int, 1>{});
-                qk_group(std::integral_constant<int, 2>{});
-                qk_group(std::integral_constant<int, 3>{});
-                qk_group(std::integral_constant<int, 4>{});
-                qk_group(std::integral_constant<int, 5>{});
-            }
-            const f32x4_t s0 = s0a + s0b, s1 = s1a + s1b;
-
-            // ---- online softmax (log2 domain); lane's keys: 4g+i and 16+4g+i
-            float x0[4], x1[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                x0[i] = s0[i] * scale_log2;
-                x1[i] = s1[i] * scale_log2;
-            }
-            if (nvalid < AB_TILE) {  // ragged last tile: rows past the end are padding
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    x0[i] = (4 * g + i < nvalid) ? x0[i] : -INFINITY;
-                    x1[i] = (16 + 4 * g + i < nvalid) ? x1[i] : -INFINITY;
+        const uint32_t lkeys = lds_list + 4u * (uint32_t)first;
+        auto tile_buf = [&](int t) { return lds_tiles + (uint32_t)((t % AB_STAGES) * AB_TILEB); };
+        auto tile_ptr = [&](int t) { return sm.tile[t % AB_STAGES]; };
+        auto tile_n = [&](int t) { return min(AB_TILE, n_my - t * AB_TILE); };
+        if (loader) {
+            if (ntiles > 0)
+                issue(std::integral_constant<int, 0>{}, std::integral_constant<int, AB_DMA>{},
+                      tile_ptr(0), lkeys, tile_n(0));
+            for (int j = 1; j <= ntiles; ++j) {
+                // tile j's first loads, then tile j-1 has landed: release it
+                if (j < ntiles) {
+                    issue(std::integral_constant<int, 0>{},
+                          std::integral_constant<int, AB_EARLY>{}, tile_ptr(j),
+                          lkeys + 4u * (uint32_t)(j * AB_TILE), tile_n(j));
+                    vm_wait<AB_EARLY>();
+                } else {
+                    vm_wait<0>();
                 }
+                lds_barrier();  // B_{j-1}
+                if (j < ntiles)
+                    issue(std::integral_constant<int, AB_EARLY>{},
+                          std::integral_constant<int, AB_DMA>{}, tile_ptr(j),
+                          lkeys + 4u * (uint32_t)(j * AB_TILE), tile_n(j));
             }
-            float tmax = fmaxf(fmaxf(fmaxf(x0[0], x0[1]), fmaxf(x0[2], x0[3])),
-                               fmaxf(fmaxf(x1[0], x1[1]), fmaxf(x1[2], x1[3])));
-            tmax = max_across_rows(tmax);
-            // Lazy rescale: the reference max only moves when the tile max
-            // exceeds it by more than kRescaleLog2, so p <= 2^kRescaleLog2
-            // and the O accumulators are rarely touched.  Exact: l and O
-            // always share the same reference.
-            const bool grow = tmax > m_run + kRescaleLog2;
-            if (__any(grow)) {
-                const float m_new = grow ? tmax : m_run;
-                // lanes that do not grow keep alpha = 1 (m_run may still be -inf
-                // there, and -inf - -inf would be NaN); a growing lane with
-                // m_run = -inf gets 0
-                const float alpha = grow ? exp2f(m_run - m_new) : 1.f;
-                if (__any(grow && m_run != -INFINITY)) {
-#pragma unroll
-                    for (int n = 0; n < AB_NC; ++n)
-                        oacc[n] *= alpha;
-                }
-                l_part *= alpha;
-                m_run = m_new;
-            }
-            // m_run is -inf only while every key seen so far (this tile
-            // included) is masked; then all x are -inf and p must be 0.
-            // x - m_ref <= kRescaleLog2, so the hardware exp2 (no denormal
-            // results) is all that is needed.
-            const float m_ref = (m_run == -INFINITY) ? 0.f : m_run;
-            float p[8];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                p[i] = __builtin_amdgcn_exp2f(x0[i] - m_ref);
-                p[4 + i] = __builtin_amdgcn_exp2f(x1[i] - m_ref);
-            }
-            l_part += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-            // ---- P^T fragments (B operand): element j <-> key 4g+j (j < 4),
-            //      16+4g+(j-4) (j >= 4); two-term bf16 split
-            u32x4_t bhi, blo;
-            {
-                uint32_t h[4], l[4];
-                split_bf16x8(p, h, l);
-                bhi = u32x4_t{h[0], h[1], h[2], h[3]};
-                blo = u32x4_t{l[0], l[1], l[2], l[3]};
-            }
-            // ---- O^T[c][head] += V^T[c][keys] P^T[keys][head], 8 column tiles
-            //      per group: 16 transposing reads, then the hi terms of all 8
-            //      tiles and the lo terms, so no MFMA waits on its predecessor
-            {
-                const uint32_t b0 = tb + pv_base[0], b1 = tb + pv_base[1];
-                const uint32_t b2 = tb + pv_base[2], b3 = tb + pv_base[3];
-                auto pv_group = [&](auto M) {
-                    constexpr int m = decltype(M)::value;
-                    u32x2_t va[8], vb[8];
-                    lds_read_tr16x4_x16<256 * m, 256 * m + 128, R16>(va, vb, b0, b1, b2, b3);
-                    u32x4_t av[8];
-#pragma unroll
-                    for (int r = 0; r < 8; ++r)
-                        av[r] = u32x4_t{va[r][0], va[r][1], vb[r][0], vb[r][1]};
-#pragma unroll
-                    for (int r = 0; r < 8; ++r)
-                        oacc[8 * m + r] = mfma_16x16x32(av[r], bhi, oacc[8 * m + r]);
-#pragma unroll
-                    for (int r = 0; r < 8; ++r)
-                        oacc[8 * m + r] = mfma_16x16x32(av[r], blo, oacc[8 * m + r]);
-                };
-                pv_group(std::integral_constant<int, 0>{});
-                pv_group(std::integral_constant<int, 1>{});
-                pv_group(std::integral_constant<int, 2>{});
-                pv_group(std::integral_constant<int, 3>{});
+        } else {
+            // the Q fragments (and anything else loaded) are in registers
+            vm_wait<0>();
+            for (int t = 0; t < ntiles; ++t) {
+                lds_barrier();  // B_t
+                compute_tile(tile_buf(t), tile_n(t));
             }
         }
     };
 
-    int n_my = 0, n_valid = 0;
+    int n_valid = 0;
     if (fast) {
-        // valid entries, their ranks in index order (entry order = position)
+        // valid entries, their ranks in index order (entry order = position);
+        // the whole list goes to sm_list
+        uint32_t vm = 0;
+        int c = 0, incl = 0;
+        if (!loader) {
 #pragma unroll
-        for (int u = 0; u < AB_IDX_U; ++u)
-            vm |= (ent[u] >= lo && ent[u] < hi) ? 1u << u : 0u;  // lo >= 0: INVALID drops
-        const int c = __popc(vm);
-        const int incl = wave_inclusive_scan(c);
-        if (lane == 63)
-            sm_wave_tot[wid] = incl;
+            for (int u = 0; u < AB_IDX_U; ++u)
+                vm |= (ent[u] >= lo && ent[u] < hi) ? 1u << u : 0u;  // lo >= 0: INVALID drops
+            c = __popc(vm);
+            incl = wave_inclusive_scan(c);
+            if (lane == 63)
+                sm_wave_tot[wid] = incl;
+        }
         __syncthreads();  // also orders the set-bitmap clear before the inserts
         int before = 0;
 #pragma unroll
-        for (int i = 0; i < AB_NW; ++i) {
+        for (int i = 0; i < AB_CW; ++i) {
             const int t = sm_wave_tot[i];
             before += i < wid ? t : 0;
             n_valid += t;
         }
-        // balanced contiguous shares of the valid entries: the first
-        // n_valid % splits get one more
-        const int per = n_valid / splits, extra = n_valid % splits;
-        const int r0 = split * per + min(split, extra);
-        const int r1 = r0 + per + (split < extra ? 1 : 0);
-        int rank = before + incl - c;
+        if (!loader) {
+            int rank = before + incl - c;
 #pragma unroll
-        for (int u = 0; u < AB_IDX_U; ++u) {
-            if (vm & (1u << u)) {
-                if (rank >= r0 && rank < r1)
-                    sm_list[rank - r0] = ent[u];
-                ++rank;
+            for (int u = 0; u < AB_IDX_U; ++u) {
+                if (vm & (1u << u))
+                    sm_list[rank++] = ent[u];
             }
         }
         __syncthreads();
-        n_my = r1 - r0;
     } else {
         // the set bitmap of the whole row, in one pass
         int first[8];
-        load_indices<AB_NT, 8>(first, idx_row, n_sel, 0);
+        if (!loader)
+            load_indices<AB_CT, 8>(first, idx_row, n_sel, 0);
         __syncthreads();  // the clear above is complete
-        for (int base = 0; base < n_sel; base += AB_NT * 8) {
-            if (base > 0)
-                load_indices<AB_NT, 8>(first, idx_row, n_sel, base);
+        if (!loader) {
+            for (int base = 0; base < n_sel; base += AB_CT * 8) {
+                if (base > 0)
+                    load_indices<AB_CT, 8>(first, idx_row, n_sel, base);
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int j = first[u];
-                if (j >= lo && j < hi)
-                    atomicOr(&sm_set[j >> 5], 1u << (j & 31));
+                for (int u = 0; u < 8; ++u) {
+                    const int j = first[u];
+                    if (j >= lo && j < hi)
+                        atomicOr(&sm_set[j >> 5], 1u << (j & 31));
+                }
             }
         }
         __syncthreads();
     }
 
     int c0, c1;
-    wave_chunk_range<AB_NW>(nw, wid, c0, c1);
+    wave_chunk_range<AB_CW>(nw, min(wid, AB_CW - 1), c0, c1);
+    // balanced contiguous shares of `total` keys: the first total % splits
+    // get one more
+    auto share = [&](int total, int &r0, int &r1) {
+        const int per = total / splits, extra = total % splits;
+        r0 = split * per + min(split, extra);
+        r1 = r0 + per + (split < extra ? 1 : 0);
+    };
+    bool restart = false;
     for (int batch = fast ? -1 : 0;; ++batch) {
-        int re = 0, r1 = 0, total = 0, before = 0;
-        if (batch >= 0) {
+        if (restart) {  // a key repeats: start over on the bitmap
+            reset_acc();
+            restart = false;
+        }
+        // this batch: list entries [first, first + n_my); the fast path's
+        // list is the whole row, the slow path's one batch of its share
+        int first = 0, n_my = 0, re = 0, r1 = 0;
+        if (batch < 0) {
+            share(n_valid, first, r1);
+            n_my = r1 - first;
+        } else {
             // Slow path: the block's share is ranks [r0, r1) of the selected
             // set in ascending key order, in batches of AB_LIST keys.
-            const int wcnt = wave_chunk_count(sm_set, nw, c0, c1);
-            if (lane == 0)
-                sm_wave_tot[wid] = wcnt;
+            int before = 0, total = 0;
+            if (!loader) {
+                const int wcnt = wave_chunk_count(sm_set, nw, c0, c1);
+                if (lane == 0)
+                    sm_wave_tot[wid] = wcnt;
+            }
             __syncthreads();
 #pragma unroll
-            for (int i = 0; i < AB_NW; ++i) {
+            for (int i = 0; i < AB_CW; ++i) {
                 const int t = sm_wave_tot[i];
                 before += i < wid ? t : 0;
                 total += t;
             }
-            const int per = total / splits, extra = total % splits;
-            const int r0 = split * per + min(split, extra);
-            r1 = r0 + per + (split < extra ? 1 : 0);
+            int r0;
+            share(total, r0, r1);
             const int rb = r0 + batch * AB_LIST;
             if (rb >= r1)
                 break;
             re = min(rb + AB_LIST, r1);
-            wave_chunk_extract(sm_set, nw, c0, c1, before, rb, re, sm_list);
+            if (!loader)
+                wave_chunk_extract(sm_set, nw, c0, c1, before, rb, re, sm_list);
             __syncthreads();
             n_my = re - rb;
         }
-        run_tiles(n_my);
-        if (batch < 0) {
-            // the rest of this thread's entries go into the set bitmap; fewer
-            // set bits than valid entries means a key repeats in the row
+        run_tiles(first, n_my);
+        if (batch < 0 && loader) {
+            // the loader puts the listed entries into the set bitmap while
+            // the compute waves finish the last tile
+            for (int i0 = 0; i0 < n_valid; i0 += 64 * AB_KB) {
+                uint32_t ka[AB_KB], key[AB_KB];
 #pragma unroll
-            for (int u = 0; u < AB_IDX_U; ++u)
-                insert_one();
-            lds_barrier();  // every insert is in, every wave is done with the tiles
-            const int wcnt = wave_chunk_count(sm_set, nw, c0, c1);
-            if (lane == 0)
-                sm_wave_tot[wid] = wcnt;
+                for (int b = 0; b < AB_KB; ++b)
+                    ka[b] = lds_list + 4u * (uint32_t)min(i0 + 64 * b + lane, n_valid - 1);
+                lds_read_u32_x6(key, ka);
+#pragma unroll
+                for (int b = 0; b < AB_KB; ++b)
+                    lds_or_async(lds_set + (key[b] >> 5) * 4u, 1u << (key[b] & 31));
+            }
+        }
+        lds_barrier();  // every insert is in, every wave is done with the tiles and the list
+        if (batch < 0) {
+            // fewer set bits than valid entries means a key repeats in the row
+            if (!loader) {
+                const int wcnt = wave_chunk_count(sm_set, nw, c0, c1);
+                if (lane == 0)
+                    sm_wave_tot[wid] = wcnt;
+            }
             __syncthreads();
             int bits = 0;
 #pragma unroll
-            for (int i = 0; i < AB_NW; ++i)
+            for (int i = 0; i < AB_CW; ++i)
                 bits += sm_wave_tot[i];
             if (bits == n_valid)
                 break;
-            reset_acc();
-            fast = false;
+            restart = true;
             __syncthreads();  // sm_wave_tot is rewritten by the first batch
             continue;
         }
         if (re >= r1)
             break;
-        __syncthreads();  // the list is rewritten only after every wave's last tile
     }
+    if (loader)
+        return;
 
     // ---- epilogue: l over the 4 lane groups of the head
     const float l_tot = sum_across_rows(l_part);
@@ -595,6 +669,23 @@ __global__ __launch_bounds__(AB_NT) void attend_gather_kernel(
         if (g == 0)
             ws_ml[pr_] = f32x4_t{l_tot > 0.f ? m_run : -INFINITY, l_tot, (float)e, 0.f};
     }
+}
+
+__global__ __launch_bounds__(AB_NT) void attend_gather_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ kv, int64_t row_stride,
+    const int32_t *__restrict__ idx, const int32_t *__restrict__ vlo,
+    const int32_t *__restrict__ vhi, float *__restrict__ out, float *__restrict__ lse,
+    uint16_t *__restrict__ ws_o, f32x4_t *__restrict__ ws_ml, int n_q, int n_k, int n_sel,
+    int splits, float scale_log2)
+{
+    __shared__ AbsShared shm;
+    DSA_LDS_ESCAPE(shm);
+    if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == AB_CW)
+        attend_gather_role<true>(shm, q, kv, row_stride, idx, vlo, vhi, out, lse, ws_o, ws_ml,
+                                 n_q, n_k, n_sel, splits, scale_log2);
+    else
+        attend_gather_role<false>(shm, q, kv, row_stride, idx, vlo, vhi, out, lse, ws_o, ws_ml,
+                                  n_q, n_k, n_sel, splits, scale_log2);
 }
 
 // Merge the split partials of each (row, head):
