@@ -22,6 +22,7 @@
 // chunk top-ks because the order is total), then one block per row selects
 // and sorts among those candidates.
 #include "dsa_internal.hpp"
+#include <algorithm>
 #include "topk_device.hpp"
 
 namespace dsa {
@@ -82,21 +83,14 @@ __global__ __launch_bounds__(NT) void topk_rows_kernel(const float *__restrict__
     }
 }
 
-// Whole row in one block, sorted output: 32-bit select, stable compaction,
-// stable radix sort (topk_device.hpp).
+// Sorted top-k of the n order keys cached in sm (column lo + i for key i):
+// 32-bit select, compaction, bucket sort (stable radix sort for ties and
+// crowded buckets).  Returns m = min(k, n); the winners' columns in rank
+// order are sm.wcol[buf][0 .. m).
 template <int NT, int CAP>
-__global__ __launch_bounds__(NT) void topk_sorted_kernel(const float *__restrict__ scores,
-                                                         int n_cols, int64_t row_stride,
-                                                         const int32_t *__restrict__ vlo,
-                                                         const int32_t *__restrict__ vhi, int k,
-                                                         int32_t *__restrict__ out)
+__device__ int topk_sort_cached(Topk32Smem<NT, CAP> &sm, int n, int lo, int k, uint32_t omin,
+                                uint32_t omax, int &buf)
 {
-    __shared__ Topk32Smem<NT, CAP> sm;
-    const int tid = threadIdx.x;
-    const int row = blockIdx.x;
-    const int lo = max(vlo[row], 0), hi = min(vhi[row], n_cols);
-    uint32_t omin, omax;
-    const int n = load_row32(sm, scores + (int64_t)row * row_stride, lo, hi, omin, omax);
     // n <= k: everything wins (mask 0 makes every key a candidate, all taken)
     uint32_t prefix = 0u, mask = 0u;
     int need = n, cand = n;
@@ -114,16 +108,188 @@ __global__ __launch_bounds__(NT) void topk_sorted_kernel(const float *__restrict
     int m = any_order ? compact32_any(sm, n, lo, prefix, mask, wmin, wmax)
                       : compact32(sm, n, lo, prefix, mask, need, cand, wmin, wmax);
     bool sorted = (!any_order || wmin != wmax) && bucket_sort32(sm, m, wmin, wmax);
-    int buf = 0;
+    buf = 0;
     if (!sorted) {
         if (any_order)
             m = compact32(sm, n, lo, prefix, mask, need, cand, wmin, wmax);
         // all keys equal: column order is the rank order already
         buf = wmin == wmax ? 0 : sort32(sm, m, wmin, wmax);
     }
+    return m;
+}
+
+// Whole row in one block, sorted output.
+template <int NT, int CAP>
+__global__ __launch_bounds__(NT) void topk_sorted_kernel(const float *__restrict__ scores,
+                                                         int n_cols, int64_t row_stride,
+                                                         const int32_t *__restrict__ vlo,
+                                                         const int32_t *__restrict__ vhi, int k,
+                                                         int32_t *__restrict__ out)
+{
+    __shared__ Topk32Smem<NT, CAP> sm;
+    const int tid = threadIdx.x;
+    const int row = blockIdx.x;
+    const int lo = max(vlo[row], 0), hi = min(vhi[row], n_cols);
+    uint32_t omin, omax;
+    const int n = load_row32(sm, scores + (int64_t)row * row_stride, lo, hi, omin, omax);
+    int buf;
+    const int m = topk_sort_cached(sm, n, lo, k, omin, omax, buf);
     int32_t *o = out + (int64_t)row * k;
     for (int i = tid; i < k; i += NT)
         o[i] = i < m ? (int32_t)sm.wcol[buf][i] : -1;
+}
+
+// Float value of an order key (inverse of score_order_key; -0 comes back
+// as +0).
+__device__ __forceinline__ float order_key_value(uint32_t o)
+{
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+
+// Segmented top-k: `parts` blocks share a row, block `seg` writes output
+// positions [seg*seg_len, seg*seg_len + seg_len) of it, so a few rows still
+// fill the chip.  Every block caches the whole row and counts it into NB
+// buckets linear in the score value over [min, max] (a monotonic map, so a
+// higher bucket never holds a lower-ranked key); the prefix sums give each
+// bucket's first rank.  The block then collects only the buckets that hold
+// its ranks and places each collected key inside its bucket by counting the
+// members with a larger composite key (order key, then smaller column) --
+// the exact rank order, ties included.  No block selects, compacts or sorts
+// the whole row.  When its ranks fall into crowded buckets (a score range
+// stretched by outliers) or the value range is not finite, the block takes
+// the full sorted top-k of the row instead and writes its positions from it.
+constexpr int kSegMaxBucket = 256;
+template <int NT, int CAP>
+__global__ __launch_bounds__(NT) void topk_seg_kernel(const float *__restrict__ scores,
+                                                      int n_cols, int64_t row_stride,
+                                                      const int32_t *__restrict__ vlo,
+                                                      const int32_t *__restrict__ vhi, int k,
+                                                      int32_t *__restrict__ out, int parts,
+                                                      int seg_len)
+{
+    using S = Topk32Smem<NT, CAP>;
+    constexpr int NB = S::NB, NW = S::NW, PB = NB / NT;
+    static_assert(PB >= 1 && NB % NT == 0, "every thread owns whole buckets");
+    __shared__ S sm;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int row = blockIdx.x / parts;
+    const int seg = blockIdx.x - row * parts;
+    const int lo = max(vlo[row], 0), hi = min(vhi[row], n_cols);
+    uint32_t omin, omax;
+    const int n = load_row32(sm, scores + (int64_t)row * row_stride, lo, hi, omin, omax);
+    const int m = min(k, n);
+    int32_t *o = out + (int64_t)row * k;
+    const int p0 = seg * seg_len, p1 = min(p0 + seg_len, k);
+    for (int i = max(p0, m) + tid; i < p1; i += NT)
+        o[i] = -1;
+    const int s0 = p0, s1 = min(p1, m);  // ranks this block writes
+    if (s0 >= s1)
+        return;
+    if (omin == omax) {  // every key equal: column order is the rank order
+        for (int i = s0 + tid; i < s1; i += NT)
+            o[i] = lo + i;
+        return;
+    }
+    const float vmin = order_key_value(omin), vmax = order_key_value(omax);
+    const float scale = (float)NB / (vmax - vmin);
+    bool ok = __builtin_isfinite(vmin) && __builtin_isfinite(vmax) &&
+              __builtin_isfinite(scale) && scale > 0.f;
+    // descending bucket of a key: 0 holds the largest values
+    auto bucket = [&](uint32_t ord) {
+        const int b = (int)((order_key_value(ord) - vmin) * scale);
+        return NB - 1 - min(max(b, 0), NB - 1);
+    };
+    if (ok) {
+        for (int i = tid; i < NB; i += NT)
+            sm.bk.fill[i] = 0u;
+        __syncthreads();
+        for (int i = tid; i < n; i += NT)
+            atomicAdd(&sm.bk.fill[bucket(sm.a.ord[i])], 1u);
+        __syncthreads();
+        // exclusive prefix over the buckets (thread t owns PB consecutive
+        // ones); the buckets holding ranks s0 and s1-1
+        uint32_t v[PB];
+        int sum = 0;
+#pragma unroll
+        for (int j = 0; j < PB; ++j) {
+            v[j] = sm.bk.fill[tid * PB + j];
+            sum += (int)v[j];
+        }
+        const int incl = wave_inclusive_scan(sum);
+        if (lane == 63)
+            sm.tab[0][wid] = incl;
+        __syncthreads();
+        int before = incl - sum;
+#pragma unroll
+        for (int w = 0; w < NW; ++w)
+            before += w < wid ? sm.tab[0][w] : 0;
+        int run = before;
+#pragma unroll
+        for (int j = 0; j < PB; ++j) {
+            const int b = tid * PB + j, c = (int)v[j];
+            sm.bk.off[b] = (uint32_t)run;
+            if (run <= s0 && s0 < run + c)
+                sm.tab[1][0] = b;
+            if (run <= s1 - 1 && s1 - 1 < run + c)
+                sm.tab[1][1] = b;
+            run += c;
+        }
+        __syncthreads();
+        const int bf = sm.tab[1][0], bl = sm.tab[1][1];
+        const int base = (int)sm.bk.off[bf];
+        // crowded buckets in the range make the in-bucket placement costly
+        int crowd = 0;
+#pragma unroll
+        for (int j = 0; j < PB; ++j) {
+            const int b = tid * PB + j;
+            if (b >= bf && b <= bl) {
+                crowd = max(crowd, (int)v[j]);
+                sm.bk.fill[b] = sm.bk.off[b] - (uint32_t)base;  // fill pointers
+            }
+        }
+        crowd = (int)wave_max_u32((uint32_t)crowd);
+        if (lane == 0)
+            sm.red[0][0][wid] = crowd;
+        __syncthreads();
+        int total = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w)
+            crowd = max(crowd, sm.red[0][0][w]);
+        total = (bl + 1 < NB ? (int)sm.bk.off[bl + 1] : n) - base;  // keys of buckets bf .. bl
+        ok = crowd <= kSegMaxBucket && total <= kTopkMaxK;
+        if (ok) {
+            // collect the keys of buckets bf .. bl as composite keys
+            uint64_t *ck = reinterpret_cast<uint64_t *>(&sm.word[1][0]);
+            static_assert(sizeof(sm.word[1]) + sizeof(sm.wcol) >= kTopkMaxK * 8,
+                          "composite key buffer");
+            for (int i = tid; i < n; i += NT) {
+                const uint32_t ord = sm.a.ord[i];
+                const int b = bucket(ord);
+                if (b >= bf && b <= bl)
+                    ck[atomicAdd(&sm.bk.fill[b], 1u)] =
+                        ((uint64_t)ord << 32) | (uint64_t)(0xffffffffu - (uint32_t)(lo + i));
+            }
+            __syncthreads();
+            // rank of each collected key: its bucket's first rank plus the
+            // members of the bucket above it
+            for (int j = tid; j < total; j += NT) {
+                const uint64_t key = ck[j];
+                const int b = bucket((uint32_t)(key >> 32));
+                const int b0 = (int)sm.bk.off[b] - base, b1 = (int)sm.bk.fill[b];
+                int r = (int)sm.bk.off[b];
+                for (int x = b0; x < b1; ++x)
+                    r += ck[x] > key;
+                if (r >= s0 && r < s1)
+                    o[r] = (int32_t)(0xffffffffu - (uint32_t)key);
+            }
+            return;
+        }
+        __syncthreads();  // the bucket arrays are reused below
+    }
+    int buf;
+    topk_sort_cached(sm, n, lo, k, omin, omax, buf);
+    for (int i = s0 + tid; i < s1; i += NT)
+        o[i] = (int32_t)sm.wcol[buf][i];
 }
 
 // Second launch of the long-row path: select and sort among the chunk
@@ -216,6 +382,16 @@ size_t topk_workspace_bytes(int rows, int n_cols, int k)
     return (size_t)rows * (size_t)n_chunks * (size_t)k * sizeof(uint64_t);
 }
 
+// Blocks per row for the segmented kernel: enough for about 256 blocks in
+// all, at most 16, and segments of at least 128 ranks; 1 = one block per row.
+int topk_seg_parts(int rows, int k)
+{
+    int parts = (256 + rows - 1) / rows;
+    parts = std::min(parts, 16);
+    parts = std::min(parts, k / 128);
+    return std::max(parts, 1);
+}
+
 hipError_t launch_topk(const TopkArgs &a, hipStream_t st)
 {
     // sort sizes: NT threads x EPT keys >= k
@@ -226,6 +402,15 @@ hipError_t launch_topk(const TopkArgs &a, hipStream_t st)
     }
     constexpr int NT = 1024;
     if (a.n_cols <= kCapLarge) {
+        // few rows: several blocks per row, each writing a segment of it
+        const int parts = topk_seg_parts(a.rows, a.k);
+        if (parts > 1) {
+            const int seg_len = (a.k + parts - 1) / parts;
+            hipLaunchKernelGGL((topk_seg_kernel<NT, kCapLarge>), dim3(a.rows * parts), dim3(NT),
+                               0, st, a.scores, a.n_cols, a.row_stride, a.vis_lo, a.vis_hi, a.k,
+                               a.out, parts, seg_len);
+            return hipGetLastError();
+        }
         hipLaunchKernelGGL((topk_sorted_kernel<NT, kCapLarge>), dim3(a.rows), dim3(NT), 0, st,
                            a.scores, a.n_cols, a.row_stride, a.vis_lo, a.vis_hi, a.k, a.out);
         return hipGetLastError();

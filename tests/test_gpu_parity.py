@@ -186,6 +186,38 @@ def test_topk_edge_rows(dsa):
             assert got[i].tolist() == exp, (i, k)
 
 
+def test_topk_segmented_rows(dsa):
+    """Few rows, so several blocks share each row and each writes one segment
+    of its ranks: ties straddling segment boundaries and the k-th rank,
+    crowded value buckets, an outlier, a value range that overflows f32, a
+    visibility window, and a k that the segments do not divide."""
+    note("topk segmented rows")
+    rng = np.random.default_rng(33)
+    n = 8192
+    rows = [
+        np.round(rng.standard_normal(n) * 50.0) / 50.0,      # ~400 levels: ties everywhere
+        rng.integers(0, 4, n).astype(np.float64),            # 4 levels: crowded buckets
+        np.concatenate([[1e30], rng.standard_normal(n - 1)]),  # one outlier
+        np.concatenate([[3e38, -3e38], rng.standard_normal(n - 2)]),  # range overflows
+        rng.standard_normal(n),
+        rng.standard_normal(n) * 1e-30,                      # tiny values
+    ]
+    rows = np.stack(rows).astype(np.float32)
+    S = torch.tensor(rows, device="cuda")
+    lo = torch.tensor([0, 0, 0, 0, 1000, 0], dtype=torch.int32, device="cuda")
+    hi = torch.tensor([n, n, n, n, 7000, n], dtype=torch.int32, device="cuda")
+    for k in (2048, 1000, 256):
+        idx = dsa.topk(S, lo, hi, k)
+        torch.cuda.synchronize()
+        got = cpu(idx).numpy()
+        for i in range(rows.shape[0]):
+            l0, h0 = int(lo[i]), int(hi[i])
+            cand = np.arange(l0, h0)
+            order = cand[np.lexsort((cand, -rows[i][l0:h0].astype(np.float64)))][:k]
+            exp = np.concatenate([order, np.full(k - order.size, INV)])
+            assert (got[i] == exp).all(), (i, k, np.nonzero(got[i] != exp)[0][:8])
+
+
 # ---------------------------------------------------------------- attention
 
 def _oracle_sel(inp, S, k):
