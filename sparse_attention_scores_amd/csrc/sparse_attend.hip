@@ -657,15 +657,30 @@ __device__ __forceinline__ void attend_gather_role(
         amax = max_across_rows(amax);
         const int e = __builtin_amdgcn_frexp_expf(amax) - 15;
         const int64_t pr_ = ((int64_t)row * splits + split) * AB_H + head;
-        uint16_t *op = ws_o + pr_ * AB_VD + 4 * g;
+        // The wave's 16 x 512 fp16 block goes through LDS (the tile ring is
+        // free now; each wave has a region of its own) so that every store
+        // instruction writes one whole 1 KB head row: the accumulator layout
+        // would scatter each store over 16 rows in 32-byte pieces.  Rows are
+        // padded by 16 bytes to spread the transposing writes over the banks.
+        constexpr int SROW = AB_VD + 8;  // fp16 per staged row
+        static_assert(AB_CW * 16 * SROW * 2 <= (int)sizeof(AbsTiles), "staging fits the tiles");
+        uint16_t *stg = reinterpret_cast<uint16_t *>(sm.tile[0]) + wid * 16 * SROW;
 #pragma unroll
         for (int n = 0; n < AB_NC; ++n) {
             typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
             const f32x4_t sc = {ldexpf(oacc[n][0], -e), ldexpf(oacc[n][1], -e),
                                 ldexpf(oacc[n][2], -e), ldexpf(oacc[n][3], -e)};
-            *reinterpret_cast<u32x2_t *>(op + n * 16) =
+            *reinterpret_cast<u32x2_t *>(stg + col * SROW + 16 * n + 4 * g) =
                 __builtin_bit_cast(u32x2_t, __builtin_convertvector(sc, h4_t));
         }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        uint16_t *op = ws_o + (pr_ - col) * AB_VD + 8 * lane;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            *reinterpret_cast<u32x4_t *>(op + r * AB_VD) =
+                *reinterpret_cast<const u32x4_t *>(stg + r * SROW + 8 * lane);
         if (g == 0)
             ws_ml[pr_] = f32x4_t{l_tot > 0.f ? m_run : -INFINITY, l_tot, (float)e, 0.f};
     }
