@@ -317,6 +317,46 @@ __device__ __forceinline__ void lds_read_u32_x6(uint32_t (&v)[6], const uint32_t
         : "memory");
 }
 
+// N 16-byte LDS reads from per-lane byte addresses and the wait for them, in
+// one asm statement (N = 4 or 8).
+__device__ __forceinline__ void lds_read_b128_a4(u32x4_t (&v)[4], const uint32_t (&a)[4])
+{
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %5\n\t"
+        "ds_read_b128 %2, %6\n\t"
+        "ds_read_b128 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+        : "memory");
+}
+__device__ __forceinline__ void lds_read_b128_a8(u32x4_t (&v)[8], const uint32_t (&a)[8])
+{
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %9\n\t"
+        "ds_read_b128 %2, %10\n\t"
+        "ds_read_b128 %3, %11\n\t"
+        "ds_read_b128 %4, %12\n\t"
+        "ds_read_b128 %5, %13\n\t"
+        "ds_read_b128 %6, %14\n\t"
+        "ds_read_b128 %7, %15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
+          "=&v"(v[6]), "=&v"(v[7])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]),
+          "v"(a[7])
+        : "memory");
+}
+// One 4-byte LDS read and the wait for it.
+__device__ __forceinline__ uint32_t lds_read_u32_wait(uint32_t a)
+{
+    uint32_t v;
+    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(a) : "memory");
+    return v;
+}
+
 // 32-bit LDS byte address of a pointer into shared memory.
 __device__ __forceinline__ uint32_t lds_addr(const void *p)
 {

@@ -18,6 +18,8 @@
 
 #include <float.h>
 
+#include <algorithm>
+
 namespace dsa {
 
 // D: head_dim; MT: 32-head groups (n_heads = 32*MT); QPW: queries per wave;
@@ -183,6 +185,168 @@ __global__ __launch_bounds__(256) void index_scores_mfma_kernel(
         ga = gb;
         act_a = act_b;
         tile = nxt;
+    }
+}
+
+// Decode kernel (one query per block): the same MFMA tile and epilogue, but
+// each wave streams its key tiles through an LDS ring of its own.  A tile's
+// rows arrive by direct-to-LDS 16-byte loads, every load instruction one
+// contiguous 1 KB of key rows (whole cache lines), with the 16-byte chunks of
+// row r stored at chunk ^ (r & (chunks per row - 1)); the B operands are then
+// read from LDS, where 32 rows at one chunk hit different banks.  (Loaded
+// straight in the operand layout, one instruction touches 32 rows in 32-byte
+// pieces, and the key stream ran about an eighth slower, measured.)  The
+// fp8 keys' per-row scales ride along as one 4-byte-per-lane load per tile.
+// No barrier: a wave reads only the tiles it loaded, after waiting for them.
+constexpr int ID_STAGES = 2;
+template <int D, int MT, bool FP8>
+__global__ __launch_bounds__(256) void index_scores_decode_kernel(
+    const uint16_t *__restrict__ q, const void *__restrict__ kv, const float *__restrict__ kscale,
+    const float *__restrict__ w, const int32_t *__restrict__ vlo, const int32_t *__restrict__ vhi,
+    float *__restrict__ scores, int n_q, int n_k, float scale, int n_chunks, int chunk)
+{
+    constexpr int H = 32 * MT;
+    constexpr int KS = D / 16;                      // MFMA k-steps of 16 dims
+    constexpr int RB = D * (FP8 ? 1 : 2);           // bytes per key row
+    constexpr int CPR = RB / 16;                    // 16-byte chunks per row
+    constexpr int TB = 32 * RB;                     // tile bytes
+    constexpr int DPT = TB / 1024;                  // load instructions per tile
+    constexpr int VPT = DPT + (FP8 ? 1 : 0);        // vector-memory ops per tile
+    constexpr int NCH = FP8 ? KS / 2 : KS;          // 16-byte operand chunks per lane
+    constexpr int SB = TB + (FP8 ? 256 : 0);        // stage bytes (tile, k-scales)
+    static_assert(TB % 1024 == 0 && (NCH == 4 || NCH == 8), "tile shape");
+    __shared__ __attribute__((aligned(16))) unsigned char ring[4][ID_STAGES][SB];
+    DSA_LDS_ESCAPE(ring);
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 5, col = lane & 31;
+
+    int bid = blockIdx.x;
+    const int kc = bid % n_chunks;
+    bid /= n_chunks;
+    const int64_t qrow = bid;                       // (batch, query) row
+    const int64_t b = qrow / n_q;
+    const int lo = max(vlo[qrow], 0), hi = min(vhi[qrow], n_k);
+
+    // q fragments and head weights (as in the tile kernel above)
+    u32x4_t qf[MT][KS];
+    float wr[MT][16];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int head = mt * 32 + col;
+        const uint16_t *qp = q + (qrow * H + head) * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int d0 = FP8 ? g * (D / 2) + ks * 8 : ks * 16 + g * 8;
+            qf[mt][ks] = *reinterpret_cast<const u32x4_t *>(qp + d0);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            wr[mt][i] = w[qrow * H + mt * 32 + 8 * (i / 4) + 4 * g + (i % 4)];
+    }
+
+    // this wave's tiles of the chunk, and the ones that see a key
+    const int c0 = kc * chunk, c1 = min(c0 + chunk, n_k);
+    const int ntc = (c1 - c0 + 31) / 32;
+    const int wt0 = wid * ntc / 4, wt1 = (wid + 1) * ntc / 4;
+    int at0 = wt1, at1 = wt1;
+    if (lo < hi) {
+        at0 = min(max(wt0, (lo - c0) / 32), wt1);
+        at1 = max(min(wt1, (hi - c0 + 31) / 32), at0);
+    }
+    float *srow = scores + qrow * n_k;
+    // keys of the wave's tiles outside [at0, at1) see nothing
+    for (int s = c0 + wt0 * 32 + lane; s < min(c1, c0 + at0 * 32); s += 64)
+        srow[s] = -FLT_MAX;
+    for (int s = c0 + at1 * 32 + lane; s < min(c1, c0 + wt1 * 32); s += 64)
+        srow[s] = -FLT_MAX;
+
+    // load slot of this lane in instruction i: (row, byte offset of the
+    // logical chunk it fetches), fixed over tiles
+    uint32_t dslot[DPT];
+#pragma unroll
+    for (int i = 0; i < DPT; ++i) {
+        const int off = i * 1024 + lane * 16, r = off / RB, pc = (off % RB) / 16;
+        dslot[i] = ((uint32_t)r << 16) | (uint32_t)((pc ^ (r & (CPR - 1))) * 16);
+    }
+    // operand chunk offsets inside a stage: key col, logical chunk lc
+    uint32_t rofs[NCH];
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+        const int lc = FP8 ? g * (CPR / 2) + j : 2 * j + g;
+        rofs[j] = (uint32_t)(col * RB + (lc ^ (col & (CPR - 1))) * 16);
+    }
+    const unsigned char *kbase =
+        reinterpret_cast<const unsigned char *>(kv) + b * (int64_t)n_k * RB;
+    auto load_tile = [&](int t, int st) {
+        const int s0 = c0 + t * 32;
+        unsigned char *dst = ring[wid][st];
+#pragma unroll
+        for (int i = 0; i < DPT; ++i) {
+            const int r = min(s0 + (int)(dslot[i] >> 16), n_k - 1);
+            lds_dma16(kbase + (int64_t)r * RB + (dslot[i] & 0xffffu), dst + i * 1024);
+        }
+        if constexpr (FP8)
+            lds_dma4(kscale + b * n_k + min(s0 + col, n_k - 1), dst + TB);
+    };
+
+    vm_wait<0>();  // q and w are in registers: the ring's waits count tiles only
+    const int nt = at1 - at0;
+    for (int j = 0; j < ID_STAGES - 1 && j < nt; ++j)
+        load_tile(at0 + j, j);
+    for (int t = 0; t < nt; ++t) {
+        vm_wait_tiles<VPT>(min(nt - 1, t + ID_STAGES - 2) - t);  // tile t is in
+        if (t + ID_STAGES - 1 < nt)  // refill the stage read in the last iteration
+            load_tile(at0 + t + ID_STAGES - 1, (t + ID_STAGES - 1) % ID_STAGES);
+        const uint32_t sb = lds_addr(ring[wid][t % ID_STAGES]);
+        uint32_t ad[NCH];
+#pragma unroll
+        for (int j = 0; j < NCH; ++j)
+            ad[j] = sb + rofs[j];
+        u32x4_t kf[KS];
+        float gsc = scale;
+        if constexpr (NCH == 8) {
+            u32x4_t v[8];
+            lds_read_b128_a8(v, ad);
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                kf[FP8 ? 2 * j : j] = v[j];
+        } else {
+            u32x4_t v[4];
+            lds_read_b128_a4(v, ad);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                kf[FP8 ? 2 * j : j] = v[j];
+        }
+        if constexpr (FP8) {
+            gsc = scale * __uint_as_float(lds_read_u32_wait(sb + TB + 4 * col));
+            // 16 raw e4m3 codes per chunk -> two k-steps of 8 bf16
+#pragma unroll
+            for (int p = KS / 2 - 1; p >= 0; --p) {
+                const u32x4_t c = kf[2 * p];
+                const u32x2_t a0 = e4m3x4_to_bf16x4(c[0]);
+                const u32x2_t a1 = e4m3x4_to_bf16x4(c[1]);
+                const u32x2_t a2 = e4m3x4_to_bf16x4(c[2]);
+                const u32x2_t a3 = e4m3x4_to_bf16x4(c[3]);
+                kf[2 * p] = u32x4_t{a0[0], a0[1], a1[0], a1[1]};
+                kf[2 * p + 1] = u32x4_t{a2[0], a2[1], a3[0], a3[1]};
+            }
+        }
+        float part = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            f32x16_t acc = {};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                acc = mfma_32x32x16(qf[mt][ks], kf[ks], acc);
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                part += wr[mt][i] * fmaxf(acc[i] * gsc, 0.f);
+        }
+        part += __shfl_xor(part, 32, kWave);
+        const int key = c0 + (at0 + t) * 32 + col;
+        if (lane < 32 && key < c1)
+            srow[key] = (key >= lo && key < hi) ? part : -FLT_MAX;
     }
 }
 
@@ -403,6 +567,24 @@ static hipError_t launch_mfma(const IndexArgs &a, hipStream_t st)
     return hipGetLastError();
 }
 
+// Decode launch: chunks sized for about two blocks per CU (at least 128 keys,
+// a multiple of 128 so each of the 4 waves has whole tiles).
+template <int D, int MT, bool FP8>
+static hipError_t launch_decode(const IndexArgs &a, hipStream_t st)
+{
+    const int64_t rows = (int64_t)a.batch * a.n_q;
+    int64_t chunk = ((int64_t)a.n_k * rows + 511) / 512;
+    chunk = std::max<int64_t>(128, (chunk + 127) / 128 * 128);
+    const int n_chunks = (int)((a.n_k + chunk - 1) / chunk);
+    const int64_t blocks = rows * n_chunks;
+    if (blocks > 0x7fffffff || chunk > 0x7fffffff)
+        return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((index_scores_decode_kernel<D, MT, FP8>), dim3((unsigned)blocks), dim3(256),
+                       0, st, static_cast<const uint16_t *>(a.q), a.k, a.k_scale, a.w, a.vis_lo,
+                       a.vis_hi, a.scores, a.n_q, a.n_k, a.scale, n_chunks, (int)chunk);
+    return hipGetLastError();
+}
+
 template <int D, int MT, bool FP8>
 static hipError_t launch_mfma_mode(const IndexArgs &a, hipStream_t st)
 {
@@ -422,7 +604,10 @@ static hipError_t launch_mfma_mode(const IndexArgs &a, hipStream_t st)
     }
     if (a.n_q >= 8)
         return launch_mfma<D, MT, 2, 4, FP8>(a, st);
-    return launch_mfma<D, MT, 1, 1, FP8>(a, st);
+    if constexpr (FP8 && D == 64)  // 64-byte rows: too few chunks for the ring's swizzle
+        return launch_mfma<D, MT, 1, 1, FP8>(a, st);
+    else
+        return launch_decode<D, MT, FP8>(a, st);
 }
 
 template <int D, int MT>
