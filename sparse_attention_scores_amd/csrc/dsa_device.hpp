@@ -451,6 +451,11 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
     return wave_reduce_bits(v, [](uint32_t x, uint32_t y) { return x > y ? x : y; });
 }
 
+__device__ __forceinline__ int wave_sum_int(int v)
+{
+    return (int)wave_reduce_bits((uint32_t)v, [](uint32_t x, uint32_t y) { return x + y; });
+}
+
 // max / sum over the four lanes l, l^16, l^32, l^48 (the four 16-lane rows)
 // with the gfx950 row-swap instructions: v_permlane16_swap pairs each lane
 // with its partner one row away, v_permlane32_swap with the partner half a

@@ -5,83 +5,25 @@
 // rest INVALID (ik_llama.cpp PR #2063, batch-local indexer commit:
 // top_k(min(top_k, n_tokens))).
 //
-// Each candidate becomes one 64-bit composite key
+// A key's place in that order is its composite key
 //     (order_key(score) << 32) | (0xffffffff - column)
-// whose unsigned order is exactly the rank order (larger key = better rank),
-// with -0 folded onto +0.  All keys of a row are distinct, so "the k
-// largest keys" is one well-defined set and the selection is exact.
+// (larger = better rank, -0 folded onto +0); all keys of a row are
+// distinct, so "the k largest keys" is one well-defined set.
 //
-// One block owns a row (or a chunk of a long row):
-//  1. the row's order keys are cached in LDS (coalesced loads);
-//  2. a block-wide min/max finds the bits all keys share;
-//  3. radix select, 8 bits per pass starting below the shared bits, with an
-//     LDS histogram, finds the threshold T with exactly k keys >= T;
-//  4. the k winners are compacted to LDS and bitonic-sorted (descending).
-// Rows longer than one block's cache run in two launches: each chunk keeps
-// its own k largest keys (the global top-k is a subset of the union of the
-// chunk top-ks because the order is total), then one block per row selects
-// and sorts among those candidates.
+// Paths, by shape (every one exact):
+//  * many rows, up to 16384 keys: one block per row -- 32-bit radix select
+//    over the cached order keys, compaction, bucket sort (topk_sorted_kernel);
+//  * few rows, up to 16384 keys: several blocks per row, each writing one
+//    segment of the ranks from value buckets (topk_seg_kernel);
+//  * longer rows: each 16384-key chunk keeps its own top k (the global top-k
+//    is a subset of the union of the chunk top-ks, the order being total),
+//    then a merge selects and sorts among those candidates -- segmented over
+//    several blocks per row when the candidates fit one block's cache.
 #include "dsa_internal.hpp"
 #include <algorithm>
 #include "topk_device.hpp"
 
 namespace dsa {
-
-// Mode 0: whole row in one block, writes the sorted index row.
-// Mode 1: chunk c of the row, writes its (unsorted) winners as composite
-//         keys to ws[row][c][0..k), zero-padded.
-template <int NT, int CAP, int MODE, int EPT>
-__global__ __launch_bounds__(NT) void topk_rows_kernel(const float *__restrict__ scores,
-                                                       int n_cols, int64_t row_stride,
-                                                       const int32_t *__restrict__ vlo,
-                                                       const int32_t *__restrict__ vhi, int k,
-                                                       int32_t *__restrict__ out,
-                                                       uint64_t *__restrict__ ws, int n_chunks)
-{
-    __shared__ TopkSmem<NT, CAP> sm;
-    const int tid = threadIdx.x;
-    int row, chunk = 0;
-    if (MODE == 0) {
-        row = blockIdx.x;
-    } else {
-        row = blockIdx.x / n_chunks;
-        chunk = blockIdx.x % n_chunks;
-    }
-    int lo = max(vlo[row], 0), hi = min(vhi[row], n_cols);
-    if (MODE == 1) {
-        const int c0 = chunk * CAP;
-        lo = max(lo, c0);
-        hi = min(hi, c0 + CAP);
-    }
-    const float *rp = scores + (int64_t)row * row_stride;
-    const int n = load_row(sm, rp, lo, hi);
-    auto key_at = [&](int i) -> uint64_t { return compose_key(sm.ord[i], (uint32_t)(lo + i)); };
-    int m;
-    if (n > k) {
-        radix_select(sm, n, k, key_at);
-        m = k;
-    } else {
-        for (int i = tid; i < n; i += NT)
-            sm.sel[i] = key_at(i);
-        __syncthreads();
-        m = n;
-    }
-    if (MODE == 0) {
-        uint64_t v[EPT];
-        bitonic_sort_regs<NT, EPT>(sm, m, v);
-        int32_t *o = out + (int64_t)row * k;
-#pragma unroll
-        for (int b = 0; b < EPT; ++b) {
-            const int i = tid * EPT + b;
-            if (i < k)
-                o[i] = i < m ? (int32_t)(0xffffffffu - (uint32_t)v[b]) : -1;
-        }
-    } else {
-        uint64_t *o = ws + ((int64_t)row * n_chunks + chunk) * k;
-        for (int i = tid; i < k; i += NT)
-            o[i] = i < m ? sm.sel[i] : 0ull;
-    }
-}
 
 // Sorted top-k of the n order keys cached in sm (column lo + i for key i):
 // 32-bit select, compaction, bucket sort (stable radix sort for ties and
@@ -298,17 +240,17 @@ __global__ __launch_bounds__(NT) void topk_seg_kernel(const float *__restrict__ 
 // CACHE the candidates (at most CACHE_KEYS) are first copied to LDS in one
 // batched pass, so the select passes re-read LDS instead of global memory.
 constexpr int kMergeCacheKeys = 16384;
+template <int NT, bool CACHE>
+using MergeSmem = TopkSmem<NT, CACHE ? 2 * kMergeCacheKeys : 1>;
+
+// Sorted top-k of the n candidates cand[0 .. n): m = min(k, real candidates)
+// and, on return, v[b] of thread t holds the key of rank t*EPT + b.
 template <int NT, int EPT, bool CACHE>
-__global__ __launch_bounds__(NT) void topk_merge_kernel(const uint64_t *__restrict__ ws,
-                                                        int n_chunks, int k,
-                                                        int32_t *__restrict__ out)
+__device__ void merge_sorted(MergeSmem<NT, CACHE> &sm, const uint64_t *__restrict__ cand, int n,
+                             int k, uint64_t (&v)[EPT], int &m)
 {
-    // CACHE: the 64-bit candidates live in sm.ord (two words each)
-    __shared__ TopkSmem<NT, CACHE ? 2 * kMergeCacheKeys : 1> sm;
     const int tid = threadIdx.x;
-    const int row = blockIdx.x;
-    const uint64_t *cand = ws + (int64_t)row * n_chunks * k;
-    const int n = n_chunks * k;
+    // CACHE: the 64-bit candidates live in sm.ord (two words each)
     uint64_t *cache = reinterpret_cast<uint64_t *>(sm.ord);
     // count the real candidates (and fill the cache)
     if (tid == 0)
@@ -318,18 +260,18 @@ __global__ __launch_bounds__(NT) void topk_merge_kernel(const uint64_t *__restri
     if (CACHE) {
         constexpr int U = 8;
         for (int base = 0; base < n; base += NT * U) {
-            uint64_t v[U];
+            uint64_t x[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int i = base + u * NT + tid;
-                v[u] = i < n ? cand[i] : 0ull;
+                x[u] = i < n ? cand[i] : 0ull;
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int i = base + u * NT + tid;
                 if (i < n) {
-                    cache[i] = v[u];
-                    local += v[u] != 0ull;
+                    cache[i] = x[u];
+                    local += x[u] != 0ull;
                 }
             }
         }
@@ -342,7 +284,6 @@ __global__ __launch_bounds__(NT) void topk_merge_kernel(const uint64_t *__restri
     const int real = sm.count;
     __syncthreads();
     auto key_at = [&](int i) -> uint64_t { return CACHE ? cache[i] : cand[i]; };
-    int m;
     if (real > k) {
         radix_select(sm, n, k, key_at);
         m = k;
@@ -360,14 +301,340 @@ __global__ __launch_bounds__(NT) void topk_merge_kernel(const uint64_t *__restri
         __syncthreads();
         m = real;
     }
-    uint64_t v[EPT];
     bitonic_sort_regs<NT, EPT>(sm, m, v);
+}
+
+template <int NT, int EPT, bool CACHE>
+__global__ __launch_bounds__(NT) void topk_merge_kernel(const uint64_t *__restrict__ ws,
+                                                        int n_chunks, int k,
+                                                        int32_t *__restrict__ out)
+{
+    __shared__ MergeSmem<NT, CACHE> sm;
+    const int tid = threadIdx.x;
+    const int row = blockIdx.x;
+    uint64_t v[EPT];
+    int m;
+    merge_sorted<NT, EPT, CACHE>(sm, ws + (int64_t)row * n_chunks * k, n_chunks * k, k, v, m);
     int32_t *o = out + (int64_t)row * k;
 #pragma unroll
     for (int b = 0; b < EPT; ++b) {
         const int i = tid * EPT + b;
         if (i < k)
             o[i] = i < m ? (int32_t)(0xffffffffu - (uint32_t)v[b]) : -1;
+    }
+}
+
+// Value buckets of a row segment (shared by the bucket kernels below): NB
+// buckets linear in the score value over [vmin, vmax], numbered from the top
+// (bucket 0 holds the largest values).  The map is monotonic, so every key
+// of a lower-numbered bucket ranks above every key of a higher-numbered one.
+struct ValueBuckets {
+    float vmin, scale;
+    int nb;
+    __device__ bool init(uint32_t omin, uint32_t omax, int nbuckets)
+    {
+        nb = nbuckets;
+        vmin = order_key_value(omin);
+        const float vmax = order_key_value(omax);
+        scale = (float)nb / (vmax - vmin);
+        return __builtin_isfinite(vmin) && __builtin_isfinite(vmax) &&
+               __builtin_isfinite(scale) && scale > 0.f;
+    }
+    __device__ int operator()(uint32_t ord) const
+    {
+        const int b = (int)((order_key_value(ord) - vmin) * scale);
+        return nb - 1 - min(max(b, 0), nb - 1);
+    }
+};
+
+// First launch of the long-row path: chunk c of the row keeps its exact top
+// min(k, n_c) keys, as composite keys in any order, in ws[row][c][0 .. k),
+// zero-padded.  The chunk's keys are counted into value buckets; every key
+// of a bucket above the one that holds rank k-1 wins outright, and the
+// members of that boundary bucket are ranked among themselves by composite
+// key for the remaining places.  Without a finite value range, or with a
+// crowded boundary bucket, the 32-bit select and compaction decide instead.
+template <int NT, int CAP>
+__global__ __launch_bounds__(NT) void topk_chunk_kernel(const float *__restrict__ scores,
+                                                        int n_cols, int64_t row_stride,
+                                                        const int32_t *__restrict__ vlo,
+                                                        const int32_t *__restrict__ vhi, int k,
+                                                        uint64_t *__restrict__ ws, int n_chunks)
+{
+    using S = Topk32Smem<NT, CAP>;
+    constexpr int NB = S::NB, NW = S::NW, PB = NB / NT, R = CAP / NT;
+    static_assert(PB >= 1 && NB % NT == 0, "every thread owns whole buckets");
+    __shared__ S sm;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const uint64_t lt = (1ull << lane) - 1ull;
+    const int row = blockIdx.x / n_chunks;
+    const int chunk = blockIdx.x - row * n_chunks;
+    const int c0 = chunk * CAP;
+    const int lo = max(max(vlo[row], 0), c0);
+    const int hi = min(min(vhi[row], n_cols), c0 + CAP);
+    uint32_t omin, omax;
+    const int n = load_row32(sm, scores + (int64_t)row * row_stride, lo, hi, omin, omax);
+    uint64_t *o = ws + ((int64_t)row * n_chunks + chunk) * k;
+    const int m = min(k, n);
+    for (int i = m + tid; i < k; i += NT)
+        o[i] = 0ull;
+    if (n <= k) {
+        for (int i = tid; i < n; i += NT)
+            o[i] = compose_key(sm.a.ord[i], (uint32_t)(lo + i));
+        return;
+    }
+    ValueBuckets bucket;
+    if (omin != omax && bucket.init(omin, omax, NB)) {
+        for (int i = tid; i < NB; i += NT)
+            sm.bk.fill[i] = 0u;
+        if (tid == 0) {
+            sm.fill = 0;
+            sm.bincnt = 0;
+        }
+        __syncthreads();
+        for (int i = tid; i < n; i += NT)
+            atomicAdd(&sm.bk.fill[bucket(sm.a.ord[i])], 1u);
+        __syncthreads();
+        // the bucket holding rank k-1, the ranks above it and its size
+        uint32_t v[PB];
+        int sum = 0;
+#pragma unroll
+        for (int j = 0; j < PB; ++j) {
+            v[j] = sm.bk.fill[tid * PB + j];
+            sum += (int)v[j];
+        }
+        const int incl = wave_inclusive_scan(sum);
+        if (lane == 63)
+            sm.tab[0][wid] = incl;
+        __syncthreads();
+        int run = incl - sum;
+#pragma unroll
+        for (int w = 0; w < NW; ++w)
+            run += w < wid ? sm.tab[0][w] : 0;
+#pragma unroll
+        for (int j = 0; j < PB; ++j) {
+            const int c = (int)v[j];
+            if (run <= k - 1 && k - 1 < run + c) {
+                sm.bin = tid * PB + j;
+                sm.above = run;
+                sm.red[0][0][0] = c;
+            }
+            run += c;
+        }
+        __syncthreads();
+        const int bb = sm.bin, above = sm.above, cnt_b = sm.red[0][0][0];
+        if (cnt_b <= kSegMaxBucket) {
+            uint64_t *ck = reinterpret_cast<uint64_t *>(&sm.word[1][0]);
+            const int rounds = (n + NT - 1) / NT;
+            for (int r = 0; r < rounds; ++r) {  // uniform
+                const int i = r * NT + tid;
+                const uint32_t ord = i < n ? sm.a.ord[i] : 0u;
+                const int b = i < n ? bucket(ord) : NB;
+                const uint64_t win = __ballot(b < bb);
+                int base = 0;
+                if (lane == 0 && win)
+                    base = atomicAdd(&sm.fill, __popcll(win));
+                base = __builtin_amdgcn_readfirstlane(base);
+                if (b < bb)
+                    o[base + __popcll(win & lt)] = compose_key(ord, (uint32_t)(lo + i));
+                else if (b == bb)
+                    ck[atomicAdd(&sm.bincnt, 1)] = compose_key(ord, (uint32_t)(lo + i));
+            }
+            __syncthreads();
+            for (int j = tid; j < cnt_b; j += NT) {
+                const uint64_t key = ck[j];
+                int r = 0;
+                for (int x = 0; x < cnt_b; ++x)
+                    r += ck[x] > key;
+                if (above + r < k)
+                    o[above + r] = key;
+            }
+            return;
+        }
+        __syncthreads();  // the bucket arrays are reused below
+    }
+    uint32_t prefix, mask;
+    int need, cand;
+    select32(sm, n, k, omin, omax, prefix, mask, need, cand);
+    uint32_t wmin, wmax;
+    const int mm = cand == need ? compact32_any(sm, n, lo, prefix, mask, wmin, wmax)
+                                : compact32(sm, n, lo, prefix, mask, need, cand, wmin, wmax);
+    for (int i = tid; i < mm; i += NT)
+        o[i] = compose_key(sm.word[0][i], sm.wcol[0][i]);
+    (void)R;
+}
+
+// Second launch of the long-row path for few rows: `parts` blocks share a
+// row's candidates (the chunk winners ws[row][0 .. n), zero keys padding;
+// at most kMergeCacheKeys), block `seg` writes output positions
+// [seg*seg_len, seg*seg_len + seg_len), as in topk_seg_kernel: value buckets
+// over the real candidates, the buckets that hold the block's ranks
+// collected and ranked inside by composite key.  Crowded buckets or a
+// non-finite range fall back to the full merge of the row.
+template <int NT>
+__global__ __launch_bounds__(NT) void topk_merge_seg_kernel(const uint64_t *__restrict__ ws,
+                                                            int n_chunks, int k,
+                                                            int32_t *__restrict__ out, int parts,
+                                                            int seg_len)
+{
+    using S = Topk32Smem<NT, kMergeCacheKeys>;
+    using M = MergeSmem<NT, true>;
+    constexpr int NB = S::NB, NW = S::NW, PB = NB / NT;
+    union U {
+        S a;
+        M b;
+    };
+    __shared__ U u;
+    S &sm = u.a;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int row = blockIdx.x / parts;
+    const int seg = blockIdx.x - row * parts;
+    const uint64_t *cand = ws + (int64_t)row * n_chunks * k;
+    const int n = n_chunks * k;
+    // order keys of the candidates (0 = padding: a real key's order part is
+    // at least 0x007fffff), their count and range
+    int nv = 0;
+    uint32_t mn = ~0u, mx = 0u;
+    {
+        constexpr int U8 = 8;
+        for (int base = 0; base < n; base += NT * U8) {
+            uint64_t x[U8];
+#pragma unroll
+            for (int u8 = 0; u8 < U8; ++u8) {
+                const int i = base + u8 * NT + tid;
+                x[u8] = i < n ? cand[i] : 0ull;
+            }
+#pragma unroll
+            for (int u8 = 0; u8 < U8; ++u8) {
+                const int i = base + u8 * NT + tid;
+                if (i < n) {
+                    const uint32_t ord = (uint32_t)(x[u8] >> 32);
+                    sm.a.ord[i] = ord;
+                    if (ord) {
+                        ++nv;
+                        mn = min(mn, ord);
+                        mx = max(mx, ord);
+                    }
+                }
+            }
+        }
+    }
+    nv = wave_sum_int(nv);
+    mn = wave_min_u32(mn);
+    mx = wave_max_u32(mx);
+    if (lane == 0) {
+        sm.mm[0][wid] = mn;
+        sm.mm[1][wid] = mx;
+        sm.red[0][0][wid] = nv;
+    }
+    __syncthreads();
+    uint32_t omin = ~0u, omax = 0u;
+    int n_valid = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        omin = min(omin, sm.mm[0][w]);
+        omax = max(omax, sm.mm[1][w]);
+        n_valid += sm.red[0][0][w];
+    }
+    __syncthreads();
+    const int m = min(k, n_valid);
+    int32_t *o = out + (int64_t)row * k;
+    const int p0 = seg * seg_len, p1 = min(p0 + seg_len, k);
+    for (int i = max(p0, m) + tid; i < p1; i += NT)
+        o[i] = -1;
+    const int s0 = p0, s1 = min(p1, m);  // ranks this block writes
+    if (s0 >= s1)
+        return;
+    ValueBuckets bucket;
+    if (omin != omax && bucket.init(omin, omax, NB)) {
+        for (int i = tid; i < NB; i += NT)
+            sm.bk.fill[i] = 0u;
+        __syncthreads();
+        for (int i = tid; i < n; i += NT) {
+            const uint32_t ord = sm.a.ord[i];
+            if (ord)
+                atomicAdd(&sm.bk.fill[bucket(ord)], 1u);
+        }
+        __syncthreads();
+        uint32_t v[PB];
+        int sum = 0;
+#pragma unroll
+        for (int j = 0; j < PB; ++j) {
+            v[j] = sm.bk.fill[tid * PB + j];
+            sum += (int)v[j];
+        }
+        const int incl = wave_inclusive_scan(sum);
+        if (lane == 63)
+            sm.tab[0][wid] = incl;
+        __syncthreads();
+        int run = incl - sum;
+#pragma unroll
+        for (int w = 0; w < NW; ++w)
+            run += w < wid ? sm.tab[0][w] : 0;
+#pragma unroll
+        for (int j = 0; j < PB; ++j) {
+            const int b = tid * PB + j, c = (int)v[j];
+            sm.bk.off[b] = (uint32_t)run;
+            if (run <= s0 && s0 < run + c)
+                sm.tab[1][0] = b;
+            if (run <= s1 - 1 && s1 - 1 < run + c)
+                sm.tab[1][1] = b;
+            run += c;
+        }
+        __syncthreads();
+        const int bf = sm.tab[1][0], bl = sm.tab[1][1];
+        const int base = (int)sm.bk.off[bf];
+        int crowd = 0;
+#pragma unroll
+        for (int j = 0; j < PB; ++j) {
+            const int b = tid * PB + j;
+            if (b >= bf && b <= bl) {
+                crowd = max(crowd, (int)v[j]);
+                sm.bk.fill[b] = sm.bk.off[b] - (uint32_t)base;
+            }
+        }
+        crowd = (int)wave_max_u32((uint32_t)crowd);
+        if (lane == 0)
+            sm.red[1][0][wid] = crowd;
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < NW; ++w)
+            crowd = max(crowd, sm.red[1][0][w]);
+        const int total = (bl + 1 < NB ? (int)sm.bk.off[bl + 1] : n_valid) - base;
+        if (crowd <= kSegMaxBucket && total <= kTopkMaxK) {
+            uint64_t *ck = reinterpret_cast<uint64_t *>(&sm.word[1][0]);
+            for (int i = tid; i < n; i += NT) {
+                const uint32_t ord = sm.a.ord[i];
+                if (ord) {
+                    const int b = bucket(ord);
+                    if (b >= bf && b <= bl)
+                        ck[atomicAdd(&sm.bk.fill[b], 1u)] = cand[i];
+                }
+            }
+            __syncthreads();
+            for (int j = tid; j < total; j += NT) {
+                const uint64_t key = ck[j];
+                const int b = bucket((uint32_t)(key >> 32));
+                const int b0 = (int)sm.bk.off[b] - base, b1 = (int)sm.bk.fill[b];
+                int r = (int)sm.bk.off[b];
+                for (int x = b0; x < b1; ++x)
+                    r += ck[x] > key;
+                if (r >= s0 && r < s1)
+                    o[r] = (int32_t)(0xffffffffu - (uint32_t)key);
+            }
+            return;
+        }
+    }
+    __syncthreads();  // the segment path's LDS is reused by the full merge
+    constexpr int EPT = 2;
+    uint64_t v[EPT];
+    int mm;
+    merge_sorted<NT, EPT, true>(u.b, cand, n, k, v, mm);
+#pragma unroll
+    for (int b = 0; b < EPT; ++b) {
+        const int i = tid * EPT + b;
+        if (i >= s0 && i < s1)
+            o[i] = (int32_t)(0xffffffffu - (uint32_t)v[b]);
     }
 }
 
@@ -382,13 +649,14 @@ size_t topk_workspace_bytes(int rows, int n_cols, int k)
     return (size_t)rows * (size_t)n_chunks * (size_t)k * sizeof(uint64_t);
 }
 
-// Blocks per row for the segmented kernel: enough for about 256 blocks in
-// all, at most 16, and segments of at least 128 ranks; 1 = one block per row.
-int topk_seg_parts(int rows, int k)
+// Blocks per row for the segmented kernels: enough for about 256 blocks in
+// all, at most max_parts, and segments of at least 64 ranks; 1 = one block
+// per row.
+int topk_seg_parts(int rows, int k, int max_parts)
 {
     int parts = (256 + rows - 1) / rows;
-    parts = std::min(parts, 16);
-    parts = std::min(parts, k / 128);
+    parts = std::min(parts, max_parts);
+    parts = std::min(parts, k / 64);
     return std::max(parts, 1);
 }
 
@@ -403,7 +671,7 @@ hipError_t launch_topk(const TopkArgs &a, hipStream_t st)
     constexpr int NT = 1024;
     if (a.n_cols <= kCapLarge) {
         // few rows: several blocks per row, each writing a segment of it
-        const int parts = topk_seg_parts(a.rows, a.k);
+        const int parts = topk_seg_parts(a.rows, a.k, 16);
         if (parts > 1) {
             const int seg_len = (a.k + parts - 1) / parts;
             hipLaunchKernelGGL((topk_seg_kernel<NT, kCapLarge>), dim3(a.rows * parts), dim3(NT),
@@ -416,12 +684,20 @@ hipError_t launch_topk(const TopkArgs &a, hipStream_t st)
         return hipGetLastError();
     }
     const int n_chunks = (a.n_cols + kCapLarge - 1) / kCapLarge;
-    hipLaunchKernelGGL((topk_rows_kernel<NT, kCapLarge, 1, 2>), dim3(a.rows * n_chunks),
-                       dim3(NT), 0, st, a.scores, a.n_cols, a.row_stride, a.vis_lo, a.vis_hi, a.k,
-                       a.out, static_cast<uint64_t *>(a.workspace), n_chunks);
+    hipLaunchKernelGGL((topk_chunk_kernel<NT, kCapLarge>), dim3(a.rows * n_chunks), dim3(NT), 0,
+                       st, a.scores, a.n_cols, a.row_stride, a.vis_lo, a.vis_hi, a.k,
+                       static_cast<uint64_t *>(a.workspace), n_chunks);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
+    const int mparts = topk_seg_parts(a.rows, a.k, 32);
+    if ((int64_t)n_chunks * a.k <= kMergeCacheKeys && mparts > 1) {
+        const int seg_len = (a.k + mparts - 1) / mparts;
+        hipLaunchKernelGGL((topk_merge_seg_kernel<NT>), dim3(a.rows * mparts), dim3(NT), 0, st,
+                           static_cast<const uint64_t *>(a.workspace), n_chunks, a.k, a.out,
+                           mparts, seg_len);
+        return hipGetLastError();
+    }
     if ((int64_t)n_chunks * a.k <= kMergeCacheKeys)
         hipLaunchKernelGGL((topk_merge_kernel<NT, 2, true>), dim3(a.rows), dim3(NT), 0, st,
                            static_cast<const uint64_t *>(a.workspace), n_chunks, a.k, a.out);

@@ -218,6 +218,40 @@ def test_topk_segmented_rows(dsa):
             assert (got[i] == exp).all(), (i, k, np.nonzero(got[i] != exp)[0][:8])
 
 
+def test_topk_long_rows_segmented_merge(dsa):
+    """Rows longer than one block's cache whose chunk winners fit the merge
+    cache, so the merge is split over several blocks per row: quantized
+    ties, four levels (crowded buckets), an outlier, every score equal,
+    plain values, and a window that leaves the last chunk short."""
+    note("topk long rows, segmented merge")
+    rng = np.random.default_rng(44)
+    n, k = 100000, 2048
+    rows = [
+        np.round(rng.standard_normal(n) * 50.0) / 50.0,
+        rng.integers(0, 4, n).astype(np.float64),
+        np.concatenate([[1e30], rng.standard_normal(n - 1)]),
+        np.full(n, 0.25),
+        rng.standard_normal(n),
+        rng.standard_normal(n),
+    ]
+    rows = np.stack(rows).astype(np.float32)
+    S = torch.tensor(rows, device="cuda")
+    lo = torch.tensor([0, 0, 0, 0, 0, 30000], dtype=torch.int32, device="cuda")
+    hi = torch.tensor([n, n, n, n, n, 50100], dtype=torch.int32, device="cuda")
+    for kk in (k, 700):
+        ws = torch.empty(max(dsa.topk_workspace_size(rows.shape[0], n, kk), 1), dtype=torch.uint8,
+                         device="cuda")
+        idx = dsa.topk(S, lo, hi, kk, workspace=ws)
+        torch.cuda.synchronize()
+        got = cpu(idx).numpy()
+        for i in range(rows.shape[0]):
+            l0, h0 = int(lo[i]), int(hi[i])
+            cand = np.arange(l0, h0)
+            order = cand[np.lexsort((cand, -rows[i][l0:h0].astype(np.float64)))][:kk]
+            exp = np.concatenate([order, np.full(kk - order.size, INV)])
+            assert (got[i] == exp).all(), (i, kk, np.nonzero(got[i] != exp)[0][:8])
+
+
 # ---------------------------------------------------------------- attention
 
 def _oracle_sel(inp, S, k):
