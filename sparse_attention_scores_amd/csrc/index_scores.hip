@@ -361,6 +361,13 @@ constexpr int IP_D = 128, IP_H = 32, IP_QPW = 2, IP_NW = 8, IP_QB = IP_QPW * IP_
 constexpr int IP_TILEB = 32 * IP_D * 2, IP_STAGES = 3;
 static_assert(IP_TILEB == 1024 * IP_NW, "one DMA instruction per wave per tile");
 
+// Balance: under a causal mask the number of key tiles a query block sees
+// grows with its position, and with about one block per CU the kernel would
+// last as long as the latest block.  Query blocks are therefore paired (the
+// i-th earliest with the i-th latest) and each pair's visible tiles, the
+// later block's first, are split evenly between two workgroups; a
+// workgroup reloads the queries when its share moves on to the earlier
+// block.
 __global__ __launch_bounds__(64 * IP_NW) void index_scores_prefill_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kv, const float *__restrict__ w,
     const int32_t *__restrict__ vlo, const int32_t *__restrict__ vhi, float *__restrict__ scores,
@@ -372,18 +379,26 @@ __global__ __launch_bounds__(64 * IP_NW) void index_scores_prefill_kernel(
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int g = lane >> 5, col = lane & 31;
+    const int n_pairs = (n_qblocks + 1) / 2;
     int bid = blockIdx.x;
+    const int half = bid & 1;
+    bid >>= 1;
     const int kc = bid % n_chunks;
     bid /= n_chunks;
-    // latest query blocks first: under a causal mask they see the most keys,
-    // and the light early blocks then fill in behind them
-    const int qblk = n_qblocks - 1 - bid % n_qblocks;
-    const int b = bid / n_qblocks;
+    const int pair = bid % n_pairs;
+    const int b = bid / n_pairs;
+    const int qb_late = n_qblocks - 1 - pair, qb_early = pair;  // equal for a middle block
 
-    // the block's queries and the union of their visible ranges
-    int ulo = n_k, uhi = 0;
-    {
-        const int t = qblk * IP_QB + (lane & (IP_QB - 1));
+    const int c0 = kc * chunk;
+    const int c1 = min(c0 + chunk, n_k);
+    const int nt = (c1 - c0 + 31) / 32;
+    const bool neg_scale = scale < 0.f;
+    const unsigned char *kb = reinterpret_cast<const unsigned char *>(kv) + (int64_t)b * n_k * IP_D * 2;
+
+    // tiles [ta, tb) of the chunk hold a key some query of block qb sees
+    auto visible_tiles = [&](int qb, int &ta, int &tb) {
+        int ulo = n_k, uhi = 0;
+        const int t = qb * IP_QB + (lane & (IP_QB - 1));
         if (t < n_q) {
             const int64_t r = (int64_t)b * n_q + t;
             ulo = max(vlo[r], 0);
@@ -395,50 +410,18 @@ __global__ __launch_bounds__(64 * IP_NW) void index_scores_prefill_kernel(
         }
         ulo = (int)wave_min_u32((uint32_t)ulo);
         uhi = (int)wave_max_u32((uint32_t)uhi);
-    }
-    u32x4_t qf[IP_QPW][KS];
-    float wr[IP_QPW][16];
-    int lo[IP_QPW], hi[IP_QPW];
-    int64_t qrow[IP_QPW];
-    bool qok[IP_QPW];
-#pragma unroll
-    for (int qi = 0; qi < IP_QPW; ++qi) {
-        const int t = qblk * IP_QB + wid * IP_QPW + qi;
-        qok[qi] = t < n_q;
-        qrow[qi] = (int64_t)b * n_q + (qok[qi] ? t : 0);
-        lo[qi] = qok[qi] ? max(vlo[qrow[qi]], 0) : 0;
-        hi[qi] = qok[qi] ? min(vhi[qrow[qi]], n_k) : 0;
-        const uint16_t *qp = q + (qrow[qi] * IP_H + col) * IP_D + g * 8;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            qf[qi][ks] = *reinterpret_cast<const u32x4_t *>(qp + ks * 16);
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-            wr[qi][i] = w[qrow[qi] * IP_H + 8 * (i / 4) + 4 * g + (i % 4)] * fabsf(scale);
-    }
-    const bool neg_scale = scale < 0.f;
+        ta = ulo < uhi ? min(nt, max(0, (ulo - c0) / 32)) : nt;
+        tb = ulo < uhi ? max(ta, min(nt, (uhi - c0 + 31) / 32)) : nt;
+    };
+    int la, lb, ea = 0, eb = 0;
+    visible_tiles(qb_late, la, lb);
+    if (qb_early != qb_late)
+        visible_tiles(qb_early, ea, eb);
+    // the pair's visible tiles, the later block's first, split in two halves
+    const int n_late = lb - la, n_all = n_late + (eb - ea);
+    const int cut = (n_all + 1) / 2;
+    const int w0 = half ? cut : 0, w1 = half ? n_all : cut;
 
-    const int c0 = kc * chunk;
-    const int c1 = min(c0 + chunk, n_k);
-    const int nt = (c1 - c0 + 31) / 32;
-    // tiles [ta, tb) hold a key some query of the block sees
-    const int ta = ulo < uhi ? max(0, (ulo - c0) / 32) : nt;
-    const int tb = ulo < uhi ? min(nt, (uhi - c0 + 31) / 32) : nt;
-
-    // tiles no query sees: -FLT_MAX
-    for (int tt = 0; tt < nt; ++tt) {
-        if (tt >= ta && tt < tb)
-            continue;
-        const int key = c0 + tt * 32 + col;
-#pragma unroll
-        for (int qi = 0; qi < IP_QPW; ++qi)
-            if (lane < 32 && key < c1 && qok[qi])
-                scores[qrow[qi] * n_k + key] = -FLT_MAX;
-    }
-    if (ta >= tb)
-        return;
-
-    const unsigned char *kb = reinterpret_cast<const unsigned char *>(kv) + (int64_t)b * n_k * IP_D * 2;
     // DMA: wave w fills LDS bytes w*1024 + 16*lane of the tile = row r, physical
     // chunk p <- logical chunk p ^ (r & 15) of key c0 + 32*tile + r
     const int dr = (wid * 64 + lane) / 16;
@@ -454,69 +437,130 @@ __global__ __launch_bounds__(64 * IP_NW) void index_scores_prefill_kernel(
         kaddr[ks] = (uint32_t)((col * 16 + ((2 * ks + g) ^ (col & 15))) * 16);
     const uint32_t lds0 = lds_addr(tiles[0]);
 
-    // epilogue of one tile: w * relu(scale * s) = (w * |scale|) * max(sign(scale) * s, 0),
-    // summed over the lane's 16 heads and the other half-wave's 16
-    auto finish = [&](const f32x16_t(&acc)[IP_QPW], int tt) {
-        const int key = c0 + tt * 32 + col;
+    // Tiles [t0, t1) (chunk tile indices, all visible to block qb) for the
+    // wave's queries of block qb, and the -FLT_MAX rows of the block's
+    // invisible tiles of this half's parity (the two halves share that work).
+    auto run = [&](int qb, int t0, int t1, int ta, int tb) {
+        u32x4_t qf[IP_QPW][KS];
+        float wr[IP_QPW][16];
+        int lo[IP_QPW], hi[IP_QPW];
+        int64_t qrow[IP_QPW];
+        bool qok[IP_QPW];
 #pragma unroll
         for (int qi = 0; qi < IP_QPW; ++qi) {
-            float part = 0.f;
-            if (neg_scale) {
+            const int t = qb * IP_QB + wid * IP_QPW + qi;
+            qok[qi] = t < n_q;
+            qrow[qi] = (int64_t)b * n_q + (qok[qi] ? t : 0);
+            lo[qi] = qok[qi] ? max(vlo[qrow[qi]], 0) : 0;
+            hi[qi] = qok[qi] ? min(vhi[qrow[qi]], n_k) : 0;
+            // the sign of the scale goes into q (bf16 sign bits), so the
+            // epilogue is relu(s) * (w * |scale|) whatever the sign
+            const uint16_t *qp = q + (qrow[qi] * IP_H + col) * IP_D + g * 8;
+            const uint32_t qsign = neg_scale ? 0x80008000u : 0u;
 #pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    part += wr[qi][i] * fmaxf(-acc[qi][i], 0.f);
-            } else {
+            for (int ks = 0; ks < KS; ++ks)
+                qf[qi][ks] = *reinterpret_cast<const u32x4_t *>(qp + ks * 16) ^ qsign;
 #pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    part += wr[qi][i] * fmaxf(acc[qi][i], 0.f);
-            }
-            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part),
-                                                             __float_as_uint(part), false, false);
-            part = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-            if (lane < 32 && key < c1 && qok[qi])
-                scores[qrow[qi] * n_k + key] = (key >= lo[qi] && key < hi[qi]) ? part : -FLT_MAX;
+            for (int i = 0; i < 16; ++i)
+                wr[qi][i] = w[qrow[qi] * IP_H + 8 * (i / 4) + 4 * g + (i % 4)] * fabsf(scale);
         }
-    };
-
-    // the query data are in registers before the first tile DMA
-    vm_wait<0>();
-    for (int j = 0; j < IP_STAGES - 1 && ta + j < tb; ++j)
-        dma_tile(ta + j, j);
-    for (int tt = ta; tt < tb; ++tt) {
-        const int st = (tt - ta) % IP_STAGES;
-        vm_wait_tiles<1>(min(tb - 1, tt + IP_STAGES - 2) - tt);
-        lds_barrier();
-        if (tt + IP_STAGES - 1 < tb)
-            dma_tile(tt + IP_STAGES - 1, (tt - ta + IP_STAGES - 1) % IP_STAGES);
-        const uint32_t base = lds0 + st * IP_TILEB;
-        u32x4_t kf[KS];
-        asm volatile(
-            "ds_read_b128 %0, %8\n\t"
-            "ds_read_b128 %1, %9\n\t"
-            "ds_read_b128 %2, %10\n\t"
-            "ds_read_b128 %3, %11\n\t"
-            "ds_read_b128 %4, %12\n\t"
-            "ds_read_b128 %5, %13\n\t"
-            "ds_read_b128 %6, %14\n\t"
-            "ds_read_b128 %7, %15\n\t"
-            "s_waitcnt lgkmcnt(0)"
-            : "=&v"(kf[0]), "=&v"(kf[1]), "=&v"(kf[2]), "=&v"(kf[3]), "=&v"(kf[4]),
-              "=&v"(kf[5]), "=&v"(kf[6]), "=&v"(kf[7])
-            : "v"(base + kaddr[0]), "v"(base + kaddr[1]), "v"(base + kaddr[2]),
-              "v"(base + kaddr[3]), "v"(base + kaddr[4]), "v"(base + kaddr[5]),
-              "v"(base + kaddr[6]), "v"(base + kaddr[7])
-            : "memory");
-        f32x16_t acc[IP_QPW];
+        {
+            for (int tt = half; tt < nt; tt += 2) {
+                if (tt >= ta && tt < tb)
+                    continue;
+                const int key = c0 + tt * 32 + col;
 #pragma unroll
-        for (int qi = 0; qi < IP_QPW; ++qi)
-            acc[qi] = f32x16_t{};
+                for (int qi = 0; qi < IP_QPW; ++qi)
+                    if (lane < 32 && key < c1 && qok[qi])
+                        scores[qrow[qi] * n_k + key] = -FLT_MAX;
+            }
+        }
+        if (t0 >= t1)
+            return;
+        // epilogue of one tile: w * relu(scale * s) = (w * |scale|) * relu(sign(scale) * s),
+        // summed over the lane's 16 heads and the other half-wave's 16; relu
+        // is a signed-integer max on the bits (negative floats, -0 included,
+        // are negative integers), one instruction per element
+        auto finish = [&](const f32x16_t(&acc)[IP_QPW], int tt) {
+            const int key = c0 + tt * 32 + col;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
+            for (int qi = 0; qi < IP_QPW; ++qi) {
+                float part = 0.f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    part += wr[qi][i] * __int_as_float(max(__float_as_int(acc[qi][i]), 0));
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part),
+                                                                 __float_as_uint(part), false, false);
+                part = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+                if (lane < 32 && key < c1 && qok[qi])
+                    scores[qrow[qi] * n_k + key] =
+                        (key >= lo[qi] && key < hi[qi]) ? part : -FLT_MAX;
+            }
+        };
+        // the query data are in registers before the first tile DMA
+        vm_wait<0>();
+        for (int j = 0; j < IP_STAGES - 1 && t0 + j < t1; ++j)
+            dma_tile(t0 + j, j);
+        // Tile tt's MFMAs into acc (after the ring barrier that releases it).
+        // The loop issues tile tt+1's MFMAs before tile tt's epilogue, so the
+        // epilogue's VALU work runs while the matrix core is busy (all waves
+        // reach the ring barrier together, so without this their MFMA and
+        // VALU phases would coincide).
+        auto mma = [&](int tt, f32x16_t(&acc)[IP_QPW]) {
+            const int st = (tt - t0) % IP_STAGES;
+            vm_wait_tiles<1>(min(t1 - 1, tt + IP_STAGES - 2) - tt);
+            lds_barrier();
+            if (tt + IP_STAGES - 1 < t1)
+                dma_tile(tt + IP_STAGES - 1, (tt - t0 + IP_STAGES - 1) % IP_STAGES);
+            const uint32_t base = lds0 + st * IP_TILEB;
+            u32x4_t kf[KS];
+            asm volatile(
+                "ds_read_b128 %0, %8\n\t"
+                "ds_read_b128 %1, %9\n\t"
+                "ds_read_b128 %2, %10\n\t"
+                "ds_read_b128 %3, %11\n\t"
+                "ds_read_b128 %4, %12\n\t"
+                "ds_read_b128 %5, %13\n\t"
+                "ds_read_b128 %6, %14\n\t"
+                "ds_read_b128 %7, %15\n\t"
+                "s_waitcnt lgkmcnt(0)"
+                : "=&v"(kf[0]), "=&v"(kf[1]), "=&v"(kf[2]), "=&v"(kf[3]), "=&v"(kf[4]),
+                  "=&v"(kf[5]), "=&v"(kf[6]), "=&v"(kf[7])
+                : "v"(base + kaddr[0]), "v"(base + kaddr[1]), "v"(base + kaddr[2]),
+                  "v"(base + kaddr[3]), "v"(base + kaddr[4]), "v"(base + kaddr[5]),
+                  "v"(base + kaddr[6]), "v"(base + kaddr[7])
+                : "memory");
 #pragma unroll
             for (int qi = 0; qi < IP_QPW; ++qi)
-                acc[qi] = mfma_32x32x16(qf[qi][ks], kf[ks], acc[qi]);
-        finish(acc, tt);
-    }
+                acc[qi] = f32x16_t{};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int qi = 0; qi < IP_QPW; ++qi)
+                    acc[qi] = mfma_32x32x16(qf[qi][ks], kf[ks], acc[qi]);
+        };
+        f32x16_t acc_a[IP_QPW], acc_b[IP_QPW];
+        mma(t0, acc_a);
+        int tt = t0 + 1;
+        for (; tt + 1 < t1; tt += 2) {
+            mma(tt, acc_b);
+            finish(acc_a, tt - 1);
+            mma(tt + 1, acc_a);
+            finish(acc_b, tt);
+        }
+        if (tt < t1) {
+            mma(tt, acc_b);
+            finish(acc_a, tt - 1);
+            finish(acc_b, tt);
+        } else {
+            finish(acc_a, tt - 1);
+        }
+        lds_barrier();  // every wave is done with the ring before it is refilled
+    };
+    // this half's share of the pair's list
+    run(qb_late, la + min(w0, n_late), la + min(w1, n_late), la, lb);
+    if (qb_early != qb_late)
+        run(qb_early, ea + max(w0 - n_late, 0), ea + max(w1 - n_late, 0), ea, eb);
 }
 
 // Plain f32 kernel: one thread per (query row, key).
@@ -593,7 +637,8 @@ static hipError_t launch_mfma_mode(const IndexArgs &a, hipStream_t st)
         const int n_qblocks = (a.n_q + IP_QB - 1) / IP_QB;
         const int chunk = 4096;
         const int n_chunks = (a.n_k + chunk - 1) / chunk;
-        const int64_t blocks = (int64_t)a.batch * n_qblocks * n_chunks;
+        // two workgroups per pair of query blocks (see the kernel)
+        const int64_t blocks = (int64_t)a.batch * ((n_qblocks + 1) / 2) * n_chunks * 2;
         if (blocks > 0x7fffffff)
             return hipErrorInvalidConfiguration;
         hipLaunchKernelGGL(index_scores_prefill_kernel, dim3((unsigned)blocks), dim3(64 * IP_NW), 0,

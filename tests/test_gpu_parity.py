@@ -89,6 +89,24 @@ def test_index_scores_parity(dsa, cfg, over, variant):
     check_scores(cpu(S).numpy().reshape(ref.shape), ref, A, rtol, f"config {cfg}")
 
 
+@pytest.mark.parametrize("cfg,over", [(3, dict(Tq=200, Tk=200)), (2, dict(B=2, Tk=1000)),
+                                      (4, dict(B=1, Tk=2000))])
+def test_index_scores_negative_scale_and_weights(dsa, cfg, over):
+    """A negative scale and weights of both signs (prefill, decode, fp8 keys)."""
+    note(f"index scores negative scale config {cfg} {over}")
+    inp = W.make(cfg, device="cuda", **over)
+    scale = -abs(inp["scale_idx"])
+    w = inp["w"] - 0.5
+    lo, hi = _ranges(dsa, inp)
+    S = dsa.index_scores(inp["q_idx"], inp["k_idx"], w, lo, hi, scale, k_scale=inp["k_scale"])
+    torch.cuda.synchronize()
+    ref, A = oracle.index_scores(cpu(inp["q_idx"]), cpu(inp["k_idx"]), cpu(w), scale,
+                                 cpu(inp["q_pos"]), cpu(inp["pad"]),
+                                 k_scale=None if inp["k_scale"] is None else cpu(inp["k_scale"]),
+                                 want_mag=True)
+    check_scores(cpu(S).numpy().reshape(ref.shape), ref, A, 1e-3, f"config {cfg} negative scale")
+
+
 def test_index_scores_padding_and_pooled_ranges(dsa):
     note("index scores: left padding + pooled visibility")
     B, L, H, d, kp = 3, 70, 32, 128, 4
