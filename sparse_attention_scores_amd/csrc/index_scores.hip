@@ -501,12 +501,15 @@ __global__ __launch_bounds__(64 * IP_NW) void index_scores_prefill_kernel(
         vm_wait<0>();
         for (int j = 0; j < IP_STAGES - 1 && t0 + j < t1; ++j)
             dma_tile(t0 + j, j);
-        // Tile tt's MFMAs into acc (after the ring barrier that releases it).
-        // The loop issues tile tt+1's MFMAs before tile tt's epilogue, so the
-        // epilogue's VALU work runs while the matrix core is busy (all waves
-        // reach the ring barrier together, so without this their MFMA and
-        // VALU phases would coincide).
-        auto mma = [&](int tt, f32x16_t(&acc)[IP_QPW]) {
+        // Tile tt's MFMAs into acc (after the ring barrier that releases it),
+        // interleaved with the epilogue sums of the previous tile (prev, if
+        // `fin`): a wave issues in order, and a run of MFMAs would hold it at
+        // each one until the matrix core takes it, so the VALU work goes in
+        // between -- two relu-weighted terms after each MFMA, pinned by
+        // scheduling-group barriers -- and the two streams overlap.
+        auto step = [&](int tt, f32x16_t(&acc)[IP_QPW], const f32x16_t(&prev)[IP_QPW],
+                        float (&part)[IP_QPW], bool fin) {
+            static_assert(IP_QPW == 2, "the sums are pinned for two queries");
             const int st = (tt - t0) % IP_STAGES;
             vm_wait_tiles<1>(min(t1 - 1, tt + IP_STAGES - 2) - tt);
             lds_barrier();
@@ -531,26 +534,56 @@ __global__ __launch_bounds__(64 * IP_NW) void index_scores_prefill_kernel(
                   "v"(base + kaddr[6]), "v"(base + kaddr[7])
                 : "memory");
 #pragma unroll
-            for (int qi = 0; qi < IP_QPW; ++qi)
+            for (int qi = 0; qi < IP_QPW; ++qi) {
                 acc[qi] = f32x16_t{};
+                part[qi] = 0.f;
+            }
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
+            for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-                for (int qi = 0; qi < IP_QPW; ++qi)
+                for (int qi = 0; qi < IP_QPW; ++qi) {
                     acc[qi] = mfma_32x32x16(qf[qi][ks], kf[ks], acc[qi]);
+                    if (fin) {
+                        // MFMA number j = 2ks + qi takes terms 2(j%8), 2(j%8)+1 of
+                        // query j/8
+                        const int j = 2 * ks + qi, pq = j / 8, i0 = 2 * (j % 8);
+#pragma unroll
+                        for (int i = i0; i < i0 + 2; ++i)
+                            part[pq] += wr[pq][i] * __int_as_float(max(__float_as_int(prev[pq][i]), 0));
+                    }
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // then VALU
+                }
+            }
+            // the sums are complete here (kept from sinking past the MFMAs)
+            asm volatile("" : "+v"(part[0]), "+v"(part[1]));
+        };
+        // the head sum's second half and the stores of tile tt
+        auto store = [&](float (&part)[IP_QPW], int tt) {
+            const int key = c0 + tt * 32 + col;
+#pragma unroll
+            for (int qi = 0; qi < IP_QPW; ++qi) {
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[qi]),
+                                                                 __float_as_uint(part[qi]), false,
+                                                                 false);
+                const float v = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+                if (lane < 32 && key < c1 && qok[qi])
+                    scores[qrow[qi] * n_k + key] = (key >= lo[qi] && key < hi[qi]) ? v : -FLT_MAX;
+            }
         };
         f32x16_t acc_a[IP_QPW], acc_b[IP_QPW];
-        mma(t0, acc_a);
+        float part[IP_QPW];
+        step(t0, acc_a, acc_b, part, false);
         int tt = t0 + 1;
         for (; tt + 1 < t1; tt += 2) {
-            mma(tt, acc_b);
-            finish(acc_a, tt - 1);
-            mma(tt + 1, acc_a);
-            finish(acc_b, tt);
+            step(tt, acc_b, acc_a, part, true);
+            store(part, tt - 1);
+            step(tt + 1, acc_a, acc_b, part, true);
+            store(part, tt);
         }
         if (tt < t1) {
-            mma(tt, acc_b);
-            finish(acc_a, tt - 1);
+            step(tt, acc_b, acc_a, part, true);
+            store(part, tt - 1);
             finish(acc_b, tt);
         } else {
             finish(acc_a, tt - 1);
