@@ -111,6 +111,37 @@ __device__ __forceinline__ void lds_read_tr16x4_8(u32x2_t (&a)[8], uint32_t r0, 
         : "memory");
 }
 
+// Three 16-byte LDS reads with one base each and the wait.
+template <int O0, int O1, int O2>
+__device__ __forceinline__ void lds_read_b128_3(u32x4_t (&a)[3], uint32_t b0, uint32_t b1,
+                                                uint32_t b2)
+{
+    asm volatile(
+        "ds_read_b128 %0, %3 offset:%6\n\t"
+        "ds_read_b128 %1, %4 offset:%7\n\t"
+        "ds_read_b128 %2, %5 offset:%8\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2])
+        : "v"(b0), "v"(b1), "v"(b2), "i"(O0), "i"(O1), "i"(O2)
+        : "memory");
+}
+
+// Four transposing LDS reads (2 column tiles x rows ra / rb) and the wait.
+template <int O>
+__device__ __forceinline__ void lds_read_tr16x4_4(u32x2_t (&a)[4], uint32_t r0, uint32_t r1,
+                                                  uint32_t s0, uint32_t s1)
+{
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %4 offset:%8\n\t"
+        "ds_read_b64_tr_b16 %1, %6 offset:%8\n\t"
+        "ds_read_b64_tr_b16 %2, %5 offset:%8\n\t"
+        "ds_read_b64_tr_b16 %3, %7 offset:%8\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3])
+        : "v"(r0), "v"(r1), "v"(s0), "v"(s1), "i"(O)
+        : "memory");
+}
+
 // Three 4-byte LDS reads and the wait (asm: the words arrive by direct-to-LDS
 // loads, and the compiler would otherwise wait for every such load in flight).
 __device__ __forceinline__ void lds_read_b32_3(uint32_t &x, uint32_t &y, uint32_t &z,
@@ -144,7 +175,7 @@ struct __attribute__((aligned(16))) MaskedSmem {
 // each wave issues the same number of loads per tile (7 of the 28 K/V
 // instructions plus its mask words), so a counted wait finds its tile.
 template <int KD, int VD>
-__global__ __launch_bounds__(256) void attend_masked_kernel(
+__global__ __launch_bounds__(256, 2) void attend_masked_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, int64_t ksr,
     const uint16_t *__restrict__ v, int64_t vsr, const uint32_t *__restrict__ mask,
     const int32_t *__restrict__ vlo, const int32_t *__restrict__ vhi, float *__restrict__ out,
@@ -228,33 +259,33 @@ __global__ __launch_bounds__(256) void attend_masked_kernel(
     const uint32_t *mrow =
         mask + ((int64_t)b * n_q + min(q0 + wid * 32 + col, n_q - 1)) * nw;
 
-    // DMA slots of this wave: instruction s = wid + 4i (i < 7) of the tile's
-    // 28 (12 for K, then 16 for V); row in bits 16+, byte offset in the low 16
-    uint32_t slot[PER];
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        const int s_ = wid + 4 * i;
-        if (s_ < Sm::KB / 1024) {
-            const int c = s_ * 64 + lane, r = c / KCH;
-            slot[i] = ((uint32_t)r << 16) | (uint32_t)(((c % KCH) ^ mk_swz_k(r)) * 16);
-        } else {
-            const int c = (s_ - Sm::KB / 1024) * 64 + lane, r = c / VCH;
-            slot[i] = ((uint32_t)r << 16) | (uint32_t)(((c % VCH) ^ mk_swz_v(r)) * 16);
-        }
-    }
+    // DMA: this wave issues instructions s = wid + 4i (i < 7) of the tile's 28
+    // (12 for K, then 16 for V); lane l of instruction s fills LDS bytes
+    // 16l of that KB = (row, physical chunk), fetching the row's logical chunk
+    // (recomputed per tile: a few VALU instead of seven live registers)
     const uint32_t ksr2 = (uint32_t)(ksr * 2), vsr2 = (uint32_t)(vsr * 2);
     auto dma_tile = [&](int t, int st) {
         const int k0 = t * 32;
+        // an opaque copy of the lane index keeps the compiler from hoisting the
+        // seven 64-bit addresses out of the tile loop (as live registers)
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int s_ = wid + 4 * i;
-            const int key = min(k0 + (int)(slot[i] >> 16), n_k - 1);  // rows past n_k masked
-            if (s_ < Sm::KB / 1024)
-                lds_dma16(kb + (uint64_t)(uint32_t)key * ksr2 + (slot[i] & 0xffffu),
+            if (s_ < Sm::KB / 1024) {
+                const int c = s_ * 64 + ln, r = c / KCH;
+                const int key = min(k0 + r, n_k - 1);  // rows past n_k are masked
+                lds_dma16(kb + (uint64_t)(uint32_t)key * ksr2 +
+                              (uint32_t)(((c % KCH) ^ mk_swz_k(r)) * 16),
                           sm.k[st] + s_ * 1024);
-            else
-                lds_dma16(vb + (uint64_t)(uint32_t)key * vsr2 + (slot[i] & 0xffffu),
+            } else {
+                const int c = (s_ - Sm::KB / 1024) * 64 + ln, r = c / VCH;
+                const int key = min(k0 + r, n_k - 1);
+                lds_dma16(vb + (uint64_t)(uint32_t)key * vsr2 +
+                              (uint32_t)(((c % VCH) ^ mk_swz_v(r)) * 16),
                           sm.v[st] + (s_ - Sm::KB / 1024) * 1024);
+            }
         }
         lds_dma4(mrow + t, sm.mw[st][wid]);
     };
@@ -306,17 +337,24 @@ __global__ __launch_bounds__(256) void attend_masked_kernel(
         f32x16_t s = {};
         {
             const uint32_t kt = lds_k + st * Sm::KB;
-            u32x4_t a6[6];
-            lds_read_b128_6<0, 0, 0, 0, 128, 128>(a6, kt + kq[0], kt + kq[1], kt + kq[2],
-                                                  kt + kq[3], kt + kq[0], kt + kq[1]);
+            // k-step ks reads base kq[ks & 3] + 128 * (ks >> 2), in groups of 3
+            u32x4_t a3[3];
+            lds_read_b128_3<0, 0, 0>(a3, kt + kq[0], kt + kq[1], kt + kq[2]);
 #pragma unroll
-            for (int j = 0; j < 6; ++j)
-                s = mfma_32x32x16(a6[j], qf[j], s);
-            lds_read_b128_6<128, 128, 256, 256, 256, 256>(a6, kt + kq[2], kt + kq[3], kt + kq[0],
-                                                          kt + kq[1], kt + kq[2], kt + kq[3]);
+            for (int j = 0; j < 3; ++j)
+                s = mfma_32x32x16(a3[j], qf[j], s);
+            lds_read_b128_3<0, 128, 128>(a3, kt + kq[3], kt + kq[0], kt + kq[1]);
 #pragma unroll
-            for (int j = 0; j < 6; ++j)
-                s = mfma_32x32x16(a6[j], qf[6 + j], s);
+            for (int j = 0; j < 3; ++j)
+                s = mfma_32x32x16(a3[j], qf[3 + j], s);
+            lds_read_b128_3<128, 128, 256>(a3, kt + kq[2], kt + kq[3], kt + kq[0]);
+#pragma unroll
+            for (int j = 0; j < 3; ++j)
+                s = mfma_32x32x16(a3[j], qf[6 + j], s);
+            lds_read_b128_3<256, 256, 256>(a3, kt + kq[1], kt + kq[2], kt + kq[3]);
+#pragma unroll
+            for (int j = 0; j < 3; ++j)
+                s = mfma_32x32x16(a3[j], qf[9 + j], s);
         }
         // lane holds keys 8*(i/4) + 4g + i%4 of the tile for query qi
         float x[16];
@@ -374,26 +412,28 @@ __global__ __launch_bounds__(256) void attend_masked_kernel(
             const u32x4_t bhi = {hi4[0], hi4[1], hi4[2], hi4[3]};
             const u32x4_t blo = {lo4[0], lo4[1], lo4[2], lo4[3]};
             const uint32_t vk = vt + kh * 16 * VD * 2;
-            auto pv4 = [&](auto N0, const u32x2_t(&rd)[8]) {
-                constexpr int n0 = decltype(N0)::value;
-                u32x4_t av[4];
+            // column tile n = n0 + j reads bases va_/vb_[n & 3] at 256 * (n >> 2),
+            // two tiles per group
+            auto pv2 = [&](auto N0) {
+                constexpr int n0 = decltype(N0)::value, j0 = n0 & 3, o = 256 * (n0 >> 2);
+                u32x2_t rd[4];
+                lds_read_tr16x4_4<o>(rd, vk + va_[j0], vk + va_[j0 + 1], vk + vb_[j0],
+                                     vk + vb_[j0 + 1]);
+                u32x4_t av[2];
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < 2; ++j)
                     av[j] = u32x4_t{rd[2 * j][0], rd[2 * j][1], rd[2 * j + 1][0], rd[2 * j + 1][1]};
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < 2; ++j)
                     oacc[n0 + j] = mfma_32x32x16(av[j], bhi, oacc[n0 + j]);
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < 2; ++j)
                     oacc[n0 + j] = mfma_32x32x16(av[j], blo, oacc[n0 + j]);
             };
-            u32x2_t rd[8];
-            lds_read_tr16x4_8<0>(rd, vk + va_[0], vk + va_[1], vk + va_[2], vk + va_[3],
-                                 vk + vb_[0], vk + vb_[1], vk + vb_[2], vk + vb_[3]);
-            pv4(std::integral_constant<int, 0>{}, rd);
-            lds_read_tr16x4_8<256>(rd, vk + va_[0], vk + va_[1], vk + va_[2], vk + va_[3],
-                                   vk + vb_[0], vk + vb_[1], vk + vb_[2], vk + vb_[3]);
-            pv4(std::integral_constant<int, 4>{}, rd);
+            pv2(std::integral_constant<int, 0>{});
+            pv2(std::integral_constant<int, 2>{});
+            pv2(std::integral_constant<int, 4>{});
+            pv2(std::integral_constant<int, 6>{});
         }
     }
 
