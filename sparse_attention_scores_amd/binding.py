@@ -8,6 +8,7 @@ no fallback: if libdsa.so is missing or does not load, every call raises.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 import threading
 
@@ -112,7 +113,15 @@ def _check(rc: int):
         raise DsaError(rc, load().dsa_last_error().decode())
 
 
+# torch's current HIP stream on the current device, as a raw handle (torch's
+# own accessor of it, without building a Stream object per call; the public
+# route is kept for torch builds that lack it)
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream():
+    if _raw_stream is not None:
+        return ctypes.c_void_p(_raw_stream(torch.cuda.current_device()))
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
@@ -195,7 +204,7 @@ def topk(scores, vis_lo, vis_hi, top_k: int, out=None, workspace=None):
     _dev(scores, vis_lo, vis_hi, out)
     lead = scores.shape[:-1]
     n_cols = scores.shape[-1]
-    rows = int(torch.tensor(lead).prod().item()) if len(lead) else 1
+    rows = math.prod(lead)
     if out is None:
         out = torch.empty((*lead, top_k), dtype=torch.int32, device=scores.device)
     ws, wsb = _workspace(topk_workspace_size(rows, n_cols, top_k), workspace, scores.device)

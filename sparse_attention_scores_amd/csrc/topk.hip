@@ -100,6 +100,29 @@ __device__ __forceinline__ float order_key_value(uint32_t o)
 // the whole row.  When its ranks fall into crowded buckets (a score range
 // stretched by outliers) or the value range is not finite, the block takes
 // the full sorted top-k of the row instead and writes its positions from it.
+// Value buckets of a row segment (shared by the bucket kernels below): NB
+// buckets linear in the score value over [vmin, vmax], numbered from the top
+// (bucket 0 holds the largest values).  The map is monotonic, so every key
+// of a lower-numbered bucket ranks above every key of a higher-numbered one.
+struct ValueBuckets {
+    float vmin, scale;
+    int nb;
+    __device__ bool init(uint32_t omin, uint32_t omax, int nbuckets)
+    {
+        nb = nbuckets;
+        vmin = order_key_value(omin);
+        const float vmax = order_key_value(omax);
+        scale = (float)nb / (vmax - vmin);
+        return __builtin_isfinite(vmin) && __builtin_isfinite(vmax) &&
+               __builtin_isfinite(scale) && scale > 0.f;
+    }
+    __device__ int operator()(uint32_t ord) const
+    {
+        const int b = (int)((order_key_value(ord) - vmin) * scale);
+        return nb - 1 - min(max(b, 0), nb - 1);
+    }
+};
+
 constexpr int kSegMaxBucket = 256;
 template <int NT, int CAP>
 __global__ __launch_bounds__(NT) void topk_seg_kernel(const float *__restrict__ scores,
@@ -110,15 +133,49 @@ __global__ __launch_bounds__(NT) void topk_seg_kernel(const float *__restrict__ 
                                                       int seg_len)
 {
     using S = Topk32Smem<NT, CAP>;
-    constexpr int NB = S::NB, NW = S::NW, PB = NB / NT;
+    constexpr int NB = S::NB, NW = S::NW, PB = NB / NT, R = CAP / NT;
     static_assert(PB >= 1 && NB % NT == 0, "every thread owns whole buckets");
     __shared__ S sm;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int row = blockIdx.x / parts;
     const int seg = blockIdx.x - row * parts;
     const int lo = max(vlo[row], 0), hi = min(vhi[row], n_cols);
-    uint32_t omin, omax;
-    const int n = load_row32(sm, scores + (int64_t)row * row_stride, lo, hi, omin, omax);
+    const int n = max(hi - lo, 0);
+    const int rounds = (n + NT - 1) / NT;  // uniform, at most R
+    // thread t keeps keys r*NT + t (r < rounds) in registers: their order keys
+    // and, below, their buckets (all loads issued before any is used)
+    const float *rp = scores + (int64_t)row * row_stride + lo;
+    uint32_t ord[R];
+    {
+        float v[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            v[r] = (r < rounds && r * NT + tid < n) ? rp[r * NT + tid] : 0.f;
+        uint32_t mn = ~0u, mx = 0u;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            ord[r] = score_order_key(v[r]);
+            if (r < rounds && r * NT + tid < n) {
+                mn = min(mn, ord[r]);
+                mx = max(mx, ord[r]);
+            }
+        }
+        mn = wave_min_u32(mn);
+        mx = wave_max_u32(mx);
+        if (lane == 0) {
+            sm.mm[0][wid] = mn;
+            sm.mm[1][wid] = mx;
+        }
+    }
+    for (int i = tid; i < NB; i += NT)
+        sm.bk.fill[i] = 0u;
+    __syncthreads();
+    uint32_t omin = sm.mm[0][0], omax = sm.mm[1][0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+        omin = min(omin, sm.mm[0][w]);
+        omax = max(omax, sm.mm[1][w]);
+    }
     const int m = min(k, n);
     int32_t *o = out + (int64_t)row * k;
     const int p0 = seg * seg_len, p1 = min(p0 + seg_len, k);
@@ -132,21 +189,18 @@ __global__ __launch_bounds__(NT) void topk_seg_kernel(const float *__restrict__ 
             o[i] = lo + i;
         return;
     }
-    const float vmin = order_key_value(omin), vmax = order_key_value(omax);
-    const float scale = (float)NB / (vmax - vmin);
-    bool ok = __builtin_isfinite(vmin) && __builtin_isfinite(vmax) &&
-              __builtin_isfinite(scale) && scale > 0.f;
-    // descending bucket of a key: 0 holds the largest values
-    auto bucket = [&](uint32_t ord) {
-        const int b = (int)((order_key_value(ord) - vmin) * scale);
-        return NB - 1 - min(max(b, 0), NB - 1);
-    };
+    ValueBuckets bucket;
+    bool ok = bucket.init(omin, omax, NB);
     if (ok) {
-        for (int i = tid; i < NB; i += NT)
-            sm.bk.fill[i] = 0u;
-        __syncthreads();
-        for (int i = tid; i < n; i += NT)
-            atomicAdd(&sm.bk.fill[bucket(sm.a.ord[i])], 1u);
+        int bk[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            bk[r] = NB;  // none
+            if (r < rounds && r * NT + tid < n) {
+                bk[r] = bucket(ord[r]);
+                atomicAdd(&sm.bk.fill[bk[r]], 1u);
+            }
+        }
         __syncthreads();
         // exclusive prefix over the buckets (thread t owns PB consecutive
         // ones); the buckets holding ranks s0 and s1-1
@@ -161,55 +215,57 @@ __global__ __launch_bounds__(NT) void topk_seg_kernel(const float *__restrict__ 
         if (lane == 63)
             sm.tab[0][wid] = incl;
         __syncthreads();
-        int before = incl - sum;
+        int run = incl - sum;
 #pragma unroll
         for (int w = 0; w < NW; ++w)
-            before += w < wid ? sm.tab[0][w] : 0;
-        int run = before;
+            run += w < wid ? sm.tab[0][w] : 0;
+        int crowd_lo = 0, crowd_hi = 0;  // sizes of the buckets holding s0 and s1-1
 #pragma unroll
         for (int j = 0; j < PB; ++j) {
             const int b = tid * PB + j, c = (int)v[j];
             sm.bk.off[b] = (uint32_t)run;
-            if (run <= s0 && s0 < run + c)
+            if (run <= s0 && s0 < run + c) {
                 sm.tab[1][0] = b;
-            if (run <= s1 - 1 && s1 - 1 < run + c)
+                crowd_lo = c;
+            }
+            if (run <= s1 - 1 && s1 - 1 < run + c) {
                 sm.tab[1][1] = b;
+                crowd_hi = c;
+            }
             run += c;
         }
+        // a bucket strictly between them holds only ranks of this segment
+        // (all of which are placed anyway); the two end buckets can hold many
+        // keys outside it (ties, or a range stretched by an outlier), and
+        // placing a key costs one compare per member of its bucket
+        if (crowd_lo)
+            sm.red[0][0][0] = crowd_lo;
+        if (crowd_hi)
+            sm.red[0][0][1] = crowd_hi;
         __syncthreads();
         const int bf = sm.tab[1][0], bl = sm.tab[1][1];
         const int base = (int)sm.bk.off[bf];
-        // crowded buckets in the range make the in-bucket placement costly
-        int crowd = 0;
-#pragma unroll
-        for (int j = 0; j < PB; ++j) {
-            const int b = tid * PB + j;
-            if (b >= bf && b <= bl) {
-                crowd = max(crowd, (int)v[j]);
-                sm.bk.fill[b] = sm.bk.off[b] - (uint32_t)base;  // fill pointers
-            }
-        }
-        crowd = (int)wave_max_u32((uint32_t)crowd);
-        if (lane == 0)
-            sm.red[0][0][wid] = crowd;
-        __syncthreads();
-        int total = 0;
-#pragma unroll
-        for (int w = 0; w < NW; ++w)
-            crowd = max(crowd, sm.red[0][0][w]);
-        total = (bl + 1 < NB ? (int)sm.bk.off[bl + 1] : n) - base;  // keys of buckets bf .. bl
+        const int crowd = max(sm.red[0][0][0], sm.red[0][0][1]);
+        const int total = (bl + 1 < NB ? (int)sm.bk.off[bl + 1] : n) - base;  // keys of bf .. bl
         ok = crowd <= kSegMaxBucket && total <= kTopkMaxK;
         if (ok) {
-            // collect the keys of buckets bf .. bl as composite keys
+            // fill pointers of buckets bf .. bl, then the collection from registers
+#pragma unroll
+            for (int j = 0; j < PB; ++j) {
+                const int b = tid * PB + j;
+                if (b >= bf && b <= bl)
+                    sm.bk.fill[b] = sm.bk.off[b] - (uint32_t)base;
+            }
+            __syncthreads();
             uint64_t *ck = reinterpret_cast<uint64_t *>(&sm.word[1][0]);
             static_assert(sizeof(sm.word[1]) + sizeof(sm.wcol) >= kTopkMaxK * 8,
                           "composite key buffer");
-            for (int i = tid; i < n; i += NT) {
-                const uint32_t ord = sm.a.ord[i];
-                const int b = bucket(ord);
-                if (b >= bf && b <= bl)
-                    ck[atomicAdd(&sm.bk.fill[b], 1u)] =
-                        ((uint64_t)ord << 32) | (uint64_t)(0xffffffffu - (uint32_t)(lo + i));
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                if (bk[r] >= bf && bk[r] <= bl)
+                    ck[atomicAdd(&sm.bk.fill[bk[r]], 1u)] =
+                        ((uint64_t)ord[r] << 32) |
+                        (uint64_t)(0xffffffffu - (uint32_t)(lo + r * NT + tid));
             }
             __syncthreads();
             // rank of each collected key: its bucket's first rank plus the
@@ -228,17 +284,18 @@ __global__ __launch_bounds__(NT) void topk_seg_kernel(const float *__restrict__ 
         }
         __syncthreads();  // the bucket arrays are reused below
     }
+    // the full sorted top-k of the row, from the key cache
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        if (r < rounds && r * NT + tid < n)
+            sm.a.ord[r * NT + tid] = ord[r];
+    __syncthreads();
     int buf;
     topk_sort_cached(sm, n, lo, k, omin, omax, buf);
     for (int i = s0 + tid; i < s1; i += NT)
         o[i] = (int32_t)sm.wcol[buf][i];
 }
 
-// Second launch of the long-row path: select and sort among the chunk
-// winners ws[row][0 .. n_chunks*k).  Zero keys are padding; there are always
-// at least min(k, n_visible) real keys, and every real key is > 0.  With
-// CACHE the candidates (at most CACHE_KEYS) are first copied to LDS in one
-// batched pass, so the select passes re-read LDS instead of global memory.
 constexpr int kMergeCacheKeys = 16384;
 template <int NT, bool CACHE>
 using MergeSmem = TopkSmem<NT, CACHE ? 2 * kMergeCacheKeys : 1>;
@@ -323,29 +380,6 @@ __global__ __launch_bounds__(NT) void topk_merge_kernel(const uint64_t *__restri
             o[i] = i < m ? (int32_t)(0xffffffffu - (uint32_t)v[b]) : -1;
     }
 }
-
-// Value buckets of a row segment (shared by the bucket kernels below): NB
-// buckets linear in the score value over [vmin, vmax], numbered from the top
-// (bucket 0 holds the largest values).  The map is monotonic, so every key
-// of a lower-numbered bucket ranks above every key of a higher-numbered one.
-struct ValueBuckets {
-    float vmin, scale;
-    int nb;
-    __device__ bool init(uint32_t omin, uint32_t omax, int nbuckets)
-    {
-        nb = nbuckets;
-        vmin = order_key_value(omin);
-        const float vmax = order_key_value(omax);
-        scale = (float)nb / (vmax - vmin);
-        return __builtin_isfinite(vmin) && __builtin_isfinite(vmax) &&
-               __builtin_isfinite(scale) && scale > 0.f;
-    }
-    __device__ int operator()(uint32_t ord) const
-    {
-        const int b = (int)((order_key_value(ord) - vmin) * scale);
-        return nb - 1 - min(max(b, 0), nb - 1);
-    }
-};
 
 // First launch of the long-row path: chunk c of the row keeps its exact top
 // min(k, n_c) keys, as composite keys in any order, in ws[row][c][0 .. k),
