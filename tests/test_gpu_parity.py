@@ -124,6 +124,32 @@ def test_index_scores_padding_and_pooled_ranges(dsa):
     check_scores(cpu(S).numpy().reshape(ref.shape), ref, A, 1e-3, "pooled ranges")
 
 
+@pytest.mark.parametrize("fp8", [False, True])
+def test_index_scores_decode_padding(dsa, fp8):
+    """Decode rows (one and three queries per sequence) with left padding,
+    one sequence wholly padded, and query positions short of the end: the
+    decode kernel's visible tiles, its partial tiles and its -FLT_MAX rows."""
+    note(f"index scores decode padding fp8={fp8}")
+    B, H, d, Tk = 4, 32, 128, 1000
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    for n_q in (1, 3):
+        q = (torch.randn(B, n_q, H, d, generator=gen, device="cuda") / d ** 0.5).bfloat16()
+        kf = torch.randn(B, Tk, d, generator=gen, device="cuda") / d ** 0.5
+        k, k_scale = W.quantize_fp8_rows(kf) if fp8 else (kf.bfloat16(), None)
+        w = torch.rand(B, n_q, H, generator=gen, device="cuda")
+        pad = torch.tensor([0, 37, 999, 1000], dtype=torch.int32, device="cuda")
+        last = torch.tensor([999, 999, 999, 700], dtype=torch.int32, device="cuda")
+        q_pos = (last[:, None] - torch.arange(n_q - 1, -1, -1, dtype=torch.int32,
+                                              device="cuda")[None, :] * 333).contiguous()
+        lo, hi = dsa.visibility_ranges(pad, q_pos)
+        S = dsa.index_scores(q, k, w, lo, hi, 0.088, k_scale=k_scale)
+        torch.cuda.synchronize()
+        ref, A = oracle.index_scores(cpu(q), cpu(k), cpu(w), 0.088, cpu(q_pos), cpu(pad),
+                                     k_scale=None if k_scale is None else cpu(k_scale),
+                                     want_mag=True)
+        check_scores(cpu(S).numpy().reshape(ref.shape), ref, A, 1e-3, f"decode n_q={n_q}")
+
+
 # ---------------------------------------------------------------- top-k
 
 TOPK_CASES = [
