@@ -10,6 +10,11 @@
     python -m sparse_attention_scores_amd.profile_summary traffic \\
         --fetch FETCH_CSV --write WRITE_CSV --copy-bytes N --cmd-fetch "..." --cmd-write "..."
 
+    # matrix-core use per kernel: one counter run (--pmc SQ_INSTS_MFMA
+    # SQ_VALU_MFMA_BUSY_CYCLES) and one kernel-trace run of the same command
+    python -m sparse_attention_scores_amd.profile_summary mfma \
+        --counters COUNTER_CSV --stats STATS_CSV --cmd-counters "..." --cmd-trace "..."
+
 The traffic record carries a digest of the kernel sources; bench.py only
 reports the recorded traffic while the sources still match it.
 """
@@ -132,6 +137,33 @@ def read_traffic(path: str):
     return digest, ff, wf, kern
 
 
+# MI355X: 256 CUs x 4 SIMDs, 2.4 GHz at the published dense peaks
+N_SIMD, CLOCK_HZ = 1024, 2.4e9
+
+
+def mfma(counter_csv: str, stats_csv: str, cmd_counters: str, cmd_trace: str) -> str:
+    """Per kernel: MFMA instructions and matrix-core busy cycles per dispatch
+    (SQ_VALU_MFMA_BUSY_CYCLES is summed over the SIMDs), the kernel's average
+    duration from the trace run, and busy cycles / (duration x clock x SIMDs):
+    the fraction of the chip's matrix-core time in use at the peak clock."""
+    inst = _per_dispatch(counter_csv, "SQ_INSTS_MFMA")
+    busy = _per_dispatch(counter_csv, "SQ_VALU_MFMA_BUSY_CYCLES")
+    dur = {short_name(r["Name"]): float(r["AverageNs"]) * 1e-9
+           for r in csv.DictReader(open(stats_csv))}
+    lines = [f"# matrix-core use per kernel (MI355X: {N_SIMD} SIMDs, {CLOCK_HZ / 1e9:.1f} GHz)",
+             f"# counters: {cmd_counters}",
+             f"# trace:    {cmd_trace}",
+             "# use = SQ_VALU_MFMA_BUSY_CYCLES per dispatch / (avg duration x clock x SIMDs)",
+             f"# {'kernel':<60s} {'mfma_insts':>12s} {'busy_cycles':>14s} {'avg_us':>10s} {'use':>6s}"]
+    for k in sorted(busy, key=lambda k: -busy[k][0]):
+        if busy[k][0] <= 0 or k not in dur:
+            continue
+        use = busy[k][0] / (dur[k] * CLOCK_HZ * N_SIMD)
+        lines.append(f"  {k[:60]:<60s} {inst.get(k, (0, 0))[0]:12.0f} {busy[k][0]:14.0f} "
+                     f"{dur[k] * 1e6:10.2f} {use:6.3f}")
+    return "\n".join(lines) + "\n"
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -144,9 +176,16 @@ def main(argv=None):
     c.add_argument("--copy-bytes", type=int, required=True)
     c.add_argument("--cmd-fetch", required=True)
     c.add_argument("--cmd-write", required=True)
+    m = sub.add_parser("mfma")
+    m.add_argument("--counters", required=True)
+    m.add_argument("--stats", required=True)
+    m.add_argument("--cmd-counters", required=True)
+    m.add_argument("--cmd-trace", required=True)
     a = ap.parse_args(argv)
     if a.what == "trace":
         sys.stdout.write(trace(a.stats_csv, a.cmd))
+    elif a.what == "mfma":
+        sys.stdout.write(mfma(a.counters, a.stats, a.cmd_counters, a.cmd_trace))
     else:
         sys.stdout.write(traffic(a.fetch, a.write, a.copy_bytes, a.cmd_fetch, a.cmd_write))
 
