@@ -49,3 +49,21 @@ def test_bench_uses_record_only_for_current_sources(tmp_path, monkeypatch):
     assert bench.measured_traffic(2, "attend")[0] is None
     os.remove(prof / name)
     assert bench.measured_traffic(2, "attend") == (None, None)
+
+
+def test_mfma_record_use_fraction(tmp_path):
+    counters = tmp_path / "c.csv"
+    stats = tmp_path / "s.csv"
+    counters.write_text("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n"
+                        "1,dsa::attend_gather_kernel(int),SQ_INSTS_MFMA,1000\n"
+                        "1,dsa::attend_gather_kernel(int),SQ_VALU_MFMA_BUSY_CYCLES,1228800\n"
+                        "2,dsa::attend_gather_kernel(int),SQ_INSTS_MFMA,1000\n"
+                        "2,dsa::attend_gather_kernel(int),SQ_VALU_MFMA_BUSY_CYCLES,1228800\n"
+                        "3,dsa::topk_seg_kernel<1024,16384>(float),SQ_VALU_MFMA_BUSY_CYCLES,0\n")
+    stats.write_text("Name,Calls,TotalDurationNs,AverageNs,Percentage,MinNs,MaxNs\n"
+                     "dsa::attend_gather_kernel(int),2,2000,1000,90,1000,1000\n"
+                     "dsa::topk_seg_kernel<1024,16384>(float),1,200,200,10,200,200\n")
+    text = ps.mfma(str(counters), str(stats), "cmd c", "cmd t")
+    rows = [l.split() for l in text.splitlines() if not l.startswith("#")]
+    # 1228800 busy cycles over 1 us at 2.4 GHz on 1024 SIMDs = 0.5 of the chip
+    assert rows == [["dsa::attend_gather_kernel", "1000", "1228800", "1.00", "0.500"]]
