@@ -136,6 +136,24 @@ __device__ __forceinline__ void vm_wait()
     asm volatile("" ::: "memory");
 }
 
+// An LDS operand read issued now and waited for later, so that reads run a
+// few MFMAs ahead of their use.  lds_operand_wait<N> waits until at most N
+// LDS operations are outstanding (LDS reads complete in issue order, and an
+// SMEM load in flight only makes the wait stricter) and ties the register to
+// that wait, so the compiler cannot use it earlier.  Nothing may read or
+// copy the destination between the two calls; users check the generated
+// code for that.
+__device__ __forceinline__ void lds_read_b128_nowait(u32x4_t &v, uint32_t a)
+{
+    asm volatile("ds_read_b128 %0, %1" : "=&v"(v) : "v"(a) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void lds_operand_wait(u32x4_t &v)
+{
+    static_assert(N >= 0 && N < 16, "lgkmcnt is 4 bits");
+    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(v) : "n"(N) : "memory");
+}
+
 // vm_wait<N * per_tile> for a runtime N in [0, 3] (the tiles still in flight
 // behind the one needed).
 template <int PER_TILE>

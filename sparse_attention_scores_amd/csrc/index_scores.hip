@@ -516,23 +516,12 @@ __global__ __launch_bounds__(64 * IP_NW) void index_scores_prefill_kernel(
             if (tt + IP_STAGES - 1 < t1)
                 dma_tile(tt + IP_STAGES - 1, (tt - t0 + IP_STAGES - 1) % IP_STAGES);
             const uint32_t base = lds0 + st * IP_TILEB;
+            // operand reads run two k-steps ahead of the MFMAs that use them,
+            // so the tile's LDS reads (all 8 waves read all of it) overlap
+            // the matrix work instead of preceding it
             u32x4_t kf[KS];
-            asm volatile(
-                "ds_read_b128 %0, %8\n\t"
-                "ds_read_b128 %1, %9\n\t"
-                "ds_read_b128 %2, %10\n\t"
-                "ds_read_b128 %3, %11\n\t"
-                "ds_read_b128 %4, %12\n\t"
-                "ds_read_b128 %5, %13\n\t"
-                "ds_read_b128 %6, %14\n\t"
-                "ds_read_b128 %7, %15\n\t"
-                "s_waitcnt lgkmcnt(0)"
-                : "=&v"(kf[0]), "=&v"(kf[1]), "=&v"(kf[2]), "=&v"(kf[3]), "=&v"(kf[4]),
-                  "=&v"(kf[5]), "=&v"(kf[6]), "=&v"(kf[7])
-                : "v"(base + kaddr[0]), "v"(base + kaddr[1]), "v"(base + kaddr[2]),
-                  "v"(base + kaddr[3]), "v"(base + kaddr[4]), "v"(base + kaddr[5]),
-                  "v"(base + kaddr[6]), "v"(base + kaddr[7])
-                : "memory");
+            lds_read_b128_nowait(kf[0], base + kaddr[0]);
+            lds_read_b128_nowait(kf[1], base + kaddr[1]);
 #pragma unroll
             for (int qi = 0; qi < IP_QPW; ++qi) {
                 acc[qi] = f32x16_t{};
@@ -540,6 +529,14 @@ __global__ __launch_bounds__(64 * IP_NW) void index_scores_prefill_kernel(
             }
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
+                if (ks + 2 < KS) {
+                    lds_read_b128_nowait(kf[ks + 2], base + kaddr[ks + 2]);
+                    lds_operand_wait<2>(kf[ks]);
+                } else if (ks + 1 < KS) {
+                    lds_operand_wait<1>(kf[ks]);
+                } else {
+                    lds_operand_wait<0>(kf[ks]);
+                }
 #pragma unroll
                 for (int qi = 0; qi < IP_QPW; ++qi) {
                     acc[qi] = mfma_32x32x16(qf[qi][ks], kf[ks], acc[qi]);
