@@ -43,12 +43,6 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
     return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
-// Two floats -> packed bf16x2 (low half = a).
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
-{
-    return f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
-}
-
 // Two floats -> packed bf16x2 (low half = a), one v_cvt_pk_bf16_f32 (RNE).
 __device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b)
 {
@@ -114,16 +108,6 @@ __device__ __forceinline__ void lds_dma16(const void *src, void *lds_base)
 // stored to (its initial value is undefined), and reads of it may be folded.
 #define DSA_LDS_ESCAPE(obj) asm volatile("" ::"s"((const void *)&(obj)) : "memory")
 
-// Wait for this wave's outstanding global loads, LDS DMA included.  The
-// memory clobber tells the optimizer that LDS contents changed: data that
-// arrives only through lds_dma16 is otherwise invisible to it, and reads of
-// an LDS array it never saw stored to could be folded away.
-__device__ __forceinline__ void lds_dma_wait()
-{
-    __builtin_amdgcn_s_waitcnt(0);
-    asm volatile("" ::: "memory");
-}
-
 // Wait until at most N of this wave's vector-memory operations (LDS DMA
 // included; they complete in issue order) are outstanding.  gfx9 s_waitcnt
 // immediate: vmcnt in bits [3:0] and [15:14]; expcnt (7) and lgkmcnt (15)
@@ -152,6 +136,11 @@ __device__ __forceinline__ void lds_operand_wait(u32x4_t &v)
 {
     static_assert(N >= 0 && N < 16, "lgkmcnt is 4 bits");
     asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(v) : "n"(N) : "memory");
+}
+template <int O>
+__device__ __forceinline__ void lds_read_b128_nowait(u32x4_t &v, uint32_t a)
+{
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=&v"(v) : "v"(a), "i"(O) : "memory");
 }
 
 // vm_wait<N * per_tile> for a runtime N in [0, 3] (the tiles still in flight
@@ -183,17 +172,6 @@ __device__ __forceinline__ void lds_dma4(const void *src, void *lds_base)
     __builtin_amdgcn_global_load_lds(src, DSA_LDS_PTR(void, lds_base), 4, 0, 0);
 }
 
-// Transposing LDS read (ds_read_b64_tr_b16): in each group of 16 lanes, lane
-// r points at 4 consecutive 16-bit values M[r][0..3]; lane i receives
-// M[i/4 + 4j][i%4] for j = 0..3.  With source lane r = a + 4j pointing at
-// row key_j, columns 4a..4a+3 of a row-major tile, lane i therefore receives
-// column i of rows key_0..key_3 -- an MFMA operand fragment read across rows.
-__device__ __forceinline__ u32x2_t lds_read_tr16x4(const void *lds_addr)
-{
-    const lds_v4i16_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(DSA_LDS_PTR(lds_v4i16_t, lds_addr));
-    return __builtin_bit_cast(u32x2_t, r);
-}
-
 // Plain LDS reads at a 32-bit LDS byte address, for waves that issue no
 // direct-to-LDS loads themselves (the compiler then has no such loads to wait
 // for in front of them, and schedules and allocates them freely).
@@ -206,106 +184,6 @@ __device__ __forceinline__ u32x2_t lds_ld_tr16(uint32_t a)
     const lds_v4i16_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (lds_v4i16_t __attribute__((address_space(3))) *)(uintptr_t)a);
     return __builtin_bit_cast(u32x2_t, r);
-}
-
-// Sixteen transposing LDS reads and the wait for them, in one asm statement:
-// va[r] from b[r & 3] + (r < 4 ? O0 : O1), vb[r] from the same address + ROW.
-// The wait sits inside the statement, so the destination registers are
-// complete when the compiler first sees them.  (The builtin form cannot be
-// used next to direct-to-LDS loads: the compiler puts a wait for every
-// outstanding vector-memory operation in front of it, which would drain the
-// tiles still in flight.)
-template <int O0, int O1, int ROW>
-__device__ __forceinline__ void lds_read_tr16x4_x16(u32x2_t (&va)[8], u32x2_t (&vb)[8],
-                                                    uint32_t b0, uint32_t b1, uint32_t b2,
-                                                    uint32_t b3)
-{
-    static_assert(O0 >= 0 && O1 + ROW < 65536, "ds offset is 16 bits");
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %16 offset:%20\n\t"
-        "ds_read_b64_tr_b16 %1, %17 offset:%20\n\t"
-        "ds_read_b64_tr_b16 %2, %18 offset:%20\n\t"
-        "ds_read_b64_tr_b16 %3, %19 offset:%20\n\t"
-        "ds_read_b64_tr_b16 %4, %16 offset:%21\n\t"
-        "ds_read_b64_tr_b16 %5, %17 offset:%21\n\t"
-        "ds_read_b64_tr_b16 %6, %18 offset:%21\n\t"
-        "ds_read_b64_tr_b16 %7, %19 offset:%21\n\t"
-        "ds_read_b64_tr_b16 %8, %16 offset:%22\n\t"
-        "ds_read_b64_tr_b16 %9, %17 offset:%22\n\t"
-        "ds_read_b64_tr_b16 %10, %18 offset:%22\n\t"
-        "ds_read_b64_tr_b16 %11, %19 offset:%22\n\t"
-        "ds_read_b64_tr_b16 %12, %16 offset:%23\n\t"
-        "ds_read_b64_tr_b16 %13, %17 offset:%23\n\t"
-        "ds_read_b64_tr_b16 %14, %18 offset:%23\n\t"
-        "ds_read_b64_tr_b16 %15, %19 offset:%23\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(va[0]), "=&v"(va[1]), "=&v"(va[2]), "=&v"(va[3]), "=&v"(va[4]), "=&v"(va[5]),
-          "=&v"(va[6]), "=&v"(va[7]), "=&v"(vb[0]), "=&v"(vb[1]), "=&v"(vb[2]), "=&v"(vb[3]),
-          "=&v"(vb[4]), "=&v"(vb[5]), "=&v"(vb[6]), "=&v"(vb[7])
-        : "v"(b0), "v"(b1), "v"(b2), "v"(b3), "i"(O0), "i"(O1), "i"(O0 + ROW), "i"(O1 + ROW)
-        : "memory");
-}
-
-// Six 16-byte LDS reads and the wait for them, in one asm statement (for
-// the same reason as above): a[2j] from base + O + 128j and a[2j+1] from
-// base + O + 128j + ROW, j < 3.
-template <int O, int ROW>
-__device__ __forceinline__ void lds_read_b128_x6(u32x4_t (&a)[6], uint32_t base)
-{
-    static_assert(O >= 0 && O + 256 + ROW < 65536, "ds offset is 16 bits");
-    asm volatile(
-        "ds_read_b128 %0, %6 offset:%7\n\t"
-        "ds_read_b128 %1, %6 offset:%8\n\t"
-        "ds_read_b128 %2, %6 offset:%9\n\t"
-        "ds_read_b128 %3, %6 offset:%10\n\t"
-        "ds_read_b128 %4, %6 offset:%11\n\t"
-        "ds_read_b128 %5, %6 offset:%12\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4]), "=&v"(a[5])
-        : "v"(base), "i"(O), "i"(O + ROW), "i"(O + 128), "i"(O + 128 + ROW), "i"(O + 256),
-          "i"(O + 256 + ROW)
-        : "memory");
-}
-
-// Six 16-byte LDS reads and the wait for them: a[2j] from be + O + 128j and
-// a[2j+1] from bo + O + 128j, j < 3 (three even/odd k-step pairs of one row).
-template <int O>
-__device__ __forceinline__ void lds_read_b128_x6eo(u32x4_t (&a)[6], uint32_t be, uint32_t bo)
-{
-    static_assert(O >= 0 && O + 256 < 65536, "ds offset is 16 bits");
-    asm volatile(
-        "ds_read_b128 %0, %6 offset:%8\n\t"
-        "ds_read_b128 %1, %7 offset:%8\n\t"
-        "ds_read_b128 %2, %6 offset:%9\n\t"
-        "ds_read_b128 %3, %7 offset:%9\n\t"
-        "ds_read_b128 %4, %6 offset:%10\n\t"
-        "ds_read_b128 %5, %7 offset:%10\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4]), "=&v"(a[5])
-        : "v"(be), "v"(bo), "i"(O), "i"(O + 128), "i"(O + 256)
-        : "memory");
-}
-
-// Eight 16-byte LDS reads and the wait for them: a[2j] from be + O + j*ROW,
-// a[2j+1] from bo + O + j*ROW, j < 4.
-template <int O, int ROW>
-__device__ __forceinline__ void lds_read_b128_x8(u32x4_t (&a)[8], uint32_t be, uint32_t bo)
-{
-    static_assert(O >= 0 && O + 3 * ROW < 65536, "ds offset is 16 bits");
-    asm volatile(
-        "ds_read_b128 %0, %8 offset:%10\n\t"
-        "ds_read_b128 %1, %9 offset:%10\n\t"
-        "ds_read_b128 %2, %8 offset:%11\n\t"
-        "ds_read_b128 %3, %9 offset:%11\n\t"
-        "ds_read_b128 %4, %8 offset:%12\n\t"
-        "ds_read_b128 %5, %9 offset:%12\n\t"
-        "ds_read_b128 %6, %8 offset:%13\n\t"
-        "ds_read_b128 %7, %9 offset:%13\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4]), "=&v"(a[5]),
-          "=&v"(a[6]), "=&v"(a[7])
-        : "v"(be), "v"(bo), "i"(O), "i"(O + ROW), "i"(O + 2 * ROW), "i"(O + 3 * ROW)
-        : "memory");
 }
 
 // LDS atomic OR without return (ds_or_b32) at a byte address.  Written as asm

@@ -68,65 +68,8 @@ __global__ __launch_bounds__(256) void topk_to_mask_kernel(const int32_t *__rest
 __device__ __forceinline__ int mk_swz_k(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int mk_swz_v(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 
-// Six 16-byte LDS reads with one base each and the wait for them (asm, for
-// the reason given at lds_read_tr16x4_x16).
-template <int O0, int O1, int O2, int O3, int O4, int O5>
-__device__ __forceinline__ void lds_read_b128_6(u32x4_t (&a)[6], uint32_t b0, uint32_t b1,
-                                                uint32_t b2, uint32_t b3, uint32_t b4,
-                                                uint32_t b5)
-{
-    asm volatile(
-        "ds_read_b128 %0, %6 offset:%12\n\t"
-        "ds_read_b128 %1, %7 offset:%13\n\t"
-        "ds_read_b128 %2, %8 offset:%14\n\t"
-        "ds_read_b128 %3, %9 offset:%15\n\t"
-        "ds_read_b128 %4, %10 offset:%16\n\t"
-        "ds_read_b128 %5, %11 offset:%17\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4]), "=&v"(a[5])
-        : "v"(b0), "v"(b1), "v"(b2), "v"(b3), "v"(b4), "v"(b5), "i"(O0), "i"(O1), "i"(O2),
-          "i"(O3), "i"(O4), "i"(O5)
-        : "memory");
-}
-
-// Eight transposing LDS reads (4 column tiles x rows ra / rb) and the wait.
-template <int O>
-__device__ __forceinline__ void lds_read_tr16x4_8(u32x2_t (&a)[8], uint32_t r0, uint32_t r1,
-                                                  uint32_t r2, uint32_t r3, uint32_t s0,
-                                                  uint32_t s1, uint32_t s2, uint32_t s3)
-{
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %8 offset:%16\n\t"
-        "ds_read_b64_tr_b16 %1, %12 offset:%16\n\t"
-        "ds_read_b64_tr_b16 %2, %9 offset:%16\n\t"
-        "ds_read_b64_tr_b16 %3, %13 offset:%16\n\t"
-        "ds_read_b64_tr_b16 %4, %10 offset:%16\n\t"
-        "ds_read_b64_tr_b16 %5, %14 offset:%16\n\t"
-        "ds_read_b64_tr_b16 %6, %11 offset:%16\n\t"
-        "ds_read_b64_tr_b16 %7, %15 offset:%16\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4]), "=&v"(a[5]),
-          "=&v"(a[6]), "=&v"(a[7])
-        : "v"(r0), "v"(r1), "v"(r2), "v"(r3), "v"(s0), "v"(s1), "v"(s2), "v"(s3), "i"(O)
-        : "memory");
-}
-
-// Three 16-byte LDS reads with one base each and the wait.
-template <int O0, int O1, int O2>
-__device__ __forceinline__ void lds_read_b128_3(u32x4_t (&a)[3], uint32_t b0, uint32_t b1,
-                                                uint32_t b2)
-{
-    asm volatile(
-        "ds_read_b128 %0, %3 offset:%6\n\t"
-        "ds_read_b128 %1, %4 offset:%7\n\t"
-        "ds_read_b128 %2, %5 offset:%8\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2])
-        : "v"(b0), "v"(b1), "v"(b2), "i"(O0), "i"(O1), "i"(O2)
-        : "memory");
-}
-
-// Four transposing LDS reads (2 column tiles x rows ra / rb) and the wait.
+// Four transposing LDS reads (2 column tiles x rows ra / rb) and the wait
+// (asm, for the reason given at lds_read_b32_3).
 template <int O>
 __device__ __forceinline__ void lds_read_tr16x4_4(u32x2_t (&a)[4], uint32_t r0, uint32_t r1,
                                                   uint32_t s0, uint32_t s1)
@@ -337,24 +280,36 @@ __global__ __launch_bounds__(256, 2) void attend_masked_kernel(
         f32x16_t s = {};
         {
             const uint32_t kt = lds_k + st * Sm::KB;
-            // k-step ks reads base kq[ks & 3] + 128 * (ks >> 2), in groups of 3
-            u32x4_t a3[3];
-            lds_read_b128_3<0, 0, 0>(a3, kt + kq[0], kt + kq[1], kt + kq[2]);
-#pragma unroll
-            for (int j = 0; j < 3; ++j)
-                s = mfma_32x32x16(a3[j], qf[j], s);
-            lds_read_b128_3<0, 128, 128>(a3, kt + kq[3], kt + kq[0], kt + kq[1]);
-#pragma unroll
-            for (int j = 0; j < 3; ++j)
-                s = mfma_32x32x16(a3[j], qf[3 + j], s);
-            lds_read_b128_3<128, 128, 256>(a3, kt + kq[2], kt + kq[3], kt + kq[0]);
-#pragma unroll
-            for (int j = 0; j < 3; ++j)
-                s = mfma_32x32x16(a3[j], qf[6 + j], s);
-            lds_read_b128_3<256, 256, 256>(a3, kt + kq[1], kt + kq[2], kt + kq[3]);
-#pragma unroll
-            for (int j = 0; j < 3; ++j)
-                s = mfma_32x32x16(a3[j], qf[9 + j], s);
+            // k-step ks reads base kq[ks & 3] + 128 * (ks >> 2); the reads run
+            // two k-steps ahead of the MFMAs that use them
+            u32x4_t a[KS];
+            lds_read_b128_nowait<0>(a[0], kt + kq[0]);
+            lds_read_b128_nowait<0>(a[1], kt + kq[1]);
+            auto qk = [&](auto KSc) {
+                constexpr int ks = decltype(KSc)::value;
+                if constexpr (ks + 2 < KS) {
+                    lds_read_b128_nowait<128 * ((ks + 2) >> 2)>(a[ks + 2], kt + kq[(ks + 2) & 3]);
+                    lds_operand_wait<2>(a[ks]);
+                } else if constexpr (ks + 1 < KS) {
+                    lds_operand_wait<1>(a[ks]);
+                } else {
+                    lds_operand_wait<0>(a[ks]);
+                }
+                s = mfma_32x32x16(a[ks], qf[ks], s);
+            };
+            static_assert(KS == 12, "twelve k-steps");
+            qk(std::integral_constant<int, 0>{});
+            qk(std::integral_constant<int, 1>{});
+            qk(std::integral_constant<int, 2>{});
+            qk(std::integral_constant<int, 3>{});
+            qk(std::integral_constant<int, 4>{});
+            qk(std::integral_constant<int, 5>{});
+            qk(std::integral_constant<int, 6>{});
+            qk(std::integral_constant<int, 7>{});
+            qk(std::integral_constant<int, 8>{});
+            qk(std::integral_constant<int, 9>{});
+            qk(std::integral_constant<int, 10>{});
+            qk(std::integral_constant<int, 11>{});
         }
         // lane holds keys 8*(i/4) + 4g + i%4 of the tile for query qi
         float x[16];
