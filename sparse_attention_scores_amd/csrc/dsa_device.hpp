@@ -142,6 +142,19 @@ __device__ __forceinline__ void lds_read_b128_nowait(u32x4_t &v, uint32_t a)
 {
     asm volatile("ds_read_b128 %0, %1 offset:%2" : "=&v"(v) : "v"(a), "i"(O) : "memory");
 }
+// Transposing 4 x 16-bit read (ds_read_b64_tr_b16) issued now, waited for
+// by lds_operand_wait on the pair it belongs to.
+template <int O>
+__device__ __forceinline__ void lds_read_tr16_nowait(u32x2_t &v, uint32_t a)
+{
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=&v"(v) : "v"(a), "i"(O) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void lds_operand_wait(u32x2_t &v0, u32x2_t &v1)
+{
+    static_assert(N >= 0 && N < 16, "lgkmcnt is 4 bits");
+    asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(v0), "+v"(v1) : "n"(N) : "memory");
+}
 
 // vm_wait<N * per_tile> for a runtime N in [0, 3] (the tiles still in flight
 // behind the one needed).

@@ -325,40 +325,53 @@ __device__ __forceinline__ void attend_gather_role(
 
     // One tile of a compute wave: S^T = K Q^T, online softmax, O^T += V^T P^T.
     auto compute_tile = [&](uint32_t tb, int nvalid) {
-        // ---- S^T[key][head]: keys 0-15 (s0) and 16-31 (s1), two chains
-        //      each (even and odd k-steps); operands read in groups of 3
-        //      k-steps of one parity x 2 rows
-        f32x4_t s0a = {0.f, 0.f, 0.f, 0.f}, s0b = s0a, s1a = s0a, s1b = s0a;
+        // ---- S^T[key][head]: keys 0-15 (s0) and 16-31 (s1).  Operand read
+        //      i = 2ks + r (k-step ks, row block r) is issued three reads ahead
+        //      of its MFMA: with the registers this wave has left, the
+        //      compiler would otherwise issue each read right before its MFMA
+        //      and wait out the whole LDS latency 36 times per tile.
+        f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
         {
-            auto qk_group = [&](auto G) {
-                constexpr int gi = decltype(G)::value, j = gi >> 1, par = gi & 1;
-                const uint32_t base = tb + (par ? qk_o : qk_e) + 384 * j;
-                u32x4_t a[6];
-#pragma unroll
-                for (int u = 0; u < 3; ++u) {
-                    a[2 * u] = lds_ld128(base + 128 * u);
-                    a[2 * u + 1] = lds_ld128(base + 128 * u + R16);
+            const uint32_t be = tb + qk_e, bo = tb + qk_o;
+            u32x4_t a[2 * AB_KS];
+            auto rd = [&](auto Ic) {
+                constexpr int i = decltype(Ic)::value, ks = i >> 1, r = i & 1;
+                lds_read_b128_nowait<128 * (ks >> 1) + r * R16>(a[i], (ks & 1) ? bo : be);
+            };
+            auto step = [&](auto Ic) {
+                constexpr int i = decltype(Ic)::value, ks = i >> 1;
+                constexpr int n = 2 * AB_KS;
+                if constexpr (i + 3 < n) {
+                    rd(std::integral_constant<int, i + 3>{});
+                    lds_operand_wait<3>(a[i]);
+                } else {
+                    lds_operand_wait<n - 1 - i>(a[i]);
                 }
-#pragma unroll
-                for (int u = 0; u < 3; ++u) {
-                    const int ks = 2 * (3 * j + u) + par;
-                    if (par == 0) {
-                        s0a = mfma_16x16x32(a[2 * u], qf[ks], s0a);
-                        s1a = mfma_16x16x32(a[2 * u + 1], qf[ks], s1a);
-                    } else {
-                        s0b = mfma_16x16x32(a[2 * u], qf[ks], s0b);
-                        s1b = mfma_16x16x32(a[2 * u + 1], qf[ks], s1b);
-                    }
+                // the empty asm keeps each MFMA between its wait and the next
+                // read (the scheduler would otherwise sink them all, and keep
+                // every operand live)
+                if constexpr ((i & 1) == 0) {
+                    s0 = mfma_16x16x32(a[i], qf[ks], s0);
+                    asm volatile("" : "+v"(s0));
+                } else {
+                    s1 = mfma_16x16x32(a[i], qf[ks], s1);
+                    asm volatile("" : "+v"(s1));
                 }
             };
-            qk_group(std::integral_constant<int, 0>{});
-            qk_group(std::integral_constant<int, 1>{});
-            qk_group(std::integral_constant<int, 2>{});
-            qk_group(std::integral_constant<int, 3>{});
-            qk_group(std::integral_constant<int, 4>{});
-            qk_group(std::integral_constant<int, 5>{});
+            rd(std::integral_constant<int, 0>{});
+            rd(std::integral_constant<int, 1>{});
+            rd(std::integral_constant<int, 2>{});
+            static_assert(2 * AB_KS == 36, "36 operand reads");
+#define AB_QK_STEP(I) step(std::integral_constant<int, I>{});
+            AB_QK_STEP(0) AB_QK_STEP(1) AB_QK_STEP(2) AB_QK_STEP(3) AB_QK_STEP(4) AB_QK_STEP(5)
+            AB_QK_STEP(6) AB_QK_STEP(7) AB_QK_STEP(8) AB_QK_STEP(9) AB_QK_STEP(10) AB_QK_STEP(11)
+            AB_QK_STEP(12) AB_QK_STEP(13) AB_QK_STEP(14) AB_QK_STEP(15) AB_QK_STEP(16)
+            AB_QK_STEP(17) AB_QK_STEP(18) AB_QK_STEP(19) AB_QK_STEP(20) AB_QK_STEP(21)
+            AB_QK_STEP(22) AB_QK_STEP(23) AB_QK_STEP(24) AB_QK_STEP(25) AB_QK_STEP(26)
+            AB_QK_STEP(27) AB_QK_STEP(28) AB_QK_STEP(29) AB_QK_STEP(30) AB_QK_STEP(31)
+            AB_QK_STEP(32) AB_QK_STEP(33) AB_QK_STEP(34) AB_QK_STEP(35)
+#undef AB_QK_STEP
         }
-        const f32x4_t s0 = s0a + s0b, s1 = s1a + s1b;
 
         // ---- online softmax (log2 domain); lane's keys: 4g+i and 16+4g+i
         float x0[4], x1[4];
@@ -417,37 +430,46 @@ __device__ __forceinline__ void attend_gather_role(
             bhi = u32x4_t{h[0], h[1], h[2], h[3]};
             blo = u32x4_t{l[0], l[1], l[2], l[3]};
         }
-        // ---- O^T[c][head] += V^T[c][keys] P^T[keys][head], 4 column tiles
-        //      per group: 8 transposing reads, then the hi terms of all 4
-        //      tiles and the lo terms, so no MFMA waits on its predecessor
+        // ---- O^T[c][head] += V^T[c][keys] P^T[keys][head], one column tile n
+        //      per step: its two transposing reads are issued three tiles
+        //      ahead, and step n runs the hi term of tile n and the lo term of
+        //      tile n-1, so no MFMA waits on its predecessor
         {
             const uint32_t b0 = tb + pv_base[0], b1 = tb + pv_base[1];
             const uint32_t b2 = tb + pv_base[2], b3 = tb + pv_base[3];
-            auto pv_group = [&](auto M) {
-                constexpr int m = decltype(M)::value;
-                const uint32_t bb[4] = {b0, b1, b2, b3};
-                u32x4_t av[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const uint32_t a = bb[r] + 128 * m;
-                    const u32x2_t va = lds_ld_tr16(a), vb = lds_ld_tr16(a + R16);
-                    av[r] = u32x4_t{va[0], va[1], vb[0], vb[1]};
-                }
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    oacc[4 * m + r] = mfma_16x16x32(av[r], bhi, oacc[4 * m + r]);
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    oacc[4 * m + r] = mfma_16x16x32(av[r], blo, oacc[4 * m + r]);
+            u32x2_t va[AB_NC], vb[AB_NC];
+            auto rd = [&](auto Nc) {
+                constexpr int n = decltype(Nc)::value, r = n & 3, o = 128 * (n >> 2);
+                const uint32_t bb = r == 0 ? b0 : r == 1 ? b1 : r == 2 ? b2 : b3;
+                lds_read_tr16_nowait<o>(va[n], bb);
+                lds_read_tr16_nowait<o + R16>(vb[n], bb);
             };
-            pv_group(std::integral_constant<int, 0>{});
-            pv_group(std::integral_constant<int, 1>{});
-            pv_group(std::integral_constant<int, 2>{});
-            pv_group(std::integral_constant<int, 3>{});
-            pv_group(std::integral_constant<int, 4>{});
-            pv_group(std::integral_constant<int, 5>{});
-            pv_group(std::integral_constant<int, 6>{});
-            pv_group(std::integral_constant<int, 7>{});
+            auto av = [&](int n) { return u32x4_t{va[n][0], va[n][1], vb[n][0], vb[n][1]}; };
+            auto step = [&](auto Nc) {
+                constexpr int n = decltype(Nc)::value;
+                if constexpr (n + 3 < AB_NC) {
+                    rd(std::integral_constant<int, n + 3>{});
+                    lds_operand_wait<6>(va[n], vb[n]);
+                } else {
+                    lds_operand_wait<2 * (AB_NC - 1 - n)>(va[n], vb[n]);
+                }
+                oacc[n] = mfma_16x16x32(av(n), bhi, oacc[n]);
+                if constexpr (n > 0)
+                    oacc[n - 1] = mfma_16x16x32(av(n - 1), blo, oacc[n - 1]);
+            };
+            rd(std::integral_constant<int, 0>{});
+            rd(std::integral_constant<int, 1>{});
+            rd(std::integral_constant<int, 2>{});
+            static_assert(AB_NC == 32, "32 column tiles");
+#define AB_PV_STEP(N) step(std::integral_constant<int, N>{});
+            AB_PV_STEP(0) AB_PV_STEP(1) AB_PV_STEP(2) AB_PV_STEP(3) AB_PV_STEP(4) AB_PV_STEP(5)
+            AB_PV_STEP(6) AB_PV_STEP(7) AB_PV_STEP(8) AB_PV_STEP(9) AB_PV_STEP(10) AB_PV_STEP(11)
+            AB_PV_STEP(12) AB_PV_STEP(13) AB_PV_STEP(14) AB_PV_STEP(15) AB_PV_STEP(16)
+            AB_PV_STEP(17) AB_PV_STEP(18) AB_PV_STEP(19) AB_PV_STEP(20) AB_PV_STEP(21)
+            AB_PV_STEP(22) AB_PV_STEP(23) AB_PV_STEP(24) AB_PV_STEP(25) AB_PV_STEP(26)
+            AB_PV_STEP(27) AB_PV_STEP(28) AB_PV_STEP(29) AB_PV_STEP(30) AB_PV_STEP(31)
+#undef AB_PV_STEP
+            oacc[AB_NC - 1] = mfma_16x16x32(av(AB_NC - 1), blo, oacc[AB_NC - 1]);
         }
     };
 
