@@ -143,16 +143,19 @@ constexpr int AB_TILEB = AB_TILE * AB_ROWB;   // 36 KB per tile
 constexpr int AB_DMA = AB_TILEB / 1024;       // 36 one-KB wave DMA instructions per tile
 constexpr int AB_CW = 4;                      // compute waves, one per SIMD: 16 heads each
 constexpr int AB_CT = 64 * AB_CW;             // compute threads
-constexpr int AB_NT = AB_CT + 64;             // plus one loader wave
+constexpr int AB_NL = 2;                      // loader waves
+constexpr int AB_NT = AB_CT + 64 * AB_NL;     // plus the loader waves
 constexpr int AB_NC = AB_VD / 16;             // 32 output column tiles per wave
 constexpr int AB_STAGES = 3;                  // tiles resident in LDS (ring)
-constexpr int AB_EARLY = 12;                  // DMAs of tile j issued before tile j-1 is released
+constexpr int AB_DMA_L = AB_DMA / AB_NL;      // 18 of them per loader wave
+constexpr int AB_EARLY = 6;                   // loader's DMAs of tile j issued before tile j-1 is released
 constexpr int AB_KB = 6;                      // loader key reads per LDS batch
 constexpr int AB_LIST = 2048;                 // keys per batch of a block
 constexpr int AB_IDX_U = 8;                   // fast path: row entries per thread (n_sel <= 2048)
 constexpr int AB_SET_WORDS = 8192;            // set bitmap of the row: n_k <= 262144
-static_assert(AB_DMA % AB_KB == 0 && AB_EARLY % AB_KB == 0 && AB_EARLY < AB_DMA,
-              "the loader issues whole key batches");
+static_assert(AB_DMA % AB_NL == 0 && AB_DMA_L % AB_KB == 0 && AB_EARLY % AB_KB == 0 &&
+                  AB_EARLY < AB_DMA_L,
+              "each loader issues whole key batches");
 static_assert(AB_LIST == AB_CT * AB_IDX_U, "the fast path lists a whole row");
 
 // LDS tile: 32 latent rows, 1152 bytes apart, with the 16-byte chunks of row
@@ -167,26 +170,28 @@ struct __attribute__((aligned(16))) AbsTiles {
     unsigned char tile[AB_STAGES][AB_TILEB];
 };
 
-// Block = (query row, key split): 4 compute waves (one per SIMD) and one
-// loader wave.  Compute wave w owns heads 16w .. 16w+15 with Q for all 576
+// Block = (query row, key split): 4 compute waves (one per SIMD) and two
+// loader waves.  Compute wave w owns heads 16w .. 16w+15 with Q for all 576
 // dims and O for all 512 columns in registers, and every key of every tile;
-// each tile (loaded once, 36 KB) feeds all 64 heads.  The loader wave issues
-// every direct-to-LDS load of the tiles, so the compute waves never stall on
-// a full memory queue: a wave that issues loads waits at each one until the
-// queue takes it, and while the kernel streams rows the queue is full.  Tile
-// j's first AB_EARLY loads are issued before the loader waits for tile j-1,
-// so the queue stays fed across the barrier that releases tile j-1.
+// each tile (loaded once, 36 KB) feeds all 64 heads.  The loader waves issue
+// every direct-to-LDS load of the tiles (half each), so the compute waves
+// never stall on a full memory queue: a wave that issues loads waits at each
+// one until the queue takes it, and while the kernel streams rows the queue
+// is full.  Two loaders keep more loads in flight than one, which alone
+// held a CU near 10 bytes per cycle.  Tile j's first AB_EARLY loads (per
+// loader) are issued before the loaders wait for tile j-1, so the queue
+// stays fed across the barrier that releases tile j-1.
 //
 // Which keys: the selected set of the row (distinct, in range, visible) is
 // split into `splits` contiguous shares.  Fast path (n_sel <= 2048): the
 // valid entries are listed in index order and the shares taken from that
-// list, so the tiles start streaming at once; the loader wave builds the
+// list, so the tiles start streaming at once; the loader waves build the
 // row's set bitmap from the list while the last tile is computed, and if it
 // holds fewer keys than there were valid entries (a key repeats) the block
 // starts over from the bitmap (keys in ascending order, duplicates
 // collapsed).  Rows with n_sel > 2048 go to the bitmap directly.
 // The two roles are separate instantiations, so the registers of one (Q and
-// O of the compute waves, the load slots of the loader) are not live in the
+// O of the compute waves, the load slots of the loaders) are not live in the
 // other; they share only LDS and the barriers, which both pass in the same
 // sequence.
 struct AbsShared {
@@ -211,7 +216,8 @@ __device__ __forceinline__ void attend_gather_role(
     constexpr bool loader = LOADER;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wid = LOADER ? AB_CW : __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lw = LOADER ? wid - AB_CW : 0;  // loader wave index
     const int g = lane >> 4, col = lane & 15;
     // the splits of one row run on one XCD (shared q, idx and partials);
     // without splits the rows keep launch order, which spreads the uneven
@@ -271,16 +277,16 @@ __device__ __forceinline__ void attend_gather_role(
     const uint32_t lds_list = lds_addr(sm_list);
     const uint32_t lds_set = lds_addr(sm_set);
 
-    // Loader: wave instruction s (1 KB) of a tile fills LDS bytes s*1024 +
+    // Loaders: wave instruction s (1 KB) of a tile fills LDS bytes s*1024 +
     // 16*lane = (row, physical chunk) from the logical chunk of that row's
-    // key.  The (row, byte offset) of this lane's slot s is fixed and packed
-    // in one register.  Offsets are 32-bit (the host keeps 2*row_stride
-    // below 2^31).
-    uint32_t slot[AB_DMA];
+    // key; loader lw issues instructions 18lw .. 18lw+17.  The (row, byte
+    // offset) of this lane's slot is fixed and packed in one register.
+    // Offsets are 32-bit (the host keeps 2*row_stride below 2^31).
+    uint32_t slot[AB_DMA_L];
     if (loader) {
 #pragma unroll
-        for (int s = 0; s < AB_DMA; ++s) {
-            const int c = s * 64 + lane;
+        for (int s = 0; s < AB_DMA_L; ++s) {
+            const int c = (lw * AB_DMA_L + s) * 64 + lane;
             slot[s] = ((uint32_t)(c / AB_CPR) << 16) |
                       (uint32_t)(((c % AB_CPR) ^ chunk_swz_odd(c / AB_CPR)) * 16);
         }
@@ -299,7 +305,7 @@ __device__ __forceinline__ void attend_gather_role(
 #pragma unroll
             for (int b = 0; b < AB_KB; ++b)
                 lds_dma16(kvb + (uint64_t)key[b] * rs2 + (slot[s + b] & 0xffffu),
-                          dst + (s + b) * 1024);
+                          dst + (lw * AB_DMA_L + s + b) * 1024);
         }
     };
 
@@ -486,7 +492,7 @@ __device__ __forceinline__ void attend_gather_role(
         auto tile_n = [&](int t) { return min(AB_TILE, n_my - t * AB_TILE); };
         if (loader) {
             if (ntiles > 0)
-                issue(std::integral_constant<int, 0>{}, std::integral_constant<int, AB_DMA>{},
+                issue(std::integral_constant<int, 0>{}, std::integral_constant<int, AB_DMA_L>{},
                       tile_ptr(0), lkeys, tile_n(0));
             for (int j = 1; j <= ntiles; ++j) {
                 // tile j's first loads, then tile j-1 has landed: release it
@@ -501,7 +507,7 @@ __device__ __forceinline__ void attend_gather_role(
                 lds_barrier();  // B_{j-1}
                 if (j < ntiles)
                     issue(std::integral_constant<int, AB_EARLY>{},
-                          std::integral_constant<int, AB_DMA>{}, tile_ptr(j),
+                          std::integral_constant<int, AB_DMA_L>{}, tile_ptr(j),
                           lkeys + 4u * (uint32_t)(j * AB_TILE), tile_n(j));
             }
         } else {
@@ -617,9 +623,9 @@ __device__ __forceinline__ void attend_gather_role(
         }
         run_tiles(first, n_my);
         if (batch < 0 && loader) {
-            // the loader puts the listed entries into the set bitmap while
+            // the loaders put the listed entries into the set bitmap while
             // the compute waves finish the last tile
-            for (int i0 = 0; i0 < n_valid; i0 += 64 * AB_KB) {
+            for (int i0 = lw * 64 * AB_KB; i0 < n_valid; i0 += 64 * AB_KB * AB_NL) {
                 uint32_t ka[AB_KB], key[AB_KB];
 #pragma unroll
                 for (int b = 0; b < AB_KB; ++b)
@@ -717,7 +723,7 @@ __global__ __launch_bounds__(AB_NT) void attend_gather_kernel(
 {
     __shared__ AbsShared shm;
     DSA_LDS_ESCAPE(shm);
-    if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == AB_CW)
+    if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) >= AB_CW)
         attend_gather_role<true>(shm, q, kv, row_stride, idx, vlo, vhi, out, lse, ws_o, ws_ml,
                                  n_q, n_k, n_sel, splits, scale_log2);
     else
