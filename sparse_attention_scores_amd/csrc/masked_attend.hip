@@ -68,23 +68,6 @@ __global__ __launch_bounds__(256) void topk_to_mask_kernel(const int32_t *__rest
 __device__ __forceinline__ int mk_swz_k(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int mk_swz_v(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 
-// Four transposing LDS reads (2 column tiles x rows ra / rb) and the wait
-// (asm, for the reason given at lds_read_b32_3).
-template <int O>
-__device__ __forceinline__ void lds_read_tr16x4_4(u32x2_t (&a)[4], uint32_t r0, uint32_t r1,
-                                                  uint32_t s0, uint32_t s1)
-{
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %4 offset:%8\n\t"
-        "ds_read_b64_tr_b16 %1, %6 offset:%8\n\t"
-        "ds_read_b64_tr_b16 %2, %5 offset:%8\n\t"
-        "ds_read_b64_tr_b16 %3, %7 offset:%8\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3])
-        : "v"(r0), "v"(r1), "v"(s0), "v"(s1), "i"(O)
-        : "memory");
-}
-
 // Three 4-byte LDS reads and the wait (asm: the words arrive by direct-to-LDS
 // loads, and the compiler would otherwise wait for every such load in flight).
 __device__ __forceinline__ void lds_read_b32_3(uint32_t &x, uint32_t &y, uint32_t &z,
@@ -353,43 +336,50 @@ __global__ __launch_bounds__(256, 2) void attend_masked_kernel(
         }
         l_part += psum;
         // ---- O^T[c][query] += V^T[c][keys] P^T[keys][query], per 16-key half
+        // step T (kh = T >> 3, column tile n = T & 7) reads V^T rows ra / rb
+        // of key half kh at column tile n: bases va_/vb_[n & 3], immediate
+        // 256 * (n >> 2) + 16 rows * kh; the reads run two steps ahead of
+        // the MFMAs that use them
         const uint32_t vt = lds_v + st * Sm::VB;
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-            uint32_t hi4[4], lo4[4];
-            {
+        u32x2_t ra2[2 * NCT], rb2[2 * NCT];
+        auto rd = [&](auto Tc) {
+            constexpr int T = decltype(Tc)::value, n = T & 7, kh = T >> 3;
+            constexpr int o = 256 * (n >> 2) + kh * 16 * VD * 2;
+            lds_read_tr16_nowait<o>(ra2[T], vt + va_[n & 3]);
+            lds_read_tr16_nowait<o>(rb2[T], vt + vb_[n & 3]);
+        };
+        u32x4_t bhi, blo;
+        auto step = [&](auto Tc) {
+            constexpr int T = decltype(Tc)::value, n = T & 7;
+            constexpr int NS = 2 * NCT;
+            if constexpr (T + 2 < NS) {
+                rd(std::integral_constant<int, T + 2>{});
+                lds_operand_wait<4>(ra2[T], rb2[T]);
+            } else {
+                lds_operand_wait<2 * (NS - 1 - T)>(ra2[T], rb2[T]);
+            }
+            if constexpr (n == 0) {
+                uint32_t hi4[4], lo4[4];
                 float ph[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j)
-                    ph[j] = p[kh * 8 + j];
+                    ph[j] = p[(T >> 3) * 8 + j];
                 split_bf16x8(ph, hi4, lo4);
+                bhi = u32x4_t{hi4[0], hi4[1], hi4[2], hi4[3]};
+                blo = u32x4_t{lo4[0], lo4[1], lo4[2], lo4[3]};
             }
-            const u32x4_t bhi = {hi4[0], hi4[1], hi4[2], hi4[3]};
-            const u32x4_t blo = {lo4[0], lo4[1], lo4[2], lo4[3]};
-            const uint32_t vk = vt + kh * 16 * VD * 2;
-            // column tile n = n0 + j reads bases va_/vb_[n & 3] at 256 * (n >> 2),
-            // two tiles per group
-            auto pv2 = [&](auto N0) {
-                constexpr int n0 = decltype(N0)::value, j0 = n0 & 3, o = 256 * (n0 >> 2);
-                u32x2_t rd[4];
-                lds_read_tr16x4_4<o>(rd, vk + va_[j0], vk + va_[j0 + 1], vk + vb_[j0],
-                                     vk + vb_[j0 + 1]);
-                u32x4_t av[2];
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    av[j] = u32x4_t{rd[2 * j][0], rd[2 * j][1], rd[2 * j + 1][0], rd[2 * j + 1][1]};
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    oacc[n0 + j] = mfma_32x32x16(av[j], bhi, oacc[n0 + j]);
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    oacc[n0 + j] = mfma_32x32x16(av[j], blo, oacc[n0 + j]);
-            };
-            pv2(std::integral_constant<int, 0>{});
-            pv2(std::integral_constant<int, 2>{});
-            pv2(std::integral_constant<int, 4>{});
-            pv2(std::integral_constant<int, 6>{});
-        }
+            const u32x4_t av = {ra2[T][0], ra2[T][1], rb2[T][0], rb2[T][1]};
+            oacc[n] = mfma_32x32x16(av, bhi, oacc[n]);
+            oacc[n] = mfma_32x32x16(av, blo, oacc[n]);
+        };
+        static_assert(NCT == 8, "eight column tiles");
+        rd(std::integral_constant<int, 0>{});
+        rd(std::integral_constant<int, 1>{});
+#define MK_PV_STEP(T) step(std::integral_constant<int, T>{});
+        MK_PV_STEP(0) MK_PV_STEP(1) MK_PV_STEP(2) MK_PV_STEP(3) MK_PV_STEP(4) MK_PV_STEP(5)
+        MK_PV_STEP(6) MK_PV_STEP(7) MK_PV_STEP(8) MK_PV_STEP(9) MK_PV_STEP(10) MK_PV_STEP(11)
+        MK_PV_STEP(12) MK_PV_STEP(13) MK_PV_STEP(14) MK_PV_STEP(15)
+#undef MK_PV_STEP
     }
 
     // ---- epilogue
