@@ -465,14 +465,34 @@ __global__ __launch_bounds__(64 * IP_NW) void index_scores_prefill_kernel(
                 wr[qi][i] = w[qrow[qi] * IP_H + 8 * (i / 4) + 4 * g + (i % 4)] * fabsf(scale);
         }
         {
-            for (int tt = half; tt < nt; tt += 2) {
-                if (tt >= ta && tt < tb)
-                    continue;
-                const int key = c0 + tt * 32 + col;
+            // the keys of the chunk before tile ta and from tile tb on, in
+            // 16-byte stores (the two halves take half of each range): 8x
+            // fewer store instructions than one 4-byte score per lane
+            const int ra[2] = {c0, min(c1, c0 + 32 * tb)};
+            const int rb[2] = {min(c1, c0 + 32 * ta), c1};
 #pragma unroll
-                for (int qi = 0; qi < IP_QPW; ++qi)
-                    if (lane < 32 && key < c1 && qok[qi])
-                        scores[qrow[qi] * n_k + key] = -FLT_MAX;
+            for (int qi = 0; qi < IP_QPW; ++qi) {
+                if (!qok[qi])
+                    continue;
+                float *rp = scores + qrow[qi] * n_k;
+                const int g0 = (int)((reinterpret_cast<uintptr_t>(rp) >> 2) & 3);  // row start mod 4 floats
+#pragma unroll
+                for (int r = 0; r < 2; ++r) {
+                    const int mid = ra[r] + ((rb[r] - ra[r]) / 2 & ~3);
+                    const int a = half ? mid : ra[r], b = half ? rb[r] : mid;
+                    if (a >= b)
+                        continue;
+                    // scalar head up to a 16-byte boundary, vector body, scalar tail
+                    const int ha = min(b, a + (int)((4 - ((g0 + a) & 3)) & 3));
+                    const int tb4 = max(ha, b - (int)((g0 + b) & 3));
+                    if (a + lane < ha)
+                        rp[a + lane] = -FLT_MAX;
+                    for (int j = ha + 4 * lane; j < tb4; j += 256)
+                        *reinterpret_cast<f32x4_t *>(rp + j) =
+                            f32x4_t{-FLT_MAX, -FLT_MAX, -FLT_MAX, -FLT_MAX};
+                    if (tb4 + lane < b)
+                        rp[tb4 + lane] = -FLT_MAX;
+                }
             }
         }
         if (t0 >= t1)
