@@ -576,17 +576,25 @@ __global__ __launch_bounds__(64 * IP_NW) void index_scores_prefill_kernel(
             asm volatile("" : "+v"(part[0]), "+v"(part[1]));
         };
         // the head sum's second half and the stores of tile tt
+        // (one store for both queries: lanes 0-31 write query 0's row,
+        // lanes 32-63 query 1's; after the swap both halves hold each sum)
         auto store = [&](float (&part)[IP_QPW], int tt) {
             const int key = c0 + tt * 32 + col;
+            float v[IP_QPW];
 #pragma unroll
             for (int qi = 0; qi < IP_QPW; ++qi) {
                 const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[qi]),
                                                                  __float_as_uint(part[qi]), false,
                                                                  false);
-                const float v = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-                if (lane < 32 && key < c1 && qok[qi])
-                    scores[qrow[qi] * n_k + key] = (key >= lo[qi] && key < hi[qi]) ? v : -FLT_MAX;
+                v[qi] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
             }
+            static_assert(IP_QPW == 2, "one query per half-wave");
+            const float val = g ? v[1] : v[0];
+            const bool ok = g ? qok[1] : qok[0];
+            const int klo = g ? lo[1] : lo[0], khi = g ? hi[1] : hi[0];
+            const int64_t rowoff = (g ? qrow[1] : qrow[0]) * n_k;
+            if (key < c1 && ok)
+                scores[rowoff + key] = (key >= klo && key < khi) ? val : -FLT_MAX;
         };
         f32x16_t acc_a[IP_QPW], acc_b[IP_QPW];
         float part[IP_QPW];
