@@ -309,6 +309,8 @@ def _oracle_sel(inp, S, k):
 
 ABSORBED_CASES = [
     (2, dict(B=3, Tk=1500), None, 512),
+    # 15 splits of 66-67 keys: ragged last tiles in every split-K block
+    (2, dict(B=3, Tk=1500), None, 1000),
     (2, dict(B=2, Tk=2111), "sharp", 2048),
     (3, dict(Tq=200, Tk=200), None, 64),
     (4, dict(B=2, Tk=5000), None, 2048),
