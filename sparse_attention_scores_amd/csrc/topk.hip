@@ -247,7 +247,9 @@ __global__ __launch_bounds__(NT) void topk_seg_kernel(const float *__restrict__ 
         const int base = (int)sm.bk.off[bf];
         const int crowd = max(sm.red[0][0][0], sm.red[0][0][1]);
         const int total = (bl + 1 < NB ? (int)sm.bk.off[bl + 1] : n) - base;  // keys of bf .. bl
-        ok = crowd <= kSegMaxBucket && total <= kTopkMaxK;
+        // the collection buffer holds 3072 keys: k plus the rest of the last bucket
+        constexpr int kCollect = (int)((sizeof(sm.word[1]) + sizeof(sm.wcol)) / 8);
+        ok = crowd <= kSegMaxBucket && total <= kCollect;
         if (ok) {
             // fill pointers of buckets bf .. bl, then the collection from registers
 #pragma unroll
@@ -258,7 +260,7 @@ __global__ __launch_bounds__(NT) void topk_seg_kernel(const float *__restrict__ 
             }
             __syncthreads();
             uint64_t *ck = reinterpret_cast<uint64_t *>(&sm.word[1][0]);
-            static_assert(sizeof(sm.word[1]) + sizeof(sm.wcol) >= kTopkMaxK * 8,
+            static_assert(kCollect >= kTopkMaxK + kSegMaxBucket,
                           "composite key buffer");
 #pragma unroll
             for (int r = 0; r < R; ++r) {
@@ -698,8 +700,13 @@ hipError_t launch_topk(const TopkArgs &a, hipStream_t st)
 {
     // sort sizes: NT threads x EPT keys >= k
     if (a.n_cols <= kCapSmall) {
-        hipLaunchKernelGGL((topk_sorted_kernel<512, kCapSmall>), dim3(a.rows), dim3(512), 0, st,
-                           a.scores, a.n_cols, a.row_stride, a.vis_lo, a.vis_hi, a.k, a.out);
+        // value buckets place each winner without sorting the row; several
+        // blocks per row when there are few rows
+        const int parts = topk_seg_parts(a.rows, a.k, 16);
+        const int seg_len = (a.k + parts - 1) / parts;
+        hipLaunchKernelGGL((topk_seg_kernel<512, kCapSmall>), dim3(a.rows * parts), dim3(512), 0,
+                           st, a.scores, a.n_cols, a.row_stride, a.vis_lo, a.vis_hi, a.k, a.out,
+                           parts, seg_len);
         return hipGetLastError();
     }
     constexpr int NT = 1024;
