@@ -49,7 +49,7 @@ WORKLOAD_NAME = {1: "tiny_fp32_64", 2: "decode_b32x8192", 3: "prefill_4096",
 # the kernels each ABI call of a stage launches (substrings of their names)
 STAGE_KERNELS = {
     "index": ("index_scores",),
-    "topk": ("topk_sorted_kernel", "topk_seg_kernel", "topk_chunk_kernel", "topk_merge_kernel",
+    "topk": ("topk_seg_kernel", "topk_chunk_kernel", "topk_merge_kernel",
              "topk_merge_seg_kernel"),
     "attend": ("attend_gather_kernel", "attend_combine_kernel", "topk_to_mask_kernel",
                "attend_masked_kernel", "attend_plain_kernel"),

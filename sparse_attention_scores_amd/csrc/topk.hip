@@ -11,10 +11,11 @@
 // distinct, so "the k largest keys" is one well-defined set.
 //
 // Paths, by shape (every one exact):
-//  * many rows, up to 16384 keys: one block per row -- 32-bit radix select
-//    over the cached order keys, compaction, bucket sort (topk_sorted_kernel);
-//  * few rows, up to 16384 keys: several blocks per row, each writing one
-//    segment of the ranks from value buckets (topk_seg_kernel);
+//  * up to 16384 keys: value buckets place each winner without sorting the
+//    row (topk_seg_kernel), one block per row, or several blocks per row each
+//    writing one segment of the ranks when there are few rows; a block whose
+//    ranks fall into a crowded bucket sorts the row instead (32-bit radix
+//    select, compaction, bucket sort: topk_sort_cached);
 //  * longer rows: each 16384-key chunk keeps its own top k (the global top-k
 //    is a subset of the union of the chunk top-ks, the order being total),
 //    then a merge selects and sorts among those candidates -- segmented over
@@ -58,27 +59,6 @@ __device__ int topk_sort_cached(Topk32Smem<NT, CAP> &sm, int n, int lo, int k, u
         buf = wmin == wmax ? 0 : sort32(sm, m, wmin, wmax);
     }
     return m;
-}
-
-// Whole row in one block, sorted output.
-template <int NT, int CAP>
-__global__ __launch_bounds__(NT) void topk_sorted_kernel(const float *__restrict__ scores,
-                                                         int n_cols, int64_t row_stride,
-                                                         const int32_t *__restrict__ vlo,
-                                                         const int32_t *__restrict__ vhi, int k,
-                                                         int32_t *__restrict__ out)
-{
-    __shared__ Topk32Smem<NT, CAP> sm;
-    const int tid = threadIdx.x;
-    const int row = blockIdx.x;
-    const int lo = max(vlo[row], 0), hi = min(vhi[row], n_cols);
-    uint32_t omin, omax;
-    const int n = load_row32(sm, scores + (int64_t)row * row_stride, lo, hi, omin, omax);
-    int buf;
-    const int m = topk_sort_cached(sm, n, lo, k, omin, omax, buf);
-    int32_t *o = out + (int64_t)row * k;
-    for (int i = tid; i < k; i += NT)
-        o[i] = i < m ? (int32_t)sm.wcol[buf][i] : -1;
 }
 
 // Float value of an order key (inverse of score_order_key; -0 comes back
@@ -713,15 +693,10 @@ hipError_t launch_topk(const TopkArgs &a, hipStream_t st)
     if (a.n_cols <= kCapLarge) {
         // few rows: several blocks per row, each writing a segment of it
         const int parts = topk_seg_parts(a.rows, a.k, 16);
-        if (parts > 1) {
-            const int seg_len = (a.k + parts - 1) / parts;
-            hipLaunchKernelGGL((topk_seg_kernel<NT, kCapLarge>), dim3(a.rows * parts), dim3(NT),
-                               0, st, a.scores, a.n_cols, a.row_stride, a.vis_lo, a.vis_hi, a.k,
-                               a.out, parts, seg_len);
-            return hipGetLastError();
-        }
-        hipLaunchKernelGGL((topk_sorted_kernel<NT, kCapLarge>), dim3(a.rows), dim3(NT), 0, st,
-                           a.scores, a.n_cols, a.row_stride, a.vis_lo, a.vis_hi, a.k, a.out);
+        const int seg_len = (a.k + parts - 1) / parts;
+        hipLaunchKernelGGL((topk_seg_kernel<NT, kCapLarge>), dim3(a.rows * parts), dim3(NT), 0,
+                           st, a.scores, a.n_cols, a.row_stride, a.vis_lo, a.vis_hi, a.k, a.out,
+                           parts, seg_len);
         return hipGetLastError();
     }
     const int n_chunks = (a.n_cols + kCapLarge - 1) / kCapLarge;

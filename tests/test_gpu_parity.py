@@ -160,6 +160,7 @@ TOPK_CASES = [
     (2, dict(B=4, Tk=8192), None, 2048),     # bench row length, one block per row
     (2, dict(B=3, Tk=517), "tie", 64),       # massive exact ties
     (2, dict(B=2, Tk=3000), None, 2048),     # k > visible for none, small-block path
+    (2, dict(B=300, Tk=6000), None, 2048),   # many rows of 6000 keys: one block per row
     (3, dict(Tq=300, Tk=300), None, 100),    # causal: k >= visible on early rows
     (3, dict(Tq=2600, Tk=2600), None, 2048), # short rows, k = 2048: the last bucket spills past k
     (4, dict(B=2, Tk=40000), None, 2048),    # > one block's cache: two-launch path
