@@ -204,6 +204,7 @@ __global__ __launch_bounds__(NT) void topk_seg_kernel(const float *__restrict__ 
         for (int j = 0; j < PB; ++j) {
             const int b = tid * PB + j, c = (int)v[j];
             sm.bk.off[b] = (uint32_t)run;
+            sm.bk.fill[b] = (uint32_t)run;  // fill pointer of the collection below
             if (run <= s0 && s0 < run + c) {
                 sm.tab[1][0] = b;
                 crowd_lo = c;
@@ -231,21 +232,14 @@ __global__ __launch_bounds__(NT) void topk_seg_kernel(const float *__restrict__ 
         constexpr int kCollect = (int)((sizeof(sm.word[1]) + sizeof(sm.wcol)) / 8);
         ok = crowd <= kSegMaxBucket && total <= kCollect;
         if (ok) {
-            // fill pointers of buckets bf .. bl, then the collection from registers
-#pragma unroll
-            for (int j = 0; j < PB; ++j) {
-                const int b = tid * PB + j;
-                if (b >= bf && b <= bl)
-                    sm.bk.fill[b] = sm.bk.off[b] - (uint32_t)base;
-            }
-            __syncthreads();
+            // the collection from registers (key of rank base + i at ck[i])
             uint64_t *ck = reinterpret_cast<uint64_t *>(&sm.word[1][0]);
             static_assert(kCollect >= kTopkMaxK + kSegMaxBucket,
                           "composite key buffer");
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 if (bk[r] >= bf && bk[r] <= bl)
-                    ck[atomicAdd(&sm.bk.fill[bk[r]], 1u)] =
+                    ck[atomicAdd(&sm.bk.fill[bk[r]], 1u) - (uint32_t)base] =
                         ((uint64_t)ord[r] << 32) |
                         (uint64_t)(0xffffffffu - (uint32_t)(lo + r * NT + tid));
             }
@@ -255,7 +249,7 @@ __global__ __launch_bounds__(NT) void topk_seg_kernel(const float *__restrict__ 
             for (int j = tid; j < total; j += NT) {
                 const uint64_t key = ck[j];
                 const int b = bucket((uint32_t)(key >> 32));
-                const int b0 = (int)sm.bk.off[b] - base, b1 = (int)sm.bk.fill[b];
+                const int b0 = (int)sm.bk.off[b] - base, b1 = (int)sm.bk.fill[b] - base;
                 int r = (int)sm.bk.off[b];
                 for (int x = b0; x < b1; ++x)
                     r += ck[x] > key;
