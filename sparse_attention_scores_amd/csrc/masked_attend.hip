@@ -36,7 +36,7 @@ __global__ __launch_bounds__(256) void topk_to_mask_kernel(const int32_t *__rest
                                                            uint32_t *__restrict__ mask, int n_k,
                                                            int n_sel, int nw)
 {
-    __shared__ uint32_t bits[MK_MAXWORDS];
+    extern __shared__ uint32_t bits[];  // nw words (launch size), at most MK_MAXWORDS
     const int row = blockIdx.x;
     int lo = 0, hi = n_k;
     if (vlo) {
@@ -425,7 +425,11 @@ hipError_t launch_attend_masked(const AttendArgs &a, hipStream_t st)
     const int64_t rows = (int64_t)a.batch * a.n_q;
     const int nw = (a.n_k + 31) / 32;
     uint32_t *mask = static_cast<uint32_t *>(a.workspace);
-    hipLaunchKernelGGL(topk_to_mask_kernel, dim3((unsigned)rows), dim3(256), 0, st, a.idx,
+    if (nw > MK_MAXWORDS)  // the ABI rejects such rows before this
+        return hipErrorInvalidValue;
+    // LDS sized to the row (2 KB for 16384 keys) so that many rows share a CU
+    hipLaunchKernelGGL(topk_to_mask_kernel, dim3((unsigned)rows), dim3(256),
+                       (unsigned)(nw * sizeof(uint32_t)), st, a.idx,
                        a.vis_lo, a.vis_hi, mask, a.n_k, a.n_sel, nw);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
