@@ -221,9 +221,12 @@ def pooled_work(inp):
 
 
 def algorithmic_work(inp):
-    """Bytes the method must move and flops it must do, per stage (see the
-    measurement section of the design doc): only visible pairs and selected keys
-    count, not the dense work the method avoids."""
+    """Bytes the method must move and flops it must do, per stage: only
+    visible pairs and selected keys count, not the dense work the method
+    avoids.  Index: the keys once, the queries and head weights, one f32 score
+    per visible pair.  Top-k: the visible scores and the selected indices.
+    Attend: the selected latent rows once (prefill: the distinct rows once),
+    the queries, the indices and the f32 output and lse."""
     B, Tq, Tk, Hi, d = inp["B"], inp["Tq"], inp["Tk"], inp["Hi"], inp["d"]
     H, kd, vd, k = inp["H"], inp["kd"], inp["vd"], inp["top_k"]
     f32 = inp["dtype"] == "f32"
@@ -319,8 +322,8 @@ def main():
     args = _parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(see DESIGN.md for how it would shard)", file=sys.stderr)
+        print("bench.py runs on one GPU only: the layer step here has no "
+              "multi-GPU path (the design notes say how it would shard)", file=sys.stderr)
         sys.exit(2)
     import torch
 

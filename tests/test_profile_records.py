@@ -67,3 +67,24 @@ def test_mfma_record_use_fraction(tmp_path):
     rows = [l.split() for l in text.splitlines() if not l.startswith("#")]
     # 1228800 busy cycles over 1 us at 2.4 GHz on 1024 SIMDs = 0.5 of the chip
     assert rows == [["dsa::attend_gather_kernel", "1000", "1228800", "1.00", "0.500"]]
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_algorithmic_work_decode_closed_form():
+    # decode config: every visible pair and every selected key counted once
+    inp = dict(B=2, Tq=1, Tk=1000, Hi=4, d=8, H=3, kd=16, vd=8, top_k=100, dtype="bf16")
+    w = bench.algorithmic_work(inp)
+    idx_bytes = 2 * 1000 * 8 * 2 + 2 * 4 * 8 * 2 + 2 * 4 * 4 + 2 * 1000 * 4
+    assert w["index"] == (idx_bytes, 2 * 4 * 8 * 2 * 1000)
+    assert w["topk"] == (2 * 1000 * 4 + 2 * 100 * 4, 0)
+    att_bytes = 2 * 100 * 16 * 2 + 2 * 3 * 16 * 2 + 2 * 100 * 4 + 2 * 3 * (8 + 1) * 4
+    assert w["attend"] == (att_bytes, 2 * 3 * (16 + 8) * 2 * 100)
