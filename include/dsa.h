@@ -111,10 +111,12 @@ int dsa_visibility_ranges(int32_t batch, int32_t n_q, const int32_t *pad,
  * vis_lo, vis_hi: [batch, n_q] int32
  * scores:  [batch, n_q, n_k] f32 output
  *
- * Envelope: BF16 q requires n_heads a multiple of 32 (at most 64) and
- * head_dim 64 or 128, accumulating bf16 products in f32 on MFMA; F32 takes
- * any shape.  Rounding: each product is exact and the sums are f32, so
- * |err| is a few f32 ulps of sum_h |w| |scale| sum_c |q k|.
+ * Envelope: BF16 q requires n_heads 32 or 64 and head_dim 64 or 128,
+ * accumulating the exact bf16 products in f32 on MFMA, so |err| <=
+ * (head_dim + n_heads + 4) * 2^-23 * sum_h |w| |scale| sum_c |q k|.  F32
+ * takes any shape and sums the exact products in f64, so the score is
+ * within a few f32 ulps of its own value unless the sum cancels almost
+ * completely.
  * ------------------------------------------------------------------------ */
 typedef struct {
     int32_t batch, n_q, n_k, n_heads, head_dim;

@@ -154,6 +154,18 @@ def _i32(t):
     return t
 
 
+def _shape(t, shape, name: str, dtype=None):
+    """Raise unless t (when given) has exactly `shape` (and `dtype`): a short
+    or mistyped tensor would otherwise become an out-of-bounds device read."""
+    if t is None:
+        return t
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    return t
+
+
 def _workspace(nbytes: int, ws, device):
     if nbytes == 0:
         return None, 0
@@ -168,10 +180,13 @@ def _workspace(nbytes: int, ws, device):
 
 def visibility_ranges(pad, q_pos, kpool: int = 0, lo=None, hi=None):
     """[vis_lo, vis_hi) per query (token keys, or pools when kpool > 0)."""
-    _dev(pad, q_pos)
+    _dev(pad, q_pos, lo, hi)
     B, n_q = q_pos.shape
+    _shape(pad, (B,), "visibility_ranges: pad", torch.int32)
     lo = torch.empty((B, n_q), dtype=torch.int32, device=q_pos.device) if lo is None else lo
     hi = torch.empty((B, n_q), dtype=torch.int32, device=q_pos.device) if hi is None else hi
+    _shape(lo, (B, n_q), "visibility_ranges: lo", torch.int32)
+    _shape(hi, (B, n_q), "visibility_ranges: hi", torch.int32)
     _check(load().dsa_visibility_ranges(B, n_q, _p(_i32(pad)), _p(_i32(q_pos)), kpool, _p(lo),
                                         _p(hi), _stream()))
     return lo, hi
@@ -186,8 +201,11 @@ def index_scores(q, k, w, vis_lo, vis_hi, scale: float, k_scale=None, out=None):
         raise ValueError("index_scores: shape/dtype mismatch")
     if k_scale is not None and (k_scale.shape != (B, n_k) or k_scale.dtype != torch.float32):
         raise ValueError("index_scores: k_scale must be f32 [B, n_k]")
+    _shape(vis_lo, (B, n_q), "index_scores: vis_lo", torch.int32)
+    _shape(vis_hi, (B, n_q), "index_scores: vis_hi", torch.int32)
     if out is None:
         out = torch.empty((B, n_q, n_k), dtype=torch.float32, device=q.device)
+    _shape(out, (B, n_q, n_k), "index_scores: out", torch.float32)
     dims = _IndexDims(B, n_q, n_k, H, d, float(scale))
     _check(load().dsa_index_scores(ctypes.byref(dims), _p(q), _dtype_code(q), _p(k),
                                    _dtype_code(k), _p(k_scale), _p(w), _p(_i32(vis_lo)),
@@ -202,11 +220,18 @@ def topk_workspace_size(rows: int, n_cols: int, top_k: int) -> int:
 def topk(scores, vis_lo, vis_hi, top_k: int, out=None, workspace=None):
     """Top-k index rows [..., top_k] (int32, rank order, INVALID-padded)."""
     _dev(scores, vis_lo, vis_hi, out)
+    if scores.dtype != torch.float32:
+        raise TypeError(f"topk: scores must be float32, got {scores.dtype}")
     lead = scores.shape[:-1]
     n_cols = scores.shape[-1]
     rows = math.prod(lead)
+    if vis_lo.numel() != rows or vis_hi.numel() != rows:
+        raise ValueError(f"topk: vis_lo/vis_hi need {rows} elements, got "
+                         f"{vis_lo.numel()}/{vis_hi.numel()}")
     if out is None:
         out = torch.empty((*lead, top_k), dtype=torch.int32, device=scores.device)
+    if out.numel() != rows * top_k or out.dtype != torch.int32:
+        raise ValueError(f"topk: out must be int32 with {rows} x {top_k} elements")
     ws, wsb = _workspace(topk_workspace_size(rows, n_cols, top_k), workspace, scores.device)
     _check(load().dsa_topk(_p(scores), rows, n_cols, n_cols, _p(_i32(vis_lo)), _p(_i32(vis_hi)),
                            top_k, _p(out), _p(ws), wsb, _stream()))
@@ -244,13 +269,19 @@ def sparse_attend(q, k, v, idx, scale: float, kv_heads: int, vd: int | None = No
         v_ptr, v_row = _p(v), v.stride(1)
         if v.dtype != q.dtype or v.shape[:2] != (B, n_k):
             raise ValueError("sparse_attend: v shape/dtype mismatch")
-    if k.dtype != q.dtype or k.shape[0] != B or idx.shape[:2] != (B, n_q):
+    if k.dtype != q.dtype or k.shape[0] != B or idx.dim() != 3 or idx.shape[:2] != (B, n_q):
         raise ValueError("sparse_attend: shape/dtype mismatch")
+    if (vis_lo is None) != (vis_hi is None):
+        raise ValueError("sparse_attend: give both vis_lo and vis_hi or neither")
+    _shape(vis_lo, (B, n_q), "sparse_attend: vis_lo", torch.int32)
+    _shape(vis_hi, (B, n_q), "sparse_attend: vis_hi", torch.int32)
     dims = _attn_dims(q, k, n_k, idx, kv_heads, vd, kd, scale)
     if out is None:
         out = torch.empty((B, n_q, H, vd), dtype=torch.float32, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty((B, n_q, H), dtype=torch.float32, device=q.device)
+    _shape(out, (B, n_q, H, vd), "sparse_attend: out", torch.float32)
+    _shape(lse, (B, n_q, H), "sparse_attend: lse", torch.float32)
     ws, wsb = _workspace(sparse_attend_workspace_size(dims), workspace, q.device)
     _check(load().dsa_sparse_attend(ctypes.byref(dims), _dtype_code(q), _p(q), _p(k), k_row,
                                     v_ptr, v_row, _p(_i32(idx)), _p(vis_lo), _p(vis_hi), _p(out),
@@ -264,10 +295,13 @@ def pool_keys(k, gate, pad, kpool: int, out=None, n_pools=None):
     B, L, d = k.shape
     if gate.shape != k.shape or gate.dtype != k.dtype:
         raise ValueError("pool_keys: gate must match k")
+    _shape(pad, (B,), "pool_keys: pad", torch.int32)
     if out is None:
         out = torch.empty((B, L // kpool, d), dtype=k.dtype, device=k.device)
     if n_pools is None:
         n_pools = torch.empty(B, dtype=torch.int32, device=k.device)
+    _shape(out, (B, L // kpool, d), "pool_keys: out", k.dtype)
+    _shape(n_pools, (B,), "pool_keys: n_pools", torch.int32)
     dims = _PoolDims(B, L, 0, kpool, d, 1, 1)
     _check(load().dsa_pool_keys(ctypes.byref(dims), _dtype_code(k), _p(k), _p(gate),
                                 _p(_i32(pad)), _p(out), _p(n_pools), _stream()))
@@ -278,12 +312,18 @@ def pool_select(scores, pad, q_pos, kpool: int, select_k: int, out_width: int, o
                 out_pools=None, want_pools: bool = False):
     """topk_pools + expand_selection.  scores: [B, n_q, seq//kpool] f32."""
     _dev(scores, pad, q_pos, out_tok, out_pools)
+    if scores.dtype != torch.float32:
+        raise TypeError(f"pool_select: scores must be float32, got {scores.dtype}")
     B, n_q, n_pool_cols = scores.shape
     seq = n_pool_cols * kpool
+    _shape(pad, (B,), "pool_select: pad", torch.int32)
+    _shape(q_pos, (B, n_q), "pool_select: q_pos", torch.int32)
     if out_tok is None:
         out_tok = torch.empty((B, n_q, out_width), dtype=torch.int32, device=scores.device)
     if out_pools is None and want_pools:
         out_pools = torch.empty((B, n_q, select_k), dtype=torch.int32, device=scores.device)
+    _shape(out_tok, (B, n_q, out_width), "pool_select: out_tok", torch.int32)
+    _shape(out_pools, (B, n_q, select_k), "pool_select: out_pools", torch.int32)
     dims = _PoolDims(B, seq, n_q, kpool, 0, select_k, out_width)
     _check(load().dsa_pool_select(ctypes.byref(dims), _p(scores), _p(_i32(pad)),
                                   _p(_i32(q_pos)), _p(out_tok), _p(out_pools), None, 0,

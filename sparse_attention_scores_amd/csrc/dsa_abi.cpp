@@ -135,22 +135,37 @@ size_t dsa_topk_workspace_size(int32_t rows, int32_t n_cols, int32_t top_k)
     return dsa::topk_workspace_bytes(rows, n_cols, top_k);
 }
 
+// Argument checks shared by both top-k entry points: DSA_OK to go on, 1 when
+// there is nothing to do, else the error.
+static int topk_args(const char *fn, const float *scores, int32_t rows, int32_t n_cols,
+                     int64_t row_stride, const int32_t *vis_lo, const int32_t *vis_hi,
+                     int32_t top_k, const int32_t *out_idx)
+{
+    if (rows < 0 || n_cols < 0)
+        return fail(DSA_ERR_ARG, "%s: negative size", fn);
+    if (top_k < 1 || top_k > 2048)
+        return fail(top_k < 1 ? DSA_ERR_ARG : DSA_ERR_UNSUPPORTED,
+                    "%s: top_k must be in 1..2048 (got %d)", fn, top_k);
+    if (rows == 0)
+        return 1;
+    if (!out_idx || !vis_lo || !vis_hi || (n_cols > 0 && !scores))
+        return fail(DSA_ERR_ARG, "%s: null pointer", fn);
+    if (row_stride < n_cols)
+        return fail(DSA_ERR_ARG, "%s: row_stride %lld < n_cols %d", fn, (long long)row_stride,
+                    n_cols);
+    return DSA_OK;
+}
+
 int dsa_topk(const float *scores, int32_t rows, int32_t n_cols, int64_t row_stride,
              const int32_t *vis_lo, const int32_t *vis_hi, int32_t top_k, int32_t *out_idx,
              void *workspace, size_t workspace_bytes, void *stream)
 {
-    if (rows < 0 || n_cols < 0)
-        return fail(DSA_ERR_ARG, "dsa_topk: negative size");
-    if (top_k < 1 || top_k > 2048)
-        return fail(top_k < 1 ? DSA_ERR_ARG : DSA_ERR_UNSUPPORTED,
-                    "dsa_topk: top_k must be in 1..2048 (got %d)", top_k);
-    if (rows == 0)
+    const int rc =
+        topk_args("dsa_topk", scores, rows, n_cols, row_stride, vis_lo, vis_hi, top_k, out_idx);
+    if (rc == 1)
         return ok();
-    if (!out_idx || !vis_lo || !vis_hi || (n_cols > 0 && !scores))
-        return fail(DSA_ERR_ARG, "dsa_topk: null pointer");
-    if (row_stride < n_cols)
-        return fail(DSA_ERR_ARG, "dsa_topk: row_stride %lld < n_cols %d", (long long)row_stride,
-                    n_cols);
+    if (rc != DSA_OK)
+        return rc;
     const size_t need = dsa_topk_workspace_size(rows, n_cols, top_k);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(DSA_ERR_WORKSPACE, "dsa_topk: workspace of %zu bytes needed, %zu given", need,

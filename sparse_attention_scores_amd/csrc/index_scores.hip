@@ -640,16 +640,20 @@ __global__ void index_scores_f32_kernel(const float *__restrict__ q, const float
         scores[e] = -FLT_MAX;
         return;
     }
+    // f64 sums: a product of two f32 values is exact in f64, so the score
+    // carries one f32 rounding at the end and the f64 sums' error (a few
+    // 2^-53 of sum_h |w| |scale| sum_c |q k|) on top -- relative accuracy far
+    // below 1e-5 wherever the sum does not cancel almost completely
     const float *kr = k + (b * n_k + s) * D;
-    float total_s = 0.f;
+    double total_s = 0.0;
     for (int h = 0; h < H; ++h) {
         const float *qr = q + (row * H + h) * D;
-        float dot = 0.f;
+        double dot = 0.0;
         for (int c = 0; c < D; ++c)
-            dot = fmaf(qr[c], kr[c], dot);
-        total_s += w[row * H + h] * fmaxf(scale * dot, 0.f);
+            dot = fma((double)qr[c], (double)kr[c], dot);
+        total_s += (double)w[row * H + h] * fmax((double)scale * dot, 0.0);
     }
-    scores[e] = total_s;
+    scores[e] = (float)total_s;
 }
 
 template <int D, int MT, int QPW, int WQ, bool FP8>

@@ -1,10 +1,16 @@
 """Shared checks for the GPU-vs-oracle parity tests (not collected).
 
 Criteria (stated per stage):
-  * index scores: |S_gpu - S_ref| <= rtol * A elementwise, where
-    A = sum_h |w| |scale| sum_c |q_c k_c| bounds the rounding error of any
-    summation order; rtol = 1e-3 for bf16 inputs, 1e-5 for f32 inputs.
-    Invisible scores must be exactly -FLT_MAX on both sides.
+  * index scores: |S_gpu - S_ref| <= rtol * |S_ref| on every visible
+    element (rtol = 1e-3 for bf16 inputs, 1e-5 for f32 inputs), except where
+    S_ref is cancellation-dominated.  That is where the kernel's own
+    worst-case rounding bound gamma * A exceeds rtol * |S_ref|, with
+    A = sum_h |w| |scale| sum_c |q_c k_c| and gamma = (d + heads + 4) * unit:
+    unit = 2^-23 for the f32 sums of exact bf16 products, 2^-52 for the f64
+    sums of the f32-input kernel (any summation order, any rounding with a
+    relative error of at most unit per operation).  There |S_gpu - S_ref| <=
+    gamma * A is required instead, and the count of such elements is
+    reported.  Invisible scores must be exactly -FLT_MAX on both sides.
   * top-k / pool select: bit-exact against the oracle applied to the GPU's
     own scores.
   * attention (given the oracle's selection): per query row over all heads x
@@ -29,7 +35,12 @@ def note(msg: str):
     sys.stdout.flush()
 
 
-def check_scores(S_gpu: np.ndarray, S_ref: np.ndarray, A: np.ndarray, rtol: float, what=""):
+def check_scores(S_gpu: np.ndarray, S_ref: np.ndarray, A: np.ndarray, rtol: float, what="",
+                 d: int = 128, heads: int = 64):
+    """Relative check of the index scores (see the module docstring).
+
+    Returns (worst error / allowed error, cancellation-dominated count,
+    visible count)."""
     S_gpu = np.asarray(S_gpu, np.float64)
     S_ref = np.asarray(S_ref, np.float64)
     inv_ref = S_ref == -FLT_MAX
@@ -37,12 +48,26 @@ def check_scores(S_gpu: np.ndarray, S_ref: np.ndarray, A: np.ndarray, rtol: floa
     assert np.array_equal(inv_ref, inv_gpu), f"{what}: visibility pattern differs"
     vis = ~inv_ref
     if not vis.any():
-        return 0.0
+        return 0.0, 0, 0
+    unit = 2.0 ** -52 if rtol <= 1e-5 else 2.0 ** -23
+    gamma = (d + heads + 4) * unit
     err = np.abs(S_gpu[vis] - S_ref[vis])
-    bound = rtol * A[vis] + 1e-30
-    worst = float((err / bound).max())
-    assert worst <= 1.0, f"{what}: score error {worst:.3g} x the bound (rtol {rtol})"
-    return worst
+    rel_bound = rtol * np.abs(S_ref[vis])
+    rnd_bound = gamma * np.asarray(A, np.float64)[vis]
+    dominated = rnd_bound > rel_bound
+    bound = np.where(dominated, rnd_bound, rel_bound)
+    ok = err <= bound
+    if not ok.all():
+        i = int(np.argmax(~ok))
+        raise AssertionError(
+            f"{what}: {int((~ok).sum())} of {err.size} visible scores out of tolerance; first: "
+            f"|d| {err[i]:.3g} vs {'gamma*A' if dominated[i] else 'rtol*|S|'} {bound[i]:.3g} "
+            f"(S_ref {S_ref[vis][i]:.6g}, rtol {rtol}, gamma {gamma:.3g})")
+    ratio = np.where(bound > 0, err / np.where(bound > 0, bound, 1.0), 0.0)
+    n_dom = int(dominated.sum())
+    note(f"  {what}: worst {float(ratio.max()):.3g} of the allowed error; "
+         f"{n_dom} of {err.size} visible scores cancellation-dominated")
+    return float(ratio.max()), n_dom, int(err.size)
 
 
 def check_attend(out_gpu, out_ref, lse_gpu, lse_ref, bf16: bool, what=""):

@@ -14,6 +14,10 @@ def _declared():
 
 
 def _lib_path():
+    # torch first: libdsa then binds to torch's HIP runtime instead of mapping
+    # a second one (the binding refuses a process with two)
+    import torch  # noqa: F401
+
     from sparse_attention_scores_amd import build
     if not os.path.exists(build.LIB):
         build.build()
@@ -48,3 +52,67 @@ def test_host_side_validation_without_gpu():
     assert lib.dsa_index_scores(None, None, 0, None, 0, None, None, None, None, None, None) == -1
     assert lib.dsa_topk_workspace_size(8, 131072, 2048) > 0
     assert lib.dsa_topk_workspace_size(8, 8192, 2048) == 0
+
+
+def test_workspace_errors_without_gpu():
+    """A missing or short workspace is DSA_ERR_WORKSPACE, found on the host
+    before any launch (the pointers below are never dereferenced: every call
+    here fails validation)."""
+    from sparse_attention_scores_amd import binding
+    lib = binding.load()
+    fake = ctypes.c_void_p(0x1000)
+    # long rows: the chunked top-k keeps its chunk winners in the workspace
+    need = lib.dsa_topk_workspace_size(1, 20000, 2048)
+    assert need == 2 * 2048 * 8
+    assert lib.dsa_topk(fake, 1, 20000, 20000, fake, fake, 2048, fake, None, 0, None) == -4
+    assert b"workspace" in lib.dsa_last_error()
+    assert lib.dsa_topk(fake, 1, 20000, 20000, fake, fake, 2048, fake, fake, need - 1,
+                        None) == -4
+    # few decode rows: the gather kernel's split-K partials
+    dims = binding._AttnDims(2, 1, 8192, 64, 576, 512, 1, 2048, 576 ** -0.5)
+    need = lib.dsa_sparse_attend_workspace_size(ctypes.byref(dims))
+    assert need > 0
+    for ws, nb in ((None, 0), (fake, need - 1)):
+        rc = lib.dsa_sparse_attend(ctypes.byref(dims), 1, fake, fake, 576, fake, 576, fake,
+                                   None, None, fake, None, ws, nb, None)
+        assert rc == -4, rc
+    # the per-head kernel's selection bitmap
+    dims = binding._AttnDims(1, 300, 300, 8, 192, 256, 8, 40, 192 ** -0.5)
+    need = lib.dsa_sparse_attend_workspace_size(ctypes.byref(dims))
+    assert need == 300 * ((300 + 31) // 32) * 4
+    rc = lib.dsa_sparse_attend(ctypes.byref(dims), 1, fake, fake, 8 * 192, fake, 8 * 256, fake,
+                               None, None, fake, None, fake, need - 4, None)
+    assert rc == -4, rc
+
+
+def test_binding_rejects_short_or_mistyped_tensors():
+    """The binding checks shapes and dtypes before the ABI call, so a short
+    range tensor or a bf16 score tensor is an error, not a device fault
+    (CPU tensors reach the checks after the device check only, so these use
+    a stand-in that passes it)."""
+    import pytest
+    import torch
+
+    from sparse_attention_scores_amd import binding
+
+    class Dev(torch.Tensor):
+        @property
+        def is_cuda(self):
+            return True
+
+    def dev(t):
+        return t.as_subclass(Dev)
+
+    S = dev(torch.zeros(2, 10, dtype=torch.bfloat16))
+    lo = dev(torch.zeros(2, dtype=torch.int32))
+    with pytest.raises(TypeError):
+        binding.topk(S, lo, lo, 4)
+    S = dev(torch.zeros(2, 10))
+    short = dev(torch.zeros(1, dtype=torch.int32))
+    with pytest.raises(ValueError):
+        binding.topk(S, short, lo, 4)
+    with pytest.raises(TypeError):
+        binding.pool_select(dev(torch.zeros(1, 4, 2, dtype=torch.bfloat16)), lo, lo, 4, 1, 8)
+    with pytest.raises(ValueError):
+        binding.pool_select(dev(torch.zeros(2, 4, 2)), lo, short, 4, 1, 8)
+

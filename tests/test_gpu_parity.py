@@ -386,8 +386,10 @@ def test_absorbed_attend_split_partials_large_values(dsa):
 
 
 def test_absorbed_attend_long_context_distinct(dsa):
-    """n_k past the duplicate-check bitmap (300000 keys): the set bitmap path
-    with distinct keys, INVALID entries and a visibility window."""
+    """n_k past the gather kernel's limit of 262144 keys (300000 keys): the
+    absorbed layout then runs attend_plain_kernel, here with distinct keys,
+    INVALID entries and a visibility window.  The gather kernel's own
+    set-bitmap path at n_k = 262144 is covered in test_gpu_paths.py."""
     note("absorbed attend: n_k = 300000")
     B, Tk = 1, 300000
     inp = W.make(2, device="cuda", B=B, Tk=Tk)
