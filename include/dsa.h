@@ -7,10 +7,12 @@
  * Conventions shared by every entry point:
  *  - Tensor pointers are DEVICE pointers owned by the caller (for instance
  *    torch.Tensor.data_ptr()).  Tensors are dense, row-major, with the shape
- *    given next to each argument.  The library never allocates, frees or
- *    keeps device memory; scratch memory comes from a caller-provided
- *    `workspace` of at least the size the matching *_workspace_size() call
- *    returns (NULL is fine when that size is 0).
+ *    given next to each argument.  The library never allocates or frees
+ *    device memory; scratch memory comes from a caller-provided `workspace`
+ *    of at least the size the matching *_workspace_size() call returns (NULL
+ *    is fine when that size is 0).  The one exception is dsa_topk_noalloc,
+ *    whose scratch is a fixed array the library's code object holds on each
+ *    GPU.
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *    Every call is asynchronous on that stream: it only validates arguments
  *    on the host and enqueues kernels.  There is no device synchronisation
@@ -151,6 +153,33 @@ int dsa_topk(const float *scores, int32_t rows, int32_t n_cols,
              int64_t row_stride, const int32_t *vis_lo, const int32_t *vis_hi,
              int32_t top_k, int32_t *out_idx, void *workspace,
              size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Top-k that allocates nothing, for callers that cannot allocate device
+ * memory: code under HIP graph capture, serving loops and harnesses that
+ * forbid hipMalloc.
+ *
+ * Arguments and results are those of dsa_topk without the workspace.  Rows
+ * longer than 16384 keys keep their chunk winners in a scratch array the
+ * library holds in each GPU's memory until the process ends
+ * (DSA_TOPK_NOALLOC_SCRATCH_BYTES per GPU); its device address is looked up
+ * once per device, on the first call made with that device current.
+ * Limit: dsa_topk_workspace_size(rows, n_cols, top_k) <= 16 MiB (for
+ * instance 8 rows of 131072 keys at top_k 2048 need 1 MiB); a larger call
+ * returns DSA_ERR_UNSUPPORTED and enqueues nothing.  The call itself
+ * allocates nothing (no hipMalloc, no library allocation).
+ * Every call on one GPU shares that GPU's array, which keeps the last
+ * call's contents: calls ordered on one stream are safe, but two calls
+ * whose kernels may overlap on one GPU (different streams without ordering)
+ * race and give wrong results.  `stream` must belong to the current device
+ * (DSA_ERR_ARG otherwise).
+ * ------------------------------------------------------------------------ */
+#define DSA_TOPK_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+int dsa_topk_noalloc(const float *scores, int32_t rows, int32_t n_cols,
+                     int64_t row_stride, const int32_t *vis_lo,
+                     const int32_t *vis_hi, int32_t top_k, int32_t *out_idx,
+                     void *stream);
 
 /* ------------------------------------------------------------------------
  * Sparse attention over each query's selected keys.

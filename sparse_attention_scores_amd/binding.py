@@ -51,7 +51,8 @@ class _PoolDims(ctypes.Structure):
 _lock = threading.Lock()
 _lib = None
 EXPORTS = ("dsa_last_error", "dsa_version", "dsa_visibility_ranges", "dsa_index_scores",
-           "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_attend_workspace_size",
+           "dsa_topk_workspace_size", "dsa_topk", "dsa_topk_noalloc",
+           "dsa_sparse_attend_workspace_size",
            "dsa_sparse_attend", "dsa_pool_keys", "dsa_pool_select_workspace_size",
            "dsa_pool_select")
 
@@ -92,6 +93,7 @@ def load():
         lib.dsa_topk_workspace_size.argtypes = [I32, I32, I32]
         lib.dsa_topk_workspace_size.restype = SZ
         lib.dsa_topk.argtypes = [P, I32, I32, I64, P, P, I32, P, P, SZ, P]
+        lib.dsa_topk_noalloc.argtypes = [P, I32, I32, I64, P, P, I32, P, P]
         lib.dsa_sparse_attend_workspace_size.argtypes = [P]
         lib.dsa_sparse_attend_workspace_size.restype = SZ
         lib.dsa_sparse_attend.argtypes = [P, ctypes.c_int, P, P, I64, P, I64, P, P, P, P, P, P,
@@ -235,6 +237,24 @@ def topk(scores, vis_lo, vis_hi, top_k: int, out=None, workspace=None):
     ws, wsb = _workspace(topk_workspace_size(rows, n_cols, top_k), workspace, scores.device)
     _check(load().dsa_topk(_p(scores), rows, n_cols, n_cols, _p(_i32(vis_lo)), _p(_i32(vis_hi)),
                            top_k, _p(out), _p(ws), wsb, _stream()))
+    return out
+
+
+def topk_noalloc(scores, vis_lo, vis_hi, top_k: int, out):
+    """Top-k into a caller-given `out`, with no workspace: the library's own
+    per-GPU scratch holds the chunk winners of long rows (nothing is
+    allocated, here or in the library)."""
+    _dev(scores, vis_lo, vis_hi, out)
+    if scores.dtype != torch.float32:
+        raise TypeError(f"topk_noalloc: scores must be float32, got {scores.dtype}")
+    n_cols = scores.shape[-1]
+    rows = math.prod(scores.shape[:-1])
+    if vis_lo.numel() != rows or vis_hi.numel() != rows:
+        raise ValueError(f"topk_noalloc: vis_lo/vis_hi need {rows} elements")
+    if out.numel() != rows * top_k or out.dtype != torch.int32:
+        raise ValueError(f"topk_noalloc: out must be int32 with {rows} x {top_k} elements")
+    _check(load().dsa_topk_noalloc(_p(scores), rows, n_cols, n_cols, _p(_i32(vis_lo)),
+                                   _p(_i32(vis_hi)), top_k, _p(out), _stream()))
     return out
 
 

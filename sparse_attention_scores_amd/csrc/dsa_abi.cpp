@@ -174,6 +174,40 @@ int dsa_topk(const float *scores, int32_t rows, int32_t n_cols, int64_t row_stri
     return hip_status(dsa::launch_topk(a, as_stream(stream)), "dsa_topk");
 }
 
+int dsa_topk_noalloc(const float *scores, int32_t rows, int32_t n_cols, int64_t row_stride,
+                     const int32_t *vis_lo, const int32_t *vis_hi, int32_t top_k,
+                     int32_t *out_idx, void *stream)
+{
+    const int rc = topk_args("dsa_topk_noalloc", scores, rows, n_cols, row_stride, vis_lo,
+                             vis_hi, top_k, out_idx);
+    if (rc == 1)
+        return ok();
+    if (rc != DSA_OK)
+        return rc;
+    const size_t need = dsa_topk_workspace_size(rows, n_cols, top_k);
+    static_assert(DSA_TOPK_NOALLOC_SCRATCH_BYTES == dsa::kTopkScratchBytes,
+                  "the header states the scratch size");
+    if (need > dsa::kTopkScratchBytes)
+        return fail(DSA_ERR_UNSUPPORTED,
+                    "dsa_topk_noalloc: these rows need %zu bytes of scratch, more than the "
+                    "library's %zu (use dsa_topk with a workspace)",
+                    need, dsa::kTopkScratchBytes);
+    void *ws = nullptr;
+    if (need > 0) {
+        int dev = -1;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess)
+            return hip_status(e, "dsa_topk_noalloc");
+        if (hipGetStreamDeviceId(as_stream(stream)) != dev)
+            return fail(DSA_ERR_ARG, "dsa_topk_noalloc: the stream is not on the current device");
+        e = dsa::topk_scratch(&ws);
+        if (e != hipSuccess)
+            return hip_status(e, "dsa_topk_noalloc: scratch lookup");
+    }
+    dsa::TopkArgs a{scores, rows, n_cols, row_stride, vis_lo, vis_hi, top_k, out_idx, ws};
+    return hip_status(dsa::launch_topk(a, as_stream(stream)), "dsa_topk_noalloc");
+}
+
 static int attend_args(const dsa_attn_dims *d, int dtype, dsa::AttendArgs &a)
 {
     if (!d)

@@ -34,6 +34,10 @@ struct TopkArgs {
 };
 size_t topk_workspace_bytes(int rows, int n_cols, int k);
 hipError_t launch_topk(const TopkArgs &a, hipStream_t st);
+// the allocation-free top-k's scratch: its size, and its device address on
+// the current device (looked up once per device)
+constexpr size_t kTopkScratchBytes = (size_t)16 << 20;
+hipError_t topk_scratch(void **ptr);
 
 struct AttendArgs {
     int batch, n_q, n_k, n_heads, kd, vd, kv_heads, n_sel;

@@ -22,6 +22,7 @@
 //    several blocks per row when the candidates fit one block's cache.
 #include "dsa_internal.hpp"
 #include <algorithm>
+#include <mutex>
 #include "topk_device.hpp"
 
 namespace dsa {
@@ -668,6 +669,44 @@ int topk_seg_parts(int rows, int k, int max_parts)
     parts = std::min(parts, max_parts);
     parts = std::min(parts, k / 64);
     return std::max(parts, 1);
+}
+
+// Scratch of the allocation-free top-k entry point: the chunk winners of
+// rows longer than kCapLarge keys, in memory the library holds on each GPU
+// for the life of the process.  Host code must not pass `scratch` itself to
+// a kernel (in host code the name stands for a host-side shadow, not the
+// device address): topk_scratch() looks the device address up once per
+// device, with that device current, and every launch takes that pointer.
+// The chunk kernel writes every slot it owns (zero keys pad short chunks),
+// so nothing in it has to start at zero.
+static __device__ __align__(256) unsigned char scratch[kTopkScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+} // namespace
+
+hipError_t topk_scratch(void **ptr)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        if (p == nullptr)
+            return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_topk(const TopkArgs &a, hipStream_t st)

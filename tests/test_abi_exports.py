@@ -116,3 +116,16 @@ def test_binding_rejects_short_or_mistyped_tensors():
     with pytest.raises(ValueError):
         binding.pool_select(dev(torch.zeros(2, 4, 2)), lo, short, 4, 1, 8)
 
+
+def test_noalloc_topk_limit_without_gpu():
+    """The allocation-free top-k refuses rows whose chunk winners would not
+    fit its fixed scratch, before anything else (pointers never used)."""
+    from sparse_attention_scores_amd import binding
+    lib = binding.load()
+    fake = ctypes.c_void_p(0x1000)
+    # 2000 rows of 20000 keys at k 2048 need 2000 * 2 * 2048 * 8 bytes > 16 MiB
+    assert lib.dsa_topk_workspace_size(2000, 20000, 2048) > (16 << 20)
+    rc = lib.dsa_topk_noalloc(fake, 2000, 20000, 20000, fake, fake, 2048, fake, None)
+    assert rc == -2
+    assert b"scratch" in lib.dsa_last_error()
+    assert lib.dsa_topk_noalloc(fake, 1, 10, 10, fake, fake, 0, fake, None) == -1
