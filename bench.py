@@ -1,18 +1,37 @@
 """Benchmark of the DSA layer step on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--config 2] [--no-cpu]
+    python bench.py [--steps K] [--warmup W] [--config 5] [--only] [--no-cpu]
 
 One step = the whole hot path over one batch of synthetic inputs already
-resident in HBM: lightning-indexer scores -> per-query top-k -> sparse MLA
-attention (for the pooled configuration: pool keys -> pooled scores -> pool
-select -> per-head attention).  Prints one JSON line with the throughput in
-query tokens/s, the roofline of the dominant kernel (timed live with HIP
-events on the stream the kernels run on), and the CPU oracle timed on a
-bounded sample of the same workload.
+resident in HBM.  The headline workload is the pooled NoPE configuration
+(4 x 16384 tokens, every position a query): pool keys -> pooled index scores
+-> pool select -> per-head attention over the selected tokens.  The other
+workloads (decode 32 x 8192, prefill 4096, long decode 8 x 131072 with fp8
+indexer keys: index scores -> top-k -> absorbed sparse MLA attention) follow
+in "configs".
+
+Prints one JSON line:
+  * value: query tokens/s of the headline workload (wall clock over K steps);
+  * roofline: the dominant stage's bound, its achieved rate from HIP events
+    on the stream the kernels run on, the published MI355X peak and the
+    rate this GPU reaches in a plain copy / an MFMA-only loop
+    (peaks_measured);
+  * stages: every stage's average launch time and algorithmic rates;
+  * configs: the same for the other workloads.  On the decode workloads
+    the per-step footprint (~150 MB) fits the 256 MB last-level cache, so
+    their inputs rotate over four seeded sets (more than 512 MB touched)
+    and the cold figures are reported beside the repeated-input (hot) ones;
+  * cpu_baseline: the CPU oracle on a stated sample of the headline
+    workload, fed the same input bytes as the GPU.
+
+Algorithmic work counts only what the method itself must move or compute:
+visible pairs, selected keys, the inputs once and the outputs once, not the
+dense work a kernel executes around them (algorithmic_work, pooled_work).
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -77,29 +96,96 @@ def measured_traffic(cfg, stage):
     return (round(tot) if hit else None), os.path.relpath(path, ROOT)
 
 
+PROBE_LIB = os.path.join(ROOT, "sparse_attention_scores_amd", "probe", "libdsa_probe.so")
+
+
+def _probe():
+    if not os.path.exists(PROBE_LIB):
+        raise RuntimeError(f"{PROBE_LIB} is not built: run `python -m "
+                           "sparse_attention_scores_amd.build`")
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                               ctypes.c_void_p]
+    lib.probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    return lib
+
+
+def _cur_stream(torch):
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+COPY_BLOCKS = 256 * 16
+
+
 def copy_probe(mib):
-    """A plain streaming kernel of known traffic (y = -x over float32, `mib`
-    MiB each way): its counter readings calibrate FETCH_SIZE / WRITE_SIZE."""
+    """The calibration copy kernel over `mib` MiB each way (its counter
+    readings calibrate FETCH_SIZE / WRITE_SIZE: it moves exactly that many
+    bytes in and out)."""
     import torch
-    n = mib * (1 << 20) // 4
-    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    lib = _probe()
+    nbytes = mib * (1 << 20)
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
     y = torch.empty_like(x)
     for _ in range(3):
-        torch.neg(x, out=y)
+        assert lib.probe_copy(x.data_ptr(), y.data_ptr(), nbytes, COPY_BLOCKS,
+                              _cur_stream(torch)) == 0
     torch.cuda.synchronize()
-    return n * 4
+    return nbytes
+
+
+def measure_peaks():
+    """What this GPU reaches in a plain 1 GiB streaming copy (bytes read +
+    written / time) and in a loop of bf16 MFMAs with no memory traffic, each
+    timed with HIP events on the current stream."""
+    import torch
+    lib = _probe()
+    st = _cur_stream(torch)
+    nbytes = 1 << 30
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    t_copy = timed(lambda: lib.probe_copy(x.data_ptr(), y.data_ptr(), nbytes, COPY_BLOCKS, st), 10)
+    t_torch = timed(lambda: y.copy_(x), 10)   # torch's own copy kernel, as a cross-check
+    del x, y
+    blocks, iters = 256 * 8, 4000
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    t_mfma = timed(lambda: lib.probe_mfma_bf16(blocks, iters, out.data_ptr(), st), 5)
+    flops = blocks * 4 * iters * 4 * 32 * 32 * 16 * 2
+    return {"hbm_copy_GBps": round(2 * nbytes / min(t_copy, t_torch) / 1e9, 1),
+            "hbm_copy_probe_GBps": round(2 * nbytes / t_copy / 1e9, 1),
+            "hbm_copy_torch_GBps": round(2 * nbytes / t_torch / 1e9, 1),
+            "mfma_bf16_TFLOPs": round(flops / t_mfma / 1e12, 1),
+            "how": "copy: 1 GiB read + 1 GiB written, the faster of a 16-byte-per-lane "
+                   "span-per-workgroup kernel and torch's copy; "
+                   "mfma: 2048 workgroups x 4 waves, each 4 independent chains of "
+                   "v_mfma_f32_32x32x16_bf16, no memory traffic"}
 
 
 def _parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=5, choices=[1, 2, 3, 4, 5],
+                    help="headline workload (default: the pooled NoPE workload, the largest)")
+    ap.add_argument("--only", action="store_true",
+                    help="time the headline workload only (no configs object, no peaks)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-rows", type=int, default=64, help="query rows in the oracle sample")
+    ap.add_argument("--cpu-rows", type=int, default=48, help="query rows in the oracle sample")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
-                    help="also run a plain copy kernel of MIB MiB (counter calibration)")
+                    help="also run the calibration copy kernel over MIB MiB (counter "
+                         "calibration)")
     ap.add_argument("--graph", action="store_true",
                     help="replay one captured HIP graph per timed step instead of launching "
                          "the step's kernels one by one")
@@ -273,36 +359,233 @@ def capture_step(torch, run_once):
     return g
 
 
-def cpu_baseline(cfg, rows_wanted, min_seconds=10.0, max_passes=20):
-    """The oracle (as it stands) on a bounded sample of the same workload:
-    up to `rows_wanted` query rows through index scores -> top-k ->
-    attention, repeated until about `min_seconds` of CPU work."""
+# Seeded input sets per workload: the decode workloads rotate over four so
+# that a step's inputs are not left in the last-level cache by the previous
+# step (about 150 MB touched per step against 256 MB of cache).
+ROTATE_SETS = {2: 4, 4: 4}
+
+
+def executed_masked_flops(inp, qblock=32, tile=32):
+    """Flops the per-head masked-tile kernel executes: every (query, key)
+    pair of the key tiles each wave's 32 queries compute (from the block's
+    first visible tile to the wave's last query; a wave skips the tiles in
+    which none of its queries selects a key), whether selected or not."""
+    B, L, H, kd, vd = inp["B"], inp["L"], inp["H"], inp["kd"], inp["vd"]
+    pads = [int(p) for p in inp["pad"].cpu().tolist()]
+    pairs = 0
+    for p in pads:
+        for q0 in range(0, L, qblock):
+            q1 = min(q0 + qblock, L)
+            if q1 <= p:
+                continue
+            lo, hi = p, q1          # keys [pad, last query + 1)
+            t0, t1 = lo // tile, (hi + tile - 1) // tile
+            pairs += (q1 - q0) * (t1 - t0) * tile
+    return 2 * H * (kd + vd) * pairs
+
+
+def _rates(by, fl, t):
+    return {"alg_GBps": round(by / t / 1e9, 1), "alg_TFLOPs": round(fl / t / 1e12, 2)}
+
+
+def stage_bound(cfg, stage):
+    """The roofline that bounds each stage of each workload: the decode
+    workloads and the selection stages stream memory; the prefill and
+    pooled indexers and attends are contractions."""
+    if stage in ("topk", "pool_select", "pool_keys") or cfg in (1, 2, 4):
+        return "hbm"
+    return "mfma"
+
+
+def run_workload(cfg, dsa, W, K, warmup, graph=False):
+    """Times one workload: whole steps by wall clock, then each stage by HIP
+    events; on the rotating workloads also with the inputs cycling over
+    several seeded sets (cold) besides one set repeated (hot)."""
+    import torch
+    n_sets = ROTATE_SETS.get(cfg, 1)
+    sets = []
+    for i in range(n_sets):
+        inp = W.make(cfg, device="cuda", seed=1000 + cfg + 7919 * i)
+        sets.append(PooledStep(dsa, inp) if cfg == 5 else Step(dsa, inp))
+    names = type(sets[0]).stages
+
+    def run_once(st):
+        for n in names:
+            getattr(st, n)()
+
+    for _ in range(warmup):
+        for st in sets:
+            run_once(st)
+    torch.cuda.synchronize()
+    g = None
+    if graph:
+        g = capture_step(torch, lambda: run_once(sets[0]))
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+    print(f"[bench] config {cfg}: warmup done; timing {K} steps "
+          f"({'graph replay' if g else 'eager'}, {n_sets} input set(s))", file=sys.stderr,
+          flush=True)
+
+    def wall(rotate):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(K):
+            if g is not None:
+                g.replay()
+            else:
+                run_once(sets[s % n_sets] if rotate else sets[0])
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    def stage_time(name, rotate):
+        # K launches of the stage alone between two HIP events on the stream
+        # the kernels run on (torch's current stream, which the binding uses)
+        fns = [getattr(st, name) for st in (sets if rotate else sets[:1])]
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for s in range(K):
+            fns[s % len(fns)]()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / K
+
+    inp = sets[0].inp
+    if cfg == 5:
+        work, tokens = pooled_work(inp)
+    else:
+        work, tokens = algorithmic_work(inp), inp["B"] * inp["Tq"]
+    res = {"workload": WORKLOAD_TEXT[cfg], "config_id": cfg, "query_tokens_per_step": tokens,
+           "seed": inp["seed"], "launch": "hip graph per step" if g else "eager"}
+    t_hot = wall(False)
+    res["value"] = round(tokens * K / t_hot, 1)
+    res["ms_per_step"] = round(t_hot * 1e3 / K, 5)
+    if n_sets > 1:
+        t_cold = wall(True)
+        res["value_cold"] = round(tokens * K / t_cold, 1)
+        res["ms_per_step_cold"] = round(t_cold * 1e3 / K, 5)
+        res["input_sets"] = n_sets
+    stages = {}
+    for name in names:
+        by, fl = work[name]
+        ms = stage_time(name, False)
+        st = {"ms": round(ms, 5), "bound": stage_bound(cfg, name), **_rates(by, fl, ms * 1e-3)}
+        if n_sets > 1:
+            ms_c = stage_time(name, True)
+            st["ms_cold"] = round(ms_c, 5)
+            st.update({k + "_cold": v for k, v in _rates(by, fl, ms_c * 1e-3).items()})
+        stages[name] = st
+    res["stages"] = stages
+    res["_work"] = work
+    res["_inp"] = inp
+    res["_sets"] = sets
+    return res
+
+
+def roofline_of(cfg, res, peaks):
+    """The dominant stage's roofline: its bound, achieved algorithmic rate
+    (cold inputs where they rotate), the published peak, the measured
+    peak and the recorded counter traffic."""
+    stages = res["stages"]
+    dom = max(stages, key=lambda n: stages[n].get("ms_cold", stages[n]["ms"]))
+    st = stages[dom]
+    by, fl = res["_work"][dom]
+    ms = st.get("ms_cold", st["ms"])
+    t = ms * 1e-3
+    if st["bound"] == "hbm":
+        ach = by / t / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4)}
+        if "ms_cold" in st:
+            roof["frac_hot"] = round(by / (st["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+        if peaks:
+            roof["peak_measured"] = peaks["hbm_copy_GBps"]
+            roof["frac_of_measured"] = round(ach / peaks["hbm_copy_GBps"], 4)
+    else:
+        ach = fl / t / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFS,
+                "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFS, 4)}
+        if peaks:
+            roof["peak_measured"] = peaks["mfma_bf16_TFLOPs"]
+            roof["frac_of_measured"] = round(ach / peaks["mfma_bf16_TFLOPs"], 4)
+        if cfg == 5 and dom == "attend":
+            ex = executed_masked_flops(res["_inp"])
+            roof["executed_flops_per_launch"] = ex
+            roof["executed_TFLOPs"] = round(ex / t / 1e12, 2)
+            roof["frac_executed"] = round(ex / t / 1e12 / MFMA_BF16_PEAK_TFS, 4)
+    traffic, tsrc = measured_traffic(cfg, dom)
+    roof["traffic"] = traffic
+    roof["traffic_record"] = tsrc
+    roof["kernel"] = dom
+    roof["kernels"] = list(STAGE_KERNELS[dom])
+    roof["ms_per_launch"] = round(ms, 5)
+    roof["alg_bytes_per_launch"] = by
+    roof["alg_flops_per_launch"] = fl
+    return roof
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _host(t):
+    return t.detach().cpu()
+
+
+def cpu_baseline(res, rows_wanted, min_seconds=10.0, max_passes=50):
+    """The oracle (as it stands) on a bounded sample of the timed workload,
+    fed the GPU's own input bytes copied to the host: up to `rows_wanted`
+    query rows through the whole step, repeated to about `min_seconds`."""
     import numpy as np
 
     import oracle
-    from sparse_attention_scores_amd import workloads as W
-    inp = W.make(cfg, device="cpu")
+    cfg = res["config_id"]
+    inp = res["_inp"]
     B, Tq = inp["B"], inp["Tq"]
-    rows = np.linspace(0, B * Tq - 1, num=min(rows_wanted, B * Tq)).round().astype(np.int64)
-    rows = np.unique(rows)
-    qp_all = inp["q_pos"].numpy().reshape(-1)
-    pd_all = np.repeat(inp["pad"].numpy(), Tq)
+    h = {k: (_host(v) if hasattr(v, "detach") else v) for k, v in inp.items()}
+    qp_all = h["q_pos"].numpy().reshape(-1)
+    pd_all = np.repeat(h["pad"].numpy(), Tq)
+    rows = np.unique(np.linspace(0, B * Tq - 1, num=min(rows_wanted, B * Tq)).round()
+                     .astype(np.int64))
+    if cfg == 5:
+        kp, sk, width = inp["kpool"], inp["select_k"], inp["out_width"]
 
-    def one_pass():
-        S = oracle.index_scores(inp["q_idx"], inp["k_idx"], inp["w"], inp["scale_idx"],
-                                inp["q_pos"], inp["pad"], k_scale=inp["k_scale"], rows=rows)
-        sel = oracle.topk(S, qp_all[rows], pd_all[rows], inp["top_k"])
-        idx = np.full((B * Tq, inp["top_k"]), -1, np.int32)
-        idx[rows] = sel
-        idx = idx.reshape(B, Tq, -1)
-        if inp["dtype"] == "f32":
-            oracle.sparse_attend(inp["q"], inp["K"], inp["V"], idx, inp["scale_attn"], inp["H"],
-                                 q_pos=inp["q_pos"], pad=inp["pad"], rows=rows)
-        else:
-            oracle.sparse_attend(inp["q"], inp["KV"], None, idx, inp["scale_attn"], 1,
-                                 q_pos=inp["q_pos"], pad=inp["pad"], rows=rows,
-                                 k_row_stride=inp["kd"], vd=inp["vd"])
-
+        def one_pass():
+            pk, _ = oracle.pool_keys(h["k_idx"], h["gate"], h["pad"], kp)
+            S = oracle.index_scores(h["q_idx"], pk, h["w"], inp["scale_idx"], h["q_pos"],
+                                    h["pad"], kpool=kp, rows=rows)
+            tok = oracle.pool_select(S, qp_all[rows], pd_all[rows], kp, sk, width)
+            idx = np.full((B * Tq, width), -1, np.int32)
+            idx[rows] = tok
+            oracle.sparse_attend(h["q"], h["K"], h["V"], idx.reshape(B, Tq, width),
+                                 inp["scale_attn"], inp["H"], q_pos=h["q_pos"], pad=h["pad"],
+                                 rows=rows)
+        what = ("pool keys (all pools), pooled index scores over all visible pools, pool "
+                "select and per-head attention")
+    else:
+        def one_pass():
+            S = oracle.index_scores(h["q_idx"], h["k_idx"], h["w"], inp["scale_idx"],
+                                    h["q_pos"], h["pad"], k_scale=h.get("k_scale"), rows=rows)
+            sel = oracle.topk(S, qp_all[rows], pd_all[rows], inp["top_k"])
+            idx = np.full((B * Tq, inp["top_k"]), -1, np.int32)
+            idx[rows] = sel
+            idx = idx.reshape(B, Tq, -1)
+            if inp["dtype"] == "f32":
+                oracle.sparse_attend(h["q"], h["K"], h["V"], idx, inp["scale_attn"], inp["H"],
+                                     q_pos=h["q_pos"], pad=h["pad"], rows=rows)
+            else:
+                oracle.sparse_attend(h["q"], h["KV"], None, idx, inp["scale_attn"], 1,
+                                     q_pos=h["q_pos"], pad=h["pad"], rows=rows,
+                                     k_row_stride=inp["kd"], vd=inp["vd"])
+        what = "index scores over all keys, top-k and attention"
     passes = 0
     t0 = time.perf_counter()
     while True:
@@ -313,9 +596,13 @@ def cpu_baseline(cfg, rows_wanted, min_seconds=10.0, max_passes=20):
             break
     return {"value": round(len(rows) * passes / dt, 3), "unit": "tokens/s",
             "cores": oracle.threads(), "kind": "oracle",
-            "sample": f"{len(rows)} of {B * Tq} query rows of the same workload, full step "
-                      f"(index scores over all keys, top-k, attention), {passes} pass(es) in "
-                      f"{dt:.1f} s"}
+            "nproc": os.cpu_count(), "cpu_model": _cpu_model(),
+            "sample": f"{len(rows)} of {B * Tq} query rows of the timed workload, evenly spaced, "
+                      f"on the GPU's own input bytes: {what}; {passes} pass(es) in {dt:.1f} s"}
+
+
+def _public(res):
+    return {k: v for k, v in res.items() if not k.startswith("_")}
 
 
 def main():
@@ -335,112 +622,54 @@ def main():
         sys.exit(1)
     dsa.load()
     cfg = args.config
-    print(f"[bench] config {cfg}: generating inputs", file=sys.stderr, flush=True)
-    inp = W.make(cfg, device="cuda")
-    step = PooledStep(dsa, inp) if cfg == 5 else Step(dsa, inp)
-    names = type(step).stages
-    stages = [getattr(step, s) for s in names]
-
-    def run_once():
-        for f in stages:
-            f()
-
-    for _ in range(args.warmup):
-        run_once()
-    torch.cuda.synchronize()
     K = args.steps
-    # Whole-step timing: K steps launched back to back (or K replays of one
-    # captured HIP graph per step), nothing recorded between them.  An event
-    # recorded between two kernels holds the second back until the first has
-    # fully drained, so per-stage events inside this loop would add their own
-    # gaps to the step.
-    graph = None
-    if args.graph:
-        graph = capture_step(torch, run_once)
-        for _ in range(args.warmup):
-            graph.replay()
-        torch.cuda.synchronize()
-    print(f"[bench] warmup {args.warmup} done; timing {K} steps "
-          f"({'eager' if graph is None else 'graph replay'})", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(K):
-        if graph is None:
-            run_once()
-        else:
-            graph.replay()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    # Per-stage timing: K back-to-back launches of each stage on the step's
-    # own buffers, bracketed by two HIP events on the stream the kernels run
-    # on; the average launch duration feeds the stage breakdown and the
-    # roofline.
-    stage_ms = {}
-    for name, f in zip(names, stages):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(K):
-            f()
-        e1.record()
-        torch.cuda.synchronize()
-        stage_ms[name] = e0.elapsed_time(e1) / K
-    if cfg == 5:
-        work, tokens = pooled_work(inp)
-    else:
-        work, tokens = algorithmic_work(inp), inp["B"] * inp["Tq"]
-    ms_per_step = wall * 1e3 / K
-    per_stage = {}
-    for name in names:
-        by, fl = work[name]
-        t = stage_ms[name] * 1e-3
-        per_stage[name] = {"ms": round(stage_ms[name], 5),
-                           "alg_GBps": round(by / t / 1e9, 1),
-                           "alg_TFLOPs": round(fl / t / 1e12, 2)}
-    dom = max(names, key=lambda n: stage_ms[n])
-    by, fl = work[dom]
-    t = stage_ms[dom] * 1e-3
-    hbm_bound = cfg in (1, 2, 4) or dom in ("topk", "pool_select", "pool_keys")
-    if hbm_bound:
-        ach = by / t / 1e9
-        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4)}
-    else:
-        ach = fl / t / 1e12
-        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFS,
-                "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFS, 4)}
-    traffic, tsrc = measured_traffic(cfg, dom)
-    roof["traffic"] = traffic
-    roof["traffic_record"] = tsrc
-    roof["kernel"] = dom
-    roof["kernels"] = list(STAGE_KERNELS[dom])
-    roof["ms_per_launch"] = round(stage_ms[dom], 5)
-    roof["alg_bytes_per_launch"] = by
-    roof["alg_flops_per_launch"] = fl
+    peaks = None
+    if not args.only:
+        print("[bench] measuring the copy and MFMA-loop peaks", file=sys.stderr, flush=True)
+        peaks = measure_peaks()
+    print(f"[bench] config {cfg}: generating inputs", file=sys.stderr, flush=True)
+    res = run_workload(cfg, dsa, W, K, args.warmup, graph=args.graph)
+    roof = roofline_of(cfg, res, peaks)
+    inp = res["_inp"]
     result = {
         "metric": METRIC,
-        "value": round(tokens * K / wall, 1),
+        "value": res["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": res["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32" if inp["dtype"] == "f32" else "bf16",
         "data": "synthetic",
-        "config": {"workload": WORKLOAD_TEXT[cfg], "config_id": cfg,
-                   "query_tokens_per_step": tokens, "seed": inp["seed"],
-                   "launch": "eager" if graph is None else "hip graph per step"},
+        "config": {k: res[k] for k in ("workload", "config_id", "query_tokens_per_step",
+                                       "seed", "launch")},
         "roofline": roof,
-        "stages": per_stage,
+        "stages": res["stages"],
     }
+    if peaks:
+        result["peaks_measured"] = peaks
     if args.copy_probe:
         copy_probe(args.copy_probe)
-    if not args.no_cpu and cfg != 5:
+    if not args.no_cpu:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_rows)
+        result["cpu_baseline"] = cpu_baseline(res, args.cpu_rows)
+    del res, inp
+    torch.cuda.empty_cache()
+    if not args.only:
+        configs = {}
+        for c in (2, 3, 4, 5):
+            if c == cfg:
+                continue
+            print(f"[bench] config {c}", file=sys.stderr, flush=True)
+            r = run_workload(c, dsa, W, K, args.warmup)
+            r["roofline"] = roofline_of(c, r, peaks)
+            configs[str(c)] = _public(r)
+            del r
+            torch.cuda.empty_cache()
+        result["configs"] = configs
     print(json.dumps(result), flush=True)
 
 

@@ -65,7 +65,24 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    build_probe()
     return LIB
+
+
+PROBE_SRC = os.path.join(HERE, "probe", "peaks.hip")
+PROBE_LIB = os.path.join(HERE, "probe", "libdsa_probe.so")
+
+
+def build_probe() -> str:
+    """The measurement harness's calibration kernels (a streaming copy and
+    an MFMA-only loop), in a library of their own beside libdsa."""
+    tmp = PROBE_LIB + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), *COMMON, "-shared", "-o", tmp, PROBE_SRC]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"probe build failed\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
 
 
 if __name__ == "__main__":

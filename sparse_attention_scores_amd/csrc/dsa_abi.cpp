@@ -284,6 +284,13 @@ int dsa_sparse_attend(const dsa_attn_dims *d, int dtype, const void *q, const vo
     if (!dsa::attend_gather_supported(a) && !dsa::attend_masked_supported(a) &&
         !dsa::attend_plain_supported(a))
         return fail(DSA_ERR_UNSUPPORTED, "dsa_sparse_attend: vd %d too large", d->vd);
+    if (dsa::attend_gather_supported(a) || dsa::attend_masked_supported(a)) {
+        // the MFMA kernels move q, K, V and out in 16-byte pieces
+        auto al16 = [](const void *p) { return ((uintptr_t)p & 15u) == 0; };
+        if (!al16(q) || !al16(k) || !al16(v) || !al16(out) || !al16(workspace))
+            return fail(DSA_ERR_UNSUPPORTED,
+                        "dsa_sparse_attend: q, k, v, out and workspace must be 16-byte aligned");
+    }
     const size_t need = dsa::attend_workspace_bytes(a);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(DSA_ERR_WORKSPACE, "dsa_sparse_attend: workspace of %zu bytes needed, %zu given",

@@ -5,20 +5,29 @@
 // entries are dropped -- and mla_masked_attention attends over it).
 //
 // With per-head K and V nothing is shared across heads, so gathering each
-// query's ~2k selected rows per head would move ~100 MB per query.  Instead:
-//  1. topk_to_mask_kernel writes one bit per (query, key): the query's
-//     selected set, intersected with its visible range;
-//  2. attend_masked_kernel is a flash-style pass per (head, block of 128
-//     queries) over the key tiles the block's causal range covers; each tile
-//     is staged once in LDS and used by all 128 queries, non-selected keys
-//     are masked out of the online softmax, and tiles no query selects are
-//     skipped.
-// MFMA layout (32x32x16 bf16): S^T[key][query] = K_tile * Q^T with the
+// query's ~2k selected rows per head would move ~100 MB per query.  Instead
+// the selection becomes a bitmap and the attention runs over key tiles:
+//  1. topk_to_mask_kernel writes one bit per (query, key) -- the query's
+//     selected set intersected with its visible range -- tile-major, so the
+//     words of one key tile for a block of consecutive queries are one
+//     contiguous run;
+//  2. v_scale_max_kernel / v_to_f16_kernel re-encode V once as fp16 with a
+//     power-of-two scale per (sequence, head) that puts the largest |V| in
+//     [2^14, 2^15): every bf16 value whose magnitude is above 2^-29 of that
+//     maximum is exact in fp16, so the softmax weights can enter the P.V
+//     product as fp16 (11 significant bits) in one MFMA instead of a
+//     two-term bf16 split;
+//  3. attend_masked_kernel is a flash-style pass per (sequence, head, block
+//     of 256 queries) over the key tiles the block's causal range covers:
+//     each K/V tile is staged once in LDS and used by all 256 queries,
+//     non-selected keys are masked out of the online softmax, and a wave
+//     skips the tiles in which none of its 32 queries selects a key.
+// MFMA layout (32x32x16): S^T[key][query] = K_tile * Q^T (bf16) with the
 // queries of a wave in the B operand (held in registers), and
-// O^T[c][query] += V^T * P^T, where each lane's accumulators all belong to
-// one query, so the softmax rescale needs no cross-lane traffic.  V^T keeps
-// the keys of each 16-key half in the order the S^T accumulators hold them,
-// so P^T comes straight from the softmax registers.
+// O^T[c][query] += V^T * P^T (fp16), where each lane's accumulators all
+// belong to one query, so the softmax rescale needs no cross-lane traffic.
+// V^T keeps the keys of each 16-key half in the order the S^T accumulators
+// hold them, so P^T comes straight from the softmax registers.
 #include "dsa_device.hpp"
 #include "dsa_internal.hpp"
 
@@ -27,86 +36,212 @@
 
 namespace dsa {
 
-constexpr int MK_MAXWORDS = 16384;  // n_k <= 524288
+constexpr int MK_QB = 256;          // queries per attention block (8 waves x 32)
+constexpr int MK_TILE = 32;         // keys per tile
+constexpr int MK_ROWS = 32;         // query rows per mask-building block
+constexpr int MK_WCHUNK = 512;      // mask words per row held in LDS at once
+constexpr int MK_VKEYS = 256;       // keys per block of the V passes
 
-// One block per query row: the row's selected set as bits over n_k keys.
+// ------------------------------------------------------------------ mask
+
+// Block (b, group of 32 queries): the rows' selected sets as bits, written
+// tile-major: mask[(b * nw + w) * q_pad + q] holds keys 32w .. 32w+31 of
+// query q.  Rows past n_q (up to q_pad) get zero words, so every word of the
+// mask is written.  Keys are processed MK_WCHUNK words at a time.
 __global__ __launch_bounds__(256) void topk_to_mask_kernel(const int32_t *__restrict__ idx,
                                                            const int32_t *__restrict__ vlo,
                                                            const int32_t *__restrict__ vhi,
-                                                           uint32_t *__restrict__ mask, int n_k,
-                                                           int n_sel, int nw)
+                                                           uint32_t *__restrict__ mask, int n_q,
+                                                           int n_k, int n_sel, int nw, int q_pad)
 {
-    extern __shared__ uint32_t bits[];  // nw words (launch size), at most MK_MAXWORDS
-    const int row = blockIdx.x;
-    int lo = 0, hi = n_k;
-    if (vlo) {
-        lo = max(vlo[row], 0);
-        hi = min(vhi[row], n_k);
+    __shared__ uint32_t bits[MK_ROWS][MK_WCHUNK + 1];
+    const int groups = q_pad / MK_ROWS;
+    const int b = blockIdx.x / groups;
+    const int q0 = (blockIdx.x % groups) * MK_ROWS;
+    const int tid = threadIdx.x;
+    for (int w0 = 0; w0 < nw; w0 += MK_WCHUNK) {
+        const int wn = min(MK_WCHUNK, nw - w0);
+        for (int i = tid; i < MK_ROWS * (MK_WCHUNK + 1); i += 256)
+            (&bits[0][0])[i] = 0u;
+        __syncthreads();
+        for (int r = 0; r < MK_ROWS; ++r) {
+            const int q = q0 + r;
+            if (q >= n_q)
+                break;
+            const int64_t row = (int64_t)b * n_q + q;
+            int lo = 0, hi = n_k;
+            if (vlo) {
+                lo = max(vlo[row], 0);
+                hi = min(vhi[row], n_k);
+            }
+            lo = max(lo, w0 * 32);
+            hi = min(hi, (w0 + wn) * 32);
+            const int32_t *ir = idx + row * n_sel;
+            for (int i = tid; i < n_sel; i += 256) {
+                const int j = ir[i];
+                if (j >= lo && j < hi)
+                    atomicOr(&bits[r][(j >> 5) - w0], 1u << (j & 31));
+            }
+        }
+        __syncthreads();
+        uint32_t *mb = mask + ((int64_t)b * nw + w0) * q_pad + q0;
+        for (int i = tid; i < wn * MK_ROWS; i += 256) {
+            const int w = i / MK_ROWS, r = i % MK_ROWS;
+            mb[(int64_t)w * q_pad + r] = bits[r][w];
+        }
+        __syncthreads();
     }
-    for (int i = threadIdx.x; i < nw; i += 256)
-        bits[i] = 0u;
-    __syncthreads();
-    const int32_t *ir = idx + (int64_t)row * n_sel;
-    for (int i = threadIdx.x; i < n_sel; i += 256) {
-        const int j = ir[i];
-        if (j >= lo && j < hi)
-            atomicOr(&bits[j >> 5], 1u << (j & 31));
-    }
-    __syncthreads();
-    uint32_t *mr = mask + (int64_t)row * nw;
-    for (int i = threadIdx.x; i < nw; i += 256)
-        mr[i] = bits[i];
 }
+
+// ------------------------------------------------------------------ V as fp16
+
+// Exponent e of the power-of-two scale 2^-e that puts the largest |V| of a
+// (sequence, head) in [2^14, 2^15) -- well inside fp16's finite range -- from
+// the f32 bits of that largest magnitude; 0 when V is all zero.
+__device__ __forceinline__ int v16_exponent(uint32_t maxbits)
+{
+    if (maxbits == 0u)
+        return 0;
+    const int ex = (int)((maxbits >> 23) & 0xffu) - 127;
+    return min(max(ex - 14, -120), 120);
+}
+
+// Block (b, h, run of MK_VKEYS keys): largest |V| of the run, one partial
+// per block (no atomics, nothing to clear first).
+__global__ __launch_bounds__(256) void v_scale_max_kernel(const uint16_t *__restrict__ v,
+                                                          int64_t vsr, int n_k, int H, int vd,
+                                                          int nkb, uint32_t *__restrict__ part)
+{
+    __shared__ uint32_t red[4];
+    const int bh = blockIdx.x / nkb, kb = blockIdx.x % nkb;
+    const int b = bh / H, h = bh % H;
+    const int cpr = vd / 8;  // 16-byte chunks per head row
+    const int tid = threadIdx.x;
+    uint32_t mx = 0u;
+    const int k0 = kb * MK_VKEYS, k1 = min(k0 + MK_VKEYS, n_k);
+    for (int c = tid; c < (k1 - k0) * cpr; c += 256) {
+        const int key = k0 + c / cpr, ch = c % cpr;
+        const u32x4_t x = *reinterpret_cast<const u32x4_t *>(
+            v + ((int64_t)b * n_k + key) * vsr + (int64_t)h * vd + ch * 8);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            // |bf16| as f32 bits: the sign cleared, compared as integers
+            mx = max(mx, (x[j] << 16) & 0x7fffffffu);
+            mx = max(mx, x[j] & 0x7fff0000u);
+        }
+    }
+    mx = wave_max_u32(mx);
+    if ((tid & 63) == 0)
+        red[tid >> 6] = mx;
+    __syncthreads();
+    if (tid == 0)
+        part[blockIdx.x] = max(max(red[0], red[1]), max(red[2], red[3]));
+}
+
+// Same blocks: V * 2^-e(b,h) as fp16 (round to nearest even) into the dense
+// workspace copy v16[b][key][h][vd]; every block also writes its head's
+// 2^e (the same value from each block of the head).
+__global__ __launch_bounds__(256) void v_to_f16_kernel(const uint16_t *__restrict__ v, int64_t vsr,
+                                                       int n_k, int H, int vd, int nkb,
+                                                       const uint32_t *__restrict__ part,
+                                                       uint16_t *__restrict__ v16,
+                                                       float *__restrict__ vexp)
+{
+    const int bh = blockIdx.x / nkb, kb = blockIdx.x % nkb;
+    const int b = bh / H, h = bh % H;
+    const int tid = threadIdx.x;
+    uint32_t mx = 0u;
+    for (int i = tid & 63; i < nkb; i += 64)
+        mx = max(mx, part[(int64_t)bh * nkb + i]);
+    mx = wave_max_u32(mx);
+    const int e = v16_exponent(mx);
+    const float down = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e
+    if (tid == 0 && kb == 0)
+        vexp[bh] = __uint_as_float((uint32_t)(127 + e) << 23);      // 2^e
+    typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+    const int cpr = vd / 8;
+    const int k0 = kb * MK_VKEYS, k1 = min(k0 + MK_VKEYS, n_k);
+    for (int c = tid; c < (k1 - k0) * cpr; c += 256) {
+        const int key = k0 + c / cpr, ch = c % cpr;
+        const u32x4_t x = *reinterpret_cast<const u32x4_t *>(
+            v + ((int64_t)b * n_k + key) * vsr + (int64_t)h * vd + ch * 8);
+        u32x4_t y;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float lo = __uint_as_float(x[j] << 16) * down;
+            const float hi = __uint_as_float(x[j] & 0xffff0000u) * down;
+            y[j] = __builtin_bit_cast(uint32_t,
+                                      __builtin_convertvector(f32x2_t{lo, hi}, f16x2_t));
+        }
+        *reinterpret_cast<u32x4_t *>(v16 + (((int64_t)b * n_k + key) * H + h) * vd + ch * 8) = y;
+    }
+}
+
+// ------------------------------------------------------------------ attention
 
 // LDS row swizzles of the per-head tiles, chosen by measurement on gfx950
 // (both keep their access pattern at the full LDS rate):
 //  K rows (192 bf16 = 384 bytes = 24 chunks): physical chunk = logical ^
 //  ((row >> 1) & 7) -- the 32x32x16 operand reads (32 rows at one chunk);
-//  V rows (256 bf16 = 512 bytes = 32 chunks, so every row starts on bank 0):
+//  V rows (256 fp16 = 512 bytes = 32 chunks, so every row starts on bank 0):
 //  physical chunk = logical ^ (((row & 3) << 2) | ((row >> 2) & 3)) -- the
 //  transposing reads (4 rows x 2 chunks per 16 lanes).
 __device__ __forceinline__ int mk_swz_k(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int mk_swz_v(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 
-// Three 4-byte LDS reads and the wait (asm: the words arrive by direct-to-LDS
-// loads, and the compiler would otherwise wait for every such load in flight).
-__device__ __forceinline__ void lds_read_b32_3(uint32_t &x, uint32_t &y, uint32_t &z,
-                                               uint32_t ax, uint32_t ay, uint32_t az)
-{
-    asm volatile(
-        "ds_read_b32 %0, %3\n\t"
-        "ds_read_b32 %1, %4\n\t"
-        "ds_read_b32 %2, %5\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(x), "=&v"(y), "=&v"(z)
-        : "v"(ax), "v"(ay), "v"(az)
-        : "memory");
-}
-
-constexpr int MK_STAGES = 2;  // tiles resident in LDS (ring)
+constexpr int MK_STAGES = 4;  // tiles resident in LDS (ring)
 
 template <int KD, int VD>
 struct __attribute__((aligned(16))) MaskedSmem {
-    static constexpr int KB = 32 * KD * 2;  // K tile bytes (32 keys, row-major, swizzled)
-    static constexpr int VB = 32 * VD * 2;  // V tile bytes
+    static constexpr int KB = MK_TILE * KD * 2;  // K tile bytes (row-major, swizzled)
+    static constexpr int VB = MK_TILE * VD * 2;  // V tile bytes (fp16)
     unsigned char k[MK_STAGES][KB];
     unsigned char v[MK_STAGES][VB];
-    uint32_t mw[MK_STAGES][4][64];          // mask words of the tile: [wave][lane & 31]
+    uint32_t mw[MK_STAGES][MK_QB];              // the block's mask words of the tile
 };
 
-// Per (sequence, head, block of 128 queries); wave w owns queries
-// q0 + 32w .. +31 (lane col = query, half g = lane >> 5).  Tiles of 32 keys
-// stream through a ring of MK_STAGES LDS tiles by direct-to-LDS loads, with the
-// queries' mask words for the tile riding along (one 4-byte load per lane);
-// each wave issues the same number of loads per tile (7 of the 28 K/V
-// instructions plus its mask words), so a counted wait finds its tile.
+__device__ __forceinline__ f32x16_t mfma_32x32x16_f16(const u32x4_t &a, const u32x4_t &b,
+                                                      f32x16_t c)
+{
+    typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t cvt_pk_f16(float a, float b)
+{
+    typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, f16x2_t));
+}
+
+// One LDS read of a 4-byte word and the wait (asm: the word arrives by a
+// direct-to-LDS load, and the compiler would otherwise wait for every such
+// load in flight).
+__device__ __forceinline__ uint32_t mk_read_word(uint32_t a)
+{
+    uint32_t x;
+    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(x) : "v"(a) : "memory");
+    return x;
+}
+
+// Per (sequence, head, block of 256 queries), 8 waves: wave w owns queries
+// q0 + 32w .. +31 (lane col = query, half g = lane >> 5).  Key tiles of 32
+// stream through a ring of MK_STAGES LDS stages by direct-to-LDS loads (12
+// one-KB instructions for K, 16 for V, one for the block's mask words: 29,
+// four per wave for waves 0-6 and the mask for wave 7).
+//
+// Ping-pong: the waves of one SIMD (w and w + 4) alternate between a matrix
+// phase (P.V of the previous tile, then Q.K^T of this one) and a vector
+// phase (this tile's softmax).  Waves 4-7 run half an iteration behind waves
+// 0-3, held there by one workgroup barrier at each phase boundary, so while
+// one wave of a SIMD issues its MFMAs the other runs its exponentials.
 template <int KD, int VD>
-__global__ __launch_bounds__(256, 2) void attend_masked_kernel(
+__global__ __launch_bounds__(512, 1) void attend_masked_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, int64_t ksr,
-    const uint16_t *__restrict__ v, int64_t vsr, const uint32_t *__restrict__ mask,
-    const int32_t *__restrict__ vlo, const int32_t *__restrict__ vhi, float *__restrict__ out,
-    float *__restrict__ lse, int n_q, int n_k, int H, int kv_heads, int nw, int n_qblocks,
-    int BH, float scale_log2)
+    const uint16_t *__restrict__ v16, const float *__restrict__ vexp,
+    const uint32_t *__restrict__ mask, const int32_t *__restrict__ vlo,
+    const int32_t *__restrict__ vhi, float *__restrict__ out, float *__restrict__ lse, int n_q,
+    int n_k, int H, int nw, int q_pad, int n_qblocks, float c_log2, float thr, bool neg_q)
 {
     constexpr int KS = KD / 16;      // k-steps of the 32x32x16 MFMA over kd
     constexpr int NCT = VD / 32;     // output column tiles of 32
@@ -114,25 +249,27 @@ __global__ __launch_bounds__(256, 2) void attend_masked_kernel(
     constexpr int VCH = VD / 8;      // 16-byte chunks of a V row
     static_assert(KD == 192 && VD == 256, "the swizzles and read groups are laid out for 192/256");
     using Sm = MaskedSmem<KD, VD>;
-    constexpr int NKV = (Sm::KB + Sm::VB) / 1024;  // 28 K/V DMA instructions per tile
-    constexpr int PER = NKV / 4;                   // 7 per wave
-    static_assert(NKV % 4 == 0, "K/V DMA splits evenly over the waves");
+    constexpr int NK_DMA = Sm::KB / 1024;            // 12
+    constexpr int NV_DMA = Sm::VB / 1024;            // 16
+    constexpr int NSLOT = NK_DMA + NV_DMA + 1;       // 29 one-KB loads per tile
+    static_assert(NSLOT <= 32, "four load slots per wave");
     __shared__ Sm sm;
-    __shared__ int sm_red[8];
+    __shared__ int sm_red[16];
     DSA_LDS_ESCAPE(sm);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool grp_b = wid >= 4;
     const int g = lane >> 5, col = lane & 31;
-    // Head-major order: the query blocks of one (sequence, head) run together
-    // and stream the same K/V tiles (served from L2/MALL after the first
-    // read); within a head the heaviest (latest) query blocks go first.
-    const int qblk = n_qblocks - 1 - (int)(blockIdx.x % n_qblocks);
-    const int bh = blockIdx.x / n_qblocks;
+    // Each XCD takes a contiguous range of blocks: the query blocks of one
+    // (sequence, head) run together on one XCD and stream the same K/V tiles
+    // through its L2; within a head the heaviest (latest) blocks go first.
+    const int lb = xcd_remap(blockIdx.x, gridDim.x);
+    const int qblk = n_qblocks - 1 - lb % n_qblocks;
+    const int bh = lb / n_qblocks;
     const int b = bh / H, h = bh % H;
-    const int kvh = h / (H / kv_heads);
-    const int q0 = qblk * 128;
+    const int q0 = qblk * MK_QB;
     const int qi = q0 + wid * 32 + col;  // this lane's query
     const bool q_ok = qi < n_q;
     const int64_t row = (int64_t)b * n_q + (q_ok ? qi : 0);
@@ -152,23 +289,32 @@ __global__ __launch_bounds__(256, 2) void attend_masked_kernel(
         }
         if (lane == 0) {
             sm_red[wid] = mn;
-            sm_red[4 + wid] = mx;
+            sm_red[8 + wid] = mx;
         }
         __syncthreads();
-        lo = min(min(sm_red[0], sm_red[1]), min(sm_red[2], sm_red[3]));
-        hi = max(max(sm_red[4], sm_red[5]), max(sm_red[6], sm_red[7]));
+        lo = sm_red[0];
+        hi = sm_red[8];
+#pragma unroll
+        for (int w = 1; w < 8; ++w) {
+            lo = min(lo, sm_red[w]);
+            hi = max(hi, sm_red[8 + w]);
+        }
     }
-    const int t_begin = lo / 32;
-    const int t_end = hi > lo ? (hi + 31) / 32 : t_begin;
+    const int T0 = lo / MK_TILE;
+    const int T1 = hi > lo ? (hi + MK_TILE - 1) / MK_TILE : T0;
 
-    // Q^T fragments (B operand): query qi, dims ks*16 + g*8 .. +8
+    // Q^T fragments (B operand): query qi, dims ks*16 + g*8 .. +8; negated
+    // (exactly) when the scale is negative, so the softmax runs on |scale|
     u32x4_t qf[KS];
     {
         const uint16_t *qp = q + (row * H + h) * KD + g * 8;
+        const uint32_t flip = neg_q ? 0x80008000u : 0u;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
+        for (int ks = 0; ks < KS; ++ks) {
             qf[ks] = q_ok ? *reinterpret_cast<const u32x4_t *>(qp + ks * 16)
                           : u32x4_t{0u, 0u, 0u, 0u};
+            qf[ks] ^= u32x4_t{flip, flip, flip, flip};
+        }
     }
     f32x16_t oacc[NCT];
 #pragma unroll
@@ -177,43 +323,51 @@ __global__ __launch_bounds__(256, 2) void attend_masked_kernel(
     float m_run = -INFINITY, l_part = 0.f;
 
     const unsigned char *kb =
-        reinterpret_cast<const unsigned char *>(k + (int64_t)b * n_k * ksr + (int64_t)kvh * KD);
+        reinterpret_cast<const unsigned char *>(k + (int64_t)b * n_k * ksr + (int64_t)h * KD);
     const unsigned char *vb =
-        reinterpret_cast<const unsigned char *>(v + (int64_t)b * n_k * vsr + (int64_t)kvh * VD);
-    // mask words of this lane's query (lanes 32..63 repeat lanes 0..31; an
-    // invalid query reads a valid row of the batch and is never used)
-    const uint32_t *mrow =
-        mask + ((int64_t)b * n_q + min(q0 + wid * 32 + col, n_q - 1)) * nw;
+        reinterpret_cast<const unsigned char *>(v16 + ((int64_t)b * n_k * H + h) * VD);
+    const unsigned char *mb = reinterpret_cast<const unsigned char *>(
+        mask + (int64_t)b * nw * q_pad + q0);
+    const uint32_t ksr2 = (uint32_t)(ksr * 2), vsr2 = (uint32_t)(H * VD * 2);
+    const uint32_t q_pad4 = (uint32_t)q_pad * 4u;
+    // this wave's load slots: 4w .. 4w+3 of the tile's 29
+    const int n_mine = min(4, NSLOT - 4 * wid);
 
-    // DMA: this wave issues instructions s = wid + 4i (i < 7) of the tile's 28
-    // (12 for K, then 16 for V); lane l of instruction s fills LDS bytes
-    // 16l of that KB = (row, physical chunk), fetching the row's logical chunk
-    // (recomputed per tile: a few VALU instead of seven live registers)
-    const uint32_t ksr2 = (uint32_t)(ksr * 2), vsr2 = (uint32_t)(vsr * 2);
+    // DMA of tile t into stage st: slot s < 12 fills K chunk row, 12..27 V,
+    // 28 the mask words; lane l of a slot fills LDS bytes 16l of that KB =
+    // (row, physical chunk), fetching the row's logical chunk (addresses
+    // recomputed per tile: a few VALU instead of live registers)
     auto dma_tile = [&](int t, int st) {
-        const int k0 = t * 32;
-        // an opaque copy of the lane index keeps the compiler from hoisting the
-        // seven 64-bit addresses out of the tile loop (as live registers)
+        const int k0 = t * MK_TILE;
         int ln = lane;
         asm volatile("" : "+v"(ln));
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int s_ = wid + 4 * i;
-            if (s_ < Sm::KB / 1024) {
+        for (int j = 0; j < 4; ++j) {
+            const int s_ = 4 * wid + j;
+            if (s_ < NK_DMA) {
                 const int c = s_ * 64 + ln, r = c / KCH;
                 const int key = min(k0 + r, n_k - 1);  // rows past n_k are masked
                 lds_dma16(kb + (uint64_t)(uint32_t)key * ksr2 +
                               (uint32_t)(((c % KCH) ^ mk_swz_k(r)) * 16),
                           sm.k[st] + s_ * 1024);
-            } else {
-                const int c = (s_ - Sm::KB / 1024) * 64 + ln, r = c / VCH;
+            } else if (s_ < NK_DMA + NV_DMA) {
+                const int c = (s_ - NK_DMA) * 64 + ln, r = c / VCH;
                 const int key = min(k0 + r, n_k - 1);
                 lds_dma16(vb + (uint64_t)(uint32_t)key * vsr2 +
                               (uint32_t)(((c % VCH) ^ mk_swz_v(r)) * 16),
-                          sm.v[st] + (s_ - Sm::KB / 1024) * 1024);
+                          sm.v[st] + (s_ - NK_DMA) * 1024);
+            } else if (s_ < NSLOT) {
+                lds_dma16(mb + (uint64_t)t * q_pad4 + 16u * (uint32_t)ln, &sm.mw[st][0]);
             }
         }
-        lds_dma4(mrow + t, sm.mw[st][wid]);
+    };
+    // wait until this wave's loads of the tile `after` tiles before the
+    // newest one issued have landed
+    auto wait_tile = [&](int after) {
+        if (n_mine == 4)
+            vm_wait_tiles<4>(after);
+        else
+            vm_wait_tiles<1>(after);
     };
 
     // per-lane LDS byte offsets inside a stage (constant over tiles)
@@ -239,107 +393,51 @@ __global__ __launch_bounds__(256, 2) void attend_masked_kernel(
         vb_[j] = (rb * VCH + ((4 * j + cp) ^ mk_swz_v(rb))) * 16 + 8 * (la & 1);
     }
     const uint32_t lds_k = lds_addr(sm.k[0]), lds_v = lds_addr(sm.v[0]);
+    const uint32_t lds_mw = lds_addr(&sm.mw[0][0]) + 4u * (uint32_t)(wid * 32 + col);
 
-    // the Q fragments and ranges are in registers before the first tile DMA
-    vm_wait<0>();
-    for (int j = 0; j < MK_STAGES - 1 && t_begin + j < t_end; ++j)
-        dma_tile(t_begin + j, j);
-    for (int t = t_begin; t < t_end; ++t) {
-        const int st = (t - t_begin) % MK_STAGES;
-        // this wave's part of tile t has landed (later tiles may still fly)
-        vm_wait_tiles<PER + 1>(min(t_end - 1, t + MK_STAGES - 2) - t);
-        lds_barrier();  // ... every wave's, and tile t-1's stage is free
-        if (t + MK_STAGES - 1 < t_end)
-            dma_tile(t + MK_STAGES - 1, (t - t_begin + MK_STAGES - 1) % MK_STAGES);
-        uint32_t word, w0, w1;
-        {
-            const uint32_t mb = lds_addr(&sm.mw[st][0][0]) + 4 * col;
-            lds_read_b32_3(word, w0, w1, mb + 256 * wid, mb + 256 * g, mb + 256 * (2 + g));
-        }
-        // skip the tile when none of the block's 128 queries selects a key in it
-        if (!__any((w0 | w1) != 0u))
-            continue;
-        // ---- S^T[key][query] for the 32 keys of the tile
+    // Q.K^T for the 32 keys of the tile in stage st
+    auto qk = [&](int st) {
         f32x16_t s = {};
-        {
-            const uint32_t kt = lds_k + st * Sm::KB;
-            // k-step ks reads base kq[ks & 3] + 128 * (ks >> 2); the reads run
-            // two k-steps ahead of the MFMAs that use them
-            u32x4_t a[KS];
-            lds_read_b128_nowait<0>(a[0], kt + kq[0]);
-            lds_read_b128_nowait<0>(a[1], kt + kq[1]);
-            auto qk = [&](auto KSc) {
-                constexpr int ks = decltype(KSc)::value;
-                if constexpr (ks + 2 < KS) {
-                    lds_read_b128_nowait<128 * ((ks + 2) >> 2)>(a[ks + 2], kt + kq[(ks + 2) & 3]);
-                    lds_operand_wait<2>(a[ks]);
-                } else if constexpr (ks + 1 < KS) {
-                    lds_operand_wait<1>(a[ks]);
-                } else {
-                    lds_operand_wait<0>(a[ks]);
-                }
-                s = mfma_32x32x16(a[ks], qf[ks], s);
-            };
-            static_assert(KS == 12, "twelve k-steps");
-            qk(std::integral_constant<int, 0>{});
-            qk(std::integral_constant<int, 1>{});
-            qk(std::integral_constant<int, 2>{});
-            qk(std::integral_constant<int, 3>{});
-            qk(std::integral_constant<int, 4>{});
-            qk(std::integral_constant<int, 5>{});
-            qk(std::integral_constant<int, 6>{});
-            qk(std::integral_constant<int, 7>{});
-            qk(std::integral_constant<int, 8>{});
-            qk(std::integral_constant<int, 9>{});
-            qk(std::integral_constant<int, 10>{});
-            qk(std::integral_constant<int, 11>{});
-        }
-        // lane holds keys 8*(i/4) + 4g + i%4 of the tile for query qi
-        float x[16];
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int kk = 8 * (i / 4) + 4 * g + (i % 4);
-            x[i] = ((word >> kk) & 1u) ? s[i] * scale_log2 : -INFINITY;
-            tmax = fmaxf(tmax, x[i]);
-        }
-        {
-            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax),
-                                                             __float_as_uint(tmax), false, false);
-            tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-        }
-        // lazy rescale (see the gather kernel): p <= 2^kRescaleLog2
-        const bool grow = tmax > m_run + kRescaleLog2;
-        if (__any(grow)) {
-            const float m_new = grow ? tmax : m_run;
-            // lanes that do not grow keep alpha = 1 (m_run may still be -inf
-            // there, and -inf - -inf would be NaN); a growing lane with
-            // m_run = -inf gets 0
-            const float alpha = grow ? exp2f(m_run - m_new) : 1.f;
-            if (__any(grow && m_run != -INFINITY)) {
-#pragma unroll
-                for (int n = 0; n < NCT; ++n)
-                    oacc[n] *= alpha;
+        const uint32_t kt = lds_k + st * Sm::KB;
+        // k-step ks reads base kq[ks & 3] + 128 * (ks >> 2); the reads run
+        // two k-steps ahead of the MFMAs that use them
+        u32x4_t a[KS];
+        lds_read_b128_nowait<0>(a[0], kt + kq[0]);
+        lds_read_b128_nowait<0>(a[1], kt + kq[1]);
+        auto step = [&](auto KSc) {
+            constexpr int ks = decltype(KSc)::value;
+            if constexpr (ks + 2 < KS) {
+                lds_read_b128_nowait<128 * ((ks + 2) >> 2)>(a[ks + 2], kt + kq[(ks + 2) & 3]);
+                lds_operand_wait<2>(a[ks]);
+            } else if constexpr (ks + 1 < KS) {
+                lds_operand_wait<1>(a[ks]);
+            } else {
+                lds_operand_wait<0>(a[ks]);
             }
-            l_part *= alpha;
-            m_run = m_new;
-        }
-        // m_run is -inf only while every key seen so far (this tile
-        // included) is masked; then all x are -inf and p must be 0.
-        const float m_ref = (m_run == -INFINITY) ? 0.f : m_run;
-        float p[16];
-        float psum = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            p[i] = __builtin_amdgcn_exp2f(x[i] - m_ref);
-            psum += p[i];
-        }
-        l_part += psum;
-        // ---- O^T[c][query] += V^T[c][keys] P^T[keys][query], per 16-key half
-        // step T (kh = T >> 3, column tile n = T & 7) reads V^T rows ra / rb
-        // of key half kh at column tile n: bases va_/vb_[n & 3], immediate
-        // 256 * (n >> 2) + 16 rows * kh; the reads run two steps ahead of
-        // the MFMAs that use them
+            s = mfma_32x32x16(a[ks], qf[ks], s);
+        };
+        static_assert(KS == 12, "twelve k-steps");
+        step(std::integral_constant<int, 0>{});
+        step(std::integral_constant<int, 1>{});
+        step(std::integral_constant<int, 2>{});
+        step(std::integral_constant<int, 3>{});
+        step(std::integral_constant<int, 4>{});
+        step(std::integral_constant<int, 5>{});
+        step(std::integral_constant<int, 6>{});
+        step(std::integral_constant<int, 7>{});
+        step(std::integral_constant<int, 8>{});
+        step(std::integral_constant<int, 9>{});
+        step(std::integral_constant<int, 10>{});
+        step(std::integral_constant<int, 11>{});
+        return s;
+    };
+
+    // O^T[c][query] += V^T[c][keys] P^T[keys][query] for the tile in stage
+    // st: step T (kh = T >> 3, column tile n = T & 7) reads V^T rows ra / rb
+    // of key half kh at column tile n: bases va_/vb_[n & 3], immediate
+    // 256 * (n >> 2) + 16 rows * kh; the reads run two steps ahead of the
+    // MFMAs that use them
+    auto pv = [&](int st, const u32x4_t &p0, const u32x4_t &p1) {
         const uint32_t vt = lds_v + st * Sm::VB;
         u32x2_t ra2[2 * NCT], rb2[2 * NCT];
         auto rd = [&](auto Tc) {
@@ -348,7 +446,6 @@ __global__ __launch_bounds__(256, 2) void attend_masked_kernel(
             lds_read_tr16_nowait<o>(ra2[T], vt + va_[n & 3]);
             lds_read_tr16_nowait<o>(rb2[T], vt + vb_[n & 3]);
         };
-        u32x4_t bhi, blo;
         auto step = [&](auto Tc) {
             constexpr int T = decltype(Tc)::value, n = T & 7;
             constexpr int NS = 2 * NCT;
@@ -358,19 +455,8 @@ __global__ __launch_bounds__(256, 2) void attend_masked_kernel(
             } else {
                 lds_operand_wait<2 * (NS - 1 - T)>(ra2[T], rb2[T]);
             }
-            if constexpr (n == 0) {
-                uint32_t hi4[4], lo4[4];
-                float ph[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    ph[j] = p[(T >> 3) * 8 + j];
-                split_bf16x8(ph, hi4, lo4);
-                bhi = u32x4_t{hi4[0], hi4[1], hi4[2], hi4[3]};
-                blo = u32x4_t{lo4[0], lo4[1], lo4[2], lo4[3]};
-            }
             const u32x4_t av = {ra2[T][0], ra2[T][1], rb2[T][0], rb2[T][1]};
-            oacc[n] = mfma_32x32x16(av, bhi, oacc[n]);
-            oacc[n] = mfma_32x32x16(av, blo, oacc[n]);
+            oacc[n] = mfma_32x32x16_f16(av, (T >> 3) ? p1 : p0, oacc[n]);
         };
         static_assert(NCT == 8, "eight column tiles");
         rd(std::integral_constant<int, 0>{});
@@ -380,7 +466,106 @@ __global__ __launch_bounds__(256, 2) void attend_masked_kernel(
         MK_PV_STEP(6) MK_PV_STEP(7) MK_PV_STEP(8) MK_PV_STEP(9) MK_PV_STEP(10) MK_PV_STEP(11)
         MK_PV_STEP(12) MK_PV_STEP(13) MK_PV_STEP(14) MK_PV_STEP(15)
 #undef MK_PV_STEP
+    };
+
+    // the Q fragments and ranges are in registers before the first tile DMA
+    vm_wait<0>();
+    for (int j = 0; j < MK_STAGES - 1 && T0 + j < T1; ++j)
+        dma_tile(T0 + j, j);
+    if (T1 > T0)
+        wait_tile(min(T1 - 1, T0 + MK_STAGES - 2) - T0);
+    lds_barrier();  // tile T0 is in LDS for every wave
+    if (grp_b)
+        lds_barrier();  // waves 4-7 start half an iteration behind
+
+    f32x16_t s = {};
+    u32x4_t p0 = {}, p1 = {};  // P^T of the previous tile (fp16, both key halves)
+    bool act_prev = false;
+    for (int t = T0; t <= T1; ++t) {
+        const int st = (t - T0) % MK_STAGES;
+        // ---------------- matrix phase: P.V of tile t-1, Q.K^T of tile t
+        if (!grp_b && t - 1 >= T0 && t + MK_STAGES - 2 < T1)
+            dma_tile(t + MK_STAGES - 2, (t + MK_STAGES - 2 - T0) % MK_STAGES);
+        uint32_t word = 0u;
+        bool act = false;
+        if (t < T1) {
+            word = mk_read_word(lds_mw + st * (MK_QB * 4));
+            act = __any(word != 0u);
+        }
+        if (act_prev)
+            pv((st + MK_STAGES - 1) % MK_STAGES, p0, p1);
+        if (act)
+            s = qk(st);
+        if (grp_b && t + 1 < T1)
+            wait_tile(min(T1 - 1, t + MK_STAGES - 2) - (t + 1));
+        lds_barrier();
+        if (t == T1)
+            break;
+        // ---------------- vector phase: the softmax of tile t
+        if (grp_b && t + MK_STAGES - 1 < T1)
+            dma_tile(t + MK_STAGES - 1, (t + MK_STAGES - 1 - T0) % MK_STAGES);
+        if (act) {
+            // lane holds keys 8*(i/4) + 4g + i%4 of the tile for query qi;
+            // unselected keys become -inf (sign-extended bit as a bit mask)
+            float x[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int kk = 8 * (i / 4) + 4 * g + (i % 4);
+                const uint32_t m = (uint32_t)__builtin_amdgcn_sbfe((int)word, kk, 1);
+                x[i] = __uint_as_float((__float_as_uint(s[i]) & m) | (~m & 0xff800000u));
+            }
+            float tmax = fmaxf(fmaxf(x[0], x[1]), x[2]);
+            tmax = fmaxf(fmaxf(tmax, x[3]), x[4]);
+            tmax = fmaxf(fmaxf(tmax, x[5]), x[6]);
+            tmax = fmaxf(fmaxf(tmax, x[7]), x[8]);
+            tmax = fmaxf(fmaxf(tmax, x[9]), x[10]);
+            tmax = fmaxf(fmaxf(tmax, x[11]), x[12]);
+            tmax = fmaxf(fmaxf(tmax, x[13]), x[14]);
+            tmax = fmaxf(tmax, x[15]);
+            {
+                const auto sw = __builtin_amdgcn_permlane32_swap(
+                    __float_as_uint(tmax), __float_as_uint(tmax), false, false);
+                tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+            }
+            // lazy rescale (raw score units; thr = 8 / c): p <= 2^8
+            const bool grow = tmax > m_run + thr;
+            if (__any(grow)) {
+                const float m_new = grow ? tmax : m_run;
+                // lanes that do not grow keep alpha = 1 (m_run may still be
+                // -inf there, and -inf - -inf would be NaN); a growing lane
+                // with m_run = -inf gets 0
+                const float alpha = grow ? exp2f((m_run - m_new) * c_log2) : 1.f;
+                if (__any(grow && m_run != -INFINITY)) {
+#pragma unroll
+                    for (int n = 0; n < NCT; ++n)
+                        oacc[n] *= alpha;
+                }
+                l_part *= alpha;
+                m_run = m_new;
+            }
+            // m_run is -inf only while every key seen so far (this tile
+            // included) is masked; then all x are -inf and p must be 0.
+            const float mc = (m_run == -INFINITY) ? 0.f : m_run * c_log2;
+            float p[16];
+            float psum = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], c_log2, -mc));
+                psum += p[i];
+            }
+            l_part += psum;
+            p0 = u32x4_t{cvt_pk_f16(p[0], p[1]), cvt_pk_f16(p[2], p[3]),
+                         cvt_pk_f16(p[4], p[5]), cvt_pk_f16(p[6], p[7])};
+            p1 = u32x4_t{cvt_pk_f16(p[8], p[9]), cvt_pk_f16(p[10], p[11]),
+                         cvt_pk_f16(p[12], p[13]), cvt_pk_f16(p[14], p[15])};
+        }
+        act_prev = act;
+        if (!grp_b && t + 1 < T1)
+            wait_tile(min(T1 - 1, t + MK_STAGES - 2) - (t + 1));
+        lds_barrier();
     }
+    if (!grp_b)
+        lds_barrier();  // the barrier count of waves 0-3 matches waves 4-7
 
     // ---- epilogue
     float l_tot;
@@ -390,7 +575,7 @@ __global__ __launch_bounds__(256, 2) void attend_masked_kernel(
         l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
     }
     if (q_ok) {
-        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        const float inv = l_tot > 0.f ? vexp[(int64_t)b * H + h] / l_tot : 0.f;
         float *op = out + (row * H + h) * VD;
 #pragma unroll
         for (int n = 0; n < NCT; ++n) {
@@ -403,45 +588,89 @@ __global__ __launch_bounds__(256, 2) void attend_masked_kernel(
             }
         }
         if (lse && g == 0)
-            lse[row * H + h] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+            lse[row * H + h] = l_tot > 0.f ? (m_run * c_log2 + log2f(l_tot)) * kLn2 : -INFINITY;
     }
 }
 
+// ------------------------------------------------------------------ host side
+
+namespace {
+struct MaskedLayout {
+    int nw, q_pad, nkb;
+    size_t mask_bytes, v16_bytes, part_bytes, vexp_bytes;
+    size_t v16_off, part_off, vexp_off, total;
+};
+
+MaskedLayout masked_layout(const AttendArgs &a)
+{
+    MaskedLayout L{};
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    L.nw = (a.n_k + 31) / 32;
+    L.q_pad = (a.n_q + MK_QB - 1) / MK_QB * MK_QB;
+    L.nkb = (a.n_k + MK_VKEYS - 1) / MK_VKEYS;
+    L.mask_bytes = (size_t)a.batch * L.nw * L.q_pad * sizeof(uint32_t);
+    L.v16_bytes = (size_t)a.batch * a.n_k * a.n_heads * a.vd * sizeof(uint16_t);
+    L.part_bytes = (size_t)a.batch * a.n_heads * L.nkb * sizeof(uint32_t);
+    L.vexp_bytes = (size_t)a.batch * a.n_heads * sizeof(float);
+    L.v16_off = up(L.mask_bytes);
+    L.part_off = L.v16_off + up(L.v16_bytes);
+    L.vexp_off = L.part_off + up(L.part_bytes);
+    L.total = L.vexp_off + up(L.vexp_bytes);
+    return L;
+}
+} // namespace
+
 bool attend_masked_supported(const AttendArgs &a)
 {
-    return !a.f32 && a.kv_heads == a.n_heads && a.kd == 192 && a.vd == 256 &&
-           a.k_row_stride % 8 == 0 && a.v_row_stride % 8 == 0;
+    return !a.f32 && a.kv_heads == a.n_heads && a.kd == 192 && a.vd == 256 && a.n_k > 0 &&
+           a.k_row_stride % 8 == 0 && a.v_row_stride % 8 == 0 &&
+           (int64_t)a.n_heads * a.vd * 2 < (1ll << 31) && a.k_row_stride * 2 < (1ll << 31);
 }
 
 size_t attend_masked_workspace_bytes(const AttendArgs &a)
 {
-    const int64_t rows = (int64_t)a.batch * a.n_q;
-    const int64_t nw = (a.n_k + 31) / 32;
-    return (size_t)(rows * nw) * sizeof(uint32_t);
+    return masked_layout(a).total;
 }
 
 hipError_t launch_attend_masked(const AttendArgs &a, hipStream_t st)
 {
-    const int64_t rows = (int64_t)a.batch * a.n_q;
-    const int nw = (a.n_k + 31) / 32;
-    uint32_t *mask = static_cast<uint32_t *>(a.workspace);
-    if (nw > MK_MAXWORDS)  // the ABI rejects such rows before this
-        return hipErrorInvalidValue;
-    // LDS sized to the row (2 KB for 16384 keys) so that many rows share a CU
-    hipLaunchKernelGGL(topk_to_mask_kernel, dim3((unsigned)rows), dim3(256),
-                       (unsigned)(nw * sizeof(uint32_t)), st, a.idx,
-                       a.vis_lo, a.vis_hi, mask, a.n_k, a.n_sel, nw);
+    const MaskedLayout L = masked_layout(a);
+    unsigned char *ws = static_cast<unsigned char *>(a.workspace);
+    uint32_t *mask = reinterpret_cast<uint32_t *>(ws);
+    uint16_t *v16 = reinterpret_cast<uint16_t *>(ws + L.v16_off);
+    uint32_t *part = reinterpret_cast<uint32_t *>(ws + L.part_off);
+    float *vexp = reinterpret_cast<float *>(ws + L.vexp_off);
+    const int64_t mblocks = (int64_t)a.batch * (L.q_pad / MK_ROWS);
+    const int64_t vblocks = (int64_t)a.batch * a.n_heads * L.nkb;
+    const int n_qblocks = L.q_pad / MK_QB;
+    const int64_t blocks = (int64_t)n_qblocks * a.batch * a.n_heads;
+    if (mblocks > 0x7fffffff || vblocks > 0x7fffffff || blocks > 0x7fffffff)
+        return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(topk_to_mask_kernel, dim3((unsigned)mblocks), dim3(256), 0, st, a.idx,
+                       a.vis_lo, a.vis_hi, mask, a.n_q, a.n_k, a.n_sel, L.nw, L.q_pad);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    const int n_qblocks = (a.n_q + 127) / 128;
-    const int BH = a.batch * a.n_heads;
-    const int64_t blocks = (int64_t)n_qblocks * BH;
-    hipLaunchKernelGGL((attend_masked_kernel<192, 256>), dim3((unsigned)blocks), dim3(256), 0, st,
+    const uint16_t *v = static_cast<const uint16_t *>(a.v);
+    hipLaunchKernelGGL(v_scale_max_kernel, dim3((unsigned)vblocks), dim3(256), 0, st, v,
+                       a.v_row_stride, a.n_k, a.n_heads, a.vd, L.nkb, part);
+    e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(v_to_f16_kernel, dim3((unsigned)vblocks), dim3(256), 0, st, v,
+                       a.v_row_stride, a.n_k, a.n_heads, a.vd, L.nkb, part, v16, vexp);
+    e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    // softmax in base 2 on |scale| (the queries are negated for a negative
+    // scale); a zero scale keeps a tiny positive factor so that masked keys
+    // still come out as -inf rather than NaN
+    const float c = fmaxf(fabsf(a.scale) * kLog2e, 1e-30f);
+    hipLaunchKernelGGL((attend_masked_kernel<192, 256>), dim3((unsigned)blocks), dim3(512), 0, st,
                        static_cast<const uint16_t *>(a.q), static_cast<const uint16_t *>(a.k),
-                       a.k_row_stride, static_cast<const uint16_t *>(a.v), a.v_row_stride, mask,
-                       a.vis_lo, a.vis_hi, a.out, a.lse, a.n_q, a.n_k, a.n_heads, a.kv_heads, nw,
-                       n_qblocks, BH, a.scale * kLog2e);
+                       a.k_row_stride, v16, vexp, mask, a.vis_lo, a.vis_hi, a.out, a.lse, a.n_q,
+                       a.n_k, a.n_heads, L.nw, L.q_pad, n_qblocks, c, kRescaleLog2 / c,
+                       a.scale < 0.f);
     return hipGetLastError();
 }
 

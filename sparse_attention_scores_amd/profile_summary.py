@@ -32,8 +32,8 @@ from collections import defaultdict
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 
-# the kernel that bench.py --copy-probe launches (y = -x over float32)
-COPY_KERNEL_PATTERN = "neg_kernel"
+# the calibration copy kernel that bench.py --copy-probe launches
+COPY_KERNEL_PATTERN = "probe_copy_kernel"
 
 
 def source_digest() -> str:

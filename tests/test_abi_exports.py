@@ -76,10 +76,11 @@ def test_workspace_errors_without_gpu():
         rc = lib.dsa_sparse_attend(ctypes.byref(dims), 1, fake, fake, 576, fake, 576, fake,
                                    None, None, fake, None, ws, nb, None)
         assert rc == -4, rc
-    # the per-head kernel's selection bitmap
+    # the per-head kernel's tile-major selection bitmap (300 queries padded
+    # to 512, 10 words of keys) and its fp16 copy of V
     dims = binding._AttnDims(1, 300, 300, 8, 192, 256, 8, 40, 192 ** -0.5)
     need = lib.dsa_sparse_attend_workspace_size(ctypes.byref(dims))
-    assert need == 300 * ((300 + 31) // 32) * 4
+    assert need >= 512 * 10 * 4 + 300 * 8 * 256 * 2
     rc = lib.dsa_sparse_attend(ctypes.byref(dims), 1, fake, fake, 8 * 192, fake, 8 * 256, fake,
                                None, None, fake, None, fake, need - 4, None)
     assert rc == -4, rc

@@ -16,11 +16,11 @@ def test_traffic_record_round_trip(tmp_path):
     fetch = tmp_path / "f.csv"
     write = tmp_path / "w.csv"
     hdr = "Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n"
-    fetch.write_text(hdr + "1,void at::native::neg_kernel_cuda(float),FETCH_SIZE,512\n"
+    fetch.write_text(hdr + "1,probe_copy_kernel(uint4 const*),FETCH_SIZE,512\n"
                      "2,dsa::attend_gather_kernel(int),FETCH_SIZE,100\n"
                      "2,dsa::attend_gather_kernel(int),FETCH_SIZE,20\n"
                      "3,dsa::attend_gather_kernel(int),FETCH_SIZE,120\n")
-    write.write_text(hdr + "1,void at::native::neg_kernel_cuda(float),WRITE_SIZE,1024\n"
+    write.write_text(hdr + "1,probe_copy_kernel(uint4 const*),WRITE_SIZE,1024\n"
                      "2,dsa::attend_gather_kernel(int),WRITE_SIZE,8\n"
                      "3,dsa::attend_gather_kernel(int),WRITE_SIZE,8\n")
     text = ps.traffic(str(fetch), str(write), 1 << 20, "cmd f", "cmd w")
