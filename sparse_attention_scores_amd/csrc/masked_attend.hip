@@ -190,6 +190,52 @@ __device__ __forceinline__ int mk_swz_k(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int mk_swz_v(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 
 constexpr int MK_STAGES = 4;  // tiles resident in LDS (ring)
+constexpr int MK_AHEAD = 3;   // MFMAs between an operand read and its use
+
+// The matrix phase's stream of NP P.V steps and NQ Q.K^T k-steps: op j is a
+// P.V step while P.V is behind its share of the ops issued so far.
+template <int NP, int NQ>
+constexpr bool mk_is_pv(int j)
+{
+    int np = 0, nq = 0;
+    for (int x = 0; x <= j; ++x) {
+        const bool pv = nq >= NQ || (np < NP && np * NQ <= nq * NP);
+        if (x == j)
+            return pv;
+        if (pv)
+            ++np;
+        else
+            ++nq;
+    }
+    return false;
+}
+// index of op j among the ops of its own kind
+template <int NP, int NQ>
+constexpr int mk_index_of(int j)
+{
+    int c = 0;
+    for (int x = 0; x < j; ++x)
+        c += mk_is_pv<NP, NQ>(x) == mk_is_pv<NP, NQ>(j);
+    return c;
+}
+// LDS read instructions of ops j0 .. j1 (a P.V step reads twice, a Q.K^T
+// k-step once)
+template <int NP, int NQ>
+constexpr int mk_reads_between(int j0, int j1)
+{
+    int c = 0;
+    for (int y = j0; y <= j1 && y < NP + NQ; ++y)
+        c += mk_is_pv<NP, NQ>(y) ? 2 : 1;
+    return c;
+}
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void mk_unroll(F &f)
+{
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        mk_unroll<N, I + 1>(f);
+    }
+}
 
 template <int KD, int VD>
 struct __attribute__((aligned(16))) MaskedSmem {
@@ -199,6 +245,25 @@ struct __attribute__((aligned(16))) MaskedSmem {
     unsigned char v[MK_STAGES][VB];
     uint32_t mw[MK_STAGES][MK_QB];              // the block's mask words of the tile
 };
+
+// Direct-to-LDS 16-byte load per lane from a scalar base plus a 32-bit lane
+// offset (global_load_lds_dwordx4, saddr form) into LDS bytes lds_dst + 16 *
+// lane.  Written as asm so the compiler neither hoists base + offset out of
+// the tile loop as 64-bit registers nor merges the K, V and mask loads into
+// one load with selected operands; M0 carries the LDS address (one wait
+// state after writing it).  Completion is tracked with vm_wait.
+// (The compiler keeps M0 reserved and warns that the clobber is not
+// honoured; no other code of these kernels uses M0.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16_s(const void *sbase, uint32_t voff, uint32_t lds_dst)
+{
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(lds_dst)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
 __device__ __forceinline__ f32x16_t mfma_32x32x16_f16(const u32x4_t &a, const u32x4_t &b,
                                                       f32x16_t c)
@@ -329,35 +394,70 @@ __global__ __launch_bounds__(512, 1) void attend_masked_kernel(
     const unsigned char *mb = reinterpret_cast<const unsigned char *>(
         mask + (int64_t)b * nw * q_pad + q0);
     const uint32_t ksr2 = (uint32_t)(ksr * 2), vsr2 = (uint32_t)(H * VD * 2);
-    const uint32_t q_pad4 = (uint32_t)q_pad * 4u;
+    const uint64_t q_pad4 = (uint64_t)q_pad * 4u;
     // this wave's load slots: 4w .. 4w+3 of the tile's 29
     const int n_mine = min(4, NSLOT - 4 * wid);
 
-    // DMA of tile t into stage st: slot s < 12 fills K chunk row, 12..27 V,
-    // 28 the mask words; lane l of a slot fills LDS bytes 16l of that KB =
-    // (row, physical chunk), fetching the row's logical chunk (addresses
-    // recomputed per tile: a few VALU instead of live registers)
+    // Load slot s of a tile: s < 12 fills K bytes 1 KB * s, 12..27 V bytes
+    // 1 KB * (s - 12), 28 the block's mask words.  Lane l of a slot fills LDS
+    // bytes 16l of that KB = (row, physical chunk) and fetches the row's
+    // logical chunk; its byte offset from the tile's first key row is the
+    // same for every tile, so each load is a scalar tile base plus this
+    // per-lane constant.
+    uint32_t voff[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int s_ = 4 * wid + j;
+        if (s_ < NK_DMA) {
+            const int c = s_ * 64 + lane, r = c / KCH;
+            voff[j] = (uint32_t)r * ksr2 + (uint32_t)(((c % KCH) ^ mk_swz_k(r)) * 16);
+        } else if (s_ < NK_DMA + NV_DMA) {
+            const int c = (s_ - NK_DMA) * 64 + lane, r = c / VCH;
+            voff[j] = (uint32_t)r * vsr2 + (uint32_t)(((c % VCH) ^ mk_swz_v(r)) * 16);
+        } else {
+            voff[j] = 16u * (uint32_t)lane;
+        }
+    }
+    const uint32_t lds_k0 = __builtin_amdgcn_readfirstlane(lds_addr(sm.k[0])),
+                   lds_v0 = __builtin_amdgcn_readfirstlane(lds_addr(sm.v[0])),
+                   lds_m0 = __builtin_amdgcn_readfirstlane(lds_addr(&sm.mw[0][0]));
+    // DMA of tile t into stage st; the last tile of a row whose length is
+    // not a multiple of 32 clamps its rows past n_k to the last key (those
+    // keys are masked) with addresses computed per lane
     auto dma_tile = [&](int t, int st) {
         const int k0 = t * MK_TILE;
+        const bool full = k0 + MK_TILE <= n_k;
+        const unsigned char *ks_ = kb + (uint64_t)(uint32_t)k0 * ksr2;
+        const unsigned char *vs_ = vb + (uint64_t)(uint32_t)k0 * vsr2;
+        const unsigned char *ms_ = mb + (uint64_t)(uint32_t)t * q_pad4;
+        const uint32_t lk = lds_k0 + st * Sm::KB, lv = lds_v0 + st * Sm::VB,
+                       lm = lds_m0 + st * (MK_QB * 4);
+        // the clamped addresses of a partial tile derive from an opaque copy
+        // of the lane index, so none of them is hoisted out of the loop
         int ln = lane;
-        asm volatile("" : "+v"(ln));
+        if (!full)
+            asm volatile("" : "+v"(ln));
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int s_ = 4 * wid + j;
             if (s_ < NK_DMA) {
-                const int c = s_ * 64 + ln, r = c / KCH;
-                const int key = min(k0 + r, n_k - 1);  // rows past n_k are masked
-                lds_dma16(kb + (uint64_t)(uint32_t)key * ksr2 +
-                              (uint32_t)(((c % KCH) ^ mk_swz_k(r)) * 16),
-                          sm.k[st] + s_ * 1024);
+                uint32_t o = voff[j];
+                if (!full) {
+                    const int c = s_ * 64 + ln, r = c / KCH;
+                    o = (uint32_t)(min(k0 + r, n_k - 1) - k0) * ksr2 +
+                        (uint32_t)(((c % KCH) ^ mk_swz_k(r)) * 16);
+                }
+                lds_dma16_s(ks_, o, lk + s_ * 1024);
             } else if (s_ < NK_DMA + NV_DMA) {
-                const int c = (s_ - NK_DMA) * 64 + ln, r = c / VCH;
-                const int key = min(k0 + r, n_k - 1);
-                lds_dma16(vb + (uint64_t)(uint32_t)key * vsr2 +
-                              (uint32_t)(((c % VCH) ^ mk_swz_v(r)) * 16),
-                          sm.v[st] + (s_ - NK_DMA) * 1024);
+                uint32_t o = voff[j];
+                if (!full) {
+                    const int c = (s_ - NK_DMA) * 64 + ln, r = c / VCH;
+                    o = (uint32_t)(min(k0 + r, n_k - 1) - k0) * vsr2 +
+                        (uint32_t)(((c % VCH) ^ mk_swz_v(r)) * 16);
+                }
+                lds_dma16_s(vs_, o, lv + (s_ - NK_DMA) * 1024);
             } else if (s_ < NSLOT) {
-                lds_dma16(mb + (uint64_t)t * q_pad4 + 16u * (uint32_t)ln, &sm.mw[st][0]);
+                lds_dma16_s(ms_, voff[j], lm);
             }
         }
     };
@@ -395,79 +495,61 @@ __global__ __launch_bounds__(512, 1) void attend_masked_kernel(
     const uint32_t lds_k = lds_addr(sm.k[0]), lds_v = lds_addr(sm.v[0]);
     const uint32_t lds_mw = lds_addr(&sm.mw[0][0]) + 4u * (uint32_t)(wid * 32 + col);
 
-    // Q.K^T for the 32 keys of the tile in stage st
-    auto qk = [&](int st) {
-        f32x16_t s = {};
-        const uint32_t kt = lds_k + st * Sm::KB;
-        // k-step ks reads base kq[ks & 3] + 128 * (ks >> 2); the reads run
-        // two k-steps ahead of the MFMAs that use them
-        u32x4_t a[KS];
-        lds_read_b128_nowait<0>(a[0], kt + kq[0]);
-        lds_read_b128_nowait<0>(a[1], kt + kq[1]);
-        auto step = [&](auto KSc) {
-            constexpr int ks = decltype(KSc)::value;
-            if constexpr (ks + 2 < KS) {
-                lds_read_b128_nowait<128 * ((ks + 2) >> 2)>(a[ks + 2], kt + kq[(ks + 2) & 3]);
-                lds_operand_wait<2>(a[ks]);
-            } else if constexpr (ks + 1 < KS) {
-                lds_operand_wait<1>(a[ks]);
-            } else {
-                lds_operand_wait<0>(a[ks]);
-            }
-            s = mfma_32x32x16(a[ks], qf[ks], s);
-        };
-        static_assert(KS == 12, "twelve k-steps");
-        step(std::integral_constant<int, 0>{});
-        step(std::integral_constant<int, 1>{});
-        step(std::integral_constant<int, 2>{});
-        step(std::integral_constant<int, 3>{});
-        step(std::integral_constant<int, 4>{});
-        step(std::integral_constant<int, 5>{});
-        step(std::integral_constant<int, 6>{});
-        step(std::integral_constant<int, 7>{});
-        step(std::integral_constant<int, 8>{});
-        step(std::integral_constant<int, 9>{});
-        step(std::integral_constant<int, 10>{});
-        step(std::integral_constant<int, 11>{});
-        return s;
-    };
+    f32x16_t s = {};
+    u32x4_t p0 = {}, p1 = {};  // P^T of the previous tile (fp16, both key halves)
 
-    // O^T[c][query] += V^T[c][keys] P^T[keys][query] for the tile in stage
-    // st: step T (kh = T >> 3, column tile n = T & 7) reads V^T rows ra / rb
-    // of key half kh at column tile n: bases va_/vb_[n & 3], immediate
-    // 256 * (n >> 2) + 16 rows * kh; the reads run two steps ahead of the
-    // MFMAs that use them
-    auto pv = [&](int st, const u32x4_t &p0, const u32x4_t &p1) {
-        const uint32_t vt = lds_v + st * Sm::VB;
+    // Matrix phase: P.V of the tile in stage sv and Q.K^T of the tile in
+    // stage sk as one stream of MFMAs, P.V steps and
+    // Q.K^T k-steps interleaved, every operand read issued MK_AHEAD MFMAs
+    // before the MFMA that uses it (the two read kinds share the LDS counter,
+    // so each wait counts the reads issued after its own).
+    //  P.V step T: column tile n = T & 7 of key half T >> 3, two transposing
+    //  reads of V^T rows ra / rb (bases va_/vb_[n & 3], immediate
+    //  256 * (n >> 2) + 16 rows * 512 for the key half).
+    //  Q.K^T k-step ks: one read of K rows at base kq[ks & 3], immediate
+    //  128 * (ks >> 2).
+    auto m_phase = [&](int sv, int sk) {
+        constexpr int NP = 2 * NCT, NQ = KS, N = NP + NQ;
+        const uint32_t vt = lds_v + sv * Sm::VB, kt = lds_k + sk * Sm::KB;
         u32x2_t ra2[2 * NCT], rb2[2 * NCT];
-        auto rd = [&](auto Tc) {
-            constexpr int T = decltype(Tc)::value, n = T & 7, kh = T >> 3;
-            constexpr int o = 256 * (n >> 2) + kh * 16 * VD * 2;
-            lds_read_tr16_nowait<o>(ra2[T], vt + va_[n & 3]);
-            lds_read_tr16_nowait<o>(rb2[T], vt + vb_[n & 3]);
-        };
-        auto step = [&](auto Tc) {
-            constexpr int T = decltype(Tc)::value, n = T & 7;
-            constexpr int NS = 2 * NCT;
-            if constexpr (T + 2 < NS) {
-                rd(std::integral_constant<int, T + 2>{});
-                lds_operand_wait<4>(ra2[T], rb2[T]);
-            } else {
-                lds_operand_wait<2 * (NS - 1 - T)>(ra2[T], rb2[T]);
+        u32x4_t a[KS];
+        auto issue = [&](auto Jc) {
+            constexpr int J = decltype(Jc)::value;
+            if constexpr (J < N) {
+                constexpr int x = mk_index_of<NP, NQ>(J);
+                if constexpr (mk_is_pv<NP, NQ>(J)) {
+                    constexpr int n = x & 7, kh = x >> 3;
+                    constexpr int o = 256 * (n >> 2) + kh * 16 * VD * 2;
+                    lds_read_tr16_nowait<o>(ra2[x], vt + va_[n & 3]);
+                    lds_read_tr16_nowait<o>(rb2[x], vt + vb_[n & 3]);
+                } else {
+                    lds_read_b128_nowait<128 * (x >> 2)>(a[x], kt + kq[x & 3]);
+                }
             }
-            const u32x4_t av = {ra2[T][0], ra2[T][1], rb2[T][0], rb2[T][1]};
-            oacc[n] = mfma_32x32x16_f16(av, (T >> 3) ? p1 : p0, oacc[n]);
         };
-        static_assert(NCT == 8, "eight column tiles");
-        rd(std::integral_constant<int, 0>{});
-        rd(std::integral_constant<int, 1>{});
-#define MK_PV_STEP(T) step(std::integral_constant<int, T>{});
-        MK_PV_STEP(0) MK_PV_STEP(1) MK_PV_STEP(2) MK_PV_STEP(3) MK_PV_STEP(4) MK_PV_STEP(5)
-        MK_PV_STEP(6) MK_PV_STEP(7) MK_PV_STEP(8) MK_PV_STEP(9) MK_PV_STEP(10) MK_PV_STEP(11)
-        MK_PV_STEP(12) MK_PV_STEP(13) MK_PV_STEP(14) MK_PV_STEP(15)
-#undef MK_PV_STEP
+        auto op = [&](auto Jc) {
+            constexpr int J = decltype(Jc)::value;
+            issue(std::integral_constant<int, J + MK_AHEAD>{});
+            constexpr int after = mk_reads_between<NP, NQ>(J + 1, J + MK_AHEAD);
+            constexpr int x = mk_index_of<NP, NQ>(J);
+            if constexpr (mk_is_pv<NP, NQ>(J)) {
+                lds_operand_wait<after>(ra2[x], rb2[x]);
+                const u32x4_t av = {ra2[x][0], ra2[x][1], rb2[x][0], rb2[x][1]};
+                oacc[x & 7] = mfma_32x32x16_f16(av, (x >> 3) ? p1 : p0, oacc[x & 7]);
+            } else {
+                lds_operand_wait<after>(a[x]);
+                s = mfma_32x32x16(a[x], qf[x], s);
+            }
+        };
+        s = f32x16_t{};
+        mk_unroll<MK_AHEAD>(issue);
+        mk_unroll<N>(op);
     };
 
+    // the first matrix phase runs P.V with zero weights over the last stage,
+    // which no tile has filled yet: clear its V so that 0 * V stays 0
+    for (int i = tid; i < Sm::VB / 16; i += 512)
+        reinterpret_cast<u32x4_t *>(sm.v[MK_STAGES - 1])[i] = u32x4_t{0u, 0u, 0u, 0u};
     // the Q fragments and ranges are in registers before the first tile DMA
     vm_wait<0>();
     for (int j = 0; j < MK_STAGES - 1 && T0 + j < T1; ++j)
@@ -478,30 +560,33 @@ __global__ __launch_bounds__(512, 1) void attend_masked_kernel(
     if (grp_b)
         lds_barrier();  // waves 4-7 start half an iteration behind
 
-    f32x16_t s = {};
-    u32x4_t p0 = {}, p1 = {};  // P^T of the previous tile (fp16, both key halves)
     bool act_prev = false;
     for (int t = T0; t <= T1; ++t) {
         const int st = (t - T0) % MK_STAGES;
+        const int sp = (st + MK_STAGES - 1) % MK_STAGES;
         // ---------------- matrix phase: P.V of tile t-1, Q.K^T of tile t
-        if (!grp_b && t - 1 >= T0 && t + MK_STAGES - 2 < T1)
-            dma_tile(t + MK_STAGES - 2, (t + MK_STAGES - 2 - T0) % MK_STAGES);
         uint32_t word = 0u;
         bool act = false;
         if (t < T1) {
             word = mk_read_word(lds_mw + st * (MK_QB * 4));
             act = __any(word != 0u);
         }
-        if (act_prev)
-            pv((st + MK_STAGES - 1) % MK_STAGES, p0, p1);
-        if (act)
-            s = qk(st);
+        // one instruction stream for both products keeps the register
+        // allocation within 256: an inactive previous tile contributes zero
+        // weights (P = 0 against finite V), and the scores of an inactive
+        // tile are not used
+        if (act_prev || act)
+            m_phase(sp, st);
         if (grp_b && t + 1 < T1)
             wait_tile(min(T1 - 1, t + MK_STAGES - 2) - (t + 1));
         lds_barrier();
         if (t == T1)
             break;
-        // ---------------- vector phase: the softmax of tile t
+        // ---------------- vector phase: tile loads, then the softmax of tile t
+        // (waves 0-3 refill the stage that held tile t-2, waves 4-7 the one
+        // that held tile t-1: both are done with it by now)
+        if (!grp_b && t > T0 && t + MK_STAGES - 2 < T1)
+            dma_tile(t + MK_STAGES - 2, (t + MK_STAGES - 2 - T0) % MK_STAGES);
         if (grp_b && t + MK_STAGES - 1 < T1)
             dma_tile(t + MK_STAGES - 1, (t + MK_STAGES - 1 - T0) % MK_STAGES);
         if (act) {
@@ -558,6 +643,9 @@ __global__ __launch_bounds__(512, 1) void attend_masked_kernel(
                          cvt_pk_f16(p[4], p[5]), cvt_pk_f16(p[6], p[7])};
             p1 = u32x4_t{cvt_pk_f16(p[8], p[9]), cvt_pk_f16(p[10], p[11]),
                          cvt_pk_f16(p[12], p[13]), cvt_pk_f16(p[14], p[15])};
+        } else {
+            p0 = u32x4_t{0u, 0u, 0u, 0u};
+            p1 = p0;
         }
         act_prev = act;
         if (!grp_b && t + 1 < T1)
