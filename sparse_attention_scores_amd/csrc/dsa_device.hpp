@@ -142,6 +142,17 @@ __device__ __forceinline__ void lds_read_b128_nowait(u32x4_t &v, uint32_t a)
 {
     asm volatile("ds_read_b128 %0, %1 offset:%2" : "=&v"(v) : "v"(a), "i"(O) : "memory");
 }
+template <int O>
+__device__ __forceinline__ void lds_read_b32_nowait(uint32_t &v, uint32_t a)
+{
+    asm volatile("ds_read_b32 %0, %1 offset:%2" : "=&v"(v) : "v"(a), "i"(O) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void lds_operand_wait(uint32_t &v)
+{
+    static_assert(N >= 0 && N < 16, "lgkmcnt is 4 bits");
+    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(v) : "n"(N) : "memory");
+}
 // Transposing 4 x 16-bit read (ds_read_b64_tr_b16) issued now, waited for
 // by lds_operand_wait on the pair it belongs to.
 template <int O>

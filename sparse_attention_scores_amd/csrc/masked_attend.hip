@@ -190,7 +190,7 @@ __device__ __forceinline__ int mk_swz_k(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int mk_swz_v(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 
 constexpr int MK_STAGES = 4;  // tiles resident in LDS (ring)
-constexpr int MK_AHEAD = 3;   // MFMAs between an operand read and its use
+constexpr int MK_AHEAD = 5;   // MFMAs between an operand read and its use
 
 // The matrix phase's stream of NP P.V steps and NQ Q.K^T k-steps: op j is a
 // P.V step while P.V is behind its share of the ops issued so far.
@@ -424,7 +424,8 @@ __global__ __launch_bounds__(512, 1) void attend_masked_kernel(
     // DMA of tile t into stage st; the last tile of a row whose length is
     // not a multiple of 32 clamps its rows past n_k to the last key (those
     // keys are masked) with addresses computed per lane
-    auto dma_tile = [&](int t, int st) {
+    auto dma_tile = [&](int t, auto STc) {
+        constexpr int st = decltype(STc)::value;
         const int k0 = t * MK_TILE;
         const bool full = k0 + MK_TILE <= n_k;
         const unsigned char *ks_ = kb + (uint64_t)(uint32_t)k0 * ksr2;
@@ -494,6 +495,12 @@ __global__ __launch_bounds__(512, 1) void attend_masked_kernel(
     }
     const uint32_t lds_k = lds_addr(sm.k[0]), lds_v = lds_addr(sm.v[0]);
     const uint32_t lds_mw = lds_addr(&sm.mw[0][0]) + 4u * (uint32_t)(wid * 32 + col);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        kq[j] += lds_k;
+        va_[j] += lds_v;
+        vb_[j] += lds_v;
+    }
 
     f32x16_t s = {};
     u32x4_t p0 = {}, p1 = {};  // P^T of the previous tile (fp16, both key halves)
@@ -508,9 +515,11 @@ __global__ __launch_bounds__(512, 1) void attend_masked_kernel(
     //  256 * (n >> 2) + 16 rows * 512 for the key half).
     //  Q.K^T k-step ks: one read of K rows at base kq[ks & 3], immediate
     //  128 * (ks >> 2).
-    auto m_phase = [&](int sv, int sk) {
+    auto m_phase = [&](auto SVc, auto SKc) {
+        constexpr int SV = decltype(SVc)::value, SK = decltype(SKc)::value;
         constexpr int NP = 2 * NCT, NQ = KS, N = NP + NQ;
-        const uint32_t vt = lds_v + sv * Sm::VB, kt = lds_k + sk * Sm::KB;
+        // every LDS address is a per-lane register plus an immediate (the
+        // stage is a compile-time constant of the unrolled loop)
         u32x2_t ra2[2 * NCT], rb2[2 * NCT];
         u32x4_t a[KS];
         auto issue = [&](auto Jc) {
@@ -519,11 +528,11 @@ __global__ __launch_bounds__(512, 1) void attend_masked_kernel(
                 constexpr int x = mk_index_of<NP, NQ>(J);
                 if constexpr (mk_is_pv<NP, NQ>(J)) {
                     constexpr int n = x & 7, kh = x >> 3;
-                    constexpr int o = 256 * (n >> 2) + kh * 16 * VD * 2;
-                    lds_read_tr16_nowait<o>(ra2[x], vt + va_[n & 3]);
-                    lds_read_tr16_nowait<o>(rb2[x], vt + vb_[n & 3]);
+                    constexpr int o = SV * Sm::VB + 256 * (n >> 2) + kh * 16 * VD * 2;
+                    lds_read_tr16_nowait<o>(ra2[x], va_[n & 3]);
+                    lds_read_tr16_nowait<o>(rb2[x], vb_[n & 3]);
                 } else {
-                    lds_read_b128_nowait<128 * (x >> 2)>(a[x], kt + kq[x & 3]);
+                    lds_read_b128_nowait<SK * Sm::KB + 128 * (x >> 2)>(a[x], kq[x & 3]);
                 }
             }
         };
@@ -552,45 +561,67 @@ __global__ __launch_bounds__(512, 1) void attend_masked_kernel(
         reinterpret_cast<u32x4_t *>(sm.v[MK_STAGES - 1])[i] = u32x4_t{0u, 0u, 0u, 0u};
     // the Q fragments and ranges are in registers before the first tile DMA
     vm_wait<0>();
-    for (int j = 0; j < MK_STAGES - 1 && T0 + j < T1; ++j)
-        dma_tile(T0 + j, j);
+    {
+        auto pro = [&](auto Jc) {
+            constexpr int j = decltype(Jc)::value;
+            if (T0 + j < T1)
+                dma_tile(T0 + j, Jc);
+        };
+        mk_unroll<MK_STAGES - 1>(pro);
+    }
     if (T1 > T0)
         wait_tile(min(T1 - 1, T0 + MK_STAGES - 2) - T0);
     lds_barrier();  // tile T0 is in LDS for every wave
     if (grp_b)
         lds_barrier();  // waves 4-7 start half an iteration behind
 
+    // this wave's tiles: the union of its 32 queries' visible ranges (the
+    // mask words are zero outside it; inside it a tile none of the queries
+    // selects skips its softmax)
+    int tw_begin, tw_end;
+    {
+        int wl = q_ok ? (vlo ? max(vlo[row], 0) : 0) : n_k;
+        int wh = q_ok ? (vhi ? min(vhi[row], n_k) : n_k) : 0;
+        wl = (int)wave_min_u32((uint32_t)wl);
+        wh = (int)wave_max_u32((uint32_t)wh);
+        tw_begin = wl / MK_TILE;
+        tw_end = wh > wl ? (wh + MK_TILE - 1) / MK_TILE : tw_begin;
+    }
+
     bool act_prev = false;
-    for (int t = T0; t <= T1; ++t) {
-        const int st = (t - T0) % MK_STAGES;
-        const int sp = (st + MK_STAGES - 1) % MK_STAGES;
+    // One ping-pong iteration for tile t held in stage ST, a compile-time
+    // constant (the loop is unrolled over the ring); false after the final
+    // matrix phase.
+    auto iteration = [&](auto STc, int t) -> bool {
+        constexpr int ST = decltype(STc)::value;
+        constexpr int SP = (ST + MK_STAGES - 1) % MK_STAGES;
         // ---------------- matrix phase: P.V of tile t-1, Q.K^T of tile t
+        // (the mask word is read now and waited for after the phase)
         uint32_t word = 0u;
-        bool act = false;
-        if (t < T1) {
-            word = mk_read_word(lds_mw + st * (MK_QB * 4));
-            act = __any(word != 0u);
-        }
+        if (t < T1)
+            lds_read_b32_nowait<ST * MK_QB * 4>(word, lds_mw);
+        const bool act = t < T1 && t >= tw_begin && t < tw_end;
         // one instruction stream for both products keeps the register
         // allocation within 256: an inactive previous tile contributes zero
         // weights (P = 0 against finite V), and the scores of an inactive
         // tile are not used
         if (act_prev || act)
-            m_phase(sp, st);
+            m_phase(std::integral_constant<int, SP>{}, std::integral_constant<int, ST>{});
         if (grp_b && t + 1 < T1)
             wait_tile(min(T1 - 1, t + MK_STAGES - 2) - (t + 1));
         lds_barrier();
         if (t == T1)
-            break;
+            return false;
+        lds_operand_wait<0>(word);
         // ---------------- vector phase: tile loads, then the softmax of tile t
         // (waves 0-3 refill the stage that held tile t-2, waves 4-7 the one
         // that held tile t-1: both are done with it by now)
         if (!grp_b && t > T0 && t + MK_STAGES - 2 < T1)
-            dma_tile(t + MK_STAGES - 2, (t + MK_STAGES - 2 - T0) % MK_STAGES);
+            dma_tile(t + MK_STAGES - 2, std::integral_constant<int, (ST + MK_STAGES - 2) % MK_STAGES>{});
         if (grp_b && t + MK_STAGES - 1 < T1)
-            dma_tile(t + MK_STAGES - 1, (t + MK_STAGES - 1 - T0) % MK_STAGES);
-        if (act) {
-            // lane holds keys 8*(i/4) + 4g + i%4 of the tile for query qi;
+            dma_tile(t + MK_STAGES - 1, std::integral_constant<int, (ST + MK_STAGES - 1) % MK_STAGES>{});
+        const bool soft = act && __any(word != 0u);
+        if (soft) {            // lane holds keys 8*(i/4) + 4g + i%4 of the tile for query qi;
             // unselected keys become -inf (sign-extended bit as a bit mask)
             float x[16];
 #pragma unroll
@@ -634,7 +665,12 @@ __global__ __launch_bounds__(512, 1) void attend_masked_kernel(
             float p[16];
             float psum = 0.f;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
+            for (int i = 0; i < 8; ++i) {
+                p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], c_log2, -mc));
+                psum += p[i];
+            }
+#pragma unroll
+            for (int i = 8; i < 16; ++i) {
                 p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], c_log2, -mc));
                 psum += p[i];
             }
@@ -651,6 +687,17 @@ __global__ __launch_bounds__(512, 1) void attend_masked_kernel(
         if (!grp_b && t + 1 < T1)
             wait_tile(min(T1 - 1, t + MK_STAGES - 2) - (t + 1));
         lds_barrier();
+        return true;
+    };
+    for (int t = T0;; t += MK_STAGES) {
+        bool go = true;
+        auto step = [&](auto STc) {
+            if (go)
+                go = iteration(STc, t + decltype(STc)::value);
+        };
+        mk_unroll<MK_STAGES>(step);
+        if (!go)
+            break;
     }
     if (!grp_b)
         lds_barrier();  // the barrier count of waves 0-3 matches waves 4-7
