@@ -280,3 +280,82 @@ def sparse_attend(q, K, V, idx, scale, kv_heads, q_pos=None, pad=None, rows=None
     if rc != 0:
         raise ValueError("oracle sparse_attend: bad kv_heads")
     return out, lse
+
+
+# --------------------------------------------------------------------------
+# indexer-key cache write ("Another DSA attempt": the decode indexer-K cache
+# commit and the serving-correctness commit)
+# --------------------------------------------------------------------------
+
+def hadamard_rows(x, want_f64=False):
+    """Sylvester Hadamard rotation of each last-axis row, y = H x / sqrt(d):
+    returns y rounded once to float32 (and the float64 value)."""
+    xa, xt = _storage(x)
+    d = xa.shape[-1]
+    rows = int(np.prod(xa.shape[:-1])) if xa.ndim > 1 else 1
+    lib = _load()
+    lib.orc_hadamard_rows.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                                      ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    y32 = np.empty(xa.shape, np.float32)
+    y64 = np.empty(xa.shape, np.float64) if want_f64 else None
+    if lib.orc_hadamard_rows(_ptr(xa), xt, rows, d, _ptr(y64), _ptr(y32)) != 0:
+        raise ValueError("oracle hadamard_rows: d must be a power of two")
+    return (y32, y64) if want_f64 else y32
+
+
+def e4m3_encode(v):
+    """OCP e4m3fn codes (uint8) of float32 values: nearest, ties to even,
+    saturating at 448, sign kept."""
+    lib = _load()
+    lib.orc_e4m3_encode.argtypes = [ctypes.c_float]
+    lib.orc_e4m3_encode.restype = ctypes.c_uint8
+    a = np.asarray(v, np.float32)
+    return np.array([lib.orc_e4m3_encode(float(t)) for t in a.reshape(-1)],
+                    np.uint8).reshape(a.shape)
+
+
+def quantize_e4m3_rows(y):
+    """Per-row fp8: scale = max|row| / 448 (f32 division; 1 for a zero row),
+    codes = e4m3(y / scale).  y: [..., d] float32."""
+    ya = np.ascontiguousarray(np.asarray(y, np.float32))
+    d = ya.shape[-1]
+    rows = ya.size // d
+    lib = _load()
+    lib.orc_quantize_e4m3_rows.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                           ctypes.c_void_p, ctypes.c_void_p]
+    lib.orc_quantize_e4m3_rows.restype = None
+    codes = np.empty(ya.shape, np.uint8)
+    scales = np.empty(ya.shape[:-1], np.float32)
+    lib.orc_quantize_e4m3_rows(_ptr(ya), rows, d, _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def index_cache_write(k_new, kv_head, cache, scales=None):
+    """The cache after writing the rotated new keys of each sequence at its
+    kv_head: rows kv_head[b] .. kv_head[b] + n_new - 1 of sequence b get the
+    rotated rows (fp8 codes with their scales when `scales` is given, else
+    bf16 bits); rows outside [0, n_cache) are not written; every other row
+    keeps its value.  k_new: [B, n_new, d]; cache: [B, n_cache, d] uint8
+    (fp8 codes) or uint16 (bf16 bits); scales: [B, n_cache] float32 or None.
+    Returns new (cache, scales) arrays."""
+    y = hadamard_rows(k_new)
+    B, n_new, d = y.shape
+    cache = np.array(cache, copy=True)
+    scales = None if scales is None else np.array(scales, np.float32, copy=True)
+    if scales is not None:
+        codes, sc = quantize_e4m3_rows(y)
+    else:
+        import torch
+        bits = torch.from_numpy(y).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    n_cache = cache.shape[1]
+    heads = np.asarray(kv_head, np.int64).reshape(B)
+    for b in range(B):
+        for i in range(n_new):
+            r = int(heads[b]) + i
+            if 0 <= r < n_cache:
+                if scales is not None:
+                    cache[b, r] = codes[b, i]
+                    scales[b, r] = sc[b, i]
+                else:
+                    cache[b, r] = bits[b, i]
+    return cache, scales

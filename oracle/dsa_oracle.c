@@ -449,6 +449,103 @@ int orc_sparse_attend(int64_t B, int64_t Tq, int64_t Tk, int64_t H, int64_t kd,
     return 0;
 }
 
+/* ------------------------------------------------------------------------ */
+/* Indexer-key cache write.                                                  */
+/*                                                                           */
+/* "Another DSA attempt" (ik_llama.cpp PR #2063), the commit message of the  */
+/* decode indexer-K cache: the batch's indexer keys are Walsh-Hadamard       */
+/* rotated -- orthonormal, so scores are unchanged -- and written into the   */
+/* per-layer key cache at kv_head, from where scoring reads all past keys;   */
+/* the queries get the same rotation.  The serving-correctness commit: the   */
+/* rotation is the Sylvester construction, symmetric and orthonormal         */
+/* (H*H = I).  The cache stores one fp8 e4m3 row with one f32 scale per key  */
+/* (readings: scale = max|row| / 448, round to nearest even, saturating).    */
+/* ------------------------------------------------------------------------ */
+
+/* Entry (i, j) of the Sylvester Hadamard matrix of order 2^k: the sign
+ * (-1)^(number of bit positions set in both i and j). */
+static double sylvester_entry(int64_t i, int64_t j)
+{
+    return (__builtin_popcountll((unsigned long long)(i & j)) & 1) ? -1.0 : 1.0;
+}
+
+/* y[r][i] = (1/sqrt(d)) * sum_j H[i][j] x[r][j], the sum in f64 in column
+ * order, then one multiplication by the f64 constant 1/sqrt(d).  y64 (may be
+ * NULL) gets the f64 value, y32 (may be NULL) that value rounded once to f32.
+ * d must be a power of two.  Returns -1 for a bad d. */
+int orc_hadamard_rows(const void *x, int dtype, int64_t rows, int64_t d, double *y64, float *y32)
+{
+    if (d <= 0 || (d & (d - 1)) != 0)
+        return -1;
+    const double c = 1.0 / sqrt((double)d);
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t i = 0; i < d; ++i) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < d; ++j)
+                acc += sylvester_entry(i, j) * load(x, dtype, r * d + j);
+            const double y = acc * c;
+            if (y64)
+                y64[r * d + i] = y;
+            if (y32)
+                y32[r * d + i] = (float)y;
+        }
+    }
+    return 0;
+}
+
+/* OCP e4m3fn code of a finite f32: the representable value nearest to v,
+ * ties to the code with an even last mantissa bit; magnitudes at or beyond
+ * the largest finite value (448) give 448 (saturation).  The sign of v is
+ * kept, so -0 and small negatives that round to zero give 0x80.  Found by
+ * scanning the 127 non-negative finite codes, which are increasing in
+ * value. */
+uint8_t orc_e4m3_encode(float v)
+{
+    const int neg = signbit(v) ? 1 : 0;
+    const double a = fabs((double)v);
+    int best = 126;
+    if (a < orc_e4m3_value(126)) {
+        for (int c = 0; c < 126; ++c) {
+            const double lo = orc_e4m3_value((uint8_t)c), hi = orc_e4m3_value((uint8_t)(c + 1));
+            if (a >= lo && a <= hi) {
+                const double dl = a - lo, dh = hi - a;
+                if (dl < dh)
+                    best = c;
+                else if (dh < dl)
+                    best = c + 1;
+                else
+                    best = (c & 1) ? c + 1 : c;
+                break;
+            }
+        }
+    }
+    return (uint8_t)(best | (neg << 7));
+}
+
+/* One fp8 row per key: s = max_i |y_i| / 448 as an f32 division (1 when the
+ * row is all zero), code_i = e4m3(y_i / s) with y_i / s an f32 division. */
+void orc_quantize_e4m3_rows(const float *y, int64_t rows, int64_t d, uint8_t *codes,
+                            float *scales)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        float mx = 0.f;
+        for (int64_t i = 0; i < d; ++i) {
+            const float a = fabsf(y[r * d + i]);
+            if (a > mx)
+                mx = a;
+        }
+        volatile float s = mx / 448.0f;  /* one f32 division, not fused away */
+        const float sc = mx > 0.f ? s : 1.0f;
+        scales[r] = sc;
+        for (int64_t i = 0; i < d; ++i) {
+            volatile float q = y[r * d + i] / sc;
+            codes[r * d + i] = orc_e4m3_encode(q);
+        }
+    }
+}
+
 int orc_max_threads(void)
 {
 #ifdef _OPENMP
