@@ -230,6 +230,54 @@ int dsa_sparse_attend(const dsa_attn_dims *d, int dtype, const void *q,
                       void *stream);
 
 /* ------------------------------------------------------------------------
+ * Walsh-Hadamard rotation and the indexer-key cache write.
+ *
+ * "Another DSA attempt" (ik_llama.cpp PR #2063), the commit message of the
+ * decode indexer-K cache: the batch's indexer keys are Walsh-Hadamard
+ * rotated and written into the per-layer indexer-key cache at kv_head, from
+ * where the indexer scores every past key; the queries get the same
+ * rotation, which leaves every score unchanged (orthonormal).  The
+ * serving-correctness commit: the rotation is the Sylvester construction,
+ * symmetric and orthonormal (H*H = I).
+ *
+ * Rotation: y = H_d x / sqrt(d) per row of d elements, H_d[i][j] =
+ * (-1)^popcount(i & j), computed with f64 sums and one f64 multiplication by
+ * 1/sqrt(d), then rounded once to f32 (exact rotation, correctly rounded,
+ * whenever the f64 sums are exact -- inputs whose magnitudes within a row
+ * span less than about 2^29).
+ * ------------------------------------------------------------------------ */
+
+/* out[r,:] = H_d in[r,:] / sqrt(d), stored as f32, or as bf16 rounded to
+ * nearest even from the f32 value.  in, out: [rows, d] device, F32 or BF16
+ * (in == out is allowed: each row is read whole before it is written).
+ * Envelope: d in {32, 64, 128, 256}. */
+int dsa_hadamard_rotate(int64_t rows, int32_t d, const void *in, int in_dtype,
+                        void *out, int out_dtype, void *stream);
+
+typedef struct {
+    int32_t batch, n_new, n_cache, head_dim;
+} dsa_cache_dims;
+
+/* Rotates the n_new new key rows of each sequence and writes them into the
+ * cache at that sequence's kv_head: row i of sequence b goes to cache row
+ * kv_head[b] + i.  FP8_E4M3 cache: per row s = max|y| / 448 (f32 division;
+ * 1 for an all-zero row), code = e4m3(y / s) (f32 division, OCP e4m3fn,
+ * round to nearest even), and k_scale[b, row] = s -- the keys
+ * dsa_index_scores reads as FP8 with k_scale.  BF16 cache: y rounded to
+ * nearest even.
+ * k_new:   [batch, n_new, head_dim] F32 or BF16
+ * kv_head: [batch] int32 device array
+ * cache:   [batch, n_cache, head_dim] FP8_E4M3 codes or BF16
+ * k_scale: [batch, n_cache] f32 for an FP8 cache, else NULL
+ * Rows that would land outside [0, n_cache) are not written (kv_head is a
+ * device value, so this cannot be checked before the launch); every other
+ * cache row and scale is left as it was.  Envelope: head_dim in
+ * {32, 64, 128, 256}. */
+int dsa_index_cache_write(const dsa_cache_dims *d, const void *k_new,
+                          int k_dtype, const int32_t *kv_head, void *cache,
+                          int cache_dtype, float *k_scale, void *stream);
+
+/* ------------------------------------------------------------------------
  * Pooled (kpool) variant.
  *
  * Sequence b has pad[b] left-padding tokens.  Pools start at the first

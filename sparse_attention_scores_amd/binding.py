@@ -42,6 +42,11 @@ class _AttnDims(ctypes.Structure):
                 ("scale", ctypes.c_float)]
 
 
+class _CacheDims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_new", ctypes.c_int32), ("n_cache", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32)]
+
+
 class _PoolDims(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("seq", ctypes.c_int32), ("n_q", ctypes.c_int32),
                 ("kpool", ctypes.c_int32), ("head_dim", ctypes.c_int32),
@@ -54,7 +59,7 @@ EXPORTS = ("dsa_last_error", "dsa_version", "dsa_visibility_ranges", "dsa_index_
            "dsa_topk_workspace_size", "dsa_topk", "dsa_topk_noalloc",
            "dsa_sparse_attend_workspace_size",
            "dsa_sparse_attend", "dsa_pool_keys", "dsa_pool_select_workspace_size",
-           "dsa_pool_select")
+           "dsa_pool_select", "dsa_hadamard_rotate", "dsa_index_cache_write")
 
 
 def _hip_runtimes_mapped():
@@ -102,6 +107,8 @@ def load():
         lib.dsa_pool_select_workspace_size.argtypes = [P]
         lib.dsa_pool_select_workspace_size.restype = SZ
         lib.dsa_pool_select.argtypes = [P, P, P, P, P, P, P, SZ, P]
+        lib.dsa_hadamard_rotate.argtypes = [I64, I32, P, ctypes.c_int, P, ctypes.c_int, P]
+        lib.dsa_index_cache_write.argtypes = [P, P, ctypes.c_int, P, P, ctypes.c_int, P, P]
         _lib = lib
         return lib
 
@@ -349,3 +356,35 @@ def pool_select(scores, pad, q_pos, kpool: int, select_k: int, out_width: int, o
                                   _p(_i32(q_pos)), _p(out_tok), _p(out_pools), None, 0,
                                   _stream()))
     return (out_tok, out_pools) if want_pools else out_tok
+
+
+def hadamard_rotate(x, out=None, out_dtype=None):
+    """y = H_d x / sqrt(d) over the last axis (Sylvester Hadamard), as f32 or
+    bf16 (default: x's dtype).  out may be x itself."""
+    _dev(x, out)
+    d = x.shape[-1]
+    rows = math.prod(x.shape[:-1])
+    if out is None:
+        out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
+    _shape(out, x.shape, "hadamard_rotate: out")
+    _check(load().dsa_hadamard_rotate(rows, d, _p(x), _dtype_code(x), _p(out), _dtype_code(out),
+                                      _stream()))
+    return out
+
+
+def index_cache_write(k_new, kv_head, cache, k_scale=None):
+    """Rotate the new indexer keys [B, n_new, d] and write them into the
+    cache [B, n_cache, d] (float8_e4m3fn with k_scale [B, n_cache], or bf16)
+    at each sequence's kv_head [B] (int32)."""
+    _dev(k_new, kv_head, cache, k_scale)
+    B, n_new, d = k_new.shape
+    if cache.dim() != 3 or cache.shape[0] != B or cache.shape[2] != d:
+        raise ValueError("index_cache_write: cache must be [B, n_cache, d]")
+    n_cache = cache.shape[1]
+    _shape(kv_head, (B,), "index_cache_write: kv_head", torch.int32)
+    _shape(k_scale, (B, n_cache), "index_cache_write: k_scale", torch.float32)
+    dims = _CacheDims(B, n_new, n_cache, d)
+    _check(load().dsa_index_cache_write(ctypes.byref(dims), _p(k_new), _dtype_code(k_new),
+                                        _p(kv_head), _p(cache), _dtype_code(cache), _p(k_scale),
+                                        _stream()))
+    return cache, k_scale

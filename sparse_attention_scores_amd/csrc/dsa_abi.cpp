@@ -299,6 +299,58 @@ int dsa_sparse_attend(const dsa_attn_dims *d, int dtype, const void *q, const vo
     return hip_status(dsa::launch_attend(a, as_stream(stream)), "dsa_sparse_attend");
 }
 
+int dsa_hadamard_rotate(int64_t rows, int32_t d, const void *in, int in_dtype, void *out,
+                        int out_dtype, void *stream)
+{
+    if (rows < 0)
+        return fail(DSA_ERR_ARG, "dsa_hadamard_rotate: negative row count");
+    if (!dsa::hadamard_supported(d))
+        return fail(DSA_ERR_UNSUPPORTED, "dsa_hadamard_rotate: d must be 32, 64, 128 or 256 (got %d)",
+                    d);
+    if ((in_dtype != DSA_F32 && in_dtype != DSA_BF16) ||
+        (out_dtype != DSA_F32 && out_dtype != DSA_BF16))
+        return fail(DSA_ERR_ARG, "dsa_hadamard_rotate: dtypes must be F32 or BF16");
+    if (rows * d > kMaxElems)
+        return fail(DSA_ERR_UNSUPPORTED, "dsa_hadamard_rotate: too many rows");
+    if (rows == 0)
+        return ok();
+    if (!in || !out)
+        return fail(DSA_ERR_ARG, "dsa_hadamard_rotate: null pointer");
+    return hip_status(dsa::launch_hadamard_rotate(in, in_dtype == DSA_F32, out, out_dtype == DSA_F32,
+                                                  rows, d, as_stream(stream)),
+                      "dsa_hadamard_rotate");
+}
+
+int dsa_index_cache_write(const dsa_cache_dims *d, const void *k_new, int k_dtype,
+                          const int32_t *kv_head, void *cache, int cache_dtype, float *k_scale,
+                          void *stream)
+{
+    if (!d)
+        return fail(DSA_ERR_ARG, "dsa_index_cache_write: dims is NULL");
+    if (d->batch < 0 || d->n_new < 0 || d->n_cache < 0)
+        return fail(DSA_ERR_ARG, "dsa_index_cache_write: negative size");
+    if (!dsa::hadamard_supported(d->head_dim))
+        return fail(DSA_ERR_UNSUPPORTED,
+                    "dsa_index_cache_write: head_dim must be 32, 64, 128 or 256 (got %d)",
+                    d->head_dim);
+    if (k_dtype != DSA_F32 && k_dtype != DSA_BF16)
+        return fail(DSA_ERR_ARG, "dsa_index_cache_write: k_new must be F32 or BF16");
+    if (cache_dtype != DSA_FP8_E4M3 && cache_dtype != DSA_BF16)
+        return fail(DSA_ERR_ARG, "dsa_index_cache_write: the cache must be FP8_E4M3 or BF16");
+    if ((cache_dtype == DSA_FP8_E4M3) != (k_scale != nullptr))
+        return fail(DSA_ERR_ARG, "dsa_index_cache_write: k_scale goes with (only) an FP8 cache");
+    if ((int64_t)d->batch * d->n_cache * d->head_dim > kMaxElems ||
+        (int64_t)d->batch * d->n_new * d->head_dim > kMaxElems)
+        return fail(DSA_ERR_UNSUPPORTED, "dsa_index_cache_write: tensors too large");
+    if ((int64_t)d->batch * d->n_new == 0)
+        return ok();
+    if (!k_new || !kv_head || !cache)
+        return fail(DSA_ERR_ARG, "dsa_index_cache_write: null pointer");
+    dsa::CacheWriteArgs a{d->batch, d->n_new, d->n_cache, d->head_dim, k_new, k_dtype == DSA_F32,
+                          kv_head, cache, cache_dtype == DSA_FP8_E4M3, k_scale};
+    return hip_status(dsa::launch_index_cache_write(a, as_stream(stream)), "dsa_index_cache_write");
+}
+
 static int pool_dims_ok(const dsa_pool_dims *d, const char *fn)
 {
     if (!d)

@@ -58,6 +58,20 @@ size_t attend_masked_workspace_bytes(const AttendArgs &a);
 hipError_t launch_attend_masked(const AttendArgs &a, hipStream_t st);
 hipError_t launch_attend(const AttendArgs &a, hipStream_t st);
 
+struct CacheWriteArgs {
+    int batch, n_new, n_cache, head_dim;
+    const void *k_new;
+    bool k_f32;
+    const int32_t *kv_head;
+    void *cache;
+    bool fp8;
+    float *scales;
+};
+bool hadamard_supported(int d);
+hipError_t launch_hadamard_rotate(const void *x, bool x_f32, void *out, bool out_f32, int64_t rows,
+                                  int d, hipStream_t st);
+hipError_t launch_index_cache_write(const CacheWriteArgs &a, hipStream_t st);
+
 struct RangeArgs {
     int batch, n_q, kpool;
     const int32_t *pad, *q_pos;
