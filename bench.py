@@ -67,6 +67,8 @@ WORKLOAD_NAME = {1: "tiny_fp32_64", 2: "decode_b32x8192", 3: "prefill_4096",
 
 # the kernels each ABI call of a stage launches (substrings of their names)
 STAGE_KERNELS = {
+    "rotate_q": ("hadamard_rotate_kernel",),
+    "cache_write": ("index_cache_write_kernel",),
     "index": ("index_scores",),
     "topk": ("topk_seg_kernel", "topk_chunk_kernel", "topk_merge_kernel",
              "topk_merge_seg_kernel"),
@@ -193,11 +195,21 @@ def _parse():
 
 
 class Step:
-    """Preallocated buffers and the three ABI calls of one layer step."""
+    """Preallocated buffers and the ABI calls of one layer step: index scores,
+    top-k and attention; with an fp8 indexer-key cache (the long-context
+    decode workload) the step first rotates the queries and writes the new
+    token's rotated key into the cache at its row (write-then-score)."""
 
     def __init__(self, dsa, inp):
         import torch
         self.dsa, self.inp = dsa, inp
+        self.cached = inp.get("k_new") is not None
+        self.stages = (("rotate_q", "cache_write") if self.cached else ()) + ("index", "topk",
+                                                                              "attend")
+        self.q_used = torch.empty_like(inp["q_idx"]) if self.cached else inp["q_idx"]
+        if self.cached:
+            B, Tk = inp["B"], inp["Tk"]
+            self.kv_head = torch.full((B,), Tk - 1, dtype=torch.int32, device=inp["q_pos"].device)
         self.lo, self.hi = dsa.visibility_ranges(inp["pad"], inp["q_pos"])
         B, Tq, Tk = inp["B"], inp["Tq"], inp["Tk"]
         dev = inp["q_pos"].device
@@ -219,9 +231,16 @@ class Step:
             na = dsa.sparse_attend_workspace_size(dims)
             self.ws_attn = torch.empty(max(na, 1), dtype=torch.uint8, device=dev)
 
+    def rotate_q(self):
+        self.dsa.hadamard_rotate(self.inp["q_idx"], out=self.q_used)
+
+    def cache_write(self):
+        i = self.inp
+        self.dsa.index_cache_write(i["k_new"], self.kv_head, i["k_idx"], i["k_scale"])
+
     def index(self):
         i = self.inp
-        self.dsa.index_scores(i["q_idx"], i["k_idx"], i["w"], self.lo, self.hi, i["scale_idx"],
+        self.dsa.index_scores(self.q_used, i["k_idx"], i["w"], self.lo, self.hi, i["scale_idx"],
                               k_scale=i["k_scale"], out=self.S)
 
     def topk(self):
@@ -233,7 +252,6 @@ class Step:
                                vd=i["vd"], vis_lo=self.lo, vis_hi=self.hi, out=self.out,
                                lse=self.lse, workspace=self.ws_attn)
 
-    stages = ("index", "topk", "attend")
 
 
 class PooledStep:
@@ -337,8 +355,16 @@ def algorithmic_work(inp):
         gather = sel_pairs * row_bytes
     att_bytes = gather + B * Tq * H * kd * eb + B * Tq * k * 4 + B * Tq * H * (vd + 1) * 4
     att_flops = 2 * H * (kd + vd) * sel_pairs
-    return {"index": (idx_bytes, idx_flops), "topk": (topk_bytes, 0),
+    work = {"index": (idx_bytes, idx_flops), "topk": (topk_bytes, 0),
             "attend": (att_bytes, att_flops)}
+    if inp.get("k_new") is not None:
+        # rotation: the queries read and written once (bf16); cache write: the
+        # new key read (bf16), its fp8 row and scale written; d log2 d flops
+        # per row of the butterflies
+        lg = max(d.bit_length() - 1, 1)
+        work["rotate_q"] = (2 * B * Tq * Hi * d * 2, B * Tq * Hi * d * lg)
+        work["cache_write"] = (B * d * 2 + B * (d + 4), B * d * lg)
+    return work
 
 
 def capture_step(torch, run_once):
@@ -407,7 +433,7 @@ def run_workload(cfg, dsa, W, K, warmup, graph=False):
     for i in range(n_sets):
         inp = W.make(cfg, device="cuda", seed=1000 + cfg + 7919 * i)
         sets.append(PooledStep(dsa, inp) if cfg == 5 else Step(dsa, inp))
-    names = type(sets[0]).stages
+    names = sets[0].stages
 
     def run_once(st):
         for n in names:

@@ -142,6 +142,11 @@ def make(config: int, device="cpu", seed=None, variant=None, **over):
         out["q"] = to_bf16(_randn((B, Tq, H, kd), gen, device, qmul / math.sqrt(kd)))
         # absorbed MLA: one latent row of kd per key; V is its first vd columns
         out["KV"] = to_bf16(_randn((B, Tk, kd), gen, device, 1.0 / math.sqrt(kd)))
+    if cfg.get("fp8_keys") and not f32:
+        # the decode token's own indexer key, to be rotated and appended to
+        # the fp8 key cache (k_idx) at its last row; drawn last so that every
+        # other tensor keeps its values
+        out["k_new"] = to_bf16(_randn((B, 1, d), gen, device, 1.0 / math.sqrt(d)))
     return out
 
 

@@ -38,10 +38,22 @@ def test_fullsize_absorbed_step(dsa, cfg, score_rows, attend_rows):
     note(f"full-size step, config {cfg}")
     inp = W.make(cfg, device="cuda")
     step = bench.Step(dsa, inp)
-    step.index()
-    step.topk()
-    step.attend()
+    if step.cached:
+        k_before = cpu(inp["k_idx"]).view(torch.uint8).numpy().copy()
+        s_before = cpu(inp["k_scale"]).numpy().copy()
+    for name in step.stages:
+        getattr(step, name)()
     torch.cuda.synchronize()
+    if step.cached:
+        # write-then-score: the cache holds the new token's rotated fp8 row,
+        # every other row is untouched, and the queries were rotated
+        B, Tk = inp["B"], inp["Tk"]
+        rc, rs = oracle.index_cache_write(cpu(inp["k_new"]), np.full(B, Tk - 1, np.int32),
+                                          k_before, s_before)
+        assert np.array_equal(cpu(inp["k_idx"]).view(torch.uint8).numpy(), rc)
+        assert np.array_equal(cpu(inp["k_scale"]).numpy(), rs)
+        qr = oracle.hadamard_rows(cpu(inp["q_idx"]))
+        assert torch.equal(cpu(step.q_used), torch.from_numpy(qr).bfloat16())
     B, Tq, Tk, k = inp["B"], inp["Tq"], inp["Tk"], inp["top_k"]
     n_rows = B * Tq
     qp = cpu(inp["q_pos"]).numpy().reshape(-1)
@@ -52,7 +64,7 @@ def test_fullsize_absorbed_step(dsa, cfg, score_rows, attend_rows):
     note(f"  oracle scores on {len(rows)} rows")
     kq = cpu(inp["k_idx"])
     ks = None if inp["k_scale"] is None else cpu(inp["k_scale"])
-    ref, A = oracle.index_scores(cpu(inp["q_idx"]), kq, cpu(inp["w"]), inp["scale_idx"],
+    ref, A = oracle.index_scores(cpu(step.q_used), kq, cpu(inp["w"]), inp["scale_idx"],
                                  cpu(inp["q_pos"]), cpu(inp["pad"]), k_scale=ks, rows=rows,
                                  want_mag=True)
     S_rows = cpu(step.S.reshape(n_rows, Tk)[torch.tensor(rows, device="cuda")]).numpy()
