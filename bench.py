@@ -73,7 +73,8 @@ STAGE_KERNELS = {
     "topk": ("topk_seg_kernel", "topk_chunk_kernel", "topk_merge_kernel",
              "topk_merge_seg_kernel"),
     "attend": ("attend_gather_kernel", "attend_combine_kernel", "topk_to_mask_kernel",
-               "attend_masked_kernel", "attend_plain_kernel"),
+               "v_scale_max_kernel", "v_to_f16_kernel", "attend_masked_kernel",
+               "attend_plain_kernel"),
     "pool_keys": ("pool_keys_kernel", "pool_counts_kernel"),
     "pool_select": ("pool_select_kernel",),
 }
