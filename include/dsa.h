@@ -145,7 +145,9 @@ int dsa_index_scores(const dsa_index_dims *d, const void *q, int q_dtype,
  * scores:  rows x n_cols f32, row r at scores + r*row_stride
  * vis_lo, vis_hi: [rows] int32
  * out_idx: [rows, top_k] int32 output
- * Envelope: 1 <= top_k <= 2048; n_cols < 2^31.
+ * Envelope: 1 <= top_k <= 2048; n_cols < 2^31; rows x row_stride <= 2^46.
+ * dsa_topk_workspace_size returns the bytes dsa_topk needs for these sizes
+ * (0 for rows of at most 16384 keys, and 0 for sizes dsa_topk refuses).
  * ------------------------------------------------------------------------ */
 size_t dsa_topk_workspace_size(int32_t rows, int32_t n_cols, int32_t top_k);
 
@@ -211,9 +213,16 @@ int dsa_topk_noalloc(const float *scores, int32_t rows, int32_t n_cols,
  * shared by all heads; n_heads == 64, kd == 576, vd == 512, n_k <= 262144).
  * BF16 with kv_heads == n_heads runs the masked-tile kernel (MFMA over key
  * tiles with a per-query selection bitmap; kd == 192, vd == 256).  Other
- * shapes run a plain (non-MFMA) kernel.  The softmax weights enter the
- * value product as a two-term bf16 split (about 16 significant bits); sums
- * are f32.
+ * shapes run a plain (non-MFMA) kernel.  In the gather kernel the softmax
+ * weights enter the value product as a two-term bf16 split (about 16
+ * significant bits); the masked-tile kernel re-encodes V once per call as
+ * fp16 with a power-of-two scale per (sequence, head) and multiplies fp16
+ * weights (11 significant bits); sums are f32.
+ * dsa_sparse_attend_workspace_size returns the bytes the kernel chosen for
+ * these dims needs (assuming, for kv_heads == 1, the absorbed aliasing
+ * v == k with one row stride), or 0 when it needs none or the dims are
+ * invalid.  Tensors beyond 2^46 elements and more than 2^31 - 1 (query,
+ * head) rows return DSA_ERR_UNSUPPORTED.
  * ------------------------------------------------------------------------ */
 typedef struct {
     int32_t batch, n_q, n_k, n_heads, kd, vd, kv_heads, n_sel;

@@ -48,9 +48,14 @@ def _load():
     global _lib
     with _lock:
         if _lib is None:
-            if not os.path.exists(_LIB_PATH):
-                build(force=True)
-            lib = ctypes.CDLL(_LIB_PATH)
+            # DSA_ORACLE_LIB names another build of dsa_oracle.c (the
+            # sanitizer test loads one built with ASan/UBSan)
+            path = os.environ.get("DSA_ORACLE_LIB")
+            if not path:
+                path = _LIB_PATH
+                if not os.path.exists(path):
+                    build(force=True)
+            lib = ctypes.CDLL(path)
             P = ctypes.c_void_p
             I64 = ctypes.c_int64
             I32 = ctypes.c_int32

@@ -151,11 +151,6 @@ __global__ __launch_bounds__(256) void index_cache_write_kernel(
     }
 }
 
-bool hadamard_supported(int d)
-{
-    return d == 32 || d == 64 || d == 128 || d == 256;
-}
-
 template <int D>
 static hipError_t launch_rotate_d(const void *x, bool x_f32, void *out, bool out_f32,
                                   int64_t rows, hipStream_t st)

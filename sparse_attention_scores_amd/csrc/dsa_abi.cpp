@@ -45,6 +45,12 @@ hipStream_t as_stream(void *s)
 
 constexpr int64_t kMaxElems = (int64_t)1 << 46;
 
+// true when the product of the sizes exceeds `limit` (no overflow on the way)
+bool too_many(std::initializer_list<int64_t> sizes, int64_t limit = kMaxElems)
+{
+    return dsa::checked_product(sizes, limit) < 0;
+}
+
 } // namespace
 
 extern "C" {
@@ -84,11 +90,11 @@ int dsa_index_scores(const dsa_index_dims *d, const void *q, int q_dtype, const 
     if (d->batch < 0 || d->n_q < 0 || d->n_k < 0 || d->n_heads <= 0 || d->head_dim <= 0)
         return fail(DSA_ERR_ARG, "dsa_index_scores: bad dims (batch %d n_q %d n_k %d heads %d dim %d)",
                     d->batch, d->n_q, d->n_k, d->n_heads, d->head_dim);
-    const int64_t n_scores = (int64_t)d->batch * d->n_q * d->n_k;
-    if (n_scores > kMaxElems ||
-        (int64_t)d->batch * d->n_q * d->n_heads * d->head_dim > kMaxElems)
+    if (too_many({d->batch, d->n_q, d->n_k}) ||
+        too_many({d->batch, d->n_q, d->n_heads, d->head_dim}) ||
+        too_many({d->batch, d->n_k, d->head_dim}))
         return fail(DSA_ERR_UNSUPPORTED, "dsa_index_scores: tensors too large");
-    if (n_scores == 0)
+    if ((int64_t)d->batch * d->n_q * d->n_k == 0)
         return ok();
     if (!q || !k || !w || !vis_lo || !vis_hi || !scores)
         return fail(DSA_ERR_ARG, "dsa_index_scores: null pointer");
@@ -153,6 +159,8 @@ static int topk_args(const char *fn, const float *scores, int32_t rows, int32_t 
     if (row_stride < n_cols)
         return fail(DSA_ERR_ARG, "%s: row_stride %lld < n_cols %d", fn, (long long)row_stride,
                     n_cols);
+    if (too_many({rows, row_stride}))
+        return fail(DSA_ERR_UNSUPPORTED, "%s: rows x row_stride too large", fn);
     return DSA_OK;
 }
 
@@ -261,7 +269,8 @@ int dsa_sparse_attend(const dsa_attn_dims *d, int dtype, const void *q, const vo
     if (rc != DSA_OK)
         return rc;
     const int64_t rows = (int64_t)d->batch * d->n_q;
-    if (rows * d->n_heads > 0x7fffffff || rows * d->n_sel > kMaxElems)
+    if (too_many({rows, d->n_heads}, 0x7fffffff) || too_many({rows, d->n_sel}) ||
+        too_many({rows, d->n_heads, d->kd}) || too_many({rows, d->n_heads, d->vd}))
         return fail(DSA_ERR_UNSUPPORTED, "dsa_sparse_attend: too many rows");
     if (rows == 0)
         return ok();
@@ -271,6 +280,8 @@ int dsa_sparse_attend(const dsa_attn_dims *d, int dtype, const void *q, const vo
         return fail(DSA_ERR_ARG, "dsa_sparse_attend: give both vis_lo and vis_hi or neither");
     if (k_row_stride < (int64_t)d->kv_heads * d->kd || v_row_stride < (int64_t)d->kv_heads * d->vd)
         return fail(DSA_ERR_ARG, "dsa_sparse_attend: row stride smaller than a key row");
+    if (too_many({d->batch, d->n_k, k_row_stride}) || too_many({d->batch, d->n_k, v_row_stride}))
+        return fail(DSA_ERR_UNSUPPORTED, "dsa_sparse_attend: key or value rows too large");
     a.q = q;
     a.k = k;
     a.v = v;
@@ -310,7 +321,7 @@ int dsa_hadamard_rotate(int64_t rows, int32_t d, const void *in, int in_dtype, v
     if ((in_dtype != DSA_F32 && in_dtype != DSA_BF16) ||
         (out_dtype != DSA_F32 && out_dtype != DSA_BF16))
         return fail(DSA_ERR_ARG, "dsa_hadamard_rotate: dtypes must be F32 or BF16");
-    if (rows * d > kMaxElems)
+    if (too_many({rows, d}))
         return fail(DSA_ERR_UNSUPPORTED, "dsa_hadamard_rotate: too many rows");
     if (rows == 0)
         return ok();
@@ -339,8 +350,8 @@ int dsa_index_cache_write(const dsa_cache_dims *d, const void *k_new, int k_dtyp
         return fail(DSA_ERR_ARG, "dsa_index_cache_write: the cache must be FP8_E4M3 or BF16");
     if ((cache_dtype == DSA_FP8_E4M3) != (k_scale != nullptr))
         return fail(DSA_ERR_ARG, "dsa_index_cache_write: k_scale goes with (only) an FP8 cache");
-    if ((int64_t)d->batch * d->n_cache * d->head_dim > kMaxElems ||
-        (int64_t)d->batch * d->n_new * d->head_dim > kMaxElems)
+    if (too_many({d->batch, d->n_cache, d->head_dim}) ||
+        too_many({d->batch, d->n_new, d->head_dim}))
         return fail(DSA_ERR_UNSUPPORTED, "dsa_index_cache_write: tensors too large");
     if ((int64_t)d->batch * d->n_new == 0)
         return ok();
@@ -370,7 +381,7 @@ int dsa_pool_keys(const dsa_pool_dims *d, int dtype, const void *k, const void *
         return fail(DSA_ERR_ARG, "dsa_pool_keys: head_dim must be positive");
     if (dtype != DSA_F32 && dtype != DSA_BF16)
         return fail(DSA_ERR_ARG, "dsa_pool_keys: dtype must be F32 or BF16");
-    if ((int64_t)d->batch * d->seq * d->head_dim > kMaxElems)
+    if (too_many({d->batch, d->seq, d->head_dim}))
         return fail(DSA_ERR_UNSUPPORTED, "dsa_pool_keys: tensors too large");
     if (d->batch == 0)
         return ok();
@@ -406,7 +417,8 @@ int dsa_pool_select(const dsa_pool_dims *d, const float *pool_scores, const int3
         return fail(DSA_ERR_UNSUPPORTED, "dsa_pool_select: more than %d pools per row",
                     dsa::kPoolSelectMaxPools);
     const int64_t rows = (int64_t)d->batch * d->n_q;
-    if (rows > 0x7fffffff || rows * d->out_width > kMaxElems)
+    if (rows > 0x7fffffff || too_many({rows, d->out_width}) ||
+        too_many({rows, d->seq / d->kpool}))
         return fail(DSA_ERR_UNSUPPORTED, "dsa_pool_select: too many rows");
     if (rows == 0)
         return ok();

@@ -6,7 +6,29 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <initializer_list>
+
 namespace dsa {
+
+// Kernel envelopes: the shapes the MFMA kernels are built for.  The kernels
+// define their tile constants from these, and the host-side predicates and
+// workspace sizes (envelopes.cpp) read them, so both agree by construction.
+constexpr int kAbsHeads = 64;         // absorbed gather kernel: heads sharing a latent row,
+constexpr int kAbsKd = 576;           //   its key width,
+constexpr int kAbsVd = 512;           //   its value width (the row's first vd columns)
+constexpr int kAbsMaxKeys = 262144;   //   and its per-row set bitmap's reach
+constexpr int kPlainMaxVd = 1024;     // plain attend kernel: value columns per thread block
+constexpr int kMaskedKd = 192;        // per-head masked attend: key width,
+constexpr int kMaskedVd = 256;        //   value width,
+constexpr int kMaskedQBlock = 256;    //   queries per block (the mask's q_pad granule)
+constexpr int kMaskedVKeys = 256;     //   keys per block of the V re-encoding passes
+constexpr int kTopkChunkKeys = 16384; // top-k: rows longer than this go by chunks
+constexpr int kTopkMaxSelect = 2048;  // top-k: largest k
+
+// Product of sizes when it is at most `limit`, else -1, computed without an
+// intermediate product overflowing; a negative factor gives -1, a zero
+// factor 0.
+int64_t checked_product(std::initializer_list<int64_t> factors, int64_t limit);
 
 struct IndexArgs {
     int batch, n_q, n_k, n_heads, head_dim;
@@ -53,8 +75,19 @@ struct AttendArgs {
 bool attend_gather_supported(const AttendArgs &a);
 bool attend_masked_supported(const AttendArgs &a);
 bool attend_plain_supported(const AttendArgs &a);
+// blocks per query row of the gather kernel (split-K over the selected keys)
+int attend_gather_splits(const AttendArgs &a);
 size_t attend_workspace_bytes(const AttendArgs &a);
 size_t attend_masked_workspace_bytes(const AttendArgs &a);
+// the per-head attend's workspace: the tile-major selection mask, V as
+// fp16, per-run partial maxima of |V| and the per-(sequence, head) scale
+// exponents, each region 256-byte aligned
+struct MaskedLayout {
+    int nw, q_pad, nkb;  // key words (tiles), padded query count, V-pass key runs
+    size_t mask_bytes, v16_bytes, part_bytes, vexp_bytes;
+    size_t v16_off, part_off, vexp_off, total;
+};
+MaskedLayout masked_layout(const AttendArgs &a);
 hipError_t launch_attend_masked(const AttendArgs &a, hipStream_t st);
 hipError_t launch_attend(const AttendArgs &a, hipStream_t st);
 

@@ -723,11 +723,6 @@ static hipError_t launch_mfma_keys(const IndexArgs &a, hipStream_t st)
     return a.k_fp8 ? launch_mfma_mode<D, MT, true>(a, st) : launch_mfma_mode<D, MT, false>(a, st);
 }
 
-bool index_mfma_supported(int n_heads, int head_dim)
-{
-    return (n_heads == 32 || n_heads == 64) && (head_dim == 64 || head_dim == 128);
-}
-
 hipError_t launch_index_scores(const IndexArgs &a, hipStream_t st)
 {
     if (a.f32) {

@@ -36,11 +36,11 @@
 
 namespace dsa {
 
-constexpr int MK_QB = 256;          // queries per attention block (8 waves x 32)
+constexpr int MK_QB = kMaskedQBlock; // queries per attention block (8 waves x 32)
 constexpr int MK_TILE = 32;         // keys per tile
 constexpr int MK_ROWS = 32;         // query rows per mask-building block
 constexpr int MK_WCHUNK = 512;      // mask words per row held in LDS at once
-constexpr int MK_VKEYS = 256;       // keys per block of the V passes
+constexpr int MK_VKEYS = kMaskedVKeys; // keys per block of the V passes
 
 // ------------------------------------------------------------------ mask
 
@@ -312,7 +312,8 @@ __global__ __launch_bounds__(512, 1) void attend_masked_kernel(
     constexpr int NCT = VD / 32;     // output column tiles of 32
     constexpr int KCH = KD / 8;      // 16-byte chunks of a K row
     constexpr int VCH = VD / 8;      // 16-byte chunks of a V row
-    static_assert(KD == 192 && VD == 256, "the swizzles and read groups are laid out for 192/256");
+    static_assert(KD == kMaskedKd && VD == kMaskedVd && KD == 192 && VD == 256,
+                  "the swizzles and read groups are laid out for 192/256");
     using Sm = MaskedSmem<KD, VD>;
     constexpr int NK_DMA = Sm::KB / 1024;            // 12
     constexpr int NV_DMA = Sm::VB / 1024;            // 16
@@ -728,44 +729,6 @@ __global__ __launch_bounds__(512, 1) void attend_masked_kernel(
 }
 
 // ------------------------------------------------------------------ host side
-
-namespace {
-struct MaskedLayout {
-    int nw, q_pad, nkb;
-    size_t mask_bytes, v16_bytes, part_bytes, vexp_bytes;
-    size_t v16_off, part_off, vexp_off, total;
-};
-
-MaskedLayout masked_layout(const AttendArgs &a)
-{
-    MaskedLayout L{};
-    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-    L.nw = (a.n_k + 31) / 32;
-    L.q_pad = (a.n_q + MK_QB - 1) / MK_QB * MK_QB;
-    L.nkb = (a.n_k + MK_VKEYS - 1) / MK_VKEYS;
-    L.mask_bytes = (size_t)a.batch * L.nw * L.q_pad * sizeof(uint32_t);
-    L.v16_bytes = (size_t)a.batch * a.n_k * a.n_heads * a.vd * sizeof(uint16_t);
-    L.part_bytes = (size_t)a.batch * a.n_heads * L.nkb * sizeof(uint32_t);
-    L.vexp_bytes = (size_t)a.batch * a.n_heads * sizeof(float);
-    L.v16_off = up(L.mask_bytes);
-    L.part_off = L.v16_off + up(L.v16_bytes);
-    L.vexp_off = L.part_off + up(L.part_bytes);
-    L.total = L.vexp_off + up(L.vexp_bytes);
-    return L;
-}
-} // namespace
-
-bool attend_masked_supported(const AttendArgs &a)
-{
-    return !a.f32 && a.kv_heads == a.n_heads && a.kd == 192 && a.vd == 256 && a.n_k > 0 &&
-           a.k_row_stride % 8 == 0 && a.v_row_stride % 8 == 0 &&
-           (int64_t)a.n_heads * a.vd * 2 < (1ll << 31) && a.k_row_stride * 2 < (1ll << 31);
-}
-
-size_t attend_masked_workspace_bytes(const AttendArgs &a)
-{
-    return masked_layout(a).total;
-}
 
 hipError_t launch_attend_masked(const AttendArgs &a, hipStream_t st)
 {

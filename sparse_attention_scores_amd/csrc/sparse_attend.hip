@@ -132,9 +132,9 @@ __device__ __forceinline__ void wave_chunk_extract(const uint32_t *bitmap, int n
 }
 
 // ------------------------------------------------------------------ gather kernel
-constexpr int AB_H = 64;                      // heads of the absorbed attention
-constexpr int AB_KD = 576;
-constexpr int AB_VD = 512;
+constexpr int AB_H = kAbsHeads;                    // heads of the absorbed attention
+constexpr int AB_KD = kAbsKd;
+constexpr int AB_VD = kAbsVd;
 constexpr int AB_TILE = 32;                   // keys per LDS tile
 constexpr int AB_KS = AB_KD / 32;             // 18 k-steps of the 16x16x32 MFMA
 constexpr int AB_ROWB = AB_KD * 2;            // 1152 bytes per latent row
@@ -152,7 +152,7 @@ constexpr int AB_EARLY = 6;                   // loader's DMAs of tile j issued 
 constexpr int AB_KB = 6;                      // loader key reads per LDS batch
 constexpr int AB_LIST = 2048;                 // keys per batch of a block
 constexpr int AB_IDX_U = 8;                   // fast path: row entries per thread (n_sel <= 2048)
-constexpr int AB_SET_WORDS = 8192;            // set bitmap of the row: n_k <= 262144
+constexpr int AB_SET_WORDS = kAbsMaxKeys / 32;           // set bitmap of the row: n_k <= 262144
 static_assert(AB_DMA % AB_NL == 0 && AB_DMA_L % AB_KB == 0 && AB_EARLY % AB_KB == 0 &&
                   AB_EARLY < AB_DMA_L,
               "each loader issues whole key batches");
@@ -811,7 +811,7 @@ __device__ __forceinline__ float ld_elem<uint16_t>(const uint16_t *p, int64_t i)
 }
 
 constexpr int PL_NT = 128;
-constexpr int PL_MAXVD = 1024;
+constexpr int PL_MAXVD = kPlainMaxVd;
 
 struct PlainSmem {
     uint32_t bitmap[kBitmapMaxWords];
@@ -896,43 +896,6 @@ __global__ __launch_bounds__(PL_NT) void attend_plain_kernel(
 }
 
 // ------------------------------------------------------------------ host side
-bool attend_gather_supported(const AttendArgs &a)
-{
-    return !a.f32 && a.kv_heads == 1 && a.n_heads == AB_H && a.kd == AB_KD && a.vd == AB_VD &&
-           a.n_k <= AB_SET_WORDS * 32 &&
-           a.v == a.k && a.v_row_stride == a.k_row_stride && a.k_row_stride % 8 == 0 &&
-           a.k_row_stride >= AB_KD && a.k_row_stride < (1ll << 30);
-}
-
-int attend_gather_splits(const AttendArgs &a)
-{
-    // blocks = rows x splits; 256 of them fill the CUs
-    const int64_t rows = (int64_t)a.batch * a.n_q;
-    int by_fill = (int)((256 + rows - 1) / rows);
-    int by_work = max(1, min(a.n_sel, a.n_k) / 64);
-    // the merge kernel keeps one split per lane
-    return max(1, min(min(by_fill, by_work), 64));
-}
-
-size_t attend_workspace_bytes(const AttendArgs &a)
-{
-    if (attend_masked_supported(a))
-        return attend_masked_workspace_bytes(a);
-    if (!attend_gather_supported(a))
-        return 0;
-    const int s = attend_gather_splits(a);
-    if (s <= 1)
-        return 0;
-    const int64_t rows = (int64_t)a.batch * a.n_q;
-    // fp16 partials plus one (m, l, e, -) f32 quadruple per (row, split, head)
-    return (size_t)rows * s * AB_H * (AB_VD * sizeof(uint16_t) + 4 * sizeof(float));
-}
-
-bool attend_plain_supported(const AttendArgs &a)
-{
-    return a.vd <= PL_MAXVD;
-}
-
 hipError_t launch_attend(const AttendArgs &a, hipStream_t st)
 {
     const int64_t rows = (int64_t)a.batch * a.n_q;

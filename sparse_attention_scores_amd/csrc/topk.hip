@@ -649,16 +649,9 @@ __global__ __launch_bounds__(NT) void topk_merge_seg_kernel(const uint64_t *__re
     }
 }
 
-constexpr int kCapLarge = 16384;
+constexpr int kCapLarge = kTopkChunkKeys;
+static_assert(kTopkMaxK == kTopkMaxSelect, "one largest k for the host and the kernels");
 constexpr int kCapSmall = 4096;
-
-size_t topk_workspace_bytes(int rows, int n_cols, int k)
-{
-    if (n_cols <= kCapLarge)
-        return 0;
-    const int64_t n_chunks = (n_cols + kCapLarge - 1) / kCapLarge;
-    return (size_t)rows * (size_t)n_chunks * (size_t)k * sizeof(uint64_t);
-}
 
 // Blocks per row for the segmented kernels: enough for about 256 blocks in
 // all, at most max_parts, and segments of at least 64 ranks; 1 = one block
