@@ -68,7 +68,9 @@ def _load():
             lib.orc_pool_visible.argtypes = [I32, I32, I32, I64]
             lib.orc_index_scores.argtypes = [I64, I64, I64, I64, I64, P, ctypes.c_int, P,
                                              ctypes.c_int, P, P, D, P, P, I32, P, I64, P, P]
-            lib.orc_topk.argtypes = [P, I64, I64, I64, P, P, I32, I32, P]
+            lib.orc_topk.argtypes = [P, I64, I64, I64, P, P, I32, I32, I32, P]
+            lib.orc_index_share_source.argtypes = [I32]
+            lib.orc_index_share_source.restype = I32
             lib.orc_pool_keys.argtypes = [I64, I64, I64, I32, P, ctypes.c_int, P,
                                           ctypes.c_int, P, P, P, P]
             lib.orc_pool_select.argtypes = [P, I64, I64, I64, P, P, I32, I32, I32, P, P]
@@ -190,19 +192,26 @@ def index_scores(q, k, w, scale, q_pos, pad, k_scale=None, kpool=0, rows=None,
     return (S, A) if want_mag else S
 
 
-def topk(S, row_qpos, row_pad, k, kpool=0):
+def topk(S, row_qpos, row_pad, k, kpool=0, n_sink=0):
     """Top-k per row (higher score, then smaller index), INVALID-padded.
 
     S: [rows, n_cols] float32; row_qpos/row_pad: per-row query position and
-    sequence padding (visibility)."""
+    sequence padding (visibility).  n_sink > 0 adds the attention-sink boost
+    (1e20, in f32) to each row's first n_sink visible columns first."""
     Sa = _f32(S)
     n_rows, n_cols = Sa.shape
     out = np.empty((n_rows, k), np.int32)
     rc = _load().orc_topk(_ptr(Sa), n_rows, n_cols, n_cols, _ptr(_i32(row_qpos)),
-                          _ptr(_i32(row_pad)), int(kpool), int(k), _ptr(out))
+                          _ptr(_i32(row_pad)), int(kpool), int(k), int(n_sink), _ptr(out))
     if rc != 0:
         raise ValueError("oracle topk: NaN score")
     return out
+
+
+def index_share_source(layer: int) -> int:
+    """IndexShare: the layer whose indexer selection `layer` uses (itself
+    when it is a full layer: layer <= 1 or layer % 4 == 2)."""
+    return int(_load().orc_index_share_source(int(layer)))
 
 
 def pool_keys(k, gate, pad, kpool, want_mag=False):

@@ -208,12 +208,28 @@ static int64_t gather_candidates(const float *row, int64_t n_cols, int32_t pd,
     return n;
 }
 
+/* Attention-sink force-inclusion ("Another DSA attempt": the decode
+ * indexer-K cache commit boosts the first key(s) so that the sink survives
+ * top-k; the per-sequence sink commit adds the boost only to keys of the
+ * query's own sequence; the serving-correctness commit anchors it on the
+ * sequence's first PRESENT position).  The boost is an f32 addition of 1e20
+ * to the score, as the pages' graph adds it before the top-k.  The sink keys
+ * are the first n_sink candidates in column order -- the sequence's first
+ * present positions that the query can see (the causal mask still applies
+ * to them); for pooled keys, the first visible pools. */
+static void add_sink_boost(cand_t *c, int64_t n, int32_t n_sink)
+{
+    for (int64_t j = 0; j < n && j < n_sink; ++j)
+        c[j].score = c[j].score + 1e20f;
+}
+
 /* Per row: the min(k, #visible) visible columns in rank order, then INVALID
  * up to width k.  Row r's scores start at S + r*row_stride; its query
- * position and padding are row_qpos[r], row_pad[r]. */
+ * position and padding are row_qpos[r], row_pad[r].  n_sink > 0 boosts the
+ * row's first n_sink visible columns (add_sink_boost) before ranking. */
 int orc_topk(const float *S, int64_t n_rows, int64_t n_cols, int64_t row_stride,
              const int32_t *row_qpos, const int32_t *row_pad, int32_t kpool,
-             int32_t k, int32_t *out)
+             int32_t k, int32_t n_sink, int32_t *out)
 {
     int bad = 0;
 #pragma omp parallel for schedule(dynamic, 4) reduction(| : bad)
@@ -225,6 +241,7 @@ int orc_topk(const float *S, int64_t n_rows, int64_t n_cols, int64_t row_stride,
             bad = 1;
             n = 0;
         }
+        add_sink_boost(c, n, n_sink);
         qsort(c, (size_t)n, sizeof(cand_t), cand_cmp);
         for (int64_t i = 0; i < k; ++i)
             out[r * k + i] = i < n ? c[i].idx : ORC_INVALID;
@@ -544,6 +561,26 @@ void orc_quantize_e4m3_rows(const float *y, int64_t rows, int64_t d, uint8_t *co
             codes[r * d + i] = orc_e4m3_encode(q);
         }
     }
+}
+
+/* ------------------------------------------------------------------------ */
+/* IndexShare ("Another DSA attempt": the IndexShare commit message and the  */
+/* review comments around it).                                               */
+/* ------------------------------------------------------------------------ */
+
+/* GLM-5.2 marks some layers "full" (they compute their own indexer top-k)
+ * and the rest "shared" (they reuse the selection of the most recent full
+ * layer).  The rule the pages derive from the model config: layer il is
+ * full iff il <= 1 or il % 4 == 2.  Returns the layer whose selection layer
+ * il uses (il itself when full), or -1 for il < 0. */
+int32_t orc_index_share_source(int32_t il)
+{
+    if (il < 0)
+        return -1;
+    for (int32_t l = il; l >= 0; --l)
+        if (l <= 1 || l % 4 == 2)
+            return l;
+    return -1;
 }
 
 int orc_max_threads(void)
