@@ -142,8 +142,21 @@ int dsa_index_scores(const dsa_index_dims *d, const void *q, int q_dtype,
  * indexer commit: top_k(min(top_k, n_tokens)); [fak] host f64 top-k.)
  * The result is exact: the selection is a pure comparison of the f32 scores.
  *
+ * Attention sinks (n_sink > 0): the first n_sink columns of each row's
+ * visible range -- for token keys, the sequence's first present positions
+ * that the query can see -- take ranks 0 .. n_sink-1 in column order, and
+ * the row's other visible columns follow in rank order ([ik] decode
+ * indexer-K cache commit: the first key(s) get a boost so the sink always
+ * survives top-k; per-sequence sink commit: only the query's own sequence's
+ * sink; serving-correctness commit: anchored on the first present
+ * position).  The pages add 1e20 to the f32 scores of those columns; when
+ * every score's magnitude is below 2^42 that addition gives each sink
+ * exactly 1e20f and leaves every other score below it, which is the order
+ * stated here.  n_sink = 0: no sinks.
+ *
  * scores:  rows x n_cols f32, row r at scores + r*row_stride
  * vis_lo, vis_hi: [rows] int32
+ * n_sink:  >= 0 (values above top_k act as top_k)
  * out_idx: [rows, top_k] int32 output
  * Envelope: 1 <= top_k <= 2048; n_cols < 2^31; rows x row_stride <= 2^46.
  * dsa_topk_workspace_size returns the bytes dsa_topk needs for these sizes
@@ -153,7 +166,7 @@ size_t dsa_topk_workspace_size(int32_t rows, int32_t n_cols, int32_t top_k);
 
 int dsa_topk(const float *scores, int32_t rows, int32_t n_cols,
              int64_t row_stride, const int32_t *vis_lo, const int32_t *vis_hi,
-             int32_t top_k, int32_t *out_idx, void *workspace,
+             int32_t top_k, int32_t n_sink, int32_t *out_idx, void *workspace,
              size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
@@ -180,8 +193,24 @@ int dsa_topk(const float *scores, int32_t rows, int32_t n_cols,
 
 int dsa_topk_noalloc(const float *scores, int32_t rows, int32_t n_cols,
                      int64_t row_stride, const int32_t *vis_lo,
-                     const int32_t *vis_hi, int32_t top_k, int32_t *out_idx,
-                     void *stream);
+                     const int32_t *vis_hi, int32_t top_k, int32_t n_sink,
+                     int32_t *out_idx, void *stream);
+
+/* ------------------------------------------------------------------------
+ * IndexShare: which layer's selection a layer attends with.
+ *
+ * [ik] IndexShare commit message and review comments: GLM-5.2 marks 21 of
+ * its 78 layers "full" (layers 0, 1, 2, then every 4th up to 74); a full
+ * layer computes its own indexer scores and top-k, and each of the other
+ * ("shared") layers reuses the selection of the most recent full layer.
+ * The rule: layer il is full iff il <= 1 or il % 4 == 2.
+ *
+ * Returns the layer whose top-k rows layer `layer` uses -- `layer` itself
+ * when it is full -- or -1 when layer < 0.  Host function (no GPU work): a
+ * caller runs dsa_index_scores and dsa_topk on full layers only and passes
+ * the kept rows to dsa_sparse_attend on the shared ones.
+ * ------------------------------------------------------------------------ */
+int32_t dsa_index_share_source(int32_t layer);
 
 /* ------------------------------------------------------------------------
  * Sparse attention over each query's selected keys.

@@ -56,7 +56,7 @@ class _PoolDims(ctypes.Structure):
 _lock = threading.Lock()
 _lib = None
 EXPORTS = ("dsa_last_error", "dsa_version", "dsa_visibility_ranges", "dsa_index_scores",
-           "dsa_topk_workspace_size", "dsa_topk", "dsa_topk_noalloc",
+           "dsa_topk_workspace_size", "dsa_topk", "dsa_topk_noalloc", "dsa_index_share_source",
            "dsa_sparse_attend_workspace_size",
            "dsa_sparse_attend", "dsa_pool_keys", "dsa_pool_select_workspace_size",
            "dsa_pool_select", "dsa_hadamard_rotate", "dsa_index_cache_write")
@@ -97,8 +97,10 @@ def load():
         lib.dsa_index_scores.argtypes = [P, P, ctypes.c_int, P, ctypes.c_int, P, P, P, P, P, P]
         lib.dsa_topk_workspace_size.argtypes = [I32, I32, I32]
         lib.dsa_topk_workspace_size.restype = SZ
-        lib.dsa_topk.argtypes = [P, I32, I32, I64, P, P, I32, P, P, SZ, P]
-        lib.dsa_topk_noalloc.argtypes = [P, I32, I32, I64, P, P, I32, P, P]
+        lib.dsa_index_share_source.argtypes = [I32]
+        lib.dsa_index_share_source.restype = I32
+        lib.dsa_topk.argtypes = [P, I32, I32, I64, P, P, I32, I32, P, P, SZ, P]
+        lib.dsa_topk_noalloc.argtypes = [P, I32, I32, I64, P, P, I32, I32, P, P]
         lib.dsa_sparse_attend_workspace_size.argtypes = [P]
         lib.dsa_sparse_attend_workspace_size.restype = SZ
         lib.dsa_sparse_attend.argtypes = [P, ctypes.c_int, P, P, I64, P, I64, P, P, P, P, P, P,
@@ -222,12 +224,20 @@ def index_scores(q, k, w, vis_lo, vis_hi, scale: float, k_scale=None, out=None):
     return out
 
 
+def index_share_source(layer: int) -> int:
+    """IndexShare: the layer whose top-k rows `layer` attends with (itself
+    when it is a full layer)."""
+    return int(load().dsa_index_share_source(int(layer)))
+
+
 def topk_workspace_size(rows: int, n_cols: int, top_k: int) -> int:
     return int(load().dsa_topk_workspace_size(rows, n_cols, top_k))
 
 
-def topk(scores, vis_lo, vis_hi, top_k: int, out=None, workspace=None):
-    """Top-k index rows [..., top_k] (int32, rank order, INVALID-padded)."""
+def topk(scores, vis_lo, vis_hi, top_k: int, out=None, workspace=None, n_sink: int = 0):
+    """Top-k index rows [..., top_k] (int32, rank order, INVALID-padded);
+    with n_sink > 0 the first n_sink visible columns of each row rank first
+    (attention sinks)."""
     _dev(scores, vis_lo, vis_hi, out)
     if scores.dtype != torch.float32:
         raise TypeError(f"topk: scores must be float32, got {scores.dtype}")
@@ -243,11 +253,11 @@ def topk(scores, vis_lo, vis_hi, top_k: int, out=None, workspace=None):
         raise ValueError(f"topk: out must be int32 with {rows} x {top_k} elements")
     ws, wsb = _workspace(topk_workspace_size(rows, n_cols, top_k), workspace, scores.device)
     _check(load().dsa_topk(_p(scores), rows, n_cols, n_cols, _p(_i32(vis_lo)), _p(_i32(vis_hi)),
-                           top_k, _p(out), _p(ws), wsb, _stream()))
+                           top_k, int(n_sink), _p(out), _p(ws), wsb, _stream()))
     return out
 
 
-def topk_noalloc(scores, vis_lo, vis_hi, top_k: int, out):
+def topk_noalloc(scores, vis_lo, vis_hi, top_k: int, out, n_sink: int = 0):
     """Top-k into a caller-given `out`, with no workspace: the library's own
     per-GPU scratch holds the chunk winners of long rows (nothing is
     allocated, here or in the library)."""
@@ -261,7 +271,7 @@ def topk_noalloc(scores, vis_lo, vis_hi, top_k: int, out):
     if out.numel() != rows * top_k or out.dtype != torch.int32:
         raise ValueError(f"topk_noalloc: out must be int32 with {rows} x {top_k} elements")
     _check(load().dsa_topk_noalloc(_p(scores), rows, n_cols, n_cols, _p(_i32(vis_lo)),
-                                   _p(_i32(vis_hi)), top_k, _p(out), _stream()))
+                                   _p(_i32(vis_hi)), top_k, int(n_sink), _p(out), _stream()))
     return out
 
 

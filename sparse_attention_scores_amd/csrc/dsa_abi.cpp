@@ -145,9 +145,9 @@ size_t dsa_topk_workspace_size(int32_t rows, int32_t n_cols, int32_t top_k)
 // there is nothing to do, else the error.
 static int topk_args(const char *fn, const float *scores, int32_t rows, int32_t n_cols,
                      int64_t row_stride, const int32_t *vis_lo, const int32_t *vis_hi,
-                     int32_t top_k, const int32_t *out_idx)
+                     int32_t top_k, int32_t n_sink, const int32_t *out_idx)
 {
-    if (rows < 0 || n_cols < 0)
+    if (rows < 0 || n_cols < 0 || n_sink < 0)
         return fail(DSA_ERR_ARG, "%s: negative size", fn);
     if (top_k < 1 || top_k > 2048)
         return fail(top_k < 1 ? DSA_ERR_ARG : DSA_ERR_UNSUPPORTED,
@@ -165,11 +165,11 @@ static int topk_args(const char *fn, const float *scores, int32_t rows, int32_t 
 }
 
 int dsa_topk(const float *scores, int32_t rows, int32_t n_cols, int64_t row_stride,
-             const int32_t *vis_lo, const int32_t *vis_hi, int32_t top_k, int32_t *out_idx,
-             void *workspace, size_t workspace_bytes, void *stream)
+             const int32_t *vis_lo, const int32_t *vis_hi, int32_t top_k, int32_t n_sink,
+             int32_t *out_idx, void *workspace, size_t workspace_bytes, void *stream)
 {
-    const int rc =
-        topk_args("dsa_topk", scores, rows, n_cols, row_stride, vis_lo, vis_hi, top_k, out_idx);
+    const int rc = topk_args("dsa_topk", scores, rows, n_cols, row_stride, vis_lo, vis_hi, top_k,
+                             n_sink, out_idx);
     if (rc == 1)
         return ok();
     if (rc != DSA_OK)
@@ -178,16 +178,17 @@ int dsa_topk(const float *scores, int32_t rows, int32_t n_cols, int64_t row_stri
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(DSA_ERR_WORKSPACE, "dsa_topk: workspace of %zu bytes needed, %zu given", need,
                     workspace ? workspace_bytes : (size_t)0);
-    dsa::TopkArgs a{scores, rows, n_cols, row_stride, vis_lo, vis_hi, top_k, out_idx, workspace};
+    dsa::TopkArgs a{scores, rows,  n_cols,  row_stride, vis_lo,
+                    vis_hi, top_k, n_sink, out_idx,    workspace};
     return hip_status(dsa::launch_topk(a, as_stream(stream)), "dsa_topk");
 }
 
 int dsa_topk_noalloc(const float *scores, int32_t rows, int32_t n_cols, int64_t row_stride,
                      const int32_t *vis_lo, const int32_t *vis_hi, int32_t top_k,
-                     int32_t *out_idx, void *stream)
+                     int32_t n_sink, int32_t *out_idx, void *stream)
 {
     const int rc = topk_args("dsa_topk_noalloc", scores, rows, n_cols, row_stride, vis_lo,
-                             vis_hi, top_k, out_idx);
+                             vis_hi, top_k, n_sink, out_idx);
     if (rc == 1)
         return ok();
     if (rc != DSA_OK)
@@ -212,8 +213,19 @@ int dsa_topk_noalloc(const float *scores, int32_t rows, int32_t n_cols, int64_t 
         if (e != hipSuccess)
             return hip_status(e, "dsa_topk_noalloc: scratch lookup");
     }
-    dsa::TopkArgs a{scores, rows, n_cols, row_stride, vis_lo, vis_hi, top_k, out_idx, ws};
+    dsa::TopkArgs a{scores, rows, n_cols, row_stride, vis_lo, vis_hi, top_k, n_sink, out_idx, ws};
     return hip_status(dsa::launch_topk(a, as_stream(stream)), "dsa_topk_noalloc");
+}
+
+int32_t dsa_index_share_source(int32_t layer)
+{
+    if (layer < 0)
+        return -1;
+    // full layers: 0, 1 and every layer congruent to 2 mod 4; any other
+    // layer il > 2 reuses the full layer just below it, il - ((il - 2) % 4)
+    if (layer <= 1 || layer % 4 == 2)
+        return layer;
+    return layer - (layer - 2) % 4;
 }
 
 static int attend_args(const dsa_attn_dims *d, int dtype, dsa::AttendArgs &a)

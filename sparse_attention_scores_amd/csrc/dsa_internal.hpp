@@ -51,6 +51,7 @@ struct TopkArgs {
     int64_t row_stride;
     const int32_t *vis_lo, *vis_hi;
     int k;
+    int n_sink;  // attention sinks: the first n_sink visible columns rank first
     int32_t *out;
     void *workspace;
 };

@@ -105,12 +105,38 @@ struct ValueBuckets {
 };
 
 constexpr int kSegMaxBucket = 256;
+
+// First column a row ranks by score: the start of its visible range [lo, hi)
+// moved past the `skip` attention-sink columns that lead it (clamped to hi;
+// no overflow for any lo).
+__device__ __forceinline__ int first_ranked(int lo, int hi, int skip)
+{
+    lo = max(lo, 0);
+    return lo + min(skip, max(hi - lo, 0));
+}
+
+// Attention sinks: the first n_s columns of each row's visible range take
+// ranks 0 .. n_s - 1 in column order (INVALID past the range's end).
+__global__ __launch_bounds__(256) void topk_sink_prefix_kernel(const int32_t *__restrict__ vlo,
+                                                               const int32_t *__restrict__ vhi,
+                                                               int n_cols, int rows, int n_s,
+                                                               int k, int32_t *__restrict__ out)
+{
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= (int64_t)rows * n_s)
+        return;
+    const int row = (int)(e / n_s), j = (int)(e % n_s);
+    const int hi = min(vhi[row], n_cols);
+    const int lo = max(vlo[row], 0);
+    out[(int64_t)row * k + j] = j < hi - lo ? lo + j : -1;
+}
 template <int NT, int CAP>
 __global__ __launch_bounds__(NT) void topk_seg_kernel(const float *__restrict__ scores,
                                                       int n_cols, int64_t row_stride,
                                                       const int32_t *__restrict__ vlo,
                                                       const int32_t *__restrict__ vhi, int k,
-                                                      int32_t *__restrict__ out, int parts,
+                                                      int32_t *__restrict__ out,
+                                                      int64_t out_stride, int lo_skip, int parts,
                                                       int seg_len)
 {
     using S = Topk32Smem<NT, CAP>;
@@ -120,7 +146,8 @@ __global__ __launch_bounds__(NT) void topk_seg_kernel(const float *__restrict__ 
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int row = blockIdx.x / parts;
     const int seg = blockIdx.x - row * parts;
-    const int lo = max(vlo[row], 0), hi = min(vhi[row], n_cols);
+    const int hi = min(vhi[row], n_cols);
+    const int lo = first_ranked(vlo[row], hi, lo_skip);
     const int n = max(hi - lo, 0);
     const int rounds = (n + NT - 1) / NT;  // uniform, at most R
     // thread t keeps keys r*NT + t (r < rounds) in registers: their order keys
@@ -158,7 +185,7 @@ __global__ __launch_bounds__(NT) void topk_seg_kernel(const float *__restrict__ 
         omax = max(omax, sm.mm[1][w]);
     }
     const int m = min(k, n);
-    int32_t *o = out + (int64_t)row * k;
+    int32_t *o = out + (int64_t)row * out_stride;
     const int p0 = seg * seg_len, p1 = min(p0 + seg_len, k);
     for (int i = max(p0, m) + tid; i < p1; i += NT)
         o[i] = -1;
@@ -341,7 +368,8 @@ __device__ void merge_sorted(MergeSmem<NT, CACHE> &sm, const uint64_t *__restric
 template <int NT, int EPT, bool CACHE>
 __global__ __launch_bounds__(NT) void topk_merge_kernel(const uint64_t *__restrict__ ws,
                                                         int n_chunks, int k,
-                                                        int32_t *__restrict__ out)
+                                                        int32_t *__restrict__ out,
+                                                        int64_t out_stride)
 {
     __shared__ MergeSmem<NT, CACHE> sm;
     const int tid = threadIdx.x;
@@ -349,7 +377,7 @@ __global__ __launch_bounds__(NT) void topk_merge_kernel(const uint64_t *__restri
     uint64_t v[EPT];
     int m;
     merge_sorted<NT, EPT, CACHE>(sm, ws + (int64_t)row * n_chunks * k, n_chunks * k, k, v, m);
-    int32_t *o = out + (int64_t)row * k;
+    int32_t *o = out + (int64_t)row * out_stride;
 #pragma unroll
     for (int b = 0; b < EPT; ++b) {
         const int i = tid * EPT + b;
@@ -370,7 +398,8 @@ __global__ __launch_bounds__(NT) void topk_chunk_kernel(const float *__restrict_
                                                         int n_cols, int64_t row_stride,
                                                         const int32_t *__restrict__ vlo,
                                                         const int32_t *__restrict__ vhi, int k,
-                                                        uint64_t *__restrict__ ws, int n_chunks)
+                                                        uint64_t *__restrict__ ws, int n_chunks,
+                                                        int lo_skip)
 {
     using S = Topk32Smem<NT, CAP>;
     constexpr int NB = S::NB, NW = S::NW, PB = NB / NT, R = CAP / NT;
@@ -381,8 +410,9 @@ __global__ __launch_bounds__(NT) void topk_chunk_kernel(const float *__restrict_
     const int row = blockIdx.x / n_chunks;
     const int chunk = blockIdx.x - row * n_chunks;
     const int c0 = chunk * CAP;
-    const int lo = max(max(vlo[row], 0), c0);
-    const int hi = min(min(vhi[row], n_cols), c0 + CAP);
+    const int row_hi = min(vhi[row], n_cols);
+    const int lo = max(first_ranked(vlo[row], row_hi, lo_skip), c0);
+    const int hi = min(row_hi, c0 + CAP);
     uint32_t omin, omax;
     const int n = load_row32(sm, scores + (int64_t)row * row_stride, lo, hi, omin, omax);
     uint64_t *o = ws + ((int64_t)row * n_chunks + chunk) * k;
@@ -485,7 +515,8 @@ __global__ __launch_bounds__(NT) void topk_chunk_kernel(const float *__restrict_
 template <int NT>
 __global__ __launch_bounds__(NT) void topk_merge_seg_kernel(const uint64_t *__restrict__ ws,
                                                             int n_chunks, int k,
-                                                            int32_t *__restrict__ out, int parts,
+                                                            int32_t *__restrict__ out,
+                                                            int64_t out_stride, int parts,
                                                             int seg_len)
 {
     using S = Topk32Smem<NT, kMergeCacheKeys>;
@@ -549,7 +580,7 @@ __global__ __launch_bounds__(NT) void topk_merge_seg_kernel(const uint64_t *__re
     }
     __syncthreads();
     const int m = min(k, n_valid);
-    int32_t *o = out + (int64_t)row * k;
+    int32_t *o = out + (int64_t)row * out_stride;
     const int p0 = seg * seg_len, p1 = min(p0 + seg_len, k);
     for (int i = max(p0, m) + tid; i < p1; i += NT)
         o[i] = -1;
@@ -704,48 +735,63 @@ hipError_t topk_scratch(void **ptr)
 
 hipError_t launch_topk(const TopkArgs &a, hipStream_t st)
 {
+    // attention sinks take the first n_s ranks of every row; the kernels
+    // below rank the rest of the visible range into the remaining k - n_s
+    // places (rows keep their stride k)
+    const int n_s = std::min(std::max(a.n_sink, 0), a.k);
+    if (n_s > 0) {
+        const int64_t blocks = ((int64_t)a.rows * n_s + 255) / 256;
+        hipLaunchKernelGGL(topk_sink_prefix_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
+                           a.vis_lo, a.vis_hi, a.n_cols, a.rows, n_s, a.k, a.out);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess || n_s == a.k)
+            return e;
+    }
+    const int k = a.k - n_s;
+    int32_t *const out = a.out + n_s;
+    const int64_t ostride = a.k;
     // sort sizes: NT threads x EPT keys >= k
     if (a.n_cols <= kCapSmall) {
         // value buckets place each winner without sorting the row; several
         // blocks per row when there are few rows
-        const int parts = topk_seg_parts(a.rows, a.k, 16);
-        const int seg_len = (a.k + parts - 1) / parts;
+        const int parts = topk_seg_parts(a.rows, k, 16);
+        const int seg_len = (k + parts - 1) / parts;
         hipLaunchKernelGGL((topk_seg_kernel<512, kCapSmall>), dim3(a.rows * parts), dim3(512), 0,
-                           st, a.scores, a.n_cols, a.row_stride, a.vis_lo, a.vis_hi, a.k, a.out,
-                           parts, seg_len);
+                           st, a.scores, a.n_cols, a.row_stride, a.vis_lo, a.vis_hi, k, out,
+                           ostride, n_s, parts, seg_len);
         return hipGetLastError();
     }
     constexpr int NT = 1024;
     if (a.n_cols <= kCapLarge) {
         // few rows: several blocks per row, each writing a segment of it
-        const int parts = topk_seg_parts(a.rows, a.k, 16);
-        const int seg_len = (a.k + parts - 1) / parts;
+        const int parts = topk_seg_parts(a.rows, k, 16);
+        const int seg_len = (k + parts - 1) / parts;
         hipLaunchKernelGGL((topk_seg_kernel<NT, kCapLarge>), dim3(a.rows * parts), dim3(NT), 0,
-                           st, a.scores, a.n_cols, a.row_stride, a.vis_lo, a.vis_hi, a.k, a.out,
-                           parts, seg_len);
+                           st, a.scores, a.n_cols, a.row_stride, a.vis_lo, a.vis_hi, k, out,
+                           ostride, n_s, parts, seg_len);
         return hipGetLastError();
     }
     const int n_chunks = (a.n_cols + kCapLarge - 1) / kCapLarge;
     hipLaunchKernelGGL((topk_chunk_kernel<NT, kCapLarge>), dim3(a.rows * n_chunks), dim3(NT), 0,
-                       st, a.scores, a.n_cols, a.row_stride, a.vis_lo, a.vis_hi, a.k,
-                       static_cast<uint64_t *>(a.workspace), n_chunks);
+                       st, a.scores, a.n_cols, a.row_stride, a.vis_lo, a.vis_hi, k,
+                       static_cast<uint64_t *>(a.workspace), n_chunks, n_s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    const int mparts = topk_seg_parts(a.rows, a.k, 32);
-    if ((int64_t)n_chunks * a.k <= kMergeCacheKeys && mparts > 1) {
-        const int seg_len = (a.k + mparts - 1) / mparts;
+    const int mparts = topk_seg_parts(a.rows, k, 32);
+    if ((int64_t)n_chunks * k <= kMergeCacheKeys && mparts > 1) {
+        const int seg_len = (k + mparts - 1) / mparts;
         hipLaunchKernelGGL((topk_merge_seg_kernel<NT>), dim3(a.rows * mparts), dim3(NT), 0, st,
-                           static_cast<const uint64_t *>(a.workspace), n_chunks, a.k, a.out,
+                           static_cast<const uint64_t *>(a.workspace), n_chunks, k, out, ostride,
                            mparts, seg_len);
         return hipGetLastError();
     }
-    if ((int64_t)n_chunks * a.k <= kMergeCacheKeys)
+    if ((int64_t)n_chunks * k <= kMergeCacheKeys)
         hipLaunchKernelGGL((topk_merge_kernel<NT, 2, true>), dim3(a.rows), dim3(NT), 0, st,
-                           static_cast<const uint64_t *>(a.workspace), n_chunks, a.k, a.out);
+                           static_cast<const uint64_t *>(a.workspace), n_chunks, k, out, ostride);
     else
         hipLaunchKernelGGL((topk_merge_kernel<NT, 2, false>), dim3(a.rows), dim3(NT), 0, st,
-                           static_cast<const uint64_t *>(a.workspace), n_chunks, a.k, a.out);
+                           static_cast<const uint64_t *>(a.workspace), n_chunks, k, out, ostride);
     return hipGetLastError();
 }
 

@@ -230,34 +230,43 @@ void topk()
           (size_t)INT32_MAX * 131072 * 2048 * 8);
     CHECK(dsa_topk_workspace_size(INT32_MAX, INT32_MAX, INT32_MAX) == 0);
     CHECK(dsa_topk_workspace_size(-3, 100000, 16) == 0);
-    EXPECT(dsa_topk(S, 32, 8192, 8192, kLo, kHi, 2048, out, nullptr, 0, kStream), DSA_OK, "topk");
+    EXPECT(dsa_topk(S, 32, 8192, 8192, kLo, kHi, 2048, 0, out, nullptr, 0, kStream), DSA_OK, "topk");
     CHECK(g_topk.workspace == nullptr && g_topk.k == 2048);
-    EXPECT(dsa_topk(S, 8, 131072, 131072, kLo, kHi, 2048, out, ws, need - 1, kStream),
+    EXPECT(dsa_topk(S, 8, 131072, 131072, kLo, kHi, 2048, 0, out, ws, need - 1, kStream),
            DSA_ERR_WORKSPACE, nullptr);
-    EXPECT(dsa_topk(S, 8, 131072, 131072, kLo, kHi, 2048, out, nullptr, need, kStream),
+    EXPECT(dsa_topk(S, 8, 131072, 131072, kLo, kHi, 2048, 0, out, nullptr, need, kStream),
            DSA_ERR_WORKSPACE, nullptr);
-    EXPECT(dsa_topk(S, 8, 131072, 131072, kLo, kHi, 2048, out, ws, need, kStream), DSA_OK,
+    EXPECT(dsa_topk(S, 8, 131072, 131072, kLo, kHi, 2048, 0, out, ws, need, kStream), DSA_OK,
            "topk");
     CHECK(g_topk.workspace == ws);
-    EXPECT(dsa_topk(S, 8, 100, 99, kLo, kHi, 16, out, nullptr, 0, kStream), DSA_ERR_ARG, nullptr);
-    EXPECT(dsa_topk(S, 8, 100, 100, kLo, kHi, 0, out, nullptr, 0, kStream), DSA_ERR_ARG, nullptr);
-    EXPECT(dsa_topk(S, 8, 100, 100, kLo, kHi, 2049, out, nullptr, 0, kStream),
+    EXPECT(dsa_topk(S, 8, 100, 99, kLo, kHi, 16, 0, out, nullptr, 0, kStream), DSA_ERR_ARG, nullptr);
+    EXPECT(dsa_topk(S, 8, 100, 100, kLo, kHi, 0, 0, out, nullptr, 0, kStream), DSA_ERR_ARG, nullptr);
+    EXPECT(dsa_topk(S, 8, 100, 100, kLo, kHi, 2049, 0, out, nullptr, 0, kStream),
            DSA_ERR_UNSUPPORTED, nullptr);
-    EXPECT(dsa_topk(S, 0, 100, 100, kLo, kHi, 16, out, nullptr, 0, kStream), DSA_OK, nullptr);
-    EXPECT(dsa_topk(S, 8, 100, 100, nullptr, kHi, 16, out, nullptr, 0, kStream), DSA_ERR_ARG,
+    EXPECT(dsa_topk(S, 0, 100, 100, kLo, kHi, 16, 0, out, nullptr, 0, kStream), DSA_OK, nullptr);
+    EXPECT(dsa_topk(S, 8, 100, 100, nullptr, kHi, 16, 0, out, nullptr, 0, kStream), DSA_ERR_ARG,
            nullptr);
-    EXPECT(dsa_topk(S, INT32_MAX, 100, INT64_MAX, kLo, kHi, 16, out, nullptr, 0, kStream),
+    EXPECT(dsa_topk(S, INT32_MAX, 100, INT64_MAX, kLo, kHi, 16, 0, out, nullptr, 0, kStream),
            DSA_ERR_UNSUPPORTED, nullptr);
-    EXPECT(dsa_topk(S, 8, -1, 100, kLo, kHi, 16, out, nullptr, 0, kStream), DSA_ERR_ARG, nullptr);
+    EXPECT(dsa_topk(S, 8, -1, 100, kLo, kHi, 16, 0, out, nullptr, 0, kStream), DSA_ERR_ARG, nullptr);
+    // attention sinks: passed through; a negative count is refused
+    EXPECT(dsa_topk(S, 32, 8192, 8192, kLo, kHi, 2048, 3, out, nullptr, 0, kStream), DSA_OK,
+           "topk");
+    CHECK(g_topk.n_sink == 3 && g_topk.k == 2048);
+    EXPECT(dsa_topk(S, 32, 8192, 8192, kLo, kHi, 2048, -1, out, nullptr, 0, kStream), DSA_ERR_ARG,
+           nullptr);
+    EXPECT(dsa_topk_noalloc(S, 8, 131072, 131072, kLo, kHi, 2048, 1, out, kStream), DSA_OK,
+           "topk");
+    CHECK(g_topk.n_sink == 1);
     // the allocation-free variant: the scratch array in place of a workspace
-    EXPECT(dsa_topk_noalloc(S, 8, 131072, 131072, kLo, kHi, 2048, out, kStream), DSA_OK, "topk");
+    EXPECT(dsa_topk_noalloc(S, 8, 131072, 131072, kLo, kHi, 2048, 0, out, kStream), DSA_OK, "topk");
     CHECK(g_topk.workspace == &g_scratch_token);
-    EXPECT(dsa_topk_noalloc(S, 32, 8192, 8192, kLo, kHi, 2048, out, kStream), DSA_OK, "topk");
+    EXPECT(dsa_topk_noalloc(S, 32, 8192, 8192, kLo, kHi, 2048, 0, out, kStream), DSA_OK, "topk");
     CHECK(g_topk.workspace == nullptr);
     // 16 MiB of scratch: 1024 rows of 32768 keys at k = 2048 need 32 MiB
-    EXPECT(dsa_topk_noalloc(S, 1024, 32768, 32768, kLo, kHi, 2048, out, kStream),
+    EXPECT(dsa_topk_noalloc(S, 1024, 32768, 32768, kLo, kHi, 2048, 0, out, kStream),
            DSA_ERR_UNSUPPORTED, nullptr);
-    EXPECT(dsa_topk_noalloc(S, 8, 100, 100, kLo, kHi, 4096, out, kStream), DSA_ERR_UNSUPPORTED,
+    EXPECT(dsa_topk_noalloc(S, 8, 100, 100, kLo, kHi, 4096, 0, out, kStream), DSA_ERR_UNSUPPORTED,
            nullptr);
 }
 
@@ -423,9 +432,28 @@ void pools()
 }
 } // namespace
 
+void index_share()
+{
+    // the pages' enumeration: full layers 0, 1, 2, then every 4th up to 74
+    int n_full = 0, last_full = -1;
+    for (int il = 0; il < 78; ++il) {
+        const bool full = il <= 2 || (il >= 6 && (il - 2) % 4 == 0);
+        if (full) {
+            ++n_full;
+            last_full = il;
+        }
+        CHECK(dsa_index_share_source(il) == last_full);
+    }
+    CHECK(n_full == 21);
+    CHECK(dsa_index_share_source(-1) == -1);
+    CHECK(dsa_index_share_source(INT32_MIN) == -1);
+    CHECK(dsa_index_share_source(INT32_MAX) == INT32_MAX - (INT32_MAX - 2) % 4);
+}
+
 int main()
 {
     CHECK(std::strlen(dsa_version()) > 0);
+    index_share();
     ranges();
     index_scores();
     topk();

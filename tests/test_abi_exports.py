@@ -46,9 +46,9 @@ def test_host_side_validation_without_gpu():
     """Argument errors are reported before anything touches the GPU."""
     from sparse_attention_scores_amd import binding
     lib = binding.load()
-    assert lib.dsa_topk(None, 1, 10, 10, None, None, 0, None, None, 0, None) == -1
+    assert lib.dsa_topk(None, 1, 10, 10, None, None, 0, 0, None, None, 0, None) == -1
     assert b"top_k" in lib.dsa_last_error()
-    assert lib.dsa_topk(None, 1, 10, 10, None, None, 4096, None, None, 0, None) == -2
+    assert lib.dsa_topk(None, 1, 10, 10, None, None, 4096, 0, None, None, 0, None) == -2
     assert lib.dsa_index_scores(None, None, 0, None, 0, None, None, None, None, None, None) == -1
     assert lib.dsa_topk_workspace_size(8, 131072, 2048) > 0
     assert lib.dsa_topk_workspace_size(8, 8192, 2048) == 0
@@ -64,9 +64,9 @@ def test_workspace_errors_without_gpu():
     # long rows: the chunked top-k keeps its chunk winners in the workspace
     need = lib.dsa_topk_workspace_size(1, 20000, 2048)
     assert need == 2 * 2048 * 8
-    assert lib.dsa_topk(fake, 1, 20000, 20000, fake, fake, 2048, fake, None, 0, None) == -4
+    assert lib.dsa_topk(fake, 1, 20000, 20000, fake, fake, 2048, 0, fake, None, 0, None) == -4
     assert b"workspace" in lib.dsa_last_error()
-    assert lib.dsa_topk(fake, 1, 20000, 20000, fake, fake, 2048, fake, fake, need - 1,
+    assert lib.dsa_topk(fake, 1, 20000, 20000, fake, fake, 2048, 0, fake, fake, need - 1,
                         None) == -4
     # few decode rows: the gather kernel's split-K partials
     dims = binding._AttnDims(2, 1, 8192, 64, 576, 512, 1, 2048, 576 ** -0.5)
@@ -126,7 +126,18 @@ def test_noalloc_topk_limit_without_gpu():
     fake = ctypes.c_void_p(0x1000)
     # 2000 rows of 20000 keys at k 2048 need 2000 * 2 * 2048 * 8 bytes > 16 MiB
     assert lib.dsa_topk_workspace_size(2000, 20000, 2048) > (16 << 20)
-    rc = lib.dsa_topk_noalloc(fake, 2000, 20000, 20000, fake, fake, 2048, fake, None)
+    rc = lib.dsa_topk_noalloc(fake, 2000, 20000, 20000, fake, fake, 2048, 0, fake, None)
     assert rc == -2
     assert b"scratch" in lib.dsa_last_error()
-    assert lib.dsa_topk_noalloc(fake, 1, 10, 10, fake, fake, 0, fake, None) == -1
+    assert lib.dsa_topk_noalloc(fake, 1, 10, 10, fake, fake, 0, 0, fake, None) == -1
+
+
+def test_index_share_rule_without_gpu():
+    """dsa_index_share_source (host function) against the oracle's rule and
+    the pages' 21 full layers of 78."""
+    import oracle
+    from sparse_attention_scores_amd import binding
+    for il in range(-3, 400):
+        assert binding.index_share_source(il) == oracle.index_share_source(il), il
+    full = [il for il in range(78) if binding.index_share_source(il) == il]
+    assert full == [0, 1, 2] + list(range(6, 75, 4))
