@@ -373,3 +373,89 @@ def index_cache_write(k_new, kv_head, cache, scales=None):
                 else:
                     cache[b, r] = bits[b, i]
     return cache, scales
+
+
+# --------------------------------------------------------------------------
+# dense projections ahead of the path: the indexer front-end ("Another DSA
+# attempt": the batch-local indexer commit; the CPU crash-fix commit and the
+# review on the k_norm eps) and expand_kv ("Module glm5next_dsa_ref":
+# expand_kv, linear, layer_norm, and the NoPE invariant).  Plain float64
+# numpy; a bf16 input is decoded exactly from its bits.
+# --------------------------------------------------------------------------
+
+def _as_f64(a):
+    """float64 copy of a numpy array or CPU torch tensor (bf16 decoded from
+    its bits: the 16 bits are the top half of the f32 value)."""
+    arr, code = _storage(a)
+    if code == BF16:
+        return (arr.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    if code == E4M3:
+        raise TypeError("fp8 input is not a projection operand")
+    return arr.astype(np.float64)
+
+
+def linear(x, w):
+    """y = x @ w^T ("Module glm5next_dsa_ref" linear: torch Linear layout,
+    w [n, k], no bias) over the last axis of x, in float64."""
+    xa, wa = _as_f64(x), _as_f64(w)
+    assert xa.shape[-1] == wa.shape[1]
+    return xa @ wa.T
+
+
+def layer_norm(x, weight, bias, eps):
+    """LayerNorm over the last axis ("Module glm5next_dsa_ref" layer_norm and
+    its k_norm invariant: subtract the mean, divide by the standard deviation
+    -- population variance, eps added inside the root -- then w * x + b)."""
+    xa = _as_f64(x)
+    mu = xa.mean(axis=-1, keepdims=True)
+    var = ((xa - mu) ** 2).mean(axis=-1, keepdims=True)
+    return (xa - mu) / np.sqrt(var + float(eps)) * _as_f64(weight) + _as_f64(bias)
+
+
+def rope_neox(x, pos, rope_dim, theta):
+    """NEOX-style rotary embedding of the first rope_dim entries of the last
+    axis ("Another DSA attempt", batch-local indexer commit: the rope part is
+    rotated NEOX-style, the rest passes through).  With h = rope_dim / 2,
+    entries i and i + h (i < h) form one pair, rotated by the angle
+    pos * theta^(-2i / rope_dim).  x: [T, ..., D]; pos: [T]."""
+    xa = _as_f64(x).copy()
+    h = rope_dim // 2
+    assert rope_dim % 2 == 0 and rope_dim <= xa.shape[-1]
+    i = np.arange(h, dtype=np.float64)
+    inv = float(theta) ** (-2.0 * i / rope_dim)
+    p = np.asarray(pos, np.float64).reshape((-1,) + (1,) * (xa.ndim - 1))
+    ang = p * inv                                    # [T, 1.., h]
+    c, s = np.cos(ang), np.sin(ang)
+    a, b = xa[..., :h].copy(), xa[..., h:rope_dim].copy()
+    xa[..., :h] = a * c - b * s
+    xa[..., h:rope_dim] = b * c + a * s
+    return xa
+
+
+def indexer_frontend(q_lora, x, pos, wq_b, wk, k_norm_w, k_norm_b, w_proj, n_heads,
+                     rope_dim, theta, eps):
+    """The lightning indexer's inputs from the layer's activations ("Another
+    DSA attempt", batch-local indexer commit): q = wq_b(q_lora) per head,
+    rope part NEOX-rotated at the token's position, rest unchanged;
+    k = LayerNorm-with-bias(wk(x)), rotated the same way (one key head);
+    w = weights_proj(x).  The pages split each head vector as rope(64) then
+    nope(64) and concatenate in that order, so the rope part is the leading
+    rope_dim entries.  Returns float64 (q [T, H, d], k [T, d], w [T, H])."""
+    q = linear(q_lora, wq_b)
+    T = q.shape[0]
+    q = rope_neox(q.reshape(T, n_heads, -1), pos, rope_dim, theta)
+    k = rope_neox(layer_norm(linear(x, wk), k_norm_w, k_norm_b, eps), pos, rope_dim, theta)
+    w = linear(x, w_proj)
+    return q, k, w
+
+
+def expand_kv(latent, w_kv_b, n_heads, kd, vd):
+    """Per-head K and V from the compressed latent ("Module glm5next_dsa_ref"
+    expand_kv, NoPE: K is exactly the no-rope head width kd).  The projection
+    rows are head-major, each head's kd key rows followed by its vd value
+    rows (torch Linear layout w [n_heads * (kd + vd), r]).  latent: [T, r].
+    Returns float64 (K [T, H, kd], V [T, H, vd])."""
+    y = linear(latent, w_kv_b)
+    T = y.shape[0]
+    y = y.reshape(T, n_heads, kd + vd)
+    return y[..., :kd].copy(), y[..., kd:].copy()
