@@ -197,6 +197,75 @@ int dsa_topk_noalloc(const float *scores, int32_t rows, int32_t n_cols,
                      int32_t *out_idx, void *stream);
 
 /* ------------------------------------------------------------------------
+ * The indexer front-end: the indexer's q, k and head weights from the
+ * layer's activations.
+ *
+ * [ik] batch-local indexer commit: indexer_q = wq_b(q_lora latent), each
+ * head split rope(64) / nope(64), the rope part NEOX-rotated, concatenated
+ * back; indexer_k = wk(attention-norm output), then LayerNorm with bias
+ * (k_norm), then the same rotation (one key head); the head weights come
+ * from weights_proj.  [metrale] layer_norm: subtract the mean, divide by
+ * the standard deviation, then w * x + b; linear: y = x w^T.  [ik] CPU
+ * crash-fix commit and review: k_norm's eps must be positive (1e-6 in the
+ * reference, the model's 1e-5 in one port).
+ *
+ * For token t at position pos[t]:
+ *   q[t,h,:] = rope(q_lora[t,:] wq_b[h*128 .. h*128+128, :]^T)
+ *   k[t,:]   = rope(LayerNorm(x[t,:] wk^T; k_norm_w, k_norm_b, norm_eps))
+ *   w[t,:]   = x[t,:] w_proj^T
+ * where rope rotates entries i and i + rope_dim/2 (i < rope_dim/2) of a
+ * 128-vector by the angle pos * rope_theta^(-2i/rope_dim) and leaves
+ * entries >= rope_dim unchanged (NEOX pairing).  The variance is the
+ * population variance; eps is added inside the square root.
+ *
+ * q_lora: [tokens, q_lora_rank] bf16;  x: [tokens, hidden] bf16
+ * pos:    [tokens] int32 positions
+ * wq_b:   [n_heads*128, q_lora_rank] bf16;  wk: [128, hidden] bf16
+ * w_proj: [n_heads, hidden] bf16;  k_norm_w, k_norm_b: [128] f32
+ * q_out:  [tokens, n_heads, 128] bf16 output (round to nearest even)
+ * k_out:  [tokens, 128] bf16 output;  w_out: [tokens, n_heads] f32 output
+ * All device pointers; outputs must not overlap inputs; every pointer
+ * 16-byte aligned.  Products run on bf16 MFMA with f32 accumulation; the
+ * LayerNorm and rotation in f32 with the angle reduced in f64.
+ * Envelope: head_dim == 128, n_heads in {32, 64}, rope_dim a multiple of 16
+ * in [16, 128], q_lora_rank and hidden multiples of 64, norm_eps > 0.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+    int32_t tokens, q_lora_rank, hidden, n_heads, head_dim, rope_dim;
+    float rope_theta, norm_eps;
+} dsa_frontend_dims;
+
+int dsa_indexer_frontend(const dsa_frontend_dims *d, const void *q_lora,
+                         const void *x, const int32_t *pos, const void *wq_b,
+                         const void *wk, const float *k_norm_w,
+                         const float *k_norm_b, const void *w_proj,
+                         void *q_out, void *k_out, float *w_out, void *stream);
+
+/* ------------------------------------------------------------------------
+ * expand_kv: per-head K and V from the compressed latent ([metrale]
+ * expand_kv: NoPE only, so K is exactly the no-rope head width kd).
+ *
+ * y = latent w_kv_b^T, w_kv_b in torch Linear layout with head-major rows,
+ * each head's kd key rows followed by its vd value rows:
+ *   K[t,h,:] = y[t, h*(kd+vd) .. h*(kd+vd)+kd)
+ *   V[t,h,:] = y[t, h*(kd+vd)+kd .. (h+1)*(kd+vd))
+ * latent: [tokens, rank] bf16;  w_kv_b: [n_heads*(kd+vd), rank] bf16
+ * k_out:  token t's heads at k_out + t*k_row_stride, head h at +h*kd (bf16)
+ * v_out:  likewise with v_row_stride and vd (bf16)
+ * bf16 MFMA with f32 accumulation, one rounding to bf16 (nearest even).
+ * Envelope: rank a multiple of 64; kd, vd multiples of 8; row strides
+ * multiples of 8 elements with k_row_stride >= n_heads*kd and
+ * v_row_stride >= n_heads*vd; pointers 16-byte aligned.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+    int32_t tokens, rank, n_heads, kd, vd;
+} dsa_expand_dims;
+
+int dsa_expand_kv(const dsa_expand_dims *d, const void *latent,
+                  const void *w_kv_b, void *k_out, int64_t k_row_stride,
+                  void *v_out, int64_t v_row_stride, void *stream);
+
+/* ------------------------------------------------------------------------
  * IndexShare: which layer's selection a layer attends with.
  *
  * [ik] IndexShare commit message and review comments: GLM-5.2 marks 21 of

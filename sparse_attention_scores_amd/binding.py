@@ -47,6 +47,18 @@ class _CacheDims(ctypes.Structure):
                 ("head_dim", ctypes.c_int32)]
 
 
+class _FrontendDims(ctypes.Structure):
+    _fields_ = [("tokens", ctypes.c_int32), ("q_lora_rank", ctypes.c_int32),
+                ("hidden", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("rope_dim", ctypes.c_int32),
+                ("rope_theta", ctypes.c_float), ("norm_eps", ctypes.c_float)]
+
+
+class _ExpandDims(ctypes.Structure):
+    _fields_ = [("tokens", ctypes.c_int32), ("rank", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+                ("kd", ctypes.c_int32), ("vd", ctypes.c_int32)]
+
+
 class _PoolDims(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("seq", ctypes.c_int32), ("n_q", ctypes.c_int32),
                 ("kpool", ctypes.c_int32), ("head_dim", ctypes.c_int32),
@@ -59,7 +71,8 @@ EXPORTS = ("dsa_last_error", "dsa_version", "dsa_visibility_ranges", "dsa_index_
            "dsa_topk_workspace_size", "dsa_topk", "dsa_topk_noalloc", "dsa_index_share_source",
            "dsa_sparse_attend_workspace_size",
            "dsa_sparse_attend", "dsa_pool_keys", "dsa_pool_select_workspace_size",
-           "dsa_pool_select", "dsa_hadamard_rotate", "dsa_index_cache_write")
+           "dsa_pool_select", "dsa_hadamard_rotate", "dsa_index_cache_write",
+           "dsa_indexer_frontend", "dsa_expand_kv")
 
 
 def _hip_runtimes_mapped():
@@ -111,6 +124,8 @@ def load():
         lib.dsa_pool_select.argtypes = [P, P, P, P, P, P, P, SZ, P]
         lib.dsa_hadamard_rotate.argtypes = [I64, I32, P, ctypes.c_int, P, ctypes.c_int, P]
         lib.dsa_index_cache_write.argtypes = [P, P, ctypes.c_int, P, P, ctypes.c_int, P, P]
+        lib.dsa_indexer_frontend.argtypes = [P] * 13
+        lib.dsa_expand_kv.argtypes = [P, P, P, P, I64, P, I64, P]
         _lib = lib
         return lib
 
@@ -398,3 +413,72 @@ def index_cache_write(k_new, kv_head, cache, k_scale=None):
                                         _p(kv_head), _p(cache), _dtype_code(cache), _p(k_scale),
                                         _stream()))
     return cache, k_scale
+
+
+def indexer_frontend(q_lora, x, pos, wq_b, wk, k_norm_w, k_norm_b, w_proj, n_heads: int,
+                     rope_dim: int, rope_theta: float, norm_eps: float, q_out=None, k_out=None,
+                     w_out=None):
+    """The indexer's q [T, n_heads, 128] bf16, k [T, 128] bf16 and head
+    weights [T, n_heads] f32 from q_lora [T, r_q] and x [T, hidden] (bf16)
+    at positions pos [T] (int32)."""
+    _dev(q_lora, x, pos, wq_b, wk, k_norm_w, k_norm_b, w_proj, q_out, k_out, w_out)
+    T, r_q = q_lora.shape
+    hidden = x.shape[1]
+    for t, nm in ((q_lora, "q_lora"), (x, "x"), (wq_b, "wq_b"), (wk, "wk"), (w_proj, "w_proj")):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise TypeError(f"indexer_frontend: {nm} must be contiguous bf16")
+    _shape(x, (T, hidden), "indexer_frontend: x", torch.bfloat16)
+    _shape(pos, (T,), "indexer_frontend: pos", torch.int32)
+    _shape(wq_b, (n_heads * 128, r_q), "indexer_frontend: wq_b", torch.bfloat16)
+    _shape(wk, (128, hidden), "indexer_frontend: wk", torch.bfloat16)
+    _shape(w_proj, (n_heads, hidden), "indexer_frontend: w_proj", torch.bfloat16)
+    _shape(k_norm_w, (128,), "indexer_frontend: k_norm_w", torch.float32)
+    _shape(k_norm_b, (128,), "indexer_frontend: k_norm_b", torch.float32)
+    dev = q_lora.device
+    if q_out is None:
+        q_out = torch.empty((T, n_heads, 128), dtype=torch.bfloat16, device=dev)
+    if k_out is None:
+        k_out = torch.empty((T, 128), dtype=torch.bfloat16, device=dev)
+    if w_out is None:
+        w_out = torch.empty((T, n_heads), dtype=torch.float32, device=dev)
+    _shape(q_out, (T, n_heads, 128), "indexer_frontend: q_out", torch.bfloat16)
+    _shape(k_out, (T, 128), "indexer_frontend: k_out", torch.bfloat16)
+    _shape(w_out, (T, n_heads), "indexer_frontend: w_out", torch.float32)
+    for t, nm in ((pos, "pos"), (k_norm_w, "k_norm_w"), (k_norm_b, "k_norm_b"), (q_out, "q_out"),
+                  (k_out, "k_out"), (w_out, "w_out")):
+        if not t.is_contiguous():
+            raise ValueError(f"indexer_frontend: {nm} must be contiguous")
+    dims = _FrontendDims(T, r_q, hidden, n_heads, 128, rope_dim, float(rope_theta),
+                         float(norm_eps))
+    _check(load().dsa_indexer_frontend(ctypes.byref(dims), _p(q_lora), _p(x), _p(pos), _p(wq_b),
+                                       _p(wk), _p(k_norm_w), _p(k_norm_b), _p(w_proj), _p(q_out),
+                                       _p(k_out), _p(w_out), _stream()))
+    return q_out, k_out, w_out
+
+
+def expand_kv(latent, w_kv_b, n_heads: int, kd: int, vd: int, k_out=None, v_out=None):
+    """Per-head K [T, n_heads, kd] and V [T, n_heads, vd] (bf16) from the
+    latent [T, rank] and w_kv_b [n_heads * (kd + vd), rank] (bf16).  Outputs
+    may be views whose token stride is larger (e.g. [B, L, H, kd] slices)."""
+    _dev(latent, w_kv_b)
+    for t in (k_out, v_out):
+        if t is not None and not t.is_cuda:
+            raise ValueError("libdsa takes device tensors")
+    T, rank = latent.shape
+    for t, nm in ((latent, "latent"), (w_kv_b, "w_kv_b")):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise TypeError(f"expand_kv: {nm} must be contiguous bf16")
+    _shape(w_kv_b, (n_heads * (kd + vd), rank), "expand_kv: w_kv_b", torch.bfloat16)
+    dev = latent.device
+    if k_out is None:
+        k_out = torch.empty((T, n_heads, kd), dtype=torch.bfloat16, device=dev)
+    if v_out is None:
+        v_out = torch.empty((T, n_heads, vd), dtype=torch.bfloat16, device=dev)
+    for t, w, nm in ((k_out, kd, "k_out"), (v_out, vd, "v_out")):
+        if (t.dtype != torch.bfloat16 or t.dim() != 3 or tuple(t.shape) != (T, n_heads, w)
+                or t.stride(-1) != 1 or t.stride(-2) != w):
+            raise ValueError(f"expand_kv: {nm} must be bf16 [T, {n_heads}, {w}] with contiguous heads")
+    dims = _ExpandDims(T, rank, n_heads, kd, vd)
+    _check(load().dsa_expand_kv(ctypes.byref(dims), _p(latent), _p(w_kv_b), _p(k_out),
+                                k_out.stride(-3), _p(v_out), v_out.stride(-3), _stream()))
+    return k_out, v_out

@@ -217,6 +217,91 @@ int dsa_topk_noalloc(const float *scores, int32_t rows, int32_t n_cols, int64_t 
     return hip_status(dsa::launch_topk(a, as_stream(stream)), "dsa_topk_noalloc");
 }
 
+static bool aligned16(const void *p)
+{
+    return ((uintptr_t)p & 15u) == 0;
+}
+
+int dsa_indexer_frontend(const dsa_frontend_dims *d, const void *q_lora, const void *x,
+                         const int32_t *pos, const void *wq_b, const void *wk,
+                         const float *k_norm_w, const float *k_norm_b, const void *w_proj,
+                         void *q_out, void *k_out, float *w_out, void *stream)
+{
+    if (!d)
+        return fail(DSA_ERR_ARG, "dsa_indexer_frontend: dims is NULL");
+    if (d->tokens < 0 || d->q_lora_rank <= 0 || d->hidden <= 0 || d->n_heads <= 0 ||
+        d->head_dim <= 0 || d->rope_dim < 0)
+        return fail(DSA_ERR_ARG, "dsa_indexer_frontend: bad dims");
+    if (!(d->norm_eps > 0.f) || !(d->rope_theta > 0.f))
+        return fail(DSA_ERR_ARG, "dsa_indexer_frontend: norm_eps and rope_theta must be positive");
+    if (d->head_dim != 128 || (d->n_heads != 32 && d->n_heads != 64) || d->rope_dim < 16 ||
+        d->rope_dim > 128 || d->rope_dim % 16 != 0 || d->q_lora_rank % 64 != 0 ||
+        d->hidden % 64 != 0)
+        return fail(DSA_ERR_UNSUPPORTED,
+                    "dsa_indexer_frontend: needs head_dim 128, n_heads 32 or 64, rope_dim a "
+                    "multiple of 16 up to 128, q_lora_rank and hidden multiples of 64");
+    if (too_many({d->tokens, d->q_lora_rank}) || too_many({d->tokens, d->hidden}) ||
+        too_many({d->tokens, d->n_heads, d->head_dim}))
+        return fail(DSA_ERR_UNSUPPORTED, "dsa_indexer_frontend: tensors too large");
+    if (d->tokens == 0)
+        return ok();
+    if (!q_lora || !x || !pos || !wq_b || !wk || !k_norm_w || !k_norm_b || !w_proj || !q_out ||
+        !k_out || !w_out)
+        return fail(DSA_ERR_ARG, "dsa_indexer_frontend: null pointer");
+    if (!aligned16(q_lora) || !aligned16(x) || !aligned16(wq_b) || !aligned16(wk) ||
+        !aligned16(w_proj) || !aligned16(q_out) || !aligned16(k_out) || !aligned16(w_out))
+        return fail(DSA_ERR_UNSUPPORTED, "dsa_indexer_frontend: pointers must be 16-byte aligned");
+    dsa::FrontendArgs a{};
+    a.tokens = d->tokens;
+    a.q_lora_rank = d->q_lora_rank;
+    a.hidden = d->hidden;
+    a.n_heads = d->n_heads;
+    a.rope_dim = d->rope_dim;
+    a.rope_theta = d->rope_theta;
+    a.norm_eps = d->norm_eps;
+    a.q_lora = q_lora;
+    a.x = x;
+    a.pos = pos;
+    a.wq_b = wq_b;
+    a.wk = wk;
+    a.w_proj = w_proj;
+    a.k_norm_w = k_norm_w;
+    a.k_norm_b = k_norm_b;
+    a.q_out = q_out;
+    a.k_out = k_out;
+    a.w_out = w_out;
+    return hip_status(dsa::launch_indexer_frontend(a, as_stream(stream)), "dsa_indexer_frontend");
+}
+
+int dsa_expand_kv(const dsa_expand_dims *d, const void *latent, const void *w_kv_b, void *k_out,
+                  int64_t k_row_stride, void *v_out, int64_t v_row_stride, void *stream)
+{
+    if (!d)
+        return fail(DSA_ERR_ARG, "dsa_expand_kv: dims is NULL");
+    if (d->tokens < 0 || d->rank <= 0 || d->n_heads <= 0 || d->kd <= 0 || d->vd <= 0)
+        return fail(DSA_ERR_ARG, "dsa_expand_kv: bad dims");
+    if (k_row_stride < (int64_t)d->n_heads * d->kd || v_row_stride < (int64_t)d->n_heads * d->vd)
+        return fail(DSA_ERR_ARG, "dsa_expand_kv: row stride smaller than a token's heads");
+    if (d->rank % 64 != 0 || d->kd % 8 != 0 || d->vd % 8 != 0 || k_row_stride % 8 != 0 ||
+        v_row_stride % 8 != 0)
+        return fail(DSA_ERR_UNSUPPORTED,
+                    "dsa_expand_kv: rank must be a multiple of 64; kd, vd and the row strides "
+                    "multiples of 8");
+    if (too_many({d->n_heads, (int64_t)d->kd + d->vd}, 0x7fffffff) ||
+        too_many({d->tokens, d->rank}) || too_many({d->tokens, k_row_stride}) ||
+        too_many({d->tokens, v_row_stride}))
+        return fail(DSA_ERR_UNSUPPORTED, "dsa_expand_kv: tensors too large");
+    if (d->tokens == 0)
+        return ok();
+    if (!latent || !w_kv_b || !k_out || !v_out)
+        return fail(DSA_ERR_ARG, "dsa_expand_kv: null pointer");
+    if (!aligned16(latent) || !aligned16(w_kv_b) || !aligned16(k_out) || !aligned16(v_out))
+        return fail(DSA_ERR_UNSUPPORTED, "dsa_expand_kv: pointers must be 16-byte aligned");
+    dsa::ExpandArgs a{d->tokens, d->rank, d->n_heads, d->kd, d->vd, latent, w_kv_b,
+                      k_out,     v_out,   k_row_stride, v_row_stride};
+    return hip_status(dsa::launch_expand_kv(a, as_stream(stream)), "dsa_expand_kv");
+}
+
 int32_t dsa_index_share_source(int32_t layer)
 {
     if (layer < 0)

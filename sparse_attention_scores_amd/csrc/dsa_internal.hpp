@@ -106,6 +106,29 @@ hipError_t launch_hadamard_rotate(const void *x, bool x_f32, void *out, bool out
                                   int d, hipStream_t st);
 hipError_t launch_index_cache_write(const CacheWriteArgs &a, hipStream_t st);
 
+// the indexer front-end: q = rope(q_lora wq_b^T) per head of 128,
+// k = rope(LayerNorm(x wk^T)), w = x w_proj^T
+struct FrontendArgs {
+    int tokens, q_lora_rank, hidden, n_heads, rope_dim;
+    float rope_theta, norm_eps;
+    const void *q_lora, *x;
+    const int32_t *pos;
+    const void *wq_b, *wk, *w_proj;
+    const float *k_norm_w, *k_norm_b;
+    void *q_out, *k_out;
+    float *w_out;
+};
+hipError_t launch_indexer_frontend(const FrontendArgs &a, hipStream_t st);
+
+// expand_kv: per-head K and V from the latent
+struct ExpandArgs {
+    int tokens, rank, n_heads, kd, vd;
+    const void *latent, *w_kv_b;
+    void *k_out, *v_out;
+    int64_t k_row_stride, v_row_stride;
+};
+hipError_t launch_expand_kv(const ExpandArgs &a, hipStream_t st);
+
 struct RangeArgs {
     int batch, n_q, kpool;
     const int32_t *pad, *q_pos;

@@ -20,6 +20,15 @@ Configurations (all inputs synthetic; no checkpoint or dataset is used):
    (0, 2, 37, 64); kpool 4; indexer 32 x 128 with gate ~ N(0,1); top 512
    pools plus the visible tail, out_width 2052; per-head attention 64 heads,
    kd 192, vd 256.
+6. pooled decode: configuration 5's sequences and keys with one query per
+   sequence, at its last position.
+7. projections at configuration 5's token count (4 x 16384): the indexer
+   front-end (q_lora rank 2048, hidden 6144 -> 32 heads x 128, rope 64,
+   theta 10000, k_norm eps 1e-6) and expand_kv (latent rank 512 -> 64
+   heads x (192 + 256)).  The pages give no model widths; these are
+   stand-ins of the model's class.  Activations ~ N(0,1); weights
+   ~ N(0, 1/fan_in); the k_norm weight ~ 1 + N(0, 0.1^2), its bias
+   ~ N(0, 0.1^2); positions 0 .. 16383 per sequence.
 
 Tensors are drawn in a fixed order from one torch.Generator on the target
 device, seeded with ``1000 + config`` unless a seed is given.
@@ -44,6 +53,11 @@ CONFIGS = {
             dtype="bf16", causal=False, fp8_keys=True),
     5: dict(B=4, L=16384, pads=(0, 2, 37, 64), kpool=4, Hi=32, d=128, select_k=512,
             out_width=2052, H=64, kd=192, vd=256, dtype="bf16"),
+    6: dict(B=4, L=16384, pads=(0, 2, 37, 64), kpool=4, Hi=32, d=128, select_k=512,
+            out_width=2052, H=64, kd=192, vd=256, dtype="bf16", last_only=True),
+    7: dict(B=4, L=16384, q_lora_rank=2048, hidden=6144, Hi=32, d=128, rope_dim=64,
+            rope_theta=10000.0, norm_eps=1e-6, rank=512, H=64, kd=192, vd=256,
+            dtype="bf16"),
 }
 
 
@@ -92,8 +106,10 @@ def make(config: int, device="cpu", seed=None, variant=None, **over):
     out["config"] = config
     out["seed"] = seed
     out["variant"] = variant
-    if config == 5:
+    if config in (5, 6):
         return _make_pooled(cfg, gen, device, variant, out)
+    if config == 7:
+        return _make_projections(cfg, gen, device, out)
 
     B, Tq, Tk, Hi, d = cfg["B"], cfg["Tq"], cfg["Tk"], cfg["Hi"], cfg["d"]
     H, kd, vd = cfg["H"], cfg["kd"], cfg["vd"]
@@ -157,22 +173,46 @@ def _make_pooled(cfg, gen, device, variant, out):
     while len(pads) < B:
         pads.append(0)
     out["pad"] = torch.tensor(pads, dtype=torch.int32, device=device)
-    out["q_pos"] = torch.arange(L, dtype=torch.int32, device=device).repeat(B, 1)
-    out["Tq"] = L
+    last = cfg.get("last_only", False)
+    Tq = 1 if last else L
+    if last:
+        out["q_pos"] = torch.full((B, 1), L - 1, dtype=torch.int32, device=device)
+    else:
+        out["q_pos"] = torch.arange(L, dtype=torch.int32, device=device).repeat(B, 1)
+    out["Tq"] = Tq
     if variant == "tie":
         out["k_idx"] = to_bf16(_ints((B, L, d), -1, 2, gen, device))
         out["gate"] = to_bf16(_ints((B, L, d), -1, 2, gen, device))
-        out["q_idx"] = to_bf16(_ints((B, L, Hi, d), -1, 2, gen, device))
-        out["w"] = _ints((B, L, Hi), 1, 3, gen, device) * 0.5
+        out["q_idx"] = to_bf16(_ints((B, Tq, Hi, d), -1, 2, gen, device))
+        out["w"] = _ints((B, Tq, Hi), 1, 3, gen, device) * 0.5
     else:
         out["k_idx"] = to_bf16(_randn((B, L, d), gen, device, 1.0 / math.sqrt(d)))
         out["gate"] = to_bf16(_randn((B, L, d), gen, device))
-        out["q_idx"] = to_bf16(_randn((B, L, Hi, d), gen, device, 1.0 / math.sqrt(d)))
-        out["w"] = _rand((B, L, Hi), gen, device)
+        out["q_idx"] = to_bf16(_randn((B, Tq, Hi, d), gen, device, 1.0 / math.sqrt(d)))
+        out["w"] = _rand((B, Tq, Hi), gen, device)
     out["scale_idx"] = 1.0 / math.sqrt(d)
     out["scale_attn"] = 1.0 / math.sqrt(kd)
     qmul = 16.0 if variant == "sharp" else 1.0
-    out["q"] = to_bf16(_randn((B, L, H, kd), gen, device, qmul / math.sqrt(kd)))
+    out["q"] = to_bf16(_randn((B, Tq, H, kd), gen, device, qmul / math.sqrt(kd)))
     out["K"] = to_bf16(_randn((B, L, H, kd), gen, device, 1.0 / math.sqrt(kd)))
     out["V"] = to_bf16(_randn((B, L, H, vd), gen, device, 1.0 / math.sqrt(vd)))
+    return out
+
+
+def _make_projections(cfg, gen, device, out):
+    B, L = cfg["B"], cfg["L"]
+    T = B * L
+    r_q, hid, Hi, d = cfg["q_lora_rank"], cfg["hidden"], cfg["Hi"], cfg["d"]
+    rank, H, kd, vd = cfg["rank"], cfg["H"], cfg["kd"], cfg["vd"]
+    out["T"] = T
+    out["pos"] = torch.arange(L, dtype=torch.int32, device=device).repeat(B)
+    out["q_lora"] = to_bf16(_randn((T, r_q), gen, device))
+    out["x"] = to_bf16(_randn((T, hid), gen, device))
+    out["wq_b"] = to_bf16(_randn((Hi * d, r_q), gen, device, 1.0 / math.sqrt(r_q)))
+    out["wk"] = to_bf16(_randn((d, hid), gen, device, 1.0 / math.sqrt(hid)))
+    out["w_proj"] = to_bf16(_randn((Hi, hid), gen, device, 1.0 / math.sqrt(hid)))
+    out["k_norm_w"] = 1.0 + _randn((d,), gen, device, 0.1)
+    out["k_norm_b"] = _randn((d,), gen, device, 0.1)
+    out["latent"] = to_bf16(_randn((T, rank), gen, device))
+    out["w_kv_b"] = to_bf16(_randn((H * (kd + vd), rank), gen, device, 1.0 / math.sqrt(rank)))
     return out

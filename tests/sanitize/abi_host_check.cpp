@@ -104,6 +104,16 @@ hipError_t launch_pool_select(const PoolSelectArgs &, hipStream_t)
     g_launched = "pool_select";
     return hipSuccess;
 }
+hipError_t launch_indexer_frontend(const FrontendArgs &, hipStream_t)
+{
+    g_launched = "frontend";
+    return hipSuccess;
+}
+hipError_t launch_expand_kv(const ExpandArgs &, hipStream_t)
+{
+    g_launched = "expand_kv";
+    return hipSuccess;
+}
 } // namespace dsa
 
 // ---------------------------------------------------------------- checks
@@ -450,8 +460,55 @@ void index_share()
     CHECK(dsa_index_share_source(INT32_MAX) == INT32_MAX - (INT32_MAX - 2) % 4);
 }
 
+void projections()
+{
+    const void *ql = dev(60), *x = dev(61), *wq = dev(62), *wk = dev(63), *wp = dev(64);
+    const int32_t *pos = dev<const int32_t>(65);
+    const float *g = dev<const float>(66), *b = dev<const float>(67);
+    void *qo = dev(68), *ko = dev(69);
+    float *wo = dev<float>(70);
+    dsa_frontend_dims d{4096, 2048, 6144, 32, 128, 64, 10000.f, 1e-6f};
+    EXPECT(dsa_indexer_frontend(&d, ql, x, pos, wq, wk, g, b, wp, qo, ko, wo, kStream), DSA_OK,
+           "frontend");
+    dsa_frontend_dims e0 = d;
+    e0.norm_eps = 0.f;  // the pages' CPU crash: LayerNorm with eps 0
+    EXPECT(dsa_indexer_frontend(&e0, ql, x, pos, wq, wk, g, b, wp, qo, ko, wo, kStream),
+           DSA_ERR_ARG, nullptr);
+    dsa_frontend_dims hd = d;
+    hd.head_dim = 64;
+    EXPECT(dsa_indexer_frontend(&hd, ql, x, pos, wq, wk, g, b, wp, qo, ko, wo, kStream),
+           DSA_ERR_UNSUPPORTED, nullptr);
+    dsa_frontend_dims rd = d;
+    rd.rope_dim = 40;
+    EXPECT(dsa_indexer_frontend(&rd, ql, x, pos, wq, wk, g, b, wp, qo, ko, wo, kStream),
+           DSA_ERR_UNSUPPORTED, nullptr);
+    dsa_frontend_dims big{INT32_MAX, 1 << 30, 1 << 30, 32, 128, 64, 10000.f, 1e-6f};
+    EXPECT(dsa_indexer_frontend(&big, ql, x, pos, wq, wk, g, b, wp, qo, ko, wo, kStream),
+           DSA_ERR_UNSUPPORTED, nullptr);
+    EXPECT(dsa_indexer_frontend(&d, ql, x, nullptr, wq, wk, g, b, wp, qo, ko, wo, kStream),
+           DSA_ERR_ARG, nullptr);
+    EXPECT(dsa_indexer_frontend(&d, (const char *)ql + 8, x, pos, wq, wk, g, b, wp, qo, ko, wo,
+                                kStream),
+           DSA_ERR_UNSUPPORTED, nullptr);
+    dsa_expand_dims xd{65536, 512, 64, 192, 256};
+    EXPECT(dsa_expand_kv(&xd, x, wq, ko, 64 * 192, qo, 64 * 256, kStream), DSA_OK, "expand_kv");
+    EXPECT(dsa_expand_kv(&xd, x, wq, ko, 64 * 192 - 8, qo, 64 * 256, kStream), DSA_ERR_ARG,
+           nullptr);
+    EXPECT(dsa_expand_kv(&xd, x, wq, ko, 64 * 192 + 4, qo, 64 * 256, kStream),
+           DSA_ERR_UNSUPPORTED, nullptr);
+    dsa_expand_dims xbig{INT32_MAX, 512, INT32_MAX, INT32_MAX, 8};
+    EXPECT(dsa_expand_kv(&xbig, x, wq, ko, INT64_MAX, qo, INT64_MAX, kStream),
+           DSA_ERR_UNSUPPORTED, nullptr);
+    dsa_expand_dims xr{16, 100, 4, 8, 8};
+    EXPECT(dsa_expand_kv(&xr, x, wq, ko, 32, qo, 32, kStream), DSA_ERR_UNSUPPORTED, nullptr);
+    dsa_expand_dims x0{0, 512, 64, 192, 256};
+    EXPECT(dsa_expand_kv(&x0, nullptr, nullptr, nullptr, 64 * 192, nullptr, 64 * 256, kStream),
+           DSA_OK, nullptr);
+}
+
 int main()
 {
+    projections();
     CHECK(std::strlen(dsa_version()) > 0);
     index_share();
     ranges();
