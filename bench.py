@@ -264,19 +264,19 @@ class PooledStep:
     def __init__(self, dsa, inp):
         import torch
         self.dsa, self.inp = dsa, inp
-        B, L, d, kp = inp["B"], inp["L"], inp["d"], inp["kpool"]
+        B, L, d, kp, Tq = inp["B"], inp["L"], inp["d"], inp["kpool"], inp["Tq"]
         dev = inp["q_pos"].device
         self.kp, self.sk, self.width = kp, inp["select_k"], inp["out_width"]
         self.plo, self.phi = dsa.visibility_ranges(inp["pad"], inp["q_pos"], kp)
         self.lo, self.hi = dsa.visibility_ranges(inp["pad"], inp["q_pos"])
         self.pk = torch.empty((B, L // kp, d), dtype=torch.bfloat16, device=dev)
         self.npools = torch.empty(B, dtype=torch.int32, device=dev)
-        self.S = torch.empty((B, L, L // kp), dtype=torch.float32, device=dev)
-        self.tok = torch.empty((B, L, self.width), dtype=torch.int32, device=dev)
+        self.S = torch.empty((B, Tq, L // kp), dtype=torch.float32, device=dev)
+        self.tok = torch.empty((B, Tq, self.width), dtype=torch.int32, device=dev)
         H, vd = inp["H"], inp["vd"]
-        self.out = torch.empty((B, L, H, vd), dtype=torch.float32, device=dev)
-        self.lse = torch.empty((B, L, H), dtype=torch.float32, device=dev)
-        dims = dsa._AttnDims(B, L, L, H, inp["kd"], vd, H, self.width, inp["scale_attn"])
+        self.out = torch.empty((B, Tq, H, vd), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((B, Tq, H), dtype=torch.float32, device=dev)
+        dims = dsa._AttnDims(B, Tq, L, H, inp["kd"], vd, H, self.width, inp["scale_attn"])
         self.ws_attn = torch.empty(max(dsa.sparse_attend_workspace_size(dims), 1),
                                    dtype=torch.uint8, device=dev)
 

@@ -75,6 +75,10 @@ struct AttendArgs {
 };
 bool attend_gather_supported(const AttendArgs &a);
 bool attend_masked_supported(const AttendArgs &a);
+// the masked-tile kernel's shapes with few queries per sequence: a per-head
+// gather of each row's selected keys instead (no workspace)
+bool attend_heads_gather_supported(const AttendArgs &a);
+hipError_t launch_attend_heads(const AttendArgs &a, hipStream_t st);
 bool attend_plain_supported(const AttendArgs &a);
 // blocks per query row of the gather kernel (split-K over the selected keys)
 int attend_gather_splits(const AttendArgs &a);

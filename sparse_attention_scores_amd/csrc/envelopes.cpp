@@ -80,6 +80,14 @@ bool attend_masked_supported(const AttendArgs &a)
                            (int64_t)1 << 46) >= 0;
 }
 
+bool attend_heads_gather_supported(const AttendArgs &a)
+{
+    // the gathered keys of a sequence (n_q rows x at most n_sel keys) do not
+    // exceed what one masked-tile block streams (every key of the range)
+    return attend_masked_supported(a) && a.n_sel <= 4096 &&
+           (int64_t)a.n_q * std::min(a.n_sel, a.n_k) <= a.n_k;
+}
+
 MaskedLayout masked_layout(const AttendArgs &a)
 {
     MaskedLayout L{};
@@ -105,6 +113,8 @@ size_t attend_masked_workspace_bytes(const AttendArgs &a)
 
 size_t attend_workspace_bytes(const AttendArgs &a)
 {
+    if (attend_heads_gather_supported(a))
+        return 0;
     if (attend_masked_supported(a))
         return attend_masked_workspace_bytes(a);
     if (!attend_gather_supported(a))

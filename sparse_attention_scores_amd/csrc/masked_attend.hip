@@ -28,6 +28,7 @@
 // belong to one query, so the softmax rescale needs no cross-lane traffic.
 // V^T keeps the keys of each 16-key half in the order the S^T accumulators
 // hold them, so P^T comes straight from the softmax registers.
+#include "attend_set.hpp"
 #include "dsa_device.hpp"
 #include "dsa_internal.hpp"
 
@@ -728,7 +729,220 @@ __global__ __launch_bounds__(512, 1) void attend_masked_kernel(
     }
 }
 
+// ------------------------------------------------------------------ few queries
+
+// Per-head attention for a few queries per sequence (decode): one block per
+// (query row, head) gathers only the row's selected keys, K and V of that
+// head -- what one block of the masked-tile kernel would stream over the
+// whole key range for one useful query.  Two passes over the selected set,
+// in ascending key order: scores (eight lanes per key, 24 bf16 of K each),
+// then the max and the softmax weights in LDS, then the weighted sum of V
+// (a half-wave per key, eight columns per lane).  f32 arithmetic
+// throughout; many keys' loads are in flight per lane in both passes.
+constexpr int HG_NT = 256;       // 4 waves
+constexpr int HG_LIST = 4096;    // largest selected set the block holds
+constexpr int HG_KU = 4;         // keys per lane group per score round
+constexpr int HG_VU = 8;         // key pairs per wave per value round
+
+struct HeadsGatherSmem {
+    uint32_t bitmap[kBitmapMaxWords];
+    int32_t list[HG_LIST];
+    float p[HG_LIST];
+    float o[HG_NT / 64][256];
+    float red[HG_NT / 64];
+    int cnt[HG_NT / 64];
+};
+
+__device__ __forceinline__ void bf16x8_to_f32(const u32x4_t &r, float (&f)[8])
+{
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        f[2 * j] = __uint_as_float(r[j] << 16);
+        f[2 * j + 1] = __uint_as_float(r[j] & 0xffff0000u);
+    }
+}
+
+template <int KD, int VD>
+__global__ __launch_bounds__(HG_NT) void attend_heads_gather_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, int64_t ksr,
+    const uint16_t *__restrict__ v, int64_t vsr, const int32_t *__restrict__ idx,
+    const int32_t *__restrict__ vlo, const int32_t *__restrict__ vhi, float *__restrict__ out,
+    float *__restrict__ lse, int n_q, int n_k, int H, int n_sel, float scale_log2)
+{
+    constexpr int KC = KD / 64;  // 16-byte chunks of a K row per lane (8 lanes per key)
+    static_assert(KD % 64 == 0 && VD == HG_NT && VD / 8 == 32, "K in 8 lanes, V in a half-wave");
+    constexpr int NW = HG_NT / 64;
+    __shared__ HeadsGatherSmem sm;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    // a row's heads are consecutive blocks on one XCD: its index row comes
+    // from that L2
+    const int lb = xcd_remap(blockIdx.x, gridDim.x);
+    const int row = lb / H, h = lb % H;
+    const int64_t b = row / n_q;
+    int lo = 0, hi = n_k;
+    if (vlo) {
+        lo = max(vlo[row], 0);
+        hi = min(vhi[row], n_k);
+    }
+    const int nw = (n_k + 31) >> 5;
+    const int32_t *idx_row = idx + (int64_t)row * n_sel;
+    int first[8];
+    load_indices<HG_NT, 8>(first, idx_row, n_sel, 0);
+    // this lane's share of q (chunks sub, sub + 8, ...), scaled to log2 units
+    const int sub = lane & 7, grp = lane >> 3;
+    float qf[KC][8];
+    {
+        const uint16_t *qp = q + ((int64_t)row * H + h) * KD;
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+            bf16x8_to_f32(*reinterpret_cast<const u32x4_t *>(qp + (c * 8 + sub) * 8), qf[c]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                qf[c][e] *= scale_log2;
+        }
+    }
+    build_bitmap<HG_NT, 8>(sm.bitmap, nw, first, idx_row, n_sel, lo, hi);
+    int c0, c1;
+    wave_chunk_range<NW>(nw, wid, c0, c1);
+    const int cnt = wave_chunk_count(sm.bitmap, nw, c0, c1);
+    if (lane == 0)
+        sm.cnt[wid] = cnt;
+    __syncthreads();
+    int run = 0, n = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        run += w < wid ? sm.cnt[w] : 0;
+        n += sm.cnt[w];
+    }
+    wave_chunk_extract(sm.bitmap, nw, c0, c1, run, 0, HG_LIST, sm.list);
+    n = min(n, HG_LIST);
+    __syncthreads();
+    float *orow = out + ((int64_t)row * H + h) * VD;
+    if (n == 0) {  // empty set: zero output, lse = -inf
+        orow[tid] = 0.f;
+        if (lse && tid == 0)
+            lse[(int64_t)row * H + h] = -INFINITY;
+        return;
+    }
+
+    // pass 1: scores of the selected keys, in log2 units
+    const uint16_t *kb = k + (int64_t)b * n_k * ksr + (int64_t)h * KD + sub * 8;
+    float mloc = -INFINITY;
+    for (int base = wid * (8 * HG_KU); base < n; base += NW * 8 * HG_KU) {
+        u32x4_t kr[HG_KU][KC];
+#pragma unroll
+        for (int u = 0; u < HG_KU; ++u) {
+            const int i = min(base + u * 8 + grp, n - 1);
+            const uint16_t *p = kb + (int64_t)sm.list[i] * ksr;
+#pragma unroll
+            for (int c = 0; c < KC; ++c)
+                kr[u][c] = *reinterpret_cast<const u32x4_t *>(p + c * 64);
+        }
+#pragma unroll
+        for (int u = 0; u < HG_KU; ++u) {
+            float dot = 0.f;
+#pragma unroll
+            for (int c = 0; c < KC; ++c) {
+                float kf[8];
+                bf16x8_to_f32(kr[u][c], kf);
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    dot = fmaf(qf[c][e], kf[e], dot);
+            }
+            dot += __shfl_xor(dot, 1);
+            dot += __shfl_xor(dot, 2);
+            dot += __shfl_xor(dot, 4);
+            const int i = base + u * 8 + grp;
+            if (i < n) {
+                mloc = fmaxf(mloc, dot);
+                if (sub == 0)
+                    sm.p[i] = dot;
+            }
+        }
+    }
+    mloc = wave_max(mloc);
+    if (lane == 0)
+        sm.red[wid] = mloc;
+    __syncthreads();
+    float m = sm.red[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w)
+        m = fmaxf(m, sm.red[w]);
+    float lloc = 0.f;
+    for (int i = tid; i < n; i += HG_NT) {
+        const float pw = exp2f(sm.p[i] - m);
+        sm.p[i] = pw;
+        lloc += pw;
+    }
+    lloc = wave_sum(lloc);
+    __syncthreads();  // every max is read before red is reused; the weights are written
+    if (lane == 0)
+        sm.red[wid] = lloc;
+    __syncthreads();
+    float l = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+        l += sm.red[w];
+
+    // pass 2: sum of p_j V_j, a half-wave per key
+    const int half = lane >> 5, col = (lane & 31) * 8;
+    const uint16_t *vb = v + (int64_t)b * n_k * vsr + (int64_t)h * VD + col;
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        o[e] = 0.f;
+    for (int base = wid * (2 * HG_VU); base < n; base += NW * 2 * HG_VU) {
+        u32x4_t vr[HG_VU];
+        float pw[HG_VU];
+#pragma unroll
+        for (int u = 0; u < HG_VU; ++u) {
+            const int i = base + 2 * u + half;
+            const int ii = min(i, n - 1);
+            vr[u] = *reinterpret_cast<const u32x4_t *>(vb + (int64_t)sm.list[ii] * vsr);
+            pw[u] = i < n ? sm.p[ii] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < HG_VU; ++u) {
+            float vf[8];
+            bf16x8_to_f32(vr[u], vf);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                o[e] = fmaf(pw[u], vf[e], o[e]);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        o[e] += __shfl_xor(o[e], 32);
+    if (half == 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            sm.o[wid][col + e] = o[e];
+    }
+    __syncthreads();
+    float acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+        acc += sm.o[w][tid];
+    orow[tid] = acc / l;
+    if (lse && tid == 0)
+        lse[(int64_t)row * H + h] = (m + log2f(l)) * kLn2;
+}
+
 // ------------------------------------------------------------------ host side
+
+hipError_t launch_attend_heads(const AttendArgs &a, hipStream_t st)
+{
+    const int64_t blocks = (int64_t)a.batch * a.n_q * a.n_heads;
+    if (blocks > 0x7fffffff)
+        return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((attend_heads_gather_kernel<192, 256>), dim3((unsigned)blocks),
+                       dim3(HG_NT), 0, st, static_cast<const uint16_t *>(a.q),
+                       static_cast<const uint16_t *>(a.k), a.k_row_stride,
+                       static_cast<const uint16_t *>(a.v), a.v_row_stride, a.idx, a.vis_lo,
+                       a.vis_hi, a.out, a.lse, a.n_q, a.n_k, a.n_heads, a.n_sel,
+                       a.scale * kLog2e);
+    return hipGetLastError();
+}
 
 hipError_t launch_attend_masked(const AttendArgs &a, hipStream_t st)
 {

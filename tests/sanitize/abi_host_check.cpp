@@ -73,9 +73,10 @@ hipError_t launch_attend_masked(const AttendArgs &a, hipStream_t)
 hipError_t launch_attend(const AttendArgs &a, hipStream_t)
 {
     // the library's own launch_attend dispatches on the same predicates
-    g_launched = attend_gather_supported(a)   ? "attend_gather"
-                 : attend_masked_supported(a) ? "attend_masked"
-                                              : "attend_plain";
+    g_launched = attend_gather_supported(a)         ? "attend_gather"
+                 : attend_heads_gather_supported(a) ? "attend_heads"
+                 : attend_masked_supported(a)       ? "attend_masked"
+                                                    : "attend_plain";
     g_attend = a;
     return hipSuccess;
 }
@@ -318,6 +319,14 @@ void attend()
     EXPECT(dsa_sparse_attend(&ph, DSA_BF16, q, kv, 64 * 192, v, 64 * 256, idx, kLo, kHi, out,
                              lse, ws, need_ph, kStream),
            DSA_OK, "attend_masked");
+    // pooled decode (one query per sequence): the per-head gather, no workspace
+    dsa_attn_dims pd{4, 1, 16384, 64, 192, 256, 64, 2052, 0.072f};
+    CHECK(dsa_sparse_attend_workspace_size(&pd) == 0);
+    EXPECT(dsa_sparse_attend(&pd, DSA_BF16, q, kv, 64 * 192, v, 64 * 256, idx, kLo, kHi, out,
+                             lse, nullptr, 0, kStream),
+           DSA_OK, "attend_heads");
+    dsa_attn_dims pd_big{4, 1, 16384, 64, 192, 256, 64, 4097, 0.072f};   // beyond its set size
+    CHECK(dsa_sparse_attend_workspace_size(&pd_big) > 0);
     // f32 per-head: the plain kernel, no workspace
     dsa_attn_dims tiny{1, 64, 64, 4, 48, 32, 4, 8, 0.14f};
     CHECK(dsa_sparse_attend_workspace_size(&tiny) == 0);
