@@ -58,12 +58,19 @@ WORKLOAD_TEXT = {
     5: "pooled NoPE: 4 sequences x 16384 tokens (left pads 0, 2, 37, 64), all positions are "
        "queries; kpool 4 softmax-pooled indexer keys, 32 heads x 128; top 512 pools + visible "
        "tail (out_width 2052); per-head attention 64 heads, kd 192, vd 256",
+    6: "pooled decode: the pooled NoPE workload's 4 sequences x 16384 tokens with one query "
+       "per sequence at its last position; per-head attention gathers each query's selected "
+       "tokens",
+    7: "projections at 65536 tokens: indexer front-end (q_lora 2048 and hidden 6144 -> 32 "
+       "heads x 128 with NEOX rope 64, LayerNorm k, head weights) and expand_kv (latent 512 "
+       "-> 64 heads x (192 + 256))",
 }
 
 
 # short workload names (file names under profiles/)
 WORKLOAD_NAME = {1: "tiny_fp32_64", 2: "decode_b32x8192", 3: "prefill_4096",
-                 4: "decode_b8x131072_fp8", 5: "pooled_b4x16384"}
+                 4: "decode_b8x131072_fp8", 5: "pooled_b4x16384", 6: "pooled_decode_b4x16384",
+                 7: "projections_65536"}
 
 # the kernels each ABI call of a stage launches (substrings of their names)
 STAGE_KERNELS = {
@@ -74,7 +81,9 @@ STAGE_KERNELS = {
              "topk_merge_seg_kernel"),
     "attend": ("attend_gather_kernel", "attend_combine_kernel", "topk_to_mask_kernel",
                "v_scale_max_kernel", "v_to_f16_kernel", "attend_masked_kernel",
-               "attend_plain_kernel"),
+               "attend_heads_gather_kernel", "attend_plain_kernel"),
+    "frontend": ("pj_rope_q_kernel", "pj_norm_k_kernel"),
+    "expand_kv": ("pj_expand_kv_kernel",),
     "pool_keys": ("pool_keys_kernel", "pool_counts_kernel"),
     "pool_select": ("pool_select_kernel",),
 }
@@ -180,7 +189,7 @@ def _parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=5, choices=[1, 2, 3, 4, 5],
+    ap.add_argument("--config", type=int, default=5, choices=[1, 2, 3, 4, 5, 6, 7],
                     help="headline workload (default: the pooled NoPE workload, the largest)")
     ap.add_argument("--only", action="store_true",
                     help="time the headline workload only (no configs object, no peaks)")
@@ -304,25 +313,78 @@ class PooledStep:
 
 def pooled_work(inp):
     """Algorithmic bytes/flops of the pooled step (visible pool pairs and
-    selected tokens only)."""
+    selected tokens only) for its queries (every position, or the last one
+    of each sequence on decode).  Attend reads each query's vectors, the K
+    and V rows of the selected tokens -- every token's rows once when the
+    queries select more (query, token) pairs than there are tokens -- the
+    index rows, and writes the f32 output and lse."""
     B, L, d, Hi, kp = inp["B"], inp["L"], inp["d"], inp["Hi"], inp["kpool"]
     H, kd, vd, sk, width = inp["H"], inp["kd"], inp["vd"], inp["select_k"], inp["out_width"]
     pads = [int(p) for p in inp["pad"].cpu().tolist()]
+    qpos = inp["q_pos"].cpu().tolist()
     vis_pairs = sel_pairs = queries = 0
-    for p in pads:
-        for t in range(p, L):
+    for b, p in enumerate(pads):
+        for t in qpos[b]:
+            if t < p:
+                continue
             n_full = (t - p + 1) // kp
             vis_pairs += n_full
             sel_pairs += min(sk, n_full) * kp + (t + 1 - (p + n_full * kp))
             queries += 1
     np_ = L // kp
+    n_q = B * inp["Tq"]
+    tokens = sum(L - p for p in pads)
     pk_bytes = 2 * B * L * d * 2 + B * np_ * d * 2
-    idx_bytes = B * L * Hi * d * 2 + B * np_ * d * 2 + B * L * Hi * 4 + vis_pairs * 4
-    sel_bytes = vis_pairs * 4 + B * L * width * 4
-    att_bytes = (B * L * H * (kd + kd + vd) * 2 + B * L * width * 4 + B * L * H * (vd + 1) * 4)
+    idx_bytes = n_q * Hi * d * 2 + B * np_ * d * 2 + n_q * Hi * 4 + vis_pairs * 4
+    sel_bytes = vis_pairs * 4 + n_q * width * 4
+    kv_bytes = min(sel_pairs, tokens) * H * (kd + vd) * 2
+    att_bytes = n_q * H * kd * 2 + kv_bytes + n_q * width * 4 + n_q * H * (vd + 1) * 4
     return {"pool_keys": (pk_bytes, 0), "index": (idx_bytes, 2 * Hi * d * vis_pairs),
             "pool_select": (sel_bytes, 0),
             "attend": (att_bytes, 2 * H * (kd + vd) * sel_pairs)}, queries
+
+
+def projection_work(inp):
+    """Algorithmic bytes/flops of the projections: each operand and output
+    once; flops 2 x M x N x K of each product."""
+    T, r_q, hid, Hi = inp["T"], inp["q_lora_rank"], inp["hidden"], inp["Hi"]
+    rank, H, kd, vd = inp["rank"], inp["H"], inp["kd"], inp["vd"]
+    fe_bytes = (T * r_q * 2 + T * hid * 2 + Hi * 128 * r_q * 2 + (128 + Hi) * hid * 2
+                + T * Hi * 128 * 2 + T * 128 * 2 + T * Hi * 4 + T * 4)
+    fe_flops = 2 * T * (r_q * Hi * 128 + hid * (128 + Hi))
+    ex_bytes = T * rank * 2 + H * (kd + vd) * rank * 2 + T * H * (kd + vd) * 2
+    ex_flops = 2 * T * rank * H * (kd + vd)
+    return {"frontend": (fe_bytes, fe_flops), "expand_kv": (ex_bytes, ex_flops)}
+
+
+class ProjStep:
+    """The dense projections at the pooled workload's token count: the
+    indexer front-end (q, k, head weights) and expand_kv (per-head K, V)."""
+
+    stages = ("frontend", "expand_kv")
+
+    def __init__(self, dsa, inp):
+        import torch
+        self.dsa, self.inp = dsa, inp
+        T, Hi, H = inp["T"], inp["Hi"], inp["H"]
+        dev = inp["pos"].device
+        self.q = torch.empty((T, Hi, 128), dtype=torch.bfloat16, device=dev)
+        self.k = torch.empty((T, 128), dtype=torch.bfloat16, device=dev)
+        self.w = torch.empty((T, Hi), dtype=torch.float32, device=dev)
+        self.K = torch.empty((T, H, inp["kd"]), dtype=torch.bfloat16, device=dev)
+        self.V = torch.empty((T, H, inp["vd"]), dtype=torch.bfloat16, device=dev)
+
+    def frontend(self):
+        i = self.inp
+        self.dsa.indexer_frontend(i["q_lora"], i["x"], i["pos"], i["wq_b"], i["wk"], i["k_norm_w"],
+                                  i["k_norm_b"], i["w_proj"], i["Hi"], i["rope_dim"],
+                                  i["rope_theta"], i["norm_eps"], q_out=self.q, k_out=self.k,
+                                  w_out=self.w)
+
+    def expand_kv(self):
+        i = self.inp
+        self.dsa.expand_kv(i["latent"], i["w_kv_b"], i["H"], i["kd"], i["vd"], k_out=self.K,
+                           v_out=self.V)
 
 
 def algorithmic_work(inp):
@@ -419,7 +481,7 @@ def stage_bound(cfg, stage):
     """The roofline that bounds each stage of each workload: the decode
     workloads and the selection stages stream memory; the prefill and
     pooled indexers and attends are contractions."""
-    if stage in ("topk", "pool_select", "pool_keys") or cfg in (1, 2, 4):
+    if stage in ("topk", "pool_select", "pool_keys") or cfg in (1, 2, 4, 6):
         return "hbm"
     return "mfma"
 
@@ -433,7 +495,8 @@ def run_workload(cfg, dsa, W, K, warmup, graph=False):
     sets = []
     for i in range(n_sets):
         inp = W.make(cfg, device="cuda", seed=1000 + cfg + 7919 * i)
-        sets.append(PooledStep(dsa, inp) if cfg == 5 else Step(dsa, inp))
+        sets.append(PooledStep(dsa, inp) if cfg in (5, 6)
+                    else ProjStep(dsa, inp) if cfg == 7 else Step(dsa, inp))
     names = sets[0].stages
 
     def run_once(st):
@@ -479,8 +542,10 @@ def run_workload(cfg, dsa, W, K, warmup, graph=False):
         return e0.elapsed_time(e1) / K
 
     inp = sets[0].inp
-    if cfg == 5:
+    if cfg in (5, 6):
         work, tokens = pooled_work(inp)
+    elif cfg == 7:
+        work, tokens = projection_work(inp), inp["T"]
     else:
         work, tokens = algorithmic_work(inp), inp["B"] * inp["Tq"]
     res = {"workload": WORKLOAD_TEXT[cfg], "config_id": cfg, "query_tokens_per_step": tokens,
@@ -576,13 +641,15 @@ def cpu_baseline(res, rows_wanted, min_seconds=10.0, max_passes=50):
     import oracle
     cfg = res["config_id"]
     inp = res["_inp"]
-    B, Tq = inp["B"], inp["Tq"]
     h = {k: (_host(v) if hasattr(v, "detach") else v) for k, v in inp.items()}
+    if cfg == 7:
+        return _cpu_baseline_projections(inp, h, rows_wanted, min_seconds, max_passes)
+    B, Tq = inp["B"], inp["Tq"]
     qp_all = h["q_pos"].numpy().reshape(-1)
     pd_all = np.repeat(h["pad"].numpy(), Tq)
     rows = np.unique(np.linspace(0, B * Tq - 1, num=min(rows_wanted, B * Tq)).round()
                      .astype(np.int64))
-    if cfg == 5:
+    if cfg in (5, 6):
         kp, sk, width = inp["kpool"], inp["select_k"], inp["out_width"]
 
         def one_pass():
@@ -613,6 +680,11 @@ def cpu_baseline(res, rows_wanted, min_seconds=10.0, max_passes=50):
                                      q_pos=h["q_pos"], pad=h["pad"], rows=rows,
                                      k_row_stride=inp["kd"], vd=inp["vd"])
         what = "index scores over all keys, top-k and attention"
+    return _time_passes(one_pass, len(rows), B * Tq, what, min_seconds, max_passes)
+
+
+def _time_passes(one_pass, n_rows, n_all, what, min_seconds, max_passes):
+    import oracle
     passes = 0
     t0 = time.perf_counter()
     while True:
@@ -621,11 +693,28 @@ def cpu_baseline(res, rows_wanted, min_seconds=10.0, max_passes=50):
         dt = time.perf_counter() - t0
         if dt >= min_seconds or passes >= max_passes:
             break
-    return {"value": round(len(rows) * passes / dt, 3), "unit": "tokens/s",
+    return {"value": round(n_rows * passes / dt, 3), "unit": "tokens/s",
             "cores": oracle.threads(), "kind": "oracle",
             "nproc": os.cpu_count(), "cpu_model": _cpu_model(),
-            "sample": f"{len(rows)} of {B * Tq} query rows of the timed workload, evenly spaced, "
+            "sample": f"{n_rows} of {n_all} query rows of the timed workload, evenly spaced, "
                       f"on the GPU's own input bytes: {what}; {passes} pass(es) in {dt:.1f} s"}
+
+
+def _cpu_baseline_projections(inp, h, rows_wanted, min_seconds, max_passes):
+    import numpy as np
+
+    import oracle
+    T = inp["T"]
+    rows = np.unique(np.linspace(0, T - 1, num=min(rows_wanted, T)).round().astype(np.int64))
+    pos = h["pos"].numpy()[rows]
+
+    def one_pass():
+        oracle.indexer_frontend(h["q_lora"][rows], h["x"][rows], pos, h["wq_b"], h["wk"],
+                                h["k_norm_w"], h["k_norm_b"], h["w_proj"], inp["Hi"],
+                                inp["rope_dim"], inp["rope_theta"], inp["norm_eps"])
+        oracle.expand_kv(h["latent"][rows], h["w_kv_b"], inp["H"], inp["kd"], inp["vd"])
+    return _time_passes(one_pass, len(rows), T, "indexer front-end and expand_kv", min_seconds,
+                        max_passes)
 
 
 def _public(res):
@@ -687,7 +776,7 @@ def main():
     torch.cuda.empty_cache()
     if not args.only:
         configs = {}
-        for c in (2, 3, 4, 5):
+        for c in (2, 3, 4, 5, 6, 7):
             if c == cfg:
                 continue
             print(f"[bench] config {c}", file=sys.stderr, flush=True)

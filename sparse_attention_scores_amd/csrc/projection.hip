@@ -12,10 +12,9 @@
 // One GEMM body, C[m][n] = sum_k A[m][k] B[n][k] (both operands K-major,
 // the torch Linear layout), bf16 on v_mfma_f32_32x32x16_bf16 with f32
 // accumulation: a block owns a BM x BN tile, its waves a (BM/WM) x (BN/WN)
-// sub-tile; K streams through a three-stage LDS ring in steps of 64 by
+// sub-tile; K streams through an LDS ring in steps of 64 by
 // direct-to-LDS loads (each one-KB load is eight 128-byte row segments, the
-// 16-byte chunks of row r stored at chunk ^ chunk_swz(r) so that the
-// operand reads of eight rows at one logical chunk hit eight chunk slots).
+// 16-byte chunks of row r stored at chunk ^ pj_swz(r)).
 // After the last step the f32 tile is staged in LDS and an epilogue policy
 // finishes the rows: the K/V split store, the rotary q store, or LayerNorm +
 // rotary k plus the f32 head weights.
@@ -27,9 +26,8 @@
 namespace dsa {
 
 constexpr int PJ_BK = 64;     // K elements per stage: 128 bytes of each row
-constexpr int PJ_STAGES = 3;
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int ST>
 struct PjCfg {
     static constexpr int NW = WM * WN;
     static constexpr int NT = 64 * NW;
@@ -39,13 +37,13 @@ struct PjCfg {
     static constexpr int SB = AB + BN * PJ_BK * 2;
     static constexpr int DMA = SB / 1024;     // one-KB loads per stage
     static constexpr int LPW = DMA / NW;      // of them per wave
-    static constexpr int CP = BN + 4;         // staged C row pitch in floats
-    static constexpr int RING = PJ_STAGES * SB;
+    static constexpr int CP = BN + 8;         // staged C row pitch in floats
+    static constexpr int RING = ST * SB;
     static constexpr int CTILE = BM * CP * 4;
     static constexpr int LDS = RING > CTILE ? RING : CTILE;
     static_assert(BM % (WM * 32) == 0 && BN % (WN * 32) == 0, "whole MFMA tiles per wave");
     static_assert(DMA * 1024 == SB && DMA % NW == 0, "equal one-KB loads per wave");
-    static_assert(LPW * PJ_STAGES <= 63, "vmcnt range");
+    static_assert(LPW * 3 <= 63 && ST >= 2 && ST <= 4, "vmcnt range, ring depth");
 };
 
 // Operand sources: rows [0, n_split) of B come from b0, the rest from b1
@@ -142,7 +140,7 @@ struct EpiRopeQ {
             const int m = m0 + r;
             if (m >= M)
                 continue;
-            head_item(C + r * (BN + 4), out + (int64_t)m * out_row + n0, item, pos[m], rope);
+            head_item(C + r * (BN + 8), out + (int64_t)m * out_row + n0, item, pos[m], rope);
         }
     }
 };
@@ -163,7 +161,7 @@ struct EpiNormRopeK {
     __device__ void run(float *C, int m0, int n0, int M, int tid) const
     {
         static_assert(NT == 2 * BM, "two threads per row");
-        constexpr int CP = BN + 4;
+        constexpr int CP = BN + 8;
         {
             const int r = tid >> 1, h = tid & 1;
             float *row = C + r * CP + 64 * h;
@@ -228,7 +226,7 @@ struct EpiSplitKV {
             uint16_t *dst = j < kd ? k + (int64_t)m * ksr + (int64_t)head * kd + j
                                    : v + (int64_t)m * vsr + (int64_t)head * vd + (j - kd);
             float x[8];
-            load_f32x8(x, C + r * (BN + 4) + 8 * c);
+            load_f32x8(x, C + r * (BN + 8) + 8 * c);
             store_bf16x8(dst, x);
         }
     }
@@ -236,22 +234,35 @@ struct EpiSplitKV {
 
 // ---------------------------------------------------------------- GEMM body
 
-template <int N>
+// Chunk swizzle of the 128-byte operand rows: physical chunk = logical chunk
+// ^ ((r >> 1) & 7).  A ds_read_b128 serves 16 lanes per pass (64 banks x 4
+// bytes); the operand reads give 16 consecutive rows at one logical chunk to
+// those lanes.  Row r starts at bank 32 (r & 1), so the even rows and the odd
+// rows each need eight distinct chunk slots, which (r >> 1) & 7 gives.
+__device__ __forceinline__ int pj_swz(int r)
+{
+    return (r >> 1) & 7;
+}
+
+// wait until at most W LDS reads are outstanding, tied to every register
+// of one operand buffer
+template <int W, int N>
 __device__ __forceinline__ void wait_operands(u32x4_t (&v)[N])
 {
 #pragma unroll
     for (int i = 0; i < N; ++i)
-        lds_operand_wait<0>(v[i]);
+        lds_operand_wait<W>(v[i]);
 }
 
 // The block's f32 tile C = A[m0 .. m0+BM) B[n0 .. n0+BN)^T, left staged in
-// LDS at `smem` with row pitch BN + 4 floats.  Rows past M (and past N) load
+// LDS at `smem` with row pitch BN + 8 floats (the two half-waves' rows, four
+// apart, then start 32 banks apart).  Rows past M (and past N) load
 // the last valid row instead, so every load stays inside the operands; the
 // epilogues skip them.
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int ST>
 __device__ __forceinline__ void pj_tile(const PjOperands &op, int m0, int n0, unsigned char *smem)
 {
-    using Cfg = PjCfg<BM, BN, WM, WN>;
+    using Cfg = PjCfg<BM, BN, WM, WN, ST>;
     constexpr int TM = Cfg::TM, TN = Cfg::TN, LPW = Cfg::LPW;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -264,7 +275,7 @@ __device__ __forceinline__ void pj_tile(const PjOperands &op, int m0, int n0, un
     for (int i = 0; i < LPW; ++i) {
         const int j = wid + Cfg::NW * i;        // the load: rows 8j .. 8j+7
         const int r = 8 * j + (lane >> 3);      // row of the stage (A rows, then B rows)
-        const int chunk = (lane & 7) ^ chunk_swz(r);
+        const int chunk = (lane & 7) ^ pj_swz(r);
         if (r < BM) {
             const int m = min(m0 + r, op.M - 1);
             src[i] = op.a + (int64_t)m * op.lda + chunk * 8;
@@ -287,12 +298,12 @@ __device__ __forceinline__ void pj_tile(const PjOperands &op, int m0, int n0, un
 #pragma unroll
     for (int t = 0; t < TM; ++t) {
         const int r = wm * (BM / WM) + t * 32 + (lane & 31);
-        a_addr[t] = lds0 + r * 128 + ((g ^ chunk_swz(r)) << 4);
+        a_addr[t] = lds0 + r * 128 + ((g ^ pj_swz(r)) << 4);
     }
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
         const int r = BM + wn * (BN / WN) + t * 32 + (lane & 31);
-        b_addr[t] = lds0 + r * 128 + ((g ^ chunk_swz(r)) << 4);
+        b_addr[t] = lds0 + r * 128 + ((g ^ pj_swz(r)) << 4);
     }
 
     f32x16_t acc[TM][TN];
@@ -306,35 +317,46 @@ __device__ __forceinline__ void pj_tile(const PjOperands &op, int m0, int n0, un
 
     const int nk = op.K / PJ_BK;
     int issued = 0;
-    for (; issued < PJ_STAGES - 1 && issued < nk; ++issued)
+    for (; issued < ST - 1 && issued < nk; ++issued)
         issue(issued, issued);
     for (int kt = 0; kt < nk; ++kt) {
         vm_wait_tiles<LPW>(issued - kt - 1);
         lds_barrier();  // stage kt landed for every wave; stage kt-1 is free
         if (issued < nk) {
-            issue(issued, issued % PJ_STAGES);
+            issue(issued, issued % ST);
             ++issued;
         }
-        const uint32_t so = (uint32_t)((kt % PJ_STAGES) * Cfg::SB);
-#pragma unroll
-        for (int s = 0; s < PJ_BK / 16; ++s) {
-            // the chunk pair of k-step s: logical chunks 2s + g; the swizzle
-            // XORs the low three bits, and 2s only touches bits 1-2, so the
-            // physical chunk is (g ^ swz) ^ 2s
-            u32x4_t av[TM], bv[TN];
+        const uint32_t so = (uint32_t)((kt % ST) * Cfg::SB);
+        // the chunk pair of k-step s: logical chunks 2s + g; the swizzle XORs
+        // the low three bits, and 2s only touches bits 1-2, so the physical
+        // chunk is (g ^ swz) ^ 2s.  The operands of k-step s+1 are read while
+        // the MFMAs of k-step s run (two register buffers).
+        u32x4_t av[2][TM], bv[2][TN];
+        auto read = [&](int s, int buf) {
 #pragma unroll
             for (int t = 0; t < TM; ++t)
-                lds_read_b128_nowait(av[t], (a_addr[t] + so) ^ (uint32_t)(s << 5));
+                lds_read_b128_nowait(av[buf][t], (a_addr[t] + so) ^ (uint32_t)(s << 5));
 #pragma unroll
             for (int t = 0; t < TN; ++t)
-                lds_read_b128_nowait(bv[t], (b_addr[t] + so) ^ (uint32_t)(s << 5));
-            wait_operands(av);
-            wait_operands(bv);
+                lds_read_b128_nowait(bv[buf][t], (b_addr[t] + so) ^ (uint32_t)(s << 5));
+        };
+        read(0, 0);
+#pragma unroll
+        for (int s = 0; s < PJ_BK / 16; ++s) {
+            const int cur = s & 1;
+            if (s + 1 < PJ_BK / 16) {
+                read(s + 1, cur ^ 1);
+                wait_operands<TM + TN>(av[cur]);
+                wait_operands<TM + TN>(bv[cur]);
+            } else {
+                wait_operands<0>(av[cur]);
+                wait_operands<0>(bv[cur]);
+            }
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
-                    acc[i][j] = mfma_32x32x16(av[i], bv[j], acc[i][j]);
+                    acc[i][j] = mfma_32x32x16(av[cur][i], bv[cur][j], acc[i][j]);
         }
     }
     lds_barrier();  // every wave is done with the ring before it is reused
@@ -355,41 +377,41 @@ __device__ __forceinline__ void pj_tile(const PjOperands &op, int m0, int n0, un
     __syncthreads();
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int ST>
 __global__ __launch_bounds__(64 * WM *WN) void pj_rope_q_kernel(PjOperands op, EpiRopeQ epi)
 {
-    using Cfg = PjCfg<BM, BN, WM, WN>;
+    using Cfg = PjCfg<BM, BN, WM, WN, ST>;
     __shared__ __attribute__((aligned(1024))) unsigned char smem[Cfg::LDS];
     DSA_LDS_ESCAPE(smem);
     const int nb = (op.N + BN - 1) / BN;
     const int b = xcd_remap(blockIdx.x, gridDim.x);
     const int m0 = (b / nb) * BM, n0 = (b % nb) * BN;
-    pj_tile<BM, BN, WM, WN>(op, m0, n0, smem);
+    pj_tile<BM, BN, WM, WN, ST>(op, m0, n0, smem);
     epi.template run<BM, BN, Cfg::NT>(reinterpret_cast<const float *>(smem), m0, n0, op.M,
                                       threadIdx.x);
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int ST>
 __global__ __launch_bounds__(64 * WM *WN) void pj_norm_k_kernel(PjOperands op, EpiNormRopeK epi)
 {
-    using Cfg = PjCfg<BM, BN, WM, WN>;
+    using Cfg = PjCfg<BM, BN, WM, WN, ST>;
     __shared__ __attribute__((aligned(1024))) unsigned char smem[Cfg::LDS];
     DSA_LDS_ESCAPE(smem);
     const int m0 = blockIdx.x * BM;
-    pj_tile<BM, BN, WM, WN>(op, m0, 0, smem);
+    pj_tile<BM, BN, WM, WN, ST>(op, m0, 0, smem);
     epi.template run<BM, BN, Cfg::NT>(reinterpret_cast<float *>(smem), m0, 0, op.M, threadIdx.x);
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int ST>
 __global__ __launch_bounds__(64 * WM *WN) void pj_expand_kv_kernel(PjOperands op, EpiSplitKV epi)
 {
-    using Cfg = PjCfg<BM, BN, WM, WN>;
+    using Cfg = PjCfg<BM, BN, WM, WN, ST>;
     __shared__ __attribute__((aligned(1024))) unsigned char smem[Cfg::LDS];
     DSA_LDS_ESCAPE(smem);
     const int nb = (op.N + BN - 1) / BN;
     const int b = xcd_remap(blockIdx.x, gridDim.x);
     const int m0 = (b / nb) * BM, n0 = (b % nb) * BN;
-    pj_tile<BM, BN, WM, WN>(op, m0, n0, smem);
+    pj_tile<BM, BN, WM, WN, ST>(op, m0, n0, smem);
     epi.template run<BM, BN, Cfg::NT>(reinterpret_cast<const float *>(smem), m0, n0, op.M, op.N,
                                       threadIdx.x);
 }
@@ -405,9 +427,13 @@ static RopeArgs rope_args(int rope_dim, float theta)
     return r;
 }
 
-constexpr int PJ_Q_BM = 256, PJ_Q_BN = 128;
+// q and expand_kv: 128 x 128 tiles, 4 waves of 64 x 64, a two-stage ring:
+// 68 KB of LDS, so two blocks share a CU and one's prologue and epilogue
+// overlap the other's matrix work.  k and the head weights: the whole
+// 128 + n_heads columns in one tile (LayerNorm needs the full row).
+constexpr int PJ_Q_BM = 128, PJ_Q_BN = 128;
 constexpr int PJ_K_BM = 128;
-constexpr int PJ_E_BM = 256, PJ_E_BN = 128;
+constexpr int PJ_E_BM = 128, PJ_E_BN = 128;
 
 hipError_t launch_indexer_frontend(const FrontendArgs &a, hipStream_t st)
 {
@@ -421,8 +447,8 @@ hipError_t launch_indexer_frontend(const FrontendArgs &a, hipStream_t st)
             (int64_t)((a.tokens + PJ_Q_BM - 1) / PJ_Q_BM) * ((op.N + PJ_Q_BN - 1) / PJ_Q_BN);
         if (blocks > 0x7fffffff)
             return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL((pj_rope_q_kernel<PJ_Q_BM, PJ_Q_BN, 4, 2>), dim3((unsigned)blocks),
-                           dim3(512), 0, st, op, epi);
+        hipLaunchKernelGGL((pj_rope_q_kernel<PJ_Q_BM, PJ_Q_BN, 2, 2, 2>), dim3((unsigned)blocks),
+                           dim3(256), 0, st, op, epi);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
@@ -434,11 +460,11 @@ hipError_t launch_indexer_frontend(const FrontendArgs &a, hipStream_t st)
                      a.norm_eps, a.n_heads, a.pos, rp};
     const unsigned blocks = (unsigned)((a.tokens + PJ_K_BM - 1) / PJ_K_BM);
     if (a.n_heads == 32)
-        hipLaunchKernelGGL((pj_norm_k_kernel<PJ_K_BM, 160, 4, 1>), dim3(blocks), dim3(256), 0, st,
-                           op, epi);
+        hipLaunchKernelGGL((pj_norm_k_kernel<PJ_K_BM, 160, 4, 1, 3>), dim3(blocks), dim3(256), 0,
+                           st, op, epi);
     else
-        hipLaunchKernelGGL((pj_norm_k_kernel<PJ_K_BM, 192, 4, 1>), dim3(blocks), dim3(256), 0, st,
-                           op, epi);
+        hipLaunchKernelGGL((pj_norm_k_kernel<PJ_K_BM, 192, 4, 1, 3>), dim3(blocks), dim3(256), 0,
+                           st, op, epi);
     return hipGetLastError();
 }
 
@@ -454,8 +480,8 @@ hipError_t launch_expand_kv(const ExpandArgs &a, hipStream_t st)
         (int64_t)((a.tokens + PJ_E_BM - 1) / PJ_E_BM) * ((N + PJ_E_BN - 1) / PJ_E_BN);
     if (blocks > 0x7fffffff)
         return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((pj_expand_kv_kernel<PJ_E_BM, PJ_E_BN, 4, 2>), dim3((unsigned)blocks),
-                       dim3(512), 0, st, op, epi);
+    hipLaunchKernelGGL((pj_expand_kv_kernel<PJ_E_BM, PJ_E_BN, 2, 2, 2>), dim3((unsigned)blocks),
+                       dim3(256), 0, st, op, epi);
     return hipGetLastError();
 }
 
