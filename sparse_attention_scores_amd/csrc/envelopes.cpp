@@ -70,9 +70,10 @@ bool attend_plain_supported(const AttendArgs &a)
 bool attend_masked_supported(const AttendArgs &a)
 {
     // V's fp16 copy ([batch, n_k, n_heads, vd]) must stay addressable
-    // and the mask ([batch, n_k / 32, q_pad]) as well
+    // and the mask ([batch, n_k / 32, q_pad]) as well; the mask builder
+    // indexes a group's 32 index rows as one span below 2^24 entries
     return !a.f32 && a.kv_heads == a.n_heads && a.kd == kMaskedKd && a.vd == kMaskedVd &&
-           a.n_k > 0 && a.n_q <= (1 << 30) && a.k_row_stride % 8 == 0 &&
+           a.n_k > 0 && a.n_q <= (1 << 30) && a.n_sel < (1 << 19) && a.k_row_stride % 8 == 0 &&
            a.v_row_stride % 8 == 0 && (int64_t)a.n_heads * a.vd * 2 < (1ll << 31) &&
            a.k_row_stride < (1ll << 30) &&
            checked_product({a.batch, a.n_k, a.n_heads, a.vd}, (int64_t)1 << 46) >= 0 &&

@@ -48,39 +48,64 @@ constexpr int MK_VKEYS = kMaskedVKeys; // keys per block of the V passes
 // Block (b, group of 32 queries): the rows' selected sets as bits, written
 // tile-major: mask[(b * nw + w) * q_pad + q] holds keys 32w .. 32w+31 of
 // query q.  Rows past n_q (up to q_pad) get zero words, so every word of the
-// mask is written.  Keys are processed MK_WCHUNK words at a time.
+// mask is written.  The group's index rows are one contiguous span of
+// 32 x n_sel entries, read flat (eight coalesced loads in flight per
+// thread); keys are processed MK_WCHUNK words at a time.
 __global__ __launch_bounds__(256) void topk_to_mask_kernel(const int32_t *__restrict__ idx,
                                                            const int32_t *__restrict__ vlo,
                                                            const int32_t *__restrict__ vhi,
                                                            uint32_t *__restrict__ mask, int n_q,
                                                            int n_k, int n_sel, int nw, int q_pad)
 {
+    constexpr int U = 8;
     __shared__ uint32_t bits[MK_ROWS][MK_WCHUNK + 1];
+    __shared__ int rlo[MK_ROWS], rhi[MK_ROWS];
     const int groups = q_pad / MK_ROWS;
     const int b = blockIdx.x / groups;
     const int q0 = (blockIdx.x % groups) * MK_ROWS;
     const int tid = threadIdx.x;
+    const int nrows = max(min(MK_ROWS, n_q - q0), 0);
+    if (tid < MK_ROWS) {
+        int lo = 0, hi = 0;
+        if (tid < nrows) {
+            const int64_t row = (int64_t)b * n_q + q0 + tid;
+            lo = 0;
+            hi = n_k;
+            if (vlo) {
+                lo = max(vlo[row], 0);
+                hi = min(vhi[row], n_k);
+            }
+        }
+        rlo[tid] = lo;
+        rhi[tid] = hi;
+    }
+    const int32_t *span = idx + ((int64_t)b * n_q + q0) * n_sel;
+    const int total = nrows * n_sel;  // < 2^31: checked on the host
+    const float inv_sel = 1.0f / (float)max(n_sel, 1);
     for (int w0 = 0; w0 < nw; w0 += MK_WCHUNK) {
         const int wn = min(MK_WCHUNK, nw - w0);
         for (int i = tid; i < MK_ROWS * (MK_WCHUNK + 1); i += 256)
             (&bits[0][0])[i] = 0u;
         __syncthreads();
-        for (int r = 0; r < MK_ROWS; ++r) {
-            const int q = q0 + r;
-            if (q >= n_q)
-                break;
-            const int64_t row = (int64_t)b * n_q + q;
-            int lo = 0, hi = n_k;
-            if (vlo) {
-                lo = max(vlo[row], 0);
-                hi = min(vhi[row], n_k);
+        const int c_lo = w0 * 32, c_hi = (w0 + wn) * 32;
+        for (int e0 = 0; e0 < total; e0 += 256 * U) {
+            int v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int e = e0 + u * 256 + tid;
+                v[u] = e < total ? span[e] : -1;
             }
-            lo = max(lo, w0 * 32);
-            hi = min(hi, (w0 + wn) * 32);
-            const int32_t *ir = idx + row * n_sel;
-            for (int i = tid; i < n_sel; i += 256) {
-                const int j = ir[i];
-                if (j >= lo && j < hi)
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int e = e0 + u * 256 + tid;
+                if (e >= total)
+                    continue;
+                // row of entry e: a float estimate, corrected by one step
+                int r = (int)((float)e * inv_sel);
+                r -= r * n_sel > e;
+                r += (r + 1) * n_sel <= e;
+                const int j = v[u];
+                if (j >= max(rlo[r], c_lo) && j < min(rhi[r], c_hi))
                     atomicOr(&bits[r][(j >> 5) - w0], 1u << (j & 31));
             }
         }
