@@ -27,7 +27,7 @@ namespace dsa {
 
 constexpr int PJ_BK = 64;     // K elements per stage: 128 bytes of each row
 
-template <int BM, int BN, int WM, int WN, int ST>
+template <int BM, int BN, int WM, int WN, int ST, int CR = BM>
 struct PjCfg {
     static constexpr int NW = WM * WN;
     static constexpr int NT = 64 * NW;
@@ -39,11 +39,12 @@ struct PjCfg {
     static constexpr int LPW = DMA / NW;      // of them per wave
     static constexpr int CP = BN + 8;         // staged C row pitch in floats
     static constexpr int RING = ST * SB;
-    static constexpr int CTILE = BM * CP * 4;
+    static constexpr int CTILE = CR * CP * 4;  // staged C rows (CR of them at a time)
     static constexpr int LDS = RING > CTILE ? RING : CTILE;
     static_assert(BM % (WM * 32) == 0 && BN % (WN * 32) == 0, "whole MFMA tiles per wave");
     static_assert(DMA * 1024 == SB && DMA % NW == 0, "equal one-KB loads per wave");
     static_assert(LPW * 3 <= 63 && ST >= 2 && ST <= 4, "vmcnt range, ring depth");
+    static_assert(BM % CR == 0 && CR % 32 == 0, "row chunks of whole 32-row tiles");
 };
 
 // Operand sources: rows [0, n_split) of B come from b0, the rest from b1
@@ -123,7 +124,7 @@ __device__ __forceinline__ void head_item(const float *row, uint16_t *dst, int i
     }
 }
 
-// q: the tile is one head (BN = 128): out[m][head][0..128).
+// q: the tile holds whole heads of 128: out[m][head][0..128).
 struct EpiRopeQ {
     uint16_t *out;
     int64_t out_row;  // elements per token (n_heads * 128)
@@ -133,14 +134,17 @@ struct EpiRopeQ {
     template <int BM, int BN, int NT>
     __device__ void run(const float *C, int m0, int n0, int M, int tid) const
     {
-        static_assert(BN == 128, "one head of 128 per tile");
+        static_assert(BN % 128 == 0, "whole heads of 128 per tile");
+        constexpr int HT = BN / 128;
         const int ipr = rope.rope_dim / 16 + (128 - rope.rope_dim) / 8;
-        for (int it = tid; it < BM * ipr; it += NT) {
-            const int r = it / ipr, item = it % ipr;
+        for (int it = tid; it < BM * HT * ipr; it += NT) {
+            const int r = it / (HT * ipr), rem = it % (HT * ipr);
+            const int hh = rem / ipr, item = rem % ipr;
             const int m = m0 + r;
             if (m >= M)
                 continue;
-            head_item(C + r * (BN + 8), out + (int64_t)m * out_row + n0, item, pos[m], rope);
+            head_item(C + r * (BN + 8) + hh * 128,
+                      out + (int64_t)m * out_row + n0 + hh * 128, item, pos[m], rope);
         }
     }
 };
@@ -234,6 +238,23 @@ struct EpiSplitKV {
 
 // ---------------------------------------------------------------- GEMM body
 
+// Tile of logical block b on a grid of mb x nb tiles: each XCD takes a
+// contiguous run of b (xcd_remap), and a run walks groups of GM tile rows
+// column by column, so the tiles an XCD holds at once share GM row blocks of
+// A and a few column blocks of B in its L2.
+template <int GM>
+__device__ __forceinline__ void pj_tile_of(int b, int mb, int nb, int &tm, int &tn)
+{
+    const int per_group = GM * nb;
+    const int grp = b / per_group, in = b % per_group;
+    const int first = grp * GM;
+    const int gm = min(mb - first, GM);
+    tm = first + in % gm;
+    tn = in / gm;
+}
+
+constexpr int PJ_GROUP_M = 8;
+
 // Chunk swizzle of the 128-byte operand rows: physical chunk = logical chunk
 // ^ ((r >> 1) & 7).  A ds_read_b128 serves 16 lanes per pass (64 banks x 4
 // bytes); the operand reads give 16 consecutive rows at one logical chunk to
@@ -254,13 +275,13 @@ __device__ __forceinline__ void wait_operands(u32x4_t (&v)[N])
         lds_operand_wait<W>(v[i]);
 }
 
-// The block's f32 tile C = A[m0 .. m0+BM) B[n0 .. n0+BN)^T, left staged in
-// LDS at `smem` with row pitch BN + 8 floats (the two half-waves' rows, four
-// apart, then start 32 banks apart).  Rows past M (and past N) load
-// the last valid row instead, so every load stays inside the operands; the
-// epilogues skip them.
+// The block's f32 tile C = A[m0 .. m0+BM) B[n0 .. n0+BN)^T in the waves'
+// accumulators (wave (wm, wn) holds rows wm * BM/WM .., columns wn * BN/WN ..).
+// Rows past M (and past N) load the last valid row instead, so every load
+// stays inside the operands; the epilogues skip them.
 template <int BM, int BN, int WM, int WN, int ST>
-__device__ __forceinline__ void pj_tile(const PjOperands &op, int m0, int n0, unsigned char *smem)
+__device__ __forceinline__ void pj_tile(const PjOperands &op, int m0, int n0, unsigned char *smem,
+                                        f32x16_t (&acc)[BM / WM / 32][BN / WN / 32])
 {
     using Cfg = PjCfg<BM, BN, WM, WN, ST>;
     constexpr int TM = Cfg::TM, TN = Cfg::TN, LPW = Cfg::LPW;
@@ -306,7 +327,6 @@ __device__ __forceinline__ void pj_tile(const PjOperands &op, int m0, int n0, un
         b_addr[t] = lds0 + r * 128 + ((g ^ pj_swz(r)) << 4);
     }
 
-    f32x16_t acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -360,35 +380,58 @@ __device__ __forceinline__ void pj_tile(const PjOperands &op, int m0, int n0, un
         }
     }
     lds_barrier();  // every wave is done with the ring before it is reused
-
-    float *C = reinterpret_cast<float *>(smem);
-    constexpr int CP = Cfg::CP;
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int col = wn * (BN / WN) + j * 32 + (lane & 31);
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int row = wm * (BM / WM) + i * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
-                C[row * CP + col] = acc[i][j][e];
-            }
-        }
-    __syncthreads();
 }
 
-template <int BM, int BN, int WM, int WN, int ST>
+// Stage the tile in LDS CR rows at a time (row pitch BN + 8 floats: the two
+// half-waves' rows, four apart, start 32 banks apart) and hand each chunk
+// to finish(C, r0) on every thread.
+template <int BM, int BN, int WM, int WN, int CR, class F>
+__device__ __forceinline__ void pj_stage(const f32x16_t (&acc)[BM / WM / 32][BN / WN / 32],
+                                         unsigned char *smem, F &&finish)
+{
+    constexpr int TM = BM / WM / 32, TN = BN / WN / 32, CP = BN + 8;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wid % WM, wn = wid / WM;
+    const int g = lane >> 5;
+    float *C = reinterpret_cast<float *>(smem);
+    for (int r0 = 0; r0 < BM; r0 += CR) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int rt = wm * (BM / WM) + i * 32;  // the 32-row tile's first row
+            if (rt < r0 || rt >= r0 + CR)
+                continue;
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int col = wn * (BN / WN) + j * 32 + (lane & 31);
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int row = rt - r0 + 8 * (e >> 2) + 4 * g + (e & 3);
+                    C[row * CP + col] = acc[i][j][e];
+                }
+            }
+        }
+        lds_barrier();  // LDS only: the chunk's global stores stay in flight
+        finish(C, r0);
+        lds_barrier();
+    }
+}
+
+template <int BM, int BN, int WM, int WN, int ST, int CR>
 __global__ __launch_bounds__(64 * WM *WN) void pj_rope_q_kernel(PjOperands op, EpiRopeQ epi)
 {
-    using Cfg = PjCfg<BM, BN, WM, WN, ST>;
+    using Cfg = PjCfg<BM, BN, WM, WN, ST, CR>;
     __shared__ __attribute__((aligned(1024))) unsigned char smem[Cfg::LDS];
     DSA_LDS_ESCAPE(smem);
-    const int nb = (op.N + BN - 1) / BN;
-    const int b = xcd_remap(blockIdx.x, gridDim.x);
-    const int m0 = (b / nb) * BM, n0 = (b % nb) * BN;
-    pj_tile<BM, BN, WM, WN, ST>(op, m0, n0, smem);
-    epi.template run<BM, BN, Cfg::NT>(reinterpret_cast<const float *>(smem), m0, n0, op.M,
-                                      threadIdx.x);
+    const int nb = (op.N + BN - 1) / BN, mb = (op.M + BM - 1) / BM;
+    int tm, tn;
+    pj_tile_of<PJ_GROUP_M>(xcd_remap(blockIdx.x, gridDim.x), mb, nb, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    f32x16_t acc[Cfg::TM][Cfg::TN];
+    pj_tile<BM, BN, WM, WN, ST>(op, m0, n0, smem, acc);
+    pj_stage<BM, BN, WM, WN, CR>(acc, smem, [&](const float *C, int r0) {
+        epi.template run<CR, BN, Cfg::NT>(C, m0 + r0, n0, op.M, threadIdx.x);
+    });
 }
 
 template <int BM, int BN, int WM, int WN, int ST>
@@ -398,22 +441,28 @@ __global__ __launch_bounds__(64 * WM *WN) void pj_norm_k_kernel(PjOperands op, E
     __shared__ __attribute__((aligned(1024))) unsigned char smem[Cfg::LDS];
     DSA_LDS_ESCAPE(smem);
     const int m0 = blockIdx.x * BM;
-    pj_tile<BM, BN, WM, WN, ST>(op, m0, 0, smem);
-    epi.template run<BM, BN, Cfg::NT>(reinterpret_cast<float *>(smem), m0, 0, op.M, threadIdx.x);
+    f32x16_t acc[Cfg::TM][Cfg::TN];
+    pj_tile<BM, BN, WM, WN, ST>(op, m0, 0, smem, acc);
+    pj_stage<BM, BN, WM, WN, BM>(acc, smem, [&](float *C, int r0) {
+        epi.template run<BM, BN, Cfg::NT>(C, m0 + r0, 0, op.M, threadIdx.x);
+    });
 }
 
-template <int BM, int BN, int WM, int WN, int ST>
+template <int BM, int BN, int WM, int WN, int ST, int CR>
 __global__ __launch_bounds__(64 * WM *WN) void pj_expand_kv_kernel(PjOperands op, EpiSplitKV epi)
 {
-    using Cfg = PjCfg<BM, BN, WM, WN, ST>;
+    using Cfg = PjCfg<BM, BN, WM, WN, ST, CR>;
     __shared__ __attribute__((aligned(1024))) unsigned char smem[Cfg::LDS];
     DSA_LDS_ESCAPE(smem);
-    const int nb = (op.N + BN - 1) / BN;
-    const int b = xcd_remap(blockIdx.x, gridDim.x);
-    const int m0 = (b / nb) * BM, n0 = (b % nb) * BN;
-    pj_tile<BM, BN, WM, WN, ST>(op, m0, n0, smem);
-    epi.template run<BM, BN, Cfg::NT>(reinterpret_cast<const float *>(smem), m0, n0, op.M, op.N,
-                                      threadIdx.x);
+    const int nb = (op.N + BN - 1) / BN, mb = (op.M + BM - 1) / BM;
+    int tm, tn;
+    pj_tile_of<PJ_GROUP_M>(xcd_remap(blockIdx.x, gridDim.x), mb, nb, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    f32x16_t acc[Cfg::TM][Cfg::TN];
+    pj_tile<BM, BN, WM, WN, ST>(op, m0, n0, smem, acc);
+    pj_stage<BM, BN, WM, WN, CR>(acc, smem, [&](const float *C, int r0) {
+        epi.template run<CR, BN, Cfg::NT>(C, m0 + r0, n0, op.M, op.N, threadIdx.x);
+    });
 }
 
 // ---------------------------------------------------------------- host side
@@ -427,13 +476,14 @@ static RopeArgs rope_args(int rope_dim, float theta)
     return r;
 }
 
-// q and expand_kv: 128 x 128 tiles, 4 waves of 64 x 64, a two-stage ring:
-// 68 KB of LDS, so two blocks share a CU and one's prologue and epilogue
-// overlap the other's matrix work.  k and the head weights: the whole
+// q and expand_kv: 256 x 256 tiles of 8 waves, each 64 x 128 (8 MFMAs per
+// 6 operand reads), a two-stage ring of 64 KB stages; the tile is staged
+// 64 rows at a time for the epilogue.  k and the head weights: the whole
 // 128 + n_heads columns in one tile (LayerNorm needs the full row).
-constexpr int PJ_Q_BM = 128, PJ_Q_BN = 128;
+constexpr int PJ_Q_BM = 256, PJ_Q_BN = 256;
 constexpr int PJ_K_BM = 128;
-constexpr int PJ_E_BM = 128, PJ_E_BN = 128;
+constexpr int PJ_E_BM = 256, PJ_E_BN = 256;
+constexpr int PJ_CR = 64;
 
 hipError_t launch_indexer_frontend(const FrontendArgs &a, hipStream_t st)
 {
@@ -447,8 +497,8 @@ hipError_t launch_indexer_frontend(const FrontendArgs &a, hipStream_t st)
             (int64_t)((a.tokens + PJ_Q_BM - 1) / PJ_Q_BM) * ((op.N + PJ_Q_BN - 1) / PJ_Q_BN);
         if (blocks > 0x7fffffff)
             return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL((pj_rope_q_kernel<PJ_Q_BM, PJ_Q_BN, 2, 2, 2>), dim3((unsigned)blocks),
-                           dim3(256), 0, st, op, epi);
+        hipLaunchKernelGGL((pj_rope_q_kernel<PJ_Q_BM, PJ_Q_BN, 4, 2, 2, PJ_CR>),
+                           dim3((unsigned)blocks), dim3(512), 0, st, op, epi);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
@@ -480,8 +530,8 @@ hipError_t launch_expand_kv(const ExpandArgs &a, hipStream_t st)
         (int64_t)((a.tokens + PJ_E_BM - 1) / PJ_E_BM) * ((N + PJ_E_BN - 1) / PJ_E_BN);
     if (blocks > 0x7fffffff)
         return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((pj_expand_kv_kernel<PJ_E_BM, PJ_E_BN, 2, 2, 2>), dim3((unsigned)blocks),
-                       dim3(256), 0, st, op, epi);
+    hipLaunchKernelGGL((pj_expand_kv_kernel<PJ_E_BM, PJ_E_BN, 4, 2, 2, PJ_CR>),
+                       dim3((unsigned)blocks), dim3(512), 0, st, op, epi);
     return hipGetLastError();
 }
 

@@ -271,3 +271,41 @@ def test_every_output_written_tiny_f32(dsa):
     torch.cuda.synchronize()
     assert not torch.isnan(S).any() and not (idx == POISON_I32).any()
     assert not torch.isnan(out).any() and not torch.isnan(lse).any()
+
+
+# ---------------------------------------------------------------- pool select paths
+
+@pytest.mark.parametrize("np_cols,sk,kp", [(4096, 512, 4), (1000, 300, 2), (4096, 600, 4),
+                                           (6000, 512, 4)])
+def test_pool_select_rows_of_every_kind(dsa, np_cols, sk, kp):
+    """pool_select_kernel on rows that stress the selection: one outlier
+    stretching the range, all scores equal, coarse ties, next to plain rows,
+    short rows, a row with exactly select_k pools and padded queries; both
+    row capacities (up to 4096 and up to 16384 pools) and select_k above
+    512.  Bit-exact against the oracle."""
+    note(f"pool select paths np_cols={np_cols} select_k={sk} kpool={kp}")
+    B, n_q = 2, 24
+    L = np_cols * kp
+    gen = torch.Generator(device="cuda").manual_seed(np_cols + sk)
+    S = torch.randn(B, n_q, np_cols, generator=gen, device="cuda")
+    S[:, 1] = 0.25                                    # all equal
+    S[:, 2] = torch.round(S[:, 2] * 2) / 2            # coarse ties
+    S[:, 3, 7] = 1e30                                 # one outlier
+    S[:, 4] = torch.round(S[:, 4] * 50) / 50
+    S[:, 4, 0] = -1e30
+    pad = torch.tensor([0, 37], dtype=torch.int32, device="cuda")
+    qp = torch.full((B, n_q), L - 1, dtype=torch.int32, device="cuda")
+    qp[:, 5] = torch.tensor([3, 36], dtype=torch.int32)          # padded / before any pool
+    qp[:, 6] = pad + kp * 100 + 1                                 # 100 pools and a tail
+    qp[:, 7] = pad + kp * sk - 1                                  # exactly select_k pools
+    width = sk * kp + kp - 1
+    tok, pools = dsa.pool_select(S, pad, qp, kp, sk, width, want_pools=True)
+    torch.cuda.synchronize()
+    rtok, rpools = oracle.pool_select(cpu(S).numpy().reshape(B * n_q, -1),
+                                      cpu(qp).numpy().reshape(-1),
+                                      np.repeat(cpu(pad).numpy(), n_q), kp, sk, width,
+                                      want_pools=True)
+    got = cpu(tok).numpy().reshape(rtok.shape)
+    bad = np.nonzero((got != rtok).any(1))[0]
+    assert bad.size == 0, f"rows differ: {bad[:8]}"
+    assert np.array_equal(cpu(pools).numpy().reshape(rpools.shape), rpools)
