@@ -78,7 +78,8 @@ STAGE_KERNELS = {
     "cache_write": ("index_cache_write_kernel",),
     "index": ("index_scores",),
     "topk": ("topk_seg_kernel", "topk_chunk_kernel", "topk_merge_kernel",
-             "topk_merge_seg_kernel"),
+             "topk_merge_seg_kernel", "topk_long_pairs_kernel", "topk_long_filter_kernel",
+             "topk_long_merge_kernel", "topk_sink_prefix_kernel"),
     "attend": ("attend_gather_kernel", "attend_combine_kernel", "topk_to_mask_kernel",
                "v_scale_max_kernel", "v_to_f16_kernel", "attend_masked_kernel",
                "attend_heads_gather_kernel", "attend_plain_kernel"),

@@ -6,6 +6,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <initializer_list>
 
 namespace dsa {
@@ -57,6 +58,35 @@ struct TopkArgs {
 };
 size_t topk_workspace_bytes(int rows, int n_cols, int k);
 hipError_t launch_topk(const TopkArgs &a, hipStream_t st);
+
+// Rows of kTopkChunkKeys < n_cols <= kTopkLongKeys * kTopkLongMaxParts keys
+// go through a shared threshold: one block per kTopkLongKeys columns reports
+// kTopkLongPairs (key, count) pairs, the threshold they imply keeps the
+// candidates, and a merge ranks those.  Workspace per row: the candidate
+// count, the pairs (keys, then counts) and up to `cap` candidates.
+constexpr int kTopkLongKeys = 4096;
+constexpr int kTopkLongPairs = 24;
+constexpr int kTopkLongMaxParts = 64;
+constexpr int kTopkLongMaxCand = 16384;
+struct TopkLongLayout {
+    int parts, cap;
+    int64_t pc_off, cand_off, row_bytes;  // byte offsets inside a row's workspace
+};
+inline bool topk_long_path(int n_cols)
+{
+    return n_cols > kTopkChunkKeys && n_cols <= kTopkLongKeys * kTopkLongMaxParts;
+}
+inline TopkLongLayout topk_long_layout(int n_cols)
+{
+    auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
+    TopkLongLayout l;
+    l.parts = (n_cols + kTopkLongKeys - 1) / kTopkLongKeys;
+    l.cap = (int)std::min<int64_t>(kTopkLongMaxCand, up(n_cols));
+    l.pc_off = 64 + (int64_t)l.parts * kTopkLongPairs * 8;
+    l.cand_off = up(l.pc_off + (int64_t)l.parts * kTopkLongPairs * 4);
+    l.row_bytes = up(l.cand_off + (int64_t)l.cap * 8);
+    return l;
+}
 // the allocation-free top-k's scratch: its size, and its device address on
 // the current device (looked up once per device)
 constexpr size_t kTopkScratchBytes = (size_t)16 << 20;

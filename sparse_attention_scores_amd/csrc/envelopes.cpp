@@ -38,6 +38,8 @@ size_t topk_workspace_bytes(int rows, int n_cols, int k)
     // outside the envelope (dsa_topk refuses such k) there is no size
     if (k > kTopkMaxSelect)
         return 0;
+    if (topk_long_path(n_cols))
+        return (size_t)rows * (size_t)topk_long_layout(n_cols).row_bytes;
     const int64_t n_chunks = ((int64_t)n_cols + kTopkChunkKeys - 1) / kTopkChunkKeys;
     return (size_t)rows * (size_t)n_chunks * (size_t)k * sizeof(uint64_t);
 }

@@ -505,34 +505,29 @@ __global__ __launch_bounds__(NT) void topk_chunk_kernel(const float *__restrict_
     (void)R;
 }
 
-// Second launch of the long-row path for few rows: `parts` blocks share a
-// row's candidates (the chunk winners ws[row][0 .. n), zero keys padding;
-// at most kMergeCacheKeys), block `seg` writes output positions
-// [seg*seg_len, seg*seg_len + seg_len), as in topk_seg_kernel: value buckets
-// over the real candidates, the buckets that hold the block's ranks
-// collected and ranked inside by composite key.  Crowded buckets or a
-// non-finite range fall back to the full merge of the row.
+// LDS of the segmented merge: the candidates' order keys and buckets, or
+// the full merge's cache.
 template <int NT>
-__global__ __launch_bounds__(NT) void topk_merge_seg_kernel(const uint64_t *__restrict__ ws,
-                                                            int n_chunks, int k,
-                                                            int32_t *__restrict__ out,
-                                                            int64_t out_stride, int parts,
-                                                            int seg_len)
+union MergeSegSmem {
+    Topk32Smem<NT, kMergeCacheKeys> a;
+    MergeSmem<NT, true> b;
+};
+
+// Segmented merge of one row's candidates cand[0 .. n) (composite keys,
+// zero keys padding; n at most kMergeCacheKeys): the block writes output
+// positions [seg*seg_len, seg*seg_len + seg_len) of o, as in
+// topk_seg_kernel: value buckets over the real candidates, the buckets that
+// hold the block's ranks collected and ranked inside by composite key.
+// Crowded buckets or a non-finite range fall back to the full merge of the
+// row.
+template <int NT>
+__device__ void merge_seg_row(MergeSegSmem<NT> &u, const uint64_t *__restrict__ cand, int n,
+                              int k, int32_t *__restrict__ o, int seg, int seg_len)
 {
     using S = Topk32Smem<NT, kMergeCacheKeys>;
-    using M = MergeSmem<NT, true>;
     constexpr int NB = S::NB, NW = S::NW, PB = NB / NT;
-    union U {
-        S a;
-        M b;
-    };
-    __shared__ U u;
     S &sm = u.a;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const int row = blockIdx.x / parts;
-    const int seg = blockIdx.x - row * parts;
-    const uint64_t *cand = ws + (int64_t)row * n_chunks * k;
-    const int n = n_chunks * k;
     // order keys of the candidates (0 = padding: a real key's order part is
     // at least 0x007fffff), their count and range
     int nv = 0;
@@ -580,7 +575,6 @@ __global__ __launch_bounds__(NT) void topk_merge_seg_kernel(const uint64_t *__re
     }
     __syncthreads();
     const int m = min(k, n_valid);
-    int32_t *o = out + (int64_t)row * out_stride;
     const int p0 = seg * seg_len, p1 = min(p0 + seg_len, k);
     for (int i = max(p0, m) + tid; i < p1; i += NT)
         o[i] = -1;
@@ -668,7 +662,7 @@ __global__ __launch_bounds__(NT) void topk_merge_seg_kernel(const uint64_t *__re
         }
     }
     __syncthreads();  // the segment path's LDS is reused by the full merge
-    constexpr int EPT = 2;
+    constexpr int EPT = kTopkMaxK / NT;
     uint64_t v[EPT];
     int mm;
     merge_sorted<NT, EPT, true>(u.b, cand, n, k, v, mm);
@@ -676,6 +670,516 @@ __global__ __launch_bounds__(NT) void topk_merge_seg_kernel(const uint64_t *__re
     for (int b = 0; b < EPT; ++b) {
         const int i = tid * EPT + b;
         if (i >= s0 && i < s1)
+            o[i] = (int32_t)(0xffffffffu - (uint32_t)v[b]);
+    }
+}
+
+// Second launch of the chunked long-row path for few rows: `parts` blocks
+// share a row's chunk winners ws[row][0 .. n_chunks * k).
+template <int NT>
+__global__ __launch_bounds__(NT) void topk_merge_seg_kernel(const uint64_t *__restrict__ ws,
+                                                            int n_chunks, int k,
+                                                            int32_t *__restrict__ out,
+                                                            int64_t out_stride, int parts,
+                                                            int seg_len)
+{
+    __shared__ MergeSegSmem<NT> u;
+    const int row = blockIdx.x / parts;
+    const int seg = blockIdx.x - row * parts;
+    merge_seg_row<NT>(u, ws + (int64_t)row * n_chunks * k, n_chunks * k, k,
+                      out + (int64_t)row * out_stride, seg, seg_len);
+}
+
+// ------------------------------------------------------ long rows, shared threshold
+//
+// A row of n keys is cut into blocks of kTopkLongKeys columns.  Block p
+// reports pairs (v, c): c is the exact number of its keys whose composite key
+// is at least v.  For a threshold t, any pair of block p with v >= t
+// guarantees c of its keys at or above t, so
+//     G(t) = sum over blocks of the count of the block's last pair with v >= t
+// is a lower bound on the row's keys at or above t.  The largest pair value
+// t with G(t) >= k is therefore at or below the k-th largest key: every
+// winner is at or above it, and the keys at or above it (typically a little
+// over k) are the only candidates the merge has to rank.  The pairs sit at
+// ranks 0, 1, 2, 3, 5, 7, 10, 15, ... (about sqrt 2 apart) up to
+// min(k, n_p) - 1, so the candidates overshoot k by a bounded factor when
+// the pairs are exact ranks; a value bucket crowded by outliers makes them
+// coarser, and when the candidates exceed the workspace the merge ranks the
+// raw row instead (exact, one block, slow).
+
+__device__ __forceinline__ int long_target_rank(int j)
+{
+    // round(sqrt(2)^(j+1)) - 1, strictly increasing from 0
+    constexpr int R[kTopkLongPairs] = {0,   1,   2,   3,   5,    7,    10,   15,
+                                       22,  31,  44,  63,  90,   127,  180,  255,
+                                       361, 511, 723, 1023, 1447, 2047, 2895, 4095};
+    return R[j];
+}
+
+// The block's scores at columns c0 + u*NT + t, loaded before the visible
+// range is known (it only masks them afterwards, so the loads need not wait
+// for it); columns past the row read its last column instead, so every load
+// is unconditional and in bounds.
+template <int NT>
+__device__ __forceinline__ void long_load_block(float (&sv)[kTopkLongKeys / NT],
+                                                const float *__restrict__ srow, int c0,
+                                                int n_cols)
+{
+#pragma unroll
+    for (int u = 0; u < kTopkLongKeys / NT; ++u)
+        sv[u] = srow[min(c0 + u * NT + (int)threadIdx.x, n_cols - 1)];
+}
+
+// First launch: the pairs of block p of every row.  Thread t holds columns
+// c0 + u*NT + t of the block.  The keys are counted into value buckets
+// (linear in the score over the block's [min, max]); each target rank's pair
+// is (smallest composite key of the bucket that holds it, keys in that
+// bucket and in better ones).  When a target lands in a crowded bucket (an
+// outlier stretches the value range, or the range is not finite) the keys
+// are counted again into buckets linear in the order key, which follows the
+// exponent, and each target keeps the smaller of its two buckets.  Also
+// clears the row's candidate count.
+template <int NT>
+__global__ __launch_bounds__(NT) void topk_long_pairs_kernel(
+    const float *__restrict__ scores, int n_cols, int64_t row_stride,
+    const int32_t *__restrict__ vlo, const int32_t *__restrict__ vhi, int k, int lo_skip,
+    unsigned char *__restrict__ ws, int parts, int64_t pc_off, int64_t row_bytes)
+{
+    constexpr int KPT = kTopkLongKeys / NT, NB = 1024, PB = NB / NT, NW = NT / 64;
+    constexpr int NP = kTopkLongPairs;
+    static_assert(KPT * NT == kTopkLongKeys && PB * NT == NB, "whole keys and buckets per thread");
+    static_assert(NP <= 64, "one lane per target");
+    __shared__ uint32_t hist[2][NB + 1];  // bucket NB counts the invisible keys
+    __shared__ int8_t first_target[2][NB + 1];
+    __shared__ unsigned long long mink[NP];
+    __shared__ int tbin[2][NP], tcnt[2][NP], tsize[2][NP];
+    __shared__ uint32_t red[2][NW];
+    __shared__ int tab[NW];
+    __shared__ int s_crowded;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int row = blockIdx.x / parts, p = blockIdx.x - row * parts;
+    unsigned char *w = ws + (int64_t)row * row_bytes;
+    uint64_t *pv = reinterpret_cast<uint64_t *>(w + 64) + p * NP;
+    uint32_t *pc = reinterpret_cast<uint32_t *>(w + pc_off) + p * NP;
+    if (p == 0 && tid == 0)
+        *reinterpret_cast<int *>(w) = 0;  // the candidate count, summed by the next launch
+    const int c0 = p * kTopkLongKeys;
+    float sv[KPT];
+    long_load_block<NT>(sv, scores + (int64_t)row * row_stride, c0, n_cols);
+    const int row_hi = min(vhi[row], n_cols);
+    const int lo = max(first_ranked(vlo[row], row_hi, lo_skip), c0);
+    const int hi = min(row_hi, c0 + kTopkLongKeys);
+    const int m = min(k, max(hi - lo, 0));  // the pairs cover ranks below m
+    uint32_t ord[KPT];
+    uint32_t valid = 0u, mn = ~0u, mx = 0u;
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+        const int col = c0 + u * NT + tid;
+        ord[u] = score_order_key(sv[u]);
+        if (col >= lo && col < hi) {
+            valid |= 1u << u;
+            mn = min(mn, ord[u]);
+            mx = max(mx, ord[u]);
+        }
+    }
+    mn = wave_min_u32(mn);
+    mx = wave_max_u32(mx);
+    if (lane == 0) {
+        red[0][wid] = mn;
+        red[1][wid] = mx;
+    }
+    for (int i = tid; i <= NB; i += NT) {
+        hist[0][i] = hist[1][i] = 0u;
+        first_target[0][i] = first_target[1][i] = -1;
+    }
+    if (tid < NP)
+        mink[tid] = ~0ull;
+    if (tid == 0)
+        s_crowded = 0;
+    __syncthreads();
+    uint32_t omin = ~0u, omax = 0u;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        omin = min(omin, red[0][i]);
+        omax = max(omax, red[1][i]);
+    }
+    // target j covers rank min(R_j, m - 1); the pairs after the first that
+    // reaches m - 1 are empty (count 0)
+    auto past_last = [&](int j) { return j > 0 && long_target_rank(j - 1) >= m - 1; };
+    if (m == 0 || omin == omax) {
+        // nothing visible, or all keys equal: rank r is column lo + r
+        if (tid < NP) {
+            const int r = min(long_target_rank(tid), m - 1);
+            const bool use = m > 0 && !past_last(tid);
+            pv[tid] = use ? compose_key(omin, (uint32_t)(lo + r)) : 0ull;
+            pc[tid] = use ? (uint32_t)(r + 1) : 0u;
+        }
+        return;
+    }
+    ValueBuckets vb;
+    const bool by_value = vb.init(omin, omax, NB);
+    // order-key buckets: floor((o - omin) * mul / 2^32), clamped below NB,
+    // with mul about NB * 2^32 / span (any mul gives a monotone map; the
+    // product stays below 2^43, no 64-bit division)
+    const double span = (double)(omax - omin) + 1.0;
+    const uint64_t mul = (uint64_t)((double)((uint64_t)NB << 32) / span);
+    auto ob = [&](uint32_t o) {
+        return NB - 1 - min((int)(((uint64_t)(o - omin) * mul) >> 32), NB - 1);
+    };
+    // Count scheme sc's buckets b[] and locate each target: thread t owns
+    // buckets t*PB .. t*PB + PB - 1 (bucket 0 the best), the keys in better
+    // buckets come from a block scan.
+    auto count_and_locate = [&](int sc, const int (&b)[KPT]) {
+#pragma unroll
+        for (int u = 0; u < KPT; ++u)
+            atomicAdd(&hist[sc][b[u]], 1u);  // invisible keys carry bucket NB
+        __syncthreads();
+        uint32_t cv[PB];
+        int sum = 0;
+#pragma unroll
+        for (int j = 0; j < PB; ++j) {
+            cv[j] = hist[sc][tid * PB + j];
+            sum += (int)cv[j];
+        }
+        const int incl = wave_inclusive_scan(sum);
+        if (lane == 63)
+            tab[wid] = incl;
+        __syncthreads();
+        int run0 = incl - sum;
+#pragma unroll
+        for (int i = 0; i < NW; ++i)
+            run0 += i < wid ? tab[i] : 0;
+#pragma unroll
+        for (int t = 0; t < NP; ++t) {
+            const int r = min(long_target_rank(t), m - 1);
+            if (run0 <= r && r < run0 + sum) {
+                int run = run0;
+#pragma unroll
+                for (int j = 0; j < PB; ++j) {
+                    const int c = (int)cv[j];
+                    if (run <= r && r < run + c) {
+                        tbin[sc][t] = tid * PB + j;
+                        tcnt[sc][t] = run + c;
+                        tsize[sc][t] = c;
+                    }
+                    run += c;
+                }
+            }
+        }
+        __syncthreads();
+    };
+    int bv[KPT], bo[KPT];
+    const int first = by_value ? 0 : 1;
+#pragma unroll
+    for (int u = 0; u < KPT; ++u)
+        bv[u] = (valid >> u & 1u) ? (by_value ? vb(ord[u]) : ob(ord[u])) : NB;
+    count_and_locate(first, bv);
+    // crowded: a target's bucket holds more than twice the keys up to its rank
+    if (tid < NP && !past_last(tid)) {
+        const int r = min(long_target_rank(tid), m - 1);
+        if (tsize[first][tid] > 2 * (r + 1) + 8)
+            s_crowded = 1;
+    }
+    __syncthreads();
+    const bool both = by_value && s_crowded;
+    if (both) {
+#pragma unroll
+        for (int u = 0; u < KPT; ++u)
+            bo[u] = (valid >> u & 1u) ? ob(ord[u]) : NB;
+        count_and_locate(1, bo);
+    }
+    // each target takes the smaller of its buckets; each chosen bucket is
+    // named by its lowest target
+    if (tid < NP) {
+        const int t = tid;
+        const int sc = (both && tsize[1][t] < tsize[0][t]) ? 1 : first;
+        bool lowest = true;
+        if (!both) {
+            // one scheme: a target's bucket is never better than the previous
+            // target's, so the targets of a bucket are consecutive
+            lowest = t == 0 || tbin[sc][t - 1] != tbin[sc][t];
+        } else {
+            for (int u = 0; u < t; ++u) {
+                const int su = tsize[1][u] < tsize[0][u] ? 1 : 0;
+                lowest = lowest && !(su == sc && tbin[su][u] == tbin[sc][t]);
+            }
+        }
+        if (lowest)
+            first_target[sc][tbin[sc][t]] = (int8_t)t;
+    }
+    __syncthreads();
+    // the smallest composite key of each chosen bucket
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+        // invisible keys sit in bucket NB, which no target names
+        const unsigned long long key = compose_key(ord[u], (uint32_t)(c0 + u * NT + tid));
+        const int t0 = first_target[first][bv[u]];
+        if (t0 >= 0)
+            atomicMin(&mink[t0], key);
+        if (both) {
+            const int t1 = first_target[1][bo[u]];
+            if (t1 >= 0)
+                atomicMin(&mink[t1], key);
+        }
+    }
+    __syncthreads();
+    if (tid < NP) {
+        const bool use = !past_last(tid);
+        const int sc = (both && tsize[1][tid] < tsize[0][tid]) ? 1 : first;
+        pv[tid] = use ? (uint64_t)mink[first_target[sc][tbin[sc][tid]]] : 0ull;
+        pc[tid] = use ? (uint32_t)tcnt[sc][tid] : 0u;
+    }
+}
+
+// Second launch: the row's threshold from all pairs, then block p keeps its
+// keys at or above it.  The threshold is found by weight: pair j of a block
+// carries the increment c_j - c_(j-1) of its count, so G(v) is the summed
+// increments of the pairs at or above v; value buckets over the pairs find
+// the bucket where the running sum reaches k, and the pairs inside it are
+// summed exactly.
+template <int NT>
+__global__ __launch_bounds__(NT) void topk_long_filter_kernel(
+    const float *__restrict__ scores, int n_cols, int64_t row_stride,
+    const int32_t *__restrict__ vlo, const int32_t *__restrict__ vhi, int k, int lo_skip,
+    unsigned char *__restrict__ ws, int parts, int64_t pc_off, int64_t cand_off,
+    int64_t row_bytes, int cap)
+{
+    constexpr int KPT = kTopkLongKeys / NT, NW = NT / 64, NP = kTopkLongPairs;
+    constexpr int NB = 256;  // pair buckets
+    constexpr int MAXP = kTopkLongMaxParts * NP;
+    static_assert(KPT * NT == kTopkLongKeys && NT >= NB, "whole keys per thread, a bucket per thread");
+    __shared__ uint64_t spv[MAXP];
+    __shared__ uint32_t sdelta[MAXP];
+    __shared__ uint32_t hist[NB];
+    __shared__ uint64_t bin_v[MAXP];
+    __shared__ uint32_t bin_d[MAXP];
+    __shared__ uint64_t red64[2][NW];
+    __shared__ int tab[NW];
+    __shared__ int s_bin, s_above, s_nbin, s_base;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int row = blockIdx.x / parts, p = blockIdx.x - row * parts;
+    unsigned char *w = ws + (int64_t)row * row_bytes;
+    const uint64_t *pv = reinterpret_cast<const uint64_t *>(w + 64);
+    const uint32_t *pc = reinterpret_cast<const uint32_t *>(w + pc_off);
+    const int np = parts * NP;
+    const int c0 = p * kTopkLongKeys;
+    float sv[KPT];
+    long_load_block<NT>(sv, scores + (int64_t)row * row_stride, c0, n_cols);
+    // every pair load in flight before any is used
+    constexpr int PPT = (MAXP + NT - 1) / NT;
+    uint64_t lv[PPT];
+    uint32_t lc[PPT], lcp[PPT];
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) {
+        const int i = j * NT + tid;
+        const bool in = i < np;
+        lv[j] = in ? pv[i] : 0ull;
+        lc[j] = in ? pc[i] : 0u;
+        lcp[j] = (in && i % NP) ? pc[i - 1] : 0u;
+    }
+    uint64_t vmn = ~0ull, vmx = 0ull;
+    int total = 0;
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) {
+        const int i = j * NT + tid;
+        if (i < np) {
+            const uint32_t d = lc[j] > lcp[j] ? lc[j] - lcp[j] : 0u;
+            spv[i] = lv[j];
+            sdelta[i] = d;
+            if (d) {
+                vmn = lv[j] < vmn ? lv[j] : vmn;
+                vmx = lv[j] > vmx ? lv[j] : vmx;
+                total += (int)d;
+            }
+        }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const uint64_t a = shfl_xor_u64(vmn, o), b = shfl_xor_u64(vmx, o);
+        vmn = a < vmn ? a : vmn;
+        vmx = b > vmx ? b : vmx;
+    }
+    total = wave_sum_int(total);
+    if (lane == 0) {
+        red64[0][wid] = vmn;
+        red64[1][wid] = vmx;
+        tab[wid] = total;
+    }
+    if (tid < NB)
+        hist[tid] = 0u;
+    if (tid == 0)
+        s_nbin = 0;
+    __syncthreads();
+    vmn = red64[0][0];
+    vmx = red64[1][0];
+    total = tab[0];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) {
+        vmn = red64[0][i] < vmn ? red64[0][i] : vmn;
+        vmx = red64[1][i] > vmx ? red64[1][i] : vmx;
+        total += tab[i];
+    }
+    uint64_t t_low = 0ull;  // fewer than k keys guaranteed anywhere: all keys are candidates
+    if (total >= k) {
+        // bucket of a pair value, linear in the 64-bit key (monotone), 0 the best
+        const double scale = vmx > vmn ? (double)(NB - 1) / (double)(vmx - vmn) : 0.0;
+        auto pb = [&](uint64_t v) {
+            const int b = (int)((double)(v - vmn) * scale);
+            return NB - 1 - min(max(b, 0), NB - 1);
+        };
+        int pbk[PPT];
+#pragma unroll
+        for (int j = 0; j < PPT; ++j) {
+            const int i = j * NT + tid;
+            pbk[j] = (i < np && sdelta[i]) ? pb(spv[i]) : -1;
+            if (pbk[j] >= 0)
+                atomicAdd(&hist[pbk[j]], sdelta[i]);
+        }
+        __syncthreads();
+        if (wid == 0) {
+            // lane l owns buckets 4l .. 4l + 3: the bucket where the running
+            // weight from the top reaches k
+            static_assert(NB == 256, "four pair buckets per lane of one wave");
+            uint32_t c4[4];
+            int sum = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                c4[j] = hist[4 * lane + j];
+                sum += (int)c4[j];
+            }
+            int run = wave_inclusive_scan(sum) - sum;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (run < k && k <= run + (int)c4[j]) {
+                    s_bin = 4 * lane + j;
+                    s_above = run;
+                }
+                run += (int)c4[j];
+            }
+        }
+        __syncthreads();
+        const int bb = s_bin, ab = s_above;
+        // the pairs of that bucket, compacted with one LDS atomic per wave
+#pragma unroll
+        for (int j = 0; j < PPT; ++j) {
+            const bool in = pbk[j] == bb;
+            const uint64_t bal = __ballot(in);
+            int base = 0;
+            if (lane == 0 && bal)
+                base = atomicAdd(&s_nbin, __popcll(bal));
+            base = __builtin_amdgcn_readfirstlane(base);
+            if (in) {
+                const int slot = base + __popcll(bal & ((1ull << lane) - 1ull));
+                const int i = j * NT + tid;
+                bin_v[slot] = spv[i];
+                bin_d[slot] = sdelta[i];
+            }
+        }
+        __syncthreads();
+        const int nbin = s_nbin;
+        uint64_t best = 0ull;
+        for (int i = tid; i < nbin; i += NT) {
+            const uint64_t v = bin_v[i];
+            int g = ab;
+            for (int j = 0; j < nbin; ++j)
+                g += bin_v[j] >= v ? (int)bin_d[j] : 0;
+            if (g >= k && v > best)
+                best = v;
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            const uint64_t a = shfl_xor_u64(best, o);
+            best = a > best ? a : best;
+        }
+        if (lane == 0)
+            red64[0][wid] = best;
+        __syncthreads();
+        t_low = red64[0][0];
+#pragma unroll
+        for (int i = 1; i < NW; ++i)
+            t_low = red64[0][i] > t_low ? red64[0][i] : t_low;
+    }
+    // this block's keys at or above the threshold, one atomic per block
+    const int row_hi = min(vhi[row], n_cols);
+    const int lo = max(first_ranked(vlo[row], row_hi, lo_skip), c0);
+    const int hi = min(row_hi, c0 + kTopkLongKeys);
+    uint32_t take = 0u;
+    int cnt = 0;
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+        const int col = c0 + u * NT + tid;
+        const bool t = col >= lo && col < hi &&
+                       compose_key(score_order_key(sv[u]), (uint32_t)col) >= t_low;
+        take |= (uint32_t)t << u;
+        cnt += t;
+    }
+    const int incl = wave_inclusive_scan(cnt);
+    __syncthreads();
+    if (lane == 63)
+        tab[wid] = incl;
+    __syncthreads();
+    int pos = incl - cnt;
+    int block_total = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        pos += i < wid ? tab[i] : 0;
+        block_total += tab[i];
+    }
+    if (block_total == 0)
+        return;
+    if (tid == 0)
+        s_base = atomicAdd(reinterpret_cast<int *>(w), block_total);
+    __syncthreads();
+    pos += s_base;
+    uint64_t *cand = reinterpret_cast<uint64_t *>(w + cand_off);
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+        if (take >> u & 1u) {
+            if (pos < cap)
+                cand[pos] = compose_key(score_order_key(sv[u]), (uint32_t)(c0 + u * NT + tid));
+            ++pos;
+        }
+    }
+}
+
+// Third launch: `parts` blocks per row rank the row's candidates
+// (merge_seg_row).  If the threshold kept more candidates than the
+// workspace holds, block 0 of the row ranks the raw row instead: radix
+// select of the k largest keys, then a sort.
+template <int NT>
+__global__ __launch_bounds__(NT) void topk_long_merge_kernel(
+    const float *__restrict__ scores, int n_cols, int64_t row_stride,
+    const int32_t *__restrict__ vlo, const int32_t *__restrict__ vhi, int k, int lo_skip,
+    const unsigned char *__restrict__ ws, int64_t cand_off, int64_t row_bytes, int cap,
+    int32_t *__restrict__ out, int64_t out_stride, int parts, int seg_len)
+{
+    __shared__ MergeSegSmem<NT> u;
+    const int row = blockIdx.x / parts;
+    const int seg = blockIdx.x - row * parts;
+    const unsigned char *w = ws + (int64_t)row * row_bytes;
+    const int n = *reinterpret_cast<const int *>(w);
+    int32_t *o = out + (int64_t)row * out_stride;
+    const uint64_t *cand = reinterpret_cast<const uint64_t *>(w + cand_off);
+    if (n <= cap) {
+        merge_seg_row<NT>(u, cand, n, k, o, seg, seg_len);
+        return;
+    }
+    if (seg != 0)
+        return;
+    const int row_hi = min(vhi[row], n_cols);
+    const int lo = first_ranked(vlo[row], row_hi, lo_skip);
+    const int nv = max(row_hi - lo, 0);  // > cap > k: the threshold kept more than cap keys
+    const float *srow = scores + (int64_t)row * row_stride + lo;
+    auto key_at = [&](int i) { return compose_key(score_order_key(srow[i]), (uint32_t)(lo + i)); };
+    radix_select(u.b, nv, k, key_at);
+    constexpr int EPT = kTopkMaxK / NT;
+    uint64_t v[EPT];
+    bitonic_sort_regs<NT, EPT>(u.b, k, v);
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int b = 0; b < EPT; ++b) {
+        const int i = tid * EPT + b;
+        if (i < k)
             o[i] = (int32_t)(0xffffffffu - (uint32_t)v[b]);
     }
 }
@@ -769,6 +1273,26 @@ hipError_t launch_topk(const TopkArgs &a, hipStream_t st)
         hipLaunchKernelGGL((topk_seg_kernel<NT, kCapLarge>), dim3(a.rows * parts), dim3(NT), 0,
                            st, a.scores, a.n_cols, a.row_stride, a.vis_lo, a.vis_hi, k, out,
                            ostride, n_s, parts, seg_len);
+        return hipGetLastError();
+    }
+    if (topk_long_path(a.n_cols)) {
+        const TopkLongLayout l = topk_long_layout(a.n_cols);
+        unsigned char *ws = static_cast<unsigned char *>(a.workspace);
+        // 1024 threads, 4 keys each: four waves per SIMD hide each other's latency
+        constexpr int LT = 1024;
+        const unsigned blocks = (unsigned)(a.rows * l.parts);
+        hipLaunchKernelGGL((topk_long_pairs_kernel<LT>), dim3(blocks), dim3(LT), 0, st, a.scores,
+                           a.n_cols, a.row_stride, a.vis_lo, a.vis_hi, k, n_s, ws, l.parts,
+                           l.pc_off, l.row_bytes);
+        hipLaunchKernelGGL((topk_long_filter_kernel<LT>), dim3(blocks), dim3(LT), 0, st, a.scores,
+                           a.n_cols, a.row_stride, a.vis_lo, a.vis_hi, k, n_s, ws, l.parts,
+                           l.pc_off, l.cand_off, l.row_bytes, l.cap);
+        const int mparts = topk_seg_parts(a.rows, k, 32);
+        const int seg_len = (k + mparts - 1) / mparts;
+        // the merge caches up to kMergeCacheKeys keys: 512 threads (32 per thread)
+        hipLaunchKernelGGL((topk_long_merge_kernel<512>), dim3(a.rows * mparts), dim3(512), 0, st,
+                           a.scores, a.n_cols, a.row_stride, a.vis_lo, a.vis_hi, k, n_s, ws,
+                           l.cand_off, l.row_bytes, l.cap, out, ostride, mparts, seg_len);
         return hipGetLastError();
     }
     const int n_chunks = (a.n_cols + kCapLarge - 1) / kCapLarge;

@@ -234,8 +234,14 @@ void topk()
     int32_t *out = dev<int32_t>(21);
     void *ws = dev(22);
     CHECK(dsa_topk_workspace_size(32, 8192, 2048) == 0);
+    // rows of 131072 keys (threshold path): per row a 64-byte header, 32
+    // blocks x 24 pairs of (8-byte key, 4-byte count) and 16384 candidates,
+    // each part starting on a 256-byte boundary
     const size_t need = dsa_topk_workspace_size(8, 131072, 2048);
-    CHECK(need == (size_t)8 * 8 * 2048 * 8);
+    CHECK(need == (size_t)8 * (9472 + 131072));
+    CHECK(9472 == ((64 + 32 * 24 * 12) + 255) / 256 * 256);
+    // rows of 300000 keys (chunked path): 19 chunks of 2048 winners
+    CHECK(dsa_topk_workspace_size(2, 300000, 2048) == (size_t)2 * 19 * 2048 * 8);
     CHECK(dsa_topk_workspace_size(8, 131072, 4096) == 0);
     CHECK(dsa_topk_workspace_size(INT32_MAX, INT32_MAX, 2048) ==
           (size_t)INT32_MAX * 131072 * 2048 * 8);

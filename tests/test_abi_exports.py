@@ -61,9 +61,11 @@ def test_workspace_errors_without_gpu():
     from sparse_attention_scores_amd import binding
     lib = binding.load()
     fake = ctypes.c_void_p(0x1000)
-    # long rows: the chunked top-k keeps its chunk winners in the workspace
+    # long rows: the threshold top-k keeps its pairs and candidates in the
+    # workspace (a 64-byte header, 5 blocks x 24 pairs of 8 + 4 bytes, then
+    # 16384 candidates of 8 bytes on a 256-byte boundary)
     need = lib.dsa_topk_workspace_size(1, 20000, 2048)
-    assert need == 2 * 2048 * 8
+    assert need == 1536 + 16384 * 8
     assert lib.dsa_topk(fake, 1, 20000, 20000, fake, fake, 2048, 0, fake, None, 0, None) == -4
     assert b"workspace" in lib.dsa_last_error()
     assert lib.dsa_topk(fake, 1, 20000, 20000, fake, fake, 2048, 0, fake, fake, need - 1,

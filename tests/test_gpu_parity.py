@@ -163,9 +163,9 @@ TOPK_CASES = [
     (2, dict(B=300, Tk=6000), None, 2048),   # many rows of 6000 keys: one block per row
     (3, dict(Tq=300, Tk=300), None, 100),    # causal: k >= visible on early rows
     (3, dict(Tq=2600, Tk=2600), None, 2048), # short rows, k = 2048: the last bucket spills past k
-    (4, dict(B=2, Tk=40000), None, 2048),    # > one block's cache: two-launch path
-    (4, dict(B=1, Tk=40000), "tie", 2048),   # two-launch path with ties
-    (4, dict(B=1, Tk=150000), None, 2048),   # merge candidates beyond the LDS cache
+    (4, dict(B=2, Tk=40000), None, 2048),    # > one block's cache: threshold path
+    (4, dict(B=1, Tk=40000), "tie", 2048),   # threshold path with ties
+    (4, dict(B=1, Tk=150000), None, 2048),   # threshold path, a partial last block
 ]
 
 
@@ -184,10 +184,10 @@ def test_topk_bit_exact_on_gpu_scores(dsa, cfg, over, variant, k):
 
 
 def test_topk_long_rows_skewed(dsa):
-    """Long rows (chunked path) where one chunk holds every top score, so the
-    merge's lower bound prunes almost nothing and the survivors overflow the
-    LDS cache; and a row whose visible window leaves chunks with fewer than
-    their quota of real keys."""
+    """Long rows where one stretch of columns holds every top score (one
+    block's pairs alone set the threshold), a row whose last, partial block
+    wins, and a row whose visible window leaves blocks with fewer keys than
+    their pairs' ranks."""
     note("topk long rows, skewed")
     rng = np.random.default_rng(21)
     n, k = 150000, 2048

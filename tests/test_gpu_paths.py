@@ -110,14 +110,14 @@ def test_index_scores_generic_kernel_left_padding(dsa):
                      d=d, heads=H)
 
 
-# ---------------------------------------------------------------- top-k merge in one block
+# ---------------------------------------------------------------- top-k, one merge block per row
 
 @pytest.mark.parametrize("rows,n,k", [(256, 20000, 2048), (4, 40000, 100), (3, 70000, 64),
                                       (300, 16385, 777)])
 def test_topk_merge_one_block_per_row(dsa, rows, n, k):
-    """Rows longer than one block's cache with one merge block per row
-    (topk_merge_kernel with the chunk candidates cached in LDS): 256 or more
-    rows, or k below 128.  Some rows carry quantised ties and a visibility
+    """Rows longer than one block's cache (the shared-threshold path) with
+    256 or more rows, or k below 128, so the merge of the candidates takes
+    one block per row.  Some rows carry quantised ties and a visibility
     window."""
     note(f"topk one-block merge rows={rows} n={n} k={k}")
     gen = torch.Generator(device="cuda").manual_seed(rows * 7 + k)
