@@ -437,10 +437,44 @@ __global__ __launch_bounds__(64 * IP_NW) void index_scores_prefill_kernel(
         kaddr[ks] = (uint32_t)((col * 16 + ((2 * ks + g) ^ (col & 15))) * 16);
     const uint32_t lds0 = lds_addr(tiles[0]);
 
+    // -FLT_MAX over the keys of the chunk before tile ta and from tile tb on
+    // (the invisible tiles of block qb) for the wave's queries, in 16-byte
+    // stores, the two halves taking half of each range: 8x fewer store
+    // instructions than one 4-byte score per lane.  Issued after the block's
+    // tiles, so no wait for the query loads or tile DMAs waits for them.
+    auto fill_invisible = [&](int qb, int ta, int tb) {
+#pragma unroll
+        for (int qi = 0; qi < IP_QPW; ++qi) {
+            const int t = qb * IP_QB + wid * IP_QPW + qi;
+            if (t >= n_q)
+                continue;
+            float *rp = scores + ((int64_t)b * n_q + t) * n_k;
+            const int g0 = (int)((reinterpret_cast<uintptr_t>(rp) >> 2) & 3);  // row start mod 4 floats
+            const int ra[2] = {c0, min(c1, c0 + 32 * tb)};
+            const int rb[2] = {min(c1, c0 + 32 * ta), c1};
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const int mid = ra[r] + ((rb[r] - ra[r]) / 2 & ~3);
+                const int a = half ? mid : ra[r], e = half ? rb[r] : mid;
+                if (a >= e)
+                    continue;
+                // scalar head up to a 16-byte boundary, vector body, scalar tail
+                const int ha = min(e, a + (int)((4 - ((g0 + a) & 3)) & 3));
+                const int tb4 = max(ha, e - (int)((g0 + e) & 3));
+                if (a + lane < ha)
+                    rp[a + lane] = -FLT_MAX;
+                for (int j = ha + 4 * lane; j < tb4; j += 256)
+                    *reinterpret_cast<f32x4_t *>(rp + j) =
+                        f32x4_t{-FLT_MAX, -FLT_MAX, -FLT_MAX, -FLT_MAX};
+                if (tb4 + lane < e)
+                    rp[tb4 + lane] = -FLT_MAX;
+            }
+        }
+    };
+
     // Tiles [t0, t1) (chunk tile indices, all visible to block qb) for the
-    // wave's queries of block qb, and the -FLT_MAX rows of the block's
-    // invisible tiles of this half's parity (the two halves share that work).
-    auto run = [&](int qb, int t0, int t1, int ta, int tb) {
+    // wave's queries of block qb.
+    auto run = [&](int qb, int t0, int t1) {
         u32x4_t qf[IP_QPW][KS];
         float wr[IP_QPW][16];
         int lo[IP_QPW], hi[IP_QPW];
@@ -463,37 +497,6 @@ __global__ __launch_bounds__(64 * IP_NW) void index_scores_prefill_kernel(
 #pragma unroll
             for (int i = 0; i < 16; ++i)
                 wr[qi][i] = w[qrow[qi] * IP_H + 8 * (i / 4) + 4 * g + (i % 4)] * fabsf(scale);
-        }
-        {
-            // the keys of the chunk before tile ta and from tile tb on, in
-            // 16-byte stores (the two halves take half of each range): 8x
-            // fewer store instructions than one 4-byte score per lane
-            const int ra[2] = {c0, min(c1, c0 + 32 * tb)};
-            const int rb[2] = {min(c1, c0 + 32 * ta), c1};
-#pragma unroll
-            for (int qi = 0; qi < IP_QPW; ++qi) {
-                if (!qok[qi])
-                    continue;
-                float *rp = scores + qrow[qi] * n_k;
-                const int g0 = (int)((reinterpret_cast<uintptr_t>(rp) >> 2) & 3);  // row start mod 4 floats
-#pragma unroll
-                for (int r = 0; r < 2; ++r) {
-                    const int mid = ra[r] + ((rb[r] - ra[r]) / 2 & ~3);
-                    const int a = half ? mid : ra[r], b = half ? rb[r] : mid;
-                    if (a >= b)
-                        continue;
-                    // scalar head up to a 16-byte boundary, vector body, scalar tail
-                    const int ha = min(b, a + (int)((4 - ((g0 + a) & 3)) & 3));
-                    const int tb4 = max(ha, b - (int)((g0 + b) & 3));
-                    if (a + lane < ha)
-                        rp[a + lane] = -FLT_MAX;
-                    for (int j = ha + 4 * lane; j < tb4; j += 256)
-                        *reinterpret_cast<f32x4_t *>(rp + j) =
-                            f32x4_t{-FLT_MAX, -FLT_MAX, -FLT_MAX, -FLT_MAX};
-                    if (tb4 + lane < b)
-                        rp[tb4 + lane] = -FLT_MAX;
-                }
-            }
         }
         if (t0 >= t1)
             return;
@@ -531,6 +534,9 @@ __global__ __launch_bounds__(64 * IP_NW) void index_scores_prefill_kernel(
                         float (&part)[IP_QPW], bool fin) {
             static_assert(IP_QPW == 2, "the sums are pinned for two queries");
             const int st = (tt - t0) % IP_STAGES;
+            // tile tt has landed once at most the later tiles' DMAs are
+            // outstanding (loads complete in order; the score stores between
+            // them only make the wait stricter)
             vm_wait_tiles<1>(min(t1 - 1, tt + IP_STAGES - 2) - tt);
             lds_barrier();
             if (tt + IP_STAGES - 1 < t1)
@@ -615,10 +621,14 @@ __global__ __launch_bounds__(64 * IP_NW) void index_scores_prefill_kernel(
         }
         lds_barrier();  // every wave is done with the ring before it is refilled
     };
-    // this half's share of the pair's list
-    run(qb_late, la + min(w0, n_late), la + min(w1, n_late), la, lb);
+    // this half's share of the pair's list, then the invisible keys of both
+    // blocks
+    run(qb_late, la + min(w0, n_late), la + min(w1, n_late));
     if (qb_early != qb_late)
-        run(qb_early, ea + max(w0 - n_late, 0), ea + max(w1 - n_late, 0), ea, eb);
+        run(qb_early, ea + max(w0 - n_late, 0), ea + max(w1 - n_late, 0));
+    fill_invisible(qb_late, la, lb);
+    if (qb_early != qb_late)
+        fill_invisible(qb_early, ea, eb);
 }
 
 // Plain f32 kernel: one thread per (query row, key).

@@ -37,7 +37,7 @@ struct PjCfg {
     static constexpr int SB = AB + BN * PJ_BK * 2;
     static constexpr int DMA = SB / 1024;     // one-KB loads per stage
     static constexpr int LPW = DMA / NW;      // of them per wave
-    static constexpr int CP = BN + 8;         // staged C row pitch in floats
+    static constexpr int CP = BN + 4;         // staged C row pitch in floats
     static constexpr int RING = ST * SB;
     static constexpr int CTILE = CR * CP * 4;  // staged C rows (CR of them at a time)
     static constexpr int LDS = RING > CTILE ? RING : CTILE;
@@ -143,7 +143,7 @@ struct EpiRopeQ {
             const int m = m0 + r;
             if (m >= M)
                 continue;
-            head_item(C + r * (BN + 8) + hh * 128,
+            head_item(C + r * (BN + 4) + hh * 128,
                       out + (int64_t)m * out_row + n0 + hh * 128, item, pos[m], rope);
         }
     }
@@ -165,7 +165,7 @@ struct EpiNormRopeK {
     __device__ void run(float *C, int m0, int n0, int M, int tid) const
     {
         static_assert(NT == 2 * BM, "two threads per row");
-        constexpr int CP = BN + 8;
+        constexpr int CP = BN + 4;
         {
             const int r = tid >> 1, h = tid & 1;
             float *row = C + r * CP + 64 * h;
@@ -230,7 +230,7 @@ struct EpiSplitKV {
             uint16_t *dst = j < kd ? k + (int64_t)m * ksr + (int64_t)head * kd + j
                                    : v + (int64_t)m * vsr + (int64_t)head * vd + (j - kd);
             float x[8];
-            load_f32x8(x, C + r * (BN + 8) + 8 * c);
+            load_f32x8(x, C + r * (BN + 4) + 8 * c);
             store_bf16x8(dst, x);
         }
     }
@@ -276,7 +276,10 @@ __device__ __forceinline__ void wait_operands(u32x4_t (&v)[N])
 }
 
 // The block's f32 tile C = A[m0 .. m0+BM) B[n0 .. n0+BN)^T in the waves'
-// accumulators (wave (wm, wn) holds rows wm * BM/WM .., columns wn * BN/WN ..).
+// accumulators (wave (wm, wn) holds rows wm * BM/WM .., columns wn * BN/WN ..),
+// each 32 x 32 block transposed: the MFMA takes the B fragment as its first
+// operand, so lane l holds row l % 32 and four consecutive columns per
+// group of four accumulators (8 (e / 4) + 4 (l / 32) + e % 4).
 // Rows past M (and past N) load the last valid row instead, so every load
 // stays inside the operands; the epilogues skip them.
 template <int BM, int BN, int WM, int WN, int ST>
@@ -376,20 +379,21 @@ __device__ __forceinline__ void pj_tile(const PjOperands &op, int m0, int n0, un
             for (int i = 0; i < TM; ++i)
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
-                    acc[i][j] = mfma_32x32x16(av[cur][i], bv[cur][j], acc[i][j]);
+                    acc[i][j] = mfma_32x32x16(bv[cur][j], av[cur][i], acc[i][j]);
         }
     }
     lds_barrier();  // every wave is done with the ring before it is reused
 }
 
-// Stage the tile in LDS CR rows at a time (row pitch BN + 8 floats: the two
-// half-waves' rows, four apart, start 32 banks apart) and hand each chunk
-// to finish(C, r0) on every thread.
+// Stage the tile in LDS CR rows at a time and hand each chunk to
+// finish(C, r0) on every thread.  A lane writes its row's four consecutive
+// columns as one 16-byte store; the row pitch of BN + 4 floats starts each
+// of 16 consecutive rows on a different group of four banks.
 template <int BM, int BN, int WM, int WN, int CR, class F>
 __device__ __forceinline__ void pj_stage(const f32x16_t (&acc)[BM / WM / 32][BN / WN / 32],
                                          unsigned char *smem, F &&finish)
 {
-    constexpr int TM = BM / WM / 32, TN = BN / WN / 32, CP = BN + 8;
+    constexpr int TM = BM / WM / 32, TN = BN / WN / 32, CP = BN + 4;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wid % WM, wn = wid / WM;
@@ -401,13 +405,15 @@ __device__ __forceinline__ void pj_stage(const f32x16_t (&acc)[BM / WM / 32][BN 
             const int rt = wm * (BM / WM) + i * 32;  // the 32-row tile's first row
             if (rt < r0 || rt >= r0 + CR)
                 continue;
+            const int row = rt - r0 + (lane & 31);
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
-                const int col = wn * (BN / WN) + j * 32 + (lane & 31);
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int row = rt - r0 + 8 * (e >> 2) + 4 * g + (e & 3);
-                    C[row * CP + col] = acc[i][j][e];
+                for (int q = 0; q < 4; ++q) {
+                    const int col = wn * (BN / WN) + j * 32 + 8 * q + 4 * g;
+                    *reinterpret_cast<f32x4_t *>(C + row * CP + col) =
+                        f32x4_t{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                acc[i][j][4 * q + 3]};
                 }
             }
         }
