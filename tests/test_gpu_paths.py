@@ -7,6 +7,8 @@ reach the rest of what the ABI accepts:
   * index_scores_mfma_kernel (8-15 queries per sequence; fp8 keys with 8 or
     more queries; 64 indexer heads; head_dim 64, bf16 and fp8) and the decode
     kernel at 64 heads / head_dim 64;
+  * pool_keys_kernel on f32 keys, and pool_counts_kernel (sequences shorter
+    than one pool);
   * attend_gather_kernel's set-bitmap path (more than 2048 entries per row)
     at the largest n_k the gather kernel takes (262144);
   * topk_merge_kernel with the candidates in LDS (one block per row: 256 or
@@ -61,6 +63,9 @@ INDEX_PATH_CASES = [
     (4, dict(B=2, Tq=9, Tk=1000, d=64), "mfma<64,32 heads> fp8, 9 queries"),
     (4, dict(B=2, Tq=1, Tk=700, d=64, Hi=64), "mfma<64,64 heads,1 query> fp8"),
     (3, dict(Tq=77, Tk=77, d=64, Hi=64), "mfma<64,64 heads> bf16 causal"),
+    (4, dict(B=2, Tq=8, Tk=1000, Hi=64), "mfma<128,64 heads> fp8, 8 queries"),
+    (4, dict(B=2, Tq=9, Tk=1000, d=64, Hi=64), "mfma<64,64 heads> fp8, 9 queries"),
+    (2, dict(B=2, Tq=1, Tk=1000, d=64, Hi=64), "decode<64,64 heads> bf16"),
 ]
 
 
@@ -309,3 +314,36 @@ def test_pool_select_rows_of_every_kind(dsa, np_cols, sk, kp):
     bad = np.nonzero((got != rtok).any(1))[0]
     assert bad.size == 0, f"rows differ: {bad[:8]}"
     assert np.array_equal(cpu(pools).numpy().reshape(rpools.shape), rpools)
+
+
+# ---------------------------------------------------------------- pool keys on f32, short sequences
+
+@pytest.mark.parametrize("L,kp", [(1030, 4), (515, 8), (3, 4)])
+def test_pool_keys_f32_and_sequences_shorter_than_a_pool(dsa, L, kp):
+    """f32 keys and gates (pool_keys_kernel<float>), and L < kpool, where no
+    pool exists and only the counts are written (pool_counts_kernel).
+    Criterion: each pooled value within 2 (kpool + 4) 2^-24 mag + 2^-23 |ref|
+    of the f64 oracle, mag = sum_j softmax_j |k_j|: the kernel forms kpool
+    exponentials (two ulps each), two sums of kpool terms and one quotient in
+    f32, a factor 2 over those rounding steps."""
+    note(f"pool keys f32 L={L} kpool={kp}")
+    gen = torch.Generator(device="cuda").manual_seed(L * 7 + kp)
+    B, d = 3, 128
+    k = torch.randn(B, L, d, generator=gen, device="cuda")
+    gate = torch.randn(B, L, d, generator=gen, device="cuda") * 3
+    pad = torch.tensor([0, min(1, L), min(13, L)], dtype=torch.int32, device="cuda")
+    out = torch.full((B, L // kp, d), float("nan"), device="cuda")
+    n_pools = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    pk, npools = dsa.pool_keys(k, gate, pad, kp, out=out, n_pools=n_pools)
+    torch.cuda.synchronize()
+    ref, rn, mag = oracle.pool_keys(cpu(k), cpu(gate), cpu(pad), kp, want_mag=True)
+    assert cpu(npools).tolist() == rn.tolist()
+    if L // kp == 0:
+        assert pk.numel() == 0
+        return
+    got = cpu(pk).double().numpy()
+    for b, n in enumerate(rn):
+        assert np.all(got[b, n:] == 0.0), "pools past n_pools must be zero"
+        g, r, m = got[b, :n], ref[b, :n], mag[b, :n]
+        bound = 2 * (kp + 4) * 2.0 ** -24 * m + 2.0 ** -23 * np.abs(r)
+        assert np.all(np.abs(g - r) <= bound), float((np.abs(g - r) / bound).max())
