@@ -175,12 +175,15 @@ int dsa_topk(const float *scores, int32_t rows, int32_t n_cols,
  * forbid hipMalloc.
  *
  * Arguments and results are those of dsa_topk without the workspace.  Rows
- * longer than 16384 keys keep their chunk winners in a scratch array the
- * library holds in each GPU's memory until the process ends
- * (DSA_TOPK_NOALLOC_SCRATCH_BYTES per GPU); its device address is looked up
- * once per device, on the first call made with that device current.
+ * longer than 16384 keys keep their per-block (key, count) pairs and their
+ * candidates (up to 262144 keys), or their chunk winners (longer rows), in
+ * a scratch array the library holds in each GPU's memory until the process
+ * ends (DSA_TOPK_NOALLOC_SCRATCH_BYTES per GPU); its device address is
+ * looked up once per device, on the first call made with that device
+ * current.  Nothing in it has to start at zero: each call clears the
+ * counters it uses in its own first kernel.
  * Limit: dsa_topk_workspace_size(rows, n_cols, top_k) <= 16 MiB (for
- * instance 8 rows of 131072 keys at top_k 2048 need 1 MiB); a larger call
+ * instance 8 rows of 131072 keys at top_k 2048 need 1.07 MiB); a larger call
  * returns DSA_ERR_UNSUPPORTED and enqueues nothing.  The call itself
  * allocates nothing (no hipMalloc, no library allocation).
  * Every call on one GPU shares that GPU's array, which keeps the last

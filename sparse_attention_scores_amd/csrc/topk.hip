@@ -1199,14 +1199,15 @@ int topk_seg_parts(int rows, int k, int max_parts)
     return std::max(parts, 1);
 }
 
-// Scratch of the allocation-free top-k entry point: the chunk winners of
-// rows longer than kCapLarge keys, in memory the library holds on each GPU
-// for the life of the process.  Host code must not pass `scratch` itself to
+// Scratch of the allocation-free top-k entry point: the threshold path's
+// pairs and candidates, or the chunk winners of longer rows, in memory the
+// library holds on each GPU for the life of the process.  Host code must not pass `scratch` itself to
 // a kernel (in host code the name stands for a host-side shadow, not the
 // device address): topk_scratch() looks the device address up once per
 // device, with that device current, and every launch takes that pointer.
-// The chunk kernel writes every slot it owns (zero keys pad short chunks),
-// so nothing in it has to start at zero.
+// Nothing in it has to start at zero: the chunk kernel writes every slot it
+// owns (zero keys pad short chunks), and the pairs kernel writes every pair
+// and clears the row's candidate count before the filter adds to it.
 static __device__ __align__(256) unsigned char scratch[kTopkScratchBytes];
 
 namespace {
