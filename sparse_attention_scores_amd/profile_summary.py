@@ -15,6 +15,11 @@
     python -m sparse_attention_scores_amd.profile_summary mfma \
         --counters COUNTER_CSV --stats STATS_CSV --cmd-counters "..." --cmd-trace "..."
 
+    # which of the library's kernels a run launched (e.g. the GPU test suite
+    # under rocprofv3 --kernel-trace --stats), against every __global__
+    # kernel defined in csrc
+    python -m sparse_attention_scores_amd.profile_summary coverage STATS_CSV --cmd "..."
+
 The traffic record carries a digest of the kernel sources; bench.py only
 reports the recorded traffic while the sources still match it.
 """
@@ -164,6 +169,31 @@ def mfma(counter_csv: str, stats_csv: str, cmd_counters: str, cmd_trace: str) ->
     return "\n".join(lines) + "\n"
 
 
+def coverage(stats_csv: str, cmd: str) -> str:
+    """The library kernels (dsa::) a run launched, with their calls, and the
+    __global__ kernels defined in csrc that it never launched."""
+    ran = {}
+    for r in csv.DictReader(open(stats_csv)):
+        n = short_name(r["Name"])
+        if "dsa::" in n:
+            ran[n] = ran.get(n, 0) + int(r["Calls"])
+    defined = {}
+    pat = re.compile(r"__global__\s+(?:__launch_bounds__\([^)]*\)\s+)?void\s+(\w+)\s*\(")
+    for path in sorted(glob.glob(os.path.join(CSRC, "*.hip"))):
+        for m_ in pat.finditer(open(path).read()):
+            defined[m_.group(1)] = os.path.basename(path)
+    base = {re.search(r"dsa::(\w+)", n).group(1) for n in ran}
+    missing = sorted(k for k in defined if k not in base)
+    lines = [f"# kernels launched by: {cmd}",
+             f"# {len(base & set(defined))} of {len(defined)} __global__ kernels in csrc ran "
+             f"({len(ran)} template instantiations); never launched: "
+             f"{', '.join(missing) if missing else 'none'}",
+             f"# {'kernel':<78s} {'calls':>6s}"]
+    for n in sorted(ran):
+        lines.append(f"  {n[:78]:<78s} {ran[n]:6d}")
+    return "\n".join(lines) + "\n"
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -181,8 +211,13 @@ def main(argv=None):
     m.add_argument("--stats", required=True)
     m.add_argument("--cmd-counters", required=True)
     m.add_argument("--cmd-trace", required=True)
+    v = sub.add_parser("coverage")
+    v.add_argument("stats_csv")
+    v.add_argument("--cmd", required=True)
     a = ap.parse_args(argv)
-    if a.what == "trace":
+    if a.what == "coverage":
+        sys.stdout.write(coverage(a.stats_csv, a.cmd))
+    elif a.what == "trace":
         sys.stdout.write(trace(a.stats_csv, a.cmd))
     elif a.what == "mfma":
         sys.stdout.write(mfma(a.counters, a.stats, a.cmd_counters, a.cmd_trace))
