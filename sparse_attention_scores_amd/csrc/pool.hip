@@ -141,79 +141,69 @@ hipError_t launch_pool_keys(const PoolKeysArgs &a, hipStream_t st)
 // topk_pools + expand_selection ("Module glm5next_dsa_ref"): the top
 // select_k visible pools of each query in rank order (higher pooled score,
 // then smaller pool id), each expanded to its kpool token ids ascending, then
-// the visible tail, then INVALID to out_width.  The pools' 64-bit composite
-// keys are selected by radix passes and ordered by a bitonic sort.
-template <int NT, int CAP, int EPT>
+// the visible tail, then INVALID to out_width.  One block per query row; the
+// pools are ranked with value buckets (seg_rank_row), and each ranked pool
+// writes its own kpool tokens, so the selection is never sorted as a list.
+template <int NT, int CAP, int KM, int NBK>
 __global__ __launch_bounds__(NT) void pool_select_kernel(
     const float *__restrict__ scores, const int32_t *__restrict__ pad,
     const int32_t *__restrict__ q_pos, int32_t *__restrict__ out_tok,
     int32_t *__restrict__ out_pools, int n_q, int np_cols, int kpool, int select_k,
     int out_width)
 {
-    __shared__ TopkSmem<NT, CAP> sm;
+    __shared__ Topk32Smem<NT, CAP, KM, NBK> sm;
     const int tid = threadIdx.x;
     const int row = blockIdx.x;
     const int b = row / n_q;
     const int p = pad[b];
     const int t = q_pos[row];
     const int n_full = t >= p ? min((t - p + 1) / kpool, np_cols) : 0;
-    const int n = load_row(sm, scores + (int64_t)row * np_cols, 0, n_full);
-    auto key_at = [&](int i) -> uint64_t { return compose_key(sm.ord[i], (uint32_t)i); };
-    int m;
-    if (n > select_k) {
-        radix_select(sm, n, select_k, key_at);
-        m = select_k;
-    } else {
-        for (int i = tid; i < n; i += NT)
-            sm.sel[i] = key_at(i);
-        __syncthreads();
-        m = n;
-    }
-    {
-        uint64_t v[EPT];
-        bitonic_sort_regs<NT, EPT>(sm, m, v);
-#pragma unroll
-        for (int b = 0; b < EPT; ++b)
-            sm.sel[tid * EPT + b] = v[b];
-        __syncthreads();
-    }
-    // expand_selection: pools' tokens (rank order), the visible tail, INVALID
+    const int m = min(select_k, n_full);
+    int32_t *o = out_tok + (int64_t)row * out_width;
+    int32_t *op = out_pools ? out_pools + (int64_t)row * select_k : nullptr;
+    // four tokens per pool as one 16-byte store where the row allows it
+    const bool quad = kpool == 4 && (reinterpret_cast<uintptr_t>(o) & 15) == 0;
+    if (m > 0)
+        seg_rank_row(sm, scores + (int64_t)row * np_cols, 0, n_full, select_k, 0, m,
+                     [&](int r, int pool) {
+                         const int tok = p + pool * kpool;
+                         if (quad) {
+                             *reinterpret_cast<int4 *>(o + 4 * r) =
+                                 make_int4(tok, tok + 1, tok + 2, tok + 3);
+                         } else {
+                             for (int j = 0; j < kpool; ++j)
+                                 o[r * kpool + j] = tok + j;
+                         }
+                         if (op)
+                             op[r] = pool;
+                     });
+    // the visible tail after the pools' tokens, then INVALID
     const int pool_toks = m * kpool;
     const int tail = t >= p ? (t + 1) - (p + n_full * kpool) : 0;
-    int32_t *o = out_tok + (int64_t)row * out_width;
-    for (int i = tid; i < out_width; i += NT) {
-        int v = -1;
-        if (i < pool_toks) {
-            const int pool = (int)(0xffffffffu - (uint32_t)sm.sel[i / kpool]);
-            v = p + pool * kpool + i % kpool;
-        } else if (i < pool_toks + tail) {
-            v = p + n_full * kpool + (i - pool_toks);
-        }
-        o[i] = v;
-    }
-    if (out_pools) {
-        int32_t *op = out_pools + (int64_t)row * select_k;
-        for (int i = tid; i < select_k; i += NT)
-            op[i] = i < m ? (int32_t)(0xffffffffu - (uint32_t)sm.sel[i]) : -1;
-    }
+    for (int i = pool_toks + tid; i < out_width; i += NT)
+        o[i] = i < pool_toks + tail ? p + n_full * kpool + (i - pool_toks) : -1;
+    if (op)
+        for (int i = m + tid; i < select_k; i += NT)
+            op[i] = -1;
 }
 
 hipError_t launch_pool_select(const PoolSelectArgs &a, hipStream_t st)
 {
     const int np_cols = a.seq / a.kpool;
     const unsigned rows = (unsigned)(a.batch * a.n_q);
-#define DSA_POOL_SELECT(NT, CAP, EPT)                                                              \
-    hipLaunchKernelGGL((pool_select_kernel<NT, CAP, EPT>), dim3(rows), dim3(NT), 0, st, a.scores,  \
-                       a.pad, a.q_pos, a.out_tok, a.out_pools, a.n_q, np_cols, a.kpool,            \
+#define DSA_POOL_SELECT(NT, CAP, KM, NBK)                                                         \
+    hipLaunchKernelGGL((pool_select_kernel<NT, CAP, KM, NBK>), dim3(rows), dim3(NT), 0, st,        \
+                       a.scores, a.pad, a.q_pos, a.out_tok, a.out_pools, a.n_q, np_cols, a.kpool,  \
                        a.select_k, a.out_width)
-    if (np_cols <= 4096) {
-        if (a.select_k <= 512)
-            DSA_POOL_SELECT(256, 4096, 2);
-        else
-            DSA_POOL_SELECT(256, 4096, 8);
-    } else {
-        DSA_POOL_SELECT(1024, 16384, 2);
-    }
+    static_assert(kPoolSelectMaxPools <= 16384, "one block caches a row of pools");
+    // up to 512 pools selected: winner arrays for 512 and 1024 buckets take
+    // 33 KB of LDS, so four blocks share a CU instead of two
+    if (np_cols <= 4096 && a.select_k <= 512)
+        DSA_POOL_SELECT(512, 4096, 512, 1024);
+    else if (np_cols <= 4096)
+        DSA_POOL_SELECT(512, 4096, kTopkMaxK, 2048);
+    else
+        DSA_POOL_SELECT(1024, 16384, kTopkMaxK, 2048);
 #undef DSA_POOL_SELECT
     return hipGetLastError();
 }

@@ -27,85 +27,6 @@
 
 namespace dsa {
 
-// Sorted top-k of the n order keys cached in sm (column lo + i for key i):
-// 32-bit select, compaction, bucket sort (stable radix sort for ties and
-// crowded buckets).  Returns m = min(k, n); the winners' columns in rank
-// order are sm.wcol[buf][0 .. m).
-template <int NT, int CAP>
-__device__ int topk_sort_cached(Topk32Smem<NT, CAP> &sm, int n, int lo, int k, uint32_t omin,
-                                uint32_t omax, int &buf)
-{
-    // n <= k: everything wins (mask 0 makes every key a candidate, all taken)
-    uint32_t prefix = 0u, mask = 0u;
-    int need = n, cand = n;
-    if (n > k)
-        select32(sm, n, k, omin, omax, prefix, mask, need, cand);
-    // The bucket sort places each winner by its composite key (order key,
-    // column), so it takes them in any order; when the whole boundary group
-    // wins (no tie at the boundary to break by column) the fast unordered
-    // compaction feeds it.  Equal order keys everywhere, or a bucket sort
-    // that gives up, need the winners in column order (the stable radix
-    // sort keeps it for equal keys): then the stable compaction reruns from
-    // the key cache, which the bucket sort leaves intact.
-    uint32_t wmin, wmax;
-    const bool any_order = cand == need;
-    int m = any_order ? compact32_any(sm, n, lo, prefix, mask, wmin, wmax)
-                      : compact32(sm, n, lo, prefix, mask, need, cand, wmin, wmax);
-    bool sorted = (!any_order || wmin != wmax) && bucket_sort32(sm, m, wmin, wmax);
-    buf = 0;
-    if (!sorted) {
-        if (any_order)
-            m = compact32(sm, n, lo, prefix, mask, need, cand, wmin, wmax);
-        // all keys equal: column order is the rank order already
-        buf = wmin == wmax ? 0 : sort32(sm, m, wmin, wmax);
-    }
-    return m;
-}
-
-// Float value of an order key (inverse of score_order_key; -0 comes back
-// as +0).
-__device__ __forceinline__ float order_key_value(uint32_t o)
-{
-    return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
-}
-
-// Segmented top-k: `parts` blocks share a row, block `seg` writes output
-// positions [seg*seg_len, seg*seg_len + seg_len) of it, so a few rows still
-// fill the chip.  Every block caches the whole row and counts it into NB
-// buckets linear in the score value over [min, max] (a monotonic map, so a
-// higher bucket never holds a lower-ranked key); the prefix sums give each
-// bucket's first rank.  The block then collects only the buckets that hold
-// its ranks and places each collected key inside its bucket by counting the
-// members with a larger composite key (order key, then smaller column) --
-// the exact rank order, ties included.  No block selects, compacts or sorts
-// the whole row.  When its ranks fall into crowded buckets (a score range
-// stretched by outliers) or the value range is not finite, the block takes
-// the full sorted top-k of the row instead and writes its positions from it.
-// Value buckets of a row segment (shared by the bucket kernels below): NB
-// buckets linear in the score value over [vmin, vmax], numbered from the top
-// (bucket 0 holds the largest values).  The map is monotonic, so every key
-// of a lower-numbered bucket ranks above every key of a higher-numbered one.
-struct ValueBuckets {
-    float vmin, scale;
-    int nb;
-    __device__ bool init(uint32_t omin, uint32_t omax, int nbuckets)
-    {
-        nb = nbuckets;
-        vmin = order_key_value(omin);
-        const float vmax = order_key_value(omax);
-        scale = (float)nb / (vmax - vmin);
-        return __builtin_isfinite(vmin) && __builtin_isfinite(vmax) &&
-               __builtin_isfinite(scale) && scale > 0.f;
-    }
-    __device__ int operator()(uint32_t ord) const
-    {
-        const int b = (int)((order_key_value(ord) - vmin) * scale);
-        return nb - 1 - min(max(b, 0), nb - 1);
-    }
-};
-
-constexpr int kSegMaxBucket = 256;
-
 // First column a row ranks by score: the start of its visible range [lo, hi)
 // moved past the `skip` attention-sink columns that lead it (clamped to hi;
 // no overflow for any lo).
@@ -130,6 +51,10 @@ __global__ __launch_bounds__(256) void topk_sink_prefix_kernel(const int32_t *__
     const int lo = max(vlo[row], 0);
     out[(int64_t)row * k + j] = j < hi - lo ? lo + j : -1;
 }
+
+// Segmented top-k: `parts` blocks share a row, block `seg` writes output
+// positions [seg*seg_len, seg*seg_len + seg_len) of it, so a few rows still
+// fill the chip; each places its ranks with value buckets (seg_rank_row).
 template <int NT, int CAP>
 __global__ __launch_bounds__(NT) void topk_seg_kernel(const float *__restrict__ scores,
                                                       int n_cols, int64_t row_stride,
@@ -139,165 +64,22 @@ __global__ __launch_bounds__(NT) void topk_seg_kernel(const float *__restrict__ 
                                                       int64_t out_stride, int lo_skip, int parts,
                                                       int seg_len)
 {
-    using S = Topk32Smem<NT, CAP>;
-    constexpr int NB = S::NB, NW = S::NW, PB = NB / NT, R = CAP / NT;
-    static_assert(PB >= 1 && NB % NT == 0, "every thread owns whole buckets");
-    __shared__ S sm;
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    __shared__ Topk32Smem<NT, CAP> sm;
+    const int tid = threadIdx.x;
     const int row = blockIdx.x / parts;
     const int seg = blockIdx.x - row * parts;
     const int hi = min(vhi[row], n_cols);
     const int lo = first_ranked(vlo[row], hi, lo_skip);
     const int n = max(hi - lo, 0);
-    const int rounds = (n + NT - 1) / NT;  // uniform, at most R
-    // thread t keeps keys r*NT + t (r < rounds) in registers: their order keys
-    // and, below, their buckets (all loads issued before any is used)
-    const float *rp = scores + (int64_t)row * row_stride + lo;
-    uint32_t ord[R];
-    {
-        float v[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-            v[r] = (r < rounds && r * NT + tid < n) ? rp[r * NT + tid] : 0.f;
-        uint32_t mn = ~0u, mx = 0u;
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            ord[r] = score_order_key(v[r]);
-            if (r < rounds && r * NT + tid < n) {
-                mn = min(mn, ord[r]);
-                mx = max(mx, ord[r]);
-            }
-        }
-        mn = wave_min_u32(mn);
-        mx = wave_max_u32(mx);
-        if (lane == 0) {
-            sm.mm[0][wid] = mn;
-            sm.mm[1][wid] = mx;
-        }
-    }
-    for (int i = tid; i < NB; i += NT)
-        sm.bk.fill[i] = 0u;
-    __syncthreads();
-    uint32_t omin = sm.mm[0][0], omax = sm.mm[1][0];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) {
-        omin = min(omin, sm.mm[0][w]);
-        omax = max(omax, sm.mm[1][w]);
-    }
     const int m = min(k, n);
     int32_t *o = out + (int64_t)row * out_stride;
     const int p0 = seg * seg_len, p1 = min(p0 + seg_len, k);
+    const int s0 = p0, s1 = min(p1, m);  // ranks this block writes
+    if (s0 < s1)
+        seg_rank_row(sm, scores + (int64_t)row * row_stride + lo, lo, n, k, s0, s1,
+                     [&](int r, int col) { o[r] = col; });
     for (int i = max(p0, m) + tid; i < p1; i += NT)
         o[i] = -1;
-    const int s0 = p0, s1 = min(p1, m);  // ranks this block writes
-    if (s0 >= s1)
-        return;
-    if (omin == omax) {  // every key equal: column order is the rank order
-        for (int i = s0 + tid; i < s1; i += NT)
-            o[i] = lo + i;
-        return;
-    }
-    ValueBuckets bucket;
-    bool ok = bucket.init(omin, omax, NB);
-    if (ok) {
-        int bk[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            bk[r] = NB;  // none
-            if (r < rounds && r * NT + tid < n) {
-                bk[r] = bucket(ord[r]);
-                atomicAdd(&sm.bk.fill[bk[r]], 1u);
-            }
-        }
-        __syncthreads();
-        // exclusive prefix over the buckets (thread t owns PB consecutive
-        // ones); the buckets holding ranks s0 and s1-1
-        uint32_t v[PB];
-        int sum = 0;
-#pragma unroll
-        for (int j = 0; j < PB; ++j) {
-            v[j] = sm.bk.fill[tid * PB + j];
-            sum += (int)v[j];
-        }
-        const int incl = wave_inclusive_scan(sum);
-        if (lane == 63)
-            sm.tab[0][wid] = incl;
-        __syncthreads();
-        int run = incl - sum;
-#pragma unroll
-        for (int w = 0; w < NW; ++w)
-            run += w < wid ? sm.tab[0][w] : 0;
-        int crowd_lo = 0, crowd_hi = 0;  // sizes of the buckets holding s0 and s1-1
-#pragma unroll
-        for (int j = 0; j < PB; ++j) {
-            const int b = tid * PB + j, c = (int)v[j];
-            sm.bk.off[b] = (uint32_t)run;
-            sm.bk.fill[b] = (uint32_t)run;  // fill pointer of the collection below
-            if (run <= s0 && s0 < run + c) {
-                sm.tab[1][0] = b;
-                crowd_lo = c;
-            }
-            if (run <= s1 - 1 && s1 - 1 < run + c) {
-                sm.tab[1][1] = b;
-                crowd_hi = c;
-            }
-            run += c;
-        }
-        // a bucket strictly between them holds only ranks of this segment
-        // (all of which are placed anyway); the two end buckets can hold many
-        // keys outside it (ties, or a range stretched by an outlier), and
-        // placing a key costs one compare per member of its bucket
-        if (crowd_lo)
-            sm.red[0][0][0] = crowd_lo;
-        if (crowd_hi)
-            sm.red[0][0][1] = crowd_hi;
-        __syncthreads();
-        const int bf = sm.tab[1][0], bl = sm.tab[1][1];
-        const int base = (int)sm.bk.off[bf];
-        const int crowd = max(sm.red[0][0][0], sm.red[0][0][1]);
-        const int total = (bl + 1 < NB ? (int)sm.bk.off[bl + 1] : n) - base;  // keys of bf .. bl
-        // the collection buffer holds 3072 keys: k plus the rest of the last bucket
-        constexpr int kCollect = (int)((sizeof(sm.word[1]) + sizeof(sm.wcol)) / 8);
-        ok = crowd <= kSegMaxBucket && total <= kCollect;
-        if (ok) {
-            // the collection from registers (key of rank base + i at ck[i])
-            uint64_t *ck = reinterpret_cast<uint64_t *>(&sm.word[1][0]);
-            static_assert(kCollect >= kTopkMaxK + kSegMaxBucket,
-                          "composite key buffer");
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                if (bk[r] >= bf && bk[r] <= bl)
-                    ck[atomicAdd(&sm.bk.fill[bk[r]], 1u) - (uint32_t)base] =
-                        ((uint64_t)ord[r] << 32) |
-                        (uint64_t)(0xffffffffu - (uint32_t)(lo + r * NT + tid));
-            }
-            __syncthreads();
-            // rank of each collected key: its bucket's first rank plus the
-            // members of the bucket above it
-            for (int j = tid; j < total; j += NT) {
-                const uint64_t key = ck[j];
-                const int b = bucket((uint32_t)(key >> 32));
-                const int b0 = (int)sm.bk.off[b] - base, b1 = (int)sm.bk.fill[b] - base;
-                int r = (int)sm.bk.off[b];
-                for (int x = b0; x < b1; ++x)
-                    r += ck[x] > key;
-                if (r >= s0 && r < s1)
-                    o[r] = (int32_t)(0xffffffffu - (uint32_t)key);
-            }
-            return;
-        }
-        __syncthreads();  // the bucket arrays are reused below
-    }
-    // the full sorted top-k of the row, from the key cache
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-        if (r < rounds && r * NT + tid < n)
-            sm.a.ord[r * NT + tid] = ord[r];
-    __syncthreads();
-    int buf;
-    topk_sort_cached(sm, n, lo, k, omin, omax, buf);
-    for (int i = s0 + tid; i < s1; i += NT)
-        o[i] = (int32_t)sm.wcol[buf][i];
 }
 
 constexpr int kMergeCacheKeys = 16384;

@@ -300,13 +300,16 @@ namespace dsa {
 //  3. a stable LSD radix sort on the inverted order key (8-bit digits, only
 //     over the bits in which the winners differ) then leaves equal keys in
 //     column order, which is exactly the tie rule.
-template <int NT, int CAP>
+// KM is the largest k the block serves (the winner arrays) and NBK the
+// number of value buckets.
+template <int NT, int CAP, int KM = kTopkMaxK, int NBK = 2048>
 struct __attribute__((aligned(16))) Topk32Smem {
     static constexpr int NW = NT / 64;
-    static constexpr int EPT = kTopkMaxK / NT;           // sort rounds (winners per thread)
+    static constexpr int EPT = KM / NT;                  // sort rounds (winners per thread)
     static constexpr int NCNT = 256 * EPT * NW;          // (digit, round, wave) counters
-    static constexpr int NB = 2048;                      // bucket-sort buckets
+    static constexpr int NB = NBK;                       // bucket-sort buckets
     static constexpr int R = CAP / NT;                   // compaction rounds
+    static_assert(KM % NT == 0 && EPT >= 1, "whole sort rounds");
     static_assert(CAP * 4 >= NCNT * 2, "radix-sort counters overlay the key cache");
     static_assert(R <= 32, "round flags are kept in one 32-bit mask");
     union {
@@ -314,8 +317,8 @@ struct __attribute__((aligned(16))) Topk32Smem {
         uint16_t cnt[NCNT];       // radix-sort counters, after the last compaction
     } a;
     int tab[2][R * NW + 1];       // (round, wave) counts -> exclusive prefixes, + total
-    uint32_t word[2][kTopkMaxK];  // winners' order keys (sort ping-pong)
-    uint32_t wcol[2][kTopkMaxK];  // winners' columns
+    uint32_t word[2][KM];         // winners' order keys (sort ping-pong)
+    uint32_t wcol[2][KM];         // winners' columns
     union {
         uint32_t hist[NW][256];   // per-wave select histograms
         struct {
@@ -329,8 +332,8 @@ struct __attribute__((aligned(16))) Topk32Smem {
 };
 
 // Load scores[lo, hi) into sm.a.ord (column order) and reduce their min/max.
-template <int NT, int CAP>
-__device__ int load_row32(Topk32Smem<NT, CAP> &sm, const float *__restrict__ row, int lo, int hi,
+template <int NT, int CAP, int KM, int NBK>
+__device__ int load_row32(Topk32Smem<NT, CAP, KM, NBK> &sm, const float *__restrict__ row, int lo, int hi,
                           uint32_t &omin, uint32_t &omax)
 {
     constexpr int U = (CAP / NT) < 8 ? (CAP / NT) : 8;
@@ -377,8 +380,8 @@ __device__ int load_row32(Topk32Smem<NT, CAP> &sm, const float *__restrict__ row
 // Boundary of the k largest of the n order keys in sm.a.ord (n > k >= 1):
 // keys with (ord & mask) > prefix win (k - need of them); of the `cand` keys
 // with (ord & mask) == prefix, the first `need` in column order win.
-template <int NT, int CAP>
-__device__ void select32(Topk32Smem<NT, CAP> &sm, int n, int k, uint32_t omin, uint32_t omax,
+template <int NT, int CAP, int KM, int NBK>
+__device__ void select32(Topk32Smem<NT, CAP, KM, NBK> &sm, int n, int k, uint32_t omin, uint32_t omax,
                          uint32_t &prefix, uint32_t &mask, int &need, int &cand)
 {
     constexpr int NW = NT / 64;
@@ -468,8 +471,8 @@ __device__ __forceinline__ void wave_scan_table(int *tab, int e)
 // is (round, wave, lane): each thread keeps its per-round flags in a bit
 // mask, the (round, wave) counts are scanned once by one wave, and the
 // positions follow from ballots -- two barriers per counted quantity.
-template <int NT, int CAP>
-__device__ int compact32(Topk32Smem<NT, CAP> &sm, int n, int col0, uint32_t prefix, uint32_t mask,
+template <int NT, int CAP, int KM, int NBK>
+__device__ int compact32(Topk32Smem<NT, CAP, KM, NBK> &sm, int n, int col0, uint32_t prefix, uint32_t mask,
                          int need, int cand, uint32_t &wmin, uint32_t &wmax)
 {
     constexpr int NW = NT / 64;
@@ -552,8 +555,8 @@ __device__ int compact32(Topk32Smem<NT, CAP> &sm, int n, int col0, uint32_t pref
 // counts its winners over all rounds first and claims one range of an LDS
 // counter with a single atomic; the positions inside it follow from the
 // ballots.  Returns the count and the winners' min / max.
-template <int NT, int CAP>
-__device__ int compact32_any(Topk32Smem<NT, CAP> &sm, int n, int col0, uint32_t prefix,
+template <int NT, int CAP, int KM, int NBK>
+__device__ int compact32_any(Topk32Smem<NT, CAP, KM, NBK> &sm, int n, int col0, uint32_t prefix,
                              uint32_t mask, uint32_t &wmin, uint32_t &wmax)
 {
     constexpr int NW = NT / 64, R = CAP / NT;
@@ -619,10 +622,10 @@ __device__ int compact32_any(Topk32Smem<NT, CAP> &sm, int n, int col0, uint32_t 
 // column).  The result replaces buffer 0.  Returns false, touching nothing
 // but the bucket arrays, when a bucket holds more than 64 winners (many
 // equal high bits): the caller then sorts with sort32.
-template <int NT, int CAP>
-__device__ bool bucket_sort32(Topk32Smem<NT, CAP> &sm, int m, uint32_t wmin, uint32_t wmax)
+template <int NT, int CAP, int KM, int NBK>
+__device__ bool bucket_sort32(Topk32Smem<NT, CAP, KM, NBK> &sm, int m, uint32_t wmin, uint32_t wmax)
 {
-    using S = Topk32Smem<NT, CAP>;
+    using S = Topk32Smem<NT, CAP, KM, NBK>;
     constexpr int NB = S::NB, NW = S::NW, PB = NB / NT;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const uint32_t diff = wmin ^ wmax;
@@ -688,7 +691,7 @@ __device__ bool bucket_sort32(Topk32Smem<NT, CAP> &sm, int m, uint32_t wmin, uin
     // composite keys (order key, complemented column): one 64-bit compare
     // then decides the rank order
     uint64_t *ck = reinterpret_cast<uint64_t *>(&sm.word[1][0]);  // word[1], wcol[0..1] region
-    static_assert(sizeof(sm.word[1]) + sizeof(sm.wcol) >= kTopkMaxK * 8, "composite key buffer");
+    static_assert(sizeof(sm.word[1]) + sizeof(sm.wcol) >= KM * 8, "composite key buffer");
     uint64_t mine[S::EPT];
     int mbkt[S::EPT];
 #pragma unroll
@@ -733,10 +736,10 @@ __device__ bool bucket_sort32(Topk32Smem<NT, CAP> &sm, int m, uint32_t wmin, uin
 
 // Stable LSD radix sort of the m winners (sm.word / sm.wcol buffer 0) by
 // descending order key; returns the buffer that holds the result.
-template <int NT, int CAP>
-__device__ int sort32(Topk32Smem<NT, CAP> &sm, int m, uint32_t wmin, uint32_t wmax)
+template <int NT, int CAP, int KM, int NBK>
+__device__ int sort32(Topk32Smem<NT, CAP, KM, NBK> &sm, int m, uint32_t wmin, uint32_t wmax)
 {
-    using S = Topk32Smem<NT, CAP>;
+    using S = Topk32Smem<NT, CAP, KM, NBK>;
     constexpr int NW = S::NW, EPT = S::EPT, NCNT = S::NCNT;
     constexpr int PER = NCNT / NT;  // counters scanned per thread
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -808,6 +811,235 @@ __device__ int sort32(Topk32Smem<NT, CAP> &sm, int m, uint32_t wmin, uint32_t wm
         src ^= 1;
     }
     return src;
+}
+
+// Sorted top-k of the n order keys cached in sm (column lo + i for key i):
+// 32-bit select, compaction, bucket sort (stable radix sort for ties and
+// crowded buckets).  Returns m = min(k, n); the winners' columns in rank
+// order are sm.wcol[buf][0 .. m).
+template <int NT, int CAP, int KM, int NBK>
+__device__ int topk_sort_cached(Topk32Smem<NT, CAP, KM, NBK> &sm, int n, int lo, int k, uint32_t omin,
+                                uint32_t omax, int &buf)
+{
+    // n <= k: everything wins (mask 0 makes every key a candidate, all taken)
+    uint32_t prefix = 0u, mask = 0u;
+    int need = n, cand = n;
+    if (n > k)
+        select32(sm, n, k, omin, omax, prefix, mask, need, cand);
+    // The bucket sort places each winner by its composite key (order key,
+    // column), so it takes them in any order; when the whole boundary group
+    // wins (no tie at the boundary to break by column) the fast unordered
+    // compaction feeds it.  Equal order keys everywhere, or a bucket sort
+    // that gives up, need the winners in column order (the stable radix
+    // sort keeps it for equal keys): then the stable compaction reruns from
+    // the key cache, which the bucket sort leaves intact.
+    uint32_t wmin, wmax;
+    const bool any_order = cand == need;
+    int m = any_order ? compact32_any(sm, n, lo, prefix, mask, wmin, wmax)
+                      : compact32(sm, n, lo, prefix, mask, need, cand, wmin, wmax);
+    bool sorted = (!any_order || wmin != wmax) && bucket_sort32(sm, m, wmin, wmax);
+    buf = 0;
+    if (!sorted) {
+        if (any_order)
+            m = compact32(sm, n, lo, prefix, mask, need, cand, wmin, wmax);
+        // all keys equal: column order is the rank order already
+        buf = wmin == wmax ? 0 : sort32(sm, m, wmin, wmax);
+    }
+    return m;
+}
+
+// Float value of an order key (inverse of score_order_key; -0 comes back
+// as +0).
+__device__ __forceinline__ float order_key_value(uint32_t o)
+{
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+
+// Value buckets of a row segment (shared by the bucket kernels below): NB
+// buckets linear in the score value over [vmin, vmax], numbered from the top
+// (bucket 0 holds the largest values).  The map is monotonic, so every key
+// of a lower-numbered bucket ranks above every key of a higher-numbered one.
+struct ValueBuckets {
+    float vmin, scale;
+    int nb;
+    __device__ bool init(uint32_t omin, uint32_t omax, int nbuckets)
+    {
+        nb = nbuckets;
+        vmin = order_key_value(omin);
+        const float vmax = order_key_value(omax);
+        scale = (float)nb / (vmax - vmin);
+        return __builtin_isfinite(vmin) && __builtin_isfinite(vmax) &&
+               __builtin_isfinite(scale) && scale > 0.f;
+    }
+    __device__ int operator()(uint32_t ord) const
+    {
+        const int b = (int)((order_key_value(ord) - vmin) * scale);
+        return nb - 1 - min(max(b, 0), nb - 1);
+    }
+};
+
+constexpr int kSegMaxBucket = 256;
+
+// Ranks s0 .. s1-1 (0 <= s0 < s1 <= min(k, n)) of the top-k of the row
+// rp[0 .. n), whose key i is column lo + i: emit(rank, column) is called once
+// for each of them, from whichever thread places it.  Block-wide (all threads
+// call it; it returns with the shared memory free for reuse after a barrier).
+// The row is counted into NB buckets linear in the score value over
+// [min, max] (a monotonic map, so a higher bucket never holds a lower-ranked
+// key); the prefix sums give each bucket's first rank.  Only the buckets that
+// hold ranks s0 .. s1-1 are collected, and each collected key is placed
+// inside its bucket by counting the members with a larger composite key
+// (order key, then smaller column) -- the exact rank order, ties included.
+// Nothing selects, compacts or sorts the whole row.  When the ranks fall into
+// crowded buckets (a score range stretched by outliers) or the value range is
+// not finite, the full sorted top-k of the row is taken instead.
+template <int NT, int CAP, int KM, int NBK, typename Emit>
+__device__ void seg_rank_row(Topk32Smem<NT, CAP, KM, NBK> &sm, const float *__restrict__ rp, int lo,
+                             int n, int k, int s0, int s1, Emit emit)
+{
+    using S = Topk32Smem<NT, CAP, KM, NBK>;
+    constexpr int NB = S::NB, NW = S::NW, PB = NB / NT, R = CAP / NT;
+    static_assert(PB >= 1 && NB % NT == 0, "every thread owns whole buckets");
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int rounds = (n + NT - 1) / NT;  // uniform, at most R
+    // thread t keeps keys r*NT + t (r < rounds) in registers: their order keys
+    // and, below, their buckets (all loads issued before any is used)
+    uint32_t ord[R];
+    {
+        float v[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            v[r] = (r < rounds && r * NT + tid < n) ? rp[r * NT + tid] : 0.f;
+        uint32_t mn = ~0u, mx = 0u;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            ord[r] = score_order_key(v[r]);
+            if (r < rounds && r * NT + tid < n) {
+                mn = min(mn, ord[r]);
+                mx = max(mx, ord[r]);
+            }
+        }
+        mn = wave_min_u32(mn);
+        mx = wave_max_u32(mx);
+        if (lane == 0) {
+            sm.mm[0][wid] = mn;
+            sm.mm[1][wid] = mx;
+        }
+    }
+    for (int i = tid; i < NB; i += NT)
+        sm.bk.fill[i] = 0u;
+    __syncthreads();
+    uint32_t omin = sm.mm[0][0], omax = sm.mm[1][0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+        omin = min(omin, sm.mm[0][w]);
+        omax = max(omax, sm.mm[1][w]);
+    }
+    if (omin == omax) {  // every key equal: column order is the rank order
+        for (int i = s0 + tid; i < s1; i += NT)
+            emit(i, lo + i);
+        return;
+    }
+    ValueBuckets bucket;
+    bool ok = bucket.init(omin, omax, NB);
+    if (ok) {
+        int bk[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            bk[r] = NB;  // none
+            if (r < rounds && r * NT + tid < n) {
+                bk[r] = bucket(ord[r]);
+                atomicAdd(&sm.bk.fill[bk[r]], 1u);
+            }
+        }
+        __syncthreads();
+        // exclusive prefix over the buckets (thread t owns PB consecutive
+        // ones); the buckets holding ranks s0 and s1-1
+        uint32_t v[PB];
+        int sum = 0;
+#pragma unroll
+        for (int j = 0; j < PB; ++j) {
+            v[j] = sm.bk.fill[tid * PB + j];
+            sum += (int)v[j];
+        }
+        const int incl = wave_inclusive_scan(sum);
+        if (lane == 63)
+            sm.tab[0][wid] = incl;
+        __syncthreads();
+        int run = incl - sum;
+#pragma unroll
+        for (int w = 0; w < NW; ++w)
+            run += w < wid ? sm.tab[0][w] : 0;
+        int crowd_lo = 0, crowd_hi = 0;  // sizes of the buckets holding s0 and s1-1
+#pragma unroll
+        for (int j = 0; j < PB; ++j) {
+            const int b = tid * PB + j, c = (int)v[j];
+            sm.bk.off[b] = (uint32_t)run;
+            sm.bk.fill[b] = (uint32_t)run;  // fill pointer of the collection below
+            if (run <= s0 && s0 < run + c) {
+                sm.tab[1][0] = b;
+                crowd_lo = c;
+            }
+            if (run <= s1 - 1 && s1 - 1 < run + c) {
+                sm.tab[1][1] = b;
+                crowd_hi = c;
+            }
+            run += c;
+        }
+        // a bucket strictly between them holds only ranks s0 .. s1-1 (all of
+        // which are placed anyway); the two end buckets can hold many keys
+        // outside them (ties, or a range stretched by an outlier), and
+        // placing a key costs one compare per member of its bucket
+        if (crowd_lo)
+            sm.red[0][0][0] = crowd_lo;
+        if (crowd_hi)
+            sm.red[0][0][1] = crowd_hi;
+        __syncthreads();
+        const int bf = sm.tab[1][0], bl = sm.tab[1][1];
+        const int base = (int)sm.bk.off[bf];
+        const int crowd = max(sm.red[0][0][0], sm.red[0][0][1]);
+        const int total = (bl + 1 < NB ? (int)sm.bk.off[bl + 1] : n) - base;  // keys of bf .. bl
+        // the collection buffer holds k plus the rest of the last bucket
+        constexpr int kCollect = (int)((sizeof(sm.word[1]) + sizeof(sm.wcol)) / 8);
+        ok = crowd <= kSegMaxBucket && total <= kCollect;
+        if (ok) {
+            // the collection from registers (key of rank base + i at ck[i])
+            uint64_t *ck = reinterpret_cast<uint64_t *>(&sm.word[1][0]);
+            static_assert(kCollect >= KM + kSegMaxBucket, "composite key buffer");
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                if (bk[r] >= bf && bk[r] <= bl)
+                    ck[atomicAdd(&sm.bk.fill[bk[r]], 1u) - (uint32_t)base] =
+                        ((uint64_t)ord[r] << 32) |
+                        (uint64_t)(0xffffffffu - (uint32_t)(lo + r * NT + tid));
+            }
+            __syncthreads();
+            // rank of each collected key: its bucket's first rank plus the
+            // members of the bucket above it
+            for (int j = tid; j < total; j += NT) {
+                const uint64_t key = ck[j];
+                const int b = bucket((uint32_t)(key >> 32));
+                const int b0 = (int)sm.bk.off[b] - base, b1 = (int)sm.bk.fill[b] - base;
+                int r = (int)sm.bk.off[b];
+                for (int x = b0; x < b1; ++x)
+                    r += ck[x] > key;
+                if (r >= s0 && r < s1)
+                    emit(r, (int)(0xffffffffu - (uint32_t)key));
+            }
+            return;
+        }
+        __syncthreads();  // the bucket arrays are reused below
+    }
+    // the full sorted top-k of the row, from the key cache
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        if (r < rounds && r * NT + tid < n)
+            sm.a.ord[r * NT + tid] = ord[r];
+    __syncthreads();
+    int buf;
+    topk_sort_cached(sm, n, lo, k, omin, omax, buf);
+    for (int i = s0 + tid; i < s1; i += NT)
+        emit(i, (int)sm.wcol[buf][i]);
 }
 
 } // namespace dsa

@@ -286,8 +286,10 @@ def test_pool_select_rows_of_every_kind(dsa, np_cols, sk, kp):
     """pool_select_kernel on rows that stress the selection: one outlier
     stretching the range, all scores equal, coarse ties, next to plain rows,
     short rows, a row with exactly select_k pools and padded queries; both
-    row capacities (up to 4096 and up to 16384 pools) and select_k above
-    512.  Bit-exact against the oracle."""
+    row capacities (up to 4096 and up to 16384 pools), the lean shared
+    layout for select_k up to 512 and the full one above it, kpool 4 rows
+    with and without 16-byte alignment (four-token stores or single ones).
+    Bit-exact against the oracle."""
     note(f"pool select paths np_cols={np_cols} select_k={sk} kpool={kp}")
     B, n_q = 2, 24
     L = np_cols * kp
