@@ -50,7 +50,9 @@ constexpr int MK_VKEYS = kMaskedVKeys; // keys per block of the V passes
 // query q.  Rows past n_q (up to q_pad) get zero words, so every word of the
 // mask is written.  The group's index rows are one contiguous span of
 // 32 x n_sel entries, read flat (eight coalesced loads in flight per
-// thread); keys are processed MK_WCHUNK words at a time.
+// thread, of four entries each when n_sel is a multiple of 4 and the base
+// is 16-byte aligned: the four then share one row); keys are processed
+// MK_WCHUNK words at a time.
 __global__ __launch_bounds__(256) void topk_to_mask_kernel(const int32_t *__restrict__ idx,
                                                            const int32_t *__restrict__ vlo,
                                                            const int32_t *__restrict__ vhi,
@@ -82,13 +84,49 @@ __global__ __launch_bounds__(256) void topk_to_mask_kernel(const int32_t *__rest
     const int32_t *span = idx + ((int64_t)b * n_q + q0) * n_sel;
     const int total = nrows * n_sel;  // < 2^31: checked on the host
     const float inv_sel = 1.0f / (float)max(n_sel, 1);
+    const bool quad = (n_sel & 3) == 0 && (reinterpret_cast<uintptr_t>(idx) & 15) == 0;
+    // row of entry e: a float estimate, corrected by one step
+    auto row_of = [&](int e) {
+        int r = (int)((float)e * inv_sel);
+        r -= r * n_sel > e;
+        r += (r + 1) * n_sel <= e;
+        return r;
+    };
     for (int w0 = 0; w0 < nw; w0 += MK_WCHUNK) {
         const int wn = min(MK_WCHUNK, nw - w0);
         for (int i = tid; i < MK_ROWS * (MK_WCHUNK + 1); i += 256)
             (&bits[0][0])[i] = 0u;
         __syncthreads();
         const int c_lo = w0 * 32, c_hi = (w0 + wn) * 32;
-        for (int e0 = 0; e0 < total; e0 += 256 * U) {
+        auto set = [&](int r, int j, int jl, int jh) {
+            if (j >= jl && j < jh)
+                atomicOr(&bits[r][(j >> 5) - w0], 1u << (j & 31));
+        };
+        if (quad) {
+            const int4 *span4 = reinterpret_cast<const int4 *>(span);
+            const int total4 = total >> 2;
+            for (int e0 = 0; e0 < total4; e0 += 256 * U) {
+                int4 v[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int e = e0 + u * 256 + tid;
+                    v[u] = e < total4 ? span4[e] : make_int4(-1, -1, -1, -1);
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int e = e0 + u * 256 + tid;
+                    if (e >= total4)
+                        continue;
+                    const int r = row_of(4 * e);
+                    const int jl = max(rlo[r], c_lo), jh = min(rhi[r], c_hi);
+                    set(r, v[u].x, jl, jh);
+                    set(r, v[u].y, jl, jh);
+                    set(r, v[u].z, jl, jh);
+                    set(r, v[u].w, jl, jh);
+                }
+            }
+        }
+        for (int e0 = 0; !quad && e0 < total; e0 += 256 * U) {
             int v[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
@@ -100,13 +138,8 @@ __global__ __launch_bounds__(256) void topk_to_mask_kernel(const int32_t *__rest
                 const int e = e0 + u * 256 + tid;
                 if (e >= total)
                     continue;
-                // row of entry e: a float estimate, corrected by one step
-                int r = (int)((float)e * inv_sel);
-                r -= r * n_sel > e;
-                r += (r + 1) * n_sel <= e;
-                const int j = v[u];
-                if (j >= max(rlo[r], c_lo) && j < min(rhi[r], c_hi))
-                    atomicOr(&bits[r][(j >> 5) - w0], 1u << (j & 31));
+                const int r = row_of(e);
+                set(r, v[u], max(rlo[r], c_lo), min(rhi[r], c_hi));
             }
         }
         __syncthreads();

@@ -537,15 +537,19 @@ def test_masked_attend_pooled_selection(dsa, L, sk, variant):
             assert torch.all(out[b, :p] == 0) and torch.all(torch.isneginf(lse[b, :p]))
 
 
-def test_masked_attend_set_semantics(dsa):
-    note("masked attend: duplicates / INVALID / out-of-range, no visibility ranges")
+@pytest.mark.parametrize("n_sel", [40, 37])
+def test_masked_attend_set_semantics(dsa, n_sel):
+    """Duplicates, INVALID and out-of-range entries; index rows of 40
+    entries (the mask kernel reads four per load) and of 37 (one per load)."""
+    note(f"masked attend: duplicates / INVALID / out-of-range, no visibility ranges, n_sel={n_sel}")
     gen = torch.Generator(device="cuda").manual_seed(13)
     B, T, H, kd, vd = 2, 150, 8, 192, 256
     q = (torch.randn(B, T, H, kd, generator=gen, device="cuda") / kd ** 0.5).bfloat16()
     K = (torch.randn(B, T, H, kd, generator=gen, device="cuda") / kd ** 0.5).bfloat16()
     V = (torch.randn(B, T, H, vd, generator=gen, device="cuda") / vd ** 0.5).bfloat16()
-    sel = np.random.default_rng(4).integers(-2, T + 9, (B, T, 40)).astype(np.int32)
-    sel[:, :, 20:] = sel[:, :, :20]
+    sel = np.random.default_rng(4).integers(-2, T + 9, (B, T, n_sel)).astype(np.int32)
+    half = n_sel // 2
+    sel[:, :, half:2 * half] = sel[:, :, :half]
     sel[0, 3, :] = INV
     idx = torch.tensor(sel, device="cuda")
     out, lse = dsa.sparse_attend(q, K, V, idx, kd ** -0.5, H)
