@@ -85,7 +85,7 @@ STAGE_KERNELS = {
                "attend_heads_gather_kernel", "attend_plain_kernel"),
     "frontend": ("pj_rope_q_kernel", "pj_norm_k_kernel"),
     "expand_kv": ("pj_expand_kv_kernel",),
-    "pool_keys": ("pool_keys_kernel", "pool_counts_kernel"),
+    "pool_keys": ("pool_keys_kernel", "pool_keys_vec_kernel", "pool_counts_kernel"),
     "pool_select": ("pool_select_kernel",),
 }
 

@@ -188,5 +188,9 @@ struct PoolSelectArgs {
 };
 constexpr int kPoolSelectMaxPools = 16384;
 hipError_t launch_pool_select(const PoolSelectArgs &a, hipStream_t st);
+// Blocks per row of the segmented top-k kernels: enough for about 256 blocks
+// in all, at most max_parts, segments of at least 64 ranks; 1 = one block
+// per row.
+int topk_seg_parts(int rows, int k, int max_parts);
 
 } // namespace dsa

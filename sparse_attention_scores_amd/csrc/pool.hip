@@ -104,6 +104,72 @@ __global__ void pool_keys_kernel(const T *__restrict__ k, const T *__restrict__ 
     pk_store(pooled, e, num / den);
 }
 
+// The same per channel, V = 16 / sizeof(T) channels per thread, each slot
+// row read as one 16-byte load per thread (D a multiple of V, 16-byte
+// aligned rows); the arithmetic per channel is that of pool_keys_kernel.
+template <typename T>
+__global__ void pool_keys_vec_kernel(const T *__restrict__ k, const T *__restrict__ gate,
+                                     const int32_t *__restrict__ pad, T *__restrict__ pooled,
+                                     int32_t *__restrict__ n_pools, int seq, int kpool, int D,
+                                     int np_max, int64_t total)
+{
+    constexpr int V = 16 / (int)sizeof(T);
+    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= total)
+        return;
+    const int dv = D / V;
+    const int cv = (int)(e % dv);
+    const int64_t bi = e / dv;
+    const int i = (int)(bi % np_max);
+    const int b = (int)(bi / np_max);
+    const int p = pad[b];
+    const int np = seq > p ? (seq - p) / kpool : 0;
+    if (i == 0 && cv == 0)
+        n_pools[b] = np;
+    u32x4_t *dst = reinterpret_cast<u32x4_t *>(pooled + bi * D) + cv;
+    if (i >= np) {
+        *dst = u32x4_t{0u, 0u, 0u, 0u};
+        return;
+    }
+    const int64_t base = ((int64_t)b * seq + p + (int64_t)i * kpool) * D + (int64_t)cv * V;
+    auto row = [&](const T *src, int j, float (&x)[V]) {
+        const u32x4_t r = *reinterpret_cast<const u32x4_t *>(src + base + (int64_t)j * D);
+        const T *t = reinterpret_cast<const T *>(&r);
+#pragma unroll
+        for (int c = 0; c < V; ++c)
+            x[c] = pk_load(t, c);
+    };
+    float m[V], x[V], y[V], num[V], den[V];
+#pragma unroll
+    for (int c = 0; c < V; ++c) {
+        m[c] = -INFINITY;
+        num[c] = 0.f;
+        den[c] = 0.f;
+    }
+    for (int j = 0; j < kpool; ++j) {
+        row(gate, j, x);
+#pragma unroll
+        for (int c = 0; c < V; ++c)
+            m[c] = fmaxf(m[c], x[c]);
+    }
+    for (int j = 0; j < kpool; ++j) {
+        row(gate, j, x);
+        row(k, j, y);
+#pragma unroll
+        for (int c = 0; c < V; ++c) {
+            const float ej = expf(x[c] - m[c]);
+            num[c] = fmaf(ej, y[c], num[c]);
+            den[c] += ej;
+        }
+    }
+    u32x4_t o;
+    T *ot = reinterpret_cast<T *>(&o);
+#pragma unroll
+    for (int c = 0; c < V; ++c)
+        pk_store(ot, c, num[c] / den[c]);
+    *dst = o;
+}
+
 __global__ void pool_counts_kernel(const int32_t *__restrict__ pad, int32_t *__restrict__ n_pools,
                                    int seq, int kpool, int batch)
 {
@@ -120,6 +186,26 @@ hipError_t launch_pool_keys(const PoolKeysArgs &a, hipStream_t st)
         // no pool rows at all: only the (zero) counts
         hipLaunchKernelGGL(pool_counts_kernel, dim3((a.batch + 255) / 256), dim3(256), 0, st,
                            a.pad, a.n_pools, a.seq, a.kpool, a.batch);
+        return hipGetLastError();
+    }
+    const int V = a.f32 ? 4 : 8;  // channels per 16-byte load
+    const bool vec = a.head_dim % V == 0 &&
+                     ((reinterpret_cast<uintptr_t>(a.k) | reinterpret_cast<uintptr_t>(a.gate) |
+                       reinterpret_cast<uintptr_t>(a.pooled)) & 15) == 0;
+    if (vec) {
+        const int64_t tv = total / (int64_t)V;
+        const unsigned vb = (unsigned)((tv + 255) / 256);
+        if (a.f32)
+            hipLaunchKernelGGL(pool_keys_vec_kernel<float>, dim3(vb), dim3(256), 0, st,
+                               static_cast<const float *>(a.k), static_cast<const float *>(a.gate),
+                               a.pad, static_cast<float *>(a.pooled), a.n_pools, a.seq, a.kpool,
+                               a.head_dim, np_max, tv);
+        else
+            hipLaunchKernelGGL(pool_keys_vec_kernel<uint16_t>, dim3(vb), dim3(256), 0, st,
+                               static_cast<const uint16_t *>(a.k),
+                               static_cast<const uint16_t *>(a.gate), a.pad,
+                               static_cast<uint16_t *>(a.pooled), a.n_pools, a.seq, a.kpool,
+                               a.head_dim, np_max, tv);
         return hipGetLastError();
     }
     const unsigned blocks = (unsigned)((total + 255) / 256);
@@ -141,19 +227,22 @@ hipError_t launch_pool_keys(const PoolKeysArgs &a, hipStream_t st)
 // topk_pools + expand_selection ("Module glm5next_dsa_ref"): the top
 // select_k visible pools of each query in rank order (higher pooled score,
 // then smaller pool id), each expanded to its kpool token ids ascending, then
-// the visible tail, then INVALID to out_width.  One block per query row; the
-// pools are ranked with value buckets (seg_rank_row), and each ranked pool
-// writes its own kpool tokens, so the selection is never sorted as a list.
+// the visible tail, then INVALID to out_width.  `parts` blocks per query row
+// (one when there are many rows), block `seg` placing ranks
+// [seg*seg_len, seg*seg_len + seg_len); the pools are ranked with value
+// buckets (seg_rank_row), and each ranked pool writes its own kpool token
+// ids, so the selection is never sorted as a list.
 template <int NT, int CAP, int KM, int NBK>
 __global__ __launch_bounds__(NT) void pool_select_kernel(
     const float *__restrict__ scores, const int32_t *__restrict__ pad,
     const int32_t *__restrict__ q_pos, int32_t *__restrict__ out_tok,
     int32_t *__restrict__ out_pools, int n_q, int np_cols, int kpool, int select_k,
-    int out_width)
+    int out_width, int parts, int seg_len)
 {
     __shared__ Topk32Smem<NT, CAP, KM, NBK> sm;
     const int tid = threadIdx.x;
-    const int row = blockIdx.x;
+    const int row = blockIdx.x / parts;
+    const int seg = blockIdx.x - row * parts;
     const int b = row / n_q;
     const int p = pad[b];
     const int t = q_pos[row];
@@ -163,8 +252,9 @@ __global__ __launch_bounds__(NT) void pool_select_kernel(
     int32_t *op = out_pools ? out_pools + (int64_t)row * select_k : nullptr;
     // four tokens per pool as one 16-byte store where the row allows it
     const bool quad = kpool == 4 && (reinterpret_cast<uintptr_t>(o) & 15) == 0;
-    if (m > 0)
-        seg_rank_row(sm, scores + (int64_t)row * np_cols, 0, n_full, select_k, 0, m,
+    const int p0 = seg * seg_len, p1 = min(p0 + seg_len, select_k);
+    if (p0 < min(p1, m))
+        seg_rank_row(sm, scores + (int64_t)row * np_cols, 0, n_full, select_k, p0, min(p1, m),
                      [&](int r, int pool) {
                          const int tok = p + pool * kpool;
                          if (quad) {
@@ -177,24 +267,30 @@ __global__ __launch_bounds__(NT) void pool_select_kernel(
                          if (op)
                              op[r] = pool;
                      });
-    // the visible tail after the pools' tokens, then INVALID
+    // the visible tail after the pools' tokens, then INVALID (the row's
+    // blocks share these positions)
     const int pool_toks = m * kpool;
     const int tail = t >= p ? (t + 1) - (p + n_full * kpool) : 0;
-    for (int i = pool_toks + tid; i < out_width; i += NT)
+    for (int i = pool_toks + seg * NT + tid; i < out_width; i += parts * NT)
         o[i] = i < pool_toks + tail ? p + n_full * kpool + (i - pool_toks) : -1;
     if (op)
-        for (int i = m + tid; i < select_k; i += NT)
+        for (int i = max(p0, m) + tid; i < p1; i += NT)
             op[i] = -1;
 }
 
 hipError_t launch_pool_select(const PoolSelectArgs &a, hipStream_t st)
 {
     const int np_cols = a.seq / a.kpool;
-    const unsigned rows = (unsigned)(a.batch * a.n_q);
+    const int rows = a.batch * a.n_q;
+    // few rows (decode): several blocks per row, each placing a segment of
+    // the ranks, so that the launch still spreads over the chip
+    const int parts = topk_seg_parts(rows, a.select_k, 16);
+    const int seg_len = (a.select_k + parts - 1) / parts;
+    const unsigned blocks = (unsigned)((int64_t)rows * parts);
 #define DSA_POOL_SELECT(NT, CAP, KM, NBK)                                                         \
-    hipLaunchKernelGGL((pool_select_kernel<NT, CAP, KM, NBK>), dim3(rows), dim3(NT), 0, st,        \
+    hipLaunchKernelGGL((pool_select_kernel<NT, CAP, KM, NBK>), dim3(blocks), dim3(NT), 0, st,      \
                        a.scores, a.pad, a.q_pos, a.out_tok, a.out_pools, a.n_q, np_cols, a.kpool,  \
-                       a.select_k, a.out_width)
+                       a.select_k, a.out_width, parts, seg_len)
     static_assert(kPoolSelectMaxPools <= 16384, "one block caches a row of pools");
     // up to 512 pools selected: winner arrays for 512 and 1024 buckets take
     // 33 KB of LDS, so four blocks share a CU instead of two

@@ -970,9 +970,6 @@ constexpr int kCapLarge = kTopkChunkKeys;
 static_assert(kTopkMaxK == kTopkMaxSelect, "one largest k for the host and the kernels");
 constexpr int kCapSmall = 4096;
 
-// Blocks per row for the segmented kernels: enough for about 256 blocks in
-// all, at most max_parts, and segments of at least 64 ranks; 1 = one block
-// per row.
 int topk_seg_parts(int rows, int k, int max_parts)
 {
     int parts = (256 + rows - 1) / rows;

@@ -7,8 +7,11 @@ reach the rest of what the ABI accepts:
   * index_scores_mfma_kernel (8-15 queries per sequence; fp8 keys with 8 or
     more queries; 64 indexer heads; head_dim 64, bf16 and fp8) and the decode
     kernel at 64 heads / head_dim 64;
-  * pool_keys_kernel on f32 keys, and pool_counts_kernel (sequences shorter
-    than one pool);
+  * pool_keys_kernel (one channel per thread: widths that 16-byte loads do
+    not divide) and pool_keys_vec_kernel<float>, and pool_counts_kernel
+    (sequences shorter than one pool);
+  * pool_select_kernel in both shared layouts and both row capacities, with
+    several blocks per row when there are few rows;
   * attend_gather_kernel's set-bitmap path (more than 2048 entries per row)
     at the largest n_k the gather kernel takes (262144);
   * topk_merge_kernel with the candidates in LDS (one block per row: 256 or
@@ -24,7 +27,7 @@ import torch
 
 import oracle
 from sparse_attention_scores_amd import workloads as W
-from tests.parity import check_attend, check_scores, cpu, note
+from tests.parity import bf16_ulp_ok, check_attend, check_scores, cpu, note
 
 pytestmark = pytest.mark.gpu
 
@@ -318,19 +321,43 @@ def test_pool_select_rows_of_every_kind(dsa, np_cols, sk, kp):
     assert np.array_equal(cpu(pools).numpy().reshape(rpools.shape), rpools)
 
 
+# ---------------------------------------------------------------- pool keys, bf16 rows of any width
+
+def test_pool_keys_bf16_one_channel_per_thread(dsa):
+    """bf16 keys whose width (36) is not a multiple of 8 take one channel per
+    thread (pool_keys_kernel<uint16_t>); 128-wide ones take eight
+    (pool_keys_vec_kernel, config 5 and 6).  Each value within one bf16 ulp
+    plus 2^-20 mag of the f64 oracle, as for config 5."""
+    note("pool keys bf16 d=36")
+    gen = torch.Generator(device="cuda").manual_seed(36)
+    B, L, d, kp = 2, 401, 36, 4
+    k = torch.randn(B, L, d, generator=gen, device="cuda").bfloat16()
+    gate = (torch.randn(B, L, d, generator=gen, device="cuda") * 2).bfloat16()
+    pad = torch.tensor([0, 9], dtype=torch.int32, device="cuda")
+    pk, npools = dsa.pool_keys(k, gate, pad, kp)
+    torch.cuda.synchronize()
+    ref, rn, mag = oracle.pool_keys(cpu(k), cpu(gate), cpu(pad), kp, want_mag=True)
+    assert cpu(npools).tolist() == rn.tolist()
+    for b, n in enumerate(rn):
+        bf16_ulp_ok(cpu(pk[b, :n]), ref[b, :n], mag[b, :n], "pool keys d=36")
+        assert torch.all(pk[b, n:] == 0)
+
+
 # ---------------------------------------------------------------- pool keys on f32, short sequences
 
-@pytest.mark.parametrize("L,kp", [(1030, 4), (515, 8), (3, 4)])
-def test_pool_keys_f32_and_sequences_shorter_than_a_pool(dsa, L, kp):
-    """f32 keys and gates (pool_keys_kernel<float>), and L < kpool, where no
-    pool exists and only the counts are written (pool_counts_kernel).
+@pytest.mark.parametrize("L,kp,d", [(1030, 4, 128), (515, 8, 128), (3, 4, 128), (1030, 4, 6)])
+def test_pool_keys_f32_and_sequences_shorter_than_a_pool(dsa, L, kp, d):
+    """f32 keys and gates: four channels per thread (pool_keys_vec_kernel
+    <float>, d a multiple of 4) and one (pool_keys_kernel<float>, d = 6); and
+    L < kpool, where no pool exists and only the counts are written
+    (pool_counts_kernel).
     Criterion: each pooled value within 2 (kpool + 4) 2^-24 mag + 2^-23 |ref|
     of the f64 oracle, mag = sum_j softmax_j |k_j|: the kernel forms kpool
     exponentials (two ulps each), two sums of kpool terms and one quotient in
     f32, a factor 2 over those rounding steps."""
-    note(f"pool keys f32 L={L} kpool={kp}")
-    gen = torch.Generator(device="cuda").manual_seed(L * 7 + kp)
-    B, d = 3, 128
+    note(f"pool keys f32 L={L} kpool={kp} d={d}")
+    gen = torch.Generator(device="cuda").manual_seed(L * 7 + kp + d)
+    B = 3
     k = torch.randn(B, L, d, generator=gen, device="cuda")
     gate = torch.randn(B, L, d, generator=gen, device="cuda") * 3
     pad = torch.tensor([0, min(1, L), min(13, L)], dtype=torch.int32, device="cuda")
