@@ -287,7 +287,8 @@ def test_every_output_written_tiny_f32(dsa):
                                            (6000, 512, 4)])
 def test_pool_select_rows_of_every_kind(dsa, np_cols, sk, kp):
     """pool_select_kernel on rows that stress the selection: one outlier
-    stretching the range, all scores equal, coarse ties, next to plain rows,
+    stretching the range, all scores equal, coarse ties, infinite scores
+    (which send the row to the full sort), next to plain rows,
     short rows, a row with exactly select_k pools and padded queries; both
     row capacities (up to 4096 and up to 16384 pools), the lean shared
     layout for select_k up to 512 and the full one above it, kpool 4 rows
@@ -303,6 +304,9 @@ def test_pool_select_rows_of_every_kind(dsa, np_cols, sk, kp):
     S[:, 3, 7] = 1e30                                 # one outlier
     S[:, 4] = torch.round(S[:, 4] * 50) / 50
     S[:, 4, 0] = -1e30
+    S[:, 8, 5] = float("inf")                         # two tied +inf, then finite
+    S[:, 8, 9] = float("inf")
+    S[:, 9, ::3] = float("-inf")                      # a third of the row -inf
     pad = torch.tensor([0, 37], dtype=torch.int32, device="cuda")
     qp = torch.full((B, n_q), L - 1, dtype=torch.int32, device="cuda")
     qp[:, 5] = torch.tensor([3, 36], dtype=torch.int32)          # padded / before any pool
