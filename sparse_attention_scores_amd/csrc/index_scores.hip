@@ -367,11 +367,13 @@ static_assert(IP_TILEB == 1024 * IP_NW, "one DMA instruction per wave per tile")
 // i-th earliest with the i-th latest) and each pair's visible tiles, the
 // later block's first, are split evenly between two workgroups; a
 // workgroup reloads the queries when its share moves on to the earlier
-// block.
+// block.  With many query blocks per CU (`paired` false) each workgroup
+// takes one query block whole, the latest first, and loads its queries
+// once.
 __global__ __launch_bounds__(64 * IP_NW) void index_scores_prefill_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kv, const float *__restrict__ w,
     const int32_t *__restrict__ vlo, const int32_t *__restrict__ vhi, float *__restrict__ scores,
-    int n_q, int n_k, float scale, int n_qblocks, int n_chunks, int chunk)
+    int n_q, int n_k, float scale, int n_qblocks, int n_chunks, int chunk, bool paired)
 {
     constexpr int KS = IP_D / 16;
     __shared__ __attribute__((aligned(16))) unsigned char tiles[IP_STAGES][IP_TILEB];
@@ -379,15 +381,17 @@ __global__ __launch_bounds__(64 * IP_NW) void index_scores_prefill_kernel(
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int g = lane >> 5, col = lane & 31;
-    const int n_pairs = (n_qblocks + 1) / 2;
+    const int n_units = paired ? (n_qblocks + 1) / 2 : n_qblocks;
     int bid = blockIdx.x;
-    const int half = bid & 1;
-    bid >>= 1;
+    const int half = paired ? bid & 1 : 0;
+    if (paired)
+        bid >>= 1;
     const int kc = bid % n_chunks;
     bid /= n_chunks;
-    const int pair = bid % n_pairs;
-    const int b = bid / n_pairs;
-    const int qb_late = n_qblocks - 1 - pair, qb_early = pair;  // equal for a middle block
+    const int unit = bid % n_units;
+    const int b = bid / n_units;
+    // a pair (equal for a middle block), or one block
+    const int qb_late = n_qblocks - 1 - unit, qb_early = paired ? unit : qb_late;
 
     const int c0 = kc * chunk;
     const int c1 = min(c0 + chunk, n_k);
@@ -419,7 +423,7 @@ __global__ __launch_bounds__(64 * IP_NW) void index_scores_prefill_kernel(
         visible_tiles(qb_early, ea, eb);
     // the pair's visible tiles, the later block's first, split in two halves
     const int n_late = lb - la, n_all = n_late + (eb - ea);
-    const int cut = (n_all + 1) / 2;
+    const int cut = paired ? (n_all + 1) / 2 : n_all;
     const int w0 = half ? cut : 0, w1 = half ? n_all : cut;
 
     // DMA: wave w fills LDS bytes w*1024 + 16*lane of the tile = row r, physical
@@ -454,7 +458,7 @@ __global__ __launch_bounds__(64 * IP_NW) void index_scores_prefill_kernel(
             const int rb[2] = {min(c1, c0 + 32 * ta), c1};
 #pragma unroll
             for (int r = 0; r < 2; ++r) {
-                const int mid = ra[r] + ((rb[r] - ra[r]) / 2 & ~3);
+                const int mid = paired ? ra[r] + ((rb[r] - ra[r]) / 2 & ~3) : rb[r];
                 const int a = half ? mid : ra[r], e = half ? rb[r] : mid;
                 if (a >= e)
                     continue;
@@ -709,14 +713,17 @@ static hipError_t launch_mfma_mode(const IndexArgs &a, hipStream_t st)
         const int n_qblocks = (a.n_q + IP_QB - 1) / IP_QB;
         const int chunk = 4096;
         const int n_chunks = (a.n_k + chunk - 1) / chunk;
-        // two workgroups per pair of query blocks (see the kernel)
-        const int64_t blocks = (int64_t)a.batch * ((n_qblocks + 1) / 2) * n_chunks * 2;
+        // two workgroups per pair of query blocks, or one per query block
+        // when there are at least eight per CU (see the kernel)
+        const bool paired = (int64_t)a.batch * n_qblocks * n_chunks < 8 * 256;
+        const int64_t blocks = paired ? (int64_t)a.batch * ((n_qblocks + 1) / 2) * n_chunks * 2
+                                      : (int64_t)a.batch * n_qblocks * n_chunks;
         if (blocks > 0x7fffffff)
             return hipErrorInvalidConfiguration;
         hipLaunchKernelGGL(index_scores_prefill_kernel, dim3((unsigned)blocks), dim3(64 * IP_NW), 0,
                            st, static_cast<const uint16_t *>(a.q),
                            static_cast<const uint16_t *>(a.k), a.w, a.vis_lo, a.vis_hi, a.scores,
-                           a.n_q, a.n_k, a.scale, n_qblocks, n_chunks, chunk);
+                           a.n_q, a.n_k, a.scale, n_qblocks, n_chunks, chunk, paired);
         return hipGetLastError();
     }
     if (a.n_q >= 8)

@@ -6,7 +6,8 @@ reach the rest of what the ABI accepts:
 
   * index_scores_mfma_kernel (8-15 queries per sequence; fp8 keys with 8 or
     more queries; 64 indexer heads; head_dim 64, bf16 and fp8) and the decode
-    kernel at 64 heads / head_dim 64;
+    kernel at 64 heads / head_dim 64; the prefill kernel with one workgroup
+    per query block (many query blocks per CU);
   * pool_keys_kernel (one channel per thread: widths that 16-byte loads do
     not divide) and pool_keys_vec_kernel<float>, and pool_counts_kernel
     (sequences shorter than one pool);
@@ -323,6 +324,38 @@ def test_pool_select_rows_of_every_kind(dsa, np_cols, sk, kp):
     bad = np.nonzero((got != rtok).any(1))[0]
     assert bad.size == 0, f"rows differ: {bad[:8]}"
     assert np.array_equal(cpu(pools).numpy().reshape(rpools.shape), rpools)
+
+
+# ---------------------------------------------------------------- prefill indexer, whole query blocks
+
+def test_prefill_index_one_workgroup_per_query_block(dsa):
+    """index_scores_prefill_kernel with one workgroup per query block, the
+    mode it takes with eight or more query blocks per CU: 8 sequences x 4100
+    causal queries over 4100 keys (a ragged last query block; two key
+    chunks, the second of 4 keys), left pads from 0 to the whole sequence.
+    Every output element is written; sampled rows within the scores'
+    criterion of the oracle."""
+    note("prefill indexer, one workgroup per query block (8 x 4100)")
+    gen = torch.Generator(device="cuda").manual_seed(4100)
+    B, T, H, d = 8, 4100, 32, 128
+    q = (torch.randn(B, T, H, d, generator=gen, device="cuda") / d ** 0.5).bfloat16()
+    k = (torch.randn(B, T, d, generator=gen, device="cuda") / d ** 0.5).bfloat16()
+    w = torch.rand(B, T, H, generator=gen, device="cuda")
+    pad = torch.tensor([0, 1, 17, 33, 64, 100, 4095, 4100], dtype=torch.int32, device="cuda")
+    q_pos = torch.arange(T, dtype=torch.int32, device="cuda").expand(B, T).contiguous()
+    lo, hi = dsa.visibility_ranges(pad, q_pos)
+    S = _nan_like((B, T, T))
+    dsa.index_scores(q, k, w, lo, hi, d ** -0.5, out=S)
+    torch.cuda.synchronize()
+    assert not torch.isnan(S).any()
+    rng = np.random.default_rng(41)
+    must = [b * T + t for b in range(B) for t in (0, 15, 16, 4095, 4096, T - 1)]
+    rows = np.array(sorted(set(must) | set(rng.choice(B * T, 120, replace=False).tolist())),
+                    np.int64)
+    ref, A = oracle.index_scores(cpu(q), cpu(k), cpu(w), d ** -0.5, cpu(q_pos), cpu(pad),
+                                 rows=rows, want_mag=True)
+    got = cpu(S.reshape(B * T, T)[torch.tensor(rows, device="cuda")]).numpy()
+    check_scores(got, ref, A, 1e-3, "prefill indexer, whole query blocks")
 
 
 # ---------------------------------------------------------------- pool keys, bf16 rows of any width
