@@ -4,7 +4,10 @@ configuration bench.py times (the tests drive bench.py's own step objects).
 The oracle recomputes a seeded sample of rows one by one: scores on sampled
 query rows, top-k / pool select on every row (cheap), attention on sampled
 rows fed the selection the GPU produced -- which equals the oracle's own
-top-k of the GPU scores, checked bit for bit first."""
+top-k of the GPU scores, checked bit for bit first.  Sample sizes: every
+row of the decode configurations; 512 score rows and 256 attention rows
+per sequence for the prefill and pooled ones, always with the first valid
+row, the last, and the rows around where the selection starts to bite."""
 import numpy as np
 import pytest
 import torch
@@ -33,7 +36,7 @@ def _sample(n_rows, n, seed, must=()):
     return np.array(sorted(pick), np.int64)
 
 
-@pytest.mark.parametrize("cfg,score_rows,attend_rows", [(2, 32, 8), (3, 40, 16), (4, 2, 8)])
+@pytest.mark.parametrize("cfg,score_rows,attend_rows", [(2, 32, 32), (3, 512, 256), (4, 8, 8)])
 def test_fullsize_absorbed_step(dsa, cfg, score_rows, attend_rows):
     note(f"full-size step, config {cfg}")
     inp = W.make(cfg, device="cuda")
@@ -110,7 +113,7 @@ def test_fullsize_pooled_step(dsa):
     bf16_ulp_ok(cpu(step.pk), pk_ref, mag, "config 5 pool keys")
     # -- pooled scores on sampled rows (the GPU's pooled keys as the input)
     must = [0, L - 1, 2 * L + 36, 2 * L + 37, 3 * L + 63, 3 * L + 64, 4 * L - 1]
-    rows = _sample(n_rows, 32, 105, must)
+    rows = _sample(n_rows, 512 * B, 105, must)
     note(f"  oracle pooled scores on {len(rows)} rows")
     ref, A = oracle.index_scores(cpu(inp["q_idx"]), cpu(step.pk), cpu(inp["w"]),
                                  inp["scale_idx"], cpu(inp["q_pos"]), pads, kpool=kp, rows=rows,
@@ -127,9 +130,14 @@ def test_fullsize_pooled_step(dsa):
     tok = cpu(step.tok).numpy().reshape(n_rows, -1)
     bad = np.nonzero((tok != tok_ref).any(1))[0]
     assert bad.size == 0, f"pool select rows differ: {bad[:8]}"
-    # -- per-head attention on sampled rows of two sequences
-    for b in (1, 3):
-        rows_b = _sample(L, 6, 300 + b, [0, int(pads[b]), L - 1])
+    # -- per-head attention on sampled rows of every sequence: the first
+    # rows, the first valid one, both sides of a 256-query block boundary,
+    # where the selection starts to bite, and the last row
+    for b in range(B):
+        p = int(pads[b])
+        bite = p + kp * inp["select_k"]  # the first position with more pools than select_k
+        must_b = [0, p, p + 1, 255, 256, bite - 1, bite + kp - 1, L - 1]
+        rows_b = _sample(L, 256, 300 + b, must_b)
         note(f"  oracle attention, sequence {b}, {len(rows_b)} rows")
         sl = slice(b, b + 1)
         out_ref, lse_ref = oracle.sparse_attend(
