@@ -107,7 +107,10 @@ __global__ void pool_keys_kernel(const T *__restrict__ k, const T *__restrict__ 
 // The same per channel, V = 16 / sizeof(T) channels per thread, each slot
 // row read as one 16-byte load per thread (D a multiple of V, 16-byte
 // aligned rows); the arithmetic per channel is that of pool_keys_kernel.
-template <typename T>
+// With KR > 0 and kpool <= KR the pool's k and gate rows are all loaded
+// before any is used and held in registers; otherwise they are read slot by
+// slot (the gate rows twice).
+template <typename T, int KR>
 __global__ void pool_keys_vec_kernel(const T *__restrict__ k, const T *__restrict__ gate,
                                      const int32_t *__restrict__ pad, T *__restrict__ pooled,
                                      int32_t *__restrict__ n_pools, int seq, int kpool, int D,
@@ -146,20 +149,59 @@ __global__ void pool_keys_vec_kernel(const T *__restrict__ k, const T *__restric
         num[c] = 0.f;
         den[c] = 0.f;
     }
-    for (int j = 0; j < kpool; ++j) {
-        row(gate, j, x);
+    if constexpr (KR > 0) {
+        u32x4_t gr[KR], kr[KR];
 #pragma unroll
-        for (int c = 0; c < V; ++c)
-            m[c] = fmaxf(m[c], x[c]);
-    }
-    for (int j = 0; j < kpool; ++j) {
-        row(gate, j, x);
-        row(k, j, y);
+        for (int j = 0; j < KR; ++j) {
+            if (j < kpool) {
+                gr[j] = *reinterpret_cast<const u32x4_t *>(gate + base + (int64_t)j * D);
+                kr[j] = *reinterpret_cast<const u32x4_t *>(k + base + (int64_t)j * D);
+            }
+        }
+        auto unpack = [&](const u32x4_t &r, float(&xo)[V]) {
+            const T *t = reinterpret_cast<const T *>(&r);
 #pragma unroll
-        for (int c = 0; c < V; ++c) {
-            const float ej = expf(x[c] - m[c]);
-            num[c] = fmaf(ej, y[c], num[c]);
-            den[c] += ej;
+            for (int c = 0; c < V; ++c)
+                xo[c] = pk_load(t, c);
+        };
+#pragma unroll
+        for (int j = 0; j < KR; ++j) {
+            if (j < kpool) {
+                unpack(gr[j], x);
+#pragma unroll
+                for (int c = 0; c < V; ++c)
+                    m[c] = fmaxf(m[c], x[c]);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < KR; ++j) {
+            if (j < kpool) {
+                unpack(gr[j], x);
+                unpack(kr[j], y);
+#pragma unroll
+                for (int c = 0; c < V; ++c) {
+                    const float ej = expf(x[c] - m[c]);
+                    num[c] = fmaf(ej, y[c], num[c]);
+                    den[c] += ej;
+                }
+            }
+        }
+    } else {
+        for (int j = 0; j < kpool; ++j) {
+            row(gate, j, x);
+#pragma unroll
+            for (int c = 0; c < V; ++c)
+                m[c] = fmaxf(m[c], x[c]);
+        }
+        for (int j = 0; j < kpool; ++j) {
+            row(gate, j, x);
+            row(k, j, y);
+#pragma unroll
+            for (int c = 0; c < V; ++c) {
+                const float ej = expf(x[c] - m[c]);
+                num[c] = fmaf(ej, y[c], num[c]);
+                den[c] += ej;
+            }
         }
     }
     u32x4_t o;
@@ -195,17 +237,24 @@ hipError_t launch_pool_keys(const PoolKeysArgs &a, hipStream_t st)
     if (vec) {
         const int64_t tv = total / (int64_t)V;
         const unsigned vb = (unsigned)((tv + 255) / 256);
-        if (a.f32)
-            hipLaunchKernelGGL(pool_keys_vec_kernel<float>, dim3(vb), dim3(256), 0, st,
-                               static_cast<const float *>(a.k), static_cast<const float *>(a.gate),
-                               a.pad, static_cast<float *>(a.pooled), a.n_pools, a.seq, a.kpool,
-                               a.head_dim, np_max, tv);
-        else
-            hipLaunchKernelGGL(pool_keys_vec_kernel<uint16_t>, dim3(vb), dim3(256), 0, st,
-                               static_cast<const uint16_t *>(a.k),
-                               static_cast<const uint16_t *>(a.gate), a.pad,
-                               static_cast<uint16_t *>(a.pooled), a.n_pools, a.seq, a.kpool,
-                               a.head_dim, np_max, tv);
+#define DSA_POOL_KEYS_VEC(T, KR)                                                                   \
+    hipLaunchKernelGGL((pool_keys_vec_kernel<T, KR>), dim3(vb), dim3(256), 0, st,                  \
+                       static_cast<const T *>(a.k), static_cast<const T *>(a.gate), a.pad,         \
+                       static_cast<T *>(a.pooled), a.n_pools, a.seq, a.kpool, a.head_dim, np_max,  \
+                       tv)
+        // up to 8 slots per pool: every row of the pool in registers at once
+        if (a.f32) {
+            if (a.kpool <= 8)
+                DSA_POOL_KEYS_VEC(float, 8);
+            else
+                DSA_POOL_KEYS_VEC(float, 0);
+        } else {
+            if (a.kpool <= 8)
+                DSA_POOL_KEYS_VEC(uint16_t, 8);
+            else
+                DSA_POOL_KEYS_VEC(uint16_t, 0);
+        }
+#undef DSA_POOL_KEYS_VEC
         return hipGetLastError();
     }
     const unsigned blocks = (unsigned)((total + 255) / 256);

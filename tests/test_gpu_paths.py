@@ -360,14 +360,16 @@ def test_prefill_index_one_workgroup_per_query_block(dsa):
 
 # ---------------------------------------------------------------- pool keys, bf16 rows of any width
 
-def test_pool_keys_bf16_one_channel_per_thread(dsa):
+@pytest.mark.parametrize("d,kp", [(36, 4), (128, 12)])
+def test_pool_keys_bf16_one_channel_per_thread(dsa, d, kp):
     """bf16 keys whose width (36) is not a multiple of 8 take one channel per
     thread (pool_keys_kernel<uint16_t>); 128-wide ones take eight
-    (pool_keys_vec_kernel, config 5 and 6).  Each value within one bf16 ulp
-    plus 2^-20 mag of the f64 oracle, as for config 5."""
-    note("pool keys bf16 d=36")
-    gen = torch.Generator(device="cuda").manual_seed(36)
-    B, L, d, kp = 2, 401, 36, 4
+    (pool_keys_vec_kernel: configs 5 and 6 with kpool 4, here kpool 12, whose
+    rows are read slot by slot).  Each value within one bf16 ulp plus
+    2^-20 mag of the f64 oracle, as for config 5."""
+    note(f"pool keys bf16 d={d} kpool={kp}")
+    gen = torch.Generator(device="cuda").manual_seed(d + kp)
+    B, L = 2, 401
     k = torch.randn(B, L, d, generator=gen, device="cuda").bfloat16()
     gate = (torch.randn(B, L, d, generator=gen, device="cuda") * 2).bfloat16()
     pad = torch.tensor([0, 9], dtype=torch.int32, device="cuda")
@@ -376,16 +378,19 @@ def test_pool_keys_bf16_one_channel_per_thread(dsa):
     ref, rn, mag = oracle.pool_keys(cpu(k), cpu(gate), cpu(pad), kp, want_mag=True)
     assert cpu(npools).tolist() == rn.tolist()
     for b, n in enumerate(rn):
-        bf16_ulp_ok(cpu(pk[b, :n]), ref[b, :n], mag[b, :n], "pool keys d=36")
+        bf16_ulp_ok(cpu(pk[b, :n]), ref[b, :n], mag[b, :n], f"pool keys d={d} kpool={kp}")
         assert torch.all(pk[b, n:] == 0)
 
 
 # ---------------------------------------------------------------- pool keys on f32, short sequences
 
-@pytest.mark.parametrize("L,kp,d", [(1030, 4, 128), (515, 8, 128), (3, 4, 128), (1030, 4, 6)])
+@pytest.mark.parametrize("L,kp,d", [(1030, 4, 128), (515, 8, 128), (3, 4, 128), (1030, 4, 6),
+                                    (1030, 12, 128)])
 def test_pool_keys_f32_and_sequences_shorter_than_a_pool(dsa, L, kp, d):
     """f32 keys and gates: four channels per thread (pool_keys_vec_kernel
-    <float>, d a multiple of 4) and one (pool_keys_kernel<float>, d = 6); and
+    <float>, d a multiple of 4; the pool's rows held in registers up to
+    kpool 8, read slot by slot at kpool 12) and one (pool_keys_kernel<float>,
+    d = 6); and
     L < kpool, where no pool exists and only the counts are written
     (pool_counts_kernel).
     Criterion: each pooled value within 2 (kpool + 4) 2^-24 mag + 2^-23 |ref|
