@@ -333,8 +333,8 @@ struct __attribute__((aligned(16))) Topk32Smem {
 
 // Load scores[lo, hi) into sm.a.ord (column order) and reduce their min/max.
 template <int NT, int CAP, int KM, int NBK>
-__device__ int load_row32(Topk32Smem<NT, CAP, KM, NBK> &sm, const float *__restrict__ row, int lo, int hi,
-                          uint32_t &omin, uint32_t &omax)
+__device__ int load_row32(Topk32Smem<NT, CAP, KM, NBK> &sm, const float *__restrict__ row, int lo,
+                          int hi, uint32_t &omin, uint32_t &omax)
 {
     constexpr int U = (CAP / NT) < 8 ? (CAP / NT) : 8;
     constexpr int NW = NT / 64;
@@ -381,8 +381,8 @@ __device__ int load_row32(Topk32Smem<NT, CAP, KM, NBK> &sm, const float *__restr
 // keys with (ord & mask) > prefix win (k - need of them); of the `cand` keys
 // with (ord & mask) == prefix, the first `need` in column order win.
 template <int NT, int CAP, int KM, int NBK>
-__device__ void select32(Topk32Smem<NT, CAP, KM, NBK> &sm, int n, int k, uint32_t omin, uint32_t omax,
-                         uint32_t &prefix, uint32_t &mask, int &need, int &cand)
+__device__ void select32(Topk32Smem<NT, CAP, KM, NBK> &sm, int n, int k, uint32_t omin,
+                         uint32_t omax, uint32_t &prefix, uint32_t &mask, int &need, int &cand)
 {
     constexpr int NW = NT / 64;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -472,8 +472,8 @@ __device__ __forceinline__ void wave_scan_table(int *tab, int e)
 // mask, the (round, wave) counts are scanned once by one wave, and the
 // positions follow from ballots -- two barriers per counted quantity.
 template <int NT, int CAP, int KM, int NBK>
-__device__ int compact32(Topk32Smem<NT, CAP, KM, NBK> &sm, int n, int col0, uint32_t prefix, uint32_t mask,
-                         int need, int cand, uint32_t &wmin, uint32_t &wmax)
+__device__ int compact32(Topk32Smem<NT, CAP, KM, NBK> &sm, int n, int col0, uint32_t prefix,
+                         uint32_t mask, int need, int cand, uint32_t &wmin, uint32_t &wmax)
 {
     constexpr int NW = NT / 64;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -818,8 +818,8 @@ __device__ int sort32(Topk32Smem<NT, CAP, KM, NBK> &sm, int m, uint32_t wmin, ui
 // crowded buckets).  Returns m = min(k, n); the winners' columns in rank
 // order are sm.wcol[buf][0 .. m).
 template <int NT, int CAP, int KM, int NBK>
-__device__ int topk_sort_cached(Topk32Smem<NT, CAP, KM, NBK> &sm, int n, int lo, int k, uint32_t omin,
-                                uint32_t omax, int &buf)
+__device__ int topk_sort_cached(Topk32Smem<NT, CAP, KM, NBK> &sm, int n, int lo, int k,
+                                uint32_t omin, uint32_t omax, int &buf)
 {
     // n <= k: everything wins (mask 0 makes every key a candidate, all taken)
     uint32_t prefix = 0u, mask = 0u;
