@@ -537,10 +537,11 @@ def test_masked_attend_pooled_selection(dsa, L, sk, variant):
             assert torch.all(out[b, :p] == 0) and torch.all(torch.isneginf(lse[b, :p]))
 
 
-@pytest.mark.parametrize("n_sel", [40, 37])
+@pytest.mark.parametrize("n_sel", [40, 37, 3001])
 def test_masked_attend_set_semantics(dsa, n_sel):
     """Duplicates, INVALID and out-of-range entries; index rows of 40
-    entries (the mask kernel reads four per load) and of 37 (one per load)."""
+    entries (the mask kernel reads four per load), of 37 (one per load) and
+    of 3001 (twenty times the 150 keys: every key many times over)."""
     note(f"masked attend: duplicates / INVALID / out-of-range, no visibility ranges, n_sel={n_sel}")
     gen = torch.Generator(device="cuda").manual_seed(13)
     B, T, H, kd, vd = 2, 150, 8, 192, 256
