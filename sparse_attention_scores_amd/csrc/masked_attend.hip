@@ -390,8 +390,14 @@ __global__ __launch_bounds__(512, 1) void attend_masked_kernel(
     // Each XCD takes a contiguous range of blocks: the query blocks of one
     // (sequence, head) run together on one XCD and stream the same K/V tiles
     // through its L2; within a head the heaviest (latest) blocks go first.
+    // The later half of a head's blocks starts together and walks its tiles
+    // upward; each block of the earlier half starts when one of those ends,
+    // the shortest first, and walks its tiles downward, so that all of the
+    // earlier half read the same tile at the same time (L2 keeps it for
+    // all of them) and end together.
     const int lb = xcd_remap(blockIdx.x, gridDim.x);
     const int qblk = n_qblocks - 1 - lb % n_qblocks;
+    const bool desc = qblk < n_qblocks / 2;
     const int bh = lb / n_qblocks;
     const int b = bh / H, h = bh % H;
     const int q0 = qblk * MK_QB;
@@ -484,8 +490,12 @@ __global__ __launch_bounds__(512, 1) void attend_masked_kernel(
     // DMA of tile t into stage st; the last tile of a row whose length is
     // not a multiple of 32 clamps its rows past n_k to the last key (those
     // keys are masked) with addresses computed per lane
-    auto dma_tile = [&](int t, auto STc) {
+    // tile u of the walk (T0 <= u < T1) is key tile u, or T0 + T1 - 1 - u
+    // downward
+    const int t_flip = T0 + T1 - 1;
+    auto dma_tile = [&](int u, auto STc) {
         constexpr int st = decltype(STc)::value;
+        const int t = desc ? t_flip - u : u;
         const int k0 = t * MK_TILE;
         const bool full = k0 + MK_TILE <= n_k;
         const unsigned char *ks_ = kb + (uint64_t)(uint32_t)k0 * ksr2;
@@ -660,7 +670,8 @@ __global__ __launch_bounds__(512, 1) void attend_masked_kernel(
         uint32_t word = 0u;
         if (t < T1)
             lds_read_b32_nowait<ST * MK_QB * 4>(word, lds_mw);
-        const bool act = t < T1 && t >= tw_begin && t < tw_end;
+        const int tp = desc ? t_flip - t : t;
+        const bool act = t < T1 && tp >= tw_begin && tp < tw_end;
         // one instruction stream for both products keeps the register
         // allocation within 256: an inactive previous tile contributes zero
         // weights (P = 0 against finite V), and the scores of an inactive
