@@ -120,6 +120,8 @@ def _probe():
     lib.probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
                                ctypes.c_void_p]
     lib.probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.probe_lds_stream.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                     ctypes.c_void_p]
     return lib
 
 
@@ -170,6 +172,15 @@ def measure_peaks():
 
     t_copy = timed(lambda: lib.probe_copy(x.data_ptr(), y.data_ptr(), nbytes, COPY_BLOCKS, st), 10)
     t_torch = timed(lambda: y.copy_(x), 10)   # torch's own copy kernel, as a cross-check
+    # direct-to-LDS tile streaming, one workgroup per CU: 32 tiles (1 MiB,
+    # served by L2) and all 32768 tiles of the 1 GiB buffer (HBM)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    steps = 2000
+    stream_bytes = 256 * steps * 29 * 1024
+    lds_stream = {}
+    for name, n_tiles in (("l2", 32), ("hbm", nbytes // 32768)):
+        t = timed(lambda: lib.probe_lds_stream(x.data_ptr(), n_tiles, steps, sink.data_ptr(), st), 3)
+        lds_stream[name] = round(stream_bytes / t / 1e9, 1)
     del x, y
     blocks, iters = 256 * 8, 4000
     out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
@@ -179,10 +190,15 @@ def measure_peaks():
             "hbm_copy_probe_GBps": round(2 * nbytes / t_copy / 1e9, 1),
             "hbm_copy_torch_GBps": round(2 * nbytes / t_torch / 1e9, 1),
             "mfma_bf16_TFLOPs": round(flops / t_mfma / 1e12, 1),
+            "lds_stream_from_l2_GBps": lds_stream["l2"],
+            "lds_stream_from_hbm_GBps": lds_stream["hbm"],
             "how": "copy: 1 GiB read + 1 GiB written, the faster of a 16-byte-per-lane "
                    "span-per-workgroup kernel and torch's copy; "
                    "mfma: 2048 workgroups x 4 waves, each 4 independent chains of "
-                   "v_mfma_f32_32x32x16_bf16, no memory traffic"}
+                   "v_mfma_f32_32x32x16_bf16, no memory traffic; "
+                   "lds_stream: 256 workgroups of 8 waves, 29 one-KB direct-to-LDS loads per "
+                   "32 KB tile, two tiles in flight, one barrier per tile, from 32 tiles (L2) "
+                   "or 32768 (HBM)"}
 
 
 def _parse():

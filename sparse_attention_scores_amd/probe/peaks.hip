@@ -59,6 +59,44 @@ __global__ __launch_bounds__(256) void probe_mfma_kernel(int iters, float *__res
     out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+// Direct-to-LDS streaming of 32 KB tiles, the way the attention kernels
+// stage theirs: one workgroup of 8 waves per CU, 29 one-KB
+// global_load_lds_dwordx4 per tile (four per wave; waves 0-6 take four
+// slots, wave 7 one), a ring of four LDS stages, two tiles in flight, one
+// workgroup barrier per tile.  Workgroup b reads tile (7b + i) mod n_tiles at
+// step i, so a small n_tiles is served by L2 and a large one by HBM.
+__global__ __launch_bounds__(512, 1) void probe_lds_stream_kernel(const unsigned char *__restrict__ src,
+                                                                 int n_tiles, int steps,
+                                                                 uint32_t *__restrict__ sink)
+{
+    __shared__ __attribute__((aligned(16))) unsigned char lds[4][32768];
+    const int lane = threadIdx.x & 63, wid = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    uint32_t acc = 0;
+    for (int i = 0; i < steps; ++i) {
+        const unsigned char *s = src + (size_t)((blockIdx.x * 7 + i) % n_tiles) * 32768;
+        const int st = i & 3;
+        for (int j = 0; j < 4; ++j) {
+            const int slot = wid * 4 + j;
+            if (slot < 29)
+                __builtin_amdgcn_global_load_lds(
+                    s + slot * 1024 + lane * 16,
+                    (__attribute__((address_space(3))) void *)&lds[st][slot * 1024], 16, 0, 0);
+        }
+        // the tile issued two steps ago has landed (at most the last two
+        // tiles' loads outstanding), then every wave's share is visible
+        if (i >= 2)
+            __builtin_amdgcn_s_waitcnt((8 & 15) | (7 << 4) | (15 << 8));  // vmcnt(8)
+        else
+            __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));  // vmcnt(0)
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        acc += *reinterpret_cast<const uint32_t *>(&lds[(i + 2) & 3][lane * 4]);
+    }
+    __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));
+    asm volatile("s_barrier" ::: "memory");
+    if (acc == 0x12345678u)
+        sink[0] = acc;
+}
+
 extern "C" {
 
 // Copies `bytes` (a multiple of 16) from src to dst on `stream`.
@@ -80,6 +118,19 @@ int probe_mfma_bf16(int blocks, int iters, float *out, void *stream)
         return -1;
     hipLaunchKernelGGL(probe_mfma_kernel, dim3(blocks), dim3(256), 0,
                        reinterpret_cast<hipStream_t>(stream), iters, out);
+    return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+// 256 workgroups stream `steps` tiles each from src (n_tiles tiles of
+// 32 KB); bytes moved = 256 * steps * 29 KB.  sink: 4 bytes, never written
+// unless the data sum is one particular value.
+int probe_lds_stream(const void *src, int n_tiles, int steps, uint32_t *sink, void *stream)
+{
+    if (!src || !sink || n_tiles <= 0 || steps <= 0)
+        return -1;
+    hipLaunchKernelGGL(probe_lds_stream_kernel, dim3(256), dim3(512), 0,
+                       reinterpret_cast<hipStream_t>(stream),
+                       static_cast<const unsigned char *>(src), n_tiles, steps, sink);
     return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
